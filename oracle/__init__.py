@@ -1,0 +1,29 @@
+"""fp64 CPU oracle for block prefix-LM joint attention (π0 / π0.5).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call, link
+or execute this package; only the tests, the smoke entry point and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP path.
+
+What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
+
+  mask.block_ids / mask.attn_mask / mask.positions / mask.decode_mask
+      the cumsum block mask AND padding AND forbidden segment pairs, and the
+      token positions ("VLA 代码精读 — OpenPI & StarVLA" §1.2, §1.5, §1.6;
+      "π0.5 vs MM-DiT joint attention", three-block permission table;
+      "Pi0-FAST 模型架构" §2.3).
+  attention.joint_attention
+      one softmax over the concatenated prefix+suffix KV pool with grouped
+      query heads ("π0.5 vs MM-DiT joint attention", first section).
+  attention.cached_decode
+      suffix queries over cached prefix K/V plus their own K/V
+      ("VLA 代码精读" §1.6).
+  flow.euler_sample / flow.euler_update
+      the Euler flow-matching sampler, t from 1 to 0 ("VLA 代码精读" §1.2, §1.6).
+  flow.velocity_net
+      the random-weight stand-in velocity network.  The pages give no weights
+      or exact layer for it: **parity unpinned** as a whole (only its pieces
+      and its W_o = 0 reduction are pinned).
+
+Readings of points the pages leave open are listed in each docstring.
+"""
+from . import bf16, mask, attention, flow  # noqa: F401

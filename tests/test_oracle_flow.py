@@ -1,0 +1,110 @@
+"""Pins of the oracle's Euler sampler (closed forms, the page's loop rule) and of
+its bf16 rounding; structural checks of the stand-in velocity net."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import flow as F
+from oracle import attention as A
+from oracle.bf16 import round_bf16
+from prefix_lm_joint_amd import inputs as I
+
+
+@pytest.mark.parametrize("N", [1, 3, 10, 28])
+def test_constant_velocity_returns_noise_minus_v(N):
+    r = np.random.default_rng(N)
+    noise = r.standard_normal((2, 50, 32))
+    v = r.standard_normal((2, 50, 32))
+    x = F.euler_sample(noise, lambda x, t: v, N)
+    np.testing.assert_allclose(x, noise - v, rtol=0, atol=1e-12)
+
+
+def test_tiny_closed_form_recovers_action():
+    """With the target velocity noise - action held fixed, 10 Euler steps land on the action."""
+    r = np.random.default_rng(11)
+    noise = r.standard_normal((1, 8, 4))
+    action = r.standard_normal((1, 8, 4))
+    x = F.euler_sample(noise, lambda x, t: noise - action, 10)
+    np.testing.assert_allclose(x, action, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("lam", [-0.7, 0.3, 2.0])
+def test_linear_velocity_closed_form(lam):
+    N = 10
+    noise = np.random.default_rng(3).standard_normal((4, 5))
+    x = F.euler_sample(noise, lambda x, t: lam * x, N)
+    np.testing.assert_allclose(x, (1 - lam / N) ** N * noise, rtol=1e-12)
+
+
+def test_time_dependent_velocity_sees_the_time_grid():
+    """v = c*t: x_N = noise + dt*c*sum_k t_k = noise - c*(N+1)/(2N)."""
+    N = 10
+    c = np.array([1.5, -2.0])
+    x = F.euler_sample(np.zeros(2), lambda x, t: c * t, N)
+    np.testing.assert_allclose(x, -c * (N + 1) / (2 * N), rtol=1e-13)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_while_loop_rule_runs_exactly_n_steps(dtype):
+    """The page's loop keeps stepping while t >= -dt/2, accumulating t += dt;
+    that yields exactly N steps, which the oracle's fixed count reproduces."""
+    for N in range(1, 60):
+        dt = dtype(-1.0 / N)
+        t, count = dtype(1.0), 0
+        while t >= -dt / dtype(2):
+            t = dtype(t + dt)
+            count += 1
+        assert count == N == len(F.time_grid(N))
+    g = F.time_grid(10)
+    assert g[0] == 1.0 and abs(g[-1] - 0.1) < 1e-15 and (np.diff(g) < 0).all()
+
+
+def test_bf16_rounding_matches_torch():
+    r = np.random.default_rng(9)
+    x = np.concatenate([r.standard_normal(100000).astype(np.float32),
+                        np.float32([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0, 3.0e-30])])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_bf16(x.astype(np.float64)), want)
+
+
+def _net_inputs(seed, B=2, P=12, layers=3):
+    W, A_, Hq, Hkv, d, H = 64, 4, 8, 1, 16, 5
+    w = I.net_weights(seed, width=W, action_dim=A_, Hq=Hq, Hkv=Hkv, d=d)
+    wf = {f: (I.bf16_bits_to_f64(getattr(w, f)) if getattr(w, f).dtype == np.uint16
+              else getattr(w, f).astype(np.float64)) for f in w.__dataclass_fields__}
+    r = np.random.default_rng(seed)
+    ck = r.standard_normal((layers, B, P, Hkv, d))
+    cv = r.standard_normal((layers, B, P, Hkv, d))
+    pre = np.ones((B, P), np.uint8)
+    pre[0, P - 3:] = 0
+    s = I.pi0_structure(P, H)
+    x = r.standard_normal((B, H, A_))
+    state = r.standard_normal((B, A_))
+    return wf, ck, cv, pre, s.ar[P:], x, state, (Hq, Hkv, d)
+
+
+def test_net_without_out_projection_ignores_the_cache():
+    wf, ck, cv, pre, sar, x, st, (Hq, Hkv, d) = _net_inputs(1)
+    wf["w_o"] = np.zeros_like(wf["w_o"])
+    v1 = F.velocity_net(x, 0.4, st, wf, ck, cv, pre, sar, Hq, Hkv, d)
+    v2 = F.velocity_net(x, 0.4, st, wf, ck * 3 + 1, cv[::-1], pre, sar, Hq, Hkv, d)
+    assert np.array_equal(v1, v2)
+
+
+def test_net_layers_use_the_pinned_decode():
+    """Each layer's attention output is the cached decode of that layer's cache."""
+    wf, ck, cv, pre, sar, x, st, (Hq, Hkv, d) = _net_inputs(2)
+    _, trace = F.velocity_net(x, 0.7, st, wf, ck, cv, pre, sar, Hq, Hkv, d, return_trace=True)
+    for layer, tr in enumerate(trace):
+        o = A.cached_decode(tr["q"], tr["k"], tr["v"], ck[layer], cv[layer], pre, sar)
+        np.testing.assert_array_equal(round_bf16(o), tr["o"])
+
+
+def test_net_padded_cache_slots_do_not_matter():
+    wf, ck, cv, pre, sar, x, st, (Hq, Hkv, d) = _net_inputs(3)
+    v1 = F.velocity_net(x, 0.2, st, wf, ck, cv, pre, sar, Hq, Hkv, d)
+    ck2, cv2 = ck.copy(), cv.copy()
+    ck2[:, 0, -3:] = 1e3
+    cv2[:, 0, -3:] = -1e3
+    v2 = F.velocity_net(x, 0.2, st, wf, ck2, cv2, pre, sar, Hq, Hkv, d)
+    assert np.array_equal(v1, v2)
