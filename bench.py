@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Benchmark of the block prefix-LM joint-attention path on one MI355X.
+
+One step = one π0 control step on synthetic inputs resident in HBM:
+    mask build for the 816-token prefix
+    18 x joint-attention prefill over the prefix (K/V read in place from the cache)
+    10 x Euler flow step, each running the stand-in velocity net over 18 cached
+         layers (QKV projection, cached suffix decode, output projection) with the
+         output projection and the Euler update fused.
+value = control steps per second (B = 1).
+
+Besides the step, the two kernels the metric names are measured live with HIP
+events on the stream they run on:
+    prefill at the π0.5 training shape (B=32, L=962, three blocks) -> MFMA fraction
+    cached decode at the serving shape (B=64, 816 slots)           -> HBM GB/s
+and the fp64 oracle is timed on the host's cores over a bounded sample.
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_BYTES = 8.0e12    # MI355X HBM3E peak
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--kernel-iters", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit"], default=None,
+                   help="run just one leg (for profiling)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Ctx:
+    def __init__(self):
+        import numpy as np
+        import torch
+        from prefix_lm_joint_amd import binding as Bd
+        from prefix_lm_joint_amd import inputs as I
+        self.np, self.torch, self.Bd, self.I = np, torch, Bd, I
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+
+    def bf(self, bits):
+        np, torch = self.np, self.torch
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(self.dev)
+
+    def u8(self, a):
+        return self.torch.from_numpy(self.np.ascontiguousarray(a, dtype=self.np.uint8)).to(self.dev)
+
+    def f32(self, a):
+        return self.torch.from_numpy(self.np.ascontiguousarray(a, dtype=self.np.float32)).to(self.dev)
+
+    def time_ms(self, fn, iters, warmup=2):
+        """Average ms per call of fn over `iters` calls, HIP events on the launch stream."""
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for _ in range(iters):
+            fn()
+        b.record(self.stream)
+        b.synchronize()
+        return a.elapsed_time(b) / iters
+
+
+# ---------------------------------------------------------------------------
+# π0 control step (B = 1)
+# ---------------------------------------------------------------------------
+
+def build_control_step(cx: Ctx):
+    np, torch, Bd, I = cx.np, cx.torch, cx.Bd, cx.I
+    w = I.pi0_step()
+    s = w.structure
+    P, H, A, L = s.n_prefix, w.horizon, w.action_dim, w.layers
+    seed = w.seed_base
+    q = torch.stack([cx.bf(I.bf16_normal(seed + 16 * l + 1, (1, P, 8, 256))) for l in range(L)])
+    ck = cx.bf(I.bf16_normal(seed + 500, (L, 1, P, 1, 256)))
+    cv = cx.bf(I.bf16_normal(seed + 501, (L, 1, P, 1, 256)))
+    pmask = np.ones((1, P), np.uint8)
+    cache = Bd.KVCache(ck, cv, cx.u8(pmask))
+    ar_pre, seg_pre = cx.u8(s.ar[:P]), cx.u8(s.seg[:P])
+    in_mask = cx.u8(pmask)
+    mask_ws = torch.empty(Bd.pi_mask_workspace_bytes(1, P), dtype=torch.uint8, device=cx.dev)
+    o = torch.empty((1, P, 8, 256), dtype=torch.bfloat16, device=cx.dev)
+    net = Bd.VelocityNet.from_numpy(I.net_weights(seed + 600, width=w.width, action_dim=A), cx.dev)
+    flow_ws = Bd.flow_workspace(net, 1, H, cx.dev)
+    sar = cx.u8(s.ar[P:])
+    state = cx.f32(I.f32_normal(seed + 601, (1, A)))
+    noise = cx.f32(I.f32_normal(seed + 602, (1, H, A)))
+    x = torch.empty_like(noise)
+
+    def step():
+        m = Bd.pi_mask_build(in_mask, ar_pre, seg_pre, 0, workspace=mask_ws)
+        for l in range(L):
+            Bd.pi_joint_attn_prefill(q[l], ck[l], cv[l], m, o=o)
+        x.copy_(noise)
+        Bd.pi_flow_sample(net, cache, sar, state, None, x, num_steps=w.steps, workspace=flow_ws)
+
+    parts = {
+        "mask_build": lambda: Bd.pi_mask_build(in_mask, ar_pre, seg_pre, 0, workspace=mask_ws),
+        "prefill_layer": None,
+        "decode_layer": None,
+    }
+    m0 = Bd.pi_mask_build(in_mask, ar_pre, seg_pre, 0, workspace=mask_ws)
+    parts["prefill_layer"] = lambda: Bd.pi_joint_attn_prefill(q[0], ck[0], cv[0], m0, o=o)
+    qs = cx.bf(I.bf16_normal(seed + 700, (1, H + 1, 8, 256)))
+    ks = cx.bf(I.bf16_normal(seed + 701, (1, H + 1, 1, 256)))
+    vs = cx.bf(I.bf16_normal(seed + 702, (1, H + 1, 1, 256)))
+    os_ = torch.empty_like(qs)
+    parts["decode_layer"] = lambda: Bd.pi_suffix_decode_step(cache, 0, qs, ks, vs, sar, o_s=os_)
+    parts["flow_sample_10_steps"] = lambda: (x.copy_(noise), Bd.pi_flow_sample(
+        net, cache, sar, state, None, x, num_steps=w.steps, workspace=flow_ws))
+    pairs_prefill = P * P
+    return w, step, parts, pairs_prefill
+
+
+# ---------------------------------------------------------------------------
+# prefill at the π0.5 training shape and decode at the serving shape
+# ---------------------------------------------------------------------------
+
+def prefill_kernel_leg(cx: Ctx, iters: int, workload: str):
+    torch, Bd, I = cx.torch, cx.Bd, cx.I
+    w = I.WORKLOADS[workload]()
+    s = w.structure
+    q, k, v = (cx.bf(t) for t in w.qkv())
+    valid = cx.u8(w.input_mask())
+    m = Bd.pi_mask_build(valid, cx.u8(s.ar), cx.u8(s.seg), I.forbid_bits(s.forbid))
+    pairs = int(Bd.pi_mask_materialize(m).sum(dtype=torch.int64).item())
+    o = torch.empty_like(q)
+    ms = cx.time_ms(lambda: Bd.pi_joint_attn_prefill(q, k, v, m, o=o), iters)
+    flops = 4.0 * w.d * w.Hq * pairs   # QK^T and PV, 2 flops per multiply-add, per head
+    byts = (q.numel() + k.numel() + v.numel() + o.numel()) * 2
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "B": w.B, "L": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+        "allowed_pairs": pairs, "gflop_per_launch": flops / 1e9, "us_per_launch": ms * 1e3,
+        "achieved_tflops": tflops, "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
+        "algorithmic_bytes": byts, "kernel": "prefill_kernel",
+    }
+
+
+def decode_kernel_leg(cx: Ctx, iters: int):
+    np, torch, Bd, I = cx.np, cx.torch, cx.Bd, cx.I
+    w = I.serving_decode()
+    s = w.structure
+    P, S, B = s.n_prefix, s.n - s.n_prefix, w.B
+    pm = w.input_mask()[:, :P]
+    lens = pm.sum(axis=1)
+    # all 18 layers (963 MB, larger than the 256 MB Infinity Cache), rotated so every
+    # launch streams its layer's K/V from HBM; drawn on the device from a seeded
+    # generator (bench-only inputs; parity is covered by the tests)
+    layers = w.layers
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(w.seed_base + 1)
+    ck = torch.randn((layers, B, P, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cv = torch.randn((layers, B, P, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cache = Bd.KVCache(ck, cv, cx.u8(pm))
+    qs = cx.bf(I.bf16_normal(w.seed_base + 3, (B, S, 8, 256)))
+    ks = cx.bf(I.bf16_normal(w.seed_base + 4, (B, S, 1, 256)))
+    vs = cx.bf(I.bf16_normal(w.seed_base + 5, (B, S, 1, 256)))
+    sar = cx.u8(s.ar[P:])
+    o = torch.empty_like(qs)
+    state = {"l": 0}
+
+    def call():
+        Bd.pi_suffix_decode_step(cache, state["l"] % layers, qs, ks, vs, sar, o_s=o)
+        state["l"] += 1
+
+    ms = cx.time_ms(call, iters)
+    kv_bytes = int(lens.sum()) * 256 * 2 * 2
+    qo_bytes = B * S * 8 * 256 * 2 * 2
+    skv_bytes = B * S * 256 * 2 * 2
+    byts = kv_bytes + qo_bytes + skv_bytes
+    # suffix self pairs: state token sees itself, actions see state + all actions
+    pairs = int(lens.sum()) * S + B * (1 + (S - 1) * S)
+    flops = 4.0 * 256 * 8 * pairs
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "B": B, "slots": P, "valid_len_mean": float(lens.mean()), "S": S,
+        "algorithmic_bytes_per_launch": byts, "us_per_launch": ms * 1e3, "achieved_gbs": gbs,
+        "hbm_frac": gbs * 1e9 / PEAK_HBM_BYTES, "gflop_per_launch": flops / 1e9,
+        "achieved_tflops": flops / (ms * 1e-3) / 1e12, "kernel": "decode_kernel",
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on the host cores, bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(sample_prefill_layers=2, sample_evals=1):
+    import numpy as np
+    from oracle import attention as OA
+    from oracle import flow as OF
+    from prefix_lm_joint_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    w = I.pi0_step()
+    s = w.structure
+    P, H, A, L = s.n_prefix, w.horizon, w.action_dim, w.layers
+    f64 = I.bf16_bits_to_f64
+    valid = np.ones((1, P), np.uint8)
+    t0 = time.perf_counter()
+    for l in range(sample_prefill_layers):
+        q = f64(I.bf16_normal(9000 + l, (1, P, 8, 256)))
+        k = f64(I.bf16_normal(9100 + l, (1, P, 1, 256)))
+        v = f64(I.bf16_normal(9200 + l, (1, P, 1, 256)))
+        OA.joint_attention(q, k, v, valid, s.ar[:P])
+    t_pre = (time.perf_counter() - t0) / sample_prefill_layers
+    nw = I.net_weights(9300, width=w.width, action_dim=A)
+    wf = {f: (f64(getattr(nw, f)) if getattr(nw, f).dtype == np.uint16 else getattr(nw, f).astype(np.float64))
+          for f in nw.__dataclass_fields__}
+    ck = f64(I.bf16_normal(9400, (L, 1, P, 1, 256)))
+    cv = f64(I.bf16_normal(9401, (L, 1, P, 1, 256)))
+    state = I.f32_normal(9402, (1, A)).astype(np.float64)
+    x = I.f32_normal(9403, (1, H, A)).astype(np.float64)
+    t0 = time.perf_counter()
+    for _ in range(sample_evals):
+        vel = OF.velocity_net(x, 0.5, state, wf, ck, cv, valid, s.ar[P:], 8, 1, 256)
+        x = OF.euler_update(x, vel, -0.1)
+    t_eval = (time.perf_counter() - t0) / sample_evals
+    t_step = L * t_pre + w.steps * t_eval
+    return {
+        "value": 1.0 / t_step, "unit": "control steps/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"pi0 control step scaled from {sample_prefill_layers} timed prefill layers "
+                   f"({t_pre:.2f} s/layer, x{L}) and {sample_evals} timed velocity evaluations "
+                   f"({t_eval:.2f} s each, 18 layers, x{w.steps}); fp64 numpy"),
+        "seconds_per_control_step": t_step,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this path is "
+              f"built and measured for a single MI355X; see the sharding note in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    cx = Ctx()
+    result = {}
+    if args.only in (None, "step"):
+        log("building the pi0 control step")
+        w, step, parts, _ = build_control_step(cx)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        log(f"timing {args.steps} control steps")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(cx.stream)
+        for _ in range(args.steps):
+            step()
+        b.record(cx.stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        breakdown = {k: cx.time_ms(fn, 10) * 1e3 for k, fn in parts.items()}
+        result.update(ms_per_step=ms, value=1000.0 / ms, breakdown_us=breakdown)
+        log(f"control step {ms:.3f} ms ({1000 / ms:.1f}/s); parts {breakdown}")
+    kernels = {}
+    if args.only in (None, "prefill"):
+        log("prefill kernel leg (pi05 B=32 L=962)")
+        kernels["prefill"] = prefill_kernel_leg(cx, args.kernel_iters, "pi05_three_block_prefill")
+        log(str(kernels["prefill"]))
+    if args.only in (None, "decode"):
+        log("decode kernel leg (B=64 816 slots)")
+        kernels["decode"] = decode_kernel_leg(cx, args.kernel_iters)
+        log(str(kernels["decode"]))
+    if args.only == "mmdit":
+        kernels["mmdit"] = prefill_kernel_leg(cx, args.kernel_iters, "mmdit_full_bidirectional")
+        log(str(kernels["mmdit"]))
+    if args.only is not None:
+        print(json.dumps({"only": args.only, **result, "kernels": kernels}))
+        return
+
+    dec = kernels["decode"]
+    pre = kernels["prefill"]
+    roofline = {
+        "kernel": "decode_kernel (cached suffix decode, B=64, 816 slots)",
+        "bound": "hbm", "achieved": dec["achieved_gbs"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+        "frac": dec["achieved_gbs"] * 1e9 / PEAK_HBM_BYTES, "traffic": None,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        cpu = cpu_baseline()
+        log(str(cpu))
+    out = {
+        "metric": "control steps/s (10-step Euler, cached prefix); MFMA% prefill, HBM GB/s decode",
+        "value": result["value"], "unit": "control steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": result["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "pi0_control_step", "B": 1, "prefix_tokens": 816, "suffix_tokens": 51,
+                   "layers": 18, "euler_steps": 10, "Hq": 8, "Hkv": 1, "head_dim": 256,
+                   "velocity_net": "stand-in, width 1024, one weight set shared by the 18 cache layers"},
+        "roofline": roofline,
+        "prefill_mfma": {"kernel": "prefill_kernel (pi05 B=32 L=962)", "bound": "mfma",
+                         "achieved": pre["achieved_tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                         "frac": pre["mfma_frac"], "us_per_launch": pre["us_per_launch"]},
+        "decode_hbm": {"kernel": "decode_kernel (B=64 816 slots)", "achieved_gbs": dec["achieved_gbs"],
+                       "frac": dec["hbm_frac"], "us_per_launch": dec["us_per_launch"]},
+        "breakdown_us": result["breakdown_us"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

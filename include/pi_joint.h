@@ -1,0 +1,218 @@
+/*
+ * pi_joint.h -- C ABI of the MI355X (gfx950) block prefix-LM joint-attention path.
+ *
+ * The operations follow the π0 / π0.5 action-generation path described in
+ *   [P1] "VLA 代码精读 — OpenPI & StarVLA", Part 1 (§1.2 mask and Euler sampling,
+ *        §1.5 joint forward, §1.6 sample_actions with a prefix KV cache);
+ *   [P3] "π0.5 vs MM-DiT joint attention" (hebangwen): one shared KV pool and one
+ *        softmax, 8 query heads / 1 KV head / head_dim 256, the π0.5 three-block
+ *        permission table, the cumsum block rule;
+ *   [P4] "Pi0-FAST 模型架构", §2.3 (mask AND padding), §4.1 (KV-cache decode).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, contiguous, in the
+ *     layouts stated below, 16-byte aligned.  bf16 tensors are passed as void*.
+ *     Host-pointer arguments are marked (host).
+ *   - The library never allocates, frees or synchronises inside these calls.
+ *     Scratch memory is passed in as a workspace whose size is queried first.
+ *   - Arguments are validated on the host before anything is launched; a bad
+ *     argument returns PI_ERR_INVALID_ARG, an unsupported shape
+ *     PI_ERR_UNSUPPORTED, a too-small workspace PI_ERR_WORKSPACE, and nothing
+ *     is launched.  A launch failure returns PI_ERR_HIP.  Faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work of one call
+ *     is ordered on that stream.  There is no global mutable state; concurrent
+ *     calls on different streams need distinct output buffers and workspaces.
+ *   - pi_last_error() returns a description of the most recent failure on the
+ *     calling thread.
+ */
+#ifndef PI_JOINT_H
+#define PI_JOINT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pi_status {
+  PI_OK = 0,
+  PI_ERR_INVALID_ARG = -1,
+  PI_ERR_UNSUPPORTED = -2,
+  PI_ERR_WORKSPACE = -3,
+  PI_ERR_HIP = -4
+} pi_status;
+
+typedef void* pi_stream; /* hipStream_t */
+
+/* Segment tags used by the forbidden-pair rule ([P3] permission table). */
+#define PI_SEG_PREFIX 0
+#define PI_SEG_FAST 1
+#define PI_SEG_EXPERT 2
+/* Bit (4*query_seg + key_seg) of a forbid mask: that query segment may not read that key segment. */
+#define PI_FORBID(qs, ks) (1u << (4u * (qs) + (ks)))
+
+/* Granularity of the mask's tile table: 16 query tokens x 32 key tokens. */
+#define PI_MASK_TILE_Q 16
+#define PI_MASK_TILE_K 32
+/* Tile classes stored in pi_mask.tiles. */
+#define PI_TILE_EMPTY 0   /* no (query, key) pair of the tile is visible: skipped */
+#define PI_TILE_PARTIAL 1 /* some pairs visible: evaluate the rule per pair */
+#define PI_TILE_FULL 2    /* every pair visible: no per-pair test */
+
+/*
+ * Block prefix-LM mask in compact form ([P1] §1.2/§1.5, [P3] cumsum rule and
+ * permission table, [P4] §2.3).  Key j is visible from query i of sample b iff
+ *     bid[j] <= bid[i]  and  valid[b,i]  and  valid[b,j]
+ *     and bit (4*seg[i] + seg[j]) of forbid_bits is clear,
+ * with bid = inclusive cumsum of ar.  No N x N mask is stored.  All pointers are
+ * device pointers into the workspace given to pi_mask_build; the struct itself
+ * is host memory filled by pi_mask_build.
+ *   bid   int32 [N]          inclusive cumsum of ar
+ *   pos   int32 [B, N]       cumsum(valid) - 1 (token positions, [P1] §1.5)
+ *   tok   uint32 [B, N]      packed per-token word: bit0 valid, bits1-2 seg, bits3.. bid
+ *   tiles uint8 [B, n_qt, n_kt]  PI_TILE_* class of each 16x32 (query, key) tile
+ */
+typedef struct pi_mask {
+  int32_t B, N;
+  int32_t n_qt, n_kt;
+  uint32_t forbid_bits;
+  int32_t* bid;
+  int32_t* pos;
+  uint32_t* tok;
+  uint8_t* tiles;
+} pi_mask;
+
+/* Workspace bytes pi_mask_build needs for B samples of N tokens. */
+size_t pi_mask_workspace_bytes(int B, int N);
+
+/*
+ * Build the compact mask.  input_mask uint8 [B,N] (nonzero = valid token),
+ * ar uint8 [N] (nonzero = the token opens a new block; shared by the batch),
+ * seg uint8 [N] or NULL (all PI_SEG_PREFIX; only the low two bits are used),
+ * forbid_bits as PI_FORBID().  1 <= B <= 65535, 1 <= N <= 1<<20.
+ * Integer results are exact.
+ */
+pi_status pi_mask_build(const uint8_t* input_mask, const uint8_t* ar, const uint8_t* seg,
+                        uint32_t forbid_bits, int B, int N, void* workspace,
+                        size_t workspace_bytes, pi_mask* out, pi_stream stream);
+
+/* Test aid: expand the compact mask into dense uint8 [B,N,N] (1 = visible). */
+pi_status pi_mask_materialize(const pi_mask* mask, uint8_t* dense, pi_stream stream);
+
+/*
+ * Joint-attention prefill over one shared KV pool ([P3] first section; [P1] §1.5):
+ *   O[b,i,h,:] = sum_j softmax_j(scale * q[b,i,h,:].k[b,j,g,:]) v[b,j,g,:]
+ * over the keys j visible from i under `mask`, g = floor(h*Hkv/Hq); one softmax
+ * per (b, i, h).  Masked keys are excluded by selection (their K/V values can
+ * never reach an output, NaN included).  A query with no visible key gets O = 0.
+ *   q  bf16 [B, L, Hq, d]    k, v  bf16 [B, L, Hkv, d]    o  bf16 [B, L, Hq, d]
+ *   mask built for the same B and N = L.  scale > 0 (usually 1/sqrt(d)).
+ * Supported heads: (Hq, Hkv, d) = (8, 1, 256) and (Hq, Hkv, d) with Hq == Hkv and
+ * d = 64.  bf16 matrix-core products with fp32 accumulation.
+ * If `cache` is non-NULL, K/V rows of tokens [0, cache->len) are also copied to
+ * cache layer `layer` (cache->B == B, cache->len <= L).
+ */
+typedef struct pi_kv_cache pi_kv_cache;
+pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
+                                int Hkv, int d, float scale, const pi_mask* mask, void* o,
+                                const pi_kv_cache* cache, int layer, pi_stream stream);
+
+/*
+ * Per-layer prefix KV cache ([P1] §1.6; [P4] §4.1).  Device memory owned by the caller.
+ *   k, v         bf16 [layers, B, capacity, Hkv, d]
+ *   prefix_mask  uint8 [B, capacity]: nonzero = slot holds a valid prefix token
+ *   len          slots in use (the prefix length P), <= capacity
+ * When capacity == L the per-layer slices k + layer*B*capacity*Hkv*d are laid out
+ * exactly as the prefill's k/v inputs, so a prefix-only prefill can read them in place.
+ */
+struct pi_kv_cache {
+  void* k;
+  void* v;
+  const uint8_t* prefix_mask;
+  int32_t layers, B, capacity, Hkv, d;
+  int32_t len;
+};
+
+/*
+ * Cached suffix decode for one layer ([P1] §1.6): the S suffix queries attend to
+ * the valid prefix slots of cache layer `layer` plus the suffix keys allowed by
+ * the suffix's own block rule (suffix key j visible from suffix query i iff
+ * cumsum(suffix_ar)[j] <= cumsum(suffix_ar)[i]); all suffix tokens are valid.
+ *   q_s  bf16 [B, S, Hq, d]   k_s, v_s  bf16 [B, S, Hkv, d]   o_s  bf16 [B, S, Hq, d]
+ *   suffix_ar  uint8 [S] (device)
+ * Supported: Hq = 8, Hkv = 1, d = 256, 1 <= S <= 128.  Each cached K/V tile is
+ * read from HBM once per sample and shared by all 8 query heads.
+ */
+pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s,
+                                const void* k_s, const void* v_s, const uint8_t* suffix_ar,
+                                int B, int S, int Hq, float scale, void* o_s, pi_stream stream);
+
+/* Euler update x <- x + dt * v over n fp32 elements ([P1] §1.2). */
+pi_status pi_euler_update(float* x, const float* v, float dt, int64_t n, pi_stream stream);
+
+/*
+ * Stand-in velocity net (random weights; the pages give no weights).  nn.Linear
+ * layout [out, in]; matrices bf16, vectors fp32.  W = width, A = action_dim.
+ *   w_state [W, A], b_state [W]        state token  = r(state) W_state^T + b_state
+ *   w_in    [W, A], b_in [W], w_time [W]  action tokens = r(x) W_in^T + b_in + t*w_time
+ *   w_q [Hq*d, W], w_k, w_v [Hkv*d, W], w_o [W, Hq*d]
+ *       per cache layer l: a = r(h); q,k,v = r(a W^T); o = r(decode_l(q,k,v)); h += o W_o^T
+ *   w_out [A, W], b_out [A]            velocity = r(h[:,1:]) W_out^T + b_out
+ * r() rounds to bf16; products accumulate in fp32; h is fp32.  The same weights
+ * serve every cache layer.
+ */
+typedef struct pi_velocity_net {
+  int32_t width, action_dim, Hq, Hkv, d;
+  const void* w_state;
+  const float* b_state;
+  const void* w_in;
+  const float* b_in;
+  const float* w_time;
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_o;
+  const void* w_out;
+  const float* b_out;
+} pi_velocity_net;
+
+/* Workspace bytes for pi_velocity_eval / pi_flow_sample with B samples of H actions. */
+size_t pi_flow_workspace_bytes(const pi_velocity_net* net, int B, int H);
+
+/*
+ * One evaluation of the stand-in velocity net at time t (the suffix forward of
+ * one denoising step, [P1] §1.6).  x fp32 [B,H,A]; state fp32 [B,A];
+ * suffix_ar uint8 [H+1] (device; state token first); vel fp32 [B,H,A].
+ * Uses cache layers [0, cache->layers).  Width W must be a multiple of 64,
+ * A <= 64 and a multiple of 8, H + 1 <= 128.
+ */
+pi_status pi_velocity_eval(const pi_velocity_net* net, const pi_kv_cache* cache,
+                           const uint8_t* suffix_ar, const float* state, const float* x, float t,
+                           float* vel, int B, int H, int A, void* workspace,
+                           size_t workspace_bytes, pi_stream stream);
+
+/*
+ * Euler flow-matching sampler ([P1] §1.2, §1.6): x holds the noise on entry and
+ * the sampled actions on exit; dt = -1/num_steps; step k evaluates the velocity
+ * at t_k = 1 + k*dt and sets x <- x + dt*v.
+ *   net != NULL: v = the stand-in velocity net (pi_velocity_eval); the output
+ *                projection and the Euler update are fused.
+ *   net == NULL: v = v_const fp32 [B,H,A] (closed-form check: x_N = noise - v).
+ * x fp32 [B,H,A] in place.  num_steps >= 1.
+ */
+pi_status pi_flow_sample(const pi_velocity_net* net, const pi_kv_cache* cache,
+                         const uint8_t* suffix_ar, const float* state, const float* v_const,
+                         float* x, int B, int H, int A, int num_steps, void* workspace,
+                         size_t workspace_bytes, pi_stream stream);
+
+/* Text of a status code, and the last failure's description on this thread. */
+const char* pi_status_string(pi_status status);
+const char* pi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PI_JOINT_H */

@@ -1,0 +1,315 @@
+"""Thin ctypes binding of libpi_joint.so (include/pi_joint.h).
+
+Argument marshalling only: every step runs in the HIP library.  Tensors are torch
+tensors on a ROCm device; their dtype and contiguity are checked here because
+the C ABI cannot see them, and shapes are passed through for the library to
+validate.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpi_joint.so")
+
+PI_SEG_PREFIX, PI_SEG_FAST, PI_SEG_EXPERT = 0, 1, 2
+PI_TILE_EMPTY, PI_TILE_PARTIAL, PI_TILE_FULL = 0, 1, 2
+PI_MASK_TILE_Q, PI_MASK_TILE_K = 16, 32
+
+_c_p = ctypes.c_void_p
+_c_i = ctypes.c_int
+_c_f = ctypes.c_float
+
+
+class PiMask(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("n_qt", ctypes.c_int32), ("n_kt", ctypes.c_int32),
+                ("forbid_bits", ctypes.c_uint32), ("bid", _c_p), ("pos", _c_p), ("tok", _c_p), ("tiles", _c_p)]
+
+
+class PiKvCache(ctypes.Structure):
+    _fields_ = [("k", _c_p), ("v", _c_p), ("prefix_mask", _c_p), ("layers", ctypes.c_int32),
+                ("B", ctypes.c_int32), ("capacity", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("len", ctypes.c_int32)]
+
+
+class PiVelocityNet(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("action_dim", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("w_state", _c_p), ("b_state", _c_p), ("w_in", _c_p), ("b_in", _c_p), ("w_time", _c_p),
+                ("w_q", _c_p), ("w_k", _c_p), ("w_v", _c_p), ("w_o", _c_p), ("w_out", _c_p), ("b_out", _c_p)]
+
+
+_SIGS = {
+    "pi_mask_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i]),
+    "pi_mask_build": (_c_i, [_c_p, _c_p, _c_p, ctypes.c_uint32, _c_i, _c_i, _c_p, ctypes.c_size_t,
+                             ctypes.POINTER(PiMask), _c_p]),
+    "pi_mask_materialize": (_c_i, [ctypes.POINTER(PiMask), _c_p, _c_p]),
+    "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask),
+                                     _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p]),
+    "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
+                                     _c_f, _c_p, _c_p]),
+    "pi_euler_update": (_c_i, [_c_p, _c_p, _c_f, ctypes.c_int64, _c_p]),
+    "pi_flow_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiVelocityNet), _c_i, _c_i]),
+    "pi_velocity_eval": (_c_i, [ctypes.POINTER(PiVelocityNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_p, _c_f,
+                                _c_p, _c_i, _c_i, _c_i, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_flow_sample": (_c_i, [ctypes.POINTER(PiVelocityNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_p, _c_p,
+                              _c_i, _c_i, _c_i, _c_i, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_status_string": (ctypes.c_char_p, [_c_i]),
+    "pi_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpi_joint.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m prefix_lm_joint_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class PiError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        L = lib()
+        super().__init__(f"{fn}: {L.pi_status_string(status).decode()} ({status}): {L.pi_last_error().decode()}")
+        self.status = status
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PiError(fn, status)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------------------
+# Mask
+# ---------------------------------------------------------------------------
+
+class Mask:
+    """Compact mask: the ctypes struct plus the device workspace it points into."""
+
+    def __init__(self, struct: PiMask, workspace: torch.Tensor):
+        self.struct = struct
+        self.workspace = workspace
+
+    @property
+    def B(self):
+        return self.struct.B
+
+    @property
+    def N(self):
+        return self.struct.N
+
+    def _view(self, addr, count, dtype):
+        base = self.workspace.data_ptr()
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        off = addr - base
+        return self.workspace[off:off + count * itemsize].view(dtype)
+
+    def bid(self):
+        return self._view(self.struct.bid, self.N, torch.int32)
+
+    def pos(self):
+        return self._view(self.struct.pos, self.B * self.N, torch.int32).view(self.B, self.N)
+
+    def tok(self):
+        return self._view(self.struct.tok, self.B * self.N, torch.int32).view(self.B, self.N)
+
+    def tiles(self):
+        s = self.struct
+        return self._view(s.tiles, s.B * s.n_qt * s.n_kt, torch.uint8).view(s.B, s.n_qt, s.n_kt)
+
+
+def pi_mask_workspace_bytes(B: int, N: int) -> int:
+    return int(lib().pi_mask_workspace_bytes(B, N))
+
+
+def pi_mask_build(input_mask: torch.Tensor, ar: torch.Tensor, seg: Optional[torch.Tensor] = None,
+                  forbid_bits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> Mask:
+    B, N = input_mask.shape
+    nbytes = pi_mask_workspace_bytes(B, N)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=input_mask.device)
+    out = PiMask()
+    _check("pi_mask_build", lib().pi_mask_build(
+        _ptr(input_mask, torch.uint8, "input_mask"), _ptr(ar, torch.uint8, "ar"), _ptr(seg, torch.uint8, "seg"),
+        forbid_bits, B, N, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), ctypes.byref(out),
+        _stream(stream)))
+    return Mask(out, workspace)
+
+
+def pi_mask_materialize(mask: Mask, dense: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if dense is None:
+        dense = torch.empty((mask.B, mask.N, mask.N), dtype=torch.uint8, device=mask.workspace.device)
+    _check("pi_mask_materialize", lib().pi_mask_materialize(ctypes.byref(mask.struct),
+                                                            _ptr(dense, torch.uint8, "dense"), _stream(stream)))
+    return dense
+
+
+# ---------------------------------------------------------------------------
+# KV cache, attention
+# ---------------------------------------------------------------------------
+
+class KVCache:
+    """Caller-owned per-layer prefix KV cache: k, v bf16 [layers, B, capacity, Hkv, d]."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, prefix_mask: torch.Tensor, length: Optional[int] = None):
+        layers, B, cap, Hkv, d = k.shape
+        assert v.shape == k.shape and prefix_mask.shape == (B, cap)
+        self.k, self.v, self.prefix_mask = k, v, prefix_mask
+        self.struct = PiKvCache(_ptr(k, torch.bfloat16, "cache.k"), _ptr(v, torch.bfloat16, "cache.v"),
+                                _ptr(prefix_mask, torch.uint8, "prefix_mask"), layers, B, cap, Hkv, d,
+                                cap if length is None else length)
+
+    @classmethod
+    def empty(cls, layers, B, capacity, Hkv, d, device, length=None):
+        k = torch.empty((layers, B, capacity, Hkv, d), dtype=torch.bfloat16, device=device)
+        v = torch.empty_like(k)
+        pm = torch.ones((B, capacity), dtype=torch.uint8, device=device)
+        return cls(k, v, pm, length)
+
+    def layer_k(self, layer):
+        return self.k[layer]
+
+    def layer_v(self, layer):
+        return self.v[layer]
+
+
+def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, o: Optional[torch.Tensor] = None,
+                          scale: Optional[float] = None, cache: Optional[KVCache] = None, layer: int = 0,
+                          stream=None) -> torch.Tensor:
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = d ** -0.5
+    if o is None:
+        o = torch.empty_like(q)
+    _check("pi_joint_attn_prefill", lib().pi_joint_attn_prefill(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), B, L, Hq, Hkv, d,
+        scale, ctypes.byref(mask.struct), _ptr(o, torch.bfloat16, "o"),
+        ctypes.byref(cache.struct) if cache is not None else None, layer, _stream(stream)))
+    return o
+
+
+def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: torch.Tensor, v_s: torch.Tensor,
+                          suffix_ar: torch.Tensor, o_s: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                          stream=None) -> torch.Tensor:
+    B, S, Hq, d = q_s.shape
+    if scale is None:
+        scale = d ** -0.5
+    if o_s is None:
+        o_s = torch.empty_like(q_s)
+    _check("pi_suffix_decode_step", lib().pi_suffix_decode_step(
+        ctypes.byref(cache.struct), layer, _ptr(q_s, torch.bfloat16, "q_s"), _ptr(k_s, torch.bfloat16, "k_s"),
+        _ptr(v_s, torch.bfloat16, "v_s"), _ptr(suffix_ar, torch.uint8, "suffix_ar"), B, S, Hq, scale,
+        _ptr(o_s, torch.bfloat16, "o_s"), _stream(stream)))
+    return o_s
+
+
+def pi_euler_update(x: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> torch.Tensor:
+    assert x.numel() == v.numel()
+    _check("pi_euler_update", lib().pi_euler_update(_ptr(x, torch.float32, "x"), _ptr(v, torch.float32, "v"), dt,
+                                                    x.numel(), _stream(stream)))
+    return x
+
+
+# ---------------------------------------------------------------------------
+# Velocity net and flow sampler
+# ---------------------------------------------------------------------------
+
+class VelocityNet:
+    """Device weights of the stand-in velocity net (see pi_joint.h)."""
+
+    FIELDS = ("w_state", "b_state", "w_in", "b_in", "w_time", "w_q", "w_k", "w_v", "w_o", "w_out", "b_out")
+
+    def __init__(self, tensors: dict, Hq=8, Hkv=1, d=256):
+        self.t = tensors
+        W, A = tensors["w_in"].shape
+        ptrs = []
+        for f in self.FIELDS:
+            want = torch.bfloat16 if f.startswith("w_") and f != "w_time" else torch.float32
+            ptrs.append(_ptr(tensors[f], want, f))
+        self.struct = PiVelocityNet(W, A, Hq, Hkv, d, *ptrs)
+        self.width, self.action_dim = W, A
+
+    @classmethod
+    def from_numpy(cls, weights, device, Hq=8, Hkv=1, d=256):
+        """``weights``: an inputs.NetWeights (bf16 bits as uint16, vectors float32)."""
+        import numpy as np
+        t = {}
+        for f in cls.FIELDS:
+            a = getattr(weights, f)
+            if a.dtype == np.uint16:
+                t[f] = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(device)
+            else:
+                t[f] = torch.from_numpy(a.astype(np.float32)).to(device)
+        return cls(t, Hq, Hkv, d)
+
+
+def pi_flow_workspace_bytes(net: VelocityNet, B: int, H: int) -> int:
+    return int(lib().pi_flow_workspace_bytes(ctypes.byref(net.struct), B, H))
+
+
+def flow_workspace(net: VelocityNet, B: int, H: int, device) -> torch.Tensor:
+    return torch.empty(pi_flow_workspace_bytes(net, B, H), dtype=torch.uint8, device=device)
+
+
+def pi_velocity_eval(net: VelocityNet, cache: KVCache, suffix_ar: torch.Tensor, state: torch.Tensor, x: torch.Tensor,
+                     t: float, vel: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    B, H, A = x.shape
+    if vel is None:
+        vel = torch.empty_like(x)
+    if workspace is None:
+        workspace = flow_workspace(net, B, H, x.device)
+    _check("pi_velocity_eval", lib().pi_velocity_eval(
+        ctypes.byref(net.struct), ctypes.byref(cache.struct), _ptr(suffix_ar, torch.uint8, "suffix_ar"),
+        _ptr(state, torch.float32, "state"), _ptr(x, torch.float32, "x"), t, _ptr(vel, torch.float32, "vel"), B, H,
+        A, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return vel
+
+
+def pi_flow_sample(net: Optional[VelocityNet], cache: Optional[KVCache], suffix_ar: Optional[torch.Tensor],
+                   state: Optional[torch.Tensor], v_const: Optional[torch.Tensor], x: torch.Tensor,
+                   num_steps: int = 10, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B, H, A = x.shape
+    if net is not None and workspace is None:
+        workspace = flow_workspace(net, B, H, x.device)
+    _check("pi_flow_sample", lib().pi_flow_sample(
+        ctypes.byref(net.struct) if net is not None else None,
+        ctypes.byref(cache.struct) if cache is not None else None,
+        _ptr(suffix_ar, torch.uint8, "suffix_ar"), _ptr(state, torch.float32, "state"),
+        _ptr(v_const, torch.float32, "v_const"), _ptr(x, torch.float32, "x"), B, H, A, num_steps,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
+        _stream(stream)))
+    return x

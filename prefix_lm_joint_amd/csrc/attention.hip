@@ -1,0 +1,476 @@
+// Masked grouped-query attention over one shared KV pool, gfx950.
+//
+// What is computed ("π0.5 vs MM-DiT joint attention", first section; "VLA 代码精读"
+// §1.5, §1.6): per (sample, query token, head) one softmax over every visible key
+// of the concatenated prefix+suffix pool, query head h reading KV head
+// floor(h*Hkv/Hq).  Masked keys are excluded by selection (score -inf before the
+// running max, weight exactly 0, never multiplied into V).
+//
+// Kernel organisation (one engine for prefill and cached decode):
+//   * A workgroup owns NW waves x NR row tiles x 16 query rows.  With one KV head
+//     and 8 query heads a row is a (token, head) pair: a 16-row tile holds two
+//     tokens x 8 heads, so every K/V element loaded is used by 8 heads.
+//   * K/V tiles of 32 keys are staged in LDS: K row-major (padded rows), V
+//     transposed to [d][key] so that both matrix-core operands are 16-byte reads.
+//   * Products are computed transposed: S^T = K Q^T (A = K from LDS, B = Q held in
+//     registers), then O^T += V^T P^T with P^T taken straight from the S^T
+//     accumulators (no LDS round trip).  The 32 keys of a tile are permuted inside
+//     V^T to match the accumulator layout of S^T.
+//   * Online softmax in base 2 with per-row max/sum reduced across the four
+//     16-lane groups of the wave.
+//   * Key tiles classified EMPTY by the mask builder are skipped; FULL tiles skip
+//     the per-pair rule.
+//   * Workgroups of one (sample, KV head) are placed on one XCD so their K/V
+//     reads share that XCD's L2.
+#include "common.h"
+
+#include <math.h>
+
+namespace {
+
+constexpr int TK = 32;  // keys per tile
+
+template <int D, int G, int NR, int NW>
+struct Cfg {
+  static constexpr int ROWS_W = NR * 16;
+  static constexpr int ROWS = NW * ROWS_W;
+  static constexpr int TOK = ROWS / G;        // query tokens per workgroup
+  static constexpr int THREADS = NW * PI_WAVE;
+  static constexpr int KSTR = D + 8;          // LDS row stride of K (bf16 elements)
+  static constexpr int VSTR = TK + 8;         // LDS row stride of V^T (bf16 elements)
+  static constexpr int DS = D / 32;           // k-steps of the QK^T product
+  static constexpr int DT = D / 16;           // 16-wide d tiles of the PV product
+  static_assert(ROWS % G == 0, "rows must cover whole tokens");
+  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+};
+
+template <int D>
+struct Smem {
+  __bf16 k[TK * (D + 8)];
+  __bf16 vt[D * (TK + 8)];
+  uint32_t kw[TK];
+};
+
+// Permuted V^T slot of key j (0..31) so that lane group g's 8 contiguous slots
+// hold keys {4g..4g+3, 16+4g..16+4g+3}, the keys its S^T accumulators cover.
+__device__ __forceinline__ int vslot(int j) { return 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3); }
+
+// Stage K (row-major) and V (transposed, permuted) for the keys of a tile whose
+// bit is set in `keymask`; other keys (past the end, or padding) are zero-filled,
+// so whatever a padded slot holds (uninitialised memory, NaN) never reaches a
+// product.  `tok_stride` is the element distance between consecutive tokens.
+template <int D, int THREADS>
+__device__ __forceinline__ void stage_kv(Smem<D>& sm, const __bf16* __restrict__ kb,
+                                         const __bf16* __restrict__ vb, int64_t tok_stride, uint32_t keymask) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int task = threadIdx.x; task < TK * CH; task += THREADS) {
+    const int j = task / CH, c = task % CH;
+    u32x4 val = zero;
+    if ((keymask >> j) & 1u) val = *reinterpret_cast<const u32x4*>(kb + j * tok_stride + 8 * c);
+    *reinterpret_cast<u32x4*>(&sm.k[j * (D + 8) + 8 * c]) = val;
+  }
+  for (int task = threadIdx.x; task < (TK / 2) * CH; task += THREADS) {
+    const int p = task / CH, c = task % CH;
+    const int j0 = 2 * p, j1 = 2 * p + 1;
+    u32x4 a = zero, b = zero;
+    if ((keymask >> j0) & 1u) a = *reinterpret_cast<const u32x4*>(vb + j0 * tok_stride + 8 * c);
+    if ((keymask >> j1) & 1u) b = *reinterpret_cast<const u32x4*>(vb + j1 * tok_stride + 8 * c);
+    const int s = vslot(j0);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.vt[0]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      dst[((8 * c + e) * (TK + 8) + s) >> 1] = lo | (hi << 16);
+    }
+  }
+}
+
+// Per-wave state of the online softmax.
+template <int D, int NR>
+struct WaveState {
+  bf16x8 qf[NR][D / 32];
+  f32x4 o[NR][D / 16];
+  float m[NR];
+  float l[NR];
+  uint32_t wq[NR];
+};
+
+// One 32-key tile for one wave.  cls: PI_TILE_FULL or PI_TILE_PARTIAL.
+template <int D, int NR>
+__device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>& st, int cls,
+                                            uint32_t forbid, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  f32x4 s[NR][2];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 16 + c) * (D + 8) + ds * 32 + 8 * g]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) s[r][kt] = mfma16x16x32(a, st.qf[r][ds], s[r][kt]);
+    }
+  }
+  const float NEG_INF = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float x[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = s[r][kt][i] * scale_log2;
+        if (cls == PI_TILE_PARTIAL) {
+          const uint32_t wk = sm.kw[kt * 16 + 4 * g + i];
+          if (!pair_visible(st.wq[r], wk, forbid)) v = NEG_INF;
+        }
+        x[kt][i] = v;
+      }
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
+    mx = group4_max(mx);
+    const float m_new = fmaxf(st.m[r], mx);
+    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
+    const float corr = exp2f(st.m[r] - m_use);
+    st.m[r] = m_new;
+    bf16x8 pf;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 pb = f2bf(exp2f(x[kt][i] - m_use));
+        pf[4 * kt + i] = pb;
+        lsum += bf2f(pb);
+      }
+    st.l[r] = st.l[r] * corr + lsum;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] *= corr;
+    // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[(dt * 16 + c) * (TK + 8) + 8 * g]);
+      st.o[r][dt] = mfma16x16x32(a, pf, st.o[r][dt]);
+    }
+  }
+}
+
+// Workgroup placement: workgroups are dispatched round-robin over the 8 XCDs;
+// give every (sample, KV head) group's `per_group` workgroups one XCD.
+__device__ __forceinline__ void xcd_place(int n_groups, int per_group, int& group, int& sub) {
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int k = id >> 3;
+  const int slot = k / per_group;
+  sub = k % per_group;
+  group = slot * 8 + xcd;
+  (void)n_groups;
+}
+
+template <int D, int NR>
+__device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    st.m[r] = -INFINITY;
+    st.l[r] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// Normalise and store O rows.  row_ptr(r) gives the output row base or nullptr.
+template <int D, int NR>
+__device__ __forceinline__ void store_rows(WaveState<D, NR>& st, __bf16* const* row_base) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float l = group4_sum(st.l[r]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    __bf16* dst = row_base[r];
+    if (dst == nullptr) continue;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f2bf(st.o[r][dt][i] * inv);
+      *reinterpret_cast<bf16x4*>(dst + dt * 16 + 4 * g) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: grid = ceil(B*Hkv / 8) * 8 groups x n_qblk workgroups (XCD-placed).
+// ---------------------------------------------------------------------------
+template <int D, int G, int NR, int NW>
+__global__ void __launch_bounds__(NW * 64)
+prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+               __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
+               const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
+               uint32_t forbid, int n_qblk) {
+  using C = Cfg<D, G, NR, NW>;
+  __shared__ Smem<D> sm;
+  int group, qblk;
+  xcd_place(B * Hkv, n_qblk, group, qblk);
+  if (group >= B * Hkv) return;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int tok0 = qblk * C::TOK;
+  const uint32_t* tk = tok + (size_t)b * L;
+
+  WaveState<D, NR> st;
+  init_state(st);
+  __bf16* row_base[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int row = wave * C::ROWS_W + r * 16 + c;
+    const int t = tok0 + row / G;
+    const int h = kvh * G + row % G;
+    const bool ok = t < L;
+    st.wq[r] = ok ? tk[t] : 0u;
+    const __bf16* qrow = q + (((size_t)b * L + (ok ? t : 0)) * Hq + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
+      if (!ok) val = bf16x8{};
+      st.qf[r][ds] = val;
+    }
+    row_base[r] = ok ? o + (((size_t)b * L + t) * Hq + h) * D : nullptr;
+  }
+
+  const int64_t tstride = (int64_t)Hkv * D;
+  const __bf16* kb = k + ((size_t)b * L * Hkv + kvh) * D;
+  const __bf16* vb = v + ((size_t)b * L * Hkv + kvh) * D;
+  const int qt_lo = tok0 / PI_MASK_TILE_Q;
+  const int qt_hi = min(n_qt, (tok0 + C::TOK + PI_MASK_TILE_Q - 1) / PI_MASK_TILE_Q);
+  const uint8_t* trow = tiles + (size_t)b * n_qt * n_kt;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    int cls = -1;
+    for (int qt = qt_lo; qt < qt_hi; ++qt) {
+      const int cl = trow[(size_t)qt * n_kt + kt];
+      cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
+    }
+    if (cls <= PI_TILE_EMPTY) continue;
+    const int key0 = kt * TK;
+    const int nvalid = min(TK, L - key0);
+    const uint32_t wk = lane < nvalid ? tk[key0 + lane] : 0u;
+    const uint32_t keymask = (uint32_t)__ballot(wk & 1u);
+    __syncthreads();
+    stage_kv<D, C::THREADS>(sm, kb + key0 * tstride, vb + key0 * tstride, tstride, keymask);
+    if (threadIdx.x < TK) sm.kw[threadIdx.x] = wk;
+    __syncthreads();
+    attend_tile<D, NR>(sm, st, cls, forbid, scale_log2);
+  }
+  store_rows<D, NR>(st, row_base);
+}
+
+// ---------------------------------------------------------------------------
+// Cached suffix decode (Hq = 8, Hkv = 1, d = 256): grid = ceil(B/8)*8 x n_qblk.
+// Keys: valid prefix slots of the cache layer, then the suffix's own K/V.
+// Query/key words reuse the prefill rule with bid 0 for every prefix slot and
+// 1 + cumsum(suffix_ar) for suffix tokens.
+// ---------------------------------------------------------------------------
+template <int D, int G, int NR, int NW>
+__global__ void __launch_bounds__(NW * 64)
+decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
+              const uint8_t* __restrict__ prefix_mask, int cap, int P,
+              const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
+              const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
+              __bf16* __restrict__ os, int n_qblk) {
+  using C = Cfg<D, G, NR, NW>;
+  constexpr int Hq = G;
+  __shared__ Smem<D> sm;
+  __shared__ uint32_t sbid[128];
+  int b, qblk;
+  xcd_place(B, n_qblk, b, qblk);
+  if (b >= B) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int tok0 = qblk * C::TOK;
+
+  // suffix block ids: inclusive cumsum of suffix_ar (S <= 128), computed by wave 0
+  if (wave == 0) {
+    int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
+    int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int u0 = __shfl_up(a0, off), u1 = __shfl_up(a1, off);
+      if (lane >= off) { a0 += u0; a1 += u1; }
+    }
+    const int tot0 = __shfl(a0, 63);
+    sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
+    sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
+  }
+  __syncthreads();
+
+  WaveState<D, NR> st;
+  init_state(st);
+  __bf16* row_base[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int row = wave * C::ROWS_W + r * 16 + c;
+    const int t = tok0 + row / G;
+    const int h = row % G;
+    const bool ok = t < S;
+    st.wq[r] = ok ? sbid[t] : 0u;
+    const __bf16* qrow = qs + (((size_t)b * S + (ok ? t : 0)) * Hq + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
+      if (!ok) val = bf16x8{};
+      st.qf[r][ds] = val;
+    }
+    row_base[r] = ok ? os + (((size_t)b * S + t) * Hq + h) * D : nullptr;
+  }
+
+  // prefix slots from the cache
+  const __bf16* kb = ck + (size_t)b * cap * D;
+  const __bf16* vb = cv + (size_t)b * cap * D;
+  const uint8_t* pm = prefix_mask + (size_t)b * cap;
+  const int n_pt = (P + TK - 1) / TK;
+  for (int kt = 0; kt < n_pt; ++kt) {
+    const int key0 = kt * TK;
+    const int nvalid = min(TK, P - key0);
+    const bool mine = lane < nvalid && pm[key0 + lane] != 0;
+    const unsigned long long bal = __ballot(mine);
+    if (bal == 0ull) continue;
+    const int cls = (nvalid == TK && bal == 0xFFFFFFFFull) ? PI_TILE_FULL : PI_TILE_PARTIAL;
+    __syncthreads();
+    stage_kv<D, C::THREADS>(sm, kb + (size_t)key0 * D, vb + (size_t)key0 * D, D, (uint32_t)bal);
+    if (threadIdx.x < TK) sm.kw[threadIdx.x] = mine ? 1u : 0u;
+    __syncthreads();
+    attend_tile<D, NR>(sm, st, cls, 0u, scale_log2);
+  }
+  // the suffix's own keys
+  const __bf16* ksb = ks + (size_t)b * S * D;
+  const __bf16* vsb = vs + (size_t)b * S * D;
+  const int n_st = (S + TK - 1) / TK;
+  for (int kt = 0; kt < n_st; ++kt) {
+    const int key0 = kt * TK;
+    const int nvalid = min(TK, S - key0);
+    const uint32_t keymask = nvalid == TK ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
+    __syncthreads();
+    stage_kv<D, C::THREADS>(sm, ksb + (size_t)key0 * D, vsb + (size_t)key0 * D, D, keymask);
+    if (threadIdx.x < TK) sm.kw[threadIdx.x] = (int)threadIdx.x < nvalid ? sbid[key0 + threadIdx.x] : 0u;
+    __syncthreads();
+    attend_tile<D, NR>(sm, st, PI_TILE_PARTIAL, 0u, scale_log2);
+  }
+  store_rows<D, NR>(st, row_base);
+}
+
+// K/V rows of tokens [0, P) into cache layer slices; one thread per 16 bytes.
+__global__ void cache_write_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                   u32x4* __restrict__ ck, u32x4* __restrict__ cv, int L, int cap, int P,
+                                   int row_chunks, int64_t total) {
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= total) return;
+  const int64_t ch = id % row_chunks;
+  const int64_t t = (id / row_chunks) % P;
+  const int64_t b = id / ((int64_t)row_chunks * P);
+  const int64_t src = (b * L + t) * row_chunks + ch;
+  const int64_t dst = (b * cap + t) * row_chunks + ch;
+  ck[dst] = k[src];
+  cv[dst] = v[src];
+}
+
+constexpr int kNW = 4;
+
+template <int D, int G, int NR>
+pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
+                         float scale, const pi_mask* m, hipStream_t s) {
+  using C = Cfg<D, G, NR, kNW>;
+  const int n_qblk = (L + C::TOK - 1) / C::TOK;
+  const int groups = (B * Hkv + 7) / 8 * 8;
+  const int64_t grid = (int64_t)groups * n_qblk;
+  PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "prefill: grid too large");
+  const float scale_log2 = scale * 1.4426950408889634f;
+  prefill_kernel<D, G, NR, kNW><<<(unsigned)grid, C::THREADS, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<__bf16*>(o), B, L, Hq, Hkv, scale_log2, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits,
+      n_qblk);
+  return pi::check_launch("prefill_kernel");
+}
+
+}  // namespace
+
+extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
+                                           int Hkv, int d, float scale, const pi_mask* mask, void* o,
+                                           const pi_kv_cache* cache, int layer, pi_stream stream) {
+  PI_REQUIRE(q && k && v && o && mask, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: null pointer");
+  PI_REQUIRE(pi::aligned16(q) && pi::aligned16(k) && pi::aligned16(v) && pi::aligned16(o), PI_ERR_INVALID_ARG,
+             "pi_joint_attn_prefill: tensors must be 16-byte aligned");
+  PI_REQUIRE(B >= 1 && L >= 1, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: B=%d L=%d", B, L);
+  PI_REQUIRE(mask->B == B && mask->N == L && mask->tok && mask->tiles, PI_ERR_INVALID_ARG,
+             "pi_joint_attn_prefill: mask built for B=%d N=%d, call has B=%d L=%d", mask->B, mask->N, B, L);
+  PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: scale must be > 0");
+  PI_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, PI_ERR_INVALID_ARG,
+             "pi_joint_attn_prefill: Hq=%d must be a multiple of Hkv=%d", Hq, Hkv);
+  const bool gqa8 = (Hq == 8 && Hkv == 1 && d == 256);
+  const bool mha64 = (Hq == Hkv && d == 64);
+  PI_REQUIRE(gqa8 || mha64, PI_ERR_UNSUPPORTED,
+             "pi_joint_attn_prefill: unsupported (Hq=%d, Hkv=%d, d=%d); supported: (8,1,256) and (H,H,64)", Hq,
+             Hkv, d);
+  if (cache) {
+    PI_REQUIRE(cache->k && cache->v, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: cache has null k/v");
+    PI_REQUIRE(cache->B == B && cache->Hkv == Hkv && cache->d == d && layer >= 0 && layer < cache->layers &&
+                   cache->len >= 1 && cache->len <= L && cache->len <= cache->capacity,
+               PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: cache shape does not match (layer %d)", layer);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pi_status st = gqa8 ? launch_prefill<256, 8, 2>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s)
+                      : launch_prefill<64, 1, 4>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s);
+  if (st != PI_OK || !cache) return st;
+  const int row_chunks = Hkv * d / 8;
+  const int64_t total = (int64_t)B * cache->len * row_chunks;
+  const size_t layer_elems = (size_t)B * cache->capacity * Hkv * d;
+  __bf16* ckl = static_cast<__bf16*>(cache->k) + (size_t)layer * layer_elems;
+  __bf16* cvl = static_cast<__bf16*>(cache->v) + (size_t)layer * layer_elems;
+  const int threads = 256;
+  cache_write_kernel<<<(unsigned)((total + threads - 1) / threads), threads, 0, s>>>(
+      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(ckl),
+      reinterpret_cast<u32x4*>(cvl), L, cache->capacity, cache->len, row_chunks, total);
+  return pi::check_launch("cache_write_kernel");
+}
+
+extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,
+                                           const void* v_s, const uint8_t* suffix_ar, int B, int S, int Hq,
+                                           float scale, void* o_s, pi_stream stream) {
+  PI_REQUIRE(cache && q_s && k_s && v_s && suffix_ar && o_s, PI_ERR_INVALID_ARG,
+             "pi_suffix_decode_step: null pointer");
+  PI_REQUIRE(cache->k && cache->v && cache->prefix_mask, PI_ERR_INVALID_ARG,
+             "pi_suffix_decode_step: cache has null pointers");
+  PI_REQUIRE(pi::aligned16(q_s) && pi::aligned16(k_s) && pi::aligned16(v_s) && pi::aligned16(o_s) &&
+                 pi::aligned16(cache->k) && pi::aligned16(cache->v),
+             PI_ERR_INVALID_ARG, "pi_suffix_decode_step: tensors must be 16-byte aligned");
+  PI_REQUIRE(B >= 1 && S >= 1 && S <= 128, PI_ERR_INVALID_ARG, "pi_suffix_decode_step: B=%d S=%d (S <= 128)", B, S);
+  PI_REQUIRE(cache->B == B && layer >= 0 && layer < cache->layers && cache->len >= 0 &&
+                 cache->len <= cache->capacity,
+             PI_ERR_INVALID_ARG, "pi_suffix_decode_step: cache/layer mismatch (layer %d of %d, B %d vs %d)", layer,
+             cache->layers, cache->B, B);
+  PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_suffix_decode_step: scale must be > 0");
+  PI_REQUIRE(Hq == 8 && cache->Hkv == 1 && cache->d == 256, PI_ERR_UNSUPPORTED,
+             "pi_suffix_decode_step: supported heads are Hq=8, Hkv=1, d=256 (got %d, %d, %d)", Hq, cache->Hkv,
+             cache->d);
+  using C = Cfg<256, 8, 2, kNW>;
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  const int groups = (B + 7) / 8 * 8;
+  const size_t layer_elems = (size_t)B * cache->capacity * 256;
+  const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
+  const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
+  decode_kernel<256, 8, 2, kNW><<<(unsigned)(groups * n_qblk), C::THREADS, 0, static_cast<hipStream_t>(stream)>>>(
+      ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
+      static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), n_qblk);
+  return pi::check_launch("decode_kernel");
+}

@@ -1,0 +1,75 @@
+// Device and host helpers shared by the gfx950 kernels of the joint-attention path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pi_joint.h"
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+#define PI_WAVE 64
+
+// ---------------------------------------------------------------------------
+// Matrix-core tile 16x16x32, bf16 operands, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
+// Lane l (g = l / 16, c = l % 16):
+//   A operand (16 rows x 32 k):   A[c][8g .. 8g+7]
+//   B operand (32 k x 16 cols):   B[8g .. 8g+7][c]
+//   C/D       (16 x 16):          C[4g + i][c], i = 0..3
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __bf16 f2bf(float f) { return static_cast<__bf16>(f); }
+__device__ __forceinline__ float bf2f(__bf16 h) { return static_cast<float>(h); }
+
+__device__ __forceinline__ bf16x8 cvt8(const float* f) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = f2bf(f[i]);
+  return r;
+}
+
+// Butterfly reductions across the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Packed per-token mask word: bit0 valid, bits1-2 segment, bits3.. block id.
+__device__ __forceinline__ bool pair_visible(uint32_t wq, uint32_t wk, uint32_t forbid) {
+  bool both_valid = (wq & wk & 1u) != 0u;
+  bool block_ok = (wk >> 3) <= (wq >> 3);
+  uint32_t bit = 4u * ((wq >> 1) & 3u) + ((wk >> 1) & 3u);
+  bool banned = (forbid >> bit) & 1u;
+  return both_valid && block_ok && !banned;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace pi {
+void set_error(const char* fmt, ...);
+pi_status check_launch(const char* what);
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+}  // namespace pi
+
+#define PI_REQUIRE(cond, code, ...)     \
+  do {                                   \
+    if (!(cond)) {                       \
+      ::pi::set_error(__VA_ARGS__);      \
+      return (code);                     \
+    }                                    \
+  } while (0)

@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every function include/pi_joint.h declares,
+and rejects bad arguments on the host before anything is launched (no GPU is
+touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from prefix_lm_joint_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pi_joint.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(Bd.LIB_PATH), reason="libpi_joint.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pi_[a-z_0-9]+)\s*\(", text)) - {"PI_FORBID"})
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pi_mask_build", "pi_joint_attn_prefill", "pi_suffix_decode_step", "pi_euler_update",
+                     "pi_flow_sample"):
+        assert required in names
+
+
+@needs_lib
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(Bd.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding declares a signature for every exported entry point
+    assert set(declared_functions()) <= set(Bd._SIGS), set(declared_functions()) - set(Bd._SIGS)
+
+
+@needs_lib
+def test_status_strings():
+    lib = Bd.lib()
+    assert lib.pi_status_string(0) == b"ok"
+    assert lib.pi_status_string(-3) == b"workspace too small"
+
+
+@needs_lib
+def test_workspace_queries_are_host_only():
+    lib = Bd.lib()
+    assert lib.pi_mask_workspace_bytes(2, 100) > 0
+    assert lib.pi_mask_workspace_bytes(0, 100) == 0
+    assert lib.pi_mask_workspace_bytes(1, (1 << 20) + 1) == 0
+    net = Bd.PiVelocityNet(1024, 32, 8, 1, 256)
+    n1 = lib.pi_flow_workspace_bytes(ctypes.byref(net), 1, 50)
+    n64 = lib.pi_flow_workspace_bytes(ctypes.byref(net), 64, 50)
+    assert 0 < n1 < n64
+
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+@needs_lib
+def test_prefill_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    m = Bd.PiMask(B=1, N=64, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
+    call = lambda **kw: lib.pi_joint_attn_prefill(
+        kw.get("q", FAKE), FAKE, FAKE, kw.get("B", 1), kw.get("L", 64), kw.get("Hq", 8), kw.get("Hkv", 1),
+        kw.get("d", 256), kw.get("scale", 0.0625), ctypes.byref(m), FAKE, None, 0, None)
+    assert call(d=128) == -2                 # unsupported head dim
+    assert call(Hq=6, Hkv=4) == -1           # Hq not a multiple of Hkv
+    assert call(L=65) == -1                  # mask built for another length
+    assert call(scale=0.0) == -1
+    assert call(q=P(0x10008)) == -1          # misaligned
+    assert call(q=None) == -1
+    assert b"pi_joint_attn_prefill" in lib.pi_last_error()
+
+
+@needs_lib
+def test_decode_and_flow_reject_bad_arguments_before_launch():
+    lib = Bd.lib()
+    cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 4, 816, 1, 256, 816)
+    dec = lambda **kw: lib.pi_suffix_decode_step(ctypes.byref(cache), kw.get("layer", 0), FAKE, FAKE, FAKE, FAKE,
+                                                 kw.get("B", 4), kw.get("S", 51), kw.get("Hq", 8), 0.0625, FAKE, None)
+    assert dec(layer=18) == -1
+    assert dec(B=3) == -1
+    assert dec(S=129) == -1
+    assert dec(Hq=4) == -2
+    assert lib.pi_euler_update(FAKE, FAKE, -0.1, -1, None) == -1
+    assert lib.pi_flow_sample(None, None, None, None, None, FAKE, 1, 50, 32, 0, None, 0, None) == -1
+    assert lib.pi_flow_sample(None, None, None, None, None, FAKE, 1, 50, 32, 10, None, 0, None) == -1  # no v_const
+    net = Bd.PiVelocityNet(1024, 32, 8, 1, 256, *([FAKE] * 11))
+    ws_need = lib.pi_flow_workspace_bytes(ctypes.byref(net), 4, 50)
+    r = lib.pi_flow_sample(ctypes.byref(net), ctypes.byref(cache), FAKE, FAKE, None, FAKE, 4, 50, 32, 10,
+                           P(0x100000), ws_need - 1, None)
+    assert r == -3
+    net_bad = Bd.PiVelocityNet(1000, 32, 8, 1, 256, *([FAKE] * 11))
+    assert lib.pi_flow_sample(ctypes.byref(net_bad), ctypes.byref(cache), FAKE, FAKE, None, FAKE, 4, 50, 32, 10,
+                              P(0x100000), 1 << 30, None) == -2
+
+
+@needs_lib
+def test_mask_build_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    out = Bd.PiMask()
+    need = lib.pi_mask_workspace_bytes(2, 100)
+    assert lib.pi_mask_build(FAKE, FAKE, None, 0, 2, 100, P(0x100000), need - 1, ctypes.byref(out), None) == -3
+    assert lib.pi_mask_build(FAKE, FAKE, None, 0, 0, 100, P(0x100000), need, ctypes.byref(out), None) == -1
+    assert lib.pi_mask_build(FAKE, FAKE, None, 1 << 16, 2, 100, P(0x100000), need, ctypes.byref(out), None) == -1
+    assert lib.pi_mask_build(FAKE, FAKE, None, 0, 2, 100, P(0x100010), need, ctypes.byref(out), None) == -1
