@@ -10,10 +10,13 @@
 // and an output projection back to the action dim):
 //   h[:,0]   = r(state) W_state^T + b_state
 //   h[:,1+i] = r(x_i) W_in^T + b_in + t * w_time
-//   per cache layer l: a = r(h); q,k,v = r(a W_{q,k,v}^T); o = r(decode_l); h += o W_o^T
-//   v = r(h[:,1:]) W_out^T + b_out
+//   per cache layer l: a = r(h); q,k,v = r(a W_{q,k,v}^T / rms(h)); o = r(decode_l); h += o W_o^T
+//   v = r(h[:,1:]) W_out^T / rms(h[:,1:]) + b_out
 // r() is rounding to bf16; every matrix product runs on the matrix cores with
-// bf16 operands and fp32 accumulation.
+// bf16 operands and fp32 accumulation.  rms(h) = sqrt(mean(h^2) + 1e-6) is the
+// per-stream RMS norm ahead of the projections ("π0.5 vs MM-DiT joint attention",
+// first section); being a per-row scalar it is applied to the accumulator, and the
+// GEMM that reads the fp32 row of h accumulates its sum of squares on the way.
 #include "common.h"
 
 #include <math.h>
@@ -47,8 +50,10 @@ struct GemmArgs {
   float dt;            // EPI_EULER
 };
 
+// 8 consecutive elements of a row as bf16 (zero past K); `ss` accumulates the
+// sum of squares of the unrounded values.
 template <typename T>
-__device__ __forceinline__ bf16x8 load_frag(const T* row, int k, int K, bool vec_ok) {
+__device__ __forceinline__ bf16x8 load_frag(const T* row, int k, int K, bool vec_ok, float& ss) {
   bf16x8 r;
   if (vec_ok && k + 8 <= K) {
     if constexpr (sizeof(T) == 2) {
@@ -60,19 +65,27 @@ __device__ __forceinline__ bf16x8 load_frag(const T* row, int k, int K, bool vec
       for (int i = 0; i < 4; ++i) {
         r[i] = f2bf(a[i]);
         r[i + 4] = f2bf(b[i]);
+        ss += a[i] * a[i] + b[i] * b[i];
       }
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = (k + i < K) ? f2bf((float)row[k + i]) : f2bf(0.f);
+    for (int i = 0; i < 8; ++i) {
+      const float f = (k + i < K) ? (float)row[k + i] : 0.f;
+      r[i] = f2bf(f);
+      ss += f * f;
+    }
   }
   return r;
 }
 
-// out[m][n] = sum_k r(A[m][k]) W[n][k].  Workgroup tile 64 (n) x 64 (m), four waves of
-// 32 x 32; computed transposed (A operand = weights, B operand = activations) so a
-// lane ends with four consecutive output columns of one row.
-template <int EPI, typename TA>
+constexpr float kRmsEps = 1e-6f;
+
+// out[m][n] = sum_k r(A[m][k]) W[n][k]  (divided by rms(A[m]) when NORM).
+// Workgroup tile 64 (n) x 64 (m), four waves of 32 x 32; computed transposed
+// (A operand = weights, B operand = activations) so a lane ends with four
+// consecutive output columns of one row.
+template <int EPI, typename TA, bool NORM>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -107,19 +120,27 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[2] = {0.f, 0.f};
+  float ss_w = 0.f;
 
   for (int k0 = 0; k0 < p.K; k0 += 32) {
     const int k = k0 + 8 * g;
     bf16x8 wf[2], af[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      wf[j] = wok[j] ? load_frag(wrow[j], k, p.K, vec_ok) : bf16x8{};
-      af[j] = aok[j] ? load_frag(arow[j], k, p.K, vec_ok) : bf16x8{};
+      wf[j] = wok[j] ? load_frag(wrow[j], k, p.K, vec_ok, ss_w) : bf16x8{};
+      af[j] = aok[j] ? load_frag(arow[j], k, p.K, vec_ok, ss[j]) : bf16x8{};
     }
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
 #pragma unroll
       for (int jm = 0; jm < 2; ++jm) acc[jn][jm] = mfma16x16x32(wf[jn], af[jm], acc[jn][jm]);
+  }
+  (void)ss_w;
+  float inv_rms[2] = {1.f, 1.f};
+  if constexpr (NORM) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) inv_rms[j] = rsqrtf(group4_sum(ss[j]) / (float)p.K + kRmsEps);
   }
 
 #pragma unroll
@@ -130,7 +151,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
     for (int jn = 0; jn < 2; ++jn) {
       const int nb = n0 + 16 * jn + 4 * g;
       if (nb >= p.N) continue;
-      const f32x4 r = acc[jn][jm];
+      const f32x4 r = acc[jn][jm] * inv_rms[jm];
       if constexpr (EPI == EPI_QKV) {
         __bf16* dst;
         if (nb < p.n1) dst = p.o0 + (int64_t)m * p.n1 + nb;
@@ -190,10 +211,10 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
   }
 }
 
-template <int EPI, typename TA>
+template <int EPI, typename TA, bool NORM>
 pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
   dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-  gemm_kernel<EPI, TA><<<grid, 256, 0, s>>>(a);
+  gemm_kernel<EPI, TA, NORM><<<grid, 256, 0, s>>>(a);
   return pi::check_launch(name);
 }
 
@@ -276,7 +297,7 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
     g.o0 = w.q;
     g.o1 = w.k;
     g.o2 = w.v;
-    pi_status st = gemm<EPI_QKV, float>(g, s, "gemm_qkv");
+    pi_status st = gemm<EPI_QKV, float, true>(g, s, "gemm_qkv");
     if (st != PI_OK) return st;
     st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, s);
     if (st != PI_OK) return st;
@@ -291,7 +312,7 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
     go.K = nq;
     go.out = w.h;
     go.omap = RowMap{M, 0, 0};
-    st = gemm<EPI_RESID, __bf16>(go, s, "gemm_out_resid");
+    st = gemm<EPI_RESID, __bf16, false>(go, s, "gemm_out_resid");
     if (st != PI_OK) return st;
   }
   GemmArgs gv{};
@@ -308,10 +329,10 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
   gv.dt = dt;
   if (EPI == EPI_EULER) {
     gv.out = x;
-    return gemm<EPI_EULER, float>(gv, s, "gemm_velocity_euler");
+    return gemm<EPI_EULER, float, true>(gv, s, "gemm_velocity_euler");
   }
   gv.out = vel;
-  return gemm<EPI_VEL, float>(gv, s, "gemm_velocity");
+  return gemm<EPI_VEL, float, true>(gv, s, "gemm_velocity");
 }
 
 }  // namespace

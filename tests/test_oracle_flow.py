@@ -108,3 +108,53 @@ def test_net_padded_cache_slots_do_not_matter():
     cv2[:, 0, -3:] = -1e3
     v2 = F.velocity_net(x, 0.2, st, wf, ck2, cv2, pre, sar, Hq, Hkv, d)
     assert np.array_equal(v1, v2)
+
+
+def _net_fp32(x, t, state, w, ck, cv, pm, sar):
+    """The stand-in net's definition evaluated in float32 with the same bf16
+    rounding points (torch CPU): what any fp32-accumulating implementation gets."""
+    def r(a):
+        return a.to(torch.bfloat16).to(torch.float32)
+    W = {k: torch.from_numpy(v.astype(np.float32)) for k, v in w.items()}
+    x, state = torch.from_numpy(x.astype(np.float32)), torch.from_numpy(state.astype(np.float32))
+    h = torch.cat([(r(state) @ W["w_state"].T + W["b_state"])[:, None],
+                   r(x) @ W["w_in"].T + W["b_in"] + np.float32(t) * W["w_time"]], 1)
+    B, S, _ = h.shape
+    from oracle.mask import decode_mask
+    vis = torch.from_numpy(decode_mask(pm, np.ones((B, S), np.uint8), sar))
+    for layer in range(ck.shape[0]):
+        a = r(h)
+        rr = torch.sqrt((h * h).mean(-1, keepdim=True) + 1e-6)
+        q = r(a @ W["w_q"].T / rr).view(B, S, 8, 256)
+        k, v = r(a @ W["w_k"].T / rr), r(a @ W["w_v"].T / rr)
+        kk = torch.cat([torch.from_numpy(ck[layer][:, :, 0].astype(np.float32)), k], 1)
+        vv = torch.cat([torch.from_numpy(cv[layer][:, :, 0].astype(np.float32)), v], 1)
+        s = torch.einsum("bshd,bkd->bshk", q, kk) / 16.0
+        s = s.masked_fill(~vis[:, :, None, :], float("-inf"))
+        o = r(torch.einsum("bshk,bkd->bshd", torch.softmax(s, -1), vv))
+        h = h + o.reshape(B, S, 2048) @ W["w_o"].T
+    hh = h[:, 1:]
+    return (r(hh) @ W["w_out"].T / torch.sqrt((hh * hh).mean(-1, keepdim=True) + 1e-6) + W["b_out"]).numpy()
+
+
+def test_net_tolerance_is_twice_the_fp32_floor():
+    """Derives the velocity-net bound used by the GPU tests: at the π0 control-step
+    shape an fp32 evaluation of the same definition sits this far from the fp64
+    oracle, only because bf16 rounding points turn accumulation-order differences
+    into whole-ulp flips.  The GPU bound is about twice that floor."""
+    from tests.gpu_util import NET_MAX_ABS, NET_MEAN_ABS
+    B, P, H, A, W, L = 1, 816, 50, 32, 1024, 18
+    nw = I.net_weights(2100, width=W, action_dim=A)
+    wf = {f: (I.bf16_bits_to_f64(getattr(nw, f)) if getattr(nw, f).dtype == np.uint16
+              else getattr(nw, f).astype(np.float64)) for f in nw.__dataclass_fields__}
+    ck = I.bf16_bits_to_f64(I.bf16_normal(2120, (L, B, P, 1, 256)))
+    cv = I.bf16_bits_to_f64(I.bf16_normal(2121, (L, B, P, 1, 256)))
+    pm = np.ones((B, P), np.uint8)
+    sar = I.pi0_structure(P, H).ar[P:]
+    st, x = I.f32_normal(2123, (B, A)), I.f32_normal(2124, (B, H, A))
+    ref = F.velocity_net(x.astype(np.float64), 0.7, st.astype(np.float64), wf, ck, cv, pm, sar, 8, 1, 256)
+    err = np.abs(_net_fp32(x, 0.7, st, wf, ck, cv, pm, sar) - ref)
+    floor_mean, floor_max = float(err.mean()), float(err.max())
+    assert 5e-4 < floor_mean < 2e-3 and floor_max < 1e-2
+    assert 1.5 * floor_mean <= NET_MEAN_ABS <= 3.0 * floor_mean
+    assert 1.5 * floor_max <= NET_MAX_ABS
