@@ -46,56 +46,117 @@ struct Cfg {
 
 template <int D>
 struct Smem {
-  __bf16 k[TK * (D + 8)];
-  __bf16 vt[D * (TK + 8)];
-  uint32_t kw[TK];
+  alignas(16) __bf16 k[TK * (D + 8)];
+  alignas(16) __bf16 vt[D * (TK + 8)];
+  alignas(16) uint32_t kw[TK];
 };
 
 // Permuted V^T slot of key j (0..31) so that lane group g's 8 contiguous slots
 // hold keys {4g..4g+3, 16+4g..16+4g+3}, the keys its S^T accumulators cover.
 __device__ __forceinline__ int vslot(int j) { return 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3); }
 
-// Stage K (row-major) and V (transposed, permuted) for the keys of a tile whose
-// bit is set in `keymask`; other keys (past the end, or padding) are zero-filled,
-// so whatever a padded slot holds (uninitialised memory, NaN) never reaches a
-// product.  `tok_stride` is the element distance between consecutive tokens.
+// Register staging of one K/V tile (software pipelining: the next tile's global
+// loads are issued before the current tile is computed, and land in LDS after).
+//   K: task = (key j, 16-byte chunk c), c fastest  -> coalesced rows
+//   V: task = (key pair p, chunk c), p fastest      -> the transposed LDS writes of
+//      a wave cover 16 consecutive words of 4 rows (at most 2-way bank conflicts)
 template <int D, int THREADS>
-__device__ __forceinline__ void stage_kv(Smem<D>& sm, const __bf16* __restrict__ kb,
-                                         const __bf16* __restrict__ vb, int64_t tok_stride, uint32_t keymask) {
-  constexpr int CH = D / 8;  // 16-byte chunks per row
+struct KVRegs {
+  static constexpr int CH = D / 8;                                     // 16-byte chunks per row
+  static constexpr int KT = (TK * CH + THREADS - 1) / THREADS;         // K tasks per thread
+  static constexpr int VT = ((TK / 2) * CH + THREADS - 1) / THREADS;   // V pair tasks per thread
+  u32x4 k[KT];
+  u32x4 v0[VT], v1[VT];
+};
+
+// Issue the global loads of a tile: keys whose bit is set in `loadmask` are read,
+// the others become zero.  `tok_stride` is the element distance between tokens.
+template <int D, int THREADS>
+__device__ __forceinline__ void load_kv(KVRegs<D, THREADS>& r, const __bf16* __restrict__ kb,
+                                        const __bf16* __restrict__ vb, int64_t tok_stride, uint32_t loadmask) {
+  using R = KVRegs<D, THREADS>;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int task = threadIdx.x; task < TK * CH; task += THREADS) {
-    const int j = task / CH, c = task % CH;
-    u32x4 val = zero;
-    if ((keymask >> j) & 1u) val = *reinterpret_cast<const u32x4*>(kb + j * tok_stride + 8 * c);
-    *reinterpret_cast<u32x4*>(&sm.k[j * (D + 8) + 8 * c]) = val;
-  }
-  for (int task = threadIdx.x; task < (TK / 2) * CH; task += THREADS) {
-    const int p = task / CH, c = task % CH;
-    const int j0 = 2 * p, j1 = 2 * p + 1;
-    u32x4 a = zero, b = zero;
-    if ((keymask >> j0) & 1u) a = *reinterpret_cast<const u32x4*>(vb + j0 * tok_stride + 8 * c);
-    if ((keymask >> j1) & 1u) b = *reinterpret_cast<const u32x4*>(vb + j1 * tok_stride + 8 * c);
-    const int s = vslot(j0);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.vt[0]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      dst[((8 * c + e) * (TK + 8) + s) >> 1] = lo | (hi << 16);
+  for (int i = 0; i < R::KT; ++i) {
+    const int task = threadIdx.x + i * THREADS;
+    const int j = task / R::CH, c = task % R::CH;
+    r.k[i] = zero;
+    if (task < TK * R::CH && ((loadmask >> j) & 1u))
+      r.k[i] = *reinterpret_cast<const u32x4*>(kb + j * tok_stride + 8 * c);
+  }
+#pragma unroll
+  for (int i = 0; i < R::VT; ++i) {
+    const int task = threadIdx.x + i * THREADS;
+    const int p = task % (TK / 2), c = task / (TK / 2);
+    r.v0[i] = zero;
+    r.v1[i] = zero;
+    if (task < (TK / 2) * R::CH) {
+      if ((loadmask >> (2 * p)) & 1u)
+        r.v0[i] = *reinterpret_cast<const u32x4*>(vb + (2 * p) * tok_stride + 8 * c);
+      if ((loadmask >> (2 * p + 1)) & 1u)
+        r.v1[i] = *reinterpret_cast<const u32x4*>(vb + (2 * p + 1) * tok_stride + 8 * c);
     }
   }
 }
 
-// Per-wave state of the online softmax.
+// Write a loaded tile to LDS: K row-major, V transposed to [d][slot] with the
+// slot permutation; keys whose bit is clear in `keymask` are written as zeros,
+// so whatever a padded slot holds (uninitialised memory, NaN) never reaches a
+// product.
+template <int D, int THREADS>
+__device__ __forceinline__ void store_kv(Smem<D>& sm, const KVRegs<D, THREADS>& r, uint32_t keymask) {
+  using R = KVRegs<D, THREADS>;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < R::KT; ++i) {
+    const int task = threadIdx.x + i * THREADS;
+    const int j = task / R::CH, c = task % R::CH;
+    if (task < TK * R::CH)
+      *reinterpret_cast<u32x4*>(&sm.k[j * (D + 8) + 8 * c]) = ((keymask >> j) & 1u) ? r.k[i] : zero;
+  }
+  uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.vt[0]);
+#pragma unroll
+  for (int i = 0; i < R::VT; ++i) {
+    const int task = threadIdx.x + i * THREADS;
+    const int p = task % (TK / 2), c = task / (TK / 2);
+    if (task < (TK / 2) * R::CH) {
+      const u32x4 a = ((keymask >> (2 * p)) & 1u) ? r.v0[i] : zero;
+      const u32x4 b = ((keymask >> (2 * p + 1)) & 1u) ? r.v1[i] : zero;
+      const int sl = vslot(2 * p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        dst[((8 * c + e) * (TK + 8) + sl) >> 1] = lo | (hi << 16);
+      }
+    }
+  }
+}
+
+// Per-wave state of the online softmax.  m is each row's reference maximum
+// (scores already multiplied by scale*log2(e)), fixed at the row's first tile
+// with a visible key; mobs is the true running maximum.
 template <int D, int NR>
 struct WaveState {
   bf16x8 qf[NR][D / 32];
   f32x4 o[NR][D / 16];
   float m[NR];
+  float mobs[NR];
   float l[NR];
   uint32_t wq[NR];
 };
+
+// Weights are exp2(score - m) against a reference maximum m fixed at a row's
+// first tile with a visible key, so the accumulators never need rescaling inside
+// the loop (a rescale there would force the compiler to shuttle all of O between
+// accumulation and vector registers every tile).  Later scores may exceed m: the
+// weights then grow above 1, exactly representable up to 2^127 in bf16 and fp32,
+// and the final division by l makes the result independent of m.  If a row's
+// true maximum ends more than kMaxGrowth above m, the workgroup reruns its tiles
+// once with m set to that true maximum (never the case for unit-variance inputs).
+constexpr float kMaxGrowth = 64.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // One 32-key tile for one wave.  cls: PI_TILE_FULL or PI_TILE_PARTIAL.
 template <int D, int NR>
@@ -118,49 +179,71 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
     }
   }
   const float NEG_INF = -INFINITY;
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float x[2][4];
+  if (cls == PI_TILE_PARTIAL) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = s[r][kt][i] * scale_log2;
-        if (cls == PI_TILE_PARTIAL) {
-          const uint32_t wk = sm.kw[kt * 16 + 4 * g + i];
-          if (!pair_visible(st.wq[r], wk, forbid)) v = NEG_INF;
-        }
-        x[kt][i] = v;
+        const uint32_t wk = sm.kw[kt * 16 + 4 * g + i];
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+          if (!pair_visible(st.wq[r], wk, forbid)) s[r][kt][i] = NEG_INF;
       }
+  }
+  // tile row maxima; the first visible tile of a row fixes its reference maximum
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
     float mx = NEG_INF;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[kt][i]);
-    mx = group4_max(mx);
-    const float m_new = fmaxf(st.m[r], mx);
-    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-    const float corr = exp2f(st.m[r] - m_use);
-    st.m[r] = m_new;
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[r][kt][i]);
+    const float mt = group4_max(mx) * scale_log2;
+    st.mobs[r] = fmaxf(st.mobs[r], mt);
+    st.m[r] = (st.m[r] == NEG_INF) ? mt : st.m[r];
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    // a row that has seen no visible key keeps m = -inf: use 0 so masked weights are exp2(-inf) = 0
+    const float m_use = (st.m[r] == NEG_INF) ? 0.f : st.m[r];
     bf16x8 pf;
     float lsum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const __bf16 pb = f2bf(exp2f(x[kt][i] - m_use));
+        const __bf16 pb = f2bf(fast_exp2(fmaf(s[r][kt][i], scale_log2, -m_use)));
         pf[4 * kt + i] = pb;
         lsum += bf2f(pb);
       }
-    st.l[r] = st.l[r] * corr + lsum;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] *= corr;
+    st.l[r] += lsum;
     // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[(dt * 16 + c) * (TK + 8) + 8 * g]);
       st.o[r][dt] = mfma16x16x32(a, pf, st.o[r][dt]);
     }
+  }
+}
+
+// True if a row's maximum grew past its reference by more than kMaxGrowth; in that
+// case the state is reset with the reference set to the true maximum.
+template <int D, int NR>
+__device__ __forceinline__ bool needs_rerun(WaveState<D, NR>& st) {
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) bad |= st.mobs[r] > st.m[r] + kMaxGrowth;
+  return bad;
+}
+
+template <int D, int NR>
+__device__ __forceinline__ void reset_for_rerun(WaveState<D, NR>& st) {
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    st.m[r] = st.mobs[r];
+    st.l[r] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -181,6 +264,7 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     st.m[r] = -INFINITY;
+    st.mobs[r] = -INFINITY;
     st.l[r] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -208,8 +292,39 @@ __device__ __forceinline__ void store_rows(WaveState<D, NR>& st, __bf16* const* 
   }
 }
 
+// Longest key sequence a workgroup walks (tiles of 32 keys): 16384 tokens.
+constexpr int kMaxTiles = 512;
+
+// Row setup shared by both kernels: Q fragments into registers, the row's
+// query word, and the output row base (nullptr for rows past the end).
+template <int D, int G, int NR, int ROWS_W>
+__device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_base, const __bf16* __restrict__ q,
+                                          __bf16* __restrict__ o, int64_t tok_base, int ntok, int Hq, int head0,
+                                          int tok0, const uint32_t* words) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int row = wave * ROWS_W + r * 16 + c;
+    const int t = tok0 + row / G;
+    const int h = head0 + row % G;
+    const bool ok = t < ntok;
+    st.wq[r] = ok ? words[t] : 0u;
+    const __bf16* qrow = q + ((tok_base + (ok ? t : 0)) * Hq + h) * D;
+#pragma unroll
+    for (int ds = 0; ds < D / 32; ++ds) {
+      bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
+      if (!ok) val = bf16x8{};
+      st.qf[r][ds] = val;
+    }
+    row_base[r] = ok ? o + ((tok_base + t) * Hq + h) * D : nullptr;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: grid = ceil(B*Hkv / 8) * 8 groups x n_qblk workgroups (XCD-placed).
+// Wave 0 first compacts the workgroup's non-EMPTY key tiles into an LDS list;
+// the loop then prefetches tile i+1 into registers while tile i is computed.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NR, int NW>
 __global__ void __launch_bounds__(NW * 64)
@@ -219,58 +334,75 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
                uint32_t forbid, int n_qblk) {
   using C = Cfg<D, G, NR, NW>;
   __shared__ Smem<D> sm;
+  __shared__ uint32_t tlist[kMaxTiles];
+  __shared__ int tcount;
   int group, qblk;
   xcd_place(B * Hkv, n_qblk, group, qblk);
   if (group >= B * Hkv) return;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g = lane >> 4;
   const int tok0 = qblk * C::TOK;
   const uint32_t* tk = tok + (size_t)b * L;
+
+  if (wave == 0) {
+    const int qt_lo = tok0 / PI_MASK_TILE_Q;
+    const int qt_hi = min(n_qt, (tok0 + C::TOK + PI_MASK_TILE_Q - 1) / PI_MASK_TILE_Q);
+    const uint8_t* trow = tiles + (size_t)b * n_qt * n_kt;
+    int cnt = 0;
+    for (int base = 0; base < n_kt; base += 64) {
+      const int kt = base + lane;
+      int cls = 0;
+      if (kt < n_kt) {
+        cls = -1;
+        for (int qt = qt_lo; qt < qt_hi; ++qt) {
+          const int cl = trow[(size_t)qt * n_kt + kt];
+          cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
+        }
+      }
+      const unsigned long long bal = __ballot(cls > 0);
+      if (cls > 0) tlist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)kt | ((uint32_t)cls << 16);
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) tcount = cnt;
+  }
 
   WaveState<D, NR> st;
   init_state(st);
   __bf16* row_base[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int row = wave * C::ROWS_W + r * 16 + c;
-    const int t = tok0 + row / G;
-    const int h = kvh * G + row % G;
-    const bool ok = t < L;
-    st.wq[r] = ok ? tk[t] : 0u;
-    const __bf16* qrow = q + (((size_t)b * L + (ok ? t : 0)) * Hq + h) * D;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
-      if (!ok) val = bf16x8{};
-      st.qf[r][ds] = val;
-    }
-    row_base[r] = ok ? o + (((size_t)b * L + t) * Hq + h) * D : nullptr;
-  }
+  load_rows<D, G, NR, C::ROWS_W>(st, row_base, q, o, (int64_t)b * L, L, Hq, kvh * G, tok0, tk);
+  __syncthreads();
+  const int count = tcount;
 
   const int64_t tstride = (int64_t)Hkv * D;
   const __bf16* kb = k + ((size_t)b * L * Hkv + kvh) * D;
   const __bf16* vb = v + ((size_t)b * L * Hkv + kvh) * D;
-  const int qt_lo = tok0 / PI_MASK_TILE_Q;
-  const int qt_hi = min(n_qt, (tok0 + C::TOK + PI_MASK_TILE_Q - 1) / PI_MASK_TILE_Q);
-  const uint8_t* trow = tiles + (size_t)b * n_qt * n_kt;
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    int cls = -1;
-    for (int qt = qt_lo; qt < qt_hi; ++qt) {
-      const int cl = trow[(size_t)qt * n_kt + kt];
-      cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
-    }
-    if (cls <= PI_TILE_EMPTY) continue;
-    const int key0 = kt * TK;
+  KVRegs<D, C::THREADS> regs;
+  uint32_t wnext = 0u;
+  auto issue = [&](int i) {
+    const int key0 = (int)(tlist[i] & 0xFFFFu) * TK;
     const int nvalid = min(TK, L - key0);
-    const uint32_t wk = lane < nvalid ? tk[key0 + lane] : 0u;
-    const uint32_t keymask = (uint32_t)__ballot(wk & 1u);
-    __syncthreads();
-    stage_kv<D, C::THREADS>(sm, kb + key0 * tstride, vb + key0 * tstride, tstride, keymask);
-    if (threadIdx.x < TK) sm.kw[threadIdx.x] = wk;
-    __syncthreads();
-    attend_tile<D, NR>(sm, st, cls, forbid, scale_log2);
+    wnext = lane < nvalid ? tk[key0 + lane] : 0u;
+    load_kv<D, C::THREADS>(regs, kb + key0 * tstride, vb + key0 * tstride, tstride,
+                           nvalid == TK ? 0xFFFFFFFFu : ((1u << nvalid) - 1u));
+  };
+  auto run = [&]() {
+    if (count > 0) issue(0);
+    for (int i = 0; i < count; ++i) {
+      const int cls = (int)((tlist[i] >> 16) & 0xFFu);
+      const uint32_t wcur = wnext;
+      const uint32_t keymask = (uint32_t)__ballot(wcur & 1u);
+      __syncthreads();
+      store_kv<D, C::THREADS>(sm, regs, keymask);
+      if (threadIdx.x < TK) sm.kw[threadIdx.x] = wcur;
+      __syncthreads();
+      if (i + 1 < count) issue(i + 1);
+      attend_tile<D, NR>(sm, st, cls, forbid, scale_log2);
+    }
+  };
+  run();
+  if (__syncthreads_or(needs_rerun(st))) {
+    reset_for_rerun(st);
+    run();
   }
   store_rows<D, NR>(st, row_base);
 }
@@ -279,7 +411,9 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
 // Cached suffix decode (Hq = 8, Hkv = 1, d = 256): grid = ceil(B/8)*8 x n_qblk.
 // Keys: valid prefix slots of the cache layer, then the suffix's own K/V.
 // Query/key words reuse the prefill rule with bid 0 for every prefix slot and
-// 1 + cumsum(suffix_ar) for suffix tokens.
+// 1 + cumsum(suffix_ar) for suffix tokens.  The per-tile validity of the prefix
+// slots is read once up front, so fully padded tiles are never fetched and
+// padded slots inside a tile are neither read nor used.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NR, int NW>
 __global__ void __launch_bounds__(NW * 64)
@@ -292,12 +426,17 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   constexpr int Hq = G;
   __shared__ Smem<D> sm;
   __shared__ uint32_t sbid[128];
+  __shared__ uint32_t pmask[kMaxTiles];
+  __shared__ uint32_t tlist[kMaxTiles];
+  __shared__ uint32_t tmask[kMaxTiles];
+  __shared__ int tcount;
   int b, qblk;
   xcd_place(B, n_qblk, b, qblk);
   if (b >= B) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g = lane >> 4;
   const int tok0 = qblk * C::TOK;
+  const int n_pt = (P + TK - 1) / TK;
+  const int n_st = (S + TK - 1) / TK;
 
   // suffix block ids: inclusive cumsum of suffix_ar (S <= 128), computed by wave 0
   if (wave == 0) {
@@ -312,59 +451,84 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
     sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
   }
+  // validity bitmap of the prefix slots, one 32-bit word per tile
+  const uint8_t* pm = prefix_mask + (size_t)b * cap;
+  for (int base = wave * 64; base < n_pt * TK; base += NW * 64) {
+    const int slot = base + lane;
+    const bool valid = slot < P && pm[slot] != 0;
+    const unsigned long long bal = __ballot(valid);
+    if (lane == 0) pmask[base / TK] = (uint32_t)bal;
+    if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
+  }
   __syncthreads();
+  // compact tile list: non-empty prefix tiles, then the suffix tiles
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < n_pt + n_st; base += 64) {
+      const int i = base + lane;
+      uint32_t m = 0u, desc = 0u;
+      if (i < n_pt) {
+        m = pmask[i];
+        const bool full = (m == 0xFFFFFFFFu);
+        desc = (uint32_t)i | ((uint32_t)(full ? PI_TILE_FULL : PI_TILE_PARTIAL) << 16);
+      } else if (i < n_pt + n_st) {
+        const int nv = min(TK, S - (i - n_pt) * TK);
+        m = nv == TK ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+        desc = (uint32_t)(i - n_pt) | ((uint32_t)PI_TILE_PARTIAL << 16) | (1u << 24);
+      }
+      const unsigned long long bal = __ballot(m != 0u);
+      if (m != 0u) {
+        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+        tlist[pos] = desc;
+        tmask[pos] = m;
+      }
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) tcount = cnt;
+  }
+  __syncthreads();
+  const int count = tcount;
 
   WaveState<D, NR> st;
   init_state(st);
   __bf16* row_base[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int row = wave * C::ROWS_W + r * 16 + c;
-    const int t = tok0 + row / G;
-    const int h = row % G;
-    const bool ok = t < S;
-    st.wq[r] = ok ? sbid[t] : 0u;
-    const __bf16* qrow = qs + (((size_t)b * S + (ok ? t : 0)) * Hq + h) * D;
-#pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
-      if (!ok) val = bf16x8{};
-      st.qf[r][ds] = val;
-    }
-    row_base[r] = ok ? os + (((size_t)b * S + t) * Hq + h) * D : nullptr;
-  }
+  load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, sbid);
 
-  // prefix slots from the cache
   const __bf16* kb = ck + (size_t)b * cap * D;
   const __bf16* vb = cv + (size_t)b * cap * D;
-  const uint8_t* pm = prefix_mask + (size_t)b * cap;
-  const int n_pt = (P + TK - 1) / TK;
-  for (int kt = 0; kt < n_pt; ++kt) {
-    const int key0 = kt * TK;
-    const int nvalid = min(TK, P - key0);
-    const bool mine = lane < nvalid && pm[key0 + lane] != 0;
-    const unsigned long long bal = __ballot(mine);
-    if (bal == 0ull) continue;
-    const int cls = (nvalid == TK && bal == 0xFFFFFFFFull) ? PI_TILE_FULL : PI_TILE_PARTIAL;
-    __syncthreads();
-    stage_kv<D, C::THREADS>(sm, kb + (size_t)key0 * D, vb + (size_t)key0 * D, D, (uint32_t)bal);
-    if (threadIdx.x < TK) sm.kw[threadIdx.x] = mine ? 1u : 0u;
-    __syncthreads();
-    attend_tile<D, NR>(sm, st, cls, 0u, scale_log2);
-  }
-  // the suffix's own keys
   const __bf16* ksb = ks + (size_t)b * S * D;
   const __bf16* vsb = vs + (size_t)b * S * D;
-  const int n_st = (S + TK - 1) / TK;
-  for (int kt = 0; kt < n_st; ++kt) {
-    const int key0 = kt * TK;
-    const int nvalid = min(TK, S - key0);
-    const uint32_t keymask = nvalid == TK ? 0xFFFFFFFFu : ((1u << nvalid) - 1u);
-    __syncthreads();
-    stage_kv<D, C::THREADS>(sm, ksb + (size_t)key0 * D, vsb + (size_t)key0 * D, D, keymask);
-    if (threadIdx.x < TK) sm.kw[threadIdx.x] = (int)threadIdx.x < nvalid ? sbid[key0 + threadIdx.x] : 0u;
-    __syncthreads();
-    attend_tile<D, NR>(sm, st, PI_TILE_PARTIAL, 0u, scale_log2);
+  KVRegs<D, C::THREADS> regs;
+  auto issue = [&](int i) {
+    const uint32_t d = tlist[i];
+    const int key0 = (int)(d & 0xFFFFu) * TK;
+    const bool suffix = (d >> 24) & 1u;
+    load_kv<D, C::THREADS>(regs, (suffix ? ksb : kb) + (size_t)key0 * D, (suffix ? vsb : vb) + (size_t)key0 * D, D,
+                           tmask[i]);
+  };
+  auto run = [&]() {
+    if (count > 0) issue(0);
+    for (int i = 0; i < count; ++i) {
+      const uint32_t d = tlist[i];
+      const int cls = (int)((d >> 16) & 0xFFu);
+      const bool suffix = (d >> 24) & 1u;
+      const int key0 = (int)(d & 0xFFFFu) * TK;
+      const uint32_t keymask = tmask[i];
+      __syncthreads();
+      store_kv<D, C::THREADS>(sm, regs, keymask);
+      if (threadIdx.x < TK) {
+        const uint32_t bit = (keymask >> threadIdx.x) & 1u;
+        sm.kw[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
+      }
+      __syncthreads();
+      if (i + 1 < count) issue(i + 1);
+      attend_tile<D, NR>(sm, st, cls, 0u, scale_log2);
+    }
+  };
+  run();
+  if (__syncthreads_or(needs_rerun(st))) {
+    reset_for_rerun(st);
+    run();
   }
   store_rows<D, NR>(st, row_base);
 }
@@ -416,6 +580,8 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: scale must be > 0");
   PI_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, PI_ERR_INVALID_ARG,
              "pi_joint_attn_prefill: Hq=%d must be a multiple of Hkv=%d", Hq, Hkv);
+  PI_REQUIRE(L <= kMaxTiles * TK, PI_ERR_UNSUPPORTED, "pi_joint_attn_prefill: L=%d exceeds %d tokens", L,
+             kMaxTiles * TK);
   const bool gqa8 = (Hq == 8 && Hkv == 1 && d == 256);
   const bool mha64 = (Hq == Hkv && d == 64);
   PI_REQUIRE(gqa8 || mha64, PI_ERR_UNSUPPORTED,
@@ -459,6 +625,8 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
              PI_ERR_INVALID_ARG, "pi_suffix_decode_step: cache/layer mismatch (layer %d of %d, B %d vs %d)", layer,
              cache->layers, cache->B, B);
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_suffix_decode_step: scale must be > 0");
+  PI_REQUIRE((cache->len + TK - 1) / TK + (S + TK - 1) / TK <= kMaxTiles, PI_ERR_UNSUPPORTED,
+             "pi_suffix_decode_step: cache length %d too long", cache->len);
   PI_REQUIRE(Hq == 8 && cache->Hkv == 1 && cache->d == 256, PI_ERR_UNSUPPORTED,
              "pi_suffix_decode_step: supported heads are Hq=8, Hkv=1, d=256 (got %d, %d, %d)", Hq, cache->Hkv,
              cache->d);

@@ -82,22 +82,33 @@ __device__ __forceinline__ bf16x8 load_frag(const T* row, int k, int K, bool vec
 constexpr float kRmsEps = 1e-6f;
 
 // out[m][n] = sum_k r(A[m][k]) W[n][k]  (divided by rms(A[m]) when NORM).
-// Workgroup tile 64 (n) x 64 (m), four waves of 32 x 32; computed transposed
-// (A operand = weights, B operand = activations) so a lane ends with four
-// consecutive output columns of one row.
+//
+// Workgroup tile 64 (n) x 64 (m).  The four waves split the contraction into four
+// contiguous ranges and each computes the whole 64 x 64 tile over its range, with
+// KB k-steps of loads in flight at a time; the four partial tiles are summed
+// through LDS and each wave finishes 16 rows.  This keeps the skinny products of
+// a small batch (M = 51 rows) from serialising on memory latency.  Products are
+// computed transposed (A operand = weights, B operand = activations) so a lane
+// holds four consecutive output columns of one row.
+constexpr int kPartStride = 68;  // LDS row stride (floats) of a 64 x 64 partial tile
+
 template <int EPI, typename TA, bool NORM>
 __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
+  constexpr int KB = sizeof(TA) == 2 ? 4 : 2;   // k-steps of loads in flight
+  __shared__ float part[4][64 * kPartStride];
+  __shared__ float ssp[4][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int wn = wave & 1, wm = wave >> 1;
-  const int n0 = blockIdx.x * 64 + wn * 32;
-  const int m0 = blockIdx.y * 64 + wm * 32;
+  const int n0 = blockIdx.x * 64;
+  const int m0 = blockIdx.y * 64;
   const bool vec_ok = (p.K & 7) == 0;
 
-  const __bf16* wrow[2];
-  bool wok[2];
+  const __bf16* wrow[4];
+  bool wok[4];
+  const TA* arow[4];
+  bool aok[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const int n = n0 + 16 * j + c;
     wok[j] = n < p.N;
     const __bf16* base = p.w0;
@@ -105,71 +116,93 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
     if (n >= p.n1 + p.n2) { base = p.w2; nn = n - p.n1 - p.n2; }
     else if (n >= p.n1) { base = p.w1; nn = n - p.n1; }
     wrow[j] = base + (int64_t)(wok[j] ? nn : 0) * p.K;
-  }
-  const TA* arow[2];
-  bool aok[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
     const int m = m0 + 16 * j + c;
     aok[j] = m < p.M;
     arow[j] = static_cast<const TA*>(p.a) + (aok[j] ? p.amap(m) : 0) * p.K;
   }
 
-  f32x4 acc[2][2];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[2] = {0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[4] = {0.f, 0.f, 0.f, 0.f};
   float ss_w = 0.f;
 
-  for (int k0 = 0; k0 < p.K; k0 += 32) {
-    const int k = k0 + 8 * g;
-    bf16x8 wf[2], af[2];
+  const int ksteps = (p.K + 31) / 32;
+  const int per = (ksteps + 3) / 4;
+  const int ks_lo = wave * per, ks_hi = min(ksteps, ks_lo + per);
+  for (int ks0 = ks_lo; ks0 < ks_hi; ks0 += KB) {
+    bf16x8 wf[KB][4], af[KB][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      wf[j] = wok[j] ? load_frag(wrow[j], k, p.K, vec_ok, ss_w) : bf16x8{};
-      af[j] = aok[j] ? load_frag(arow[j], k, p.K, vec_ok, ss[j]) : bf16x8{};
+    for (int u = 0; u < KB; ++u) {
+      const int k = (ks0 + u) * 32 + 8 * g;
+      const bool live = ks0 + u < ks_hi;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wf[u][j] = (live && wok[j]) ? load_frag(wrow[j], k, p.K, vec_ok, ss_w) : bf16x8{};
+        af[u][j] = (live && aok[j]) ? load_frag(arow[j], k, p.K, vec_ok, ss[j]) : bf16x8{};
+      }
     }
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
+    for (int u = 0; u < KB; ++u)
 #pragma unroll
-      for (int jm = 0; jm < 2; ++jm) acc[jn][jm] = mfma16x16x32(wf[jn], af[jm], acc[jn][jm]);
+      for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+        for (int jm = 0; jm < 4; ++jm) acc[jn][jm] = mfma16x16x32(wf[u][jn], af[u][jm], acc[jn][jm]);
   }
   (void)ss_w;
-  float inv_rms[2] = {1.f, 1.f};
+
+  // partial tiles and partial row sums of squares to LDS
+#pragma unroll
+  for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+    for (int jm = 0; jm < 4; ++jm)
+      *reinterpret_cast<f32x4*>(&part[wave][(16 * jm + c) * kPartStride + 16 * jn + 4 * g]) = acc[jn][jm];
   if constexpr (NORM) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) inv_rms[j] = rsqrtf(group4_sum(ss[j]) / (float)p.K + kRmsEps);
+    for (int jm = 0; jm < 4; ++jm) {
+      const float t = group4_sum(ss[jm]);
+      if (g == 0) ssp[wave][16 * jm + c] = t;
+    }
   }
+  __syncthreads();
 
+  // wave w finishes rows 16w .. 16w+15 of the tile
+  const int ml = 16 * wave + c;
+  const int m = m0 + ml;
+  float inv_rms = 1.f;
+  if constexpr (NORM) {
+    const float t = ssp[0][ml] + ssp[1][ml] + ssp[2][ml] + ssp[3][ml];
+    inv_rms = rsqrtf(t / (float)p.K + kRmsEps);
+  }
+  if (m >= p.M) return;
 #pragma unroll
-  for (int jm = 0; jm < 2; ++jm) {
-    const int m = m0 + 16 * jm + c;
-    if (m >= p.M) continue;
+  for (int jn = 0; jn < 4; ++jn) {
+    const int nl = 16 * jn + 4 * g;
+    const int nb = n0 + nl;
+    if (nb >= p.N) continue;
+    f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * kPartStride + nl]);
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn) {
-      const int nb = n0 + 16 * jn + 4 * g;
-      if (nb >= p.N) continue;
-      const f32x4 r = acc[jn][jm] * inv_rms[jm];
-      if constexpr (EPI == EPI_QKV) {
-        __bf16* dst;
-        if (nb < p.n1) dst = p.o0 + (int64_t)m * p.n1 + nb;
-        else if (nb < p.n1 + p.n2) dst = p.o1 + (int64_t)m * p.n2 + (nb - p.n1);
-        else dst = p.o2 + (int64_t)m * (p.N - p.n1 - p.n2) + (nb - p.n1 - p.n2);
-        bf16x4 v;
+    for (int w = 1; w < 4; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * kPartStride + nl]);
+    r *= inv_rms;
+    if constexpr (EPI == EPI_QKV) {
+      __bf16* dst;
+      if (nb < p.n1) dst = p.o0 + (int64_t)m * p.n1 + nb;
+      else if (nb < p.n1 + p.n2) dst = p.o1 + (int64_t)m * p.n2 + (nb - p.n1);
+      else dst = p.o2 + (int64_t)m * (p.N - p.n1 - p.n2) + (nb - p.n1 - p.n2);
+      bf16x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = f2bf(r[i]);
-        *reinterpret_cast<bf16x4*>(dst) = v;
-      } else {
-        float* dst = p.out + p.omap(m) * p.N + nb;
+      for (int i = 0; i < 4; ++i) v[i] = f2bf(r[i]);
+      *reinterpret_cast<bf16x4*>(dst) = v;
+    } else {
+      float* dst = p.out + p.omap(m) * p.N + nb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (nb + i >= p.N) break;
-          if constexpr (EPI == EPI_RESID) dst[i] += r[i];
-          else if constexpr (EPI == EPI_VEL) dst[i] = r[i] + p.bias[nb + i];
-          else dst[i] += p.dt * (r[i] + p.bias[nb + i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        if (nb + i >= p.N) break;
+        if constexpr (EPI == EPI_RESID) dst[i] += r[i];
+        else if constexpr (EPI == EPI_VEL) dst[i] = r[i] + p.bias[nb + i];
+        else dst[i] += p.dt * (r[i] + p.bias[nb + i]);
       }
     }
   }
