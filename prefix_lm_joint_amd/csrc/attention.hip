@@ -10,12 +10,15 @@
 //   * A workgroup owns NW waves x NR row tiles x 16 query rows.  With one KV head
 //     and 8 query heads a row is a (token, head) pair: a 16-row tile holds two
 //     tokens x 8 heads, so every K/V element loaded is used by 8 heads.
-//   * K/V tiles of 32 keys are staged in LDS: K row-major (padded rows), V
-//     transposed to [d][key] so that both matrix-core operands are 16-byte reads.
+//   * K/V tiles of 32 keys are staged in LDS row-major (padded rows).
 //   * Products are computed transposed: S^T = K Q^T (A = K from LDS, B = Q held in
 //     registers), then O^T += V^T P^T with P^T taken straight from the S^T
-//     accumulators (no LDS round trip).  The 32 keys of a tile are permuted inside
-//     V^T to match the accumulator layout of S^T.
+//     accumulators (no LDS round trip).  The V^T operand is read with gfx950's
+//     transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group, lane i
+//     receives element (i % 4) of the 4 elements addressed by lanes 4k + i/4,
+//     k = 0..3, so pointing lane j at row 4g + j/4, columns 4*(j%4).. of the V tile
+//     hands lane i the values of 4 keys at one d -- the keys its S^T accumulators
+//     cover.
 //   * Online softmax in base 2 with per-row max/sum reduced across the four
 //     16-lane groups of the wave.
 //   * Key tiles classified EMPTY by the mask builder are skipped; FULL tiles skip
@@ -36,37 +39,43 @@ struct Cfg {
   static constexpr int ROWS = NW * ROWS_W;
   static constexpr int TOK = ROWS / G;        // query tokens per workgroup
   static constexpr int THREADS = NW * PI_WAVE;
-  static constexpr int KSTR = D + 8;          // LDS row stride of K (bf16 elements)
-  static constexpr int VSTR = TK + 8;         // LDS row stride of V^T (bf16 elements)
-  static constexpr int DS = D / 32;           // k-steps of the QK^T product
-  static constexpr int DT = D / 16;           // 16-wide d tiles of the PV product
   static_assert(ROWS % G == 0, "rows must cover whole tokens");
   static_assert(D % 32 == 0, "head dim must be a multiple of 32");
 };
 
+// LDS row strides (bf16 elements).  K rows are padded by 16 B: the 16 rows a
+// fragment read touches then start 4 banks apart (conflict-free 16-byte reads).
+// V rows are padded by 32 B: the 4 rows x 32 bytes a transposing read of one
+// 16-lane group touches then fall on disjoint banks.
+template <int D>
+struct Lds {
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = D + 16;
+};
+
 template <int D>
 struct Smem {
-  alignas(16) __bf16 k[TK * (D + 8)];
-  alignas(16) __bf16 vt[D * (TK + 8)];
+  alignas(16) __bf16 k[TK * Lds<D>::KSTR];
+  alignas(16) __bf16 v[TK * Lds<D>::VSTR];
   alignas(16) uint32_t kw[TK];
 };
 
-// Permuted V^T slot of key j (0..31) so that lane group g's 8 contiguous slots
-// hold keys {4g..4g+3, 16+4g..16+4g+3}, the keys its S^T accumulators cover.
-__device__ __forceinline__ int vslot(int j) { return 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3); }
+#define PI_LDS __attribute__((address_space(3)))
+
+// Transposing LDS read of 4 bf16 (see the header comment for the lane mapping).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PI_LDS bf16x4*)(const_cast<__bf16*>(p)));
+}
 
 // Register staging of one K/V tile (software pipelining: the next tile's global
 // loads are issued before the current tile is computed, and land in LDS after).
-//   K: task = (key j, 16-byte chunk c), c fastest  -> coalesced rows
-//   V: task = (key pair p, chunk c), p fastest      -> the transposed LDS writes of
-//      a wave cover 16 consecutive words of 4 rows (at most 2-way bank conflicts)
+// Task = (key j, 16-byte chunk c), c fastest: coalesced rows for both tensors.
 template <int D, int THREADS>
 struct KVRegs {
-  static constexpr int CH = D / 8;                                     // 16-byte chunks per row
-  static constexpr int KT = (TK * CH + THREADS - 1) / THREADS;         // K tasks per thread
-  static constexpr int VT = ((TK / 2) * CH + THREADS - 1) / THREADS;   // V pair tasks per thread
-  u32x4 k[KT];
-  u32x4 v0[VT], v1[VT];
+  static constexpr int CH = D / 8;                                // 16-byte chunks per row
+  static constexpr int T = (TK * CH + THREADS - 1) / THREADS;     // tasks per thread
+  u32x4 k[T];
+  u32x4 v[T];
 };
 
 // Issue the global loads of a tile: keys whose bit is set in `loadmask` are read,
@@ -77,58 +86,33 @@ __device__ __forceinline__ void load_kv(KVRegs<D, THREADS>& r, const __bf16* __r
   using R = KVRegs<D, THREADS>;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < R::KT; ++i) {
+  for (int i = 0; i < R::T; ++i) {
     const int task = threadIdx.x + i * THREADS;
     const int j = task / R::CH, c = task % R::CH;
     r.k[i] = zero;
-    if (task < TK * R::CH && ((loadmask >> j) & 1u))
+    r.v[i] = zero;
+    if (task < TK * R::CH && ((loadmask >> j) & 1u)) {
       r.k[i] = *reinterpret_cast<const u32x4*>(kb + j * tok_stride + 8 * c);
-  }
-#pragma unroll
-  for (int i = 0; i < R::VT; ++i) {
-    const int task = threadIdx.x + i * THREADS;
-    const int p = task % (TK / 2), c = task / (TK / 2);
-    r.v0[i] = zero;
-    r.v1[i] = zero;
-    if (task < (TK / 2) * R::CH) {
-      if ((loadmask >> (2 * p)) & 1u)
-        r.v0[i] = *reinterpret_cast<const u32x4*>(vb + (2 * p) * tok_stride + 8 * c);
-      if ((loadmask >> (2 * p + 1)) & 1u)
-        r.v1[i] = *reinterpret_cast<const u32x4*>(vb + (2 * p + 1) * tok_stride + 8 * c);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vb + j * tok_stride + 8 * c);
     }
   }
 }
 
-// Write a loaded tile to LDS: K row-major, V transposed to [d][slot] with the
-// slot permutation; keys whose bit is clear in `keymask` are written as zeros,
-// so whatever a padded slot holds (uninitialised memory, NaN) never reaches a
-// product.
+// Write a loaded tile to LDS, both tensors row-major; keys whose bit is clear in
+// `keymask` are written as zeros, so whatever a padded slot holds (uninitialised
+// memory, NaN) never reaches a product.
 template <int D, int THREADS>
 __device__ __forceinline__ void store_kv(Smem<D>& sm, const KVRegs<D, THREADS>& r, uint32_t keymask) {
   using R = KVRegs<D, THREADS>;
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < R::KT; ++i) {
+  for (int i = 0; i < R::T; ++i) {
     const int task = threadIdx.x + i * THREADS;
     const int j = task / R::CH, c = task % R::CH;
-    if (task < TK * R::CH)
-      *reinterpret_cast<u32x4*>(&sm.k[j * (D + 8) + 8 * c]) = ((keymask >> j) & 1u) ? r.k[i] : zero;
-  }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(&sm.vt[0]);
-#pragma unroll
-  for (int i = 0; i < R::VT; ++i) {
-    const int task = threadIdx.x + i * THREADS;
-    const int p = task % (TK / 2), c = task / (TK / 2);
-    if (task < (TK / 2) * R::CH) {
-      const u32x4 a = ((keymask >> (2 * p)) & 1u) ? r.v0[i] : zero;
-      const u32x4 b = ((keymask >> (2 * p + 1)) & 1u) ? r.v1[i] : zero;
-      const int sl = vslot(2 * p);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-        dst[((8 * c + e) * (TK + 8) + sl) >> 1] = lo | (hi << 16);
-      }
+    if (task < TK * R::CH) {
+      const bool keep = (keymask >> j) & 1u;
+      *reinterpret_cast<u32x4*>(&sm.k[j * Lds<D>::KSTR + 8 * c]) = keep ? r.k[i] : zero;
+      *reinterpret_cast<u32x4*>(&sm.v[j * Lds<D>::VSTR + 8 * c]) = keep ? r.v[i] : zero;
     }
   }
 }
@@ -173,7 +157,7 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
   for (int ds = 0; ds < D / 32; ++ds) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 16 + c) * (D + 8) + ds * 32 + 8 * g]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 16 + c) * Lds<D>::KSTR + ds * 32 + 8 * g]);
 #pragma unroll
       for (int r = 0; r < NR; ++r) s[r][kt] = mfma16x16x32(a, st.qf[r][ds], s[r][kt]);
     }
@@ -217,10 +201,15 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
         lsum += bf2f(pb);
       }
     st.l[r] += lsum;
-    // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]
+    // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]; the A operand of
+    // lane (c, g) is keys {4g..4g+3, 16+4g..16+4g+3} at d = 16 dt + c
+    const __bf16* vrow0 = &sm.v[(4 * g + (c >> 2)) * Lds<D>::VSTR + 4 * (c & 3)];
+    const __bf16* vrow1 = vrow0 + 16 * Lds<D>::VSTR;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.vt[(dt * 16 + c) * (TK + 8) + 8 * g]);
+      const bf16x4 lo = lds_read_tr4(vrow0 + 16 * dt);
+      const bf16x4 hi = lds_read_tr4(vrow1 + 16 * dt);
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       st.o[r][dt] = mfma16x16x32(a, pf, st.o[r][dt]);
     }
   }
