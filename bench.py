@@ -127,7 +127,8 @@ def build_control_step(cx: Ctx):
     ks = cx.bf(I.bf16_normal(seed + 701, (1, H + 1, 1, 256)))
     vs = cx.bf(I.bf16_normal(seed + 702, (1, H + 1, 1, 256)))
     os_ = torch.empty_like(qs)
-    parts["decode_layer"] = lambda: Bd.pi_suffix_decode_step(cache, 0, qs, ks, vs, sar, o_s=os_)
+    dec_ws = Bd.decode_workspace(cache, H + 1)
+    parts["decode_layer"] = lambda: Bd.pi_suffix_decode_step(cache, 0, qs, ks, vs, sar, o_s=os_, workspace=dec_ws)
     parts["flow_sample_10_steps"] = lambda: (x.copy_(noise), Bd.pi_flow_sample(
         net, cache, sar, state, None, x, num_steps=w.steps, workspace=flow_ws))
     pairs_prefill = P * P

@@ -144,10 +144,16 @@ struct pi_kv_cache {
  *   suffix_ar  uint8 [S] (device)
  * Supported: Hq = 8, Hkv = 1, d = 256, 1 <= S <= 128.  Each cached K/V tile is
  * read from HBM once per sample and shared by all 8 query heads.
+ * workspace (device, 256-byte aligned, optional): with at least
+ * pi_decode_workspace_bytes(B, S, Hq, cache->len) bytes a small batch splits each
+ * sample's keys over several workgroups and merges the partial softmaxes; with
+ * NULL or fewer bytes the call runs unsplit (same result up to rounding).
  */
+size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len);
 pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s,
                                 const void* k_s, const void* v_s, const uint8_t* suffix_ar,
-                                int B, int S, int Hq, float scale, void* o_s, pi_stream stream);
+                                int B, int S, int Hq, float scale, void* o_s, void* workspace,
+                                size_t workspace_bytes, pi_stream stream);
 
 /* Euler update x <- x + dt * v over n fp32 elements ([P1] §1.2). */
 pi_status pi_euler_update(float* x, const float* v, float dt, int64_t n, pi_stream stream);

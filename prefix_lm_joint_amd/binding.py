@@ -51,8 +51,9 @@ _SIGS = {
     "pi_mask_materialize": (_c_i, [ctypes.POINTER(PiMask), _c_p, _c_p]),
     "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask),
                                      _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p]),
+    "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
-                                     _c_f, _c_p, _c_p]),
+                                     _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "pi_euler_update": (_c_i, [_c_p, _c_p, _c_f, ctypes.c_int64, _c_p]),
     "pi_flow_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiVelocityNet), _c_i, _c_i]),
     "pi_velocity_eval": (_c_i, [ctypes.POINTER(PiVelocityNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_p, _c_f,
@@ -221,9 +222,20 @@ def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     return o
 
 
+def pi_decode_workspace_bytes(B: int, S: int, Hq: int, length: int) -> int:
+    return int(lib().pi_decode_workspace_bytes(B, S, Hq, length))
+
+
+def decode_workspace(cache: KVCache, S: int, Hq: int = 8) -> Optional[torch.Tensor]:
+    """Device workspace that lets a small-batch decode split its keys (None if not needed)."""
+    n = pi_decode_workspace_bytes(cache.struct.B, S, Hq, cache.struct.len)
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device) if n else None
+
+
 def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: torch.Tensor, v_s: torch.Tensor,
                           suffix_ar: torch.Tensor, o_s: Optional[torch.Tensor] = None, scale: Optional[float] = None,
-                          stream=None) -> torch.Tensor:
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``workspace`` from decode_workspace() enables the key split of small batches; None runs unsplit."""
     B, S, Hq, d = q_s.shape
     if scale is None:
         scale = d ** -0.5
@@ -232,7 +244,8 @@ def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: to
     _check("pi_suffix_decode_step", lib().pi_suffix_decode_step(
         ctypes.byref(cache.struct), layer, _ptr(q_s, torch.bfloat16, "q_s"), _ptr(k_s, torch.bfloat16, "k_s"),
         _ptr(v_s, torch.bfloat16, "v_s"), _ptr(suffix_ar, torch.uint8, "suffix_ar"), B, S, Hq, scale,
-        _ptr(o_s, torch.bfloat16, "o_s"), _stream(stream)))
+        _ptr(o_s, torch.bfloat16, "o_s"), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
     return o_s
 
 

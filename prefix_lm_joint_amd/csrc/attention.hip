@@ -29,6 +29,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace {
 
 constexpr int TK = 32;  // keys per tile
@@ -410,7 +412,8 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               const uint8_t* __restrict__ prefix_mask, int cap, int P,
               const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
               const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
-              __bf16* __restrict__ os, int n_qblk) {
+              __bf16* __restrict__ os, int n_qblk, int n_split, float* __restrict__ opart,
+              float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
   __shared__ Smem<D> sm;
@@ -419,9 +422,10 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ uint32_t tmask[kMaxTiles];
   __shared__ int tcount;
-  int b, qblk;
-  xcd_place(B, n_qblk, b, qblk);
-  if (b >= B) return;
+  int grp, qblk;
+  xcd_place(B * n_split, n_qblk, grp, qblk);
+  if (grp >= B * n_split) return;
+  const int b = grp / n_split, split = grp % n_split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
   const int n_pt = (P + TK - 1) / TK;
@@ -476,7 +480,9 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     if (lane == 0) tcount = cnt;
   }
   __syncthreads();
-  const int count = tcount;
+  // this workgroup's share of the tile list (all of it when the keys are not split)
+  const int i_lo = (int)((int64_t)tcount * split / n_split);
+  const int i_hi = (int)((int64_t)tcount * (split + 1) / n_split);
 
   WaveState<D, NR> st;
   init_state(st);
@@ -496,8 +502,8 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
                            tmask[i]);
   };
   auto run = [&]() {
-    if (count > 0) issue(0);
-    for (int i = 0; i < count; ++i) {
+    if (i_lo < i_hi) issue(i_lo);
+    for (int i = i_lo; i < i_hi; ++i) {
       const uint32_t d = tlist[i];
       const int cls = (int)((d >> 16) & 0xFFu);
       const bool suffix = (d >> 24) & 1u;
@@ -510,7 +516,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
         sm.kw[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
       }
       __syncthreads();
-      if (i + 1 < count) issue(i + 1);
+      if (i + 1 < i_hi) issue(i + 1);
       attend_tile<D, NR>(sm, st, cls, 0u, scale_log2);
     }
   };
@@ -519,7 +525,56 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     reset_for_rerun(st);
     run();
   }
-  store_rows<D, NR>(st, row_base);
+  if (n_split == 1) {
+    store_rows<D, NR>(st, row_base);
+    return;
+  }
+  // split keys: unnormalised fp32 partial O plus (reference max, weight sum) per row
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const float l = group4_sum(st.l[r]);
+    const int row = wave * C::ROWS_W + r * 16 + c;
+    const int t = tok0 + row / G;
+    if (t >= S) continue;
+    const int64_t prow = ((int64_t)split * B + b) * S * Hq + (int64_t)t * Hq + row % G;
+    float* dst = opart + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16 + 4 * g) = st.o[r][dt];
+    if (g == 0) {
+      mlpart[2 * prow] = st.m[r];
+      mlpart[2 * prow + 1] = l;
+    }
+  }
+}
+
+// Merge the key splits of the decode: for each (sample, token, head) row,
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  One wave
+// per row, four d per lane (d = 256).
+__global__ void __launch_bounds__(256)
+decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__ mlpart,
+                      __bf16* __restrict__ os, int n_split, int64_t rows) {
+  constexpr int D = 256;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, mlpart[2 * (sp * rows + row)]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float m = mlpart[2 * (sp * rows + row)];
+      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+      L += w * mlpart[2 * (sp * rows + row) + 1];
+      acc += w * *reinterpret_cast<const f32x4*>(opart + (sp * rows + row) * D + 4 * lane);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  bf16x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = f2bf(acc[i] * inv);
+  *reinterpret_cast<bf16x4*>(os + row * D + 4 * lane) = v;
 }
 
 // K/V rows of tokens [0, P) into cache layer slices; one thread per 16 bytes.
@@ -598,9 +653,44 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   return pi::check_launch("cache_write_kernel");
 }
 
+namespace {
+
+constexpr int kMaxSplit = 16;
+
+// Key splits for a decode of B samples: enough workgroups to cover the chip
+// (about 256) while giving each split at least two key tiles.
+int decode_splits(int B, int S, int len) {
+  using C = Cfg<256, 8, 2, kNW>;
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
+  const int by_chip = 256 / std::max(1, B * n_qblk);
+  return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
+}
+
+size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)B * S * Hq;
+  return pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256) + (size_t)splits * rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+size_t pi::decode_workspace_max(int B, int S, int Hq) {
+  using C = Cfg<256, 8, 2, kNW>;
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  const int splits = std::max(1, std::min(kMaxSplit, 256 / std::max(1, B * n_qblk)));
+  return decode_ws_bytes(B, S, Hq, splits);
+}
+
+extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
+  if (B < 1 || S < 1 || Hq < 1 || len < 0) return 0;
+  return decode_ws_bytes(B, S, Hq, decode_splits(B, S, len));
+}
+
 extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,
                                            const void* v_s, const uint8_t* suffix_ar, int B, int S, int Hq,
-                                           float scale, void* o_s, pi_stream stream) {
+                                           float scale, void* o_s, void* workspace, size_t workspace_bytes,
+                                           pi_stream stream) {
   PI_REQUIRE(cache && q_s && k_s && v_s && suffix_ar && o_s, PI_ERR_INVALID_ARG,
              "pi_suffix_decode_step: null pointer");
   PI_REQUIRE(cache->k && cache->v && cache->prefix_mask, PI_ERR_INVALID_ARG,
@@ -621,13 +711,28 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
              cache->d);
   using C = Cfg<256, 8, 2, kNW>;
   const int n_qblk = (S + C::TOK - 1) / C::TOK;
-  const int groups = (B + 7) / 8 * 8;
+  int splits = decode_splits(B, S, cache->len);
+  const size_t need = decode_ws_bytes(B, S, Hq, splits);
+  if (workspace == nullptr || workspace_bytes < need) splits = 1;   // no workspace: one pass per sample
+  PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "pi_suffix_decode_step: workspace must be 256-byte aligned");
+  const int64_t rows = (int64_t)B * S * Hq;
+  float* opart = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+  float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                        pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256))
+                             : nullptr;
+  const int groups = (B * splits + 7) / 8 * 8;
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
   const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
-  decode_kernel<256, 8, 2, kNW><<<(unsigned)(groups * n_qblk), C::THREADS, 0, static_cast<hipStream_t>(stream)>>>(
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  decode_kernel<256, 8, 2, kNW><<<(unsigned)(groups * n_qblk), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
       static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
-      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), n_qblk);
-  return pi::check_launch("decode_kernel");
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), n_qblk, splits, opart, mlpart);
+  pi_status st = pi::check_launch("decode_kernel");
+  if (st != PI_OK || splits == 1) return st;
+  decode_combine_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o_s),
+                                                                   splits, rows);
+  return pi::check_launch("decode_combine_kernel");
 }

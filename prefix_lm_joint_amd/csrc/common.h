@@ -64,6 +64,8 @@ void set_error(const char* fmt, ...);
 pi_status check_launch(const char* what);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+// Largest decode workspace any cache length can ask for at this batch shape.
+size_t decode_workspace_max(int B, int S, int Hq);
 }  // namespace pi
 
 #define PI_REQUIRE(cond, code, ...)     \

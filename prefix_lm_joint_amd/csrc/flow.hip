@@ -255,6 +255,8 @@ struct FlowWs {
   float* h;
   __bf16 *q, *k, *v, *o;
   float* vel;
+  void* dec;          // decode key-split partials
+  size_t dec_bytes;
   size_t total;
 };
 
@@ -273,6 +275,8 @@ FlowWs flow_layout(const pi_velocity_net* n, int B, int H, char* base) {
   w.v = reinterpret_cast<__bf16*>(take(2 * B * S * n->Hkv * n->d));
   w.o = reinterpret_cast<__bf16*>(take(2 * B * S * n->Hq * n->d));
   w.vel = reinterpret_cast<float*>(take(sizeof(float) * B * H * n->action_dim));
+  w.dec_bytes = pi::decode_workspace_max(B, (int)S, n->Hq);
+  w.dec = w.dec_bytes ? take(w.dec_bytes) : nullptr;
   w.total = off;
   return w;
 }
@@ -332,7 +336,8 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
     g.o2 = w.v;
     pi_status st = gemm<EPI_QKV, float, true>(g, s, "gemm_qkv");
     if (st != PI_OK) return st;
-    st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, s);
+    st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, w.dec, w.dec_bytes,
+                               s);
     if (st != PI_OK) return st;
     GemmArgs go{};
     go.a = w.o;

@@ -81,11 +81,16 @@ def test_decode_and_flow_reject_bad_arguments_before_launch():
     lib = Bd.lib()
     cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 4, 816, 1, 256, 816)
     dec = lambda **kw: lib.pi_suffix_decode_step(ctypes.byref(cache), kw.get("layer", 0), FAKE, FAKE, FAKE, FAKE,
-                                                 kw.get("B", 4), kw.get("S", 51), kw.get("Hq", 8), 0.0625, FAKE, None)
+                                                 kw.get("B", 4), kw.get("S", 51), kw.get("Hq", 8), 0.0625, FAKE,
+                                                 kw.get("ws", None), kw.get("ws_bytes", 0), None)
     assert dec(layer=18) == -1
     assert dec(B=3) == -1
     assert dec(S=129) == -1
     assert dec(Hq=4) == -2
+    # a usable but misaligned split workspace is rejected
+    need = lib.pi_decode_workspace_bytes(4, 51, 8, 816)
+    assert need > 0 and lib.pi_decode_workspace_bytes(64, 51, 8, 816) == 0
+    assert dec(ws=P(0x100010), ws_bytes=need) == -1
     assert lib.pi_euler_update(FAKE, FAKE, -0.1, -1, None) == -1
     assert lib.pi_flow_sample(None, None, None, None, None, FAKE, 1, 50, 32, 0, None, 0, None) == -1
     assert lib.pi_flow_sample(None, None, None, None, None, FAKE, 1, 50, 32, 10, None, 0, None) == -1  # no v_const

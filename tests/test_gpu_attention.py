@@ -205,10 +205,13 @@ def _cache_from(kl, vl, pm, length=None):
     return Bd.KVCache(bf16_dev(kl), bf16_dev(vl), u8_dev(pm), length)
 
 
-@pytest.mark.parametrize("seed,B,P,S", [(0, 4, 100, 51), (1, 3, 37, 9), (2, 9, 64, 33), (3, 2, 1, 1)])
-def test_decode_parity_small(seed, B, P, S):
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("seed,B,P,S", [(0, 4, 100, 51), (1, 3, 37, 9), (2, 9, 64, 33), (3, 2, 1, 1),
+                                        (4, 1, 816, 51)])
+def test_decode_parity_small(seed, B, P, S, split):
+    """Unsplit and key-split (small-batch) decode against the oracle."""
     Bd = _bd()
-    note(f"decode seed={seed} B={B} P={P} S={S}")
+    note(f"decode seed={seed} B={B} P={P} S={S} split={split}")
     r = np.random.default_rng(seed)
     layers = 2
     ck = I.bf16_normal(seed * 7 + 1, (layers, B, P, 1, 256))
@@ -220,11 +223,16 @@ def test_decode_parity_small(seed, B, P, S):
     ks = I.bf16_normal(seed * 7 + 4, (B, S, 1, 256))
     vs = I.bf16_normal(seed * 7 + 5, (B, S, 1, 256))
     cache = _cache_from(ck, cv, pm)
+    ws = Bd.decode_workspace(cache, S) if split else None
+    tiles = -(-P // 32) + -(-S // 32)
+    if split and B <= 4 and tiles >= 4:
+        assert ws is not None   # small batches with enough key tiles split their keys
     for layer in range(layers):
-        o = Bd.pi_suffix_decode_step(cache, layer, bf16_dev(qs), bf16_dev(ks), bf16_dev(vs), u8_dev(sar))
+        o = Bd.pi_suffix_decode_step(cache, layer, bf16_dev(qs), bf16_dev(ks), bf16_dev(vs), u8_dev(sar),
+                                     workspace=ws)
         torch.cuda.synchronize()
         want = A.cached_decode(f64(qs), f64(ks), f64(vs), f64(ck[layer]), f64(cv[layer]), pm, sar)
-        assert_close(host64(o), want, f"decode seed={seed} layer={layer}")
+        assert_close(host64(o), want, f"decode seed={seed} layer={layer} split={split}")
 
 
 def test_decode_matches_full_recompute():
@@ -238,10 +246,11 @@ def test_decode_matches_full_recompute():
     valid = w.input_mask()
     full = _prefill(q, k, v, valid, s)
     cache = _cache_from(k[None, :, :P], v[None, :, :P], valid[:, :P])
-    o = Bd.pi_suffix_decode_step(cache, 0, bf16_dev(q[:, P:]), bf16_dev(k[:, P:]), bf16_dev(v[:, P:]),
-                                 u8_dev(s.ar[P:]))
-    torch.cuda.synchronize()
-    assert_close(host64(o), host64(full[:, P:]), "decode vs joint prefill")
+    for ws in (None, Bd.decode_workspace(cache, s.n - P)):
+        o = Bd.pi_suffix_decode_step(cache, 0, bf16_dev(q[:, P:]), bf16_dev(k[:, P:]), bf16_dev(v[:, P:]),
+                                     u8_dev(s.ar[P:]), workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(host64(o), host64(full[:, P:]), f"decode vs joint prefill (split={ws is not None})")
 
 
 def test_prefill_writes_cache_for_decode():
