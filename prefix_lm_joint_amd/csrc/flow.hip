@@ -83,32 +83,31 @@ constexpr float kRmsEps = 1e-6f;
 
 // out[m][n] = sum_k r(A[m][k]) W[n][k]  (divided by rms(A[m]) when NORM).
 //
-// Workgroup tile 64 (n) x 64 (m).  The four waves split the contraction into four
-// contiguous ranges and each computes the whole 64 x 64 tile over its range, with
-// KB k-steps of loads in flight at a time; the four partial tiles are summed
-// through LDS and each wave finishes 16 rows.  This keeps the skinny products of
-// a small batch (M = 51 rows) from serialising on memory latency.  Products are
-// computed transposed (A operand = weights, B operand = activations) so a lane
-// holds four consecutive output columns of one row.
-constexpr int kPartStride = 68;  // LDS row stride (floats) of a 64 x 64 partial tile
-
-template <int EPI, typename TA, bool NORM>
-__global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
-  constexpr int KB = sizeof(TA) == 2 ? 4 : 2;   // k-steps of loads in flight
-  __shared__ float part[4][64 * kPartStride];
-  __shared__ float ssp[4][64];
+// Workgroup tile TN = 16*NT columns x 64 rows.  The NWV waves split the
+// contraction into NWV contiguous ranges and each computes the whole tile over
+// its range, with KB k-steps of loads in flight at a time; the partial tiles are
+// summed through LDS.  Small batches (M = 51 rows per sample) use narrow tiles and
+// eight waves, so many workgroups each wait on one short chain of loads instead
+// of a few workgroups serialising on memory latency.  Products are computed
+// transposed (A operand = weights, B operand = activations) so a lane holds four
+// consecutive output columns of one row.
+template <int EPI, typename TA, bool NORM, int NT, int NWV>
+__global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
+  constexpr int TN = 16 * NT;
+  constexpr int PS = TN + 4;                     // LDS row stride (floats) of a partial tile
+  constexpr int KB = sizeof(TA) == 2 ? 4 : 2;    // k-steps of loads in flight
+  __shared__ float part[NWV][64 * PS];
+  __shared__ float ssp[NWV][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 64;
+  const int n0 = blockIdx.x * TN;
   const int m0 = blockIdx.y * 64;
   const bool vec_ok = (p.K & 7) == 0;
 
-  const __bf16* wrow[4];
-  bool wok[4];
-  const TA* arow[4];
-  bool aok[4];
+  const __bf16* wrow[NT];
+  bool wok[NT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NT; ++j) {
     const int n = n0 + 16 * j + c;
     wok[j] = n < p.N;
     const __bf16* base = p.w0;
@@ -116,38 +115,42 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
     if (n >= p.n1 + p.n2) { base = p.w2; nn = n - p.n1 - p.n2; }
     else if (n >= p.n1) { base = p.w1; nn = n - p.n1; }
     wrow[j] = base + (int64_t)(wok[j] ? nn : 0) * p.K;
+  }
+  const TA* arow[4];
+  bool aok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
     const int m = m0 + 16 * j + c;
     aok[j] = m < p.M;
     arow[j] = static_cast<const TA*>(p.a) + (aok[j] ? p.amap(m) : 0) * p.K;
   }
 
-  f32x4 acc[4][4];
+  f32x4 acc[NT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[4] = {0.f, 0.f, 0.f, 0.f};
   float ss_w = 0.f;
 
   const int ksteps = (p.K + 31) / 32;
-  const int per = (ksteps + 3) / 4;
+  const int per = (ksteps + NWV - 1) / NWV;
   const int ks_lo = wave * per, ks_hi = min(ksteps, ks_lo + per);
   for (int ks0 = ks_lo; ks0 < ks_hi; ks0 += KB) {
-    bf16x8 wf[KB][4], af[KB][4];
+    bf16x8 wf[KB][NT], af[KB][4];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int k = (ks0 + u) * 32 + 8 * g;
       const bool live = ks0 + u < ks_hi;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wf[u][j] = (live && wok[j]) ? load_frag(wrow[j], k, p.K, vec_ok, ss_w) : bf16x8{};
-        af[u][j] = (live && aok[j]) ? load_frag(arow[j], k, p.K, vec_ok, ss[j]) : bf16x8{};
-      }
+      for (int j = 0; j < NT; ++j) wf[u][j] = (live && wok[j]) ? load_frag(wrow[j], k, p.K, vec_ok, ss_w) : bf16x8{};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) af[u][j] = (live && aok[j]) ? load_frag(arow[j], k, p.K, vec_ok, ss[j]) : bf16x8{};
     }
 #pragma unroll
     for (int u = 0; u < KB; ++u)
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn)
+      for (int jn = 0; jn < NT; ++jn)
 #pragma unroll
         for (int jm = 0; jm < 4; ++jm) acc[jn][jm] = mfma16x16x32(wf[u][jn], af[u][jm], acc[jn][jm]);
   }
@@ -155,10 +158,10 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
 
   // partial tiles and partial row sums of squares to LDS
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn)
+  for (int jn = 0; jn < NT; ++jn)
 #pragma unroll
     for (int jm = 0; jm < 4; ++jm)
-      *reinterpret_cast<f32x4*>(&part[wave][(16 * jm + c) * kPartStride + 16 * jn + 4 * g]) = acc[jn][jm];
+      *reinterpret_cast<f32x4*>(&part[wave][(16 * jm + c) * PS + 16 * jn + 4 * g]) = acc[jn][jm];
   if constexpr (NORM) {
 #pragma unroll
     for (int jm = 0; jm < 4; ++jm) {
@@ -168,24 +171,21 @@ __global__ void __launch_bounds__(256) gemm_kernel(GemmArgs p) {
   }
   __syncthreads();
 
-  // wave w finishes rows 16w .. 16w+15 of the tile
-  const int ml = 16 * wave + c;
-  const int m = m0 + ml;
-  float inv_rms = 1.f;
-  if constexpr (NORM) {
-    const float t = ssp[0][ml] + ssp[1][ml] + ssp[2][ml] + ssp[3][ml];
-    inv_rms = rsqrtf(t / (float)p.K + kRmsEps);
-  }
-  if (m >= p.M) return;
+  // finish: each task is four consecutive columns of one row
+  for (int task = threadIdx.x; task < 16 * TN; task += NWV * 64) {
+    const int ml = task / (TN / 4);
+    const int nl = 4 * (task % (TN / 4));
+    const int m = m0 + ml, nb = n0 + nl;
+    if (m >= p.M || nb >= p.N) continue;
+    f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * PS + nl]);
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn) {
-    const int nl = 16 * jn + 4 * g;
-    const int nb = n0 + nl;
-    if (nb >= p.N) continue;
-    f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * kPartStride + nl]);
+    for (int w = 1; w < NWV; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * PS + nl]);
+    if constexpr (NORM) {
+      float t = 0.f;
 #pragma unroll
-    for (int w = 1; w < 4; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * kPartStride + nl]);
-    r *= inv_rms;
+      for (int w = 0; w < NWV; ++w) t += ssp[w][ml];
+      r *= rsqrtf(t / (float)p.K + kRmsEps);
+    }
     if constexpr (EPI == EPI_QKV) {
       __bf16* dst;
       if (nb < p.n1) dst = p.o0 + (int64_t)m * p.n1 + nb;
@@ -244,10 +244,17 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
   }
 }
 
+// Tile choice: narrow tiles and eight waves for the few rows of a small batch,
+// 64 x 64 tiles with four waves once the rows alone give enough workgroups.
 template <int EPI, typename TA, bool NORM>
 pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
-  dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-  gemm_kernel<EPI, TA, NORM><<<grid, 256, 0, s>>>(a);
+  if (a.M <= 256) {
+    dim3 grid((a.N + 31) / 32, (a.M + 63) / 64);
+    gemm_kernel<EPI, TA, NORM, 2, 8><<<grid, 512, 0, s>>>(a);
+  } else {
+    dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
+    gemm_kernel<EPI, TA, NORM, 4, 4><<<grid, 256, 0, s>>>(a);
+  }
   return pi::check_launch(name);
 }
 
