@@ -4,27 +4,33 @@
 // §1.5, §1.6): per (sample, query token, head) one softmax over every visible key
 // of the concatenated prefix+suffix pool, query head h reading KV head
 // floor(h*Hkv/Hq).  Masked keys are excluded by selection (score -inf before the
-// running max, weight exactly 0, never multiplied into V).
+// maximum, weight exactly 0).
 //
 // Kernel organisation (one engine for prefill and cached decode):
 //   * A workgroup owns NW waves x NR row tiles x 16 query rows.  With one KV head
 //     and 8 query heads a row is a (token, head) pair: a 16-row tile holds two
-//     tokens x 8 heads, so every K/V element loaded is used by 8 heads.
-//   * K/V tiles of 32 keys are staged in LDS row-major (padded rows).
+//     tokens x 8 heads, so every K/V element loaded serves 8 heads.
+//   * K/V tiles of 32 keys go from global memory straight into LDS (buffer loads
+//     with the LDS destination: no registers, no VALU), double-buffered so tile
+//     i+1 streams in while tile i is computed, one barrier per tile.  A padded or
+//     masked-out key is given an out-of-range offset, which the buffer unit turns
+//     into zeros: whatever a padded slot holds never reaches a product.
+//   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so that both
+//     matrix-core operand reads are bank-conflict free (the swizzle is applied to
+//     the global source chunk each lane fetches).
 //   * Products are computed transposed: S^T = K Q^T (A = K from LDS, B = Q held in
 //     registers), then O^T += V^T P^T with P^T taken straight from the S^T
-//     accumulators (no LDS round trip).  The V^T operand is read with gfx950's
-//     transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group, lane i
-//     receives element (i % 4) of the 4 elements addressed by lanes 4k + i/4,
-//     k = 0..3, so pointing lane j at row 4g + j/4, columns 4*(j%4).. of the V tile
-//     hands lane i the values of 4 keys at one d -- the keys its S^T accumulators
-//     cover.
-//   * Online softmax in base 2 with per-row max/sum reduced across the four
-//     16-lane groups of the wave.
+//     accumulators.  The V^T operand is read with the transposing LDS load
+//     (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+//     (i % 4) of the 4 elements addressed by lanes 4k + i/4, k = 0..3, so pointing
+//     lane j at row 4g + j/4, columns 4*(j%4).. of the V tile hands lane i the
+//     values of 4 keys at one d -- the keys its S^T accumulators cover.
+//   * Softmax in base 2 against a per-row reference maximum fixed at the row's
+//     first visible tile (see kMaxGrowth); the accumulators are never rescaled in
+//     the loop.
 //   * Key tiles classified EMPTY by the mask builder are skipped; FULL tiles skip
-//     the per-pair rule.
-//   * Workgroups of one (sample, KV head) are placed on one XCD so their K/V
-//     reads share that XCD's L2.
+//     the per-pair rule.  Workgroups of one (sample, KV head) are placed on one
+//     XCD so their K/V reads share that XCD's L2.
 #include "common.h"
 
 #include <math.h>
@@ -33,7 +39,8 @@
 
 namespace {
 
-constexpr int TK = 32;  // keys per tile
+constexpr int TK = 32;             // keys per tile
+constexpr int kMaxTiles = 512;     // longest key sequence a workgroup walks: 16384 tokens
 
 template <int D, int G, int NR, int NW>
 struct Cfg {
@@ -42,81 +49,86 @@ struct Cfg {
   static constexpr int TOK = ROWS / G;        // query tokens per workgroup
   static constexpr int THREADS = NW * PI_WAVE;
   static_assert(ROWS % G == 0, "rows must cover whole tokens");
-  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+  static_assert(D == 256 || D == 64, "head dim 256 or 64");
 };
 
-// LDS row strides (bf16 elements).  K rows are padded by 16 B: the 16 rows a
-// fragment read touches then start 4 banks apart (conflict-free 16-byte reads).
-// V rows are padded by 32 B: the 4 rows x 32 bytes a transposing read of one
-// 16-lane group touches then fall on disjoint banks.
+// ---------------------------------------------------------------------------
+// Swizzled LDS tile.  A row holds D bf16 (CHR chunks of 16 bytes); logical chunk
+// x of row r sits at physical chunk x ^ f(r).
+//   K fragment read: 16 lanes read rows r0..r0+15 at one logical chunk.  d = 256:
+//     f_K(r) = r & 15 spreads them over 16 distinct chunks (all 64 banks);
+//     d = 64 (rows of 32 banks): f_K(r) = (r >> 1) & 7 does the same.
+//   V transposing read: 16 lanes read 4 rows x 32 bytes (two chunks).
+//     d = 256: f_V(r) = 2r & 31; d = 64: f_V(r) = r & 6; 32 lanes (8 rows) then
+//     cover all 64 banks once.
+// ---------------------------------------------------------------------------
 template <int D>
-struct Lds {
-  static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = D + 16;
+struct Tile {
+  static constexpr int CHR = D / 8;                 // 16-byte chunks per row
+  static constexpr int RPI = 64 / CHR;              // rows per 64-lane load instruction
+  static constexpr int INSTS = TK / RPI;            // load instructions per tensor tile
+  __device__ static __forceinline__ int fk(int r) { return D == 256 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static __forceinline__ int fv(int r) { return D == 256 ? ((2 * r) & 31) : (r & 6); }
 };
 
 template <int D>
-struct Smem {
-  alignas(16) __bf16 k[TK * Lds<D>::KSTR];
-  alignas(16) __bf16 v[TK * Lds<D>::VSTR];
-  alignas(16) uint32_t kw[TK];
+struct Stage {
+  alignas(16) __bf16 k[TK * D];
+  alignas(16) __bf16 v[TK * D];
+  alignas(16) uint32_t w[64];   // per-key mask words (lanes >= 32 land as zeros)
 };
 
 #define PI_LDS __attribute__((address_space(3)))
 
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+extern "C" __device__ void pi_buffer_load_lds(i32x4 rsrc, PI_LDS uint32_t* lds, int size, int voffset, int soffset,
+                                              int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Buffer resource over [base, base + 2 GiB): any offset >= 0x7FFFFFFF reads as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
+  struct __attribute__((packed)) Res {
+    const void* p;
+    uint32_t range;
+    uint32_t cfg;
+  } r{base, 0x7FFFFFFFu, 0x00020000u};
+  i32x4 v = __builtin_bit_cast(i32x4, r);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  return v;
+}
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ PI_LDS uint32_t* lds_u32(const void* p) {
+  return (PI_LDS uint32_t*)(const_cast<void*>(p));
+}
+
+// Issue this wave's share of the direct-to-LDS loads of one K/V tile: keys whose
+// bit is clear in `keymask` (past the end, padding) are fetched from an
+// out-of-range offset and land as zeros.  tsb = bytes between consecutive tokens.
+template <int D, int NW>
+__device__ __forceinline__ void issue_kv(Stage<D>& st, i32x4 rk, i32x4 rv, int key0, int tsb, uint32_t keymask) {
+  using T = Tile<D>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int p = lane % T::CHR;
+#pragma unroll
+  for (int q = wave; q < T::INSTS; q += NW) {
+    const int r = q * T::RPI + lane / T::CHR;
+    const bool live = (keymask >> r) & 1u;
+    const uint32_t base = (uint32_t)(key0 + r) * (uint32_t)tsb;
+    const uint32_t ok = live ? base + 16u * (uint32_t)(p ^ T::fk(r)) : kOOB;
+    const uint32_t ov = live ? base + 16u * (uint32_t)(p ^ T::fv(r)) : kOOB;
+    pi_buffer_load_lds(rk, lds_u32(&st.k[q * T::RPI * D]), 16, (int)ok, 0, 0, 0);
+    pi_buffer_load_lds(rv, lds_u32(&st.v[q * T::RPI * D]), 16, (int)ov, 0, 0, 0);
+  }
+}
+
+// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0 only).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Transposing LDS read of 4 bf16 (see the header comment for the lane mapping).
 __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PI_LDS bf16x4*)(const_cast<__bf16*>(p)));
-}
-
-// Register staging of one K/V tile (software pipelining: the next tile's global
-// loads are issued before the current tile is computed, and land in LDS after).
-// Task = (key j, 16-byte chunk c), c fastest: coalesced rows for both tensors.
-template <int D, int THREADS>
-struct KVRegs {
-  static constexpr int CH = D / 8;                                // 16-byte chunks per row
-  static constexpr int T = (TK * CH + THREADS - 1) / THREADS;     // tasks per thread
-  u32x4 k[T];
-  u32x4 v[T];
-};
-
-// Issue the global loads of a tile: keys whose bit is set in `loadmask` are read,
-// the others become zero.  `tok_stride` is the element distance between tokens.
-template <int D, int THREADS>
-__device__ __forceinline__ void load_kv(KVRegs<D, THREADS>& r, const __bf16* __restrict__ kb,
-                                        const __bf16* __restrict__ vb, int64_t tok_stride, uint32_t loadmask) {
-  using R = KVRegs<D, THREADS>;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < R::T; ++i) {
-    const int task = threadIdx.x + i * THREADS;
-    const int j = task / R::CH, c = task % R::CH;
-    r.k[i] = zero;
-    r.v[i] = zero;
-    if (task < TK * R::CH && ((loadmask >> j) & 1u)) {
-      r.k[i] = *reinterpret_cast<const u32x4*>(kb + j * tok_stride + 8 * c);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vb + j * tok_stride + 8 * c);
-    }
-  }
-}
-
-// Write a loaded tile to LDS, both tensors row-major; keys whose bit is clear in
-// `keymask` are written as zeros, so whatever a padded slot holds (uninitialised
-// memory, NaN) never reaches a product.
-template <int D, int THREADS>
-__device__ __forceinline__ void store_kv(Smem<D>& sm, const KVRegs<D, THREADS>& r, uint32_t keymask) {
-  using R = KVRegs<D, THREADS>;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < R::T; ++i) {
-    const int task = threadIdx.x + i * THREADS;
-    const int j = task / R::CH, c = task % R::CH;
-    if (task < TK * R::CH) {
-      const bool keep = (keymask >> j) & 1u;
-      *reinterpret_cast<u32x4*>(&sm.k[j * Lds<D>::KSTR + 8 * c]) = keep ? r.k[i] : zero;
-      *reinterpret_cast<u32x4*>(&sm.v[j * Lds<D>::VSTR + 8 * c]) = keep ? r.v[i] : zero;
-    }
-  }
 }
 
 // Per-wave state of the online softmax.  m is each row's reference maximum
@@ -146,8 +158,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // One 32-key tile for one wave.  cls: PI_TILE_FULL or PI_TILE_PARTIAL.
 template <int D, int NR>
-__device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>& st, int cls,
-                                            uint32_t forbid, float scale_log2) {
+__device__ __forceinline__ void attend_tile(const Stage<D>& sm, WaveState<D, NR>& st, int cls, uint32_t forbid,
+                                            float scale_log2) {
+  using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   f32x4 s[NR][2];
@@ -155,11 +168,13 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // S^T = K Q^T: lane (c, g) reads key row kt*16 + c, logical chunk 4 ds + g
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[(kt * 16 + c) * Lds<D>::KSTR + ds * 32 + 8 * g]);
+      const int row = kt * 16 + c;
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[row * D + 8 * ((4 * ds + g) ^ T::fk(row))]);
 #pragma unroll
       for (int r = 0; r < NR; ++r) s[r][kt] = mfma16x16x32(a, st.qf[r][ds], s[r][kt]);
     }
@@ -170,7 +185,7 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t wk = sm.kw[kt * 16 + 4 * g + i];
+        const uint32_t wk = sm.w[kt * 16 + 4 * g + i];
 #pragma unroll
         for (int r = 0; r < NR; ++r)
           if (!pair_visible(st.wq[r], wk, forbid)) s[r][kt][i] = NEG_INF;
@@ -188,6 +203,12 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
     st.mobs[r] = fmaxf(st.mobs[r], mt);
     st.m[r] = (st.m[r] == NEG_INF) ? mt : st.m[r];
   }
+  // V^T operand rows for this lane: keys 4g + c/4 and 16 + 4g + c/4
+  const int vr0 = 4 * g + (c >> 2), vr1 = vr0 + 16;
+  const __bf16* v0 = &sm.v[vr0 * D + 4 * (c & 1)];
+  const __bf16* v1 = &sm.v[vr1 * D + 4 * (c & 1)];
+  const int fv0 = T::fv(vr0), fv1 = T::fv(vr1);
+  const int csel = (c & 3) >> 1;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     // a row that has seen no visible key keeps m = -inf: use 0 so masked weights are exp2(-inf) = 0
@@ -203,24 +224,21 @@ __device__ __forceinline__ void attend_tile(const Smem<D>& sm, WaveState<D, NR>&
         lsum += bf2f(pb);
       }
     st.l[r] += lsum;
-    // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]; the A operand of
-    // lane (c, g) is keys {4g..4g+3, 16+4g..16+4g+3} at d = 16 dt + c
-    const __bf16* vrow0 = &sm.v[(4 * g + (c >> 2)) * Lds<D>::VSTR + 4 * (c & 3)];
-    const __bf16* vrow1 = vrow0 + 16 * Lds<D>::VSTR;
+    // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const bf16x4 lo = lds_read_tr4(vrow0 + 16 * dt);
-      const bf16x4 hi = lds_read_tr4(vrow1 + 16 * dt);
+      const int lc = 2 * dt + csel;   // logical chunk holding columns 16 dt + 4 (c & 3) ..
+      const bf16x4 lo = lds_read_tr4(v0 + 8 * (lc ^ fv0));
+      const bf16x4 hi = lds_read_tr4(v1 + 8 * (lc ^ fv1));
       const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       st.o[r][dt] = mfma16x16x32(a, pf, st.o[r][dt]);
     }
   }
 }
 
-// True if a row's maximum grew past its reference by more than kMaxGrowth; in that
-// case the state is reset with the reference set to the true maximum.
+// True if a row's maximum grew past its reference by more than kMaxGrowth.
 template <int D, int NR>
-__device__ __forceinline__ bool needs_rerun(WaveState<D, NR>& st) {
+__device__ __forceinline__ bool needs_rerun(const WaveState<D, NR>& st) {
   bool bad = false;
 #pragma unroll
   for (int r = 0; r < NR; ++r) bad |= st.mobs[r] > st.m[r] + kMaxGrowth;
@@ -238,18 +256,6 @@ __device__ __forceinline__ void reset_for_rerun(WaveState<D, NR>& st) {
   }
 }
 
-// Workgroup placement: workgroups are dispatched round-robin over the 8 XCDs;
-// give every (sample, KV head) group's `per_group` workgroups one XCD.
-__device__ __forceinline__ void xcd_place(int n_groups, int per_group, int& group, int& sub) {
-  const int id = blockIdx.x;
-  const int xcd = id & 7;
-  const int k = id >> 3;
-  const int slot = k / per_group;
-  sub = k % per_group;
-  group = slot * 8 + xcd;
-  (void)n_groups;
-}
-
 template <int D, int NR>
 __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
 #pragma unroll
@@ -262,7 +268,17 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
   }
 }
 
-// Normalise and store O rows.  row_ptr(r) gives the output row base or nullptr.
+// Workgroup placement: workgroups are dispatched round-robin over the 8 XCDs;
+// give every group's `per_group` workgroups one XCD.
+__device__ __forceinline__ void xcd_place(int per_group, int& group, int& sub) {
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int k = id >> 3;
+  sub = k % per_group;
+  group = (k / per_group) * 8 + xcd;
+}
+
+// Normalise and store O rows (row_base[r] = output row or nullptr).
 template <int D, int NR>
 __device__ __forceinline__ void store_rows(WaveState<D, NR>& st, __bf16* const* row_base) {
   const int lane = threadIdx.x & 63;
@@ -283,11 +299,7 @@ __device__ __forceinline__ void store_rows(WaveState<D, NR>& st, __bf16* const* 
   }
 }
 
-// Longest key sequence a workgroup walks (tiles of 32 keys): 16384 tokens.
-constexpr int kMaxTiles = 512;
-
-// Row setup shared by both kernels: Q fragments into registers, the row's
-// query word, and the output row base (nullptr for rows past the end).
+// Row setup: Q fragments into registers, the row's query word and output row.
 template <int D, int G, int NR, int ROWS_W>
 __device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_base, const __bf16* __restrict__ q,
                                           __bf16* __restrict__ o, int64_t tok_base, int ntok, int Hq, int head0,
@@ -314,8 +326,9 @@ __device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_bas
 
 // ---------------------------------------------------------------------------
 // Prefill: grid = ceil(B*Hkv / 8) * 8 groups x n_qblk workgroups (XCD-placed).
-// Wave 0 first compacts the workgroup's non-EMPTY key tiles into an LDS list;
-// the loop then prefetches tile i+1 into registers while tile i is computed.
+// Up front the workgroup computes every key tile's validity bitmap and compacts
+// its non-EMPTY tiles into an LDS list; the loop then streams tile i+1 into the
+// other LDS stage while tile i is computed.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NR, int NW>
 __global__ void __launch_bounds__(NW * 64)
@@ -324,17 +337,26 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
                uint32_t forbid, int n_qblk) {
   using C = Cfg<D, G, NR, NW>;
-  __shared__ Smem<D> sm;
+  __shared__ Stage<D> stage[2];
+  __shared__ uint32_t kmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ int tcount;
   int group, qblk;
-  xcd_place(B * Hkv, n_qblk, group, qblk);
+  xcd_place(n_qblk, group, qblk);
   if (group >= B * Hkv) return;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
   const uint32_t* tk = tok + (size_t)b * L;
 
+  // validity bitmap of every key tile (one ballot per 32 keys)
+  for (int base = wave * 64; base < n_kt * TK; base += NW * 64) {
+    const int key = base + lane;
+    const bool valid = key < L && (tk[key] & 1u);
+    const unsigned long long bal = __ballot(valid);
+    if (lane == 0) kmask[base / TK] = (uint32_t)bal;
+    if (lane == 32 && base / TK + 1 < n_kt) kmask[base / TK + 1] = (uint32_t)(bal >> 32);
+  }
   if (wave == 0) {
     const int qt_lo = tok0 / PI_MASK_TILE_Q;
     const int qt_hi = min(n_qt, (tok0 + C::TOK + PI_MASK_TILE_Q - 1) / PI_MASK_TILE_Q);
@@ -364,30 +386,27 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   __syncthreads();
   const int count = tcount;
 
-  const int64_t tstride = (int64_t)Hkv * D;
-  const __bf16* kb = k + ((size_t)b * L * Hkv + kvh) * D;
-  const __bf16* vb = v + ((size_t)b * L * Hkv + kvh) * D;
-  KVRegs<D, C::THREADS> regs;
-  uint32_t wnext = 0u;
+  const i32x4 rk = make_rsrc(k + ((size_t)b * L * Hkv + kvh) * D);
+  const i32x4 rv = make_rsrc(v + ((size_t)b * L * Hkv + kvh) * D);
+  const i32x4 rw = make_rsrc(tk);
+  const int tsb = Hkv * D * 2;
   auto issue = [&](int i) {
-    const int key0 = (int)(tlist[i] & 0xFFFFu) * TK;
-    const int nvalid = min(TK, L - key0);
-    wnext = lane < nvalid ? tk[key0 + lane] : 0u;
-    load_kv<D, C::THREADS>(regs, kb + key0 * tstride, vb + key0 * tstride, tstride,
-                           nvalid == TK ? 0xFFFFFFFFu : ((1u << nvalid) - 1u));
+    Stage<D>& sg = stage[i & 1];
+    const int kt = (int)(tlist[i] & 0xFFFFu);
+    const int key0 = kt * TK;
+    issue_kv<D, NW>(sg, rk, rv, key0, tsb, kmask[kt]);
+    if (wave == NW - 1) {
+      const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
+      pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
+    }
   };
   auto run = [&]() {
     if (count > 0) issue(0);
     for (int i = 0; i < count; ++i) {
-      const int cls = (int)((tlist[i] >> 16) & 0xFFu);
-      const uint32_t wcur = wnext;
-      const uint32_t keymask = (uint32_t)__ballot(wcur & 1u);
-      __syncthreads();
-      store_kv<D, C::THREADS>(sm, regs, keymask);
-      if (threadIdx.x < TK) sm.kw[threadIdx.x] = wcur;
+      wait_vmem();
       __syncthreads();
       if (i + 1 < count) issue(i + 1);
-      attend_tile<D, NR>(sm, st, cls, forbid, scale_log2);
+      attend_tile<D, NR>(stage[i & 1], st, (int)((tlist[i] >> 16) & 0xFFu), forbid, scale_log2);
     }
   };
   run();
@@ -399,12 +418,14 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
 }
 
 // ---------------------------------------------------------------------------
-// Cached suffix decode (Hq = 8, Hkv = 1, d = 256): grid = ceil(B/8)*8 x n_qblk.
-// Keys: valid prefix slots of the cache layer, then the suffix's own K/V.
-// Query/key words reuse the prefill rule with bid 0 for every prefix slot and
-// 1 + cumsum(suffix_ar) for suffix tokens.  The per-tile validity of the prefix
-// slots is read once up front, so fully padded tiles are never fetched and
-// padded slots inside a tile are neither read nor used.
+// Cached suffix decode (Hq = 8, Hkv = 1, d = 256): grid = ceil(B*splits/8)*8 x
+// n_qblk.  Keys: valid prefix slots of the cache layer, then the suffix's own
+// K/V.  Query/key words reuse the prefill rule with bid 0 for every prefix slot
+// and 1 + cumsum(suffix_ar) for suffix tokens.  The per-tile validity of the
+// prefix slots is read once up front, so fully padded tiles are never fetched
+// and padded slots inside a tile are neither read nor used.  With n_split > 1
+// the workgroup covers a contiguous share of the tile list and writes an
+// unnormalised partial for decode_combine_kernel.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NR, int NW>
 __global__ void __launch_bounds__(NW * 64)
@@ -416,14 +437,14 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
-  __shared__ Smem<D> sm;
+  __shared__ Stage<D> stage[2];
   __shared__ uint32_t sbid[128];
   __shared__ uint32_t pmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ uint32_t tmask[kMaxTiles];
   __shared__ int tcount;
   int grp, qblk;
-  xcd_place(B * n_split, n_qblk, grp, qblk);
+  xcd_place(n_qblk, grp, qblk);
   if (grp >= B * n_split) return;
   const int b = grp / n_split, split = grp % n_split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -489,35 +510,30 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   __bf16* row_base[NR];
   load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, sbid);
 
-  const __bf16* kb = ck + (size_t)b * cap * D;
-  const __bf16* vb = cv + (size_t)b * cap * D;
-  const __bf16* ksb = ks + (size_t)b * S * D;
-  const __bf16* vsb = vs + (size_t)b * S * D;
-  KVRegs<D, C::THREADS> regs;
+  const i32x4 rk = make_rsrc(ck + (size_t)b * cap * D);
+  const i32x4 rv = make_rsrc(cv + (size_t)b * cap * D);
+  const i32x4 rks = make_rsrc(ks + (size_t)b * S * D);
+  const i32x4 rvs = make_rsrc(vs + (size_t)b * S * D);
   auto issue = [&](int i) {
+    Stage<D>& sg = stage[i & 1];
     const uint32_t d = tlist[i];
     const int key0 = (int)(d & 0xFFFFu) * TK;
     const bool suffix = (d >> 24) & 1u;
-    load_kv<D, C::THREADS>(regs, (suffix ? ksb : kb) + (size_t)key0 * D, (suffix ? vsb : vb) + (size_t)key0 * D, D,
-                           tmask[i]);
+    const uint32_t keymask = tmask[i];
+    if (suffix) issue_kv<D, NW>(sg, rks, rvs, key0, D * 2, keymask);
+    else issue_kv<D, NW>(sg, rk, rv, key0, D * 2, keymask);
+    if (threadIdx.x < TK) {
+      const uint32_t bit = (keymask >> threadIdx.x) & 1u;
+      sg.w[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
+    }
   };
   auto run = [&]() {
     if (i_lo < i_hi) issue(i_lo);
     for (int i = i_lo; i < i_hi; ++i) {
-      const uint32_t d = tlist[i];
-      const int cls = (int)((d >> 16) & 0xFFu);
-      const bool suffix = (d >> 24) & 1u;
-      const int key0 = (int)(d & 0xFFFFu) * TK;
-      const uint32_t keymask = tmask[i];
-      __syncthreads();
-      store_kv<D, C::THREADS>(sm, regs, keymask);
-      if (threadIdx.x < TK) {
-        const uint32_t bit = (keymask >> threadIdx.x) & 1u;
-        sm.kw[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
-      }
+      wait_vmem();
       __syncthreads();
       if (i + 1 < i_hi) issue(i + 1);
-      attend_tile<D, NR>(sm, st, cls, 0u, scale_log2);
+      attend_tile<D, NR>(stage[i & 1], st, (int)((tlist[i] >> 16) & 0xFFu), 0u, scale_log2);
     }
   };
   run();
@@ -550,7 +566,9 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
 
 // Merge the key splits of the decode: for each (sample, token, head) row,
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  One wave
-// per row, four d per lane (d = 256).
+// per row, four d per lane (d = 256); all of a row's loads are issued at once.
+constexpr int kMaxSplit = 16;
+
 __global__ void __launch_bounds__(256)
 decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__ mlpart,
                       __bf16* __restrict__ os, int n_split, int64_t rows) {
@@ -558,16 +576,29 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  float m[kMaxSplit], l[kMaxSplit];
+  f32x4 op[kMaxSplit];
   float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, mlpart[2 * (sp * rows + row)]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    m[sp] = -INFINITY;
+    l[sp] = 0.f;
+    op[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (sp < n_split) {
+      m[sp] = mlpart[2 * (sp * rows + row)];
+      l[sp] = mlpart[2 * (sp * rows + row) + 1];
+      op[sp] = *reinterpret_cast<const f32x4*>(opart + (sp * rows + row) * D + 4 * lane);
+    }
+    M = fmaxf(M, m[sp]);
+  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float m = mlpart[2 * (sp * rows + row)];
-      const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-      L += w * mlpart[2 * (sp * rows + row) + 1];
-      acc += w * *reinterpret_cast<const f32x4*>(opart + (sp * rows + row) * D + 4 * lane);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+      const float w = (m[sp] == -INFINITY) ? 0.f : fast_exp2(m[sp] - M);
+      L += w * l[sp];
+      acc += w * op[sp];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -592,25 +623,51 @@ __global__ void cache_write_kernel(const u32x4* __restrict__ k, const u32x4* __r
   cv[dst] = v[src];
 }
 
-constexpr int kNW = 4;
+// Launch shapes.  GQA 8:1 at d = 256: eight waves of one 16-row tile each (two
+// waves per SIMD, 16 query tokens x 8 heads per workgroup).  MHA at d = 64: four
+// waves of four row tiles.
+constexpr int kNR256 = 1, kNW256 = 8;
+constexpr int kNR64 = 4, kNW64 = 4;
+using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
 
-template <int D, int G, int NR>
+template <int D, int G, int NR, int NW>
 pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
                          float scale, const pi_mask* m, hipStream_t s) {
-  using C = Cfg<D, G, NR, kNW>;
+  using C = Cfg<D, G, NR, NW>;
   const int n_qblk = (L + C::TOK - 1) / C::TOK;
   const int groups = (B * Hkv + 7) / 8 * 8;
   const int64_t grid = (int64_t)groups * n_qblk;
   PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "prefill: grid too large");
   const float scale_log2 = scale * 1.4426950408889634f;
-  prefill_kernel<D, G, NR, kNW><<<(unsigned)grid, C::THREADS, 0, s>>>(
+  prefill_kernel<D, G, NR, NW><<<(unsigned)grid, C::THREADS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), B, L, Hq, Hkv, scale_log2, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits,
       n_qblk);
   return pi::check_launch("prefill_kernel");
 }
 
+// Key splits for a decode of B samples: enough workgroups to cover the chip
+// (about 256) while giving each split at least two key tiles.
+int decode_splits(int B, int S, int len) {
+  const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
+  const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
+  const int by_chip = 256 / std::max(1, B * n_qblk);
+  return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
+}
+
+size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)B * S * Hq;
+  return pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256) + (size_t)splits * rows * 2 * sizeof(float);
+}
+
 }  // namespace
+
+size_t pi::decode_workspace_max(int B, int S, int Hq) {
+  const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
+  const int splits = std::max(1, std::min(kMaxSplit, 256 / std::max(1, B * n_qblk)));
+  return decode_ws_bytes(B, S, Hq, splits);
+}
 
 extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
                                            int Hkv, int d, float scale, const pi_mask* mask, void* o,
@@ -631,6 +688,8 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   PI_REQUIRE(gqa8 || mha64, PI_ERR_UNSUPPORTED,
              "pi_joint_attn_prefill: unsupported (Hq=%d, Hkv=%d, d=%d); supported: (8,1,256) and (H,H,64)", Hq,
              Hkv, d);
+  PI_REQUIRE((int64_t)L * Hkv * d * 2 < 0x7FFFFFF0ll, PI_ERR_UNSUPPORTED,
+             "pi_joint_attn_prefill: one sample's K/V exceeds 2 GiB");
   if (cache) {
     PI_REQUIRE(cache->k && cache->v, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: cache has null k/v");
     PI_REQUIRE(cache->B == B && cache->Hkv == Hkv && cache->d == d && layer >= 0 && layer < cache->layers &&
@@ -638,8 +697,8 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
                PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: cache shape does not match (layer %d)", layer);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  pi_status st = gqa8 ? launch_prefill<256, 8, 2>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s)
-                      : launch_prefill<64, 1, 4>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s);
+  pi_status st = gqa8 ? launch_prefill<256, 8, kNR256, kNW256>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s)
+                      : launch_prefill<64, 1, kNR64, kNW64>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s);
   if (st != PI_OK || !cache) return st;
   const int row_chunks = Hkv * d / 8;
   const int64_t total = (int64_t)B * cache->len * row_chunks;
@@ -651,35 +710,6 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
       static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(ckl),
       reinterpret_cast<u32x4*>(cvl), L, cache->capacity, cache->len, row_chunks, total);
   return pi::check_launch("cache_write_kernel");
-}
-
-namespace {
-
-constexpr int kMaxSplit = 16;
-
-// Key splits for a decode of B samples: enough workgroups to cover the chip
-// (about 256) while giving each split at least two key tiles.
-int decode_splits(int B, int S, int len) {
-  using C = Cfg<256, 8, 2, kNW>;
-  const int n_qblk = (S + C::TOK - 1) / C::TOK;
-  const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
-  const int by_chip = 256 / std::max(1, B * n_qblk);
-  return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
-}
-
-size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
-  if (splits <= 1) return 0;
-  const size_t rows = (size_t)B * S * Hq;
-  return pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256) + (size_t)splits * rows * 2 * sizeof(float);
-}
-
-}  // namespace
-
-size_t pi::decode_workspace_max(int B, int S, int Hq) {
-  using C = Cfg<256, 8, 2, kNW>;
-  const int n_qblk = (S + C::TOK - 1) / C::TOK;
-  const int splits = std::max(1, std::min(kMaxSplit, 256 / std::max(1, B * n_qblk)));
-  return decode_ws_bytes(B, S, Hq, splits);
 }
 
 extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
@@ -709,7 +739,7 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
   PI_REQUIRE(Hq == 8 && cache->Hkv == 1 && cache->d == 256, PI_ERR_UNSUPPORTED,
              "pi_suffix_decode_step: supported heads are Hq=8, Hkv=1, d=256 (got %d, %d, %d)", Hq, cache->Hkv,
              cache->d);
-  using C = Cfg<256, 8, 2, kNW>;
+  using C = CfgG8;
   const int n_qblk = (S + C::TOK - 1) / C::TOK;
   int splits = decode_splits(B, S, cache->len);
   const size_t need = decode_ws_bytes(B, S, Hq, splits);
@@ -726,7 +756,7 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
   const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  decode_kernel<256, 8, 2, kNW><<<(unsigned)(groups * n_qblk), C::THREADS, 0, s>>>(
+  decode_kernel<256, 8, kNR256, kNW256><<<(unsigned)(groups * n_qblk), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
       static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
       scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), n_qblk, splits, opart, mlpart);
