@@ -11,10 +11,11 @@
 //     and 8 query heads a row is a (token, head) pair: a 16-row tile holds two
 //     tokens x 8 heads, so every K/V element loaded serves 8 heads.
 //   * K/V tiles of 32 keys go from global memory straight into LDS (buffer loads
-//     with the LDS destination: no registers, no VALU), double-buffered so tile
-//     i+1 streams in while tile i is computed, one barrier per tile.  A padded or
-//     masked-out key is given an out-of-range offset, which the buffer unit turns
-//     into zeros: whatever a padded slot holds never reaches a product.
+//     with the LDS destination: no registers, no VALU) over three stages, one
+//     barrier per tile: while tile i's softmax and PV run, tile i+1's scores are
+//     computed and tile i+2 streams in.  A padded or masked-out key is given an
+//     out-of-range offset, which the buffer unit turns into zeros: whatever a
+//     padded slot holds never reaches a product.
 //   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so that both
 //     matrix-core operand reads are bank-conflict free (the swizzle is applied to
 //     the global source chunk each lane fetches).
@@ -133,7 +134,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
 
 // Per-wave state of the online softmax.  m is each row's reference maximum
 // (scores already multiplied by scale*log2(e)), fixed at the row's first tile
-// with a visible key; mobs is the true running maximum.
+// with a visible key and the same in the four lanes that share a row; mobs is
+// this lane's running maximum over its own scores (reduced across the row only
+// at the end); all_set is true once every row of the wave has its reference.
 template <int D, int NR>
 struct WaveState {
   bf16x8 qf[NR][D / 32];
@@ -142,6 +145,7 @@ struct WaveState {
   float mobs[NR];
   float l[NR];
   uint32_t wq[NR];
+  bool all_set;
 };
 
 // Weights are exp2(score - m) against a reference maximum m fixed at a row's
@@ -156,29 +160,66 @@ constexpr float kMaxGrowth = 64.0f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One 32-key tile for one wave.  cls: PI_TILE_FULL or PI_TILE_PARTIAL.
-template <int D, int NR>
-__device__ __forceinline__ void attend_tile(const Stage<D>& sm, WaveState<D, NR>& st, int cls, uint32_t forbid,
-                                            float scale_log2) {
+// Byte offsets, within a stage, of this lane's LDS operand reads; computed once.
+//   K (S^T = K Q^T, A operand): lane (c, g) reads key row kt*16 + c, logical chunk
+//     4 ds + g; the swizzle term f_K(row) is the same for kt = 0 and 1, so kt = 1
+//     is a fixed +16 rows.
+//   V (transposing read): rows 4g + c/4 (+16 for the second read, same swizzle
+//     term), logical chunk 2 dt + (c & 3) / 2, half c & 1.
+template <int D>
+struct LaneOffsets {
+  uint32_t k[D / 32];
+  uint32_t v[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffsets<D> lane_offsets() {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
-  f32x4 s[NR][2];
+  LaneOffsets<D> lo;
+#pragma unroll
+  for (int ds = 0; ds < D / 32; ++ds) lo.k[ds] = 2u * (uint32_t)(c * D + 8 * ((4 * ds + g) ^ T::fk(c)));
+  const int vr = 4 * g + (c >> 2);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+    lo.v[dt] = 2u * (uint32_t)(vr * D + 4 * (c & 1) + 8 * ((2 * dt + ((c & 3) >> 1)) ^ T::fv(vr)));
+  return lo;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const void* base, uint32_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+// S^T = K Q^T for one 32-key tile (the scores of this wave's rows).
+template <int D, int NR>
+__device__ __forceinline__ void qk_tile(const Stage<D>& sm, const LaneOffsets<D>& lo, const WaveState<D, NR>& st,
+                                        f32x4 (&s)[NR][2]) {
+  constexpr uint32_t HALF = 16u * D * 2u;   // bytes of 16 rows
 #pragma unroll
   for (int r = 0; r < NR; ++r)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) s[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // S^T = K Q^T: lane (c, g) reads key row kt*16 + c, logical chunk 4 ds + g
 #pragma unroll
   for (int ds = 0; ds < D / 32; ++ds) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int row = kt * 16 + c;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[row * D + 8 * ((4 * ds + g) ^ T::fk(row))]);
+      const bf16x8 a = *at_bytes<bf16x8>(sm.k, lo.k[ds] + kt * HALF);
 #pragma unroll
       for (int r = 0; r < NR; ++r) s[r][kt] = mfma16x16x32(a, st.qf[r][ds], s[r][kt]);
     }
   }
+}
+
+// Mask (PARTIAL tiles), softmax weights and O^T += V^T P^T for one tile whose
+// scores are in s.  cls: PI_TILE_FULL or PI_TILE_PARTIAL.
+template <int D, int NR>
+__device__ __forceinline__ void softmax_pv(const Stage<D>& sm, const LaneOffsets<D>& lo, WaveState<D, NR>& st,
+                                           f32x4 (&s)[NR][2], int cls, uint32_t forbid, float scale_log2) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  constexpr uint32_t HALF = 16u * D * 2u;
   const float NEG_INF = -INFINITY;
   if (cls == PI_TILE_PARTIAL) {
 #pragma unroll
@@ -191,7 +232,9 @@ __device__ __forceinline__ void attend_tile(const Stage<D>& sm, WaveState<D, NR>
           if (!pair_visible(st.wq[r], wk, forbid)) s[r][kt][i] = NEG_INF;
       }
   }
-  // tile row maxima; the first visible tile of a row fixes its reference maximum
+  // lane maxima of this tile; until every row has a reference maximum, the row
+  // maxima (one cross-lane reduction) set the references of rows that lack one
+  bool have_all = true;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     float mx = NEG_INF;
@@ -199,16 +242,15 @@ __device__ __forceinline__ void attend_tile(const Stage<D>& sm, WaveState<D, NR>
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[r][kt][i]);
-    const float mt = group4_max(mx) * scale_log2;
-    st.mobs[r] = fmaxf(st.mobs[r], mt);
-    st.m[r] = (st.m[r] == NEG_INF) ? mt : st.m[r];
+    const float ml = mx * scale_log2;
+    st.mobs[r] = fmaxf(st.mobs[r], ml);
+    if (!st.all_set) {
+      const float mt = group4_max(ml);
+      st.m[r] = (st.m[r] == NEG_INF) ? mt : st.m[r];
+      have_all &= st.m[r] != NEG_INF;
+    }
   }
-  // V^T operand rows for this lane: keys 4g + c/4 and 16 + 4g + c/4
-  const int vr0 = 4 * g + (c >> 2), vr1 = vr0 + 16;
-  const __bf16* v0 = &sm.v[vr0 * D + 4 * (c & 1)];
-  const __bf16* v1 = &sm.v[vr1 * D + 4 * (c & 1)];
-  const int fv0 = T::fv(vr0), fv1 = T::fv(vr1);
-  const int csel = (c & 3) >> 1;
+  if (!st.all_set) st.all_set = __ballot(!have_all) == 0ull;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     // a row that has seen no visible key keeps m = -inf: use 0 so masked weights are exp2(-inf) = 0
@@ -219,6 +261,8 @@ __device__ __forceinline__ void attend_tile(const Stage<D>& sm, WaveState<D, NR>
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // l sums the weights as rounded for the matrix cores, so the final 1/l
+        // normalises exactly the weights that multiplied V
         const __bf16 pb = f2bf(fast_exp2(fmaf(s[r][kt][i], scale_log2, -m_use)));
         pf[4 * kt + i] = pb;
         lsum += bf2f(pb);
@@ -227,21 +271,60 @@ __device__ __forceinline__ void attend_tile(const Stage<D>& sm, WaveState<D, NR>
     // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
-      const int lc = 2 * dt + csel;   // logical chunk holding columns 16 dt + 4 (c & 3) ..
-      const bf16x4 lo = lds_read_tr4(v0 + 8 * (lc ^ fv0));
-      const bf16x4 hi = lds_read_tr4(v1 + 8 * (lc ^ fv1));
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x4 lo4 = lds_read_tr4(at_bytes<__bf16>(sm.v, lo.v[dt]));
+      const bf16x4 hi4 = lds_read_tr4(at_bytes<__bf16>(sm.v, lo.v[dt] + HALF));
+      const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
       st.o[r][dt] = mfma16x16x32(a, pf, st.o[r][dt]);
     }
   }
 }
 
-// True if a row's maximum grew past its reference by more than kMaxGrowth.
+// Tile loop shared by both kernels, software-pipelined over three LDS stages:
+// while tile i's softmax and PV run, tile i+1's scores are computed (its K is
+// already in LDS) and tile i+2 streams in.  Tile j lives in stage j % 3; the loop
+// is unrolled by three so every LDS address is a per-lane offset plus a constant.
+//   issue(j, stage): start the loads of tile j into `stage` (all waves take part)
+//   cls(j): PI_TILE_FULL or PI_TILE_PARTIAL
+template <int D, int NR, typename Issue, typename Cls>
+__device__ __forceinline__ void run_tiles(Stage<D> (&stage)[3], const LaneOffsets<D>& lo, WaveState<D, NR>& st,
+                                          int i_lo, int i_hi, Issue issue, Cls cls, uint32_t forbid,
+                                          float scale_log2) {
+  if (i_lo >= i_hi) return;
+  issue(i_lo, stage[0]);
+  if (i_lo + 1 < i_hi) issue(i_lo + 1, stage[1]);
+  wait_vmem();
+  __syncthreads();
+  f32x4 s_cur[NR][2];
+  qk_tile<D, NR>(stage[0], lo, st, s_cur);
+  auto step = [&](int i, Stage<D>& cur, Stage<D>& nxt, Stage<D>& free_st) {
+    wait_vmem();          // this wave's loads of tile i+1 have landed
+    __syncthreads();      // ... everyone's; and everyone is done with tile i-1
+    if (i + 2 < i_hi) issue(i + 2, free_st);
+    f32x4 s_nxt[NR][2];
+    if (i + 1 < i_hi) qk_tile<D, NR>(nxt, lo, st, s_nxt);
+    softmax_pv<D, NR>(cur, lo, st, s_cur, cls(i), forbid, scale_log2);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s_cur[r][kt] = s_nxt[r][kt];
+  };
+  for (int i = i_lo; i < i_hi; i += 3) {
+    step(i, stage[0], stage[1], stage[2]);
+    if (i + 1 < i_hi) step(i + 1, stage[1], stage[2], stage[0]);
+    if (i + 2 < i_hi) step(i + 2, stage[2], stage[0], stage[1]);
+  }
+}
+
+// True if a row's maximum grew past its reference by more than kMaxGrowth (the
+// lane maxima are reduced across each row here, once).
 template <int D, int NR>
-__device__ __forceinline__ bool needs_rerun(const WaveState<D, NR>& st) {
+__device__ __forceinline__ bool needs_rerun(WaveState<D, NR>& st) {
   bool bad = false;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) bad |= st.mobs[r] > st.m[r] + kMaxGrowth;
+  for (int r = 0; r < NR; ++r) {
+    st.mobs[r] = group4_max(st.mobs[r]);
+    bad |= st.mobs[r] > st.m[r] + kMaxGrowth;
+  }
   return bad;
 }
 
@@ -254,6 +337,7 @@ __device__ __forceinline__ void reset_for_rerun(WaveState<D, NR>& st) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  st.all_set = true;
 }
 
 template <int D, int NR>
@@ -266,6 +350,7 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  st.all_set = false;
 }
 
 // Workgroup placement: workgroups are dispatched round-robin over the 8 XCDs;
@@ -337,7 +422,7 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
                uint32_t forbid, int n_qblk) {
   using C = Cfg<D, G, NR, NW>;
-  __shared__ Stage<D> stage[2];
+  __shared__ Stage<D> stage[3];
   __shared__ uint32_t kmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ int tcount;
@@ -390,8 +475,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   const i32x4 rv = make_rsrc(v + ((size_t)b * L * Hkv + kvh) * D);
   const i32x4 rw = make_rsrc(tk);
   const int tsb = Hkv * D * 2;
-  auto issue = [&](int i) {
-    Stage<D>& sg = stage[i & 1];
+  const LaneOffsets<D> lo = lane_offsets<D>();
+  auto issue = [&](int i, Stage<D>& sg) {
     const int kt = (int)(tlist[i] & 0xFFFFu);
     const int key0 = kt * TK;
     issue_kv<D, NW>(sg, rk, rv, key0, tsb, kmask[kt]);
@@ -400,15 +485,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
       pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
     }
   };
-  auto run = [&]() {
-    if (count > 0) issue(0);
-    for (int i = 0; i < count; ++i) {
-      wait_vmem();
-      __syncthreads();
-      if (i + 1 < count) issue(i + 1);
-      attend_tile<D, NR>(stage[i & 1], st, (int)((tlist[i] >> 16) & 0xFFu), forbid, scale_log2);
-    }
-  };
+  auto cls = [&](int i) { return (int)((tlist[i] >> 16) & 0xFFu); };
+  auto run = [&]() { run_tiles<D, NR>(stage, lo, st, 0, count, issue, cls, forbid, scale_log2); };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
@@ -437,7 +515,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
-  __shared__ Stage<D> stage[2];
+  __shared__ Stage<D> stage[3];
   __shared__ uint32_t sbid[128];
   __shared__ uint32_t pmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
@@ -514,8 +592,8 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const i32x4 rv = make_rsrc(cv + (size_t)b * cap * D);
   const i32x4 rks = make_rsrc(ks + (size_t)b * S * D);
   const i32x4 rvs = make_rsrc(vs + (size_t)b * S * D);
-  auto issue = [&](int i) {
-    Stage<D>& sg = stage[i & 1];
+  const LaneOffsets<D> lo = lane_offsets<D>();
+  auto issue = [&](int i, Stage<D>& sg) {
     const uint32_t d = tlist[i];
     const int key0 = (int)(d & 0xFFFFu) * TK;
     const bool suffix = (d >> 24) & 1u;
@@ -527,15 +605,8 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
       sg.w[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
     }
   };
-  auto run = [&]() {
-    if (i_lo < i_hi) issue(i_lo);
-    for (int i = i_lo; i < i_hi; ++i) {
-      wait_vmem();
-      __syncthreads();
-      if (i + 1 < i_hi) issue(i + 1);
-      attend_tile<D, NR>(stage[i & 1], st, (int)((tlist[i] >> 16) & 0xFFu), 0u, scale_log2);
-    }
-  };
+  auto cls = [&](int i) { return (int)((tlist[i] >> 16) & 0xFFu); };
+  auto run = [&]() { run_tiles<D, NR>(stage, lo, st, i_lo, i_hi, issue, cls, 0u, scale_log2); };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
