@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit"], default=None,
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy"], default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
 
@@ -204,6 +204,46 @@ def decode_kernel_leg(cx: Ctx, iters: int):
     }
 
 
+def copy_kernel_leg(cx: Ctx, iters: int):
+    """A plain device-to-device copy of known size.  Its HBM byte counters give
+    the scale factor that turns the counters of the path's kernels into bytes."""
+    torch = cx.torch
+    n = 1 << 28                                  # 256 Mi fp32 = 1 GiB each way
+    src = torch.ones(n, dtype=torch.float32, device=cx.dev)
+    dst = torch.empty_like(src)
+    ms = cx.time_ms(lambda: dst.copy_(src), iters)
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "us_per_launch": ms * 1e3,
+            "achieved_gbs": 8 * n / (ms * 1e-3) / 1e9, "kernel": "torch copy (1 GiB)"}
+
+
+# HBM bytes per launch from the committed counter summaries; a summary only counts
+# while the kernel sources it was taken from are unchanged.
+KERNEL_SOURCES = {"decode_kernel": ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/common.h"],
+                  "prefill_kernel": ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/common.h"]}
+
+
+def source_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(kernel, summary):
+    import re
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b) or m_src.group(1) != source_digest(kernel):
+        return None
+    return float(m_b.group(1))
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on the host cores, bounded sample
 # ---------------------------------------------------------------------------
@@ -289,6 +329,9 @@ def main():
         log("decode kernel leg (B=64 816 slots)")
         kernels["decode"] = decode_kernel_leg(cx, args.kernel_iters)
         log(str(kernels["decode"]))
+    if args.only == "copy":
+        kernels["copy"] = copy_kernel_leg(cx, 5)
+        log(str(kernels["copy"]))
     if args.only == "mmdit":
         kernels["mmdit"] = prefill_kernel_leg(cx, args.kernel_iters, "mmdit_full_bidirectional")
         log(str(kernels["mmdit"]))
@@ -301,7 +344,9 @@ def main():
     roofline = {
         "kernel": "decode_kernel (cached suffix decode, B=64, 816 slots)",
         "bound": "hbm", "achieved": dec["achieved_gbs"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-        "frac": dec["achieved_gbs"] * 1e9 / PEAK_HBM_BYTES, "traffic": None,
+        "frac": dec["achieved_gbs"] * 1e9 / PEAK_HBM_BYTES,
+        "traffic": counted_traffic("decode_kernel", "decode_kernel_serving_B64_816slots_traffic.md"),
+        "algorithmic_bytes_per_launch": dec["algorithmic_bytes_per_launch"], "us_per_launch": dec["us_per_launch"],
     }
     cpu = None
     if not args.no_cpu_baseline:
@@ -319,7 +364,10 @@ def main():
         "roofline": roofline,
         "prefill_mfma": {"kernel": "prefill_kernel (pi05 B=32 L=962)", "bound": "mfma",
                          "achieved": pre["achieved_tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
-                         "frac": pre["mfma_frac"], "us_per_launch": pre["us_per_launch"]},
+                         "frac": pre["mfma_frac"], "us_per_launch": pre["us_per_launch"],
+                         "gflop_per_launch": pre["gflop_per_launch"],
+                         "traffic": counted_traffic("prefill_kernel", "prefill_kernel_pi05_B32_L962_traffic.md"),
+                         "algorithmic_bytes_per_launch": pre["algorithmic_bytes"]},
         "decode_hbm": {"kernel": "decode_kernel (B=64 816 slots)", "achieved_gbs": dec["achieved_gbs"],
                        "frac": dec["hbm_frac"], "us_per_launch": dec["us_per_launch"]},
         "breakdown_us": result["breakdown_us"],

@@ -353,14 +353,36 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
   st.all_set = false;
 }
 
-// Workgroup placement: workgroups are dispatched round-robin over the 8 XCDs;
-// give every group's `per_group` workgroups one XCD.
-__device__ __forceinline__ void xcd_place(int per_group, int& group, int& sub) {
+// Workgroup placement.  Workgroups are dispatched round-robin over the 8 XCDs,
+// each with its own L2.  A group's workgroups (which read the same K/V) are kept
+// on one XCD; with fewer groups than XCDs, each group is cut into `span` parts
+// that run on `span` different XCDs, so a single sample still fills the chip.
+// Returns false for a workgroup with no work (the grid is rounded up).
+struct Placement {
+  int n_groups, n_sub, span, per;   // per = ceil(n_sub / span) sub-blocks per part
+};
+
+__host__ __device__ inline Placement make_placement(int n_groups, int n_sub) {
+  Placement p;
+  p.n_groups = n_groups;
+  p.n_sub = n_sub;
+  p.span = n_groups >= 8 ? 1 : 8 / n_groups;
+  p.per = (n_sub + p.span - 1) / p.span;
+  return p;
+}
+
+__host__ inline int64_t placement_grid(const Placement& p) {
+  return (int64_t)((p.n_groups * p.span + 7) / 8 * 8) * p.per;
+}
+
+__device__ __forceinline__ bool xcd_place(const Placement& p, int& group, int& sub) {
   const int id = blockIdx.x;
   const int xcd = id & 7;
   const int k = id >> 3;
-  sub = k % per_group;
-  group = (k / per_group) * 8 + xcd;
+  const int part_group = (k / p.per) * 8 + xcd;
+  group = part_group / p.span;
+  sub = (part_group % p.span) * p.per + k % p.per;
+  return group < p.n_groups && sub < p.n_sub;
 }
 
 // Normalise and store O rows (row_base[r] = output row or nullptr).
@@ -410,7 +432,7 @@ __device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_bas
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: grid = ceil(B*Hkv / 8) * 8 groups x n_qblk workgroups (XCD-placed).
+// Prefill: one group per (sample, KV head), n_qblk query blocks each, XCD-placed.
 // Up front the workgroup computes every key tile's validity bitmap and compacts
 // its non-EMPTY tiles into an LDS list; the loop then streams tile i+1 into the
 // other LDS stage while tile i is computed.
@@ -420,15 +442,14 @@ __global__ void __launch_bounds__(NW * 64)
 prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
-               uint32_t forbid, int n_qblk) {
+               uint32_t forbid, Placement place) {
   using C = Cfg<D, G, NR, NW>;
   __shared__ Stage<D> stage[3];
   __shared__ uint32_t kmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ int tcount;
   int group, qblk;
-  xcd_place(n_qblk, group, qblk);
-  if (group >= B * Hkv) return;
+  if (!xcd_place(place, group, qblk)) return;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
@@ -496,8 +517,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
 }
 
 // ---------------------------------------------------------------------------
-// Cached suffix decode (Hq = 8, Hkv = 1, d = 256): grid = ceil(B*splits/8)*8 x
-// n_qblk.  Keys: valid prefix slots of the cache layer, then the suffix's own
+// Cached suffix decode (Hq = 8, Hkv = 1, d = 256): one group per (sample, key
+// split), n_qblk query blocks each, XCD-placed.  Keys: valid prefix slots of the cache layer, then the suffix's own
 // K/V.  Query/key words reuse the prefill rule with bid 0 for every prefix slot
 // and 1 + cumsum(suffix_ar) for suffix tokens.  The per-tile validity of the
 // prefix slots is read once up front, so fully padded tiles are never fetched
@@ -511,7 +532,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               const uint8_t* __restrict__ prefix_mask, int cap, int P,
               const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
               const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
-              __bf16* __restrict__ os, int n_qblk, int n_split, float* __restrict__ opart,
+              __bf16* __restrict__ os, Placement place, int n_split, float* __restrict__ opart,
               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
@@ -522,8 +543,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   __shared__ uint32_t tmask[kMaxTiles];
   __shared__ int tcount;
   int grp, qblk;
-  xcd_place(n_qblk, grp, qblk);
-  if (grp >= B * n_split) return;
+  if (!xcd_place(place, grp, qblk)) return;
   const int b = grp / n_split, split = grp % n_split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
@@ -706,14 +726,14 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
                          float scale, const pi_mask* m, hipStream_t s) {
   using C = Cfg<D, G, NR, NW>;
   const int n_qblk = (L + C::TOK - 1) / C::TOK;
-  const int groups = (B * Hkv + 7) / 8 * 8;
-  const int64_t grid = (int64_t)groups * n_qblk;
+  const Placement place = make_placement(B * Hkv, n_qblk);
+  const int64_t grid = placement_grid(place);
   PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "prefill: grid too large");
   const float scale_log2 = scale * 1.4426950408889634f;
   prefill_kernel<D, G, NR, NW><<<(unsigned)grid, C::THREADS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), B, L, Hq, Hkv, scale_log2, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits,
-      n_qblk);
+      place);
   return pi::check_launch("prefill_kernel");
 }
 
@@ -822,15 +842,15 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
   float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                         pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256))
                              : nullptr;
-  const int groups = (B * splits + 7) / 8 * 8;
+  const Placement place = make_placement(B * splits, n_qblk);
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
   const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  decode_kernel<256, 8, kNR256, kNW256><<<(unsigned)(groups * n_qblk), C::THREADS, 0, s>>>(
+  decode_kernel<256, 8, kNR256, kNW256><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
       static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
-      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), n_qblk, splits, opart, mlpart);
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), place, splits, opart, mlpart);
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
   decode_combine_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o_s),
