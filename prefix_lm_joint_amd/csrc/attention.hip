@@ -636,37 +636,51 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     store_rows<D, NR>(st, row_base);
     return;
   }
-  // split keys: unnormalised fp32 partial O plus (reference max, weight sum) per row
+  // split keys: the unnormalised fp32 partial O of each 16-row tile, stored in
+  // the accumulator's own lane order so every store writes 1 KB contiguous, plus
+  // (reference max, weight sum) per row
   const int c = lane & 15, g = lane >> 4;
+  const int64_t n_chunks = (int64_t)B * place.n_sub * NW * NR;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const float l = group4_sum(st.l[r]);
-    const int row = wave * C::ROWS_W + r * 16 + c;
-    const int t = tok0 + row / G;
-    if (t >= S) continue;
-    const int64_t prow = ((int64_t)split * B + b) * S * Hq + (int64_t)t * Hq + row % G;
-    float* dst = opart + prow * D;
+    const int64_t chunk = (((int64_t)b * place.n_sub + qblk) * NW + wave) * NR + r;
+    const int64_t at = split * n_chunks + chunk;
+    f32x4* dst = reinterpret_cast<f32x4*>(opart) + at * (D / 16) * 64 + lane;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(dst + dt * 16 + 4 * g) = st.o[r][dt];
+    for (int dt = 0; dt < D / 16; ++dt) dst[dt * 64] = st.o[r][dt];
     if (g == 0) {
-      mlpart[2 * prow] = st.m[r];
-      mlpart[2 * prow + 1] = l;
+      mlpart[at * 32 + 2 * c] = st.m[r];
+      mlpart[at * 32 + 2 * c + 1] = l;
     }
   }
 }
 
 // Merge the key splits of the decode: for each (sample, token, head) row,
-// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  One wave
-// per row, four d per lane (d = 256); all of a row's loads are issued at once.
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The
+// decode stored each 16-row chunk's partial in accumulator lane order; here four
+// workgroups share a chunk and each wave merges one 16-wide slice of d, issuing
+// the loads of all splits at once (1 KB contiguous per load).
 constexpr int kMaxSplit = 16;
 
+template <int NR, int NW>
 __global__ void __launch_bounds__(256)
 decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__ mlpart,
-                      __bf16* __restrict__ os, int n_split, int64_t rows) {
-  constexpr int D = 256;
+                      __bf16* __restrict__ os, int B, int S, int n_qblk, int n_split) {
+  constexpr int D = 256, G = 8, TOK = NR * NW * 16 / G;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t chunk = blockIdx.x >> 2;
+  const int dt = (blockIdx.x & 3) * 4 + (threadIdx.x >> 6);
+  const int64_t n_chunks = (int64_t)B * n_qblk * NW * NR;
+  const int r = (int)(chunk % NR);
+  const int w_dec = (int)((chunk / NR) % NW);
+  const int64_t bq = chunk / (NR * NW);
+  const int qblk = (int)(bq % n_qblk);
+  const int64_t b = bq / n_qblk;
+  const int row = w_dec * 16 * NR + r * 16 + c;
+  const int t = qblk * TOK + row / G;
+  const int head = row % G;
   float m[kMaxSplit], l[kMaxSplit];
   f32x4 op[kMaxSplit];
   float M = -INFINITY;
@@ -676,12 +690,14 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
     l[sp] = 0.f;
     op[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (sp < n_split) {
-      m[sp] = mlpart[2 * (sp * rows + row)];
-      l[sp] = mlpart[2 * (sp * rows + row) + 1];
-      op[sp] = *reinterpret_cast<const f32x4*>(opart + (sp * rows + row) * D + 4 * lane);
+      const int64_t at = sp * n_chunks + chunk;
+      m[sp] = mlpart[at * 32 + 2 * c];
+      l[sp] = mlpart[at * 32 + 2 * c + 1];
+      op[sp] = reinterpret_cast<const f32x4*>(opart)[(at * (D / 16) + dt) * 64 + lane];
     }
     M = fmaxf(M, m[sp]);
   }
+  if (t >= S) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
@@ -696,7 +712,7 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
   bf16x4 v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = f2bf(acc[i] * inv);
-  *reinterpret_cast<bf16x4*>(os + row * D + 4 * lane) = v;
+  *reinterpret_cast<bf16x4*>(os + ((b * S + t) * G + head) * D + dt * 16 + 4 * g) = v;
 }
 
 // K/V rows of tokens [0, P) into cache layer slices; one thread per 16 bytes.
@@ -748,8 +764,10 @@ int decode_splits(int B, int S, int len) {
 
 size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
   if (splits <= 1) return 0;
-  const size_t rows = (size_t)B * S * Hq;
-  return pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256) + (size_t)splits * rows * 2 * sizeof(float);
+  (void)Hq;
+  const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
+  const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
+  return pi::align_up(chunks * 16 * 256 * sizeof(float), 256) + chunks * 32 * sizeof(float);
 }
 
 }  // namespace
@@ -837,10 +855,10 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
   if (workspace == nullptr || workspace_bytes < need) splits = 1;   // no workspace: one pass per sample
   PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_suffix_decode_step: workspace must be 256-byte aligned");
-  const int64_t rows = (int64_t)B * S * Hq;
+  const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
   float* opart = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                        pi::align_up((size_t)splits * rows * 256 * sizeof(float), 256))
+                                                        pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
                              : nullptr;
   const Placement place = make_placement(B * splits, n_qblk);
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
@@ -853,7 +871,7 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
       scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), place, splits, opart, mlpart);
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
-  decode_combine_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o_s),
-                                                                   splits, rows);
+  decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
+      opart, mlpart, static_cast<__bf16*>(o_s), B, S, n_qblk, splits);
   return pi::check_launch("decode_combine_kernel");
 }

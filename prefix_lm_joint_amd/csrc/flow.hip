@@ -87,7 +87,7 @@ constexpr float kRmsEps = 1e-6f;
 // contraction into NWV contiguous ranges and each computes the whole tile over
 // its range, with KB k-steps of loads in flight at a time; the partial tiles are
 // summed through LDS.  Small batches (M = 51 rows per sample) use narrow tiles and
-// eight waves, so many workgroups each wait on one short chain of loads instead
+// sixteen waves, so many workgroups each wait on one short chain of loads instead
 // of a few workgroups serialising on memory latency.  Products are computed
 // transposed (A operand = weights, B operand = activations) so a lane holds four
 // consecutive output columns of one row.
@@ -244,13 +244,15 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
   }
 }
 
-// Tile choice: narrow tiles and eight waves for the few rows of a small batch,
-// 64 x 64 tiles with four waves once the rows alone give enough workgroups.
+// Tile choice: 16-column tiles with sixteen waves splitting the contraction for
+// the few rows of a small batch (each wave then waits on a single short batch of
+// loads), 64 x 64 tiles with four waves once the rows alone give enough
+// workgroups.
 template <int EPI, typename TA, bool NORM>
 pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
   if (a.M <= 256) {
-    dim3 grid((a.N + 31) / 32, (a.M + 63) / 64);
-    gemm_kernel<EPI, TA, NORM, 2, 8><<<grid, 512, 0, s>>>(a);
+    dim3 grid((a.N + 15) / 16, (a.M + 63) / 64);
+    gemm_kernel<EPI, TA, NORM, 1, 16><<<grid, 1024, 0, s>>>(a);
   } else {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
     gemm_kernel<EPI, TA, NORM, 4, 4><<<grid, 256, 0, s>>>(a);
