@@ -164,10 +164,14 @@ pi_status pi_euler_update(float* x, const float* v, float dt, int64_t n, pi_stre
  *   w_state [W, A], b_state [W]        state token  = r(state) W_state^T + b_state
  *   w_in    [W, A], b_in [W], w_time [W]  action tokens = r(x) W_in^T + b_in + t*w_time
  *   w_q [Hq*d, W], w_k, w_v [Hkv*d, W], w_o [W, Hq*d]
- *       per cache layer l: a = r(h); q,k,v = r(a W^T); o = r(decode_l(q,k,v)); h += o W_o^T
- *   w_out [A, W], b_out [A]            velocity = r(h[:,1:]) W_out^T + b_out
- * r() rounds to bf16; products accumulate in fp32; h is fp32.  The same weights
- * serve every cache layer.
+ *       per cache layer l: a = r(h); q,k,v = r(a W^T / rms(a)); o = r(decode_l(q,k,v));
+ *                          h += o W_o^T
+ *   w_out [A, W], b_out [A]            velocity = a[:,1:] W_out^T / rms(a[:,1:]) + b_out,
+ *                                      a = r(h) after the last layer
+ * r() rounds to bf16; products accumulate in fp32; h is fp32.  rms(a) =
+ * sqrt(mean(a^2) + 1e-6) over the width is the per-stream RMS norm ahead of the
+ * projections ([P3] first section), a per-row scalar applied to the product.
+ * The same weights serve every cache layer.
  */
 typedef struct pi_velocity_net {
   int32_t width, action_dim, Hq, Hkv, d;
@@ -192,7 +196,9 @@ size_t pi_flow_workspace_bytes(const pi_velocity_net* net, int B, int H);
  * one denoising step, [P1] §1.6).  x fp32 [B,H,A]; state fp32 [B,A];
  * suffix_ar uint8 [H+1] (device; state token first); vel fp32 [B,H,A].
  * Uses cache layers [0, cache->layers).  Width W must be a multiple of 64,
- * A <= 64 and a multiple of 8, H + 1 <= 128.
+ * A <= 64, H + 1 <= 128.  The workspace also holds the weights repacked into the
+ * matrix-core operand layout, redone at the start of every call (so weights may
+ * change between calls).
  */
 pi_status pi_velocity_eval(const pi_velocity_net* net, const pi_kv_cache* cache,
                            const uint8_t* suffix_ar, const float* state, const float* x, float t,

@@ -45,16 +45,16 @@ def euler_sample(noise, velocity, num_steps: int = 10) -> np.ndarray:
 #
 #   tokens      h[:,0]   = r(state) W_state^T + b_state            (state token)
 #               h[:,1+i] = r(x_i) W_in^T + b_in + t * w_time        (action tokens)
-#   18 layers   a = r(h); q = r(a W_q^T / rms(h)); k, v likewise
+#   18 layers   a = r(h); q = r(a W_q^T / rms(a)); k, v likewise
 #               o = r(cached_decode(q, k, v, cache layer l));  h += o W_o^T
-#   output      v_out = r(h[:,1:]) W_out^T / rms(h[:,1:]) + b_out
+#   output      a = r(h); v_out = a[:,1:] W_out^T / rms(a[:,1:]) + b_out
 #
 # r(.) rounds to bf16: every matrix product takes bf16 operands and
-# accumulates exactly; the attention reads and writes bf16.  rms(h) =
-# sqrt(mean(h^2) + 1e-6) over the width, taken on the unrounded h: an RMS norm
-# before the projections ("π0.5 vs MM-DiT joint attention", first section: each
-# stream has its own norm ahead of its QKV and output projections).  The norm is
-# a per-row scalar, so it is applied to the product (exactly equal in real
+# accumulates exactly; the attention reads and writes bf16.  rms(a) =
+# sqrt(mean(a^2) + 1e-6) over the width, taken on the same bf16 activations the
+# projection reads: an RMS norm before the projections ("π0.5 vs MM-DiT joint
+# attention", first section: each stream has its own norm ahead of its QKV and
+# output projections).  The norm is a per-row scalar, so it is applied to the product (exactly equal in real
 # arithmetic to normalising first).  Without it the residual stream of a
 # random-weight stack grows geometrically with depth.  One weight set is shared
 # by all layers; layer l attends to cache layer l.
@@ -94,7 +94,7 @@ def velocity_net(x, t, state, w, cache_k, cache_v, prefix_mask, suffix_ar, Hq, H
     trace = []
     for layer in range(L):
         a = round_bf16(h)
-        r_h = rms(h)
+        r_h = rms(a)
         q = round_bf16(_lin(a, w["w_q"]) / r_h).reshape(B, S, Hq, d)
         k = round_bf16(_lin(a, w["w_k"]) / r_h).reshape(B, S, Hkv, d)
         v = round_bf16(_lin(a, w["w_v"]) / r_h).reshape(B, S, Hkv, d)
@@ -102,7 +102,8 @@ def velocity_net(x, t, state, w, cache_k, cache_v, prefix_mask, suffix_ar, Hq, H
         h = h + _lin(o.reshape(B, S, Hq * d), w["w_o"])
         if return_trace:
             trace.append(dict(q=q, k=k, v=v, o=o, h=h.copy()))
-    vel = _lin(round_bf16(h[:, 1:, :]), w["w_out"]) / rms(h[:, 1:, :]) + w["b_out"]
+    a = round_bf16(h[:, 1:, :])
+    vel = _lin(a, w["w_out"]) / rms(a) + w["b_out"]
     if return_trace:
         return vel, trace
     return vel

@@ -385,26 +385,34 @@ __device__ __forceinline__ bool xcd_place(const Placement& p, int& group, int& s
   return group < p.n_groups && sub < p.n_sub;
 }
 
-// Normalise and store O rows (row_base[r] = output row or nullptr).
-template <int D, int NR>
-__device__ __forceinline__ void store_rows(WaveState<D, NR>& st, __bf16* const* row_base) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
+// Normalise and store O rows.  dst(r, dt) gives where the lane's four values
+// d = 16 dt + 4 g .. + 3 of row tile r go, or nullptr for a row with no output.
+template <int D, int NR, typename Dst>
+__device__ __forceinline__ void store_rows(WaveState<D, NR>& st, Dst dst) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const float l = group4_sum(st.l[r]);
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    __bf16* dst = row_base[r];
-    if (dst == nullptr) continue;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
+      __bf16* p = dst(r, dt);
+      if (p == nullptr) continue;
       bf16x4 v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = f2bf(st.o[r][dt][i] * inv);
-      *reinterpret_cast<bf16x4*>(dst + dt * 16 + 4 * g) = v;
+      *reinterpret_cast<bf16x4*>(p) = v;
     }
   }
 }
+
+// Row-major output rows (row_base[r] = output row or nullptr).
+template <int D>
+struct RowMajorDst {
+  __bf16* const* row_base;
+  __device__ __forceinline__ __bf16* operator()(int r, int dt) const {
+    return row_base[r] ? row_base[r] + dt * 16 + 4 * ((threadIdx.x & 63) >> 4) : nullptr;
+  }
+};
 
 // Row setup: Q fragments into registers, the row's query word and output row.
 template <int D, int G, int NR, int ROWS_W>
@@ -513,7 +521,7 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
     reset_for_rerun(st);
     run();
   }
-  store_rows<D, NR>(st, row_base);
+  store_rows<D, NR>(st, RowMajorDst<D>{row_base});
 }
 
 // ---------------------------------------------------------------------------
@@ -532,7 +540,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               const uint8_t* __restrict__ prefix_mask, int cap, int P,
               const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
               const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
-              __bf16* __restrict__ os, Placement place, int n_split, float* __restrict__ opart,
+              __bf16* __restrict__ os, int o_tiled, Placement place, int n_split, float* __restrict__ opart,
               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
@@ -633,7 +641,18 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     run();
   }
   if (n_split == 1) {
-    store_rows<D, NR>(st, row_base);
+    if (o_tiled) {
+      const int c = lane & 15, g = lane >> 4;
+      auto dst = [&](int r, int dt) -> __bf16* {
+        const int row = wave * C::ROWS_W + r * 16 + c;
+        const int t = tok0 + row / G;
+        if (t >= S) return nullptr;
+        return os + tiled_offset((int64_t)b * S + t, (row % G) * D + dt * 16 + 4 * g, G * D);
+      };
+      store_rows<D, NR>(st, dst);
+    } else {
+      store_rows<D, NR>(st, RowMajorDst<D>{row_base});
+    }
     return;
   }
   // split keys: the unnormalised fp32 partial O of each 16-row tile, stored in
@@ -666,7 +685,7 @@ constexpr int kMaxSplit = 16;
 template <int NR, int NW>
 __global__ void __launch_bounds__(256)
 decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__ mlpart,
-                      __bf16* __restrict__ os, int B, int S, int n_qblk, int n_split) {
+                      __bf16* __restrict__ os, int o_tiled, int B, int S, int n_qblk, int n_split) {
   constexpr int D = 256, G = 8, TOK = NR * NW * 16 / G;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -712,7 +731,9 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
   bf16x4 v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = f2bf(acc[i] * inv);
-  *reinterpret_cast<bf16x4*>(os + ((b * S + t) * G + head) * D + dt * 16 + 4 * g) = v;
+  __bf16* dst = o_tiled ? os + tiled_offset(b * S + t, head * D + dt * 16 + 4 * g, G * D)
+                        : os + ((b * S + t) * G + head) * D + dt * 16 + 4 * g;
+  *reinterpret_cast<bf16x4*>(dst) = v;
 }
 
 // K/V rows of tokens [0, P) into cache layer slices; one thread per 16 bytes.
@@ -826,10 +847,9 @@ extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
   return decode_ws_bytes(B, S, Hq, decode_splits(B, S, len));
 }
 
-extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,
-                                           const void* v_s, const uint8_t* suffix_ar, int B, int S, int Hq,
-                                           float scale, void* o_s, void* workspace, size_t workspace_bytes,
-                                           pi_stream stream) {
+pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
+                           const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool o_tiled,
+                           void* workspace, size_t workspace_bytes, hipStream_t s) {
   PI_REQUIRE(cache && q_s && k_s && v_s && suffix_ar && o_s, PI_ERR_INVALID_ARG,
              "pi_suffix_decode_step: null pointer");
   PI_REQUIRE(cache->k && cache->v && cache->prefix_mask, PI_ERR_INVALID_ARG,
@@ -864,14 +884,21 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
   const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   decode_kernel<256, 8, kNR256, kNW256><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
       static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
-      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), place, splits, opart, mlpart);
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), o_tiled ? 1 : 0, place, splits, opart, mlpart);
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
   decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
-      opart, mlpart, static_cast<__bf16*>(o_s), B, S, n_qblk, splits);
+      opart, mlpart, static_cast<__bf16*>(o_s), o_tiled ? 1 : 0, B, S, n_qblk, splits);
   return pi::check_launch("decode_combine_kernel");
+}
+
+extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,
+                                           const void* v_s, const uint8_t* suffix_ar, int B, int S, int Hq,
+                                           float scale, void* o_s, void* workspace, size_t workspace_bytes,
+                                           pi_stream stream) {
+  return pi::decode_layer(cache, layer, q_s, k_s, v_s, suffix_ar, B, S, Hq, scale, o_s, false, workspace,
+                          workspace_bytes, static_cast<hipStream_t>(stream));
 }

@@ -56,6 +56,15 @@ __device__ __forceinline__ bool pair_visible(uint32_t wq, uint32_t wk, uint32_t 
   return both_valid && block_ok && !banned;
 }
 
+// Matrix-core operand tile layout of an [R x K] bf16 matrix (K a multiple of 32,
+// R padded to a multiple of 16): 16 x 32 tiles stored row-block major; inside a
+// tile, lane 16 * ((k % 32) / 8) + r % 16 holds the 8 elements of row r starting
+// at k - k % 8.  A wave then loads a whole operand fragment (A[c][8g..8g+7] of
+// lane 16g + c) as one contiguous 1 KB read.
+__host__ __device__ inline int64_t tiled_offset(int64_t r, int k, int K) {
+  return ((r >> 4) * (K >> 5) + (k >> 5)) * 512 + (((k & 31) >> 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -66,6 +75,12 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Largest decode workspace any cache length can ask for at this batch shape.
 size_t decode_workspace_max(int B, int S, int Hq);
+// Cached suffix decode of one layer (arguments checked by the caller); the output
+// is row-major [B, S, Hq, d] or, with o_tiled, the operand tile layout of the
+// [B*S x Hq*d] matrix.
+pi_status decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
+                       const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool o_tiled,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 }  // namespace pi
 
 #define PI_REQUIRE(cond, code, ...)     \

@@ -10,120 +10,71 @@
 // and an output projection back to the action dim):
 //   h[:,0]   = r(state) W_state^T + b_state
 //   h[:,1+i] = r(x_i) W_in^T + b_in + t * w_time
-//   per cache layer l: a = r(h); q,k,v = r(a W_{q,k,v}^T / rms(h)); o = r(decode_l); h += o W_o^T
-//   v = r(h[:,1:]) W_out^T / rms(h[:,1:]) + b_out
+//   per cache layer l: a = r(h); q,k,v = r(a W_{q,k,v}^T / rms(a)); o = r(decode_l); h += o W_o^T
+//   v = a[:,1:] W_out^T / rms(a[:,1:]) + b_out            (a = r(h) after the last layer)
 // r() is rounding to bf16; every matrix product runs on the matrix cores with
-// bf16 operands and fp32 accumulation.  rms(h) = sqrt(mean(h^2) + 1e-6) is the
+// bf16 operands and fp32 accumulation.  rms(a) = sqrt(mean(a^2) + 1e-6) is the
 // per-stream RMS norm ahead of the projections ("π0.5 vs MM-DiT joint attention",
-// first section); being a per-row scalar it is applied to the accumulator, and the
-// GEMM that reads the fp32 row of h accumulates its sum of squares on the way.
+// first section), taken on the same bf16 activations the product reads; being a
+// per-row scalar it is applied to the accumulator.
+//
+// Layout: the residual stream h stays fp32 row-major; next to it every producer
+// of h also writes a = r(h) in the operand tile layout (tiled_offset), the
+// decode writes its output in that layout too, and the weights are repacked into
+// it once per call, so every operand fragment a GEMM wave needs is one
+// contiguous 1 KB load.
 #include "common.h"
 
 #include <math.h>
 
 namespace {
 
-// Physical row of logical row m: (m / div) * stride + off + m % div.
-struct RowMap {
-  int div, stride, off;
-  __device__ __forceinline__ int64_t operator()(int m) const {
-    return (int64_t)(m / div) * stride + off + (m % div);
-  }
-};
-
 enum { EPI_QKV = 0, EPI_RESID = 1, EPI_VEL = 2, EPI_EULER = 3 };
 
 struct GemmArgs {
-  const void* a;       // activations, fp32 or bf16, row stride K
-  RowMap amap;
-  const __bf16* w0;    // weight rows [0, n1)
-  const __bf16* w1;    // weight rows [n1, n1 + n2)
-  const __bf16* w2;    // weight rows [n1 + n2, N)
-  int n1, n2;
+  const __bf16* a;     // activations [M (padded to 64) x K], operand tile layout
+  const __bf16* w;     // weights [N (padded to 16) x K], operand tile layout
   int M, N, K;
-  __bf16* o0;          // EPI_QKV outputs, row strides n1, n2, N - n1 - n2
+  int n1, n2;          // EPI_QKV: output column split q | k | v
+  __bf16* o0;          // EPI_QKV outputs, row-major, row strides n1, n2, N - n1 - n2
   __bf16* o1;
   __bf16* o2;
-  float* out;          // EPI_RESID / EPI_VEL / EPI_EULER output, row stride N
-  RowMap omap;
+  float* out;          // EPI_RESID: h [M x N] fp32; EPI_VEL / EPI_EULER: [B*H x N]
+  __bf16* a_out;       // EPI_RESID: r(h) in tile layout, row width N
+  int S;               // EPI_VEL / EPI_EULER: tokens per sample (row m % S == 0 is the state token)
   const float* bias;   // EPI_VEL / EPI_EULER
   float dt;            // EPI_EULER
 };
 
-// 8 consecutive elements of a row as bf16 (zero past K); `ss` accumulates the
-// sum of squares of the unrounded values.
-template <typename T>
-__device__ __forceinline__ bf16x8 load_frag(const T* row, int k, int K, bool vec_ok, float& ss) {
-  bf16x8 r;
-  if (vec_ok && k + 8 <= K) {
-    if constexpr (sizeof(T) == 2) {
-      r = *reinterpret_cast<const bf16x8*>(row + k);
-    } else {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(row + k);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(row + k + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r[i] = f2bf(a[i]);
-        r[i + 4] = f2bf(b[i]);
-        ss += a[i] * a[i] + b[i] * b[i];
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float f = (k + i < K) ? (float)row[k + i] : 0.f;
-      r[i] = f2bf(f);
-      ss += f * f;
-    }
-  }
-  return r;
-}
-
 constexpr float kRmsEps = 1e-6f;
 
-// out[m][n] = sum_k r(A[m][k]) W[n][k]  (divided by rms(A[m]) when NORM).
+// out[m][n] = sum_k A[m][k] W[n][k]  (divided by rms(A[m]) when NORM).
 //
 // Workgroup tile TN = 16*NT columns x 64 rows.  The NWV waves split the
 // contraction into NWV contiguous ranges and each computes the whole tile over
-// its range, with KB k-steps of loads in flight at a time; the partial tiles are
-// summed through LDS.  Small batches (M = 51 rows per sample) use narrow tiles and
-// sixteen waves, so many workgroups each wait on one short chain of loads instead
-// of a few workgroups serialising on memory latency.  Products are computed
-// transposed (A operand = weights, B operand = activations) so a lane holds four
-// consecutive output columns of one row.
-template <int EPI, typename TA, bool NORM, int NT, int NWV>
+// its range, KB k-steps at a time: all of a batch's fragment loads (one 1 KB
+// contiguous read each, from the tile layout) are issued before the first wait.
+// The partial tiles are summed through LDS.  Small batches (M = 51 rows per
+// sample) use 16-column tiles and sixteen waves, so many workgroups each wait on
+// one short batch of loads.  Products are computed transposed (A operand =
+// weights, B operand = activations) so a lane holds four consecutive output
+// columns of one row.
+template <int EPI, bool NORM, int NT, int NWV>
 __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
   constexpr int TN = 16 * NT;
   constexpr int PS = TN + 4;                     // LDS row stride (floats) of a partial tile
-  constexpr int KB = sizeof(TA) == 2 ? 4 : 2;    // k-steps of loads in flight
+  constexpr int KB = 4;                          // k-steps of loads in flight
   __shared__ float part[NWV][64 * PS];
   __shared__ float ssp[NWV][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * TN;
   const int m0 = blockIdx.y * 64;
-  const bool vec_ok = (p.K & 7) == 0;
+  const int kb = p.K / 32;
 
-  const __bf16* wrow[NT];
-  bool wok[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int n = n0 + 16 * j + c;
-    wok[j] = n < p.N;
-    const __bf16* base = p.w0;
-    int nn = n;
-    if (n >= p.n1 + p.n2) { base = p.w2; nn = n - p.n1 - p.n2; }
-    else if (n >= p.n1) { base = p.w1; nn = n - p.n1; }
-    wrow[j] = base + (int64_t)(wok[j] ? nn : 0) * p.K;
-  }
-  const TA* arow[4];
-  bool aok[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + 16 * j + c;
-    aok[j] = m < p.M;
-    arow[j] = static_cast<const TA*>(p.a) + (aok[j] ? p.amap(m) : 0) * p.K;
-  }
+  // fragment (row block, k-step) of a tile-layout matrix
+  const bf16x8* wt = reinterpret_cast<const bf16x8*>(p.w) + (int64_t)(n0 / 16) * kb * 64 + lane;
+  const bf16x8* at = reinterpret_cast<const bf16x8*>(p.a) + (int64_t)(m0 / 16) * kb * 64 + lane;
 
   f32x4 acc[NT][4];
 #pragma unroll
@@ -131,30 +82,38 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ss[4] = {0.f, 0.f, 0.f, 0.f};
-  float ss_w = 0.f;
 
-  const int ksteps = (p.K + 31) / 32;
-  const int per = (ksteps + NWV - 1) / NWV;
-  const int ks_lo = wave * per, ks_hi = min(ksteps, ks_lo + per);
+  const int per = (kb + NWV - 1) / NWV;
+  const int ks_lo = wave * per, ks_hi = min(kb, ks_lo + per);
   for (int ks0 = ks_lo; ks0 < ks_hi; ks0 += KB) {
     bf16x8 wf[KB][NT], af[KB][4];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      const int k = (ks0 + u) * 32 + 8 * g;
-      const bool live = ks0 + u < ks_hi;
+      const bool live = ks0 + u < ks_hi;          // uniform over the wave
 #pragma unroll
-      for (int j = 0; j < NT; ++j) wf[u][j] = (live && wok[j]) ? load_frag(wrow[j], k, p.K, vec_ok, ss_w) : bf16x8{};
+      for (int j = 0; j < NT; ++j)
+        wf[u][j] = (live && n0 + 16 * j < p.N) ? wt[((int64_t)j * kb + ks0 + u) * 64] : bf16x8{};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) af[u][j] = (live && aok[j]) ? load_frag(arow[j], k, p.K, vec_ok, ss[j]) : bf16x8{};
+      for (int j = 0; j < 4; ++j) af[u][j] = live ? at[((int64_t)j * kb + ks0 + u) * 64] : bf16x8{};
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before the first wait
 #pragma unroll
-    for (int u = 0; u < KB; ++u)
+    for (int u = 0; u < KB; ++u) {
+      if constexpr (NORM) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = bf2f(af[u][j][i]);
+            ss[j] += x * x;
+          }
+      }
 #pragma unroll
       for (int jn = 0; jn < NT; ++jn)
 #pragma unroll
         for (int jm = 0; jm < 4; ++jm) acc[jn][jm] = mfma16x16x32(wf[u][jn], af[u][jm], acc[jn][jm]);
+    }
   }
-  (void)ss_w;
 
   // partial tiles and partial row sums of squares to LDS
 #pragma unroll
@@ -195,13 +154,24 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = f2bf(r[i]);
       *reinterpret_cast<bf16x4*>(dst) = v;
+    } else if constexpr (EPI == EPI_RESID) {
+      // h += o W_o^T, and r(h) for the next projection (N is a multiple of 64)
+      f32x4* dst = reinterpret_cast<f32x4*>(p.out + (int64_t)m * p.N + nb);
+      f32x4 hv = *dst;
+      hv += r;
+      *dst = hv;
+      bf16x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = f2bf(hv[i]);
+      *reinterpret_cast<bf16x4*>(p.a_out + tiled_offset(m, nb, p.N)) = v;
     } else {
-      float* dst = p.out + p.omap(m) * p.N + nb;
+      const int j = m % p.S;
+      if (j == 0) continue;                          // state token: no velocity
+      float* dst = p.out + ((int64_t)(m / p.S) * (p.S - 1) + j - 1) * p.N + nb;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (nb + i >= p.N) break;
-        if constexpr (EPI == EPI_RESID) dst[i] += r[i];
-        else if constexpr (EPI == EPI_VEL) dst[i] = r[i] + p.bias[nb + i];
+        if constexpr (EPI == EPI_VEL) dst[i] = r[i] + p.bias[nb + i];
         else dst[i] += p.dt * (r[i] + p.bias[nb + i]);
       }
     }
@@ -209,11 +179,13 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
 }
 
 // Suffix tokens: row m = b*S + j; j = 0 the state token, j >= 1 action j-1.
-// Contraction length is the action dim (<= 64): plain fp32 dot products.
+// Contraction length is the action dim (<= 64): plain fp32 dot products.  Writes
+// h (fp32, row-major) and r(h) (tile layout).
 __global__ void __launch_bounds__(256)
 embed_kernel(const float* __restrict__ x, const float* __restrict__ state, const __bf16* __restrict__ w_state,
              const float* __restrict__ b_state, const __bf16* __restrict__ w_in, const float* __restrict__ b_in,
-             const float* __restrict__ w_time, float t, float* __restrict__ h, int H, int A, int W) {
+             const float* __restrict__ w_time, float t, float* __restrict__ h, __bf16* __restrict__ a,
+             int H, int A, int W) {
   __shared__ float in[64];
   const int m = blockIdx.y;
   const int S = H + 1;
@@ -228,6 +200,20 @@ embed_kernel(const float* __restrict__ x, const float* __restrict__ state, const
   for (int k = 0; k < A; ++k) acc += in[k] * bf2f(wr[k]);
   acc += (j == 0) ? b_state[n] : (b_in[n] + t * w_time[n]);
   h[(int64_t)m * W + n] = acc;
+  a[tiled_offset(m, n, W)] = f2bf(acc);
+}
+
+// Weights [rows x K] row-major -> operand tile layout at row offset row0 of a
+// matrix with rows_pad rows; rows in [rows, rows_pad) are zero.  One thread per
+// 8 elements.
+__global__ void repack_kernel(const __bf16* __restrict__ src, __bf16* __restrict__ dst, int rows, int rows_pad,
+                              int row0, int K) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int k8 = K / 8;
+  if (i >= (int64_t)rows_pad * k8) return;
+  const int r = (int)(i / k8), k = (int)(i % k8) * 8;
+  const bf16x8 v = r < rows ? *reinterpret_cast<const bf16x8*>(src + (int64_t)r * K + k) : bf16x8{};
+  *reinterpret_cast<bf16x8*>(dst + tiled_offset(row0 + r, k, K)) = v;
 }
 
 __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, float dt, int64_t n) {
@@ -248,29 +234,39 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
 // the few rows of a small batch (each wave then waits on a single short batch of
 // loads), 64 x 64 tiles with four waves once the rows alone give enough
 // workgroups.
-template <int EPI, typename TA, bool NORM>
+template <int EPI, bool NORM>
 pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
   if (a.M <= 256) {
     dim3 grid((a.N + 15) / 16, (a.M + 63) / 64);
-    gemm_kernel<EPI, TA, NORM, 1, 16><<<grid, 1024, 0, s>>>(a);
+    gemm_kernel<EPI, NORM, 1, 16><<<grid, 1024, 0, s>>>(a);
   } else {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-    gemm_kernel<EPI, TA, NORM, 4, 4><<<grid, 256, 0, s>>>(a);
+    gemm_kernel<EPI, NORM, 4, 4><<<grid, 256, 0, s>>>(a);
   }
   return pi::check_launch(name);
 }
 
 struct FlowWs {
-  float* h;
-  __bf16 *q, *k, *v, *o;
+  float* h;           // residual stream [Mpad x W] fp32
+  __bf16* a;          // r(h), tile layout [Mpad x W]
+  __bf16 *q, *k, *v;  // projections, row-major [B*S x Hq*d | Hkv*d | Hkv*d]
+  __bf16* o;          // decode output, tile layout [Mpad x Hq*d]
+  __bf16* w_qkv;      // repacked weights, tile layout
+  __bf16* w_o;
+  __bf16* w_out;
   float* vel;
   void* dec;          // decode key-split partials
   size_t dec_bytes;
   size_t total;
 };
 
+inline int pad64(int m) { return (m + 63) / 64 * 64; }
+inline int pad16(int m) { return (m + 15) / 16 * 16; }
+
 FlowWs flow_layout(const pi_velocity_net* n, int B, int H, char* base) {
   const size_t S = (size_t)H + 1;
+  const size_t M = B * S, Mp = pad64((int)M);
+  const size_t nq = (size_t)n->Hq * n->d, nkv = (size_t)n->Hkv * n->d, W = n->width;
   size_t off = 0;
   FlowWs w;
   auto take = [&](size_t bytes) {
@@ -278,11 +274,15 @@ FlowWs flow_layout(const pi_velocity_net* n, int B, int H, char* base) {
     off = pi::align_up(off + bytes, 256);
     return base ? base + at : nullptr;
   };
-  w.h = reinterpret_cast<float*>(take(sizeof(float) * B * S * n->width));
-  w.q = reinterpret_cast<__bf16*>(take(2 * B * S * n->Hq * n->d));
-  w.k = reinterpret_cast<__bf16*>(take(2 * B * S * n->Hkv * n->d));
-  w.v = reinterpret_cast<__bf16*>(take(2 * B * S * n->Hkv * n->d));
-  w.o = reinterpret_cast<__bf16*>(take(2 * B * S * n->Hq * n->d));
+  w.h = reinterpret_cast<float*>(take(sizeof(float) * Mp * W));
+  w.a = reinterpret_cast<__bf16*>(take(2 * Mp * W));
+  w.q = reinterpret_cast<__bf16*>(take(2 * M * nq));
+  w.k = reinterpret_cast<__bf16*>(take(2 * M * nkv));
+  w.v = reinterpret_cast<__bf16*>(take(2 * M * nkv));
+  w.o = reinterpret_cast<__bf16*>(take(2 * Mp * nq));
+  w.w_qkv = reinterpret_cast<__bf16*>(take(2 * (nq + 2 * nkv) * W));
+  w.w_o = reinterpret_cast<__bf16*>(take(2 * W * nq));
+  w.w_out = reinterpret_cast<__bf16*>(take(2 * (size_t)pad16(n->action_dim) * W));
   w.vel = reinterpret_cast<float*>(take(sizeof(float) * B * H * n->action_dim));
   w.dec_bytes = pi::decode_workspace_max(B, (int)S, n->Hq);
   w.dec = w.dec_bytes ? take(w.dec_bytes) : nullptr;
@@ -312,6 +312,24 @@ pi_status check_net(const pi_velocity_net* n, const pi_kv_cache* cache, const ui
   return PI_OK;
 }
 
+pi_status repack(const void* src, __bf16* dst, int rows, int rows_pad, int row0, int K, hipStream_t s) {
+  const int64_t n = (int64_t)rows_pad * (K / 8);
+  repack_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<const __bf16*>(src), dst, rows, rows_pad,
+                                                              row0, K);
+  return pi::check_launch("repack_kernel");
+}
+
+// Weights into the operand tile layout (once per sampler or velocity call).
+pi_status repack_weights(const pi_velocity_net* n, const FlowWs& w, hipStream_t s) {
+  const int W = n->width, nq = n->Hq * n->d, nkv = n->Hkv * n->d;
+  pi_status st = repack(n->w_q, w.w_qkv, nq, nq, 0, W, s);
+  if (st == PI_OK) st = repack(n->w_k, w.w_qkv, nkv, nkv, nq, W, s);
+  if (st == PI_OK) st = repack(n->w_v, w.w_qkv, nkv, nkv, nq + nkv, W, s);
+  if (st == PI_OK) st = repack(n->w_o, w.w_o, W, W, 0, nq, s);
+  if (st == PI_OK) st = repack(n->w_out, w.w_out, n->action_dim, pad16(n->action_dim), 0, W, s);
+  return st;
+}
+
 // v = net(x, t) into `vel` (EPI_VEL) or fused x += dt*v (EPI_EULER, vel ignored).
 template <int EPI>
 pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint8_t* suffix_ar,
@@ -324,62 +342,54 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
   {
     dim3 grid((W + 255) / 256, M);
     embed_kernel<<<grid, 256, 0, s>>>(x, state, static_cast<const __bf16*>(n->w_state), n->b_state,
-                                      static_cast<const __bf16*>(n->w_in), n->b_in, n->w_time, t, w.h, H, A, W);
+                                      static_cast<const __bf16*>(n->w_in), n->b_in, n->w_time, t, w.h, w.a, H, A, W);
     pi_status st = pi::check_launch("embed_kernel");
     if (st != PI_OK) return st;
   }
   for (int layer = 0; layer < cache->layers; ++layer) {
     GemmArgs g{};
-    g.a = w.h;
-    g.amap = RowMap{M, 0, 0};
-    g.w0 = static_cast<const __bf16*>(n->w_q);
-    g.w1 = static_cast<const __bf16*>(n->w_k);
-    g.w2 = static_cast<const __bf16*>(n->w_v);
-    g.n1 = nq;
-    g.n2 = nkv;
+    g.a = w.a;
+    g.w = w.w_qkv;
     g.M = M;
     g.N = nq + 2 * nkv;
     g.K = W;
+    g.n1 = nq;
+    g.n2 = nkv;
     g.o0 = w.q;
     g.o1 = w.k;
     g.o2 = w.v;
-    pi_status st = gemm<EPI_QKV, float, true>(g, s, "gemm_qkv");
+    pi_status st = gemm<EPI_QKV, true>(g, s, "gemm_qkv");
     if (st != PI_OK) return st;
-    st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, w.dec, w.dec_bytes,
-                               s);
+    st = pi::decode_layer(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, true, w.dec, w.dec_bytes,
+                          s);
     if (st != PI_OK) return st;
     GemmArgs go{};
     go.a = w.o;
-    go.amap = RowMap{M, 0, 0};
-    go.w0 = go.w1 = go.w2 = static_cast<const __bf16*>(n->w_o);
-    go.n1 = W;
-    go.n2 = 0;
+    go.w = w.w_o;
     go.M = M;
     go.N = W;
     go.K = nq;
     go.out = w.h;
-    go.omap = RowMap{M, 0, 0};
-    st = gemm<EPI_RESID, __bf16, false>(go, s, "gemm_out_resid");
+    go.a_out = w.a;
+    st = gemm<EPI_RESID, false>(go, s, "gemm_out_resid");
     if (st != PI_OK) return st;
   }
+  // velocity over every token row; the epilogue drops the state token rows
   GemmArgs gv{};
-  gv.a = w.h;
-  gv.amap = RowMap{H, S, 1};  // action tokens of sample b are h rows b*S + 1 ..
-  gv.w0 = gv.w1 = gv.w2 = static_cast<const __bf16*>(n->w_out);
-  gv.n1 = A;
-  gv.n2 = 0;
-  gv.M = B * H;
+  gv.a = w.a;
+  gv.w = w.w_out;
+  gv.M = M;
   gv.N = A;
   gv.K = W;
+  gv.S = S;
   gv.bias = n->b_out;
-  gv.omap = RowMap{B * H, 0, 0};
   gv.dt = dt;
   if (EPI == EPI_EULER) {
     gv.out = x;
-    return gemm<EPI_EULER, float, true>(gv, s, "gemm_velocity_euler");
+    return gemm<EPI_EULER, true>(gv, s, "gemm_velocity_euler");
   }
   gv.out = vel;
-  return gemm<EPI_VEL, float, true>(gv, s, "gemm_velocity");
+  return gemm<EPI_VEL, true>(gv, s, "gemm_velocity");
 }
 
 }  // namespace
@@ -411,8 +421,10 @@ extern "C" pi_status pi_velocity_eval(const pi_velocity_net* net, const pi_kv_ca
              w.total);
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_velocity_eval: workspace must be 256-byte aligned");
-  return run_net<EPI_VEL>(net, cache, suffix_ar, state, const_cast<float*>(x), t, 0.f, vel, B, H, A, w,
-                          static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = repack_weights(net, w, s);
+  if (st != PI_OK) return st;
+  return run_net<EPI_VEL>(net, cache, suffix_ar, state, const_cast<float*>(x), t, 0.f, vel, B, H, A, w, s);
 }
 
 extern "C" pi_status pi_flow_sample(const pi_velocity_net* net, const pi_kv_cache* cache, const uint8_t* suffix_ar,
@@ -439,6 +451,8 @@ extern "C" pi_status pi_flow_sample(const pi_velocity_net* net, const pi_kv_cach
              w.total);
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_flow_sample: workspace must be 256-byte aligned");
+  st = repack_weights(net, w, s);
+  if (st != PI_OK) return st;
   for (int k = 0; k < num_steps; ++k) {
     const float t = (float)(1.0 + k * dt);
     st = run_net<EPI_EULER>(net, cache, suffix_ar, state, x, t, (float)dt, nullptr, B, H, A, w, s);

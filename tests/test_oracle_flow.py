@@ -124,7 +124,7 @@ def _net_fp32(x, t, state, w, ck, cv, pm, sar):
     vis = torch.from_numpy(decode_mask(pm, np.ones((B, S), np.uint8), sar))
     for layer in range(ck.shape[0]):
         a = r(h)
-        rr = torch.sqrt((h * h).mean(-1, keepdim=True) + 1e-6)
+        rr = torch.sqrt((a * a).mean(-1, keepdim=True) + 1e-6)
         q = r(a @ W["w_q"].T / rr).view(B, S, 8, 256)
         k, v = r(a @ W["w_k"].T / rr), r(a @ W["w_v"].T / rr)
         kk = torch.cat([torch.from_numpy(ck[layer][:, :, 0].astype(np.float32)), k], 1)
@@ -133,8 +133,8 @@ def _net_fp32(x, t, state, w, ck, cv, pm, sar):
         s = s.masked_fill(~vis[:, :, None, :], float("-inf"))
         o = r(torch.einsum("bshk,bkd->bshd", torch.softmax(s, -1), vv))
         h = h + o.reshape(B, S, 2048) @ W["w_o"].T
-    hh = h[:, 1:]
-    return (r(hh) @ W["w_out"].T / torch.sqrt((hh * hh).mean(-1, keepdim=True) + 1e-6) + W["b_out"]).numpy()
+    aa = r(h[:, 1:])
+    return (aa @ W["w_out"].T / torch.sqrt((aa * aa).mean(-1, keepdim=True) + 1e-6) + W["b_out"]).numpy()
 
 
 def test_net_tolerance_is_twice_the_fp32_floor():
