@@ -415,10 +415,14 @@ struct RowMajorDst {
 };
 
 // Row setup: Q fragments into registers, the row's query word and output row.
+// q_tiled (decode only, G == Hq): this sample's queries as rows t*G + head of a
+// matrix in the operand tile layout, padded to whole 16-row blocks, so each
+// fragment is one contiguous 1 KB load.
 template <int D, int G, int NR, int ROWS_W>
 __device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_base, const __bf16* __restrict__ q,
                                           __bf16* __restrict__ o, int64_t tok_base, int ntok, int Hq, int head0,
-                                          int tok0, const uint32_t* words) {
+                                          int tok0, const uint32_t* words,
+                                          const __bf16* __restrict__ q_tiled = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -428,12 +432,23 @@ __device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_bas
     const int h = head0 + row % G;
     const bool ok = t < ntok;
     st.wq[r] = ok ? words[t] : 0u;
-    const __bf16* qrow = q + ((tok_base + (ok ? t : 0)) * Hq + h) * D;
+    if (q_tiled != nullptr) {
+      const int r0 = tok0 * G + wave * ROWS_W + r * 16;     // first row of the block, wave-uniform
+      const bf16x8* src = reinterpret_cast<const bf16x8*>(q_tiled) + (int64_t)(r0 / 16) * (D / 32) * 64 + lane;
 #pragma unroll
-    for (int ds = 0; ds < D / 32; ++ds) {
-      bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
-      if (!ok) val = bf16x8{};
-      st.qf[r][ds] = val;
+      for (int ds = 0; ds < D / 32; ++ds) {
+        bf16x8 val = r0 < ntok * G ? src[ds * 64] : bf16x8{};
+        if (!ok) val = bf16x8{};
+        st.qf[r][ds] = val;
+      }
+    } else {
+      const __bf16* qrow = q + ((tok_base + (ok ? t : 0)) * Hq + h) * D;
+#pragma unroll
+      for (int ds = 0; ds < D / 32; ++ds) {
+        bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
+        if (!ok) val = bf16x8{};
+        st.qf[r][ds] = val;
+      }
     }
     row_base[r] = ok ? o + ((tok_base + t) * Hq + h) * D : nullptr;
   }
@@ -540,7 +555,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               const uint8_t* __restrict__ prefix_mask, int cap, int P,
               const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
               const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
-              __bf16* __restrict__ os, int o_tiled, Placement place, int n_split, float* __restrict__ opart,
+              __bf16* __restrict__ os, int tiled, Placement place, int n_split, float* __restrict__ opart,
               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
@@ -614,7 +629,8 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   WaveState<D, NR> st;
   init_state(st);
   __bf16* row_base[NR];
-  load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, sbid);
+  const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
+  load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, sbid, q_tiled);
 
   const i32x4 rk = make_rsrc(ck + (size_t)b * cap * D);
   const i32x4 rv = make_rsrc(cv + (size_t)b * cap * D);
@@ -641,7 +657,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     run();
   }
   if (n_split == 1) {
-    if (o_tiled) {
+    if (tiled) {
       const int c = lane & 15, g = lane >> 4;
       auto dst = [&](int r, int dt) -> __bf16* {
         const int row = wave * C::ROWS_W + r * 16 + c;
@@ -848,7 +864,7 @@ extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
 }
 
 pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
-                           const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool o_tiled,
+                           const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool tiled,
                            void* workspace, size_t workspace_bytes, hipStream_t s) {
   PI_REQUIRE(cache && q_s && k_s && v_s && suffix_ar && o_s, PI_ERR_INVALID_ARG,
              "pi_suffix_decode_step: null pointer");
@@ -887,11 +903,11 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   decode_kernel<256, 8, kNR256, kNW256><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
       static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
-      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), o_tiled ? 1 : 0, place, splits, opart, mlpart);
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart);
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
   decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
-      opart, mlpart, static_cast<__bf16*>(o_s), o_tiled ? 1 : 0, B, S, n_qblk, splits);
+      opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits);
   return pi::check_launch("decode_combine_kernel");
 }
 

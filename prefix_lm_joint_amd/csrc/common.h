@@ -75,11 +75,12 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Largest decode workspace any cache length can ask for at this batch shape.
 size_t decode_workspace_max(int B, int S, int Hq);
-// Cached suffix decode of one layer (arguments checked by the caller); the output
-// is row-major [B, S, Hq, d] or, with o_tiled, the operand tile layout of the
-// [B*S x Hq*d] matrix.
+// Cached suffix decode of one layer.  q_s and o_s are row-major [B, S, Hq, d],
+// or with `tiled` both are in the operand tile layout (tiled_offset): q_s as the
+// rows t*Hq + head of each sample, each sample's rows padded to whole 16-row
+// blocks; o_s as the [B*S x Hq*d] matrix.
 pi_status decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
-                       const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool o_tiled,
+                       const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool tiled,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 }  // namespace pi
 

@@ -36,12 +36,12 @@ struct GemmArgs {
   const __bf16* w;     // weights [N (padded to 16) x K], operand tile layout
   int M, N, K;
   int n1, n2;          // EPI_QKV: output column split q | k | v
-  __bf16* o0;          // EPI_QKV outputs, row-major, row strides n1, n2, N - n1 - n2
+  __bf16* o0;          // EPI_QKV outputs: q in the decode's tile layout, k / v row-major
   __bf16* o1;
   __bf16* o2;
   float* out;          // EPI_RESID: h [M x N] fp32; EPI_VEL / EPI_EULER: [B*H x N]
   __bf16* a_out;       // EPI_RESID: r(h) in tile layout, row width N
-  int S;               // EPI_VEL / EPI_EULER: tokens per sample (row m % S == 0 is the state token)
+  int S;               // tokens per sample (row m % S == 0 is the state token)
   const float* bias;   // EPI_VEL / EPI_EULER
   float dt;            // EPI_EULER
 };
@@ -146,9 +146,13 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
       r *= rsqrtf(t / (float)p.K + kRmsEps);
     }
     if constexpr (EPI == EPI_QKV) {
+      // q in the decode's tile layout (rows t*8 + head per sample, padded to 16),
+      // k and v row-major
       __bf16* dst;
-      if (nb < p.n1) dst = p.o0 + (int64_t)m * p.n1 + nb;
-      else if (nb < p.n1 + p.n2) dst = p.o1 + (int64_t)m * p.n2 + (nb - p.n1);
+      if (nb < p.n1) {
+        const int64_t qrow = (int64_t)(m / p.S) * ((p.S * 8 + 15) / 16 * 16) + (m % p.S) * 8 + nb / 256;
+        dst = p.o0 + tiled_offset(qrow, nb % 256, 256);
+      } else if (nb < p.n1 + p.n2) dst = p.o1 + (int64_t)m * p.n2 + (nb - p.n1);
       else dst = p.o2 + (int64_t)m * (p.N - p.n1 - p.n2) + (nb - p.n1 - p.n2);
       bf16x4 v;
 #pragma unroll
@@ -249,7 +253,8 @@ pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
 struct FlowWs {
   float* h;           // residual stream [Mpad x W] fp32
   __bf16* a;          // r(h), tile layout [Mpad x W]
-  __bf16 *q, *k, *v;  // projections, row-major [B*S x Hq*d | Hkv*d | Hkv*d]
+  __bf16* q;          // queries, the decode's tile layout [B x pad16(S*Hq) x d]
+  __bf16 *k, *v;      // suffix keys / values, row-major [B*S x Hkv*d]
   __bf16* o;          // decode output, tile layout [Mpad x Hq*d]
   __bf16* w_qkv;      // repacked weights, tile layout
   __bf16* w_o;
@@ -276,7 +281,7 @@ FlowWs flow_layout(const pi_velocity_net* n, int B, int H, char* base) {
   };
   w.h = reinterpret_cast<float*>(take(sizeof(float) * Mp * W));
   w.a = reinterpret_cast<__bf16*>(take(2 * Mp * W));
-  w.q = reinterpret_cast<__bf16*>(take(2 * M * nq));
+  w.q = reinterpret_cast<__bf16*>(take(2 * B * (size_t)pad16((int)S * n->Hq) * n->d));
   w.k = reinterpret_cast<__bf16*>(take(2 * M * nkv));
   w.v = reinterpret_cast<__bf16*>(take(2 * M * nkv));
   w.o = reinterpret_cast<__bf16*>(take(2 * Mp * nq));
@@ -358,6 +363,7 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
     g.o0 = w.q;
     g.o1 = w.k;
     g.o2 = w.v;
+    g.S = S;
     pi_status st = gemm<EPI_QKV, true>(g, s, "gemm_qkv");
     if (st != PI_OK) return st;
     st = pi::decode_layer(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, true, w.dec, w.dec_bytes,
