@@ -73,11 +73,17 @@ mask_scan_kernel(const uint8_t* __restrict__ input_mask, const uint8_t* __restri
   }
 }
 
-// One thread per (b, query tile, key tile): classify the tile.  A key tile that
-// runs past N is never FULL, so the attention kernels always mask its padding.
-__global__ void mask_tiles_kernel(const uint32_t* __restrict__ tok, int B, int N, int n_qt, int n_kt,
-                                  uint32_t forbid, uint8_t* __restrict__ tiles) {
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// One wave per (b, query tile, key tile): classify the tile.  Lane l takes key
+// k0 + l % 32 against the query rows q0 + l / 32 + 2r; ballots count the visible
+// and in-range pairs.  A key tile that runs past N is never FULL, so the
+// attention kernels always mask its padding.
+static_assert(PI_MASK_TILE_K == 32 && PI_MASK_TILE_Q % 2 == 0, "mask_tiles_kernel maps 32 keys x 2 rows per pass");
+
+__global__ void __launch_bounds__(256)
+mask_tiles_kernel(const uint32_t* __restrict__ tok, int B, int N, int n_qt, int n_kt, uint32_t forbid,
+                  uint8_t* __restrict__ tiles) {
+  const int lane = threadIdx.x & 63;
+  const int64_t id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t total = (int64_t)B * n_qt * n_kt;
   if (id >= total) return;
   const int kt = (int)(id % n_kt);
@@ -86,18 +92,23 @@ __global__ void mask_tiles_kernel(const uint32_t* __restrict__ tok, int B, int N
   const uint32_t* t = tok + (size_t)b * N;
   const int q0 = qt * PI_MASK_TILE_Q, q1 = min(N, q0 + PI_MASK_TILE_Q);
   const int k0 = kt * PI_MASK_TILE_K, k1 = min(N, k0 + PI_MASK_TILE_K);
+  const int j = k0 + (lane & 31);
+  const uint32_t wk = j < k1 ? t[j] : 0u;
   int vis = 0, pairs = 0;
-  for (int i = q0; i < q1; ++i) {
-    uint32_t wq = t[i];
-    for (int j = k0; j < k1; ++j) {
-      vis += pair_visible(wq, t[j], forbid);
-      ++pairs;
-    }
+#pragma unroll
+  for (int r = 0; r < PI_MASK_TILE_Q / 2; ++r) {
+    const int i = q0 + (lane >> 5) + 2 * r;
+    const bool in = i < q1 && j < k1;
+    const uint32_t wq = i < q1 ? t[i] : 0u;
+    vis += __popcll(__ballot(in && pair_visible(wq, wk, forbid)));
+    pairs += __popcll(__ballot(in));
   }
-  uint8_t cls = PI_TILE_PARTIAL;
-  if (vis == 0) cls = PI_TILE_EMPTY;
-  else if (vis == pairs && (k1 - k0) == PI_MASK_TILE_K) cls = PI_TILE_FULL;
-  tiles[id] = cls;
+  if (lane == 0) {
+    uint8_t cls = PI_TILE_PARTIAL;
+    if (vis == 0) cls = PI_TILE_EMPTY;
+    else if (vis == pairs && (k1 - k0) == PI_MASK_TILE_K) cls = PI_TILE_FULL;
+    tiles[id] = cls;
+  }
 }
 
 __global__ void mask_dense_kernel(const uint32_t* __restrict__ tok, int N, uint32_t forbid,
@@ -164,9 +175,9 @@ extern "C" pi_status pi_mask_build(const uint8_t* input_mask, const uint8_t* ar,
   pi_status st = pi::check_launch("mask_scan_kernel");
   if (st != PI_OK) return st;
   int64_t ntiles = (int64_t)B * L.n_qt * L.n_kt;
-  int threads = 256;
-  int64_t blocks = (ntiles + threads - 1) / threads;
-  mask_tiles_kernel<<<(unsigned)blocks, threads, 0, s>>>(m.tok, B, N, L.n_qt, L.n_kt, forbid_bits, m.tiles);
+  const int64_t blocks = (ntiles + 3) / 4;   // four waves of 64 per workgroup, one tile each
+  PI_REQUIRE(blocks < (1ll << 31), PI_ERR_UNSUPPORTED, "pi_mask_build: too many tiles");
+  mask_tiles_kernel<<<(unsigned)blocks, 256, 0, s>>>(m.tok, B, N, L.n_qt, L.n_kt, forbid_bits, m.tiles);
   st = pi::check_launch("mask_tiles_kernel");
   if (st != PI_OK) return st;
   *out = m;
