@@ -104,21 +104,51 @@ __device__ __forceinline__ PI_LDS uint32_t* lds_u32(const void* p) {
   return (PI_LDS uint32_t*)(const_cast<void*>(p));
 }
 
-// Issue this wave's share of the direct-to-LDS loads of one K/V tile: keys whose
-// bit is clear in `keymask` (past the end, padding) are fetched from an
-// out-of-range offset and land as zeros.  tsb = bytes between consecutive tokens.
+// This wave's share of the direct-to-LDS loads of one K/V tile: the per-lane
+// byte offsets within a tile (row r of the tile at r * tsb, the row's swizzle
+// folded in) are computed once; each tile then only moves the resource base.
 template <int D, int NW>
-__device__ __forceinline__ void issue_kv(Stage<D>& st, i32x4 rk, i32x4 rv, int key0, int tsb, uint32_t keymask) {
+struct KvLanes {
+  static constexpr int N = (Tile<D>::INSTS + NW - 1) / NW;   // loads per tensor and wave
+  uint32_t k[N], v[N];
+  int row[N];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ KvLanes<D, NW> kv_lanes(int tsb) {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int p = lane % T::CHR;
+  KvLanes<D, NW> kl;
 #pragma unroll
-  for (int q = wave; q < T::INSTS; q += NW) {
-    const int r = q * T::RPI + lane / T::CHR;
-    const bool live = (keymask >> r) & 1u;
-    const uint32_t base = (uint32_t)(key0 + r) * (uint32_t)tsb;
-    const uint32_t ok = live ? base + 16u * (uint32_t)(p ^ T::fk(r)) : kOOB;
-    const uint32_t ov = live ? base + 16u * (uint32_t)(p ^ T::fv(r)) : kOOB;
+  for (int j = 0; j < KvLanes<D, NW>::N; ++j) {
+    const int r = (wave + j * NW) * T::RPI + lane / T::CHR;
+    kl.row[j] = r;
+    kl.k[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fk(r));
+    kl.v[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fv(r));
+  }
+  return kl;
+}
+
+// Issue the loads of the tile whose first key is key0 (k0, v0: key 0 of this
+// sample and head; tsb bytes between consecutive keys).  Keys whose bit is clear
+// in `keymask` (past the end, padding) are fetched from an out-of-range offset
+// and land as zeros.
+template <int D, int NW>
+__device__ __forceinline__ void issue_kv(Stage<D>& st, const KvLanes<D, NW>& kl, const __bf16* k0,
+                                         const __bf16* v0, int key0, int tsb, uint32_t keymask) {
+  using T = Tile<D>;
+  const int wave = threadIdx.x >> 6;
+  const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(key0) * tsb;
+  const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(k0) + at);
+  const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(v0) + at);
+  const bool full = __builtin_amdgcn_readfirstlane(keymask) == 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < KvLanes<D, NW>::N; ++j) {
+    const int q = wave + j * NW;
+    if (q >= T::INSTS) break;
+    uint32_t ok = kl.k[j], ov = kl.v[j];
+    if (!full && !((keymask >> kl.row[j]) & 1u)) ok = ov = kOOB;
     pi_buffer_load_lds(rk, lds_u32(&st.k[q * T::RPI * D]), 16, (int)ok, 0, 0, 0);
     pi_buffer_load_lds(rv, lds_u32(&st.v[q * T::RPI * D]), 16, (int)ov, 0, 0, 0);
   }
@@ -136,14 +166,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
 // (scores already multiplied by scale*log2(e)), fixed at the row's first tile
 // with a visible key and the same in the four lanes that share a row; mobs is
 // this lane's running maximum over its own scores (reduced across the row only
-// at the end); all_set is true once every row of the wave has its reference.
+// at the end); l is the row sums of the weights, accumulated on the matrix cores
+// as 1^T P^T (so every lane of a row holds the row's sum in l[r][0]); all_set is
+// true once every row of the wave has its reference.
 template <int D, int NR>
 struct WaveState {
   bf16x8 qf[NR][D / 32];
   f32x4 o[NR][D / 16];
+  f32x4 l[NR];
   float m[NR];
   float mobs[NR];
-  float l[NR];
   uint32_t wq[NR];
   bool all_set;
 };
@@ -212,14 +244,13 @@ __device__ __forceinline__ void qk_tile(const Stage<D>& sm, const LaneOffsets<D>
   }
 }
 
-// Mask (PARTIAL tiles), softmax weights and O^T += V^T P^T for one tile whose
-// scores are in s.  cls: PI_TILE_FULL or PI_TILE_PARTIAL.
+// Softmax of one tile on the vector units: masks, maxima and the bf16 weights
+// P^T (the B operand of the PV product) against the rows' reference maxima.
 template <int D, int NR>
-__device__ __forceinline__ void softmax_pv(const Stage<D>& sm, const LaneOffsets<D>& lo, WaveState<D, NR>& st,
-                                           f32x4 (&s)[NR][2], int cls, uint32_t forbid, float scale_log2) {
+__device__ __forceinline__ void softmax_tile(const Stage<D>& sm, WaveState<D, NR>& st, f32x4 (&s)[NR][2],
+                                             bf16x8 (&pf)[NR], int cls, uint32_t forbid, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
-  constexpr uint32_t HALF = 16u * D * 2u;
   const float NEG_INF = -INFINITY;
   if (cls == PI_TILE_PARTIAL) {
 #pragma unroll
@@ -255,34 +286,65 @@ __device__ __forceinline__ void softmax_pv(const Stage<D>& sm, const LaneOffsets
   for (int r = 0; r < NR; ++r) {
     // a row that has seen no visible key keeps m = -inf: use 0 so masked weights are exp2(-inf) = 0
     const float m_use = (st.m[r] == NEG_INF) ? 0.f : st.m[r];
-    bf16x8 pf;
-    float lsum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // l sums the weights as rounded for the matrix cores, so the final 1/l
-        // normalises exactly the weights that multiplied V
-        const __bf16 pb = f2bf(fast_exp2(fmaf(s[r][kt][i], scale_log2, -m_use)));
-        pf[4 * kt + i] = pb;
-        lsum += bf2f(pb);
-      }
-    st.l[r] += lsum;
-    // O^T[dt] += V^T[dt rows, 32 keys] . P^T[32 keys, 16 rows]
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const bf16x4 lo4 = lds_read_tr4(at_bytes<__bf16>(sm.v, lo.v[dt]));
-      const bf16x4 hi4 = lds_read_tr4(at_bytes<__bf16>(sm.v, lo.v[dt] + HALF));
-      const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-      st.o[r][dt] = mfma16x16x32(a, pf, st.o[r][dt]);
-    }
+      for (int i = 0; i < 4; ++i) pf[r][4 * kt + i] = f2bf(fast_exp2(fmaf(s[r][kt][i], scale_log2, -m_use)));
   }
 }
 
-// Tile loop shared by both kernels, software-pipelined over three LDS stages:
-// while tile i's softmax and PV run, tile i+1's scores are computed (its K is
-// already in LDS) and tile i+2 streams in.  Tile j lives in stage j % 3; the loop
-// is unrolled by three so every LDS address is a per-lane offset plus a constant.
+// The matrix-core work of one pipeline step, as one straight-line block:
+// O^T += V^T P^T and l += 1^T P^T for the current tile (the row sums of exactly
+// the bf16 weights that multiply V), interleaved fragment by fragment with
+// S^T = K Q^T of the next tile when QK, so the LDS reads of both products are in
+// flight together.  Both products take D/16 fragments.
+template <int D, int NR, bool QK>
+__device__ __forceinline__ void mma_step(const Stage<D>& cur, const Stage<D>& nxt, const LaneOffsets<D>& lo,
+                                         WaveState<D, NR>& st, const bf16x8 (&pf)[NR], f32x4 (&s)[NR][2]) {
+  constexpr uint32_t HALF = 16u * D * 2u;
+  if constexpr (QK) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = f2bf(1.0f);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) st.l[r] = mfma16x16x32(ones, pf[r], st.l[r]);
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    const bf16x4 lo4 = lds_read_tr4(at_bytes<__bf16>(cur.v, lo.v[j]));
+    const bf16x4 hi4 = lds_read_tr4(at_bytes<__bf16>(cur.v, lo.v[j] + HALF));
+    const bf16x8 va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) st.o[r][j] = mfma16x16x32(va, pf[r], st.o[r][j]);
+    if constexpr (QK) {
+      const int ds = j >> 1, kt = j & 1;
+      const bf16x8 ka = *at_bytes<bf16x8>(nxt.k, lo.k[ds] + kt * HALF);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) s[r][kt] = mfma16x16x32(ka, st.qf[r][ds], s[r][kt]);
+    }
+  }
+  // schedule: the reads of the next AHEAD fragments are in flight while
+  // fragment j's products issue (bounded read-ahead keeps the registers in budget)
+  constexpr int RD = QK ? 3 : 2, MF = QK ? 2 * NR : NR, AHEAD = 4;
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RD, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+    if (j + AHEAD < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+  }
+}
+
+// Tile loop shared by both kernels, software-pipelined over three LDS stages
+// (tile j lives in stage (j - i_lo) % 3; the loop is unrolled by three so every
+// LDS address is a per-lane offset plus a constant).  Step i runs tile i's
+// softmax on the vector units, then one matrix-core block with tile i's PV
+// interleaved with tile i+1's scores (its K is already in LDS), while tile i+2
+// streams in.
 //   issue(j, stage): start the loads of tile j into `stage` (all waves take part)
 //   cls(j): PI_TILE_FULL or PI_TILE_PARTIAL
 template <int D, int NR, typename Issue, typename Cls>
@@ -296,17 +358,15 @@ __device__ __forceinline__ void run_tiles(Stage<D> (&stage)[3], const LaneOffset
   __syncthreads();
   f32x4 s_cur[NR][2];
   qk_tile<D, NR>(stage[0], lo, st, s_cur);
+  bf16x8 pf[NR];
   auto step = [&](int i, Stage<D>& cur, Stage<D>& nxt, Stage<D>& free_st) {
     wait_vmem();          // this wave's loads of tile i+1 have landed
     __syncthreads();      // ... everyone's; and everyone is done with tile i-1
     if (i + 2 < i_hi) issue(i + 2, free_st);
-    f32x4 s_nxt[NR][2];
-    if (i + 1 < i_hi) qk_tile<D, NR>(nxt, lo, st, s_nxt);
-    softmax_pv<D, NR>(cur, lo, st, s_cur, cls(i), forbid, scale_log2);
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s_cur[r][kt] = s_nxt[r][kt];
+    softmax_tile<D, NR>(cur, st, s_cur, pf, cls(i), forbid, scale_log2);
+    // the last step also multiplies whatever stage `nxt` holds and discards it,
+    // which keeps the block free of branches
+    mma_step<D, NR, true>(cur, nxt, lo, st, pf, s_cur);
   };
   for (int i = i_lo; i < i_hi; i += 3) {
     step(i, stage[0], stage[1], stage[2]);
@@ -333,7 +393,7 @@ __device__ __forceinline__ void reset_for_rerun(WaveState<D, NR>& st) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     st.m[r] = st.mobs[r];
-    st.l[r] = 0.f;
+    st.l[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -346,7 +406,7 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
   for (int r = 0; r < NR; ++r) {
     st.m[r] = -INFINITY;
     st.mobs[r] = -INFINITY;
-    st.l[r] = 0.f;
+    st.l[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) st.o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -391,7 +451,7 @@ template <int D, int NR, typename Dst>
 __device__ __forceinline__ void store_rows(WaveState<D, NR>& st, Dst dst) {
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const float l = group4_sum(st.l[r]);
+    const float l = st.l[r][0];
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
@@ -515,15 +575,16 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   __syncthreads();
   const int count = tcount;
 
-  const i32x4 rk = make_rsrc(k + ((size_t)b * L * Hkv + kvh) * D);
-  const i32x4 rv = make_rsrc(v + ((size_t)b * L * Hkv + kvh) * D);
+  const __bf16* k0 = k + ((size_t)b * L * Hkv + kvh) * D;
+  const __bf16* v0 = v + ((size_t)b * L * Hkv + kvh) * D;
   const i32x4 rw = make_rsrc(tk);
   const int tsb = Hkv * D * 2;
+  const KvLanes<D, NW> kl = kv_lanes<D, NW>(tsb);
   const LaneOffsets<D> lo = lane_offsets<D>();
   auto issue = [&](int i, Stage<D>& sg) {
     const int kt = (int)(tlist[i] & 0xFFFFu);
     const int key0 = kt * TK;
-    issue_kv<D, NW>(sg, rk, rv, key0, tsb, kmask[kt]);
+    issue_kv<D, NW>(sg, kl, k0, v0, key0, tsb, kmask[kt]);
     if (wave == NW - 1) {
       const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
       pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
@@ -632,18 +693,19 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
   load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, sbid, q_tiled);
 
-  const i32x4 rk = make_rsrc(ck + (size_t)b * cap * D);
-  const i32x4 rv = make_rsrc(cv + (size_t)b * cap * D);
-  const i32x4 rks = make_rsrc(ks + (size_t)b * S * D);
-  const i32x4 rvs = make_rsrc(vs + (size_t)b * S * D);
+  const __bf16* k0 = ck + (size_t)b * cap * D;
+  const __bf16* v0 = cv + (size_t)b * cap * D;
+  const __bf16* ks0 = ks + (size_t)b * S * D;
+  const __bf16* vs0 = vs + (size_t)b * S * D;
+  const KvLanes<D, NW> kl = kv_lanes<D, NW>(D * 2);
   const LaneOffsets<D> lo = lane_offsets<D>();
   auto issue = [&](int i, Stage<D>& sg) {
     const uint32_t d = tlist[i];
     const int key0 = (int)(d & 0xFFFFu) * TK;
     const bool suffix = (d >> 24) & 1u;
     const uint32_t keymask = tmask[i];
-    if (suffix) issue_kv<D, NW>(sg, rks, rvs, key0, D * 2, keymask);
-    else issue_kv<D, NW>(sg, rk, rv, key0, D * 2, keymask);
+    if (suffix) issue_kv<D, NW>(sg, kl, ks0, vs0, key0, D * 2, keymask);
+    else issue_kv<D, NW>(sg, kl, k0, v0, key0, D * 2, keymask);
     if (threadIdx.x < TK) {
       const uint32_t bit = (keymask >> threadIdx.x) & 1u;
       sg.w[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
@@ -678,7 +740,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const int64_t n_chunks = (int64_t)B * place.n_sub * NW * NR;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const float l = group4_sum(st.l[r]);
+    const float l = st.l[r][0];
     const int64_t chunk = (((int64_t)b * place.n_sub + qblk) * NW + wave) * NR + r;
     const int64_t at = split * n_chunks + chunk;
     f32x4* dst = reinterpret_cast<f32x4*>(opart) + at * (D / 16) * 64 + lane;
