@@ -102,6 +102,7 @@ def build_control_step(cx: Ctx):
     in_mask = cx.u8(pmask)
     mask_ws = torch.empty(Bd.pi_mask_workspace_bytes(1, P), dtype=torch.uint8, device=cx.dev)
     o = torch.empty((1, P, 8, 256), dtype=torch.bfloat16, device=cx.dev)
+    pre_ws = Bd.prefill_workspace(1, P, 8, 1, 256, cx.dev)   # key split: one sample alone cannot fill the chip
     net = Bd.VelocityNet.from_numpy(I.net_weights(seed + 600, width=w.width, action_dim=A), cx.dev)
     flow_ws = Bd.flow_workspace(net, 1, H, cx.dev)
     sar = cx.u8(s.ar[P:])
@@ -112,7 +113,7 @@ def build_control_step(cx: Ctx):
     def step():
         m = Bd.pi_mask_build(in_mask, ar_pre, seg_pre, 0, workspace=mask_ws)
         for l in range(L):
-            Bd.pi_joint_attn_prefill(q[l], ck[l], cv[l], m, o=o)
+            Bd.pi_joint_attn_prefill(q[l], ck[l], cv[l], m, o=o, workspace=pre_ws)
         x.copy_(noise)
         Bd.pi_flow_sample(net, cache, sar, state, None, x, num_steps=w.steps, workspace=flow_ws)
 
@@ -122,7 +123,7 @@ def build_control_step(cx: Ctx):
         "decode_layer": None,
     }
     m0 = Bd.pi_mask_build(in_mask, ar_pre, seg_pre, 0, workspace=mask_ws)
-    parts["prefill_layer"] = lambda: Bd.pi_joint_attn_prefill(q[0], ck[0], cv[0], m0, o=o)
+    parts["prefill_layer"] = lambda: Bd.pi_joint_attn_prefill(q[0], ck[0], cv[0], m0, o=o, workspace=pre_ws)
     qs = cx.bf(I.bf16_normal(seed + 700, (1, H + 1, 8, 256)))
     ks = cx.bf(I.bf16_normal(seed + 701, (1, H + 1, 1, 256)))
     vs = cx.bf(I.bf16_normal(seed + 702, (1, H + 1, 1, 256)))

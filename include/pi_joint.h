@@ -113,11 +113,18 @@ pi_status pi_mask_materialize(const pi_mask* mask, uint8_t* dense, pi_stream str
  * d = 64.  bf16 matrix-core products with fp32 accumulation.
  * If `cache` is non-NULL, K/V rows of tokens [0, cache->len) are also copied to
  * cache layer `layer` (cache->B == B, cache->len <= L).
+ * workspace (device, 256-byte aligned, optional): with at least
+ * pi_prefill_workspace_bytes(B, L, Hq, Hkv, d) bytes, a batch too small to fill
+ * the chip splits each query block's keys over several workgroups and merges
+ * the partial softmaxes (same result up to rounding order); NULL or too small
+ * runs unsplit.  Calls that share a workspace must not overlap.
  */
 typedef struct pi_kv_cache pi_kv_cache;
+size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
 pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
                                 int Hkv, int d, float scale, const pi_mask* mask, void* o,
-                                const pi_kv_cache* cache, int layer, pi_stream stream);
+                                const pi_kv_cache* cache, int layer, void* workspace,
+                                size_t workspace_bytes, pi_stream stream);
 
 /*
  * Per-layer prefix KV cache ([P1] §1.6; [P4] §4.1).  Device memory owned by the caller.

@@ -49,8 +49,9 @@ _SIGS = {
     "pi_mask_build": (_c_i, [_c_p, _c_p, _c_p, ctypes.c_uint32, _c_i, _c_i, _c_p, ctypes.c_size_t,
                              ctypes.POINTER(PiMask), _c_p]),
     "pi_mask_materialize": (_c_i, [ctypes.POINTER(PiMask), _c_p, _c_p]),
+    "pi_prefill_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i]),
     "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask),
-                                     _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p]),
+                                     _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p, ctypes.c_size_t, _c_p]),
     "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
                                      _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
@@ -206,9 +207,19 @@ class KVCache:
         return self.v[layer]
 
 
+def pi_prefill_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(lib().pi_prefill_workspace_bytes(B, L, Hq, Hkv, d))
+
+
+def prefill_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device) -> Optional[torch.Tensor]:
+    """Device workspace that lets a small-batch prefill split its keys (None if not needed)."""
+    n = pi_prefill_workspace_bytes(B, L, Hq, Hkv, d)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, o: Optional[torch.Tensor] = None,
                           scale: Optional[float] = None, cache: Optional[KVCache] = None, layer: int = 0,
-                          stream=None) -> torch.Tensor:
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
     if scale is None:
@@ -218,7 +229,9 @@ def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     _check("pi_joint_attn_prefill", lib().pi_joint_attn_prefill(
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), B, L, Hq, Hkv, d,
         scale, ctypes.byref(mask.struct), _ptr(o, torch.bfloat16, "o"),
-        ctypes.byref(cache.struct) if cache is not None else None, layer, _stream(stream)))
+        ctypes.byref(cache.struct) if cache is not None else None, layer,
+        _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
     return o
 
 

@@ -414,35 +414,36 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
 }
 
 // Workgroup placement.  Workgroups are dispatched round-robin over the 8 XCDs,
-// each with its own L2.  A group's workgroups (which read the same K/V) are kept
-// on one XCD; with fewer groups than XCDs, each group is cut into `span` parts
-// that run on `span` different XCDs, so a single sample still fills the chip.
+// each with its own L2.  With at least 8 groups, a group's workgroups (which read
+// the same K/V) are kept on one XCD.  With fewer groups (one or a few samples,
+// whose K/V are small) the workgroups simply go round-robin in group-major
+// order, which spreads every group over all XCDs and keeps the XCDs balanced.
 // Returns false for a workgroup with no work (the grid is rounded up).
 struct Placement {
-  int n_groups, n_sub, span, per;   // per = ceil(n_sub / span) sub-blocks per part
+  int n_groups, n_sub;
+  bool per_xcd;
 };
 
 __host__ __device__ inline Placement make_placement(int n_groups, int n_sub) {
-  Placement p;
-  p.n_groups = n_groups;
-  p.n_sub = n_sub;
-  p.span = n_groups >= 8 ? 1 : 8 / n_groups;
-  p.per = (n_sub + p.span - 1) / p.span;
-  return p;
+  return Placement{n_groups, n_sub, n_groups >= 8};
 }
 
 __host__ inline int64_t placement_grid(const Placement& p) {
-  return (int64_t)((p.n_groups * p.span + 7) / 8 * 8) * p.per;
+  return p.per_xcd ? (int64_t)((p.n_groups + 7) / 8 * 8) * p.n_sub : (int64_t)p.n_groups * p.n_sub;
 }
 
 __device__ __forceinline__ bool xcd_place(const Placement& p, int& group, int& sub) {
   const int id = blockIdx.x;
+  if (!p.per_xcd) {
+    group = id / p.n_sub;
+    sub = id % p.n_sub;
+    return group < p.n_groups;
+  }
   const int xcd = id & 7;
   const int k = id >> 3;
-  const int part_group = (k / p.per) * 8 + xcd;
-  group = part_group / p.span;
-  sub = (part_group % p.span) * p.per + k % p.per;
-  return group < p.n_groups && sub < p.n_sub;
+  group = (k / p.n_sub) * 8 + xcd;
+  sub = k % p.n_sub;
+  return group < p.n_groups;
 }
 
 // Normalise and store O rows.  dst(r, dt) gives where the lane's four values
@@ -473,6 +474,31 @@ struct RowMajorDst {
     return row_base[r] ? row_base[r] + dt * 16 + 4 * ((threadIdx.x & 63) >> 4) : nullptr;
   }
 };
+
+// Key-split epilogue: the unnormalised fp32 partial O of each 16-row tile,
+// stored in the accumulator's own lane order so every store writes 1 KB
+// contiguous, plus (reference max, weight sum) per row.  Chunk (16 rows) index:
+// ((group * n_qblk + qblk) * NW + wave) * NR + r; split s of n_chunks at
+// s * n_chunks + chunk.
+template <int D, int NR, int NW>
+__device__ __forceinline__ void store_partials(const WaveState<D, NR>& st, float* __restrict__ opart,
+                                               float* __restrict__ mlpart, int64_t n_chunks, int64_t group,
+                                               int n_qblk, int qblk, int split) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int64_t chunk = ((group * n_qblk + qblk) * NW + wave) * NR + r;
+    const int64_t at = split * n_chunks + chunk;
+    f32x4* dst = reinterpret_cast<f32x4*>(opart) + at * (D / 16) * 64 + lane;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) dst[dt * 64] = st.o[r][dt];
+    if (g == 0) {
+      mlpart[at * 32 + 2 * c] = st.m[r];
+      mlpart[at * 32 + 2 * c + 1] = st.l[r][0];
+    }
+  }
+}
 
 // Row setup: Q fragments into registers, the row's query word and output row.
 // q_tiled (decode only, G == Hq): this sample's queries as rows t*G + head of a
@@ -525,14 +551,16 @@ __global__ void __launch_bounds__(NW * 64)
 prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
-               uint32_t forbid, Placement place) {
+               uint32_t forbid, Placement place, int n_split, float* __restrict__ opart,
+               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   __shared__ Stage<D> stage[3];
   __shared__ uint32_t kmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ int tcount;
-  int group, qblk;
-  if (!xcd_place(place, group, qblk)) return;
+  int grp, qblk;
+  if (!xcd_place(place, grp, qblk)) return;
+  const int group = grp / n_split, split = grp % n_split;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
@@ -591,13 +619,21 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
     }
   };
   auto cls = [&](int i) { return (int)((tlist[i] >> 16) & 0xFFu); };
-  auto run = [&]() { run_tiles<D, NR>(stage, lo, st, 0, count, issue, cls, forbid, scale_log2); };
+  // this workgroup's share of the tile list (all of it when the keys are not split)
+  const int i_lo = (int)((int64_t)count * split / n_split);
+  const int i_hi = (int)((int64_t)count * (split + 1) / n_split);
+  auto run = [&]() { run_tiles<D, NR>(stage, lo, st, i_lo, i_hi, issue, cls, forbid, scale_log2); };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
     run();
   }
-  store_rows<D, NR>(st, RowMajorDst<D>{row_base});
+  if (n_split == 1) {
+    store_rows<D, NR>(st, RowMajorDst<D>{row_base});
+    return;
+  }
+  store_partials<D, NR, NW>(st, opart, mlpart, (int64_t)B * Hkv * place.n_sub * NW * NR, group, place.n_sub, qblk,
+                            split);
 }
 
 // ---------------------------------------------------------------------------
@@ -733,29 +769,12 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     }
     return;
   }
-  // split keys: the unnormalised fp32 partial O of each 16-row tile, stored in
-  // the accumulator's own lane order so every store writes 1 KB contiguous, plus
-  // (reference max, weight sum) per row
-  const int c = lane & 15, g = lane >> 4;
-  const int64_t n_chunks = (int64_t)B * place.n_sub * NW * NR;
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const float l = st.l[r][0];
-    const int64_t chunk = (((int64_t)b * place.n_sub + qblk) * NW + wave) * NR + r;
-    const int64_t at = split * n_chunks + chunk;
-    f32x4* dst = reinterpret_cast<f32x4*>(opart) + at * (D / 16) * 64 + lane;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) dst[dt * 64] = st.o[r][dt];
-    if (g == 0) {
-      mlpart[at * 32 + 2 * c] = st.m[r];
-      mlpart[at * 32 + 2 * c + 1] = l;
-    }
-  }
+  store_partials<D, NR, NW>(st, opart, mlpart, (int64_t)B * place.n_sub * NW * NR, b, place.n_sub, qblk, split);
 }
 
-// Merge the key splits of the decode: for each (sample, token, head) row,
+// Merge the key splits of a decode or GQA 8:1 prefill: for each (sample, token, head) row,
 // O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s.  The
-// decode stored each 16-row chunk's partial in accumulator lane order; here four
+// split kernel stored each 16-row chunk's partial in accumulator lane order; here four
 // workgroups share a chunk and each wave merges one 16-wide slice of d, issuing
 // the loads of all splits at once (1 KB contiguous per load).
 constexpr int kMaxSplit = 16;
@@ -838,17 +857,17 @@ using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
 
 template <int D, int G, int NR, int NW>
 pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
-                         float scale, const pi_mask* m, hipStream_t s) {
+                         float scale, const pi_mask* m, int n_split, float* opart, float* mlpart, hipStream_t s) {
   using C = Cfg<D, G, NR, NW>;
   const int n_qblk = (L + C::TOK - 1) / C::TOK;
-  const Placement place = make_placement(B * Hkv, n_qblk);
+  const Placement place = make_placement(B * Hkv * n_split, n_qblk);
   const int64_t grid = placement_grid(place);
   PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "prefill: grid too large");
   const float scale_log2 = scale * 1.4426950408889634f;
   prefill_kernel<D, G, NR, NW><<<(unsigned)grid, C::THREADS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), B, L, Hq, Hkv, scale_log2, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits,
-      place);
+      place, n_split, opart, mlpart);
   return pi::check_launch("prefill_kernel");
 }
 
@@ -857,6 +876,15 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
 int decode_splits(int B, int S, int len) {
   const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
   const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
+  const int by_chip = 256 / std::max(1, B * n_qblk);
+  return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
+}
+
+// Key splits for a GQA 8:1 prefill of B samples of L tokens (same rule as the
+// decode's, over the prefill's query blocks).
+int prefill_splits(int B, int L) {
+  const int n_qblk = (L + CfgG8::TOK - 1) / CfgG8::TOK;
+  const int tiles = (L + TK - 1) / TK;
   const int by_chip = 256 / std::max(1, B * n_qblk);
   return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
 }
@@ -877,9 +905,15 @@ size_t pi::decode_workspace_max(int B, int S, int Hq) {
   return decode_ws_bytes(B, S, Hq, splits);
 }
 
+extern "C" size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
+  if (B < 1 || L < 1 || !(Hq == 8 && Hkv == 1 && d == 256)) return 0;
+  return decode_ws_bytes(B, L, Hq, prefill_splits(B, L));
+}
+
 extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
                                            int Hkv, int d, float scale, const pi_mask* mask, void* o,
-                                           const pi_kv_cache* cache, int layer, pi_stream stream) {
+                                           const pi_kv_cache* cache, int layer, void* workspace,
+                                           size_t workspace_bytes, pi_stream stream) {
   PI_REQUIRE(q && k && v && o && mask, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: null pointer");
   PI_REQUIRE(pi::aligned16(q) && pi::aligned16(k) && pi::aligned16(v) && pi::aligned16(o), PI_ERR_INVALID_ARG,
              "pi_joint_attn_prefill: tensors must be 16-byte aligned");
@@ -905,8 +939,27 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
                PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: cache shape does not match (layer %d)", layer);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  pi_status st = gqa8 ? launch_prefill<256, 8, kNR256, kNW256>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s)
-                      : launch_prefill<64, 1, kNR64, kNW64>(q, k, v, o, B, L, Hq, Hkv, scale, mask, s);
+  pi_status st;
+  if (gqa8) {
+    int splits = prefill_splits(B, L);
+    if (workspace == nullptr || workspace_bytes < decode_ws_bytes(B, L, Hq, splits)) splits = 1;
+    PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+               "pi_joint_attn_prefill: workspace must be 256-byte aligned");
+    const int n_qblk = (L + CfgG8::TOK - 1) / CfgG8::TOK;
+    const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
+    float* opart = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+    float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                          pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
+                               : nullptr;
+    st = launch_prefill<256, 8, kNR256, kNW256>(q, k, v, o, B, L, Hq, Hkv, scale, mask, splits, opart, mlpart, s);
+    if (st == PI_OK && splits > 1) {
+      decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
+          opart, mlpart, static_cast<__bf16*>(o), 0, B, L, n_qblk, splits);
+      st = pi::check_launch("decode_combine_kernel");
+    }
+  } else {
+    st = launch_prefill<64, 1, kNR64, kNW64>(q, k, v, o, B, L, Hq, Hkv, scale, mask, 1, nullptr, nullptr, s);
+  }
   if (st != PI_OK || !cache) return st;
   const int row_chunks = Hkv * d / 8;
   const int64_t total = (int64_t)B * cache->len * row_chunks;

@@ -66,7 +66,8 @@ def test_prefill_rejects_bad_arguments_before_launch():
     m = Bd.PiMask(B=1, N=64, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
     call = lambda **kw: lib.pi_joint_attn_prefill(
         kw.get("q", FAKE), FAKE, FAKE, kw.get("B", 1), kw.get("L", 64), kw.get("Hq", 8), kw.get("Hkv", 1),
-        kw.get("d", 256), kw.get("scale", 0.0625), ctypes.byref(m), FAKE, None, 0, None)
+        kw.get("d", 256), kw.get("scale", 0.0625), ctypes.byref(m), FAKE, None, 0, kw.get("ws", None),
+        kw.get("ws_bytes", 0), None)
     assert call(d=128) == -2                 # unsupported head dim
     assert call(Hq=6, Hkv=4) == -1           # Hq not a multiple of Hkv
     assert call(L=65) == -1                  # mask built for another length
@@ -74,6 +75,12 @@ def test_prefill_rejects_bad_arguments_before_launch():
     assert call(q=P(0x10008)) == -1          # misaligned
     assert call(q=None) == -1
     assert b"pi_joint_attn_prefill" in lib.pi_last_error()
+    # a small batch asks for a split workspace; a misaligned one is rejected
+    need = lib.pi_prefill_workspace_bytes(1, 816, 8, 1, 256)
+    assert need > 0 and lib.pi_prefill_workspace_bytes(1, 816, 24, 24, 64) == 0
+    m816 = Bd.PiMask(B=1, N=816, n_qt=51, n_kt=26, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
+    assert lib.pi_joint_attn_prefill(FAKE, FAKE, FAKE, 1, 816, 8, 1, 256, 0.0625, ctypes.byref(m816), FAKE, None, 0,
+                                     P(0x100010), need, None) == -1
 
 
 @needs_lib

@@ -17,10 +17,16 @@ def _bd():
     return Bd
 
 
-def _prefill(q, k, v, valid, s, cache=None, layer=0):
+def _prefill(q, k, v, valid, s, cache=None, layer=0, split=False):
+    """split: pass the small-batch key-split workspace (asserting the shape asks for one)."""
     Bd = _bd()
     m = Bd.pi_mask_build(u8_dev(valid), u8_dev(s.ar), u8_dev(s.seg), I.forbid_bits(s.forbid))
-    o = Bd.pi_joint_attn_prefill(bf16_dev(q), bf16_dev(k), bf16_dev(v), m, cache=cache, layer=layer)
+    ws = None
+    if split:
+        B, L, Hq, d = q.shape
+        ws = Bd.prefill_workspace(B, L, Hq, k.shape[2], d, torch.device("cuda:0"))
+        assert ws is not None, "shape too small to split its keys"
+    o = Bd.pi_joint_attn_prefill(bf16_dev(q), bf16_dev(k), bf16_dev(v), m, cache=cache, layer=layer, workspace=ws)
     torch.cuda.synchronize()
     return o
 
@@ -48,21 +54,23 @@ def test_prefill_tiny():
     assert_close(host64(o), want, "prefill tiny")
 
 
+@pytest.mark.parametrize("split", [False, True])
 @pytest.mark.parametrize("seed,B,P,F,E", [(0, 2, 150, 20, 13), (1, 3, 97, 0, 50), (2, 1, 300, 64, 50)])
-def test_prefill_three_block_ragged(seed, B, P, F, E):
-    """π0.5-style prefix / FAST / expert with tail padding, ragged tiles, forbidden edge."""
+def test_prefill_three_block_ragged(seed, B, P, F, E, split):
+    """π0.5-style prefix / FAST / expert with tail padding, ragged tiles, forbidden
+    edge; unsplit and with the small-batch key split."""
     s = I.pi05_structure(P, F, E) if F else I.pi0_structure(P, E - 1)
     N = s.n
-    note(f"prefill three-block seed={seed} B={B} N={N}")
+    note(f"prefill three-block seed={seed} B={B} N={N} split={split}")
     r = np.random.default_rng(seed)
     valid = np.ones((B, N), np.uint8)
     valid[:, :P] = I.tail_padding_mask(r.integers(P // 2, P + 1, B), P)
     q = I.bf16_normal(seed * 10 + 1, (B, N, 8, 256))
     k = I.bf16_normal(seed * 10 + 2, (B, N, 1, 256))
     v = I.bf16_normal(seed * 10 + 3, (B, N, 1, 256))
-    o = _prefill(q, k, v, valid, s)
+    o = _prefill(q, k, v, valid, s, split=split)
     want = A.joint_attention(f64(q), f64(k), f64(v), valid, s.ar, s.seg, s.forbid)
-    assert_close(host64(o), want, f"prefill three-block {seed}")
+    assert_close(host64(o), want, f"prefill three-block {seed} split={split}")
     pad_rows = valid == 0
     assert (host64(o)[pad_rows] == 0).all()
 
@@ -80,15 +88,16 @@ def test_prefill_mha_d64_small():
     assert_close(host64(o), want, "prefill mha d64")
 
 
-def test_prefill_pi0_joint_867_full():
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_pi0_joint_867_full(split):
     """π0 control-step joint pool: 816 prefix + state + 50 actions, every row."""
     w = I.pi0_step()
-    note("prefill pi0 joint 867")
+    note(f"prefill pi0 joint 867 split={split}")
     q, k, v = w.qkv()
     valid = w.input_mask()
-    o = _prefill(q, k, v, valid, w.structure)
+    o = _prefill(q, k, v, valid, w.structure, split=split)
     want = A.joint_attention(f64(q), f64(k), f64(v), valid, w.structure.ar)
-    assert_close(host64(o), want, "prefill pi0 joint 867")
+    assert_close(host64(o), want, f"prefill pi0 joint 867 split={split}")
 
 
 # ----------------------------------------------------------------------------
@@ -129,7 +138,8 @@ def test_prefill_mmdit_sampled():
 # bit-exact invariances
 # ----------------------------------------------------------------------------
 
-def test_prefix_rows_invariant_to_suffix_kv_bit_exact():
+@pytest.mark.parametrize("split", [False, True])
+def test_prefix_rows_invariant_to_suffix_kv_bit_exact(split):
     """Rows that may not read a key are bit-identical whatever that key holds.
 
     Masked scores are replaced by -inf before the running max, so NaN in masked K
@@ -144,27 +154,27 @@ def test_prefix_rows_invariant_to_suffix_kv_bit_exact():
     q = I.bf16_normal(81, (B, N, 8, 256))
     k = I.bf16_normal(82, (B, N, 1, 256))
     v = I.bf16_normal(83, (B, N, 1, 256))
-    o1 = _prefill(q, k, v, valid, s).cpu()
+    o1 = _prefill(q, k, v, valid, s, split=split).cpu()
     big = I.bf16_normal(85, (B, N, 1, 256), std=3.0e4)
     k2, v2 = k.copy(), v.copy()
     k2[:, P:] = 0x7FC0      # NaN in every suffix key
     v2[:, P:] = big[:, P:]  # huge finite suffix values
     k2[1, 150:P] = 0x7FC0   # padded prefix slots: NaN in K and V
     v2[1, 150:P] = 0x7FC0
-    o2 = _prefill(q, k2, v2, valid, s).cpu()
+    o2 = _prefill(q, k2, v2, valid, s, split=split).cpu()
     assert torch.equal(o1[:, :P].view(torch.int16), o2[:, :P].view(torch.int16))
     # expert rows do not read FAST: perturb FAST K/V only
     k3, v3 = k.copy(), v.copy()
     k3[:, P:P + 64] = 0x7FC0
     v3[:, P:P + 64] = big[:, P:P + 64]
-    o3 = _prefill(q, k3, v3, valid, s).cpu()
+    o3 = _prefill(q, k3, v3, valid, s, split=split).cpu()
     assert torch.equal(o1[:, P + 64:].view(torch.int16), o3[:, P + 64:].view(torch.int16))
     # FAST token t does not read FAST tokens after it
     t = 20
     k4, v4 = k.copy(), v.copy()
     k4[:, P + t + 1:] = 0x7FC0
     v4[:, P + t + 1:] = big[:, P + t + 1:]
-    o4 = _prefill(q, k4, v4, valid, s).cpu()
+    o4 = _prefill(q, k4, v4, valid, s, split=split).cpu()
     assert torch.equal(o1[:, :P + t + 1].view(torch.int16), o4[:, :P + t + 1].view(torch.int16))
 
 
@@ -187,12 +197,13 @@ def test_decode_ignores_garbage_in_padded_slots():
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
-def test_prefill_is_deterministic():
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_is_deterministic(split):
     w = I.pi0_step()
     q, k, v = w.qkv()
     valid = w.input_mask()
-    o1 = _prefill(q, k, v, valid, w.structure).cpu()
-    o2 = _prefill(q, k, v, valid, w.structure).cpu()
+    o1 = _prefill(q, k, v, valid, w.structure, split=split).cpu()
+    o2 = _prefill(q, k, v, valid, w.structure, split=split).cpu()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
