@@ -852,8 +852,12 @@ __global__ void cache_write_kernel(const u32x4* __restrict__ k, const u32x4* __r
 // waves per SIMD, 16 query tokens x 8 heads per workgroup).  MHA at d = 64: four
 // waves of four row tiles.
 constexpr int kNR256 = 1, kNW256 = 8;
+// The decode's 51-token suffix: seven waves (14 tokens) per workgroup cover it in
+// four workgroups with 5 padded tokens instead of 13.
+constexpr int kNWdec = 7;
 constexpr int kNR64 = 4, kNW64 = 4;
 using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
+using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
 
 template <int D, int G, int NR, int NW>
 pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
@@ -874,7 +878,7 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
 // Key splits for a decode of B samples: enough workgroups to cover the chip
 // (about 256) while giving each split at least two key tiles.
 int decode_splits(int B, int S, int len) {
-  const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
+  const int n_qblk = (S + CfgDec::TOK - 1) / CfgDec::TOK;
   const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
   const int by_chip = 256 / std::max(1, B * n_qblk);
   return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
@@ -889,25 +893,32 @@ int prefill_splits(int B, int L) {
   return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
 }
 
-size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
+// Workspace of a key split over S query tokens per sample (fp32 partial chunks
+// of 16 rows x 256 d, then (m, l) per row), for a launch configuration C.
+template <typename C>
+size_t split_ws_bytes(int B, int S, int splits) {
   if (splits <= 1) return 0;
-  (void)Hq;
-  const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
-  const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  const size_t chunks = (size_t)splits * B * n_qblk * C::ROWS / 16;
   return pi::align_up(chunks * 16 * 256 * sizeof(float), 256) + chunks * 32 * sizeof(float);
+}
+
+size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
+  (void)Hq;
+  return split_ws_bytes<CfgDec>(B, S, splits);
 }
 
 }  // namespace
 
 size_t pi::decode_workspace_max(int B, int S, int Hq) {
-  const int n_qblk = (S + CfgG8::TOK - 1) / CfgG8::TOK;
+  const int n_qblk = (S + CfgDec::TOK - 1) / CfgDec::TOK;
   const int splits = std::max(1, std::min(kMaxSplit, 256 / std::max(1, B * n_qblk)));
   return decode_ws_bytes(B, S, Hq, splits);
 }
 
 extern "C" size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
   if (B < 1 || L < 1 || !(Hq == 8 && Hkv == 1 && d == 256)) return 0;
-  return decode_ws_bytes(B, L, Hq, prefill_splits(B, L));
+  return split_ws_bytes<CfgG8>(B, L, prefill_splits(B, L));
 }
 
 extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
@@ -942,7 +953,7 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   pi_status st;
   if (gqa8) {
     int splits = prefill_splits(B, L);
-    if (workspace == nullptr || workspace_bytes < decode_ws_bytes(B, L, Hq, splits)) splits = 1;
+    if (workspace == nullptr || workspace_bytes < split_ws_bytes<CfgG8>(B, L, splits)) splits = 1;
     PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
                "pi_joint_attn_prefill: workspace must be 256-byte aligned");
     const int n_qblk = (L + CfgG8::TOK - 1) / CfgG8::TOK;
@@ -999,14 +1010,14 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   PI_REQUIRE(Hq == 8 && cache->Hkv == 1 && cache->d == 256, PI_ERR_UNSUPPORTED,
              "pi_suffix_decode_step: supported heads are Hq=8, Hkv=1, d=256 (got %d, %d, %d)", Hq, cache->Hkv,
              cache->d);
-  using C = CfgG8;
+  using C = CfgDec;
   const int n_qblk = (S + C::TOK - 1) / C::TOK;
   int splits = decode_splits(B, S, cache->len);
   const size_t need = decode_ws_bytes(B, S, Hq, splits);
   if (workspace == nullptr || workspace_bytes < need) splits = 1;   // no workspace: one pass per sample
   PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_suffix_decode_step: workspace must be 256-byte aligned");
-  const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
+  const size_t chunks = (size_t)splits * B * n_qblk * kNWdec * kNR256;
   float* opart = splits > 1 ? static_cast<float*>(workspace) : nullptr;
   float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                         pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
@@ -1015,13 +1026,13 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
   const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
-  decode_kernel<256, 8, kNR256, kNW256><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
+  decode_kernel<256, 8, kNR256, kNWdec><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
       static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
       scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart);
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
-  decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
+  decode_combine_kernel<kNR256, kNWdec><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
       opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits);
   return pi::check_launch("decode_combine_kernel");
 }
