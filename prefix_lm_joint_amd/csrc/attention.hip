@@ -11,9 +11,9 @@
 //     and 8 query heads a row is a (token, head) pair: a 16-row tile holds two
 //     tokens x 8 heads, so every K/V element loaded serves 8 heads.
 //   * K/V tiles of 32 keys go from global memory straight into LDS (buffer loads
-//     with the LDS destination: no registers, no VALU) over three stages, one
-//     barrier per tile: while tile i's softmax and PV run, tile i+1's scores are
-//     computed and tile i+2 streams in.  A padded or masked-out key is given an
+//     with the LDS destination: no registers, no VALU) over four stages, one
+//     barrier per tile: one block per step runs tile i-1's PV, tile i+1's scores
+//     and tile i's softmax while tile i+2 streams in.  A padded or masked-out key is given an
 //     out-of-range offset, which the buffer unit turns into zeros: whatever a
 //     padded slot holds never reaches a product.
 //   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so that both
@@ -37,6 +37,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -114,6 +115,11 @@ struct KvLanes {
   int row[N];
 };
 
+// Pieces a wave's share of one tile's loads is cut into: one per K and per V
+// instruction, then one for the tile's key words.
+template <int D, int NW>
+constexpr int kIssueParts = 2 * KvLanes<D, NW>::N + 1;
+
 template <int D, int NW>
 __device__ __forceinline__ KvLanes<D, NW> kv_lanes(int tsb) {
   using T = Tile<D>;
@@ -130,28 +136,26 @@ __device__ __forceinline__ KvLanes<D, NW> kv_lanes(int tsb) {
   return kl;
 }
 
-// Issue the loads of the tile whose first key is key0 (k0, v0: key 0 of this
-// sample and head; tsb bytes between consecutive keys).  Keys whose bit is clear
-// in `keymask` (past the end, padding) are fetched from an out-of-range offset
-// and land as zeros.
+// Issue part p of this wave's loads of the tile whose first key is key0 (k0,
+// v0: key 0 of this sample and head; tsb bytes between consecutive keys): part
+// 2j is the wave's j-th K instruction, 2j+1 its j-th V instruction (parts past
+// the wave's share do nothing).  Keys whose bit is clear in `keymask` (past the
+// end, padding) are fetched from an out-of-range offset and land as zeros.
 template <int D, int NW>
-__device__ __forceinline__ void issue_kv(Stage<D>& st, const KvLanes<D, NW>& kl, const __bf16* k0,
-                                         const __bf16* v0, int key0, int tsb, uint32_t keymask) {
+__device__ __forceinline__ void issue_kv_part(Stage<D>& st, const KvLanes<D, NW>& kl, const __bf16* k0,
+                                              const __bf16* v0, int key0, int tsb, uint32_t keymask, int p) {
   using T = Tile<D>;
   const int wave = threadIdx.x >> 6;
+  const int j = p >> 1;
+  const int q = wave + j * NW;
+  if (j >= KvLanes<D, NW>::N || q >= T::INSTS) return;
   const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(key0) * tsb;
-  const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(k0) + at);
-  const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(v0) + at);
   const bool full = __builtin_amdgcn_readfirstlane(keymask) == 0xFFFFFFFFu;
-#pragma unroll
-  for (int j = 0; j < KvLanes<D, NW>::N; ++j) {
-    const int q = wave + j * NW;
-    if (q >= T::INSTS) break;
-    uint32_t ok = kl.k[j], ov = kl.v[j];
-    if (!full && !((keymask >> kl.row[j]) & 1u)) ok = ov = kOOB;
-    pi_buffer_load_lds(rk, lds_u32(&st.k[q * T::RPI * D]), 16, (int)ok, 0, 0, 0);
-    pi_buffer_load_lds(rv, lds_u32(&st.v[q * T::RPI * D]), 16, (int)ov, 0, 0, 0);
-  }
+  const bool is_v = p & 1;
+  uint32_t off = is_v ? kl.v[j] : kl.k[j];
+  if (!full && !((keymask >> kl.row[j]) & 1u)) off = kOOB;
+  const i32x4 rsrc = make_rsrc(reinterpret_cast<const char*>(is_v ? v0 : k0) + at);
+  pi_buffer_load_lds(rsrc, lds_u32(is_v ? &st.v[q * T::RPI * D] : &st.k[q * T::RPI * D]), 16, (int)off, 0, 0, 0);
 }
 
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0 only).
@@ -244,11 +248,13 @@ __device__ __forceinline__ void qk_tile(const Stage<D>& sm, const LaneOffsets<D>
   }
 }
 
-// Softmax of one tile on the vector units: masks, maxima and the bf16 weights
-// P^T (the B operand of the PV product) against the rows' reference maxima.
+// Softmax of one tile, branchy part (on the scores S^T of tile i, before the
+// step's block): the per-pair mask of a PARTIAL tile, and until every row of the
+// wave has a reference maximum, the row maxima (one cross-lane reduction) for
+// rows that lack one.
 template <int D, int NR>
-__device__ __forceinline__ void softmax_tile(const Stage<D>& sm, WaveState<D, NR>& st, f32x4 (&s)[NR][2],
-                                             bf16x8 (&pf)[NR], int cls, uint32_t forbid, float scale_log2) {
+__device__ __forceinline__ void softmax_pre(const Stage<D>& sm, WaveState<D, NR>& st, f32x4 (&s)[NR][2], int cls,
+                                            uint32_t forbid, float scale_log2) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const float NEG_INF = -INFINITY;
@@ -263,51 +269,107 @@ __device__ __forceinline__ void softmax_tile(const Stage<D>& sm, WaveState<D, NR
           if (!pair_visible(st.wq[r], wk, forbid)) s[r][kt][i] = NEG_INF;
       }
   }
-  // lane maxima of this tile; until every row has a reference maximum, the row
-  // maxima (one cross-lane reduction) set the references of rows that lack one
-  bool have_all = true;
+  if (!st.all_set) {
+    bool have_all = true;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float mx = NEG_INF;
+    for (int r = 0; r < NR; ++r) {
+      float mx = NEG_INF;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[r][kt][i]);
-    const float ml = mx * scale_log2;
-    st.mobs[r] = fmaxf(st.mobs[r], ml);
-    if (!st.all_set) {
-      const float mt = group4_max(ml);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[r][kt][i]);
+      const float mt = group4_max(mx * scale_log2);
       st.m[r] = (st.m[r] == NEG_INF) ? mt : st.m[r];
       have_all &= st.m[r] != NEG_INF;
     }
+    st.all_set = __ballot(!have_all) == 0ull;
   }
-  if (!st.all_set) st.all_set = __ballot(!have_all) == 0ull;
+}
+
+// One pipeline step's block.  Its three parts do not depend on one another:
+//   PV (if PV):  O^T += V^T P^T and l += 1^T P^T for tile i-1 (weights pf_prev,
+//                V from `vst`);
+//   QK:          S^T = K Q^T for tile i+1 (K from `kst`) into s_nxt;
+//   softmax:     the bf16 weights of tile i against the rows' reference maxima
+//                (s_cur -> pf_new) and the lane maxima for the growth check.
+// The products run in D/16 slots, each holding fragment j of both; the LDS reads
+// run AH fragments ahead of their products, and the NP pieces of the loads of
+// tile i+2 (iss) are dealt out over the slots, so the loads of all waves do not
+// queue at the texture unit at once.  Scheduling barriers between slots keep
+// that order.  The softmax follows the products: with two waves per SIMD it
+// overlaps the other wave's products.
+template <int D, int NR, bool PV, int NP, typename Iss>
+__device__ __forceinline__ void step_block(const Stage<D>& vst, const Stage<D>& kst, const LaneOffsets<D>& lo,
+                                           WaveState<D, NR>& st, const bf16x8 (&pf_prev)[NR],
+                                           const f32x4 (&s_cur)[NR][2], bf16x8 (&pf_new)[NR],
+                                           f32x4 (&s_nxt)[NR][2], float scale_log2, Iss iss) {
+  constexpr uint32_t HALF = 16u * D * 2u;   // bytes of 16 rows
+  constexpr int NS = D / 16;                // slots = V fragments = K fragments
+  constexpr int AH = NS >= 8 ? 3 : 2;       // read-ahead, in fragments
+  const float NEG_INF = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s_nxt[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto read_v = [&](int j) -> bf16x8 {
+    const bf16x4 lo4 = lds_read_tr4(at_bytes<__bf16>(vst.v, lo.v[j]));
+    const bf16x4 hi4 = lds_read_tr4(at_bytes<__bf16>(vst.v, lo.v[j] + HALF));
+    return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto read_k = [&](int j) -> bf16x8 { return *at_bytes<bf16x8>(kst.k, lo.k[j >> 1] + (j & 1) * HALF); };
+  bf16x8 vbuf[AH], kbuf[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    if constexpr (PV) vbuf[j] = read_v(j);
+    kbuf[j] = read_k(j);
+  }
+  if constexpr (PV) {
+    bf16x8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = f2bf(1.0f);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) st.l[r] = mfma16x16x32(ones, pf_prev[r], st.l[r]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int ds = j >> 1, kt = j & 1;
+    if constexpr (PV) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) st.o[r][j] = mfma16x16x32(vbuf[j % AH], pf_prev[r], st.o[r][j]);
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) s_nxt[r][kt] = mfma16x16x32(kbuf[j % AH], st.qf[r][ds], s_nxt[r][kt]);
+    if (j + AH < NS) {
+      if constexpr (PV) vbuf[j % AH] = read_v(j + AH);
+      kbuf[j % AH] = read_k(j + AH);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if ((p * NS) / NP == j) iss(p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     // a row that has seen no visible key keeps m = -inf: use 0 so masked weights are exp2(-inf) = 0
     const float m_use = (st.m[r] == NEG_INF) ? 0.f : st.m[r];
+    float mx = NEG_INF;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pf[r][4 * kt + i] = f2bf(fast_exp2(fmaf(s[r][kt][i], scale_log2, -m_use)));
+      for (int i = 0; i < 4; ++i) {
+        mx = fmaxf(mx, s_cur[r][kt][i]);
+        pf_new[r][4 * kt + i] = f2bf(fast_exp2(fmaf(s_cur[r][kt][i], scale_log2, -m_use)));
+      }
+    st.mobs[r] = fmaxf(st.mobs[r], mx * scale_log2);
   }
 }
 
-// The matrix-core work of one pipeline step, as one straight-line block:
-// O^T += V^T P^T and l += 1^T P^T for the current tile (the row sums of exactly
-// the bf16 weights that multiply V), interleaved fragment by fragment with
-// S^T = K Q^T of the next tile when QK, so the LDS reads of both products are in
-// flight together.  Both products take D/16 fragments.
-template <int D, int NR, bool QK>
-__device__ __forceinline__ void mma_step(const Stage<D>& cur, const Stage<D>& nxt, const LaneOffsets<D>& lo,
-                                         WaveState<D, NR>& st, const bf16x8 (&pf)[NR], f32x4 (&s)[NR][2]) {
+// O^T += V^T P^T and l += 1^T P^T for one tile (the pipeline's last PV).
+template <int D, int NR>
+__device__ __forceinline__ void pv_last(const Stage<D>& vst, const LaneOffsets<D>& lo, WaveState<D, NR>& st,
+                                        const bf16x8 (&pf)[NR]) {
   constexpr uint32_t HALF = 16u * D * 2u;
-  if constexpr (QK) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[r][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = f2bf(1.0f);
@@ -315,64 +377,90 @@ __device__ __forceinline__ void mma_step(const Stage<D>& cur, const Stage<D>& nx
   for (int r = 0; r < NR; ++r) st.l[r] = mfma16x16x32(ones, pf[r], st.l[r]);
 #pragma unroll
   for (int j = 0; j < D / 16; ++j) {
-    const bf16x4 lo4 = lds_read_tr4(at_bytes<__bf16>(cur.v, lo.v[j]));
-    const bf16x4 hi4 = lds_read_tr4(at_bytes<__bf16>(cur.v, lo.v[j] + HALF));
+    const bf16x4 lo4 = lds_read_tr4(at_bytes<__bf16>(vst.v, lo.v[j]));
+    const bf16x4 hi4 = lds_read_tr4(at_bytes<__bf16>(vst.v, lo.v[j] + HALF));
     const bf16x8 va = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
     for (int r = 0; r < NR; ++r) st.o[r][j] = mfma16x16x32(va, pf[r], st.o[r][j]);
-    if constexpr (QK) {
-      const int ds = j >> 1, kt = j & 1;
-      const bf16x8 ka = *at_bytes<bf16x8>(nxt.k, lo.k[ds] + kt * HALF);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) s[r][kt] = mfma16x16x32(ka, st.qf[r][ds], s[r][kt]);
-    }
-  }
-  // schedule: the reads of the next AHEAD fragments are in flight while
-  // fragment j's products issue (bounded read-ahead keeps the registers in budget)
-  constexpr int RD = QK ? 3 : 2, MF = QK ? 2 * NR : NR, AHEAD = 4;
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * RD, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, NR, 0);
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) {
-    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-    if (j + AHEAD < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
   }
 }
 
-// Tile loop shared by both kernels, software-pipelined over three LDS stages
-// (tile j lives in stage (j - i_lo) % 3; the loop is unrolled by three so every
-// LDS address is a per-lane offset plus a constant).  Step i runs tile i's
-// softmax on the vector units, then one matrix-core block with tile i's PV
-// interleaved with tile i+1's scores (its K is already in LDS), while tile i+2
-// streams in.
-//   issue(j, stage): start the loads of tile j into `stage` (all waves take part)
-//   cls(j): PI_TILE_FULL or PI_TILE_PARTIAL
-template <int D, int NR, typename Issue, typename Cls>
-__device__ __forceinline__ void run_tiles(Stage<D> (&stage)[3], const LaneOffsets<D>& lo, WaveState<D, NR>& st,
-                                          int i_lo, int i_hi, Issue issue, Cls cls, uint32_t forbid,
-                                          float scale_log2) {
+constexpr int kStages = 4;
+
+// A key tile as the loop sees it: d = tile index | class << 16 (| 1 << 24 for a
+// decode suffix tile), m = its key-validity bitmap, w = this thread's key word
+// for the tile (decode only).  Read from the workgroup's LDS tile list a step
+// before it is needed, so no LDS round trip sits between a step's barrier and
+// its loads.
+struct TileDesc {
+  uint32_t d, m, w;
+};
+
+__device__ __forceinline__ int tile_cls(const TileDesc& t) { return (int)((t.d >> 16) & 0xFFu); }
+
+// Tile loop shared by both kernels, software-pipelined over four LDS stages
+// (tile j lives in stage (j - i_lo) % 4; the loop is unrolled by four so every
+// LDS address is a per-lane offset plus a constant).  Step i: tile i's mask and
+// first-tile bookkeeping, then one block with tile i-1's PV, tile i+1's scores
+// (its K is already in LDS) and tile i's weights, while tile i+2 streams in.  A
+// tile's V is read one step after its weights are made, hence the fourth stage.
+//   desc(j): tile j's descriptor (LDS reads only)
+//   issue(t, stage, p): start piece p < NP of the loads of tile t into `stage`
+//     (every wave issues its own pieces)
+template <int D, int NR, int NP, typename Desc, typename Issue>
+__device__ __forceinline__ void run_tiles(Stage<D> (&stage)[kStages], const LaneOffsets<D>& lo,
+                                          WaveState<D, NR>& st, int i_lo, int i_hi, Desc desc, Issue issue,
+                                          uint32_t forbid, float scale_log2) {
   if (i_lo >= i_hi) return;
-  issue(i_lo, stage[0]);
-  if (i_lo + 1 < i_hi) issue(i_lo + 1, stage[1]);
+  TileDesc t_cur = desc(i_lo), t_nxt = t_cur, t_far = t_cur;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) issue(t_cur, stage[0], p);
+  if (i_lo + 1 < i_hi) {
+    t_nxt = desc(i_lo + 1);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) issue(t_nxt, stage[1], p);
+  }
+  if (i_lo + 2 < i_hi) t_far = desc(i_lo + 2);
   wait_vmem();
   __syncthreads();
   f32x4 s_cur[NR][2];
   qk_tile<D, NR>(stage[0], lo, st, s_cur);
   bf16x8 pf[NR];
-  auto step = [&](int i, Stage<D>& cur, Stage<D>& nxt, Stage<D>& free_st) {
+  // step i; the last step also computes scores against whatever stage `nxt`
+  // holds and discards them, which keeps the block free of branches
+  auto step = [&](auto pv, int i, Stage<D>& prev, Stage<D>& cur, Stage<D>& nxt, Stage<D>& free_st) {
     wait_vmem();          // this wave's loads of tile i+1 have landed
-    __syncthreads();      // ... everyone's; and everyone is done with tile i-1
-    if (i + 2 < i_hi) issue(i + 2, free_st);
-    softmax_tile<D, NR>(cur, st, s_cur, pf, cls(i), forbid, scale_log2);
-    // the last step also multiplies whatever stage `nxt` holds and discards it,
-    // which keeps the block free of branches
-    mma_step<D, NR, true>(cur, nxt, lo, st, pf, s_cur);
+    __syncthreads();      // ... everyone's; and everyone is done with tiles i-2 and below
+    softmax_pre<D, NR>(cur, st, s_cur, tile_cls(t_cur), forbid, scale_log2);
+    const TileDesc t_iss = t_far;
+    const bool do_issue = i + 2 < i_hi;
+    t_cur = t_nxt;
+    t_nxt = t_far;
+    if (i + 3 < i_hi) t_far = desc(i + 3);
+    bf16x8 pf_new[NR];
+    f32x4 s_nxt[NR][2];
+    auto iss = [&](int p) {
+      if (do_issue) issue(t_iss, free_st, p);
+    };
+    step_block<D, NR, decltype(pv)::value, NP>(prev, nxt, lo, st, pf, s_cur, pf_new, s_nxt, scale_log2, iss);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      pf[r] = pf_new[r];
+      s_cur[r][0] = s_nxt[r][0];
+      s_cur[r][1] = s_nxt[r][1];
+    }
   };
-  for (int i = i_lo; i < i_hi; i += 3) {
-    step(i, stage[0], stage[1], stage[2]);
-    if (i + 1 < i_hi) step(i + 1, stage[1], stage[2], stage[0]);
-    if (i + 2 < i_hi) step(i + 2, stage[2], stage[0], stage[1]);
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
+  step(NoPV{}, i_lo, stage[3], stage[0], stage[1], stage[2]);
+  for (int i = i_lo + 1; i < i_hi; i += 4) {
+    step(WithPV{}, i, stage[0], stage[1], stage[2], stage[3]);
+    if (i + 1 < i_hi) step(WithPV{}, i + 1, stage[1], stage[2], stage[3], stage[0]);
+    if (i + 2 < i_hi) step(WithPV{}, i + 2, stage[2], stage[3], stage[0], stage[1]);
+    if (i + 3 < i_hi) step(WithPV{}, i + 3, stage[3], stage[0], stage[1], stage[2]);
   }
+  // the last tile's PV (its stage is not overwritten: no load is issued past i_hi)
+  pv_last<D, NR>(stage[(i_hi - 1 - i_lo) & 3], lo, st, pf);
 }
 
 // True if a row's maximum grew past its reference by more than kMaxGrowth (the
@@ -554,7 +642,7 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
                uint32_t forbid, Placement place, int n_split, float* __restrict__ opart,
                float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
-  __shared__ Stage<D> stage[3];
+  __shared__ Stage<D> stage[kStages];
   __shared__ uint32_t kmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ int tcount;
@@ -609,20 +697,25 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   const int tsb = Hkv * D * 2;
   const KvLanes<D, NW> kl = kv_lanes<D, NW>(tsb);
   const LaneOffsets<D> lo = lane_offsets<D>();
-  auto issue = [&](int i, Stage<D>& sg) {
-    const int kt = (int)(tlist[i] & 0xFFFFu);
-    const int key0 = kt * TK;
-    issue_kv<D, NW>(sg, kl, k0, v0, key0, tsb, kmask[kt]);
-    if (wave == NW - 1) {
+  auto desc = [&](int i) {
+    const uint32_t d = tlist[i];
+    return TileDesc{d, kmask[d & 0xFFFFu], 0u};
+  };
+  auto issue = [&](const TileDesc& t, Stage<D>& sg, int p) {
+    const int key0 = (int)(t.d & 0xFFFFu) * TK;
+    if (p < kIssueParts<D, NW> - 1) {
+      issue_kv_part<D, NW>(sg, kl, k0, v0, key0, tsb, t.m, p);
+    } else if (wave == NW - 1) {
       const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
       pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
     }
   };
-  auto cls = [&](int i) { return (int)((tlist[i] >> 16) & 0xFFu); };
   // this workgroup's share of the tile list (all of it when the keys are not split)
   const int i_lo = (int)((int64_t)count * split / n_split);
   const int i_hi = (int)((int64_t)count * (split + 1) / n_split);
-  auto run = [&]() { run_tiles<D, NR>(stage, lo, st, i_lo, i_hi, issue, cls, forbid, scale_log2); };
+  auto run = [&]() {
+    run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, forbid, scale_log2);
+  };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
@@ -656,7 +749,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               float* __restrict__ mlpart) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
-  __shared__ Stage<D> stage[3];
+  __shared__ Stage<D> stage[kStages];
   __shared__ uint32_t sbid[128];
   __shared__ uint32_t pmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
@@ -735,20 +828,26 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const __bf16* vs0 = vs + (size_t)b * S * D;
   const KvLanes<D, NW> kl = kv_lanes<D, NW>(D * 2);
   const LaneOffsets<D> lo = lane_offsets<D>();
-  auto issue = [&](int i, Stage<D>& sg) {
-    const uint32_t d = tlist[i];
-    const int key0 = (int)(d & 0xFFFFu) * TK;
-    const bool suffix = (d >> 24) & 1u;
-    const uint32_t keymask = tmask[i];
-    if (suffix) issue_kv<D, NW>(sg, kl, ks0, vs0, key0, D * 2, keymask);
-    else issue_kv<D, NW>(sg, kl, k0, v0, key0, D * 2, keymask);
+  auto desc = [&](int i) {
+    const uint32_t d = tlist[i], m = tmask[i];
+    uint32_t w = 0u;
     if (threadIdx.x < TK) {
-      const uint32_t bit = (keymask >> threadIdx.x) & 1u;
-      sg.w[threadIdx.x] = suffix ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
+      const int key0 = (int)(d & 0xFFFFu) * TK;
+      const uint32_t bit = (m >> threadIdx.x) & 1u;
+      w = ((d >> 24) & 1u) ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
+    }
+    return TileDesc{d, m, w};
+  };
+  auto issue = [&](const TileDesc& t, Stage<D>& sg, int p) {
+    const int key0 = (int)(t.d & 0xFFFFu) * TK;
+    const bool suffix = (t.d >> 24) & 1u;
+    if (p < kIssueParts<D, NW> - 1) {
+      issue_kv_part<D, NW>(sg, kl, suffix ? ks0 : k0, suffix ? vs0 : v0, key0, D * 2, t.m, p);
+    } else if (threadIdx.x < TK) {
+      sg.w[threadIdx.x] = t.w;
     }
   };
-  auto cls = [&](int i) { return (int)((tlist[i] >> 16) & 0xFFu); };
-  auto run = [&]() { run_tiles<D, NR>(stage, lo, st, i_lo, i_hi, issue, cls, 0u, scale_log2); };
+  auto run = [&]() { run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, 0u, scale_log2); };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
@@ -849,13 +948,13 @@ __global__ void cache_write_kernel(const u32x4* __restrict__ k, const u32x4* __r
 }
 
 // Launch shapes.  GQA 8:1 at d = 256: eight waves of one 16-row tile each (two
-// waves per SIMD, 16 query tokens x 8 heads per workgroup).  MHA at d = 64: four
-// waves of four row tiles.
+// waves per SIMD, 16 query tokens x 8 heads per workgroup).  MHA at d = 64: eight
+// waves of one row tile (about 120 registers, so two workgroups share a CU).
 constexpr int kNR256 = 1, kNW256 = 8;
 // The decode's 51-token suffix: seven waves (14 tokens) per workgroup cover it in
 // four workgroups with 5 padded tokens instead of 13.
 constexpr int kNWdec = 7;
-constexpr int kNR64 = 4, kNW64 = 4;
+constexpr int kNR64 = 1, kNW64 = 8;
 using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
 using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
 
