@@ -588,7 +588,9 @@ __device__ __forceinline__ void store_partials(const WaveState<D, NR>& st, float
   }
 }
 
-// Row setup: Q fragments into registers, the row's query word and output row.
+// Row setup: Q fragments into registers and the output row; with `words`, also
+// the row's query word (else set later by set_row_words).  Issued first thing so
+// the Q loads are in flight while the workgroup builds its tile list.
 // q_tiled (decode only, G == Hq): this sample's queries as rows t*G + head of a
 // matrix in the operand tile layout, padded to whole 16-row blocks, so each
 // fragment is one contiguous 1 KB load.
@@ -605,26 +607,32 @@ __device__ __forceinline__ void load_rows(WaveState<D, NR>& st, __bf16** row_bas
     const int t = tok0 + row / G;
     const int h = head0 + row % G;
     const bool ok = t < ntok;
-    st.wq[r] = ok ? words[t] : 0u;
+    if (words != nullptr) st.wq[r] = ok ? words[t] : 0u;
+    // Rows past the last token (ok false) load token 0's values instead of
+    // zeros: they are never stored, and leaving the loaded registers untouched
+    // keeps the loads in flight until the first product needs them.
     if (q_tiled != nullptr) {
-      const int r0 = tok0 * G + wave * ROWS_W + r * 16;     // first row of the block, wave-uniform
+      int r0 = tok0 * G + wave * ROWS_W + r * 16;     // first row of the block, wave-uniform
+      if (r0 >= ntok * G) r0 = 0;
       const bf16x8* src = reinterpret_cast<const bf16x8*>(q_tiled) + (int64_t)(r0 / 16) * (D / 32) * 64 + lane;
 #pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        bf16x8 val = r0 < ntok * G ? src[ds * 64] : bf16x8{};
-        if (!ok) val = bf16x8{};
-        st.qf[r][ds] = val;
-      }
+      for (int ds = 0; ds < D / 32; ++ds) st.qf[r][ds] = src[ds * 64];
     } else {
       const __bf16* qrow = q + ((tok_base + (ok ? t : 0)) * Hq + h) * D;
 #pragma unroll
-      for (int ds = 0; ds < D / 32; ++ds) {
-        bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
-        if (!ok) val = bf16x8{};
-        st.qf[r][ds] = val;
-      }
+      for (int ds = 0; ds < D / 32; ++ds) st.qf[r][ds] = *reinterpret_cast<const bf16x8*>(qrow + ds * 32 + 8 * g);
     }
     row_base[r] = ok ? o + ((tok_base + t) * Hq + h) * D : nullptr;
+  }
+}
+
+template <int D, int G, int NR, int ROWS_W>
+__device__ __forceinline__ void set_row_words(WaveState<D, NR>& st, int ntok, int tok0, const uint32_t* words) {
+  const int c = threadIdx.x & 15, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int t = tok0 + (wave * ROWS_W + r * 16 + c) / G;
+    st.wq[r] = t < ntok ? words[t] : 0u;
   }
 }
 
@@ -683,7 +691,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
     }
     if (lane == 0) tcount = cnt;
   }
-
+  // the Q loads go out after the setup's own global reads (which wait on their
+  // results) and stay in flight through the barrier and the first K/V loads
   WaveState<D, NR> st;
   init_state(st);
   __bf16* row_base[NR];
@@ -811,16 +820,19 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     }
     if (lane == 0) tcount = cnt;
   }
+  // the Q loads go out after the setup's own global reads (which wait on their
+  // results) and stay in flight through the barrier and the first K/V loads
+  WaveState<D, NR> st;
+  init_state(st);
+  __bf16* row_base[NR];
+  const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
+  load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, nullptr, q_tiled);
   __syncthreads();
   // this workgroup's share of the tile list (all of it when the keys are not split)
   const int i_lo = (int)((int64_t)tcount * split / n_split);
   const int i_hi = (int)((int64_t)tcount * (split + 1) / n_split);
 
-  WaveState<D, NR> st;
-  init_state(st);
-  __bf16* row_base[NR];
-  const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
-  load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, sbid, q_tiled);
+  set_row_words<D, G, NR, C::ROWS_W>(st, S, tok0, sbid);
 
   const __bf16* k0 = ck + (size_t)b * cap * D;
   const __bf16* v0 = cv + (size_t)b * cap * D;
