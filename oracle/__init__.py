@@ -19,6 +19,9 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
       ("VLA 代码精读" §1.6).
   flow.euler_sample / flow.euler_update
       the Euler flow-matching sampler, t from 1 to 0 ("VLA 代码精读" §1.2, §1.6).
+  rope.rope / rope.joint_attention_rope
+      the rotary position embedding of Q and K at the mask's positions
+      ("VLA 代码精读" §3.2, §1.5, §1.6; the formula is a reading).
   flow.velocity_net
       the random-weight stand-in velocity network.  The pages give no weights
       or exact layer for it: **parity unpinned** as a whole (only its pieces
@@ -26,4 +29,4 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
 
 Readings of points the pages leave open are listed in each docstring.
 """
-from . import bf16, mask, attention, flow  # noqa: F401
+from . import bf16, mask, attention, flow, rope  # noqa: F401
