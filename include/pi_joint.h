@@ -111,19 +111,24 @@ pi_status pi_mask_materialize(const pi_mask* mask, uint8_t* dense, pi_stream str
  *   mask built for the same B and N = L.  scale > 0 (usually 1/sqrt(d)).
  * Supported heads: (Hq, Hkv, d) = (8, 1, 256) and (Hq, Hkv, d) with Hq == Hkv and
  * d = 64.  bf16 matrix-core products with fp32 accumulation.
+ * rope_base: 0 = no rotary embedding; > 1 = q and k are rotated at the mask's
+ * positions (pi_mask.pos) before the scores, as pi_rope_apply does (k into the
+ * workspace, q in registers; the inputs are left untouched).
  * If `cache` is non-NULL, K/V rows of tokens [0, cache->len) are also copied to
- * cache layer `layer` (cache->B == B, cache->len <= L).
- * workspace (device, 256-byte aligned, optional): with at least
- * pi_prefill_workspace_bytes(B, L, Hq, Hkv, d) bytes, a batch too small to fill
- * the chip splits each query block's keys over several workgroups and merges
- * the partial softmaxes (same result up to rounding order); NULL or too small
- * runs unsplit.  Calls that share a workspace must not overlap.
+ * cache layer `layer` (cache->B == B, cache->len <= L); with the rotary
+ * embedding the cache receives the rotated keys.
+ * workspace (device, 256-byte aligned): pi_prefill_workspace_bytes(B, L, Hq, Hkv, d)
+ * bytes cover every use.  Required with rope_base > 0 (PI_ERR_WORKSPACE without);
+ * otherwise optional: with it a batch too small to fill the chip splits each
+ * query block's keys over several workgroups and merges the partial softmaxes
+ * (same result up to rounding order), without it the call runs unsplit.  Calls
+ * that share a workspace must not overlap.
  */
 typedef struct pi_kv_cache pi_kv_cache;
 size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
 pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
-                                int Hkv, int d, float scale, const pi_mask* mask, void* o,
-                                const pi_kv_cache* cache, int layer, void* workspace,
+                                int Hkv, int d, float scale, float rope_base, const pi_mask* mask,
+                                void* o, const pi_kv_cache* cache, int layer, void* workspace,
                                 size_t workspace_bytes, pi_stream stream);
 
 /*
@@ -151,16 +156,35 @@ struct pi_kv_cache {
  *   suffix_ar  uint8 [S] (device)
  * Supported: Hq = 8, Hkv = 1, d = 256, 1 <= S <= 128.  Each cached K/V tile is
  * read from HBM once per sample and shared by all 8 query heads.
- * workspace (device, 256-byte aligned, optional): with at least
- * pi_decode_workspace_bytes(B, S, Hq, cache->len) bytes a small batch splits each
- * sample's keys over several workgroups and merges the partial softmaxes; with
- * NULL or fewer bytes the call runs unsplit (same result up to rounding).
+ * rope_base: 0 = no rotary embedding; > 1 = q_s and k_s are rotated with token t
+ * of sample b at position (valid slots of prefix_mask[b]) + t ([P1] §1.6), and
+ * the cache is taken to hold keys already rotated (as a prefill with the same
+ * rope_base writes them).
+ * workspace (device, 256-byte aligned): pi_decode_workspace_bytes(B, S, Hq,
+ * cache->len) bytes cover every use.  Required with rope_base > 0; otherwise
+ * optional: with it a small batch splits each sample's keys over several
+ * workgroups and merges the partial softmaxes, without it the call runs unsplit
+ * (same result up to rounding).
  */
 size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len);
 pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s,
                                 const void* k_s, const void* v_s, const uint8_t* suffix_ar,
-                                int B, int S, int Hq, float scale, void* o_s, void* workspace,
-                                size_t workspace_bytes, pi_stream stream);
+                                int B, int S, int Hq, float scale, float rope_base, void* o_s,
+                                void* workspace, size_t workspace_bytes, pi_stream stream);
+
+/*
+ * Rotary position embedding ([P1] §3.2: π0 keeps its LLM's rotary embedding;
+ * positions per §1.5 / §1.6, e.g. pi_mask.pos).  For each token t of each sample
+ * and each head, with p = pos[b*L + t] and i < d/2:
+ *   y[i]       = x[i] cos(a) - x[i + d/2] sin(a)
+ *   y[i + d/2] = x[i + d/2] cos(a) + x[i] sin(a),   a = p * base^(-2i/d)
+ * (the rotate-half arrangement; the pages name the method, not the formula).
+ *   x, y  bf16 [B, L, H, d] (y may equal x)   pos  int32 [B, L] (device)
+ * d a multiple of 16 up to 512, base > 1 (usually 10000).  fp32 arithmetic with
+ * the angle reduced in fp64; bf16 results.
+ */
+pi_status pi_rope_apply(const void* x, void* y, int B, int L, int H, int d, const int32_t* pos,
+                        float base, pi_stream stream);
 
 /* Euler update x <- x + dt * v over n fp32 elements ([P1] §1.2). */
 pi_status pi_euler_update(float* x, const float* v, float dt, int64_t n, pi_stream stream);

@@ -50,11 +50,13 @@ _SIGS = {
                              ctypes.POINTER(PiMask), _c_p]),
     "pi_mask_materialize": (_c_i, [ctypes.POINTER(PiMask), _c_p, _c_p]),
     "pi_prefill_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i]),
-    "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask),
-                                     _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, _c_f,
+                                     ctypes.POINTER(PiMask), _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p,
+                                     ctypes.c_size_t, _c_p]),
     "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
-                                     _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+                                     _c_f, _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_rope_apply": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_f, _c_p]),
     "pi_euler_update": (_c_i, [_c_p, _c_p, _c_f, ctypes.c_int64, _c_p]),
     "pi_flow_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiVelocityNet), _c_i, _c_i]),
     "pi_velocity_eval": (_c_i, [ctypes.POINTER(PiVelocityNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_p, _c_f,
@@ -212,14 +214,15 @@ def pi_prefill_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int
 
 
 def prefill_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device) -> Optional[torch.Tensor]:
-    """Device workspace that lets a small-batch prefill split its keys (None if not needed)."""
+    """Device workspace for the rotary embedding and the key split of small batches (None if not needed)."""
     n = pi_prefill_workspace_bytes(B, L, Hq, Hkv, d)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, o: Optional[torch.Tensor] = None,
                           scale: Optional[float] = None, cache: Optional[KVCache] = None, layer: int = 0,
-                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                          workspace: Optional[torch.Tensor] = None, stream=None,
+                          rope_base: float = 0.0) -> torch.Tensor:
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
     if scale is None:
@@ -228,7 +231,7 @@ def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
         o = torch.empty_like(q)
     _check("pi_joint_attn_prefill", lib().pi_joint_attn_prefill(
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), B, L, Hq, Hkv, d,
-        scale, ctypes.byref(mask.struct), _ptr(o, torch.bfloat16, "o"),
+        scale, rope_base, ctypes.byref(mask.struct), _ptr(o, torch.bfloat16, "o"),
         ctypes.byref(cache.struct) if cache is not None else None, layer,
         _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream(stream)))
@@ -240,15 +243,17 @@ def pi_decode_workspace_bytes(B: int, S: int, Hq: int, length: int) -> int:
 
 
 def decode_workspace(cache: KVCache, S: int, Hq: int = 8) -> Optional[torch.Tensor]:
-    """Device workspace that lets a small-batch decode split its keys (None if not needed)."""
+    """Device workspace for the rotary embedding and the key split of small batches (None if not needed)."""
     n = pi_decode_workspace_bytes(cache.struct.B, S, Hq, cache.struct.len)
     return torch.empty(n, dtype=torch.uint8, device=cache.k.device) if n else None
 
 
 def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: torch.Tensor, v_s: torch.Tensor,
                           suffix_ar: torch.Tensor, o_s: Optional[torch.Tensor] = None, scale: Optional[float] = None,
-                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """``workspace`` from decode_workspace() enables the key split of small batches; None runs unsplit."""
+                          workspace: Optional[torch.Tensor] = None, stream=None,
+                          rope_base: float = 0.0) -> torch.Tensor:
+    """``workspace`` from decode_workspace() enables the key split of small batches (None runs unsplit)
+    and is required with ``rope_base`` > 0."""
     B, S, Hq, d = q_s.shape
     if scale is None:
         scale = d ** -0.5
@@ -256,10 +261,22 @@ def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: to
         o_s = torch.empty_like(q_s)
     _check("pi_suffix_decode_step", lib().pi_suffix_decode_step(
         ctypes.byref(cache.struct), layer, _ptr(q_s, torch.bfloat16, "q_s"), _ptr(k_s, torch.bfloat16, "k_s"),
-        _ptr(v_s, torch.bfloat16, "v_s"), _ptr(suffix_ar, torch.uint8, "suffix_ar"), B, S, Hq, scale,
+        _ptr(v_s, torch.bfloat16, "v_s"), _ptr(suffix_ar, torch.uint8, "suffix_ar"), B, S, Hq, scale, rope_base,
         _ptr(o_s, torch.bfloat16, "o_s"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
     return o_s
+
+
+def pi_rope_apply(x: torch.Tensor, pos: torch.Tensor, base: float = 10000.0, y: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Rotary embedding of x [B, L, H, d] bf16 at positions pos [B, L] int32 (y may be x)."""
+    B, L, H, d = x.shape
+    assert pos.shape == (B, L)
+    if y is None:
+        y = torch.empty_like(x)
+    _check("pi_rope_apply", lib().pi_rope_apply(_ptr(x, torch.bfloat16, "x"), _ptr(y, torch.bfloat16, "y"), B, L, H,
+                                                d, _ptr(pos, torch.int32, "pos"), base, _stream(stream)))
+    return y
 
 
 def pi_euler_update(x: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> torch.Tensor:

@@ -405,12 +405,14 @@ __device__ __forceinline__ int tile_cls(const TileDesc& t) { return (int)((t.d >
 // (its K is already in LDS) and tile i's weights, while tile i+2 streams in.  A
 // tile's V is read one step after its weights are made, hence the fourth stage.
 //   desc(j): tile j's descriptor (LDS reads only)
+//   prep(): once the first loads are out, work on the Q rows (the rotary
+//     embedding); it must be idempotent, the loop may run twice
 //   issue(t, stage, p): start piece p < NP of the loads of tile t into `stage`
 //     (every wave issues its own pieces)
-template <int D, int NR, int NP, typename Desc, typename Issue>
+template <int D, int NR, int NP, typename Desc, typename Issue, typename Prep>
 __device__ __forceinline__ void run_tiles(Stage<D> (&stage)[kStages], const LaneOffsets<D>& lo,
                                           WaveState<D, NR>& st, int i_lo, int i_hi, Desc desc, Issue issue,
-                                          uint32_t forbid, float scale_log2) {
+                                          Prep prep, uint32_t forbid, float scale_log2) {
   if (i_lo >= i_hi) return;
   TileDesc t_cur = desc(i_lo), t_nxt = t_cur, t_far = t_cur;
 #pragma unroll
@@ -421,6 +423,7 @@ __device__ __forceinline__ void run_tiles(Stage<D> (&stage)[kStages], const Lane
     for (int p = 0; p < NP; ++p) issue(t_nxt, stage[1], p);
   }
   if (i_lo + 2 < i_hi) t_far = desc(i_lo + 2);
+  prep();               // row work that needs the Q registers, while the first tiles load
   wait_vmem();
   __syncthreads();
   f32x4 s_cur[NR][2];
@@ -636,6 +639,26 @@ __device__ __forceinline__ void set_row_words(WaveState<D, NR>& st, int ntok, in
   }
 }
 
+// Rotary embedding of this lane's Q rows in registers (pairs (i, i + D/2): the
+// lane's fragments ds and ds + D/64 hold them at the same offsets), row r at
+// position pos[r]; inv_freq: the D/2 pair frequencies in LDS.
+template <int D, int NR>
+__device__ __forceinline__ void rotate_q(WaveState<D, NR>& st, const int (&pos)[NR], const double* inv_freq) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int ds = 0; ds < D / 64; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float c, sn;
+        rope_cos_sin(pos[r], inv_freq[ds * 32 + 8 * g + e], c, sn);
+        const float a = bf2f(st.qf[r][ds][e]), b = bf2f(st.qf[r][ds + D / 64][e]);
+        st.qf[r][ds][e] = f2bf(a * c - b * sn);
+        st.qf[r][ds + D / 64][e] = f2bf(b * c + a * sn);
+      }
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: one group per (sample, KV head), n_qblk query blocks each, XCD-placed.
 // Up front the workgroup computes every key tile's validity bitmap and compacts
@@ -648,14 +671,16 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
                __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
                uint32_t forbid, Placement place, int n_split, float* __restrict__ opart,
-               float* __restrict__ mlpart) {
+               float* __restrict__ mlpart, const int32_t* __restrict__ rope_pos, double rope_log2_base) {
   using C = Cfg<D, G, NR, NW>;
   __shared__ Stage<D> stage[kStages];
   __shared__ uint32_t kmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
+  __shared__ double rope_if[D / 2];
   __shared__ int tcount;
   int grp, qblk;
   if (!xcd_place(place, grp, qblk)) return;
+  if (rope_pos != nullptr && threadIdx.x < D / 2) rope_if[threadIdx.x] = rope_inv_freq(threadIdx.x, D, rope_log2_base);
   const int group = grp / n_split, split = grp % n_split;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -722,8 +747,20 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   // this workgroup's share of the tile list (all of it when the keys are not split)
   const int i_lo = (int)((int64_t)count * split / n_split);
   const int i_hi = (int)((int64_t)count * (split + 1) / n_split);
+  bool rotated = rope_pos == nullptr;
+  auto prep = [&]() {
+    if (rotated) return;
+    int p[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int t = tok0 + (wave * C::ROWS_W + r * 16 + (lane & 15)) / G;
+      p[r] = rope_pos[(int64_t)b * L + min(t, L - 1)];
+    }
+    rotate_q<D, NR>(st, p, rope_if);
+    rotated = true;
+  };
   auto run = [&]() {
-    run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, forbid, scale_log2);
+    run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, prep, forbid, scale_log2);
   };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
@@ -755,7 +792,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
               const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
               __bf16* __restrict__ os, int tiled, Placement place, int n_split, float* __restrict__ opart,
-              float* __restrict__ mlpart) {
+              float* __restrict__ mlpart, int rope, double rope_log2_base) {
   using C = Cfg<D, G, NR, NW>;
   constexpr int Hq = G;
   __shared__ Stage<D> stage[kStages];
@@ -763,9 +800,11 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   __shared__ uint32_t pmask[kMaxTiles];
   __shared__ uint32_t tlist[kMaxTiles];
   __shared__ uint32_t tmask[kMaxTiles];
+  __shared__ double rope_if[D / 2];
   __shared__ int tcount;
   int grp, qblk;
   if (!xcd_place(place, grp, qblk)) return;
+  if (rope && threadIdx.x < D / 2) rope_if[threadIdx.x] = rope_inv_freq(threadIdx.x, D, rope_log2_base);
   const int b = grp / n_split, split = grp % n_split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
@@ -859,7 +898,23 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
       sg.w[threadIdx.x] = t.w;
     }
   };
-  auto run = [&]() { run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, 0u, scale_log2); };
+  // suffix token t sits at position (valid prefix slots) + t
+  bool rotated = !rope;
+  auto prep = [&]() {
+    if (rotated) return;
+    int n_valid = 0;
+    for (int w = lane; w < n_pt; w += 64) n_valid += __popc(pmask[w]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) n_valid += __shfl_xor(n_valid, off);
+    int p[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) p[r] = n_valid + tok0 + (wave * C::ROWS_W + r * 16 + (lane & 15)) / G;
+    rotate_q<D, NR>(st, p, rope_if);
+    rotated = true;
+  };
+  auto run = [&]() {
+    run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, prep, 0u, scale_log2);
+  };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
@@ -972,7 +1027,8 @@ using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
 
 template <int D, int G, int NR, int NW>
 pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
-                         float scale, const pi_mask* m, int n_split, float* opart, float* mlpart, hipStream_t s) {
+                         float scale, const pi_mask* m, int n_split, float* opart, float* mlpart,
+                         float rope_base, hipStream_t s) {
   using C = Cfg<D, G, NR, NW>;
   const int n_qblk = (L + C::TOK - 1) / C::TOK;
   const Placement place = make_placement(B * Hkv * n_split, n_qblk);
@@ -982,7 +1038,8 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
   prefill_kernel<D, G, NR, NW><<<(unsigned)grid, C::THREADS, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), B, L, Hq, Hkv, scale_log2, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits,
-      place, n_split, opart, mlpart);
+      place, n_split, opart, mlpart, rope_base > 0.f ? m->pos : nullptr,
+      rope_base > 0.f ? log2((double)rope_base) : 0.0);
   return pi::check_launch("prefill_kernel");
 }
 
@@ -1014,9 +1071,13 @@ size_t split_ws_bytes(int B, int S, int splits) {
   return pi::align_up(chunks * 16 * 256 * sizeof(float), 256) + chunks * 32 * sizeof(float);
 }
 
+// Bytes of the rotated suffix K a decode with the rotary embedding keeps in its workspace.
+size_t rope_ks_bytes(int B, int S) { return pi::align_up((size_t)B * S * 256 * 2, 256); }
+
+// Decode workspace: [rotated suffix K (rotary embedding only)] [key-split partials].
 size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
   (void)Hq;
-  return split_ws_bytes<CfgDec>(B, S, splits);
+  return rope_ks_bytes(B, S) + split_ws_bytes<CfgDec>(B, S, splits);
 }
 
 }  // namespace
@@ -1027,14 +1088,19 @@ size_t pi::decode_workspace_max(int B, int S, int Hq) {
   return decode_ws_bytes(B, S, Hq, splits);
 }
 
+// Bytes of the rotated K a prefill with the rotary embedding keeps in its workspace.
+size_t rope_k_bytes(int B, int L, int Hkv, int d) { return pi::align_up((size_t)B * L * Hkv * d * 2, 256); }
+
 extern "C" size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
-  if (B < 1 || L < 1 || !(Hq == 8 && Hkv == 1 && d == 256)) return 0;
-  return split_ws_bytes<CfgG8>(B, L, prefill_splits(B, L));
+  if (B < 1 || L < 1) return 0;
+  if (Hq == 8 && Hkv == 1 && d == 256) return rope_k_bytes(B, L, Hkv, d) + split_ws_bytes<CfgG8>(B, L, prefill_splits(B, L));
+  if (Hq == Hkv && d == 64) return rope_k_bytes(B, L, Hkv, d);
+  return 0;
 }
 
 extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
-                                           int Hkv, int d, float scale, const pi_mask* mask, void* o,
-                                           const pi_kv_cache* cache, int layer, void* workspace,
+                                           int Hkv, int d, float scale, float rope_base, const pi_mask* mask,
+                                           void* o, const pi_kv_cache* cache, int layer, void* workspace,
                                            size_t workspace_bytes, pi_stream stream) {
   PI_REQUIRE(q && k && v && o && mask, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: null pointer");
   PI_REQUIRE(pi::aligned16(q) && pi::aligned16(k) && pi::aligned16(v) && pi::aligned16(o), PI_ERR_INVALID_ARG,
@@ -1043,6 +1109,8 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   PI_REQUIRE(mask->B == B && mask->N == L && mask->tok && mask->tiles, PI_ERR_INVALID_ARG,
              "pi_joint_attn_prefill: mask built for B=%d N=%d, call has B=%d L=%d", mask->B, mask->N, B, L);
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: scale must be > 0");
+  PI_REQUIRE(rope_base == 0.f || (rope_base > 1.f && isfinite(rope_base)), PI_ERR_INVALID_ARG,
+             "pi_joint_attn_prefill: rope_base must be 0 (off) or > 1");
   PI_REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, PI_ERR_INVALID_ARG,
              "pi_joint_attn_prefill: Hq=%d must be a multiple of Hkv=%d", Hq, Hkv);
   PI_REQUIRE(L <= kMaxTiles * TK, PI_ERR_UNSUPPORTED, "pi_joint_attn_prefill: L=%d exceeds %d tokens", L,
@@ -1060,27 +1128,42 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
                    cache->len >= 1 && cache->len <= L && cache->len <= cache->capacity,
                PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: cache shape does not match (layer %d)", layer);
   }
+  const bool rope = rope_base > 0.f;
+  // workspace: [rotated K (with the rotary embedding)] [key-split partials]
+  const size_t rot_bytes = rope ? rope_k_bytes(B, L, Hkv, d) : 0;
+  PI_REQUIRE(!rope || (workspace != nullptr && workspace_bytes >= rot_bytes), PI_ERR_WORKSPACE,
+             "pi_joint_attn_prefill: the rotary embedding needs pi_prefill_workspace_bytes() of workspace");
+  PI_REQUIRE(workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "pi_joint_attn_prefill: workspace must be 256-byte aligned");
+  PI_REQUIRE(!rope || mask->pos, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: mask has no positions");
   hipStream_t s = static_cast<hipStream_t>(stream);
   pi_status st;
+  const void* kk = k;
+  if (rope) {
+    st = pi::rope_rows(k, workspace, (int64_t)B * L, Hkv, d, mask->pos, rope_base, s);
+    if (st != PI_OK) return st;
+    kk = workspace;
+  }
+  char* split_ws = workspace ? static_cast<char*>(workspace) + rot_bytes : nullptr;
+  const size_t split_avail = workspace ? workspace_bytes - rot_bytes : 0;
   if (gqa8) {
     int splits = prefill_splits(B, L);
-    if (workspace == nullptr || workspace_bytes < split_ws_bytes<CfgG8>(B, L, splits)) splits = 1;
-    PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
-               "pi_joint_attn_prefill: workspace must be 256-byte aligned");
+    if (split_ws == nullptr || split_avail < split_ws_bytes<CfgG8>(B, L, splits)) splits = 1;
     const int n_qblk = (L + CfgG8::TOK - 1) / CfgG8::TOK;
     const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
-    float* opart = splits > 1 ? static_cast<float*>(workspace) : nullptr;
-    float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                          pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
+    float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
+    float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
                                : nullptr;
-    st = launch_prefill<256, 8, kNR256, kNW256>(q, k, v, o, B, L, Hq, Hkv, scale, mask, splits, opart, mlpart, s);
+    st = launch_prefill<256, 8, kNR256, kNW256>(q, kk, v, o, B, L, Hq, Hkv, scale, mask, splits, opart, mlpart,
+                                                rope_base, s);
     if (st == PI_OK && splits > 1) {
       decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
           opart, mlpart, static_cast<__bf16*>(o), 0, B, L, n_qblk, splits);
       st = pi::check_launch("decode_combine_kernel");
     }
   } else {
-    st = launch_prefill<64, 1, kNR64, kNW64>(q, k, v, o, B, L, Hq, Hkv, scale, mask, 1, nullptr, nullptr, s);
+    st = launch_prefill<64, 1, kNR64, kNW64>(q, kk, v, o, B, L, Hq, Hkv, scale, mask, 1, nullptr, nullptr,
+                                             rope_base, s);
   }
   if (st != PI_OK || !cache) return st;
   const int row_chunks = Hkv * d / 8;
@@ -1089,8 +1172,9 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   __bf16* ckl = static_cast<__bf16*>(cache->k) + (size_t)layer * layer_elems;
   __bf16* cvl = static_cast<__bf16*>(cache->v) + (size_t)layer * layer_elems;
   const int threads = 256;
+  // the cache keeps rotated keys: a decode reads them as they are
   cache_write_kernel<<<(unsigned)((total + threads - 1) / threads), threads, 0, s>>>(
-      static_cast<const u32x4*>(k), static_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(ckl),
+      static_cast<const u32x4*>(kk), static_cast<const u32x4*>(v), reinterpret_cast<u32x4*>(ckl),
       reinterpret_cast<u32x4*>(cvl), L, cache->capacity, cache->len, row_chunks, total);
   return pi::check_launch("cache_write_kernel");
 }
@@ -1101,8 +1185,8 @@ extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
 }
 
 pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
-                           const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool tiled,
-                           void* workspace, size_t workspace_bytes, hipStream_t s) {
+                           const uint8_t* suffix_ar, int B, int S, int Hq, float scale, float rope_base, void* o_s,
+                           bool tiled, void* workspace, size_t workspace_bytes, hipStream_t s) {
   PI_REQUIRE(cache && q_s && k_s && v_s && suffix_ar && o_s, PI_ERR_INVALID_ARG,
              "pi_suffix_decode_step: null pointer");
   PI_REQUIRE(cache->k && cache->v && cache->prefix_mask, PI_ERR_INVALID_ARG,
@@ -1116,22 +1200,36 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
              PI_ERR_INVALID_ARG, "pi_suffix_decode_step: cache/layer mismatch (layer %d of %d, B %d vs %d)", layer,
              cache->layers, cache->B, B);
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_suffix_decode_step: scale must be > 0");
+  PI_REQUIRE(rope_base == 0.f || (rope_base > 1.f && isfinite(rope_base)), PI_ERR_INVALID_ARG,
+             "pi_suffix_decode_step: rope_base must be 0 (off) or > 1");
   PI_REQUIRE((cache->len + TK - 1) / TK + (S + TK - 1) / TK <= kMaxTiles, PI_ERR_UNSUPPORTED,
              "pi_suffix_decode_step: cache length %d too long", cache->len);
   PI_REQUIRE(Hq == 8 && cache->Hkv == 1 && cache->d == 256, PI_ERR_UNSUPPORTED,
              "pi_suffix_decode_step: supported heads are Hq=8, Hkv=1, d=256 (got %d, %d, %d)", Hq, cache->Hkv,
              cache->d);
+  PI_REQUIRE(workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "pi_suffix_decode_step: workspace must be 256-byte aligned");
+  const bool rope = rope_base > 0.f;
+  const size_t rot_bytes = rope ? rope_ks_bytes(B, S) : 0;
+  PI_REQUIRE(!rope || (workspace != nullptr && workspace_bytes >= rot_bytes), PI_ERR_WORKSPACE,
+             "pi_suffix_decode_step: the rotary embedding needs pi_decode_workspace_bytes() of workspace");
   using C = CfgDec;
   const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  const void* kk = k_s;
+  if (rope) {
+    // the cache holds keys rotated by the prefill; the suffix keys are rotated here
+    const pi_status st = pi::rope_suffix(k_s, workspace, B, S, 1, 256, cache->prefix_mask, cache->capacity,
+                                         cache->len, rope_base, s);
+    if (st != PI_OK) return st;
+    kk = workspace;
+  }
+  char* split_ws = workspace ? static_cast<char*>(workspace) + rot_bytes : nullptr;
+  const size_t split_avail = workspace ? workspace_bytes - rot_bytes : 0;
   int splits = decode_splits(B, S, cache->len);
-  const size_t need = decode_ws_bytes(B, S, Hq, splits);
-  if (workspace == nullptr || workspace_bytes < need) splits = 1;   // no workspace: one pass per sample
-  PI_REQUIRE(splits == 1 || (reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
-             "pi_suffix_decode_step: workspace must be 256-byte aligned");
+  if (split_ws == nullptr || split_avail < split_ws_bytes<CfgDec>(B, S, splits)) splits = 1;   // one pass per sample
   const size_t chunks = (size_t)splits * B * n_qblk * kNWdec * kNR256;
-  float* opart = splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                        pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
+  float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
+  float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
                              : nullptr;
   const Placement place = make_placement(B * splits, n_qblk);
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
@@ -1139,8 +1237,9 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
   decode_kernel<256, 8, kNR256, kNWdec><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
       ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
-      static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
-      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart);
+      static_cast<const __bf16*>(kk), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart,
+      rope ? 1 : 0, rope ? log2((double)rope_base) : 0.0);
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
   decode_combine_kernel<kNR256, kNWdec><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
@@ -1150,8 +1249,8 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
 
 extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,
                                            const void* v_s, const uint8_t* suffix_ar, int B, int S, int Hq,
-                                           float scale, void* o_s, void* workspace, size_t workspace_bytes,
-                                           pi_stream stream) {
-  return pi::decode_layer(cache, layer, q_s, k_s, v_s, suffix_ar, B, S, Hq, scale, o_s, false, workspace,
-                          workspace_bytes, static_cast<hipStream_t>(stream));
+                                           float scale, float rope_base, void* o_s, void* workspace,
+                                           size_t workspace_bytes, pi_stream stream) {
+  return pi::decode_layer(cache, layer, q_s, k_s, v_s, suffix_ar, B, S, Hq, scale, rope_base, o_s, false,
+                          workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }

@@ -56,6 +56,20 @@ __device__ __forceinline__ bool pair_visible(uint32_t wq, uint32_t wk, uint32_t 
   return both_valid && block_ok && !banned;
 }
 
+// Rotary position embedding, rotate-half pairs (i, i + d/2): pair i turns by
+// p * base^(-2i/d) radians at position p.  inv_freq = base^(-2i/d) in fp64; the
+// angle is reduced to a fraction of a turn in fp64 and handed to the hardware
+// sine/cosine, which take their argument in turns.
+__device__ __forceinline__ double rope_inv_freq(int i, int d, double log2_base) {
+  return exp2(-(2.0 * (double)i / (double)d) * log2_base);
+}
+__device__ __forceinline__ void rope_cos_sin(int p, double inv_freq, float& c, float& s) {
+  const double turns = (double)p * inv_freq * 0.15915494309189535;   // / (2 pi)
+  const float fr = (float)(turns - rint(turns));                         // [-0.5, 0.5]
+  c = __builtin_amdgcn_cosf(fr);
+  s = __builtin_amdgcn_sinf(fr);
+}
+
 // Matrix-core operand tile layout of an [R x K] bf16 matrix (K a multiple of 32,
 // R padded to a multiple of 16): 16 x 32 tiles stored row-block major; inside a
 // tile, lane 16 * ((k % 32) / 8) + r % 16 holds the 8 elements of row r starting
@@ -73,6 +87,13 @@ void set_error(const char* fmt, ...);
 pi_status check_launch(const char* what);
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+// Rotary embedding of tokens x H rows of d (bf16, y may alias x), token t at pos[t].
+pi_status rope_rows(const void* x, void* y, int64_t tokens, int H, int d, const int32_t* pos, float base,
+                    hipStream_t stream);
+// The same for a decode suffix [B, S, H, d]: token t of sample b sits at
+// (valid slots among prefix_mask[b, 0 .. P)) + t.
+pi_status rope_suffix(const void* x, void* y, int B, int S, int H, int d, const uint8_t* prefix_mask, int cap,
+                      int P, float base, hipStream_t stream);
 // Largest decode workspace any cache length can ask for at this batch shape.
 size_t decode_workspace_max(int B, int S, int Hq);
 // Cached suffix decode of one layer.  q_s and o_s are row-major [B, S, Hq, d],
@@ -80,8 +101,8 @@ size_t decode_workspace_max(int B, int S, int Hq);
 // rows t*Hq + head of each sample, each sample's rows padded to whole 16-row
 // blocks; o_s as the [B*S x Hq*d] matrix.
 pi_status decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
-                       const uint8_t* suffix_ar, int B, int S, int Hq, float scale, void* o_s, bool tiled,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+                       const uint8_t* suffix_ar, int B, int S, int Hq, float scale, float rope_base, void* o_s,
+                       bool tiled, void* workspace, size_t workspace_bytes, hipStream_t stream);
 }  // namespace pi
 
 #define PI_REQUIRE(cond, code, ...)     \

@@ -366,7 +366,7 @@ pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint
     g.S = S;
     pi_status st = gemm<EPI_QKV, true>(g, s, "gemm_qkv");
     if (st != PI_OK) return st;
-    st = pi::decode_layer(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, w.o, true, w.dec, w.dec_bytes,
+    st = pi::decode_layer(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, n->Hq, scale, 0.f, w.o, true, w.dec, w.dec_bytes,
                           s);
     if (st != PI_OK) return st;
     GemmArgs go{};

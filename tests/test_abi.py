@@ -66,21 +66,27 @@ def test_prefill_rejects_bad_arguments_before_launch():
     m = Bd.PiMask(B=1, N=64, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
     call = lambda **kw: lib.pi_joint_attn_prefill(
         kw.get("q", FAKE), FAKE, FAKE, kw.get("B", 1), kw.get("L", 64), kw.get("Hq", 8), kw.get("Hkv", 1),
-        kw.get("d", 256), kw.get("scale", 0.0625), ctypes.byref(m), FAKE, None, 0, kw.get("ws", None),
-        kw.get("ws_bytes", 0), None)
+        kw.get("d", 256), kw.get("scale", 0.0625), kw.get("rope", 0.0), ctypes.byref(m), FAKE, None, 0,
+        kw.get("ws", None), kw.get("ws_bytes", 0), None)
     assert call(d=128) == -2                 # unsupported head dim
     assert call(Hq=6, Hkv=4) == -1           # Hq not a multiple of Hkv
     assert call(L=65) == -1                  # mask built for another length
     assert call(scale=0.0) == -1
+    assert call(rope=0.5) == -1              # rope_base must be 0 or > 1
     assert call(q=P(0x10008)) == -1          # misaligned
     assert call(q=None) == -1
     assert b"pi_joint_attn_prefill" in lib.pi_last_error()
-    # a small batch asks for a split workspace; a misaligned one is rejected
+    # the rotary embedding needs the workspace (rotated K)
+    assert call(rope=10000.0) == -3
+    assert call(rope=10000.0, ws=P(0x100000), ws_bytes=64 * 256 * 2 - 1) == -3
+    # the workspace holds the rotated K, plus the key split's partials for a small GQA batch
     need = lib.pi_prefill_workspace_bytes(1, 816, 8, 1, 256)
-    assert need > 0 and lib.pi_prefill_workspace_bytes(1, 816, 24, 24, 64) == 0
+    assert need > 816 * 256 * 2
+    assert lib.pi_prefill_workspace_bytes(1, 816, 24, 24, 64) == 816 * 24 * 64 * 2
+    assert lib.pi_prefill_workspace_bytes(1, 816, 8, 2, 256) == 0          # unsupported heads
     m816 = Bd.PiMask(B=1, N=816, n_qt=51, n_kt=26, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
-    assert lib.pi_joint_attn_prefill(FAKE, FAKE, FAKE, 1, 816, 8, 1, 256, 0.0625, ctypes.byref(m816), FAKE, None, 0,
-                                     P(0x100010), need, None) == -1
+    assert lib.pi_joint_attn_prefill(FAKE, FAKE, FAKE, 1, 816, 8, 1, 256, 0.0625, 0.0, ctypes.byref(m816), FAKE,
+                                     None, 0, P(0x100010), need, None) == -1   # misaligned workspace
 
 
 @needs_lib
@@ -88,16 +94,22 @@ def test_decode_and_flow_reject_bad_arguments_before_launch():
     lib = Bd.lib()
     cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 4, 816, 1, 256, 816)
     dec = lambda **kw: lib.pi_suffix_decode_step(ctypes.byref(cache), kw.get("layer", 0), FAKE, FAKE, FAKE, FAKE,
-                                                 kw.get("B", 4), kw.get("S", 51), kw.get("Hq", 8), 0.0625, FAKE,
-                                                 kw.get("ws", None), kw.get("ws_bytes", 0), None)
+                                                 kw.get("B", 4), kw.get("S", 51), kw.get("Hq", 8), 0.0625,
+                                                 kw.get("rope", 0.0), FAKE, kw.get("ws", None), kw.get("ws_bytes", 0),
+                                                 None)
     assert dec(layer=18) == -1
     assert dec(B=3) == -1
     assert dec(S=129) == -1
     assert dec(Hq=4) == -2
-    # a usable but misaligned split workspace is rejected
+    assert dec(rope=1.0) == -1
+    assert dec(rope=10000.0) == -3           # the rotary embedding needs the workspace
+    # a misaligned workspace is rejected
     need = lib.pi_decode_workspace_bytes(4, 51, 8, 816)
-    assert need > 0 and lib.pi_decode_workspace_bytes(64, 51, 8, 816) == 0
     assert dec(ws=P(0x100010), ws_bytes=need) == -1
+    # the workspace holds the rotated suffix K (every batch) plus a small batch's split partials
+    rot64 = (64 * 51 * 256 * 2 + 255) // 256 * 256
+    assert lib.pi_decode_workspace_bytes(64, 51, 8, 816) == rot64
+    assert need > (4 * 51 * 256 * 2 + 255) // 256 * 256
     assert lib.pi_euler_update(FAKE, FAKE, -0.1, -1, None) == -1
     assert lib.pi_flow_sample(None, None, None, None, None, FAKE, 1, 50, 32, 0, None, 0, None) == -1
     assert lib.pi_flow_sample(None, None, None, None, None, FAKE, 1, 50, 32, 10, None, 0, None) == -1  # no v_const
@@ -109,6 +121,21 @@ def test_decode_and_flow_reject_bad_arguments_before_launch():
     net_bad = Bd.PiVelocityNet(1000, 32, 8, 1, 256, *([FAKE] * 11))
     assert lib.pi_flow_sample(ctypes.byref(net_bad), ctypes.byref(cache), FAKE, FAKE, None, FAKE, 4, 50, 32, 10,
                               P(0x100000), 1 << 30, None) == -2
+
+
+@needs_lib
+def test_rope_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    call = lambda **kw: lib.pi_rope_apply(kw.get("x", FAKE), kw.get("y", FAKE), kw.get("B", 2), kw.get("L", 10),
+                                          kw.get("H", 8), kw.get("d", 256), kw.get("pos", FAKE),
+                                          kw.get("base", 10000.0), None)
+    assert call(d=24) == -2                  # not a multiple of 16
+    assert call(d=1024) == -2
+    assert call(base=1.0) == -1
+    assert call(pos=None) == -1
+    assert call(y=P(0x10004)) == -1          # misaligned
+    assert call(L=0) == -1
+    assert b"pi_rope_apply" in lib.pi_last_error()
 
 
 @needs_lib
