@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy"], default=None,
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope"], default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
 
@@ -205,6 +205,38 @@ def decode_kernel_leg(cx: Ctx, iters: int):
     }
 
 
+def rope_leg(cx: Ctx, iters: int):
+    """Rotary embedding at the π0.5 training shape (B=32, L=962): the standalone
+    rotation of Q and of K (HBM-bound: every element read and written once), and
+    the prefill with and without the rotary embedding (its cost on the hot path)."""
+    torch, Bd, I = cx.torch, cx.Bd, cx.I
+    w = I.WORKLOADS["pi05_three_block_prefill"]()
+    s = w.structure
+    q, k, v = (cx.bf(t) for t in w.qkv())
+    valid = cx.u8(w.input_mask())
+    m = Bd.pi_mask_build(valid, cx.u8(s.ar), cx.u8(s.seg), I.forbid_bits(s.forbid))
+    pos = m.pos()
+    ws = Bd.prefill_workspace(w.B, w.N, w.Hq, w.Hkv, w.d, cx.dev)
+    o = torch.empty_like(q)
+    yq, yk = torch.empty_like(q), torch.empty_like(k)
+    ms_q = cx.time_ms(lambda: Bd.pi_rope_apply(q, pos, 10000.0, y=yq), iters)
+    ms_k = cx.time_ms(lambda: Bd.pi_rope_apply(k, pos, 10000.0, y=yk), iters)
+    ms_plain = cx.time_ms(lambda: Bd.pi_joint_attn_prefill(q, k, v, m, o=o, workspace=ws), iters)
+    ms_rope = cx.time_ms(lambda: Bd.pi_joint_attn_prefill(q, k, v, m, o=o, workspace=ws, rope_base=10000.0), iters)
+    q_bytes, k_bytes = 2 * q.numel() * 2, 2 * k.numel() * 2
+    return {
+        "workload": w.name, "B": w.B, "L": w.N, "base": 10000.0,
+        "rope_q": {"kernel": "rope_kernel (Q, 8 heads)", "algorithmic_bytes_per_launch": q_bytes,
+                   "us_per_launch": ms_q * 1e3, "achieved_gbs": q_bytes / (ms_q * 1e-3) / 1e9,
+                   "hbm_frac": q_bytes / (ms_q * 1e-3) / PEAK_HBM_BYTES},
+        "rope_k": {"kernel": "rope_kernel (K, 1 head)", "algorithmic_bytes_per_launch": k_bytes,
+                   "us_per_launch": ms_k * 1e3, "achieved_gbs": k_bytes / (ms_k * 1e-3) / 1e9,
+                   "hbm_frac": k_bytes / (ms_k * 1e-3) / PEAK_HBM_BYTES},
+        "prefill_us": ms_plain * 1e3, "prefill_rope_us": ms_rope * 1e3,
+        "rope_overhead_us": (ms_rope - ms_plain) * 1e3,
+    }
+
+
 def copy_kernel_leg(cx: Ctx, iters: int):
     """A plain device-to-device copy of known size.  Its HBM byte counters give
     the scale factor that turns the counters of the path's kernels into bytes."""
@@ -336,6 +368,10 @@ def main():
     if args.only == "mmdit":
         kernels["mmdit"] = prefill_kernel_leg(cx, args.kernel_iters, "mmdit_full_bidirectional")
         log(str(kernels["mmdit"]))
+    if args.only in (None, "rope"):
+        log("rotary embedding leg (pi05 B=32 L=962)")
+        kernels["rope"] = rope_leg(cx, args.kernel_iters)
+        log(str(kernels["rope"]))
     if args.only is not None:
         print(json.dumps({"only": args.only, **result, "kernels": kernels}))
         return
@@ -371,6 +407,12 @@ def main():
                          "algorithmic_bytes_per_launch": pre["algorithmic_bytes"]},
         "decode_hbm": {"kernel": "decode_kernel (B=64 816 slots)", "achieved_gbs": dec["achieved_gbs"],
                        "frac": dec["hbm_frac"], "us_per_launch": dec["us_per_launch"]},
+        "rope": {"kernel": "rope_kernel (pi05 B=32 L=962, Q)", "bound": "hbm",
+                 "achieved": kernels["rope"]["rope_q"]["achieved_gbs"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                 "frac": kernels["rope"]["rope_q"]["hbm_frac"],
+                 "us_per_launch": kernels["rope"]["rope_q"]["us_per_launch"],
+                 "k_us_per_launch": kernels["rope"]["rope_k"]["us_per_launch"],
+                 "prefill_us": kernels["rope"]["prefill_us"], "prefill_rope_us": kernels["rope"]["prefill_rope_us"]},
         "breakdown_us": result["breakdown_us"],
         "cpu_baseline": cpu,
     }
