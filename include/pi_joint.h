@@ -173,6 +173,24 @@ pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void*
                                 void* workspace, size_t workspace_bytes, pi_stream stream);
 
 /*
+ * Single-token autoregressive decode ([P4] §4.1: after the prefill, every step
+ * runs one new token against the cache, which then keeps its K/V).  A step is
+ * pi_suffix_decode_step with S = 1 and suffix_ar = {1} (the token sees every
+ * valid cache slot and itself; a one-wave workgroup per key split), followed by
+ * pi_kv_cache_append of the token's k/v to every layer, after which the caller
+ * raises cache->len by n_new.
+ *
+ * Append n_new tokens per sample to cache layer `layer` at slots
+ * [len, len + n_new): k_new, v_new bf16 [B, n_new, Hkv, d]; their prefix_mask
+ * bytes are set to 1 (the mask's const qualifier in pi_kv_cache only says the
+ * attention calls read it).  With rope_base > 1 the keys are stored rotated,
+ * token t at (valid slots among [0, len)) + t, as the decode rotates its query.
+ * Requires len + n_new <= capacity; d a multiple of 16 up to 512.
+ */
+pi_status pi_kv_cache_append(const pi_kv_cache* cache, int layer, const void* k_new, const void* v_new,
+                             int n_new, float rope_base, pi_stream stream);
+
+/*
  * Rotary position embedding ([P1] §3.2: π0 keeps its LLM's rotary embedding;
  * positions per §1.5 / §1.6, e.g. pi_mask.pos).  For each token t of each sample
  * and each head, with p = pos[b*L + t] and i < d/2:

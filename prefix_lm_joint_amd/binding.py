@@ -57,6 +57,7 @@ _SIGS = {
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
                                      _c_f, _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "pi_rope_apply": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_f, _c_p]),
+    "pi_kv_cache_append": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_i, _c_f, _c_p]),
     "pi_euler_update": (_c_i, [_c_p, _c_p, _c_f, ctypes.c_int64, _c_p]),
     "pi_flow_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiVelocityNet), _c_i, _c_i]),
     "pi_velocity_eval": (_c_i, [ctypes.POINTER(PiVelocityNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_p, _c_f,
@@ -202,6 +203,15 @@ class KVCache:
         pm = torch.ones((B, capacity), dtype=torch.uint8, device=device)
         return cls(k, v, pm, length)
 
+    @property
+    def length(self) -> int:
+        return int(self.struct.len)
+
+    def advance(self, n: int) -> None:
+        """Raise the slot count after pi_kv_cache_append has written n tokens to every layer."""
+        assert self.struct.len + n <= self.struct.capacity
+        self.struct.len += n
+
     def layer_k(self, layer):
         return self.k[layer]
 
@@ -277,6 +287,16 @@ def pi_rope_apply(x: torch.Tensor, pos: torch.Tensor, base: float = 10000.0, y: 
     _check("pi_rope_apply", lib().pi_rope_apply(_ptr(x, torch.bfloat16, "x"), _ptr(y, torch.bfloat16, "y"), B, L, H,
                                                 d, _ptr(pos, torch.int32, "pos"), base, _stream(stream)))
     return y
+
+
+def pi_kv_cache_append(cache: KVCache, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                       rope_base: float = 0.0, stream=None) -> None:
+    """Write k_new/v_new [B, n, Hkv, d] at slots [len, len + n) of one layer and mark them valid.
+    The caller advances the length (KVCache.advance) once every layer has its tokens."""
+    n = k_new.shape[1]
+    _check("pi_kv_cache_append", lib().pi_kv_cache_append(
+        ctypes.byref(cache.struct), layer, _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
+        n, rope_base, _stream(stream)))
 
 
 def pi_euler_update(x: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> torch.Tensor:

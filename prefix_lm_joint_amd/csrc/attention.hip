@@ -680,7 +680,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   __shared__ int tcount;
   int grp, qblk;
   if (!xcd_place(place, grp, qblk)) return;
-  if (rope_pos != nullptr && threadIdx.x < D / 2) rope_if[threadIdx.x] = rope_inv_freq(threadIdx.x, D, rope_log2_base);
+  if (rope_pos != nullptr)
+    for (int i = threadIdx.x; i < D / 2; i += NW * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
   const int group = grp / n_split, split = grp % n_split;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -804,7 +805,8 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   __shared__ int tcount;
   int grp, qblk;
   if (!xcd_place(place, grp, qblk)) return;
-  if (rope && threadIdx.x < D / 2) rope_if[threadIdx.x] = rope_inv_freq(threadIdx.x, D, rope_log2_base);
+  if (rope)
+    for (int i = threadIdx.x; i < D / 2; i += NW * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
   const int b = grp / n_split, split = grp % n_split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * C::TOK;
@@ -1014,6 +1016,56 @@ __global__ void cache_write_kernel(const u32x4* __restrict__ k, const u32x4* __r
   cv[dst] = v[src];
 }
 
+// Append n_new tokens per sample (grid.y = sample) at slots [len, len + n_new) of a
+// cache layer: K (rotated at (valid slots before len) + t when log2_base != 0), V,
+// and their validity bytes.  One thread per 8 rotary pairs (16 bytes of each half)
+// of one (token, head) row.
+__global__ void __launch_bounds__(256)
+cache_append_kernel(const bf16x8* __restrict__ k_new, const bf16x8* __restrict__ v_new, bf16x8* __restrict__ ck,
+                    bf16x8* __restrict__ cv, uint8_t* __restrict__ pm, int cap, int len, int n_new, int Hkv, int d,
+                    double log2_base) {
+  __shared__ double inv_freq[256];
+  __shared__ int n_valid;
+  const int b = blockIdx.y;
+  const int half8 = d / 16;                      // 16-byte chunks per half row
+  const bool rope = log2_base != 0.0;
+  if (threadIdx.x == 0) n_valid = 0;
+  if (rope)
+    for (int i = threadIdx.x; i < d / 2; i += blockDim.x) inv_freq[i] = rope_inv_freq(i, d, log2_base);
+  __syncthreads();
+  if (rope) {
+    int cnt = 0;
+    for (int t = threadIdx.x; t < len; t += blockDim.x) cnt += pm[(int64_t)b * cap + t] != 0;
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(&n_valid, cnt);
+    __syncthreads();
+  }
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= (int64_t)n_new * Hkv * half8) return;
+  const int j = (int)(id % half8);
+  const int64_t row = id / half8;                 // t * Hkv + h
+  const int t = (int)(row / Hkv);
+  const int64_t src = ((int64_t)b * n_new * Hkv + row) * (d / 8);
+  const int64_t dst = (((int64_t)b * cap + len) * Hkv + row) * (d / 8);
+  bf16x8 lo = k_new[src + j], hi = k_new[src + half8 + j];
+  if (rope) {
+    const int p = n_valid + t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c, sn;
+      rope_cos_sin(p, inv_freq[8 * j + e], c, sn);
+      const float a = bf2f(lo[e]), bb = bf2f(hi[e]);
+      lo[e] = f2bf(a * c - bb * sn);
+      hi[e] = f2bf(bb * c + a * sn);
+    }
+  }
+  ck[dst + j] = lo;
+  ck[dst + half8 + j] = hi;
+  cv[dst + j] = v_new[src + j];
+  cv[dst + half8 + j] = v_new[src + half8 + j];
+  if (j == 0 && row % Hkv == 0) pm[(int64_t)b * cap + len + t] = 1;
+}
+
 // Launch shapes.  GQA 8:1 at d = 256: eight waves of one 16-row tile each (two
 // waves per SIMD, 16 query tokens x 8 heads per workgroup).  MHA at d = 64: eight
 // waves of one row tile (about 120 registers, so two workgroups share a CU).
@@ -1021,9 +1073,13 @@ constexpr int kNR256 = 1, kNW256 = 8;
 // The decode's 51-token suffix: seven waves (14 tokens) per workgroup cover it in
 // four workgroups with 5 padded tokens instead of 13.
 constexpr int kNWdec = 7;
+// A single-token (autoregressive) decode: one wave, one 16-row tile holding the
+// token's 8 heads (the other 8 rows idle); the key split supplies the parallelism.
+constexpr int kNWar = 1;
 constexpr int kNR64 = 1, kNW64 = 8;
 using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
 using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
+using CfgAr = Cfg<256, 8, kNR256, kNWar>;
 
 template <int D, int G, int NR, int NW>
 pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
@@ -1045,11 +1101,15 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
 
 // Key splits for a decode of B samples: enough workgroups to cover the chip
 // (about 256) while giving each split at least two key tiles.
-int decode_splits(int B, int S, int len) {
-  const int n_qblk = (S + CfgDec::TOK - 1) / CfgDec::TOK;
+template <typename C>
+int decode_splits_for(int B, int S, int len) {
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
   const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
   const int by_chip = 256 / std::max(1, B * n_qblk);
   return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
+}
+int decode_splits(int B, int S, int len) {
+  return S == 1 ? decode_splits_for<CfgAr>(B, S, len) : decode_splits_for<CfgDec>(B, S, len);
 }
 
 // Key splits for a GQA 8:1 prefill of B samples of L tokens (same rule as the
@@ -1075,9 +1135,12 @@ size_t split_ws_bytes(int B, int S, int splits) {
 size_t rope_ks_bytes(int B, int S) { return pi::align_up((size_t)B * S * 256 * 2, 256); }
 
 // Decode workspace: [rotated suffix K (rotary embedding only)] [key-split partials].
+size_t decode_split_bytes(int B, int S, int splits) {
+  return S == 1 ? split_ws_bytes<CfgAr>(B, S, splits) : split_ws_bytes<CfgDec>(B, S, splits);
+}
 size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
   (void)Hq;
-  return rope_ks_bytes(B, S) + split_ws_bytes<CfgDec>(B, S, splits);
+  return rope_ks_bytes(B, S) + decode_split_bytes(B, S, splits);
 }
 
 }  // namespace
@@ -1089,7 +1152,7 @@ size_t pi::decode_workspace_max(int B, int S, int Hq) {
 }
 
 // Bytes of the rotated K a prefill with the rotary embedding keeps in its workspace.
-size_t rope_k_bytes(int B, int L, int Hkv, int d) { return pi::align_up((size_t)B * L * Hkv * d * 2, 256); }
+static size_t rope_k_bytes(int B, int L, int Hkv, int d) { return pi::align_up((size_t)B * L * Hkv * d * 2, 256); }
 
 extern "C" size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
   if (B < 1 || L < 1) return 0;
@@ -1184,6 +1247,38 @@ extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
   return decode_ws_bytes(B, S, Hq, decode_splits(B, S, len));
 }
 
+namespace {
+
+// Launch the decode with NWD waves per workgroup (split partials in split_ws when
+// split_avail allows a key split), then the merge of the splits.
+template <int NWD>
+pi_status launch_decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf16* cvl, const void* q_s,
+                        const void* k_s, const void* v_s, const uint8_t* suffix_ar, int B, int S, float scale,
+                        float rope_base, void* o_s, bool tiled, char* split_ws, size_t split_avail, hipStream_t s) {
+  using C = Cfg<256, 8, kNR256, NWD>;
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  int splits = decode_splits_for<C>(B, S, cache->len);
+  if (split_ws == nullptr || split_avail < split_ws_bytes<C>(B, S, splits)) splits = 1;   // one pass per sample
+  const size_t chunks = (size_t)splits * B * n_qblk * NWD * kNR256;
+  float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
+  float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
+                             : nullptr;
+  const Placement place = make_placement(B * splits, n_qblk);
+  const bool rope = rope_base > 0.f;
+  decode_kernel<256, 8, kNR256, NWD><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
+      ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
+      static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart,
+      rope ? 1 : 0, rope ? log2((double)rope_base) : 0.0);
+  pi_status st = pi::check_launch("decode_kernel");
+  if (st != PI_OK || splits == 1) return st;
+  decode_combine_kernel<kNR256, NWD><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
+      opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits);
+  return pi::check_launch("decode_combine_kernel");
+}
+
+}  // namespace
+
 pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s, const void* v_s,
                            const uint8_t* suffix_ar, int B, int S, int Hq, float scale, float rope_base, void* o_s,
                            bool tiled, void* workspace, size_t workspace_bytes, hipStream_t s) {
@@ -1213,8 +1308,6 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   const size_t rot_bytes = rope ? rope_ks_bytes(B, S) : 0;
   PI_REQUIRE(!rope || (workspace != nullptr && workspace_bytes >= rot_bytes), PI_ERR_WORKSPACE,
              "pi_suffix_decode_step: the rotary embedding needs pi_decode_workspace_bytes() of workspace");
-  using C = CfgDec;
-  const int n_qblk = (S + C::TOK - 1) / C::TOK;
   const void* kk = k_s;
   if (rope) {
     // the cache holds keys rotated by the prefill; the suffix keys are rotated here
@@ -1225,26 +1318,14 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   }
   char* split_ws = workspace ? static_cast<char*>(workspace) + rot_bytes : nullptr;
   const size_t split_avail = workspace ? workspace_bytes - rot_bytes : 0;
-  int splits = decode_splits(B, S, cache->len);
-  if (split_ws == nullptr || split_avail < split_ws_bytes<CfgDec>(B, S, splits)) splits = 1;   // one pass per sample
-  const size_t chunks = (size_t)splits * B * n_qblk * kNWdec * kNR256;
-  float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
-  float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
-                             : nullptr;
-  const Placement place = make_placement(B * splits, n_qblk);
   const size_t layer_elems = (size_t)B * cache->capacity * 256;
   const __bf16* ckl = static_cast<const __bf16*>(cache->k) + (size_t)layer * layer_elems;
   const __bf16* cvl = static_cast<const __bf16*>(cache->v) + (size_t)layer * layer_elems;
-  decode_kernel<256, 8, kNR256, kNWdec><<<(unsigned)placement_grid(place), C::THREADS, 0, s>>>(
-      ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
-      static_cast<const __bf16*>(kk), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
-      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart,
-      rope ? 1 : 0, rope ? log2((double)rope_base) : 0.0);
-  pi_status st = pi::check_launch("decode_kernel");
-  if (st != PI_OK || splits == 1) return st;
-  decode_combine_kernel<kNR256, kNWdec><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
-      opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits);
-  return pi::check_launch("decode_combine_kernel");
+  if (S == 1)
+    return launch_decode<kNWar>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
+                                split_ws, split_avail, s);
+  return launch_decode<kNWdec>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
+                               split_ws, split_avail, s);
 }
 
 extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,
@@ -1253,4 +1334,33 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
                                            size_t workspace_bytes, pi_stream stream) {
   return pi::decode_layer(cache, layer, q_s, k_s, v_s, suffix_ar, B, S, Hq, scale, rope_base, o_s, false,
                           workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" pi_status pi_kv_cache_append(const pi_kv_cache* cache, int layer, const void* k_new, const void* v_new,
+                                        int n_new, float rope_base, pi_stream stream) {
+  PI_REQUIRE(cache && k_new && v_new, PI_ERR_INVALID_ARG, "pi_kv_cache_append: null pointer");
+  PI_REQUIRE(cache->k && cache->v && cache->prefix_mask, PI_ERR_INVALID_ARG,
+             "pi_kv_cache_append: cache has null pointers");
+  PI_REQUIRE(pi::aligned16(k_new) && pi::aligned16(v_new) && pi::aligned16(cache->k) && pi::aligned16(cache->v),
+             PI_ERR_INVALID_ARG, "pi_kv_cache_append: tensors must be 16-byte aligned");
+  PI_REQUIRE(layer >= 0 && layer < cache->layers && cache->B >= 1 && cache->B <= 65535, PI_ERR_INVALID_ARG,
+             "pi_kv_cache_append: layer %d of %d, B %d", layer, cache->layers, cache->B);
+  PI_REQUIRE(n_new >= 1 && cache->len >= 0 && cache->len + n_new <= cache->capacity, PI_ERR_INVALID_ARG,
+             "pi_kv_cache_append: %d tokens after %d do not fit %d slots", n_new, cache->len, cache->capacity);
+  PI_REQUIRE(cache->Hkv >= 1 && cache->d >= 16 && cache->d <= 512 && cache->d % 16 == 0, PI_ERR_UNSUPPORTED,
+             "pi_kv_cache_append: Hkv=%d d=%d", cache->Hkv, cache->d);
+  PI_REQUIRE(rope_base == 0.f || (rope_base > 1.f && isfinite(rope_base)), PI_ERR_INVALID_ARG,
+             "pi_kv_cache_append: rope_base must be 0 (off) or > 1");
+  const int d = cache->d, Hkv = cache->Hkv;
+  const size_t layer_elems = (size_t)cache->B * cache->capacity * Hkv * d;
+  bf16x8* ckl = reinterpret_cast<bf16x8*>(static_cast<__bf16*>(cache->k) + (size_t)layer * layer_elems);
+  bf16x8* cvl = reinterpret_cast<bf16x8*>(static_cast<__bf16*>(cache->v) + (size_t)layer * layer_elems);
+  const int64_t per_b = (int64_t)n_new * Hkv * (d / 16);
+  const dim3 grid((unsigned)((per_b + 255) / 256), (unsigned)cache->B);
+  // the prefix_mask is const for the attention calls, which only read it; the append owns these slots
+  cache_append_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(
+      static_cast<const bf16x8*>(k_new), static_cast<const bf16x8*>(v_new), ckl, cvl,
+      const_cast<uint8_t*>(cache->prefix_mask), cache->capacity, cache->len, n_new, Hkv, d,
+      rope_base > 0.f ? log2((double)rope_base) : 0.0);
+  return pi::check_launch("cache_append_kernel");
 }

@@ -124,6 +124,20 @@ def test_decode_and_flow_reject_bad_arguments_before_launch():
 
 
 @needs_lib
+def test_cache_append_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 2, 4, 816, 1, 256, 810)
+    app = lambda **kw: lib.pi_kv_cache_append(ctypes.byref(cache), kw.get("layer", 0), kw.get("k", FAKE), FAKE,
+                                              kw.get("n", 1), kw.get("rope", 0.0), None)
+    assert app(layer=2) == -1
+    assert app(n=7) == -1                    # 810 + 7 > 816 slots
+    assert app(n=0) == -1
+    assert app(rope=0.5) == -1
+    assert app(k=P(0x10008)) == -1
+    assert b"pi_kv_cache_append" in lib.pi_last_error()
+
+
+@needs_lib
 def test_rope_rejects_bad_arguments_before_launch():
     lib = Bd.lib()
     call = lambda **kw: lib.pi_rope_apply(kw.get("x", FAKE), kw.get("y", FAKE), kw.get("B", 2), kw.get("L", 10),
