@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope"], default=None,
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar"], default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
 
@@ -237,6 +237,55 @@ def rope_leg(cx: Ctx, iters: int):
     }
 
 
+def ar_decode_leg(cx: Ctx, iters: int):
+    """Single-token autoregressive decode at the serving shape (B=64, 816 slots, valid
+    length U[600,816]): one new token per sample against one cache layer (the 18
+    layers rotated as in the decode leg), then its K/V appended.  HBM-bound: each
+    valid slot's K and V are read once."""
+    torch, Bd, I = cx.torch, cx.Bd, cx.I
+    w = I.serving_decode()
+    s = w.structure
+    P, B = s.n_prefix, w.B
+    pm = w.input_mask()[:, :P]
+    lens = pm.sum(axis=1)
+    layers = w.layers
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(w.seed_base + 11)
+    cap = P + 16
+    ck = torch.randn((layers, B, cap, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cv = torch.randn((layers, B, cap, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    pmask = torch.zeros((B, cap), dtype=torch.uint8, device=cx.dev)
+    pmask[:, :P] = cx.u8(pm)
+    cache = Bd.KVCache(ck, cv, pmask, P)
+    qs = cx.bf(I.bf16_normal(w.seed_base + 13, (B, 1, 8, 256)))
+    ks = cx.bf(I.bf16_normal(w.seed_base + 14, (B, 1, 1, 256)))
+    vs = cx.bf(I.bf16_normal(w.seed_base + 15, (B, 1, 1, 256)))
+    sar = cx.u8(cx.np.array([1], cx.np.uint8))
+    o = torch.empty_like(qs)
+    ws = Bd.decode_workspace(cache, 1)
+    state = {"l": 0}
+
+    def step():
+        Bd.pi_suffix_decode_step(cache, state["l"] % layers, qs, ks, vs, sar, o_s=o, workspace=ws)
+        state["l"] += 1
+
+    def step_append():
+        # the new token goes to slot P of this layer each time (len stays P)
+        layer = state["l"] % layers
+        Bd.pi_suffix_decode_step(cache, layer, qs, ks, vs, sar, o_s=o, workspace=ws)
+        Bd.pi_kv_cache_append(cache, layer, ks, vs)
+        state["l"] += 1
+
+    ms = cx.time_ms(step, iters)
+    ms_app = cx.time_ms(step_append, iters)
+    byts = int(lens.sum()) * 256 * 2 * 2 + B * 8 * 256 * 2 * 2 + B * 256 * 2 * 2
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": "ar_decode_serving", "B": B, "slots": P, "valid_len_mean": float(lens.mean()),
+            "algorithmic_bytes_per_launch": byts, "us_per_step": ms * 1e3, "achieved_gbs": gbs,
+            "hbm_frac": gbs * 1e9 / PEAK_HBM_BYTES, "us_per_step_with_append": ms_app * 1e3,
+            "kernel": "decode_kernel (one wave, S=1) + decode_combine_kernel"}
+
+
 def copy_kernel_leg(cx: Ctx, iters: int):
     """A plain device-to-device copy of known size.  Its HBM byte counters give
     the scale factor that turns the counters of the path's kernels into bytes."""
@@ -368,6 +417,10 @@ def main():
     if args.only == "mmdit":
         kernels["mmdit"] = prefill_kernel_leg(cx, args.kernel_iters, "mmdit_full_bidirectional")
         log(str(kernels["mmdit"]))
+    if args.only in (None, "ar"):
+        log("autoregressive single-token decode leg (B=64 816 slots)")
+        kernels["ar"] = ar_decode_leg(cx, args.kernel_iters)
+        log(str(kernels["ar"]))
     if args.only in (None, "rope"):
         log("rotary embedding leg (pi05 B=32 L=962)")
         kernels["rope"] = rope_leg(cx, args.kernel_iters)
@@ -407,6 +460,10 @@ def main():
                          "algorithmic_bytes_per_launch": pre["algorithmic_bytes"]},
         "decode_hbm": {"kernel": "decode_kernel (B=64 816 slots)", "achieved_gbs": dec["achieved_gbs"],
                        "frac": dec["hbm_frac"], "us_per_launch": dec["us_per_launch"]},
+        "ar_decode": {"kernel": kernels["ar"]["kernel"] + " (B=64, 816 slots)", "bound": "hbm",
+                      "achieved": kernels["ar"]["achieved_gbs"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                      "frac": kernels["ar"]["hbm_frac"], "us_per_step": kernels["ar"]["us_per_step"],
+                      "us_per_step_with_append": kernels["ar"]["us_per_step_with_append"]},
         "rope": {"kernel": "rope_kernel (pi05 B=32 L=962, Q)", "bound": "hbm",
                  "achieved": kernels["rope"]["rope_q"]["achieved_gbs"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                  "frac": kernels["rope"]["rope_q"]["hbm_frac"],
