@@ -49,7 +49,8 @@ struct Cfg {
   static constexpr int ROWS_W = NR * 16;
   static constexpr int ROWS = NW * ROWS_W;
   static constexpr int TOK = ROWS / G;        // query tokens per workgroup
-  static constexpr int THREADS = NW * PI_WAVE;
+  static constexpr int NWT = NW + 1;             // NW compute waves and one load wave
+  static constexpr int THREADS = NWT * PI_WAVE;
   static_assert(ROWS % G == 0, "rows must cover whole tokens");
   static_assert(D == 256 || D == 64, "head dim 256 or 64");
 };
@@ -108,27 +109,25 @@ __device__ __forceinline__ PI_LDS uint32_t* lds_u32(const void* p) {
 // This wave's share of the direct-to-LDS loads of one K/V tile: the per-lane
 // byte offsets within a tile (row r of the tile at r * tsb, the row's swizzle
 // folded in) are computed once; each tile then only moves the resource base.
-template <int D, int NW>
+// Per-lane offsets of the load wave's direct-to-LDS loads: instruction j of a
+// tensor tile fetches rows j*RPI + lane/CHR, each lane one 16-byte chunk (its
+// source chunk pre-swizzled so the LDS image comes out XOR-swizzled).
+template <int D>
 struct KvLanes {
-  static constexpr int N = (Tile<D>::INSTS + NW - 1) / NW;   // loads per tensor and wave
+  static constexpr int N = Tile<D>::INSTS;
   uint32_t k[N], v[N];
   int row[N];
 };
 
-// Pieces a wave's share of one tile's loads is cut into: one per K and per V
-// instruction, then one for the tile's key words.
-template <int D, int NW>
-constexpr int kIssueParts = 2 * KvLanes<D, NW>::N + 1;
-
-template <int D, int NW>
-__device__ __forceinline__ KvLanes<D, NW> kv_lanes(int tsb) {
+template <int D>
+__device__ __forceinline__ KvLanes<D> kv_lanes(int tsb) {
   using T = Tile<D>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int p = lane % T::CHR;
-  KvLanes<D, NW> kl;
+  KvLanes<D> kl;
 #pragma unroll
-  for (int j = 0; j < KvLanes<D, NW>::N; ++j) {
-    const int r = (wave + j * NW) * T::RPI + lane / T::CHR;
+  for (int j = 0; j < KvLanes<D>::N; ++j) {
+    const int r = j * T::RPI + lane / T::CHR;
     kl.row[j] = r;
     kl.k[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fk(r));
     kl.v[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fv(r));
@@ -136,26 +135,25 @@ __device__ __forceinline__ KvLanes<D, NW> kv_lanes(int tsb) {
   return kl;
 }
 
-// Issue part p of this wave's loads of the tile whose first key is key0 (k0,
-// v0: key 0 of this sample and head; tsb bytes between consecutive keys): part
-// 2j is the wave's j-th K instruction, 2j+1 its j-th V instruction (parts past
-// the wave's share do nothing).  Keys whose bit is clear in `keymask` (past the
-// end, padding) are fetched from an out-of-range offset and land as zeros.
-template <int D, int NW>
-__device__ __forceinline__ void issue_kv_part(Stage<D>& st, const KvLanes<D, NW>& kl, const __bf16* k0,
-                                              const __bf16* v0, int key0, int tsb, uint32_t keymask, int p) {
+// All loads of the tile whose first key is key0 (k0, v0: key 0 of this sample
+// and head; tsb bytes between consecutive keys), issued by the load wave.  Keys
+// whose bit is clear in `keymask` (past the end, padding) are fetched from an
+// out-of-range offset and land as zeros.
+template <int D>
+__device__ __forceinline__ void issue_kv(Stage<D>& st, const KvLanes<D>& kl, const __bf16* k0, const __bf16* v0,
+                                         int key0, int tsb, uint32_t keymask) {
   using T = Tile<D>;
-  const int wave = threadIdx.x >> 6;
-  const int j = p >> 1;
-  const int q = wave + j * NW;
-  if (j >= KvLanes<D, NW>::N || q >= T::INSTS) return;
   const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(key0) * tsb;
   const bool full = __builtin_amdgcn_readfirstlane(keymask) == 0xFFFFFFFFu;
-  const bool is_v = p & 1;
-  uint32_t off = is_v ? kl.v[j] : kl.k[j];
-  if (!full && !((keymask >> kl.row[j]) & 1u)) off = kOOB;
-  const i32x4 rsrc = make_rsrc(reinterpret_cast<const char*>(is_v ? v0 : k0) + at);
-  pi_buffer_load_lds(rsrc, lds_u32(is_v ? &st.v[q * T::RPI * D] : &st.k[q * T::RPI * D]), 16, (int)off, 0, 0, 0);
+  const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(k0) + at);
+  const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(v0) + at);
+#pragma unroll
+  for (int j = 0; j < KvLanes<D>::N; ++j) {
+    uint32_t ok = kl.k[j], ov = kl.v[j];
+    if (!full && !((keymask >> kl.row[j]) & 1u)) ok = ov = kOOB;
+    pi_buffer_load_lds(rk, lds_u32(&st.k[j * T::RPI * D]), 16, (int)ok, 0, 0, 0);
+    pi_buffer_load_lds(rv, lds_u32(&st.v[j * T::RPI * D]), 16, (int)ov, 0, 0, 0);
+  }
 }
 
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0 only).
@@ -293,16 +291,15 @@ __device__ __forceinline__ void softmax_pre(const Stage<D>& sm, WaveState<D, NR>
 //   softmax:     the bf16 weights of tile i against the rows' reference maxima
 //                (s_cur -> pf_new) and the lane maxima for the growth check.
 // The products run in D/16 slots, each holding fragment j of both; the LDS reads
-// run AH fragments ahead of their products, and the NP pieces of the loads of
-// tile i+2 (iss) are dealt out over the slots, so the loads of all waves do not
-// queue at the texture unit at once.  Scheduling barriers between slots keep
-// that order.  The softmax follows the products: with two waves per SIMD it
-// overlaps the other wave's products.
-template <int D, int NR, bool PV, int NP, typename Iss>
-__device__ __forceinline__ void step_block(const Stage<D>& vst, const Stage<D>& kst, const LaneOffsets<D>& lo,
-                                           WaveState<D, NR>& st, const bf16x8 (&pf_prev)[NR],
-                                           const f32x4 (&s_cur)[NR][2], bf16x8 (&pf_new)[NR],
-                                           f32x4 (&s_nxt)[NR][2], float scale_log2, Iss iss) {
+// run AH fragments ahead of their products, and scheduling barriers between
+// slots keep that order.  The softmax follows the products: with two waves per
+// SIMD it overlaps the other wave's products.
+template <int D, int NR, bool PV>
+__device__ __forceinline__ void step_block(const Stage<D>& vst, const Stage<D>& cst, const Stage<D>& kst,
+                                           const LaneOffsets<D>& lo, WaveState<D, NR>& st,
+                                           const bf16x8 (&pf_prev)[NR], f32x4 (&s_cur)[NR][2],
+                                           bf16x8 (&pf_new)[NR], f32x4 (&s_nxt)[NR][2], int cls, uint32_t forbid,
+                                           float scale_log2) {
   constexpr uint32_t HALF = 16u * D * 2u;   // bytes of 16 rows
   constexpr int NS = D / 16;                // slots = V fragments = K fragments
   constexpr int AH = NS >= 8 ? 3 : 2;       // read-ahead, in fragments
@@ -344,11 +341,11 @@ __device__ __forceinline__ void step_block(const Stage<D>& vst, const Stage<D>& 
       if constexpr (PV) vbuf[j % AH] = read_v(j + AH);
       kbuf[j % AH] = read_k(j + AH);
     }
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-      if ((p * NS) / NP == j) iss(p);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // tile i's mask and first-tile bookkeeping (cst: its stage), after the products
+  // so a wave starts on the matrix cores right after the barrier
+  softmax_pre<D, NR>(cst, st, s_cur, cls, forbid, scale_log2);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     // a row that has seen no visible key keeps m = -inf: use 0 so masked weights are exp2(-inf) = 0
@@ -400,52 +397,57 @@ __device__ __forceinline__ int tile_cls(const TileDesc& t) { return (int)((t.d >
 
 // Tile loop shared by both kernels, software-pipelined over four LDS stages
 // (tile j lives in stage (j - i_lo) % 4; the loop is unrolled by four so every
-// LDS address is a per-lane offset plus a constant).  Step i: tile i's mask and
-// first-tile bookkeeping, then one block with tile i-1's PV, tile i+1's scores
-// (its K is already in LDS) and tile i's weights, while tile i+2 streams in.  A
-// tile's V is read one step after its weights are made, hence the fourth stage.
+// LDS address is a per-lane offset plus a constant).  One wave of the workgroup
+// (`loader`) issues every global->LDS load; the others only compute.  Step i:
+//   loader:   waits for its loads of tile i+1, passes the barrier, issues tile i+2
+//             into the stage of tile i-2;
+//   compute:  passes the barrier, then one block with tile i-1's PV and tile
+//             i+1's scores (its K is already in LDS) on the matrix cores, then
+//             tile i's mask, first-tile bookkeeping and weights.
+// A tile's V is read one step after its weights are made, hence the fourth stage.
+// Loads queued at the texture unit then stall only the loader, never a wave on
+// the matrix cores.
 //   desc(j): tile j's descriptor (LDS reads only)
+//   issue(t, stage): all loads of tile t into `stage` (the loader's job)
 //   prep(): once the first loads are out, work on the Q rows (the rotary
 //     embedding); it must be idempotent, the loop may run twice
-//   issue(t, stage, p): start piece p < NP of the loads of tile t into `stage`
-//     (every wave issues its own pieces)
-template <int D, int NR, int NP, typename Desc, typename Issue, typename Prep>
+template <int D, int NR, typename Desc, typename Issue, typename Prep>
 __device__ __forceinline__ void run_tiles(Stage<D> (&stage)[kStages], const LaneOffsets<D>& lo,
-                                          WaveState<D, NR>& st, int i_lo, int i_hi, Desc desc, Issue issue,
-                                          Prep prep, uint32_t forbid, float scale_log2) {
+                                          WaveState<D, NR>& st, int i_lo, int i_hi, bool loader, Desc desc,
+                                          Issue issue, Prep prep, uint32_t forbid, float scale_log2) {
   if (i_lo >= i_hi) return;
-  TileDesc t_cur = desc(i_lo), t_nxt = t_cur, t_far = t_cur;
-#pragma unroll
-  for (int p = 0; p < NP; ++p) issue(t_cur, stage[0], p);
-  if (i_lo + 1 < i_hi) {
-    t_nxt = desc(i_lo + 1);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) issue(t_nxt, stage[1], p);
+  if (loader) {
+    issue(desc(i_lo), stage[0]);
+    if (i_lo + 1 < i_hi) issue(desc(i_lo + 1), stage[1]);
+    wait_vmem();
+    __syncthreads();
+    for (int i = i_lo; i < i_hi; ++i) {
+      const bool more = i + 2 < i_hi;
+      const TileDesc t = desc(more ? i + 2 : i);
+      wait_vmem();          // tile i+1 has landed
+      __syncthreads();      // ... and every wave is done with tiles i-2 and below
+      if (more) issue(t, stage[(i + 2 - i_lo) & 3]);
+    }
+    return;
   }
-  if (i_lo + 2 < i_hi) t_far = desc(i_lo + 2);
+  TileDesc t_cur = desc(i_lo), t_nxt = t_cur;
+  if (i_lo + 1 < i_hi) t_nxt = desc(i_lo + 1);
   prep();               // row work that needs the Q registers, while the first tiles load
-  wait_vmem();
+  wait_vmem();          // the Q loads
   __syncthreads();
   f32x4 s_cur[NR][2];
   qk_tile<D, NR>(stage[0], lo, st, s_cur);
   bf16x8 pf[NR];
   // step i; the last step also computes scores against whatever stage `nxt`
   // holds and discards them, which keeps the block free of branches
-  auto step = [&](auto pv, int i, Stage<D>& prev, Stage<D>& cur, Stage<D>& nxt, Stage<D>& free_st) {
-    wait_vmem();          // this wave's loads of tile i+1 have landed
-    __syncthreads();      // ... everyone's; and everyone is done with tiles i-2 and below
-    softmax_pre<D, NR>(cur, st, s_cur, tile_cls(t_cur), forbid, scale_log2);
-    const TileDesc t_iss = t_far;
-    const bool do_issue = i + 2 < i_hi;
-    t_cur = t_nxt;
-    t_nxt = t_far;
-    if (i + 3 < i_hi) t_far = desc(i + 3);
+  auto step = [&](auto pv, int i, Stage<D>& prev, Stage<D>& cur, Stage<D>& nxt) {
+    __syncthreads();      // tile i+1 has landed; every wave is done with tile i-2
     bf16x8 pf_new[NR];
     f32x4 s_nxt[NR][2];
-    auto iss = [&](int p) {
-      if (do_issue) issue(t_iss, free_st, p);
-    };
-    step_block<D, NR, decltype(pv)::value, NP>(prev, nxt, lo, st, pf, s_cur, pf_new, s_nxt, scale_log2, iss);
+    step_block<D, NR, decltype(pv)::value>(prev, cur, nxt, lo, st, pf, s_cur, pf_new, s_nxt, tile_cls(t_cur), forbid,
+                                           scale_log2);
+    t_cur = t_nxt;
+    if (i + 2 < i_hi) t_nxt = desc(i + 2);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       pf[r] = pf_new[r];
@@ -455,12 +457,12 @@ __device__ __forceinline__ void run_tiles(Stage<D> (&stage)[kStages], const Lane
   };
   using NoPV = std::integral_constant<bool, false>;
   using WithPV = std::integral_constant<bool, true>;
-  step(NoPV{}, i_lo, stage[3], stage[0], stage[1], stage[2]);
+  step(NoPV{}, i_lo, stage[3], stage[0], stage[1]);
   for (int i = i_lo + 1; i < i_hi; i += 4) {
-    step(WithPV{}, i, stage[0], stage[1], stage[2], stage[3]);
-    if (i + 1 < i_hi) step(WithPV{}, i + 1, stage[1], stage[2], stage[3], stage[0]);
-    if (i + 2 < i_hi) step(WithPV{}, i + 2, stage[2], stage[3], stage[0], stage[1]);
-    if (i + 3 < i_hi) step(WithPV{}, i + 3, stage[3], stage[0], stage[1], stage[2]);
+    step(WithPV{}, i, stage[0], stage[1], stage[2]);
+    if (i + 1 < i_hi) step(WithPV{}, i + 1, stage[1], stage[2], stage[3]);
+    if (i + 2 < i_hi) step(WithPV{}, i + 2, stage[2], stage[3], stage[0]);
+    if (i + 3 < i_hi) step(WithPV{}, i + 3, stage[3], stage[0], stage[1]);
   }
   // the last tile's PV (its stage is not overwritten: no load is issued past i_hi)
   pv_last<D, NR>(stage[(i_hi - 1 - i_lo) & 3], lo, st, pf);
@@ -666,7 +668,7 @@ __device__ __forceinline__ void rotate_q(WaveState<D, NR>& st, const int (&pos)[
 // other LDS stage while tile i is computed.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NR, int NW>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__((NW + 1) * 64)
 prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
                __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
@@ -681,15 +683,16 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   int grp, qblk;
   if (!xcd_place(place, grp, qblk)) return;
   if (rope_pos != nullptr)
-    for (int i = threadIdx.x; i < D / 2; i += NW * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
+    for (int i = threadIdx.x; i < D / 2; i += C::NWT * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
   const int group = grp / n_split, split = grp % n_split;
   const int b = group / Hkv, kvh = group % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool loader = wave == NW;   // the last wave issues the K/V loads and computes nothing
   const int tok0 = qblk * C::TOK;
   const uint32_t* tk = tok + (size_t)b * L;
 
   // validity bitmap of every key tile (one ballot per 32 keys)
-  for (int base = wave * 64; base < n_kt * TK; base += NW * 64) {
+  for (int base = wave * 64; base < n_kt * TK; base += C::NWT * 64) {
     const int key = base + lane;
     const bool valid = key < L && (tk[key] & 1u);
     const unsigned long long bal = __ballot(valid);
@@ -722,7 +725,7 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   WaveState<D, NR> st;
   init_state(st);
   __bf16* row_base[NR];
-  load_rows<D, G, NR, C::ROWS_W>(st, row_base, q, o, (int64_t)b * L, L, Hq, kvh * G, tok0, tk);
+  if (!loader) load_rows<D, G, NR, C::ROWS_W>(st, row_base, q, o, (int64_t)b * L, L, Hq, kvh * G, tok0, tk);
   __syncthreads();
   const int count = tcount;
 
@@ -730,20 +733,16 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   const __bf16* v0 = v + ((size_t)b * L * Hkv + kvh) * D;
   const i32x4 rw = make_rsrc(tk);
   const int tsb = Hkv * D * 2;
-  const KvLanes<D, NW> kl = kv_lanes<D, NW>(tsb);
   const LaneOffsets<D> lo = lane_offsets<D>();
   auto desc = [&](int i) {
     const uint32_t d = tlist[i];
     return TileDesc{d, kmask[d & 0xFFFFu], 0u};
   };
-  auto issue = [&](const TileDesc& t, Stage<D>& sg, int p) {
+  auto issue = [&](const TileDesc& t, Stage<D>& sg) {
     const int key0 = (int)(t.d & 0xFFFFu) * TK;
-    if (p < kIssueParts<D, NW> - 1) {
-      issue_kv_part<D, NW>(sg, kl, k0, v0, key0, tsb, t.m, p);
-    } else if (wave == NW - 1) {
-      const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
-      pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
-    }
+    issue_kv<D>(sg, kv_lanes<D>(tsb), k0, v0, key0, tsb, t.m);
+    const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
+    pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
   };
   // this workgroup's share of the tile list (all of it when the keys are not split)
   const int i_lo = (int)((int64_t)count * split / n_split);
@@ -761,13 +760,14 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
     rotated = true;
   };
   auto run = [&]() {
-    run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, prep, forbid, scale_log2);
+    run_tiles<D, NR>(stage, lo, st, i_lo, i_hi, loader, desc, issue, prep, forbid, scale_log2);
   };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
     run();
   }
+  if (loader) return;
   if (n_split == 1) {
     store_rows<D, NR>(st, RowMajorDst<D>{row_base});
     return;
@@ -787,7 +787,7 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
 // unnormalised partial for decode_combine_kernel.
 // ---------------------------------------------------------------------------
 template <int D, int G, int NR, int NW>
-__global__ void __launch_bounds__(NW * 64)
+__global__ void __launch_bounds__((NW + 1) * 64)
 decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
               const uint8_t* __restrict__ prefix_mask, int cap, int P,
               const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
@@ -806,9 +806,10 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   int grp, qblk;
   if (!xcd_place(place, grp, qblk)) return;
   if (rope)
-    for (int i = threadIdx.x; i < D / 2; i += NW * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
+    for (int i = threadIdx.x; i < D / 2; i += C::NWT * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
   const int b = grp / n_split, split = grp % n_split;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool loader = wave == NW;   // the last wave issues the K/V loads and computes nothing
   const int tok0 = qblk * C::TOK;
   const int n_pt = (P + TK - 1) / TK;
   const int n_st = (S + TK - 1) / TK;
@@ -828,7 +829,7 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   }
   // validity bitmap of the prefix slots, one 32-bit word per tile
   const uint8_t* pm = prefix_mask + (size_t)b * cap;
-  for (int base = wave * 64; base < n_pt * TK; base += NW * 64) {
+  for (int base = wave * 64; base < n_pt * TK; base += C::NWT * 64) {
     const int slot = base + lane;
     const bool valid = slot < P && pm[slot] != 0;
     const unsigned long long bal = __ballot(valid);
@@ -867,38 +868,34 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   init_state(st);
   __bf16* row_base[NR];
   const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
-  load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, nullptr, q_tiled);
+  if (!loader) load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, nullptr, q_tiled);
   __syncthreads();
   // this workgroup's share of the tile list (all of it when the keys are not split)
   const int i_lo = (int)((int64_t)tcount * split / n_split);
   const int i_hi = (int)((int64_t)tcount * (split + 1) / n_split);
 
-  set_row_words<D, G, NR, C::ROWS_W>(st, S, tok0, sbid);
+  if (!loader) set_row_words<D, G, NR, C::ROWS_W>(st, S, tok0, sbid);
 
   const __bf16* k0 = ck + (size_t)b * cap * D;
   const __bf16* v0 = cv + (size_t)b * cap * D;
   const __bf16* ks0 = ks + (size_t)b * S * D;
   const __bf16* vs0 = vs + (size_t)b * S * D;
-  const KvLanes<D, NW> kl = kv_lanes<D, NW>(D * 2);
   const LaneOffsets<D> lo = lane_offsets<D>();
   auto desc = [&](int i) {
     const uint32_t d = tlist[i], m = tmask[i];
     uint32_t w = 0u;
-    if (threadIdx.x < TK) {
+    if (lane < TK) {
       const int key0 = (int)(d & 0xFFFFu) * TK;
-      const uint32_t bit = (m >> threadIdx.x) & 1u;
-      w = ((d >> 24) & 1u) ? (bit ? sbid[key0 + threadIdx.x] : 0u) : bit;
+      const uint32_t bit = (m >> lane) & 1u;
+      w = ((d >> 24) & 1u) ? (bit ? sbid[key0 + lane] : 0u) : bit;
     }
     return TileDesc{d, m, w};
   };
-  auto issue = [&](const TileDesc& t, Stage<D>& sg, int p) {
+  auto issue = [&](const TileDesc& t, Stage<D>& sg) {
     const int key0 = (int)(t.d & 0xFFFFu) * TK;
     const bool suffix = (t.d >> 24) & 1u;
-    if (p < kIssueParts<D, NW> - 1) {
-      issue_kv_part<D, NW>(sg, kl, suffix ? ks0 : k0, suffix ? vs0 : v0, key0, D * 2, t.m, p);
-    } else if (threadIdx.x < TK) {
-      sg.w[threadIdx.x] = t.w;
-    }
+    issue_kv<D>(sg, kv_lanes<D>(D * 2), suffix ? ks0 : k0, suffix ? vs0 : v0, key0, D * 2, t.m);
+    if (lane < TK) sg.w[lane] = t.w;
   };
   // suffix token t sits at position (valid prefix slots) + t
   bool rotated = !rope;
@@ -915,13 +912,14 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     rotated = true;
   };
   auto run = [&]() {
-    run_tiles<D, NR, kIssueParts<D, NW>>(stage, lo, st, i_lo, i_hi, desc, issue, prep, 0u, scale_log2);
+    run_tiles<D, NR>(stage, lo, st, i_lo, i_hi, loader, desc, issue, prep, 0u, scale_log2);
   };
   run();
   if (__syncthreads_or(needs_rerun(st))) {
     reset_for_rerun(st);
     run();
   }
+  if (loader) return;
   if (n_split == 1) {
     if (tiled) {
       const int c = lane & 15, g = lane >> 4;
@@ -1066,17 +1064,19 @@ cache_append_kernel(const bf16x8* __restrict__ k_new, const bf16x8* __restrict__
   if (j == 0 && row % Hkv == 0) pm[(int64_t)b * cap + len + t] = 1;
 }
 
-// Launch shapes.  GQA 8:1 at d = 256: eight waves of one 16-row tile each (two
-// waves per SIMD, 16 query tokens x 8 heads per workgroup).  MHA at d = 64: eight
-// waves of one row tile (about 120 registers, so two workgroups share a CU).
-constexpr int kNR256 = 1, kNW256 = 8;
-// The decode's 51-token suffix: seven waves (14 tokens) per workgroup cover it in
-// four workgroups with 5 padded tokens instead of 13.
+// Launch shapes (compute waves; every workgroup has one more wave that issues the
+// K/V loads).  GQA 8:1 at d = 256: seven waves of one 16-row tile (14 query
+// tokens x 8 heads per workgroup), eight waves in all, two per SIMD.  The
+// decode's 51-token suffix fits four such workgroups with 5 padded tokens.
+constexpr int kNR256 = 1, kNW256 = 7;
 constexpr int kNWdec = 7;
-// A single-token (autoregressive) decode: one wave, one 16-row tile holding the
-// token's 8 heads (the other 8 rows idle); the key split supplies the parallelism.
+// A single-token (autoregressive) decode: one compute wave, one 16-row tile
+// holding the token's 8 heads (the other 8 rows idle); the key split supplies
+// the parallelism.
 constexpr int kNWar = 1;
-constexpr int kNR64 = 1, kNW64 = 8;
+// MHA at d = 64: seven waves of one row tile (about 110 registers, so two
+// workgroups share a CU).
+constexpr int kNR64 = 1, kNW64 = 7;
 using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
 using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
 using CfgAr = Cfg<256, 8, kNR256, kNWar>;
