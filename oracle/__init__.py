@@ -19,6 +19,10 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
       ("VLA 代码精读" §1.6).
   flow.euler_sample / flow.euler_update
       the Euler flow-matching sampler, t from 1 to 0 ("VLA 代码精读" §1.2, §1.6).
+  attention_bwd.masked_attention_grads / attention_bwd.lse_rows
+      the gradients of the masked attention from their definitions, and the
+      rows' log-sum-exp (training differentiates the same joint forward,
+      "VLA 代码精读" §1.5).
   rope.rope / rope.joint_attention_rope
       the rotary position embedding of Q and K at the mask's positions
       ("VLA 代码精读" §3.2, §1.5, §1.6; the formula is a reading).
@@ -29,4 +33,4 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
 
 Readings of points the pages leave open are listed in each docstring.
 """
-from . import bf16, mask, attention, flow, rope  # noqa: F401
+from . import bf16, mask, attention, attention_bwd, flow, rope  # noqa: F401
