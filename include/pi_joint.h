@@ -114,6 +114,9 @@ pi_status pi_mask_materialize(const pi_mask* mask, uint8_t* dense, pi_stream str
  * rope_base: 0 = no rotary embedding; > 1 = q and k are rotated at the mask's
  * positions (pi_mask.pos) before the scores, as pi_rope_apply does (k into the
  * workspace, q in registers; the inputs are left untouched).
+ * lse (device, optional, fp32 [B, L, Hq]): when non-NULL, each row's natural-log
+ * log-sum-exp of its visible scaled scores, log sum_j exp(scale q.k_j) (-inf for
+ * a row with no visible key), the statistic pi_joint_attn_backward takes.
  * If `cache` is non-NULL, K/V rows of tokens [0, cache->len) are also copied to
  * cache layer `layer` (cache->B == B, cache->len <= L); with the rotary
  * embedding the cache receives the rotated keys.
@@ -128,8 +131,37 @@ typedef struct pi_kv_cache pi_kv_cache;
 size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
 pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
                                 int Hkv, int d, float scale, float rope_base, const pi_mask* mask,
-                                void* o, const pi_kv_cache* cache, int layer, void* workspace,
-                                size_t workspace_bytes, pi_stream stream);
+                                void* o, float* lse, const pi_kv_cache* cache, int layer,
+                                void* workspace, size_t workspace_bytes, pi_stream stream);
+
+/*
+ * Backward of the joint-attention prefill ([P1] §1.5: training runs the same
+ * joint forward under the block mask and differentiates the loss through it).
+ * Given the upstream gradient dO = dLoss/dO, per query row (b, i, h) with visible
+ * keys j (the one KV head):
+ *   P_j = exp(scale q.k_j - lse),  dP_j = dO.v_j,  Dr = dO.O,  dS_j = P_j (dP_j - Dr)
+ *   dq[b,i,h] = scale sum_j dS_j k_j;   dk[b,j] += scale dS_j q[b,i,h];   dv[b,j] += P_j dO[b,i,h]
+ * (sums over every row that sees key j).  Masked pairs contribute exactly
+ * nothing; a row with no visible key gets dq = 0, and a key no row sees gets
+ * dk = dv = 0.
+ *   q, o, dout, dq  bf16 [B, L, Hq, d]    k, v, dk, dv  bf16 [B, L, Hkv, d]
+ *   lse  fp32 [B, L, Hq]: the forward's log-sum-exp (pi_joint_attn_prefill's lse
+ *        output for the same q, k, mask and scale, rope_base 0); o: its output.
+ *   mask built for the same B and N = L; scale as in the forward.
+ * Supported: (Hq, Hkv, d) = (8, 1, 256), no rotary embedding (for a rotated
+ * forward pass the rotated q and k, then rotate dq and dk back with the negated
+ * positions).  bf16 matrix-core products with fp32 accumulation; P and dS are
+ * rounded to bf16 as operands, the gradients to bf16 on output.  Outputs must
+ * not overlap the inputs.  Three kernels on `stream` (row statistics, dk/dv
+ * key-major, dq query-major); no atomics, so results are deterministic.
+ * workspace (device, 256-byte aligned, required):
+ * pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d) bytes (0 = unsupported).
+ */
+size_t pi_attn_backward_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
+pi_status pi_joint_attn_backward(const void* q, const void* k, const void* v, const void* o,
+                                 const void* dout, const float* lse, int B, int L, int Hq, int Hkv,
+                                 int d, float scale, const pi_mask* mask, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, pi_stream stream);
 
 /*
  * Per-layer prefix KV cache ([P1] §1.6; [P4] §4.1).  Device memory owned by the caller.

@@ -51,8 +51,11 @@ _SIGS = {
     "pi_mask_materialize": (_c_i, [ctypes.POINTER(PiMask), _c_p, _c_p]),
     "pi_prefill_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i]),
     "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, _c_f,
-                                     ctypes.POINTER(PiMask), _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p,
+                                     ctypes.POINTER(PiMask), _c_p, _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p,
                                      ctypes.c_size_t, _c_p]),
+    "pi_attn_backward_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i]),
+    "pi_joint_attn_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f,
+                                      ctypes.POINTER(PiMask), _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
                                      _c_f, _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
@@ -232,7 +235,8 @@ def prefill_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device) -> Opti
 def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Mask, o: Optional[torch.Tensor] = None,
                           scale: Optional[float] = None, cache: Optional[KVCache] = None, layer: int = 0,
                           workspace: Optional[torch.Tensor] = None, stream=None,
-                          rope_base: float = 0.0) -> torch.Tensor:
+                          rope_base: float = 0.0, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``lse`` (fp32 [B, L, Hq]), when given, receives each row's log-sum-exp for a backward pass."""
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
     if scale is None:
@@ -242,10 +246,45 @@ def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     _check("pi_joint_attn_prefill", lib().pi_joint_attn_prefill(
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"), B, L, Hq, Hkv, d,
         scale, rope_base, ctypes.byref(mask.struct), _ptr(o, torch.bfloat16, "o"),
+        _ptr(lse, torch.float32, "lse") if lse is not None else None,
         ctypes.byref(cache.struct) if cache is not None else None, layer,
         _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None,
         workspace.numel() if workspace is not None else 0, _stream(stream)))
     return o
+
+
+def pi_attn_backward_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:
+    return int(lib().pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d))
+
+
+def backward_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device) -> torch.Tensor:
+    """Device workspace of pi_joint_attn_backward (the rows' statistics)."""
+    n = pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d)
+    if n == 0:
+        raise ValueError(f"pi_joint_attn_backward does not support (Hq={Hq}, Hkv={Hkv}, d={d})")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pi_joint_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+                           lse: torch.Tensor, mask: Mask, workspace: torch.Tensor, scale: Optional[float] = None,
+                           dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                           dv: Optional[torch.Tensor] = None, stream=None):
+    """Gradients (dq, dk, dv) of the prefill for upstream gradient ``dout``; ``o`` and ``lse``
+    are the prefill's output and log-sum-exp."""
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check("pi_joint_attn_backward", lib().pi_joint_attn_backward(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
+        _ptr(o, torch.bfloat16, "o"), _ptr(dout, torch.bfloat16, "dout"), _ptr(lse, torch.float32, "lse"),
+        B, L, Hq, Hkv, d, scale, ctypes.byref(mask.struct), _ptr(dq, torch.bfloat16, "dq"),
+        _ptr(dk, torch.bfloat16, "dk"), _ptr(dv, torch.bfloat16, "dv"), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream)))
+    return dq, dk, dv
 
 
 def pi_decode_workspace_bytes(B: int, S: int, Hq: int, length: int) -> int:

@@ -33,6 +33,7 @@
 //     the per-pair rule.  Workgroups of one (sample, KV head) are placed on one
 //     XCD so their K/V reads share that XCD's L2.
 #include "common.h"
+#include "engine.h"
 
 #include <math.h>
 
@@ -41,8 +42,7 @@
 
 namespace {
 
-constexpr int TK = 32;             // keys per tile
-constexpr int kMaxTiles = 512;     // longest key sequence a workgroup walks: 16384 tokens
+using namespace pi_engine;
 
 template <int D, int G, int NR, int NW>
 struct Cfg {
@@ -54,115 +54,6 @@ struct Cfg {
   static_assert(ROWS % G == 0, "rows must cover whole tokens");
   static_assert(D == 256 || D == 64, "head dim 256 or 64");
 };
-
-// ---------------------------------------------------------------------------
-// Swizzled LDS tile.  A row holds D bf16 (CHR chunks of 16 bytes); logical chunk
-// x of row r sits at physical chunk x ^ f(r).
-//   K fragment read: 16 lanes read rows r0..r0+15 at one logical chunk.  d = 256:
-//     f_K(r) = r & 15 spreads them over 16 distinct chunks (all 64 banks);
-//     d = 64 (rows of 32 banks): f_K(r) = (r >> 1) & 7 does the same.
-//   V transposing read: 16 lanes read 4 rows x 32 bytes (two chunks).
-//     d = 256: f_V(r) = 2r & 31; d = 64: f_V(r) = r & 6; 32 lanes (8 rows) then
-//     cover all 64 banks once.
-// ---------------------------------------------------------------------------
-template <int D>
-struct Tile {
-  static constexpr int CHR = D / 8;                 // 16-byte chunks per row
-  static constexpr int RPI = 64 / CHR;              // rows per 64-lane load instruction
-  static constexpr int INSTS = TK / RPI;            // load instructions per tensor tile
-  __device__ static __forceinline__ int fk(int r) { return D == 256 ? (r & 15) : ((r >> 1) & 7); }
-  __device__ static __forceinline__ int fv(int r) { return D == 256 ? ((2 * r) & 31) : (r & 6); }
-};
-
-template <int D>
-struct Stage {
-  alignas(16) __bf16 k[TK * D];
-  alignas(16) __bf16 v[TK * D];
-  alignas(16) uint32_t w[64];   // per-key mask words (lanes >= 32 land as zeros)
-};
-
-#define PI_LDS __attribute__((address_space(3)))
-
-typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
-
-extern "C" __device__ void pi_buffer_load_lds(i32x4 rsrc, PI_LDS uint32_t* lds, int size, int voffset, int soffset,
-                                              int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Buffer resource over [base, base + 2 GiB): any offset >= 0x7FFFFFFF reads as zero.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base) {
-  struct __attribute__((packed)) Res {
-    const void* p;
-    uint32_t range;
-    uint32_t cfg;
-  } r{base, 0x7FFFFFFFu, 0x00020000u};
-  i32x4 v = __builtin_bit_cast(i32x4, r);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_readfirstlane(v[i]);
-  return v;
-}
-constexpr uint32_t kOOB = 0x80000000u;
-
-__device__ __forceinline__ PI_LDS uint32_t* lds_u32(const void* p) {
-  return (PI_LDS uint32_t*)(const_cast<void*>(p));
-}
-
-// This wave's share of the direct-to-LDS loads of one K/V tile: the per-lane
-// byte offsets within a tile (row r of the tile at r * tsb, the row's swizzle
-// folded in) are computed once; each tile then only moves the resource base.
-// Per-lane offsets of the load wave's direct-to-LDS loads: instruction j of a
-// tensor tile fetches rows j*RPI + lane/CHR, each lane one 16-byte chunk (its
-// source chunk pre-swizzled so the LDS image comes out XOR-swizzled).
-template <int D>
-struct KvLanes {
-  static constexpr int N = Tile<D>::INSTS;
-  uint32_t k[N], v[N];
-  int row[N];
-};
-
-template <int D>
-__device__ __forceinline__ KvLanes<D> kv_lanes(int tsb) {
-  using T = Tile<D>;
-  const int lane = threadIdx.x & 63;
-  const int p = lane % T::CHR;
-  KvLanes<D> kl;
-#pragma unroll
-  for (int j = 0; j < KvLanes<D>::N; ++j) {
-    const int r = j * T::RPI + lane / T::CHR;
-    kl.row[j] = r;
-    kl.k[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fk(r));
-    kl.v[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fv(r));
-  }
-  return kl;
-}
-
-// All loads of the tile whose first key is key0 (k0, v0: key 0 of this sample
-// and head; tsb bytes between consecutive keys), issued by the load wave.  Keys
-// whose bit is clear in `keymask` (past the end, padding) are fetched from an
-// out-of-range offset and land as zeros.
-template <int D>
-__device__ __forceinline__ void issue_kv(Stage<D>& st, const KvLanes<D>& kl, const __bf16* k0, const __bf16* v0,
-                                         int key0, int tsb, uint32_t keymask) {
-  using T = Tile<D>;
-  const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(key0) * tsb;
-  const bool full = __builtin_amdgcn_readfirstlane(keymask) == 0xFFFFFFFFu;
-  const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(k0) + at);
-  const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(v0) + at);
-#pragma unroll
-  for (int j = 0; j < KvLanes<D>::N; ++j) {
-    uint32_t ok = kl.k[j], ov = kl.v[j];
-    if (!full && !((keymask >> kl.row[j]) & 1u)) ok = ov = kOOB;
-    pi_buffer_load_lds(rk, lds_u32(&st.k[j * T::RPI * D]), 16, (int)ok, 0, 0, 0);
-    pi_buffer_load_lds(rv, lds_u32(&st.v[j * T::RPI * D]), 16, (int)ov, 0, 0, 0);
-  }
-}
-
-// Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0 only).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Transposing LDS read of 4 bf16 (see the header comment for the lane mapping).
-__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((PI_LDS bf16x4*)(const_cast<__bf16*>(p)));
-}
 
 // Per-wave state of the online softmax.  m is each row's reference maximum
 // (scores already multiplied by scale*log2(e)), fixed at the row's first tile
@@ -506,39 +397,6 @@ __device__ __forceinline__ void init_state(WaveState<D, NR>& st) {
   st.all_set = false;
 }
 
-// Workgroup placement.  Workgroups are dispatched round-robin over the 8 XCDs,
-// each with its own L2.  With at least 8 groups, a group's workgroups (which read
-// the same K/V) are kept on one XCD.  With fewer groups (one or a few samples,
-// whose K/V are small) the workgroups simply go round-robin in group-major
-// order, which spreads every group over all XCDs and keeps the XCDs balanced.
-// Returns false for a workgroup with no work (the grid is rounded up).
-struct Placement {
-  int n_groups, n_sub;
-  bool per_xcd;
-};
-
-__host__ __device__ inline Placement make_placement(int n_groups, int n_sub) {
-  return Placement{n_groups, n_sub, n_groups >= 8};
-}
-
-__host__ inline int64_t placement_grid(const Placement& p) {
-  return p.per_xcd ? (int64_t)((p.n_groups + 7) / 8 * 8) * p.n_sub : (int64_t)p.n_groups * p.n_sub;
-}
-
-__device__ __forceinline__ bool xcd_place(const Placement& p, int& group, int& sub) {
-  const int id = blockIdx.x;
-  if (!p.per_xcd) {
-    group = id / p.n_sub;
-    sub = id % p.n_sub;
-    return group < p.n_groups;
-  }
-  const int xcd = id & 7;
-  const int k = id >> 3;
-  group = (k / p.n_sub) * 8 + xcd;
-  sub = k % p.n_sub;
-  return group < p.n_groups;
-}
-
 // Normalise and store O rows.  dst(r, dt) gives where the lane's four values
 // d = 16 dt + 4 g .. + 3 of row tile r go, or nullptr for a row with no output.
 template <int D, int NR, typename Dst>
@@ -673,7 +531,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
                __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
                const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
                uint32_t forbid, Placement place, int n_split, float* __restrict__ opart,
-               float* __restrict__ mlpart, const int32_t* __restrict__ rope_pos, double rope_log2_base) {
+               float* __restrict__ mlpart, const int32_t* __restrict__ rope_pos, double rope_log2_base,
+               float* __restrict__ lse) {
   using C = Cfg<D, G, NR, NW>;
   __shared__ Stage<D> stage[kStages];
   __shared__ uint32_t kmask[kMaxTiles];
@@ -691,35 +550,8 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   const int tok0 = qblk * C::TOK;
   const uint32_t* tk = tok + (size_t)b * L;
 
-  // validity bitmap of every key tile (one ballot per 32 keys)
-  for (int base = wave * 64; base < n_kt * TK; base += C::NWT * 64) {
-    const int key = base + lane;
-    const bool valid = key < L && (tk[key] & 1u);
-    const unsigned long long bal = __ballot(valid);
-    if (lane == 0) kmask[base / TK] = (uint32_t)bal;
-    if (lane == 32 && base / TK + 1 < n_kt) kmask[base / TK + 1] = (uint32_t)(bal >> 32);
-  }
-  if (wave == 0) {
-    const int qt_lo = tok0 / PI_MASK_TILE_Q;
-    const int qt_hi = min(n_qt, (tok0 + C::TOK + PI_MASK_TILE_Q - 1) / PI_MASK_TILE_Q);
-    const uint8_t* trow = tiles + (size_t)b * n_qt * n_kt;
-    int cnt = 0;
-    for (int base = 0; base < n_kt; base += 64) {
-      const int kt = base + lane;
-      int cls = 0;
-      if (kt < n_kt) {
-        cls = -1;
-        for (int qt = qt_lo; qt < qt_hi; ++qt) {
-          const int cl = trow[(size_t)qt * n_kt + kt];
-          cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
-        }
-      }
-      const unsigned long long bal = __ballot(cls > 0);
-      if (cls > 0) tlist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)kt | ((uint32_t)cls << 16);
-      cnt += __popcll(bal);
-    }
-    if (lane == 0) tcount = cnt;
-  }
+  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, C::TOK, C::NWT, kmask, tlist,
+                    &tcount);
   // the Q loads go out after the setup's own global reads (which wait on their
   // results) and stay in flight through the barrier and the first K/V loads
   WaveState<D, NR> st;
@@ -769,6 +601,17 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   }
   if (loader) return;
   if (n_split == 1) {
+    if (lse != nullptr && lane < 16) {
+      // natural-log log-sum-exp of the row's visible scaled scores (-inf with none)
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int row = wave * C::ROWS_W + r * 16 + lane;
+        const int t = tok0 + row / G;
+        if (t < L)
+          lse[((int64_t)b * L + t) * Hq + kvh * G + row % G] =
+              st.l[r][0] > 0.f ? (st.m[r] + log2f(st.l[r][0])) * 0.6931471805599453f : -INFINITY;
+      }
+    }
     store_rows<D, NR>(st, RowMajorDst<D>{row_base});
     return;
   }
@@ -948,7 +791,8 @@ constexpr int kMaxSplit = 16;
 template <int NR, int NW>
 __global__ void __launch_bounds__(256)
 decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__ mlpart,
-                      __bf16* __restrict__ os, int o_tiled, int B, int S, int n_qblk, int n_split) {
+                      __bf16* __restrict__ os, int o_tiled, int B, int S, int n_qblk, int n_split,
+                      float* __restrict__ lse) {
   constexpr int D = 256, G = 8, TOK = NR * NW * 16 / G;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -991,6 +835,8 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (lse != nullptr && dt == 0 && g == 0)
+    lse[(b * S + t) * G + head] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
   bf16x4 v;
 #pragma unroll
   for (int i = 0; i < 4; ++i) v[i] = f2bf(acc[i] * inv);
@@ -1084,7 +930,7 @@ using CfgAr = Cfg<256, 8, kNR256, kNWar>;
 template <int D, int G, int NR, int NW>
 pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv,
                          float scale, const pi_mask* m, int n_split, float* opart, float* mlpart,
-                         float rope_base, hipStream_t s) {
+                         float rope_base, float* lse, hipStream_t s) {
   using C = Cfg<D, G, NR, NW>;
   const int n_qblk = (L + C::TOK - 1) / C::TOK;
   const Placement place = make_placement(B * Hkv * n_split, n_qblk);
@@ -1095,7 +941,7 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<__bf16*>(o), B, L, Hq, Hkv, scale_log2, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits,
       place, n_split, opart, mlpart, rope_base > 0.f ? m->pos : nullptr,
-      rope_base > 0.f ? log2((double)rope_base) : 0.0);
+      rope_base > 0.f ? log2((double)rope_base) : 0.0, lse);
   return pi::check_launch("prefill_kernel");
 }
 
@@ -1163,8 +1009,8 @@ extern "C" size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int 
 
 extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int B, int L, int Hq,
                                            int Hkv, int d, float scale, float rope_base, const pi_mask* mask,
-                                           void* o, const pi_kv_cache* cache, int layer, void* workspace,
-                                           size_t workspace_bytes, pi_stream stream) {
+                                           void* o, float* lse, const pi_kv_cache* cache, int layer,
+                                           void* workspace, size_t workspace_bytes, pi_stream stream) {
   PI_REQUIRE(q && k && v && o && mask, PI_ERR_INVALID_ARG, "pi_joint_attn_prefill: null pointer");
   PI_REQUIRE(pi::aligned16(q) && pi::aligned16(k) && pi::aligned16(v) && pi::aligned16(o), PI_ERR_INVALID_ARG,
              "pi_joint_attn_prefill: tensors must be 16-byte aligned");
@@ -1218,15 +1064,15 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
     float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
                                : nullptr;
     st = launch_prefill<256, 8, kNR256, kNW256>(q, kk, v, o, B, L, Hq, Hkv, scale, mask, splits, opart, mlpart,
-                                                rope_base, s);
+                                                rope_base, splits > 1 ? nullptr : lse, s);
     if (st == PI_OK && splits > 1) {
       decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
-          opart, mlpart, static_cast<__bf16*>(o), 0, B, L, n_qblk, splits);
+          opart, mlpart, static_cast<__bf16*>(o), 0, B, L, n_qblk, splits, lse);
       st = pi::check_launch("decode_combine_kernel");
     }
   } else {
     st = launch_prefill<64, 1, kNR64, kNW64>(q, kk, v, o, B, L, Hq, Hkv, scale, mask, 1, nullptr, nullptr,
-                                             rope_base, s);
+                                             rope_base, lse, s);
   }
   if (st != PI_OK || !cache) return st;
   const int row_chunks = Hkv * d / 8;
@@ -1273,7 +1119,7 @@ pi_status launch_decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf1
   pi_status st = pi::check_launch("decode_kernel");
   if (st != PI_OK || splits == 1) return st;
   decode_combine_kernel<kNR256, NWD><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
-      opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits);
+      opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits, nullptr);
   return pi::check_launch("decode_combine_kernel");
 }
 

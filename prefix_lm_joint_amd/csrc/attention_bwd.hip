@@ -1,0 +1,667 @@
+// Backward of the masked grouped-query joint attention (Hq = 8, Hkv = 1, d = 256), gfx950.
+//
+// What is computed ("VLA 代码精读 — OpenPI & StarVLA" §1.5: training runs the
+// same joint forward under the block mask and differentiates the loss through
+// it): for an upstream gradient dO of the output, per query row (b, t, h) with
+// visible keys J (all rows read the one KV head),
+//   P_j  = exp(scale q.k_j - lse)         lse: the row's log-sum-exp (the forward keeps it)
+//   dP_j = dO.v_j,   Dr = dO.O = sum_j P_j dP_j
+//   dS_j = P_j (dP_j - Dr)
+//   dQ   = scale sum_j dS_j k_j,   dK_j += scale dS_j q,   dV_j += P_j dO.
+// Masked pairs get P = 0 by selection; a row with no visible key contributes
+// nothing.
+//
+// Kernels:
+//   * bwd_prep_kernel: Dr of every row from the bf16 O and dO (fp32 sum), and
+//     the row's lse in base 2 (+inf for a row with no visible key, whose
+//     weights then come out exactly 0).
+//   * dq_kernel: query-major, organised like the forward: 7 waves x 16 rows
+//     (14 tokens x 8 heads) per workgroup with Q and dO rows in registers; a load
+//     wave streams K/V tiles of 32 keys over four LDS stages.  Per tile:
+//     S^T = K Q^T and dP^T = V dO^T (row-wise reads of K and V), dS^T
+//     elementwise, dQ^T += K^T dS^T (the transposing read of K, dS^T straight
+//     from the accumulators as in the forward's PV).
+//   * dkdv_kernel: key-major, the same engine with queries and keys swapped: 4
+//     waves x 16 keys per workgroup with K and V rows in registers, tiles of 32
+//     query rows (4 tokens x 8 heads) of Q, dO and the row statistics streamed
+//     over four LDS stages.  Per tile: S^T = Q K^T and dP^T = dO V^T (row-wise
+//     reads), P^T and dS^T elementwise, dV^T += dO^T P^T and dK^T += Q^T dS^T
+//     (transposing reads).  The fp32 dK and dV of 16 keys x 256 take 128
+//     registers per lane, so each wave runs alone on its SIMD with the whole
+//     register file and issues its share of the tile loads itself.
+//   * Every tile is swizzled with f_U, so one copy in LDS serves both the
+//     row-wise and the transposing read without bank conflicts.
+// Each pipeline step runs one block on the matrix cores: the transposed
+// products of tile i-1 and the row-wise products of tile i+1, then the
+// elementwise work of tile i; tile i+2 streams in meanwhile.
+#include "common.h"
+#include "engine.h"
+
+#include <math.h>
+
+#include <type_traits>
+
+namespace {
+
+using namespace pi_engine;
+
+constexpr int BD = 256;                       // head dim
+constexpr int BG = 8;                         // query heads (the KV head is shared)
+constexpr int kStagesB = 4;
+constexpr uint32_t kHalf = 16u * BD * 2u;     // bytes of 16 tile rows
+constexpr float kLog2e = 1.4426950408889634f;
+using T256 = Tile<BD>;
+
+// Per-lane byte offsets of the operand reads within a tile, computed once.
+//   row(ds): row-wise read, rows c (+16 rows: + kHalf), logical chunk 4 ds + g
+//            (A[c][32 ds + 8 g ..] of a 16-row block)
+//   tr(dt):  transposing read, rows 4g + c/4 (+16 rows: + kHalf), columns
+//            16 dt + 4 (c % 4) ..; hands lane (c, g) column 16 dt + c of rows
+//            4g .. 4g+3 (and 16 + 4g ..), the k slots of the accumulator layout.
+// f_U < 16 flips only the low four chunk bits, so the upper half of a row (chunks
+// 16..31) is the lower half's offset + 256 bytes: only half the offsets are kept.
+struct BwdOffsets {
+  uint32_t row_[BD / 64];
+  uint32_t tr_[BD / 32];
+  __device__ __forceinline__ uint32_t row(int ds) const { return row_[ds & 3] + (uint32_t)(ds >> 2) * 256u; }
+  __device__ __forceinline__ uint32_t tr(int dt) const { return tr_[dt & 7] + (uint32_t)(dt >> 3) * 256u; }
+};
+static_assert(BD == 256, "offset halves assume rows of 32 chunks");
+
+__device__ __forceinline__ BwdOffsets bwd_offsets() {
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  BwdOffsets lo;
+#pragma unroll
+  for (int ds = 0; ds < BD / 64; ++ds) lo.row_[ds] = 2u * (uint32_t)(c * BD + 8 * ((4 * ds + g) ^ T256::fu(c)));
+  const int vr = 4 * g + (c >> 2);
+#pragma unroll
+  for (int dt = 0; dt < BD / 32; ++dt)
+    lo.tr_[dt] = 2u * (uint32_t)(vr * BD + 4 * (c & 1) + 8 * ((2 * dt + ((c & 3) >> 1)) ^ T256::fu(vr)));
+  return lo;
+}
+
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 read_row(const __bf16* tile, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + off);
+}
+__device__ __forceinline__ bf16x8 read_tr(const __bf16* tile, uint32_t off) {
+  const bf16x4 lo4 = lds_read_tr4(reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(tile) + off));
+  const bf16x4 hi4 =
+      lds_read_tr4(reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(tile) + off + kHalf));
+  return __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics: Dr = dO . O and lse2 = lse * log2(e); for a row with no
+// visible key (lse = -inf) Dr = 0 and lse2 = +inf.
+// 32 lanes per row, 8 elements each.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+bwd_prep_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout, const float* __restrict__ lse,
+                float* __restrict__ lse2, float* __restrict__ dr, int64_t rows) {
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 5;
+  const int l = threadIdx.x & 31;
+  if (row >= rows) return;   // whole 32-lane groups leave together
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(o + row * BD + l * 8);
+  const bf16x8 b = *reinterpret_cast<const bf16x8*>(dout + row * BD + l * 8);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = fmaf(bf2f(a[i]), bf2f(b[i]), s);
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (l == 0) {
+    const float x = lse[row];
+    const bool none = x == -INFINITY;
+    dr[row] = none ? 0.f : s;     // a key-less row adds nothing, whatever its dO holds
+    lse2[row] = none ? INFINITY : x * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ (query-major).
+// ---------------------------------------------------------------------------
+constexpr int kNWq = 7;                        // compute waves; one more loads
+constexpr int kTokQ = kNWq * 16 / BG;          // query tokens per workgroup (14)
+
+struct DqWave {
+  bf16x8 qf[BD / 32], df[BD / 32];   // B operands: Q and dO of row c, d = 32 ds + 8 g ..
+  f32x4 acc[BD / 16];                 // dQ^T[16 j + 4 g + i][row c]
+  float lse2, dr;
+  uint32_t wq;
+};
+
+// dS^T of one tile from its S^T and dP^T: lane (c, g) holds keys 16 kt + 4 g + i
+// of row c; the result is packed as the B operand of dQ^T += K^T dS^T.
+__device__ __forceinline__ bf16x8 dq_dscores(const Stage<BD>& cst, const DqWave& w, const f32x4 (&s)[2],
+                                             const f32x4 (&dp)[2], int cls, uint32_t forbid, float c2) {
+  const int g = (threadIdx.x & 63) >> 4;
+  bf16x8 ds;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = hw_exp2(fmaf(s[kt][i], c2, -w.lse2));
+      if (cls == PI_TILE_PARTIAL && !pair_visible(w.wq, cst.w[kt * 16 + 4 * g + i], forbid)) p = 0.f;
+      ds[4 * kt + i] = f2bf(p * (dp[kt][i] - w.dr));
+    }
+  return ds;
+}
+
+// S^T = K Q^T and dP^T = V dO^T of one tile (the pipeline's first).
+__device__ __forceinline__ void dq_products(const Stage<BD>& st, const BwdOffsets& lo, const DqWave& w,
+                                            f32x4 (&s)[2], f32x4 (&dp)[2]) {
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) s[kt] = dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < BD / 16; ++j) {
+    s[j & 1] = mfma16x16x32(read_row(st.k, lo.row(j >> 1) + (j & 1) * kHalf), w.qf[j >> 1], s[j & 1]);
+    dp[j & 1] = mfma16x16x32(read_row(st.v, lo.row(j >> 1) + (j & 1) * kHalf), w.df[j >> 1], dp[j & 1]);
+  }
+}
+
+// One dq step's block: dQ^T += K^T dS^T for tile i-1 (K of `pst`, transposing
+// read; its dS^T in dsp), S^T = K Q^T and dP^T = V dO^T for tile i+1 (row-wise
+// reads of `nst`) into s_n / dp_n, in 16 slots with the reads 2 slots ahead;
+// then dS^T of tile i (its mask words in `cst`).
+template <bool PV>
+__device__ __forceinline__ void dq_block(const Stage<BD>& pst, const Stage<BD>& cst, const Stage<BD>& nst,
+                                         const BwdOffsets& lo, DqWave& w, const bf16x8& dsp, const f32x4 (&s)[2],
+                                         const f32x4 (&dp)[2], bf16x8& ds_new, f32x4 (&s_n)[2], f32x4 (&dp_n)[2],
+                                         int cls, uint32_t forbid, float c2) {
+  constexpr int NS = BD / 16, AH = 2;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) s_n[kt] = dp_n[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto rk = [&](int j) { return read_row(nst.k, lo.row(j >> 1) + (j & 1) * kHalf); };
+  auto rv = [&](int j) { return read_row(nst.v, lo.row(j >> 1) + (j & 1) * kHalf); };
+  auto rt = [&](int j) { return read_tr(pst.k, lo.tr(j)); };
+  bf16x8 kb[AH], vb[AH], tb[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    if constexpr (PV) tb[j] = rt(j);
+    kb[j] = rk(j);
+    vb[j] = rv(j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    if constexpr (PV) w.acc[j] = mfma16x16x32(tb[j % AH], dsp, w.acc[j]);
+    s_n[j & 1] = mfma16x16x32(kb[j % AH], w.qf[j >> 1], s_n[j & 1]);
+    dp_n[j & 1] = mfma16x16x32(vb[j % AH], w.df[j >> 1], dp_n[j & 1]);
+    if (j + AH < NS) {
+      if constexpr (PV) tb[j % AH] = rt(j + AH);
+      kb[j % AH] = rk(j + AH);
+      vb[j % AH] = rv(j + AH);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  ds_new = dq_dscores(cst, w, s, dp, cls, forbid, c2);
+}
+
+__device__ __forceinline__ void dq_last(const Stage<BD>& pst, const BwdOffsets& lo, DqWave& w, const bf16x8& dsp) {
+#pragma unroll
+  for (int j = 0; j < BD / 16; ++j) w.acc[j] = mfma16x16x32(read_tr(pst.k, lo.tr(j)), dsp, w.acc[j]);
+}
+
+__device__ __forceinline__ int entry_cls(uint32_t e) { return (int)((e >> 16) & 0xFFu); }
+
+// The dq tile loop: the forward's pipeline (a load wave, four stages, one
+// barrier per tile) with the dq block.  desc(i): tile i's list entry.
+template <typename Desc, typename Issue>
+__device__ __forceinline__ void dq_tiles(Stage<BD> (&stage)[kStagesB], const BwdOffsets& lo, DqWave& w, int n,
+                                         bool loader, Desc desc, Issue issue, uint32_t forbid, float c2) {
+  if (n <= 0) return;
+  if (loader) {
+    issue(desc(0), stage[0]);
+    if (n > 1) issue(desc(1), stage[1]);
+    wait_vmem();
+    __syncthreads();
+    for (int i = 0; i < n; ++i) {
+      const bool more = i + 2 < n;
+      const uint32_t t = desc(more ? i + 2 : i);
+      wait_vmem();          // tile i+1 has landed
+      __syncthreads();      // ... and every wave is done with tile i-2
+      if (more) issue(t, stage[(i + 2) & 3]);
+    }
+    return;
+  }
+  int cls_cur = entry_cls(desc(0)), cls_nxt = n > 1 ? entry_cls(desc(1)) : 0;
+  wait_vmem();          // the Q/dO rows
+  __syncthreads();
+  f32x4 s[2], dp[2];
+  dq_products(stage[0], lo, w, s, dp);
+  bf16x8 dsp;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dsp[e] = f2bf(0.f);
+  auto step = [&](auto pv, int i, Stage<BD>& prev, Stage<BD>& cur, Stage<BD>& nxt) {
+    __syncthreads();
+    bf16x8 ds_new;
+    f32x4 s_n[2], dp_n[2];
+    dq_block<decltype(pv)::value>(prev, cur, nxt, lo, w, dsp, s, dp, ds_new, s_n, dp_n, cls_cur, forbid, c2);
+    cls_cur = cls_nxt;
+    if (i + 2 < n) cls_nxt = entry_cls(desc(i + 2));
+    dsp = ds_new;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = s_n[kt];
+      dp[kt] = dp_n[kt];
+    }
+  };
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
+  step(NoPV{}, 0, stage[3], stage[0], stage[1]);
+  for (int i = 1; i < n; i += 4) {
+    step(WithPV{}, i, stage[0], stage[1], stage[2]);
+    if (i + 1 < n) step(WithPV{}, i + 1, stage[1], stage[2], stage[3]);
+    if (i + 2 < n) step(WithPV{}, i + 2, stage[2], stage[3], stage[0]);
+    if (i + 3 < n) step(WithPV{}, i + 3, stage[3], stage[0], stage[1]);
+  }
+  dq_last(stage[(n - 1) & 3], lo, w, dsp);
+}
+
+// One workgroup per (sample, block of 14 query tokens), XCD-placed per sample.
+__global__ void __launch_bounds__((kNWq + 1) * 64)
+dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+          const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dr,
+          __bf16* __restrict__ dq, int L, float scale, float c2, const uint32_t* __restrict__ tok,
+          const uint8_t* __restrict__ tiles, int n_qt, int n_kt, uint32_t forbid, Placement place) {
+  __shared__ Stage<BD> stage[kStagesB];
+  __shared__ uint32_t kmask[kMaxTiles];
+  __shared__ uint32_t tlist[kMaxTiles];
+  __shared__ int tcount;
+  int b, qblk;
+  if (!xcd_place(place, b, qblk)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const bool loader = wave == kNWq;
+  const int tok0 = qblk * kTokQ;
+  const uint32_t* tk = tok + (size_t)b * L;
+  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, kTokQ, kNWq + 1, kmask, tlist,
+                    &tcount);
+  DqWave w;
+  const int row = wave * 16 + c;
+  const int t = tok0 + row / BG, h = row % BG;
+  const bool ok = !loader && t < L;
+  if (!loader) {
+    // rows past the last token read token 0 and are never stored; a padded
+    // row's Q and dO are replaced by zeros so nothing it holds reaches a product
+    const int64_t r = ((int64_t)b * L + (t < L ? t : 0)) * BG + h;
+    w.wq = t < L ? tk[t] : 0u;
+    const bool live = (w.wq & 1u) != 0u;
+#pragma unroll
+    for (int ds = 0; ds < BD / 32; ++ds) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(q + r * BD + ds * 32 + 8 * g);
+      const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + r * BD + ds * 32 + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w.qf[ds][e] = live ? a[e] : f2bf(0.f);
+        w.df[ds][e] = live ? d[e] : f2bf(0.f);
+      }
+    }
+    w.lse2 = lse2[r];
+    w.dr = dr[r];
+#pragma unroll
+    for (int j = 0; j < BD / 16; ++j) w.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const int count = tcount;
+  const __bf16* k0 = k + (size_t)b * L * BD;
+  const __bf16* v0 = v + (size_t)b * L * BD;
+  const i32x4 rw = make_rsrc(tk);
+  const BwdOffsets lo = bwd_offsets();
+  auto desc = [&](int i) { return tlist[i]; };
+  auto issue = [&](uint32_t e, Stage<BD>& sg) {
+    const int kt = (int)(e & 0xFFFFu), key0 = kt * TK;
+    issue_kv<BD>(sg, kv_lanes<BD>(BD * 2, true), k0, v0, key0, BD * 2, kmask[kt]);
+    const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
+    pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
+  };
+  dq_tiles(stage, lo, w, count, loader, desc, issue, forbid, c2);
+  if (!ok) return;
+  __bf16* dst = dq + (((int64_t)b * L + t) * BG + h) * BD + 4 * g;
+#pragma unroll
+  for (int j = 0; j < BD / 16; ++j) {
+    bf16x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = f2bf(w.acc[j][i] * scale);
+    *reinterpret_cast<bf16x4*>(dst + 16 * j) = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV (key-major).
+// ---------------------------------------------------------------------------
+constexpr int kNWk = 4;                                    // waves, 16 keys each
+constexpr int kKeyBlk = kNWk * 16;                         // keys per workgroup
+constexpr int kMaxQTiles = kMaxTiles * TK / PI_MASK_TILE_Q;
+static_assert(PI_MASK_TILE_Q == 16, "a query tile is four 4-token steps");
+
+// A stage: 32 query rows (4 tokens x 8 heads) of Q (t.k) and dO (t.v), each
+// row's query word (t.w), lse2 and Dr (lanes >= 32 of their loads land as zeros).
+struct DkvStage {
+  Stage<BD> t;
+  alignas(16) float lse2[64];
+  alignas(16) float dr[64];
+};
+
+struct DkvWave {
+  bf16x8 kf[BD / 32], vf[BD / 32];   // B operands: K and V of key c, d = 32 ds + 8 g ..
+  f32x4 dk[BD / 16], dv[BD / 16];     // dK^T, dV^T [16 j + 4 g + i][key c]
+  uint32_t wk;
+};
+
+// P^T and dS^T of one tile: lane (c, g) holds rows 16 h + 4 g + i for key c,
+// packed as the B operands of dV^T += dO^T P^T and dK^T += Q^T dS^T.
+__device__ __forceinline__ void dkv_weights(const DkvStage& cst, const DkvWave& w, const f32x4 (&s)[2],
+                                            const f32x4 (&dp)[2], bf16x8& pf, bf16x8& dsf, int cls,
+                                            uint32_t forbid, float c2) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(&cst.lse2[16 * h + 4 * g]);
+    const f32x4 d2 = *reinterpret_cast<const f32x4*>(&cst.dr[16 * h + 4 * g]);
+    u32x4 wq = {0u, 0u, 0u, 0u};
+    if (cls == PI_TILE_PARTIAL) wq = *reinterpret_cast<const u32x4*>(&cst.t.w[16 * h + 4 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float p = hw_exp2(fmaf(s[h][i], c2, -l2[i]));
+      if (cls == PI_TILE_PARTIAL && !pair_visible(wq[i], w.wk, forbid)) p = 0.f;
+      pf[4 * h + i] = f2bf(p);
+      dsf[4 * h + i] = f2bf(p * (dp[h][i] - d2[i]));
+    }
+  }
+}
+
+// S^T = Q K^T and dP^T = dO V^T of one tile (the pipeline's first).
+__device__ __forceinline__ void dkv_products(const DkvStage& st, const BwdOffsets& lo, const DkvWave& w,
+                                             f32x4 (&s)[2], f32x4 (&dp)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) s[h] = dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < BD / 16; ++j) {
+    s[j & 1] = mfma16x16x32(read_row(st.t.k, lo.row(j >> 1) + (j & 1) * kHalf), w.kf[j >> 1], s[j & 1]);
+    dp[j & 1] = mfma16x16x32(read_row(st.t.v, lo.row(j >> 1) + (j & 1) * kHalf), w.vf[j >> 1], dp[j & 1]);
+  }
+}
+
+// One dK/dV step's block: dV^T += dO^T P^T and dK^T += Q^T dS^T for tile i-1
+// (transposing reads of `pst`), S^T = Q K^T and dP^T = dO V^T for tile i+1
+// (row-wise reads of `nst`), then P^T and dS^T of tile i (statistics in `cst`).
+template <bool PV>
+__device__ __forceinline__ void dkv_block(const DkvStage& pst, const DkvStage& cst, const DkvStage& nst,
+                                          const BwdOffsets& lo, DkvWave& w, const bf16x8& pfp, const bf16x8& dsp,
+                                          const f32x4 (&s)[2], const f32x4 (&dp)[2], bf16x8& pf_new,
+                                          bf16x8& ds_new, f32x4 (&s_n)[2], f32x4 (&dp_n)[2], int cls,
+                                          uint32_t forbid, float c2) {
+  constexpr int NS = BD / 16, AH = 2;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) s_n[h] = dp_n[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto rq = [&](int j) { return read_row(nst.t.k, lo.row(j >> 1) + (j & 1) * kHalf); };
+  auto ro = [&](int j) { return read_row(nst.t.v, lo.row(j >> 1) + (j & 1) * kHalf); };
+  auto tq = [&](int j) { return read_tr(pst.t.k, lo.tr(j)); };
+  auto to = [&](int j) { return read_tr(pst.t.v, lo.tr(j)); };
+  bf16x8 qb[AH], ob[AH], tqb[AH], tob[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    if constexpr (PV) {
+      tob[j] = to(j);
+      tqb[j] = tq(j);
+    }
+    qb[j] = rq(j);
+    ob[j] = ro(j);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    if constexpr (PV) {
+      w.dv[j] = mfma16x16x32(tob[j % AH], pfp, w.dv[j]);
+      w.dk[j] = mfma16x16x32(tqb[j % AH], dsp, w.dk[j]);
+    }
+    s_n[j & 1] = mfma16x16x32(qb[j % AH], w.kf[j >> 1], s_n[j & 1]);
+    dp_n[j & 1] = mfma16x16x32(ob[j % AH], w.vf[j >> 1], dp_n[j & 1]);
+    if (j + AH < NS) {
+      if constexpr (PV) {
+        tob[j % AH] = to(j + AH);
+        tqb[j % AH] = tq(j + AH);
+      }
+      qb[j % AH] = rq(j + AH);
+      ob[j % AH] = ro(j + AH);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  dkv_weights(cst, w, s, dp, pf_new, ds_new, cls, forbid, c2);
+}
+
+__device__ __forceinline__ void dkv_last(const DkvStage& pst, const BwdOffsets& lo, DkvWave& w, const bf16x8& pfp,
+                                         const bf16x8& dsp) {
+#pragma unroll
+  for (int j = 0; j < BD / 16; ++j) {
+    w.dv[j] = mfma16x16x32(read_tr(pst.t.v, lo.tr(j)), pfp, w.dv[j]);
+    w.dk[j] = mfma16x16x32(read_tr(pst.t.k, lo.tr(j)), dsp, w.dk[j]);
+  }
+}
+
+// The dK/dV tile loop: four stages, one barrier per tile; every wave issues its
+// share of tile i+2's loads right after step i's barrier.
+template <typename Desc, typename Issue>
+__device__ __forceinline__ void dkv_tiles(DkvStage (&stage)[kStagesB], const BwdOffsets& lo, DkvWave& w, int n,
+                                          Desc desc, Issue issue, uint32_t forbid, float c2) {
+  if (n <= 0) return;
+  issue(0, stage[0]);
+  if (n > 1) issue(1, stage[1]);
+  int cls_cur = entry_cls(desc(0)), cls_nxt = n > 1 ? entry_cls(desc(1)) : 0;
+  wait_vmem();          // the K/V rows and this wave's share of tiles 0 and 1
+  __syncthreads();
+  f32x4 s[2], dp[2];
+  dkv_products(stage[0], lo, w, s, dp);
+  bf16x8 pfp, dsp;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pfp[e] = dsp[e] = f2bf(0.f);
+  auto step = [&](auto pv, int i, DkvStage& prev, DkvStage& cur, DkvStage& nxt) {
+    wait_vmem();          // this wave's loads of tile i+1
+    __syncthreads();      // everyone's; and every wave is done with tile i-2
+    if (i + 2 < n) issue(i + 2, stage[(i + 2) & 3]);
+    bf16x8 pf_new, ds_new;
+    f32x4 s_n[2], dp_n[2];
+    dkv_block<decltype(pv)::value>(prev, cur, nxt, lo, w, pfp, dsp, s, dp, pf_new, ds_new, s_n, dp_n, cls_cur,
+                                   forbid, c2);
+    cls_cur = cls_nxt;
+    if (i + 2 < n) cls_nxt = entry_cls(desc(i + 2));
+    pfp = pf_new;
+    dsp = ds_new;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = s_n[h];
+      dp[h] = dp_n[h];
+    }
+  };
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
+  step(NoPV{}, 0, stage[3], stage[0], stage[1]);
+  for (int i = 1; i < n; i += 4) {
+    step(WithPV{}, i, stage[0], stage[1], stage[2]);
+    if (i + 1 < n) step(WithPV{}, i + 1, stage[1], stage[2], stage[3]);
+    if (i + 2 < n) step(WithPV{}, i + 2, stage[2], stage[3], stage[0]);
+    if (i + 3 < n) step(WithPV{}, i + 3, stage[3], stage[0], stage[1]);
+  }
+  dkv_last(stage[(n - 1) & 3], lo, w, pfp, dsp);
+}
+
+// One workgroup per (sample, block of 64 keys), XCD-placed per sample.  Up
+// front wave 0 lists the 16-token query tiles with a visible pair for any key
+// of the block (class merged over the block's two key tiles); each listed tile
+// is four steps of 4 tokens.  Rows of padded tokens and rows past the last token
+// load as zeros (their statistics give P = 0, Dr = 0): they add exactly zero.
+__global__ void __launch_bounds__(kNWk * 64)
+dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+            const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dr,
+            __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, float scale, float c2,
+            const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
+            uint32_t forbid, Placement place) {
+  __shared__ DkvStage stage[kStagesB];
+  __shared__ uint32_t qlist[kMaxQTiles];
+  __shared__ uint32_t qvalid[kMaxTiles];
+  __shared__ int qcount;
+  int b, kblk;
+  if (!xcd_place(place, b, kblk)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int key0 = kblk * kKeyBlk;
+  const uint32_t* tk = tok + (size_t)b * L;
+  token_bitmap(tk, L, n_kt, kNWk, qvalid);
+  if (wave == 0) {
+    const uint8_t* trow = tiles + (size_t)b * n_qt * n_kt;
+    const int kt_lo = key0 / TK, kt_hi = min(n_kt, (key0 + kKeyBlk + TK - 1) / TK);
+    int cnt = 0;
+    for (int base = 0; base < n_qt; base += 64) {
+      const int qt = base + lane;
+      int cls = 0;
+      if (qt < n_qt) {
+        cls = -1;
+        for (int kt = kt_lo; kt < kt_hi; ++kt) {
+          const int cl = trow[(size_t)qt * n_kt + kt];
+          cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
+        }
+      }
+      const unsigned long long bal = __ballot(cls > 0);
+      if (cls > 0) qlist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)qt | ((uint32_t)cls << 16);
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) qcount = cnt;
+  }
+  DkvWave w;
+  const int key = key0 + wave * 16 + c;
+  const bool ok = key < L;
+  {
+    // keys past the end read key 0 and are never stored; a padded key's K and V
+    // are replaced by zeros so nothing it holds reaches a product
+    const int64_t r = (int64_t)b * L + (ok ? key : 0);
+    w.wk = ok ? tk[key] : 0u;
+    const bool live = (w.wk & 1u) != 0u;
+#pragma unroll
+    for (int ds = 0; ds < BD / 32; ++ds) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(k + r * BD + ds * 32 + 8 * g);
+      const bf16x8 d = *reinterpret_cast<const bf16x8*>(v + r * BD + ds * 32 + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w.kf[ds][e] = live ? a[e] : f2bf(0.f);
+        w.vf[ds][e] = live ? d[e] : f2bf(0.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BD / 16; ++j) w.dk[j] = w.dv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  const int n = 4 * qcount;
+  // this wave's loads: rows 8 wave .. 8 wave + 7 of the tile (the 8 heads of its
+  // token), two rows per instruction, source chunks pre-swizzled with f_U
+  uint32_t roff[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int r = 8 * wave + 2 * jj + (lane >> 5), p = lane & 31;
+    roff[jj] = (uint32_t)r * (BD * 2u) + 16u * (uint32_t)(p ^ T256::fu(r));
+  }
+  const float* lse2_b = lse2 + (size_t)b * L * BG;
+  const float* dr_b = dr + (size_t)b * L * BG;
+  const __bf16* q_b = q + (size_t)b * L * BG * BD;
+  const __bf16* o_b = dout + (size_t)b * L * BG * BD;
+  auto desc = [&](int i) { return qlist[i >> 2]; };
+  auto issue = [&](int i, DkvStage& sg) {
+    const int t0 = (int)(qlist[i >> 2] & 0xFFFFu) * PI_MASK_TILE_Q + (i & 3) * 4;   // first token
+    const int tw = t0 + wave;                                                         // this wave's token
+    const bool in = (qvalid[tw >> 5] >> (tw & 31)) & 1u;   // in range and valid, else zeros
+    const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(t0) * BG * BD * 2;
+    const i32x4 rq = make_rsrc(reinterpret_cast<const char*>(q_b) + at);
+    const i32x4 ro = make_rsrc(reinterpret_cast<const char*>(o_b) + at);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t off = in ? roff[jj] : kOOB;
+      pi_buffer_load_lds(rq, lds_u32(&sg.t.k[(8 * wave + 2 * jj) * BD]), 16, (int)off, 0, 0, 0);
+      pi_buffer_load_lds(ro, lds_u32(&sg.t.v[(8 * wave + 2 * jj) * BD]), 16, (int)off, 0, 0, 0);
+    }
+    // statistics of the 32 rows: wave 0 the query words, 1 lse2, 2 Dr
+    const bool row_in = lane < 32 && t0 + (lane >> 3) < L;
+    if (wave == 0) {
+      const uint32_t off = row_in ? (uint32_t)(t0 + (lane >> 3)) * 4u : kOOB;
+      pi_buffer_load_lds(make_rsrc(tk), lds_u32(&sg.t.w[0]), 4, (int)off, 0, 0, 0);
+    } else if (wave == 1) {
+      const uint32_t off = row_in ? (uint32_t)(t0 * BG + lane) * 4u : kOOB;
+      pi_buffer_load_lds(make_rsrc(lse2_b), lds_u32(&sg.lse2[0]), 4, (int)off, 0, 0, 0);
+    } else if (wave == 2) {
+      const uint32_t off = row_in ? (uint32_t)(t0 * BG + lane) * 4u : kOOB;
+      pi_buffer_load_lds(make_rsrc(dr_b), lds_u32(&sg.dr[0]), 4, (int)off, 0, 0, 0);
+    }
+  };
+  const BwdOffsets lo = bwd_offsets();
+  dkv_tiles(stage, lo, w, n, desc, issue, forbid, c2);
+  if (!ok) return;
+  const int64_t r = ((int64_t)b * L + key) * BD + 4 * g;
+#pragma unroll
+  for (int j = 0; j < BD / 16; ++j) {
+    bf16x4 xk, xv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xk[i] = f2bf(w.dk[j][i] * scale);
+      xv[i] = f2bf(w.dv[j][i]);
+    }
+    *reinterpret_cast<bf16x4*>(dk + r + 16 * j) = xk;
+    *reinterpret_cast<bf16x4*>(dv + r + 16 * j) = xv;
+  }
+}
+
+size_t stats_bytes(int B, int L) { return pi::align_up((size_t)B * L * BG * sizeof(float), 256); }
+
+}  // namespace
+
+extern "C" size_t pi_attn_backward_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
+  if (B < 1 || L < 1 || Hq != BG || Hkv != 1 || d != BD) return 0;
+  return 2 * stats_bytes(B, L);
+}
+
+extern "C" pi_status pi_joint_attn_backward(const void* q, const void* k, const void* v, const void* o,
+                                            const void* dout, const float* lse, int B, int L, int Hq, int Hkv,
+                                            int d, float scale, const pi_mask* mask, void* dq, void* dk, void* dv,
+                                            void* workspace, size_t workspace_bytes, pi_stream stream) {
+  PI_REQUIRE(q && k && v && o && dout && lse && mask && dq && dk && dv, PI_ERR_INVALID_ARG,
+             "pi_joint_attn_backward: null pointer");
+  PI_REQUIRE(pi::aligned16(q) && pi::aligned16(k) && pi::aligned16(v) && pi::aligned16(o) && pi::aligned16(dout) &&
+                 pi::aligned16(dq) && pi::aligned16(dk) && pi::aligned16(dv) &&
+                 (reinterpret_cast<uintptr_t>(lse) & 3u) == 0,
+             PI_ERR_INVALID_ARG, "pi_joint_attn_backward: tensors must be 16-byte aligned (lse 4-byte)");
+  PI_REQUIRE(B >= 1 && L >= 1, PI_ERR_INVALID_ARG, "pi_joint_attn_backward: B=%d L=%d", B, L);
+  PI_REQUIRE(mask->B == B && mask->N == L && mask->tok && mask->tiles, PI_ERR_INVALID_ARG,
+             "pi_joint_attn_backward: mask built for B=%d N=%d, call has B=%d L=%d", mask->B, mask->N, B, L);
+  PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_attn_backward: scale must be > 0");
+  PI_REQUIRE(Hq == BG && Hkv == 1 && d == BD, PI_ERR_UNSUPPORTED,
+             "pi_joint_attn_backward: unsupported (Hq=%d, Hkv=%d, d=%d); supported: (8,1,256)", Hq, Hkv, d);
+  PI_REQUIRE(L <= kMaxTiles * TK, PI_ERR_UNSUPPORTED, "pi_joint_attn_backward: L=%d exceeds %d tokens", L,
+             kMaxTiles * TK);
+  const size_t need = pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d);
+  PI_REQUIRE(workspace != nullptr && workspace_bytes >= need, PI_ERR_WORKSPACE,
+             "pi_joint_attn_backward: needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "pi_joint_attn_backward: workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* lse2 = static_cast<float*>(workspace);
+  float* dr = reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes(B, L));
+  const int64_t rows = (int64_t)B * L * BG;
+  const float c2 = scale * kLog2e;
+  bwd_prep_kernel<<<(unsigned)((rows * 32 + 255) / 256), 256, 0, s>>>(
+      static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, lse2, dr, rows);
+  pi_status st = pi::check_launch("bwd_prep_kernel");
+  if (st != PI_OK) return st;
+  const Placement pk = make_placement(B, (L + kKeyBlk - 1) / kKeyBlk);
+  dkdv_kernel<<<(unsigned)placement_grid(pk), kNWk * 64, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(dout), lse2, dr, static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), L, scale, c2,
+      mask->tok, mask->tiles, mask->n_qt, mask->n_kt, mask->forbid_bits, pk);
+  st = pi::check_launch("dkdv_kernel");
+  if (st != PI_OK) return st;
+  const Placement pq = make_placement(B, (L + kTokQ - 1) / kTokQ);
+  dq_kernel<<<(unsigned)placement_grid(pq), (kNWq + 1) * 64, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(dout), lse2, dr, static_cast<__bf16*>(dq), L, scale, c2, mask->tok, mask->tiles,
+      mask->n_qt, mask->n_kt, mask->forbid_bits, pq);
+  return pi::check_launch("dq_kernel");
+}

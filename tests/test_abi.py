@@ -66,7 +66,7 @@ def test_prefill_rejects_bad_arguments_before_launch():
     m = Bd.PiMask(B=1, N=64, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
     call = lambda **kw: lib.pi_joint_attn_prefill(
         kw.get("q", FAKE), FAKE, FAKE, kw.get("B", 1), kw.get("L", 64), kw.get("Hq", 8), kw.get("Hkv", 1),
-        kw.get("d", 256), kw.get("scale", 0.0625), kw.get("rope", 0.0), ctypes.byref(m), FAKE, None, 0,
+        kw.get("d", 256), kw.get("scale", 0.0625), kw.get("rope", 0.0), ctypes.byref(m), FAKE, None, None, 0,
         kw.get("ws", None), kw.get("ws_bytes", 0), None)
     assert call(d=128) == -2                 # unsupported head dim
     assert call(Hq=6, Hkv=4) == -1           # Hq not a multiple of Hkv
@@ -86,7 +86,30 @@ def test_prefill_rejects_bad_arguments_before_launch():
     assert lib.pi_prefill_workspace_bytes(1, 816, 8, 2, 256) == 0          # unsupported heads
     m816 = Bd.PiMask(B=1, N=816, n_qt=51, n_kt=26, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
     assert lib.pi_joint_attn_prefill(FAKE, FAKE, FAKE, 1, 816, 8, 1, 256, 0.0625, 0.0, ctypes.byref(m816), FAKE,
-                                     None, 0, P(0x100010), need, None) == -1   # misaligned workspace
+                                     None, None, 0, P(0x100010), need, None) == -1   # misaligned workspace
+
+
+@needs_lib
+def test_backward_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    m = Bd.PiMask(B=2, N=64, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
+    need = lib.pi_attn_backward_workspace_bytes(2, 64, 8, 1, 256)
+    assert need == 2 * (2 * 64 * 8 * 4)     # lse2 and Dr, fp32 per row of 2*64*8 rows
+    assert lib.pi_attn_backward_workspace_bytes(2, 64, 24, 24, 64) == 0     # unsupported heads
+    call = lambda **kw: lib.pi_joint_attn_backward(
+        kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("lse", FAKE), kw.get("B", 2), kw.get("L", 64),
+        kw.get("Hq", 8), kw.get("Hkv", 1), kw.get("d", 256), kw.get("scale", 0.0625), ctypes.byref(m),
+        kw.get("dq", FAKE), FAKE, FAKE, kw.get("ws", P(0x100000)), kw.get("ws_bytes", need), None)
+    assert call(d=64, Hq=1) == -2            # unsupported heads
+    assert call(L=65) == -1                  # mask built for another length
+    assert call(scale=0.0) == -1
+    assert call(q=P(0x10008)) == -1          # misaligned
+    assert call(lse=P(0x10002)) == -1        # misaligned lse
+    assert call(dq=None) == -1
+    assert call(ws=None) == -3
+    assert call(ws_bytes=need - 1) == -3
+    assert call(ws=P(0x100010)) == -1        # misaligned workspace
+    assert b"pi_joint_attn_backward" in lib.pi_last_error()
 
 
 @needs_lib
