@@ -13,6 +13,7 @@ Besides the step, the two kernels the metric names are measured live with HIP
 events on the stream they run on:
     prefill at the π0.5 training shape (B=32, L=962, three blocks) -> MFMA fraction
     cached decode at the serving shape (B=64, 816 slots)           -> HBM GB/s
+plus the rotary embedding, single-token decode and attention backward legs,
 and the fp64 oracle is timed on the host's cores over a bounded sample.
 Prints ONE JSON line.
 """
@@ -39,7 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar"], default=None,
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward"],
+                   default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
 
@@ -158,6 +160,35 @@ def prefill_kernel_leg(cx: Ctx, iters: int, workload: str):
         "allowed_pairs": pairs, "gflop_per_launch": flops / 1e9, "us_per_launch": ms * 1e3,
         "achieved_tflops": tflops, "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
         "algorithmic_bytes": byts, "kernel": "prefill_kernel",
+    }
+
+
+def backward_leg(cx: Ctx, iters: int):
+    """Backward of the joint attention at the π0.5 training shape (B=32, L=962,
+    three blocks): one pi_joint_attn_backward call (row statistics, dK/dV, dQ)
+    for a unit-variance upstream gradient, after a forward that keeps the rows'
+    log-sum-exp.  Algorithmic FLOPs: five products of 2 d flops per allowed
+    (query, key) pair and query head (Q K^T, dO V^T, dV, dK, dQ)."""
+    torch, Bd, I = cx.torch, cx.Bd, cx.I
+    w = I.WORKLOADS["pi05_three_block_prefill"]()
+    s = w.structure
+    q, k, v = (cx.bf(t) for t in w.qkv())
+    u = cx.bf(I.bf16_normal(w.seed_base + 21, (w.B, w.N, w.Hq, w.d)))
+    valid = cx.u8(w.input_mask())
+    m = Bd.pi_mask_build(valid, cx.u8(s.ar), cx.u8(s.seg), I.forbid_bits(s.forbid))
+    pairs = int(Bd.pi_mask_materialize(m).sum(dtype=torch.int64).item())
+    lse = torch.empty((w.B, w.N, w.Hq), dtype=torch.float32, device=cx.dev)
+    o = Bd.pi_joint_attn_prefill(q, k, v, m, lse=lse)
+    ws = Bd.backward_workspace(w.B, w.N, w.Hq, w.Hkv, w.d, cx.dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ms = cx.time_ms(lambda: Bd.pi_joint_attn_backward(q, k, v, o, u, lse, m, ws, dq=dq, dk=dk, dv=dv), iters)
+    ms_fwd = cx.time_ms(lambda: Bd.pi_joint_attn_prefill(q, k, v, m, o=o, lse=lse), iters)
+    flops = 10.0 * w.d * w.Hq * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "B": w.B, "L": w.N, "allowed_pairs": pairs, "gflop_per_launch": flops / 1e9,
+        "us_per_launch": ms * 1e3, "achieved_tflops": tflops, "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
+        "forward_with_lse_us": ms_fwd * 1e3, "kernel": "bwd_prep_kernel + dkdv_kernel + dq_kernel",
     }
 
 
@@ -300,8 +331,9 @@ def copy_kernel_leg(cx: Ctx, iters: int):
 
 # HBM bytes per launch from the committed counter summaries; a summary only counts
 # while the kernel sources it was taken from are unchanged.
-KERNEL_SOURCES = {"decode_kernel": ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/common.h"],
-                  "prefill_kernel": ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/common.h"]}
+_ENGINE = ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/common.h",
+           "prefix_lm_joint_amd/csrc/engine.h"]
+KERNEL_SOURCES = {"decode_kernel": _ENGINE, "prefill_kernel": _ENGINE}
 
 
 def source_digest(kernel):
@@ -425,6 +457,10 @@ def main():
         log("rotary embedding leg (pi05 B=32 L=962)")
         kernels["rope"] = rope_leg(cx, args.kernel_iters)
         log(str(kernels["rope"]))
+    if args.only in (None, "backward"):
+        log("attention backward leg (pi05 B=32 L=962)")
+        kernels["backward"] = backward_leg(cx, max(5, args.kernel_iters // 5))
+        log(str(kernels["backward"]))
     if args.only is not None:
         print(json.dumps({"only": args.only, **result, "kernels": kernels}))
         return
@@ -470,6 +506,12 @@ def main():
                  "us_per_launch": kernels["rope"]["rope_q"]["us_per_launch"],
                  "k_us_per_launch": kernels["rope"]["rope_k"]["us_per_launch"],
                  "prefill_us": kernels["rope"]["prefill_us"], "prefill_rope_us": kernels["rope"]["prefill_rope_us"]},
+        "backward": {"kernel": kernels["backward"]["kernel"] + " (pi05 B=32 L=962)", "bound": "mfma",
+                     "achieved": kernels["backward"]["achieved_tflops"], "peak": PEAK_BF16_FLOPS / 1e12,
+                     "unit": "TFLOP/s", "frac": kernels["backward"]["mfma_frac"],
+                     "us_per_launch": kernels["backward"]["us_per_launch"],
+                     "gflop_per_launch": kernels["backward"]["gflop_per_launch"],
+                     "forward_with_lse_us": kernels["backward"]["forward_with_lse_us"]},
         "breakdown_us": result["breakdown_us"],
         "cpu_baseline": cpu,
     }
