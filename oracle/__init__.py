@@ -26,6 +26,12 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
   rope.rope / rope.joint_attention_rope
       the rotary position embedding of Q and K at the mask's positions
       ("VLA 代码精读" §3.2, §1.5, §1.6; the formula is a reading).
+  layer.joint_layer
+      one π0.5 joint transformer layer around the joint attention: per-stream
+      norm (plain RMS for the prefix, adaptive RMS for the expert), fused QKV,
+      concatenated KV pool, one masked softmax, split, output projection and
+      FFN per stream ("π0.5 vs MM-DiT joint attention", first section; "VLA
+      代码精读" §1.4, §2.7; the norm, FFN and rounding details are readings).
   flow.velocity_net
       the random-weight stand-in velocity network.  The pages give no weights
       or exact layer for it: **parity unpinned** as a whole (only its pieces
@@ -33,4 +39,4 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
 
 Readings of points the pages leave open are listed in each docstring.
 """
-from . import bf16, mask, attention, attention_bwd, flow, rope  # noqa: F401
+from . import bf16, mask, attention, attention_bwd, flow, layer, rope  # noqa: F401

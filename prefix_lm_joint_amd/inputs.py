@@ -240,3 +240,26 @@ def net_weights(seed: int, width: int = 1024, action_dim: int = 32, Hq: int = 8,
         w_out=bf16_normal(seed + 10, (A, W), W ** -0.5),
         b_out=f32_normal(seed + 11, (A,), bias_std),
     )
+
+
+def layer_weights(seed: int, width: int, adaptive: bool, Hq: int = 8, Hkv: int = 1, d: int = 256,
+                  ffn_mult: int = 4) -> dict:
+    """Random weights of one stream of a joint transformer layer: fused QKV
+    [Hq*d + 2*Hkv*d, W], output projection [W, Hq*d], FFN up [ffn_mult*W, W] and
+    down [W, ffn_mult*W] (bf16 bits, N(0, 1/fan_in)); per-channel norm scales
+    norm1 / norm2 (fp32, N(1, 0.1^2)) for a plain-norm stream, or modulation
+    matrices mod1 / mod2 [2W, W] (bf16 bits, N(0, 0.25/W)) for an adaptive one."""
+    W, F = width, ffn_mult * width
+    w = {
+        "w_qkv": bf16_normal(seed + 1, ((Hq + 2 * Hkv) * d, W), W ** -0.5),
+        "w_o": bf16_normal(seed + 2, (W, Hq * d), (Hq * d) ** -0.5),
+        "w_up": bf16_normal(seed + 3, (F, W), W ** -0.5),
+        "w_down": bf16_normal(seed + 4, (W, F), F ** -0.5),
+    }
+    if adaptive:
+        w["mod1"] = bf16_normal(seed + 5, (2 * W, W), 0.5 * W ** -0.5)
+        w["mod2"] = bf16_normal(seed + 6, (2 * W, W), 0.5 * W ** -0.5)
+    else:
+        w["norm1"] = (np.float32(1.0) + f32_normal(seed + 5, (W,), 0.1)).astype(np.float32)
+        w["norm2"] = (np.float32(1.0) + f32_normal(seed + 6, (W,), 0.1)).astype(np.float32)
+    return w
