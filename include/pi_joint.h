@@ -164,6 +164,49 @@ pi_status pi_joint_attn_backward(const void* q, const void* k, const void* v, co
                                  void* workspace, size_t workspace_bytes, pi_stream stream);
 
 /*
+ * One π0.5 joint transformer layer around the joint attention ([P3] first
+ * section: each stream has its own norm, QKV projection, output projection and
+ * FFN, the streams share one concatenated KV pool and one softmax; [P1] §1.4:
+ * the π0.5 action expert normalises with an adaptive RMS norm conditioned on the
+ * flow time, §2.7 the adaptive norm's shift / scale form).  Per stream, with
+ * n(h) = h / sqrt(mean(h^2) + 1e-6) over the width and r() rounding to bf16:
+ *   a = r(n(h) * norm1)  or  r(n(h) * (1 + scale1) + shift1),  [shift1 | scale1] = r(silu(cond)) mod1^T
+ *   q | k | v = r(a w_qkv^T)            (8 query heads, 1 KV head, d = 256)
+ *   o = r(joint attention over the concatenated [prefix | expert] tokens under mask)
+ *   h += o[stream rows] w_o^T
+ *   b = r(n(h) * norm2)  or  the adaptive form with mod2
+ *   h += r(gelu(b w_up^T)) w_down^T     (gelu(x) = x Phi(x))
+ * The norm, FFN and rounding details are readings of the pages.
+ *   h_p fp32 [B, Np, prefix->width], h_e fp32 [B, Ne, expert->width], updated in place
+ *   cond fp32 [B, width of the adaptive stream] (NULL if neither stream is adaptive)
+ *   mask built for B and N = Np + Ne, the prefix stream's tokens first
+ * Weights (device, bf16 row-major, out x in): w_qkv [2560, W], w_o [W, 2048],
+ * w_up [ffn, W], w_down [W, ffn]; norm1 / norm2 fp32 [W] for a plain norm, or
+ * mod1 / mod2 bf16 [2W, W] for an adaptive one (exactly one of the two pairs;
+ * at most one adaptive stream).  W and ffn multiples of 256, W <= 4096.  Every
+ * product runs on the matrix cores with fp32 accumulation.
+ * workspace (device, 256-byte aligned, required): pi_joint_layer_workspace_bytes
+ * (0 = unsupported streams).  Calls sharing a workspace must not overlap.
+ */
+typedef struct pi_layer_stream {
+  int32_t width, ffn;
+  const void* w_qkv;
+  const void* w_o;
+  const void* w_up;
+  const void* w_down;
+  const float* norm1;
+  const float* norm2;
+  const void* mod1;
+  const void* mod2;
+} pi_layer_stream;
+size_t pi_joint_layer_workspace_bytes(const pi_layer_stream* prefix, const pi_layer_stream* expert, int B,
+                                      int Np, int Ne);
+pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const pi_layer_stream* expert, float* h_p,
+                                 float* h_e, const float* cond, int B, int Np, int Ne, float scale,
+                                 const pi_mask* mask, void* workspace, size_t workspace_bytes,
+                                 pi_stream stream);
+
+/*
  * Per-layer prefix KV cache ([P1] §1.6; [P4] §4.1).  Device memory owned by the caller.
  *   k, v         bf16 [layers, B, capacity, Hkv, d]
  *   prefix_mask  uint8 [B, capacity]: nonzero = slot holds a valid prefix token

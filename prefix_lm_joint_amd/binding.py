@@ -44,6 +44,11 @@ class PiVelocityNet(ctypes.Structure):
                 ("w_q", _c_p), ("w_k", _c_p), ("w_v", _c_p), ("w_o", _c_p), ("w_out", _c_p), ("b_out", _c_p)]
 
 
+class PiLayerStream(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("ffn", ctypes.c_int32), ("w_qkv", _c_p), ("w_o", _c_p), ("w_up", _c_p),
+                ("w_down", _c_p), ("norm1", _c_p), ("norm2", _c_p), ("mod1", _c_p), ("mod2", _c_p)]
+
+
 _SIGS = {
     "pi_mask_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i]),
     "pi_mask_build": (_c_i, [_c_p, _c_p, _c_p, ctypes.c_uint32, _c_i, _c_i, _c_p, ctypes.c_size_t,
@@ -56,6 +61,10 @@ _SIGS = {
     "pi_attn_backward_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i]),
     "pi_joint_attn_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f,
                                       ctypes.POINTER(PiMask), _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_joint_layer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiLayerStream),
+                                                         _c_i, _c_i, _c_i]),
+    "pi_joint_layer_forward": (_c_i, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiLayerStream), _c_p, _c_p, _c_p,
+                                      _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask), _c_p, ctypes.c_size_t, _c_p]),
     "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
                                      _c_f, _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
@@ -285,6 +294,46 @@ def pi_joint_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o:
         _ptr(dk, torch.bfloat16, "dk"), _ptr(dv, torch.bfloat16, "dv"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream)))
     return dq, dk, dv
+
+
+class LayerStream:
+    """Device weights of one stream of a joint layer (keeps the tensors alive)."""
+
+    def __init__(self, w_qkv, w_o, w_up, w_down, norm1=None, norm2=None, mod1=None, mod2=None):
+        self.tensors = dict(w_qkv=w_qkv, w_o=w_o, w_up=w_up, w_down=w_down, norm1=norm1, norm2=norm2, mod1=mod1,
+                            mod2=mod2)
+        bf = lambda t, n: _ptr(t, torch.bfloat16, n) if t is not None else None
+        f32 = lambda t, n: _ptr(t, torch.float32, n) if t is not None else None
+        self.struct = PiLayerStream(int(w_qkv.shape[1]), int(w_up.shape[0]), bf(w_qkv, "w_qkv"), bf(w_o, "w_o"),
+                                    bf(w_up, "w_up"), bf(w_down, "w_down"), f32(norm1, "norm1"), f32(norm2, "norm2"),
+                                    bf(mod1, "mod1"), bf(mod2, "mod2"))
+
+
+def pi_joint_layer_workspace_bytes(prefix: LayerStream, expert: LayerStream, B: int, Np: int, Ne: int) -> int:
+    return int(lib().pi_joint_layer_workspace_bytes(ctypes.byref(prefix.struct), ctypes.byref(expert.struct), B, Np,
+                                                    Ne))
+
+
+def layer_workspace(prefix: LayerStream, expert: LayerStream, B: int, Np: int, Ne: int, device) -> torch.Tensor:
+    n = pi_joint_layer_workspace_bytes(prefix, expert, B, Np, Ne)
+    if n == 0:
+        raise ValueError("pi_joint_layer_forward does not support these streams")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pi_joint_layer_forward(prefix: LayerStream, expert: LayerStream, h_p: torch.Tensor, h_e: torch.Tensor,
+                           cond: Optional[torch.Tensor], mask: Mask, workspace: torch.Tensor,
+                           scale: Optional[float] = None, stream=None) -> None:
+    """One joint layer; updates h_p [B, Np, Wp] and h_e [B, Ne, We] (fp32) in place."""
+    B, Np = h_p.shape[:2]
+    Ne = h_e.shape[1]
+    if scale is None:
+        scale = 256 ** -0.5
+    _check("pi_joint_layer_forward", lib().pi_joint_layer_forward(
+        ctypes.byref(prefix.struct), ctypes.byref(expert.struct), _ptr(h_p, torch.float32, "h_p"),
+        _ptr(h_e, torch.float32, "h_e"), _ptr(cond, torch.float32, "cond") if cond is not None else None, B, Np, Ne,
+        scale, ctypes.byref(mask.struct), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))
 
 
 def pi_decode_workspace_bytes(B: int, S: int, Hq: int, length: int) -> int:

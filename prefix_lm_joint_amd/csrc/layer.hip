@@ -1,0 +1,404 @@
+// One π0.5 joint transformer layer around the joint attention, gfx950.
+//
+// What is computed ("π0.5 vs MM-DiT joint attention", first section; "VLA 代码精读
+// — OpenPI & StarVLA" §1.4, §2.7): two streams, the prefix (VLM) stream and the
+// action expert, each with its own norm, fused QKV projection, output projection
+// and FFN; their Q/K/V are concatenated along the tokens into one pool, one
+// masked softmax runs over it (pi_joint_attn_prefill), and the output is split
+// back.  Per stream, with n(h) = h / sqrt(mean(h^2) + 1e-6):
+//   a = r(n(h) * gamma1)                      plain stream
+//   a = r(n(h) * (1 + scale1) + shift1)        adaptive stream, [shift1 | scale1] = r(silu(c)) W_mod1^T
+//   q | k | v = r(a W_qkv^T);  o = r(attention);  h += o W_o^T
+//   b = the second norm of h (gamma2 or mod2);  h += r(gelu(b W_up^T)) W_down^T
+// r() rounds to bf16 (the matrix cores take bf16 operands); h stays fp32.
+//
+// Kernels:
+//   * gemm_nt_kernel: C = A W^T for row-major bf16 A [M, K] and W [N, K] with fp32
+//     accumulation, on the matrix cores.  A workgroup owns a 256 (N) x 128 (M)
+//     tile with 8 waves of 64 x 64; K advances 32 at a time through four LDS
+//     stages filled by direct-to-LDS buffer loads.  Each load instruction
+//     fetches one 16 x 32 operand fragment (16 rows x 64 bytes) and lands it in
+//     the exact image the fragment read expects (lane L's 16 bytes at 16 L), so
+//     every LDS read is 1 KB contiguous per wave, free of bank conflicts, and
+//     every fragment read feeds four products.  Products are computed
+//     transposed (A operand = W rows, B operand = A rows) so a lane ends with
+//     four consecutive output columns of one row for the epilogue: bf16 store,
+//     gelu, residual add into fp32, fp32 store, or the QKV scatter into the
+//     joint pool.  A rows can be read through a row map (the joint pool's rows
+//     of one stream).
+//   * norm_kernel: one wave per row, the RMS norm with the per-channel scale or
+//     the per-sample modulation, bf16 output.
+//   * silu_kernel: the conditioning's silu, bf16.
+#include "common.h"
+#include "engine.h"
+
+#include <math.h>
+
+namespace {
+
+using namespace pi_engine;
+
+constexpr int GN = 256, GM = 128, GK = 32;      // workgroup tile (N x M) and k step
+constexpr int GW = 8;                           // waves
+constexpr int GSTAGES = 4;
+constexpr int kFragBytes = 1024;                // one 16 x 32 bf16 operand fragment
+constexpr int kWFrags = GN / 16, kAFrags = GM / 16;
+constexpr int kStageBytes = (kWFrags + kAFrags) * kFragBytes;   // 24 KB
+
+enum { E_BF16 = 0, E_GELU = 1, E_RESID = 2, E_F32 = 3, E_QKV = 4 };
+
+// Row map of the A operand: row m of the product reads row (m / T) * S + off + m % T
+// of the A buffer (T = M, S = 0, off = 0 for a plain matrix).
+struct RowMap {
+  int T, S, off;
+  __host__ __device__ int64_t operator()(int64_t m) const { return (m / T) * S + off + m % T; }
+};
+
+struct GemmParams {
+  const __bf16* a;     // [rows, K]
+  const __bf16* w;     // [N, K]
+  int M, N, K;
+  RowMap amap;
+  void* out;           // E_BF16 / E_GELU: bf16 [M, N]; E_RESID: fp32 [M, N] (+=); E_F32: fp32 [M, N]
+  // E_QKV: q [B, Ntot, nq], k / v [B, Ntot, nkv]; stream row m = (b, t) goes to joint row b*Ntot + tok_off + t
+  __bf16 *q, *k, *v;
+  int nq, nkv, T, Ntot, tok_off;
+  int n_mt, n_nt;      // tile counts
+};
+
+__device__ __forceinline__ float gelu_exact(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
+
+template <int EPI>
+__device__ __forceinline__ void gemm_store(const GemmParams& p, int64_t m, int n, const f32x4& acc) {
+  if constexpr (EPI == E_RESID) {
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + m * p.N + n);
+    *dst = *dst + acc;
+  } else if constexpr (EPI == E_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + m * p.N + n) = acc;
+  } else {
+    bf16x4 x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = f2bf(EPI == E_GELU ? gelu_exact(acc[i]) : acc[i]);
+    __bf16* dst;
+    if constexpr (EPI == E_QKV) {
+      const int64_t row = (m / p.T) * p.Ntot + p.tok_off + m % p.T;
+      if (n < p.nq) dst = p.q + row * p.nq + n;
+      else if (n < p.nq + p.nkv) dst = p.k + row * p.nkv + (n - p.nq);
+      else dst = p.v + row * p.nkv + (n - p.nq - p.nkv);
+    } else {
+      dst = static_cast<__bf16*>(p.out) + m * p.N + n;
+    }
+    *reinterpret_cast<bf16x4*>(dst) = x;
+  }
+}
+
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  // vmcnt <= n (n in {0, 3, 6}); expcnt and lgkmcnt left at their maxima
+  if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
+  else if (n >= 3) __builtin_amdgcn_s_waitcnt(0x0F73);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(GW * 64) gemm_nt_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[GSTAGES * kStageBytes];
+  // XCD-aware tile order: the workgroups of one XCD take a contiguous run of
+  // (m tile, n tile) pairs, n fastest, so they share the A rows in that L2
+  const int total = p.n_mt * p.n_nt;
+  const int chunk = (total + 7) / 8;
+  const int lin = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= chunk || lin >= total) return;
+  const int mt = lin / p.n_nt, nt = lin % p.n_nt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int wn = wave & 3, wm = wave >> 2;
+  const int nk = p.K / GK;
+  // this wave's loads: W fragments 2 wave, 2 wave + 1 and A fragment wave
+  const i32x4 rw = make_rsrc(p.w + (int64_t)nt * GN * p.K);
+  const i32x4 ra = make_rsrc(p.a);
+  const uint32_t kb = (uint32_t)p.K * 2u;
+  uint32_t ow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ow[j] = (uint32_t)((2 * wave + j) * 16 + c) * kb + 16u * (uint32_t)g;
+  const int64_t am = (int64_t)mt * GM + wave * 16 + c;
+  const uint32_t oa = am < p.M ? (uint32_t)(p.amap(am) * p.K * 2 + 16 * g) : kOOB;
+  auto issue = [&](int i) {
+    char* st = smem + (i & 3) * kStageBytes;
+    const int so = __builtin_amdgcn_readfirstlane(i * GK * 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pi_buffer_load_lds(rw, lds_u32(st + (2 * wave + j) * kFragBytes), 16, (int)ow[j], so, 0, 0);
+    pi_buffer_load_lds(ra, lds_u32(st + kWFrags * kFragBytes + wave * kFragBytes), 16, (int)oa, so, 0, 0);
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  for (int i = 0; i < nk; ++i) {
+    wait_vmem_le(3 * min(nk - 1 - i, 2));   // this wave's loads of step i have landed
+    __syncthreads();                         // everyone's; and every wave is done with step i - 1
+    if (i + 3 < nk) issue(i + 3);            // into the stage of step i - 1
+    const char* st = smem + (i & 3) * kStageBytes;
+    bf16x8 wf[4], af[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wf[j] = *reinterpret_cast<const bf16x8*>(st + (4 * wn + j) * kFragBytes + lane * 16);
+      af[j] = *reinterpret_cast<const bf16x8*>(st + kWFrags * kFragBytes + (4 * wm + j) * kFragBytes + lane * 16);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = mfma16x16x32(wf[a], af[b], acc[a][b]);
+  }
+  // acc[a][b][i] = C[m = mt*128 + 64 wm + 16 b + c][n = nt*256 + 64 wn + 16 a + 4 g + i]
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t m = (int64_t)mt * GM + 64 * wm + 16 * b + c;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) gemm_store<EPI>(p, m, nt * GN + 64 * wn + 16 * a + 4 * g, acc[a][b]);
+  }
+}
+
+// RMS norm of one fp32 row of width W (a multiple of 256, at most 4096) per wave:
+// a = r(n(h) * gamma) (gamma != null) or r(n(h) * (1 + scale) + shift) with
+// [shift | scale] = mod[b] (fp32 [B, 2W], b = row / T).
+__global__ void __launch_bounds__(256)
+norm_kernel(const float* __restrict__ h, __bf16* __restrict__ a, int64_t rows, int W, const float* __restrict__ gamma,
+            const float* __restrict__ mod, int T) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;   // whole waves leave together
+  const f32x4* src = reinterpret_cast<const f32x4*>(h + row * W);
+  const int nv = W / 256;    // f32x4 per lane
+  f32x4 x[16];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < nv) {
+      x[j] = src[j * 64 + lane];
+      ss += x[j][0] * x[j][0] + x[j][1] * x[j][1] + x[j][2] * x[j][2] + x[j][3] * x[j][3];
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  const float inv = 1.0f / sqrtf(ss / (float)W + 1e-6f);
+  const float* shift = mod != nullptr ? mod + (row / T) * 2 * W : nullptr;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j < nv) {
+      const int col = (j * 64 + lane) * 4;
+      bf16x4 y;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float n = x[j][i] * inv;
+        y[i] = f2bf(gamma != nullptr ? n * gamma[col + i] : n * (1.0f + shift[W + col + i]) + shift[col + i]);
+      }
+      *reinterpret_cast<bf16x4*>(a + row * W + col) = y;
+    }
+  }
+}
+
+__global__ void silu_kernel(const float* __restrict__ c, __bf16* __restrict__ y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float x = c[i];
+  y[i] = f2bf(x / (1.0f + expf(-x)));
+}
+
+template <int EPI>
+pi_status launch_gemm(GemmParams p, hipStream_t s) {
+  p.n_mt = (p.M + GM - 1) / GM;
+  p.n_nt = p.N / GN;
+  const int total = p.n_mt * p.n_nt;
+  const int grid = (total + 7) / 8 * 8;
+  gemm_nt_kernel<EPI><<<grid, GW * 64, 0, s>>>(p);
+  return pi::check_launch("gemm_nt_kernel");
+}
+
+constexpr int LHq = 8, LHkv = 1, LD = 256, LQKV = (LHq + 2 * LHkv) * LD;
+
+struct LayerWs {
+  __bf16 *a, *q, *k, *v, *o, *u, *sc;
+  float* mod;
+  void* attn;
+  size_t attn_bytes, total;
+};
+
+LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, char* base) {
+  const int64_t N = (int64_t)Np + Ne;
+  const int64_t rows_max = (int64_t)B * (Np > Ne ? Np : Ne);
+  const int64_t wmax = Wp > We ? Wp : We;
+  const int64_t fmax = (int64_t)B * Np * Fp > (int64_t)B * Ne * Fe ? (int64_t)B * Np * Fp : (int64_t)B * Ne * Fe;
+  LayerWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = pi::align_up(off + bytes, 256);
+    return base ? base + at : nullptr;
+  };
+  w.a = reinterpret_cast<__bf16*>(take(rows_max * wmax * 2));
+  w.q = reinterpret_cast<__bf16*>(take(B * N * LHq * LD * 2));
+  w.k = reinterpret_cast<__bf16*>(take(B * N * LHkv * LD * 2));
+  w.v = reinterpret_cast<__bf16*>(take(B * N * LHkv * LD * 2));
+  w.o = reinterpret_cast<__bf16*>(take(B * N * LHq * LD * 2));
+  w.u = reinterpret_cast<__bf16*>(take(fmax * 2));
+  w.sc = reinterpret_cast<__bf16*>(take((size_t)B * wmax * 2));
+  w.mod = reinterpret_cast<float*>(take((size_t)2 * B * 2 * wmax * 4));
+  w.attn_bytes = pi_prefill_workspace_bytes(B, (int)N, LHq, LHkv, LD);
+  w.attn = take(w.attn_bytes);
+  w.total = off;
+  return w;
+}
+
+bool stream_ok(const pi_layer_stream* s) {
+  if (s == nullptr || !s->w_qkv || !s->w_o || !s->w_up || !s->w_down) return false;
+  if (s->width < 256 || s->width > 4096 || s->width % 256 || s->ffn < 256 || s->ffn % 256) return false;
+  const bool plain = s->norm1 && s->norm2, ada = s->mod1 && s->mod2;
+  return plain != ada;
+}
+
+// One stream's half of the layer before the attention: norm 1 and the QKV scatter.
+pi_status stream_qkv(const pi_layer_stream* sw, const float* h, int B, int T, int Ntot, int tok_off,
+                     const float* mod, const LayerWs& w, hipStream_t s) {
+  const int64_t rows = (int64_t)B * T;
+  norm_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(h, w.a, rows, sw->width, sw->norm1, sw->norm1 ? nullptr : mod,
+                                                          T);
+  pi_status st = pi::check_launch("norm_kernel");
+  if (st != PI_OK) return st;
+  GemmParams p{};
+  p.a = w.a;
+  p.w = static_cast<const __bf16*>(sw->w_qkv);
+  p.M = (int)rows;
+  p.N = LQKV;
+  p.K = sw->width;
+  p.amap = RowMap{(int)rows, 0, 0};
+  p.q = w.q;
+  p.k = w.k;
+  p.v = w.v;
+  p.nq = LHq * LD;
+  p.nkv = LHkv * LD;
+  p.T = T;
+  p.Ntot = Ntot;
+  p.tok_off = tok_off;
+  return launch_gemm<E_QKV>(p, s);
+}
+
+// One stream's half after the attention: output projection, norm 2, FFN.
+pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot, int tok_off, const float* mod,
+                     const LayerWs& w, hipStream_t s) {
+  const int64_t rows = (int64_t)B * T;
+  GemmParams p{};
+  p.a = w.o;
+  p.w = static_cast<const __bf16*>(sw->w_o);
+  p.M = (int)rows;
+  p.N = sw->width;
+  p.K = LHq * LD;
+  p.amap = RowMap{T, Ntot, tok_off};
+  p.out = h;
+  pi_status st = launch_gemm<E_RESID>(p, s);
+  if (st != PI_OK) return st;
+  norm_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(h, w.a, rows, sw->width, sw->norm2,
+                                                          sw->norm2 ? nullptr : mod, T);
+  if ((st = pi::check_launch("norm_kernel")) != PI_OK) return st;
+  GemmParams up{};
+  up.a = w.a;
+  up.w = static_cast<const __bf16*>(sw->w_up);
+  up.M = (int)rows;
+  up.N = sw->ffn;
+  up.K = sw->width;
+  up.amap = RowMap{(int)rows, 0, 0};
+  up.out = w.u;
+  if ((st = launch_gemm<E_GELU>(up, s)) != PI_OK) return st;
+  GemmParams dn{};
+  dn.a = w.u;
+  dn.w = static_cast<const __bf16*>(sw->w_down);
+  dn.M = (int)rows;
+  dn.N = sw->width;
+  dn.K = sw->ffn;
+  dn.amap = RowMap{(int)rows, 0, 0};
+  dn.out = h;
+  return launch_gemm<E_RESID>(dn, s);
+}
+
+// The two modulations [shift | scale] (fp32 [B, 2W] each) of an adaptive stream.
+pi_status stream_mod(const pi_layer_stream* sw, const float* cond, int B, const LayerWs& w, hipStream_t s) {
+  const int64_t n = (int64_t)B * sw->width;
+  silu_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(cond, w.sc, n);
+  pi_status st = pi::check_launch("silu_kernel");
+  if (st != PI_OK) return st;
+  for (int j = 0; j < 2; ++j) {
+    GemmParams p{};
+    p.a = w.sc;
+    p.w = static_cast<const __bf16*>(j == 0 ? sw->mod1 : sw->mod2);
+    p.M = B;
+    p.N = 2 * sw->width;
+    p.K = sw->width;
+    p.amap = RowMap{B, 0, 0};
+    p.out = w.mod + (size_t)j * B * 2 * sw->width;
+    if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
+  }
+  return PI_OK;
+}
+
+}  // namespace
+
+extern "C" size_t pi_joint_layer_workspace_bytes(const pi_layer_stream* prefix, const pi_layer_stream* expert, int B,
+                                                 int Np, int Ne) {
+  if (!stream_ok(prefix) || !stream_ok(expert) || B < 1 || Np < 0 || Ne < 0 || Np + Ne < 1) return 0;
+  return layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, nullptr).total;
+}
+
+extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const pi_layer_stream* expert, float* h_p,
+                                            float* h_e, const float* cond, int B, int Np, int Ne, float scale,
+                                            const pi_mask* mask, void* workspace, size_t workspace_bytes,
+                                            pi_stream stream) {
+  PI_REQUIRE(stream_ok(prefix) && stream_ok(expert), PI_ERR_INVALID_ARG,
+             "pi_joint_layer_forward: a stream needs w_qkv, w_o, w_up, w_down, a width and ffn that are multiples "
+             "of 256 (width <= 4096), and either norm1 + norm2 or mod1 + mod2");
+  PI_REQUIRE(B >= 1 && Np >= 0 && Ne >= 0 && Np + Ne >= 1, PI_ERR_INVALID_ARG, "pi_joint_layer_forward: B=%d Np=%d Ne=%d",
+             B, Np, Ne);
+  PI_REQUIRE((Np == 0 || h_p) && (Ne == 0 || h_e) && mask, PI_ERR_INVALID_ARG, "pi_joint_layer_forward: null pointer");
+  PI_REQUIRE(pi::aligned16(h_p) && pi::aligned16(h_e), PI_ERR_INVALID_ARG,
+             "pi_joint_layer_forward: h_p / h_e must be 16-byte aligned");
+  const bool need_cond = (Np > 0 && prefix->mod1) || (Ne > 0 && expert->mod1);
+  PI_REQUIRE(!need_cond || cond, PI_ERR_INVALID_ARG, "pi_joint_layer_forward: an adaptive norm needs cond");
+  PI_REQUIRE(!(prefix->mod1 && expert->mod1), PI_ERR_UNSUPPORTED,
+             "pi_joint_layer_forward: at most one stream may use the adaptive norm");
+  const int N = Np + Ne;
+  PI_REQUIRE(mask->B == B && mask->N == N, PI_ERR_INVALID_ARG,
+             "pi_joint_layer_forward: mask built for B=%d N=%d, call has B=%d N=%d", mask->B, mask->N, B, N);
+  PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_layer_forward: scale must be > 0");
+  // 32-bit buffer offsets: every operand a GEMM reads stays below 2 GiB
+  const int64_t big = (int64_t)B * N * LHq * LD * 2;
+  const int64_t ub = (int64_t)B * (Np > Ne ? Np : Ne) * (prefix->ffn > expert->ffn ? prefix->ffn : expert->ffn) * 2;
+  PI_REQUIRE(big < 0x7FFF0000ll && ub < 0x7FFF0000ll, PI_ERR_UNSUPPORTED,
+             "pi_joint_layer_forward: an activation exceeds 2 GiB");
+  const LayerWs need = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, nullptr);
+  PI_REQUIRE(workspace && workspace_bytes >= need.total, PI_ERR_WORKSPACE,
+             "pi_joint_layer_forward: needs %zu workspace bytes, got %zu", need.total, workspace_bytes);
+  PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "pi_joint_layer_forward: workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const LayerWs w = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn,
+                             static_cast<char*>(workspace));
+  pi_status st = PI_OK;
+  // modulations of the adaptive stream(s): mod1 at w.mod, mod2 after it
+  const pi_layer_stream* ada = expert->mod1 ? expert : (prefix->mod1 ? prefix : nullptr);
+  if (ada && (st = stream_mod(ada, cond, B, w, s)) != PI_OK) return st;
+  const int wa = ada ? ada->width : 0;
+  const float* mod1 = w.mod;
+  const float* mod2 = w.mod + (size_t)B * 2 * wa;
+  if (Np > 0 && (st = stream_qkv(prefix, h_p, B, Np, N, 0, mod1, w, s)) != PI_OK) return st;
+  if (Ne > 0 && (st = stream_qkv(expert, h_e, B, Ne, N, Np, mod1, w, s)) != PI_OK) return st;
+  st = pi_joint_attn_prefill(w.q, w.k, w.v, B, N, LHq, LHkv, LD, scale, 0.f, mask, w.o, nullptr, nullptr, 0, w.attn,
+                             w.attn_bytes, stream);
+  if (st != PI_OK) return st;
+  if (Np > 0 && (st = stream_out(prefix, h_p, B, Np, N, 0, mod2, w, s)) != PI_OK) return st;
+  if (Ne > 0 && (st = stream_out(expert, h_e, B, Ne, N, Np, mod2, w, s)) != PI_OK) return st;
+  return PI_OK;
+}

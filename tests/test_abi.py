@@ -113,6 +113,32 @@ def test_backward_rejects_bad_arguments_before_launch():
 
 
 @needs_lib
+def test_layer_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    m = Bd.PiMask(B=2, N=60, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
+    sp = Bd.PiLayerStream(2048, 8192, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    se = Bd.PiLayerStream(1024, 4096, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
+    need = lib.pi_joint_layer_workspace_bytes(ctypes.byref(sp), ctypes.byref(se), 2, 50, 10)
+    assert need > 2 * 60 * 2048 * 2 * 2     # at least the pooled q and o
+    call = lambda p=sp, e=se, **kw: lib.pi_joint_layer_forward(
+        ctypes.byref(p), ctypes.byref(e), FAKE, FAKE, kw.get("cond", FAKE), 2, kw.get("Np", 50), 10,
+        kw.get("scale", 0.0625), ctypes.byref(m), kw.get("ws", P(0x100000)), kw.get("ws_bytes", need), None)
+    assert call(Np=51) == -1                                    # mask built for another length
+    assert call(cond=None) == -1                                # the adaptive stream needs cond
+    assert call(scale=0.0) == -1
+    assert call(ws=None) == -3 and call(ws_bytes=need - 1) == -3
+    assert call(ws=P(0x100010)) == -1                           # misaligned workspace
+    odd = Bd.PiLayerStream(1000, 4096, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
+    assert call(e=odd) == -1                                    # width not a multiple of 256
+    both = Bd.PiLayerStream(1024, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(e=both) == -1                                   # plain and adaptive norm at once
+    ada_p = Bd.PiLayerStream(2048, 8192, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
+    assert call(p=ada_p) == -2                                  # two adaptive streams
+    assert lib.pi_joint_layer_workspace_bytes(ctypes.byref(odd), ctypes.byref(se), 2, 50, 10) == 0
+    assert b"pi_joint_layer_forward" in lib.pi_last_error()
+
+
+@needs_lib
 def test_decode_and_flow_reject_bad_arguments_before_launch():
     lib = Bd.lib()
     cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 4, 816, 1, 256, 816)
