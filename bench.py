@@ -13,7 +13,8 @@ Besides the step, the two kernels the metric names are measured live with HIP
 events on the stream they run on:
     prefill at the π0.5 training shape (B=32, L=962, three blocks) -> MFMA fraction
     cached decode at the serving shape (B=64, 816 slots)           -> HBM GB/s
-plus the rotary embedding, single-token decode and attention backward legs,
+plus the rotary embedding, single-token decode, attention backward and joint
+layer legs,
 and the fp64 oracle is timed on the host's cores over a bounded sample.
 Prints ONE JSON line.
 """
@@ -40,7 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward"],
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward",
+                                      "layer"],
                    default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
@@ -190,6 +192,47 @@ def backward_leg(cx: Ctx, iters: int):
         "us_per_launch": ms * 1e3, "achieved_tflops": tflops, "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
         "forward_with_lse_us": ms_fwd * 1e3, "kernel": "bwd_prep_kernel + dkdv_kernel + dq_kernel",
     }
+
+
+def layer_leg(cx: Ctx, iters: int):
+    """One π0.5 joint layer (pi_joint_layer_forward) at the training shape: B=32,
+    the prefix stream (848 prefix + 64 FAST tokens, width 2048, FFN 8192, plain
+    RMS norm) and the expert stream (50 tokens, width 1024, FFN 4096, adaptive
+    RMS norm) around the joint attention.  Algorithmic FLOPs: 2 per multiply-add
+    of every projection and FFN product, plus 8192 per allowed attention pair."""
+    torch, Bd, I = cx.torch, cx.Bd, cx.I
+    np = cx.np
+    w = I.WORKLOADS["pi05_three_block_prefill"]()
+    s = w.structure
+    B, N = w.B, w.N
+    Np = int(s.n_prefix + (s.seg == I.SEG_FAST).sum())
+    Ne = N - Np
+    Wp, We = 2048, 1024
+
+    def dev_stream(wt):
+        t = {k: (cx.bf(v) if v.dtype == np.uint16 else cx.f32(v)) for k, v in wt.items()}
+        return Bd.LayerStream(t["w_qkv"], t["w_o"], t["w_up"], t["w_down"], t.get("norm1"), t.get("norm2"),
+                              t.get("mod1"), t.get("mod2"))
+
+    sp = dev_stream(I.layer_weights(w.seed_base + 31, Wp, False))
+    se = dev_stream(I.layer_weights(w.seed_base + 41, We, True))
+    valid = cx.u8(w.input_mask())
+    m = Bd.pi_mask_build(valid, cx.u8(s.ar), cx.u8(s.seg), I.forbid_bits(s.forbid))
+    pairs = int(Bd.pi_mask_materialize(m).sum(dtype=torch.int64).item())
+    ws = Bd.layer_workspace(sp, se, B, Np, Ne, cx.dev)
+    h_p = cx.f32(I.f32_normal(w.seed_base + 51, (B, Np, Wp)))
+    h_e = cx.f32(I.f32_normal(w.seed_base + 52, (B, Ne, We)))
+    c = cx.f32(I.f32_normal(w.seed_base + 53, (B, We)))
+    ms = cx.time_ms(lambda: Bd.pi_joint_layer_forward(sp, se, h_p, h_e, c, m, ws), iters)
+    gemm = 2.0 * B * (Np * Wp * (2560 + 2048 + 2 * 4 * Wp) + Ne * We * (2560 + 1024 + 2 * 4 * We)) \
+        + 2.0 * B * We * 4 * We
+    attn = 8192.0 * pairs
+    tflops = (gemm + attn) / (ms * 1e-3) / 1e12
+    return {"workload": "pi05_joint_layer", "B": B, "prefix_stream_tokens": Np, "expert_stream_tokens": Ne,
+            "widths": [Wp, We], "ffn": [4 * Wp, 4 * We], "us_per_layer": ms * 1e3,
+            "gemm_gflop": gemm / 1e9, "attention_gflop": attn / 1e9, "achieved_tflops": tflops,
+            "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
+            "kernel": "norm_kernel + gemm_nt_kernel (QKV, out, FFN up/down) + prefill_kernel"}
 
 
 def decode_kernel_leg(cx: Ctx, iters: int):
@@ -457,6 +500,10 @@ def main():
         log("rotary embedding leg (pi05 B=32 L=962)")
         kernels["rope"] = rope_leg(cx, args.kernel_iters)
         log(str(kernels["rope"]))
+    if args.only in (None, "layer"):
+        log("joint layer leg (pi05 B=32, 912 + 50 tokens)")
+        kernels["layer"] = layer_leg(cx, max(3, args.kernel_iters // 10))
+        log(str(kernels["layer"]))
     if args.only in (None, "backward"):
         log("attention backward leg (pi05 B=32 L=962)")
         kernels["backward"] = backward_leg(cx, max(5, args.kernel_iters // 5))
@@ -512,6 +559,11 @@ def main():
                      "us_per_launch": kernels["backward"]["us_per_launch"],
                      "gflop_per_launch": kernels["backward"]["gflop_per_launch"],
                      "forward_with_lse_us": kernels["backward"]["forward_with_lse_us"]},
+        "joint_layer": {"kernel": kernels["layer"]["kernel"] + " (pi05 B=32, 912 + 50 tokens, widths 2048 / 1024)",
+                        "bound": "mfma", "achieved": kernels["layer"]["achieved_tflops"],
+                        "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": kernels["layer"]["mfma_frac"],
+                        "us_per_layer": kernels["layer"]["us_per_layer"],
+                        "gflop_per_layer": kernels["layer"]["gemm_gflop"] + kernels["layer"]["attention_gflop"]},
         "breakdown_us": result["breakdown_us"],
         "cpu_baseline": cpu,
     }

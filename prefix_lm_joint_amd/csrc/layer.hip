@@ -14,13 +14,14 @@
 //
 // Kernels:
 //   * gemm_nt_kernel: C = A W^T for row-major bf16 A [M, K] and W [N, K] with fp32
-//     accumulation, on the matrix cores.  A workgroup owns a 256 (N) x 128 (M)
-//     tile with 8 waves of 64 x 64; K advances 32 at a time through four LDS
-//     stages filled by direct-to-LDS buffer loads.  Each load instruction
+//     accumulation, on the matrix cores.  A workgroup owns a 256 (N) x 256 (M)
+//     tile (256 x 128 for few rows) with 8 waves of 64 x 128 (64 x 64); K
+//     advances 32 at a time through three LDS stages filled by direct-to-LDS
+//     buffer loads.  Each load instruction
 //     fetches one 16 x 32 operand fragment (16 rows x 64 bytes) and lands it in
 //     the exact image the fragment read expects (lane L's 16 bytes at 16 L), so
 //     every LDS read is 1 KB contiguous per wave, free of bank conflicts, and
-//     every fragment read feeds four products.  Products are computed
+//     every fragment read feeds four (W) or eight (A) products.  Products are computed
 //     transposed (A operand = W rows, B operand = A rows) so a lane ends with
 //     four consecutive output columns of one row for the epilogue: bf16 store,
 //     gelu, residual add into fp32, fp32 store, or the QKV scatter into the
@@ -38,12 +39,21 @@ namespace {
 
 using namespace pi_engine;
 
-constexpr int GN = 256, GM = 128, GK = 32;      // workgroup tile (N x M) and k step
-constexpr int GW = 8;                           // waves
-constexpr int GSTAGES = 4;
+constexpr int GN = 256, GK = 32;                // workgroup tile N and k step (the M tile is a parameter)
+constexpr int GW = 8;                           // waves: 4 along N x 2 along M
+constexpr int GSTAGES = 3;
+constexpr int kGroupM = 4;                      // m tiles per group of the tile order
 constexpr int kFragBytes = 1024;                // one 16 x 32 bf16 operand fragment
-constexpr int kWFrags = GN / 16, kAFrags = GM / 16;
-constexpr int kStageBytes = (kWFrags + kAFrags) * kFragBytes;   // 24 KB
+constexpr int kWFrags = GN / 16;
+template <int GM>
+struct GTile {
+  static constexpr int AFrags = GM / 16;                          // A fragments per stage
+  static constexpr int MI = GM / 32;                              // A fragments per wave (its GM/2 rows)
+  static constexpr int ALoads = AFrags / GW;                      // A fragment loads per wave and stage
+  static constexpr int Loads = 2 + ALoads;                        // loads per wave and stage
+  static constexpr int StageBytes = (kWFrags + AFrags) * kFragBytes;
+  static_assert(AFrags % GW == 0, "whole A fragments per wave");
+};
 
 enum { E_BF16 = 0, E_GELU = 1, E_RESID = 2, E_F32 = 3, E_QKV = 4 };
 
@@ -92,72 +102,96 @@ __device__ __forceinline__ void gemm_store(const GemmParams& p, int64_t m, int n
   }
 }
 
+// vmcnt <= n for n = j * L (j = 0 .. 2; L loads per wave and step, at most 5);
+// expcnt and lgkmcnt left at their maxima
+template <int L>
 __device__ __forceinline__ void wait_vmem_le(int n) {
-  // vmcnt <= n (n in {0, 3, 6}); expcnt and lgkmcnt left at their maxima
-  if (n >= 6) __builtin_amdgcn_s_waitcnt(0x0F76);
-  else if (n >= 3) __builtin_amdgcn_s_waitcnt(0x0F73);
+  static_assert(2 * L < 16, "vmcnt field");
+  if (n >= 2 * L) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * L));
+  else if (n >= L) __builtin_amdgcn_s_waitcnt(0x0F70 | L);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int EPI>
+// Workgroup barrier without the memory fence __syncthreads() carries: that
+// fence waits for every outstanding load of the wave (vmcnt 0), which would
+// drain the loads of the steps ahead.  Here each wave has waited for exactly its
+// own loads of the current step, and the previous stage's LDS reads have all
+// been consumed by products before a wave arrives, so the bare barrier (with
+// compiler-level memory ordering around it) is enough.
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int EPI, int GM>
 __global__ void __launch_bounds__(GW * 64) gemm_nt_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[GSTAGES * kStageBytes];
+  using G = GTile<GM>;
+  __shared__ __attribute__((aligned(16))) char smem[GSTAGES * G::StageBytes];
   // XCD-aware tile order: the workgroups of one XCD take a contiguous run of
-  // (m tile, n tile) pairs, n fastest, so they share the A rows in that L2
+  // tiles, and within it groups of kGroupM m tiles x all n tiles, m fastest, so
+  // the ~32 workgroups an XCD runs at once cover 4 m tiles x 8 n tiles and share
+  // both operands' k windows in that XCD's L2
   const int total = p.n_mt * p.n_nt;
   const int chunk = (total + 7) / 8;
   const int lin = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
   if ((int)(blockIdx.x >> 3) >= chunk || lin >= total) return;
-  const int mt = lin / p.n_nt, nt = lin % p.n_nt;
+  const int gsize = kGroupM * p.n_nt;
+  const int first_m = (lin / gsize) * kGroupM;
+  const int gm = min(p.n_mt - first_m, kGroupM);
+  const int mt = first_m + (lin % gsize) % gm, nt = (lin % gsize) / gm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int wn = wave & 3, wm = wave >> 2;
   const int nk = p.K / GK;
-  // this wave's loads: W fragments 2 wave, 2 wave + 1 and A fragment wave
+  // this wave's loads: W fragments 2 wave, 2 wave + 1 and A fragments wave * ALoads ..
   const i32x4 rw = make_rsrc(p.w + (int64_t)nt * GN * p.K);
   const i32x4 ra = make_rsrc(p.a);
   const uint32_t kb = (uint32_t)p.K * 2u;
-  uint32_t ow[2];
+  uint32_t ow[2], oa[G::ALoads];
 #pragma unroll
   for (int j = 0; j < 2; ++j) ow[j] = (uint32_t)((2 * wave + j) * 16 + c) * kb + 16u * (uint32_t)g;
-  const int64_t am = (int64_t)mt * GM + wave * 16 + c;
-  const uint32_t oa = am < p.M ? (uint32_t)(p.amap(am) * p.K * 2 + 16 * g) : kOOB;
+#pragma unroll
+  for (int j = 0; j < G::ALoads; ++j) {
+    const int64_t am = (int64_t)mt * GM + (wave * G::ALoads + j) * 16 + c;
+    oa[j] = am < p.M ? (uint32_t)(p.amap(am) * p.K * 2 + 16 * g) : kOOB;
+  }
   auto issue = [&](int i) {
-    char* st = smem + (i & 3) * kStageBytes;
+    char* st = smem + (i % GSTAGES) * G::StageBytes;
     const int so = __builtin_amdgcn_readfirstlane(i * GK * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       pi_buffer_load_lds(rw, lds_u32(st + (2 * wave + j) * kFragBytes), 16, (int)ow[j], so, 0, 0);
-    pi_buffer_load_lds(ra, lds_u32(st + kWFrags * kFragBytes + wave * kFragBytes), 16, (int)oa, so, 0, 0);
+#pragma unroll
+    for (int j = 0; j < G::ALoads; ++j)
+      pi_buffer_load_lds(ra, lds_u32(st + (kWFrags + wave * G::ALoads + j) * kFragBytes), 16, (int)oa[j], so, 0, 0);
   };
-  f32x4 acc[4][4];
+  f32x4 acc[4][G::MI];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  issue(0);
-  if (nk > 1) issue(1);
-  if (nk > 2) issue(2);
+    for (int b = 0; b < G::MI; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < GSTAGES - 1 && j < nk; ++j) issue(j);
   for (int i = 0; i < nk; ++i) {
-    wait_vmem_le(3 * min(nk - 1 - i, 2));   // this wave's loads of step i have landed
-    __syncthreads();                         // everyone's; and every wave is done with step i - 1
-    if (i + 3 < nk) issue(i + 3);            // into the stage of step i - 1
-    const char* st = smem + (i & 3) * kStageBytes;
-    bf16x8 wf[4], af[4];
+    wait_vmem_le<G::Loads>(G::Loads * min(nk - 1 - i, GSTAGES - 2));   // this wave's loads of step i have landed
+    step_barrier();                          // everyone's; and every wave is done with step i - 1
+    if (i + GSTAGES - 1 < nk) issue(i + GSTAGES - 1);  // into the stage of step i - 1
+    const char* st = smem + (i % GSTAGES) * G::StageBytes;
+    bf16x8 wf[4], af[G::MI];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wf[j] = *reinterpret_cast<const bf16x8*>(st + (4 * wn + j) * kFragBytes + lane * 16);
-      af[j] = *reinterpret_cast<const bf16x8*>(st + kWFrags * kFragBytes + (4 * wm + j) * kFragBytes + lane * 16);
-    }
+    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(st + (4 * wn + j) * kFragBytes + lane * 16);
+#pragma unroll
+    for (int j = 0; j < G::MI; ++j)
+      af[j] = *reinterpret_cast<const bf16x8*>(st + (kWFrags + G::MI * wm + j) * kFragBytes + lane * 16);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma16x16x32(wf[a], af[b], acc[a][b]);
+      for (int b = 0; b < G::MI; ++b) acc[a][b] = mfma16x16x32(wf[a], af[b], acc[a][b]);
   }
-  // acc[a][b][i] = C[m = mt*128 + 64 wm + 16 b + c][n = nt*256 + 64 wn + 16 a + 4 g + i]
+  // acc[a][b][i] = C[m = mt*GM + (GM/2) wm + 16 b + c][n = nt*256 + 64 wn + 16 a + 4 g + i]
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int64_t m = (int64_t)mt * GM + 64 * wm + 16 * b + c;
+  for (int b = 0; b < G::MI; ++b) {
+    const int64_t m = (int64_t)mt * GM + (GM / 2) * wm + 16 * b + c;
     if (m >= p.M) continue;
 #pragma unroll
     for (int a = 0; a < 4; ++a) gemm_store<EPI>(p, m, nt * GN + 64 * wn + 16 * a + 4 * g, acc[a][b]);
@@ -210,13 +244,17 @@ __global__ void silu_kernel(const float* __restrict__ c, __bf16* __restrict__ y,
   y[i] = f2bf(x / (1.0f + expf(-x)));
 }
 
+// 256 x 256 tiles once the rows alone give a few hundred workgroups, else 256 x 128.
 template <int EPI>
 pi_status launch_gemm(GemmParams p, hipStream_t s) {
-  p.n_mt = (p.M + GM - 1) / GM;
+  const bool wide = p.M >= 8192;
+  const int gm = wide ? 256 : 128;
+  p.n_mt = (p.M + gm - 1) / gm;
   p.n_nt = p.N / GN;
   const int total = p.n_mt * p.n_nt;
   const int grid = (total + 7) / 8 * 8;
-  gemm_nt_kernel<EPI><<<grid, GW * 64, 0, s>>>(p);
+  if (wide) gemm_nt_kernel<EPI, 256><<<grid, GW * 64, 0, s>>>(p);
+  else gemm_nt_kernel<EPI, 128><<<grid, GW * 64, 0, s>>>(p);
   return pi::check_launch("gemm_nt_kernel");
 }
 
