@@ -78,6 +78,29 @@ def stream_norm(h, p, which: int, c=None, r=round_bf16):
     return r(n * (1.0 + scale[:, None, :]) + shift[:, None, :])
 
 
+def _round_fn(rounding):
+    return round_bf16 if rounding else (lambda x: np.asarray(x, np.float64))
+
+
+def stream_qkv(h, p, c=None, Hq=8, Hkv=1, d=256, rounding=True):
+    """The stream's pooled inputs (q [B,T,Hq,d], k / v [B,T,Hkv,d]) = r(norm1(h) W_qkv^T), split (L5)."""
+    r = _round_fn(rounding)
+    h = np.asarray(h, np.float64)
+    B, T = h.shape[:2]
+    y = r(_lin(stream_norm(h, p, 1, c, r), p["w_qkv"]))
+    return (y[..., :Hq * d].reshape(B, T, Hq, d), y[..., Hq * d:(Hq + Hkv) * d].reshape(B, T, Hkv, d),
+            y[..., (Hq + Hkv) * d:].reshape(B, T, Hkv, d))
+
+
+def stream_out(h, o, p, c=None, rounding=True):
+    """The stream's half after the attention: h += o W_o^T; h += r(gelu(norm2(h) W_up^T)) W_down^T
+    (o [B, T, Hq*d] already rounded)."""
+    r = _round_fn(rounding)
+    h = np.asarray(h, np.float64) + _lin(o, p["w_o"])
+    u = r(gelu(_lin(stream_norm(h, p, 2, c, r), p["w_up"])))
+    return h + _lin(u, p["w_down"])
+
+
 def joint_layer(h_p, h_e, c, wp, we, m, Hq=8, Hkv=1, d=256, scale=None, rounding=True):
     """One layer over the prefix stream h_p [B, Np, Wp] and the expert stream
     h_e [B, Ne, We] (conditioning c [B, We] for an adaptive norm) under the joint
@@ -86,25 +109,23 @@ def joint_layer(h_p, h_e, c, wp, we, m, Hq=8, Hkv=1, d=256, scale=None, rounding
     wp / we map names to arrays: w_qkv [Hq*d + 2*Hkv*d, W], w_o [W, Hq*d],
     w_up [4W, W], w_down [W, 4W], and either norm1 / norm2 [W] (plain norm) or
     mod1 / mod2 [2W, W] (adaptive norm)."""
-    r = round_bf16 if rounding else (lambda x: np.asarray(x, np.float64))
-    h_p = np.asarray(h_p, np.float64)
-    h_e = np.asarray(h_e, np.float64)
-    B, Np, _ = h_p.shape
-    Ne = h_e.shape[1]
-    qs, ks, vs = [], [], []
-    for h, p in ((h_p, wp), (h_e, we)):
-        a = stream_norm(h, p, 1, c, r)
-        y = r(_lin(a, p["w_qkv"]))
-        T = h.shape[1]
-        qs.append(y[..., :Hq * d].reshape(B, T, Hq, d))
-        ks.append(y[..., Hq * d:(Hq + Hkv) * d].reshape(B, T, Hkv, d))
-        vs.append(y[..., (Hq + Hkv) * d:].reshape(B, T, Hkv, d))
-    q, k, v = (np.concatenate(t, axis=1) for t in (qs, ks, vs))
+    r = _round_fn(rounding)
+    B, Np, _ = np.shape(h_p)
+    Ne = np.shape(h_e)[1]
+    parts = [stream_qkv(h, p, c, Hq, Hkv, d, rounding) for h, p in ((h_p, wp), (h_e, we))]
+    q, k, v = (np.concatenate([pt[j] for pt in parts], axis=1) for j in range(3))
     o = r(_attn.masked_attention(q, k, v, m, scale=scale)).reshape(B, Np + Ne, Hq * d)
-    out = []
-    for h, p, sl in ((h_p, wp, slice(0, Np)), (h_e, we, slice(Np, Np + Ne))):
-        h = h + _lin(o[:, sl], p["w_o"])
-        b = stream_norm(h, p, 2, c, r)
-        u = r(gelu(_lin(b, p["w_up"])))
-        out.append(h + _lin(u, p["w_down"]))
-    return out[0], out[1]
+    return (stream_out(h_p, o[:, :Np], wp, c, rounding), stream_out(h_e, o[:, Np:], we, c, rounding))
+
+
+def expert_layer_decode(h_e, c, we, cache_k, cache_v, prefix_mask, suffix_ar, Hq=8, Hkv=1, d=256, scale=None,
+                        rounding=True):
+    """The expert stream's half of one layer in the cached form ("VLA 代码精读"
+    §1.6): its S tokens h_e [B, S, W] attend to the valid slots of the cached
+    prefix K/V cache_k / cache_v [B, P, Hkv, d] plus their own K/V under the
+    suffix block rule (suffix_ar [S]); norms, projections and FFN as joint_layer."""
+    r = _round_fn(rounding)
+    B, S = np.shape(h_e)[:2]
+    q, k, v = stream_qkv(h_e, we, c, Hq, Hkv, d, rounding)
+    o = r(_attn.cached_decode(q, k, v, cache_k, cache_v, prefix_mask, suffix_ar, scale=scale))
+    return stream_out(h_e, o.reshape(B, S, Hq * d), we, c, rounding)

@@ -228,3 +228,26 @@ def test_layer_tolerance_is_twice_the_fp32_floor():
     assert 2e-4 < worst_mean < 2e-3 and worst_max < 2e-2
     assert 1.5 * worst_mean <= LAYER_MEAN_ABS <= 3.0 * worst_mean
     assert 1.5 * worst_max <= LAYER_MAX_ABS
+
+
+def test_expert_decode_equals_the_joint_layers_expert_rows():
+    """With the cache holding the prefix stream's K/V of the same layer, the cached
+    form of the expert's layer is bit-identical to the expert rows of the joint
+    layer (the prefix rows cannot see the expert, so the prefix is computed once)."""
+    B, P, S, Wp, We = 2, 11, 6, 32, 24
+    r = np.random.default_rng(8)
+    h_p, h_e, c = r.standard_normal((B, P, Wp)), r.standard_normal((B, S, We)), r.standard_normal((B, We))
+    wp, we = _weights(30, Wp, False), _weights(40, We, True)
+    s = I.pi0_structure(P, S - 1)
+    valid = np.ones((B, P + S), np.uint8)
+    valid[1, P - 3:P] = 0
+    m = M.attn_mask(valid, s.ar, s.seg, s.forbid)
+    want = Y.joint_layer(h_p, h_e, c, wp, we, m, Hq, Hkv, d)[1]
+    _, ck, cv = Y.stream_qkv(h_p, wp, None, Hq, Hkv, d)
+    got = Y.expert_layer_decode(h_e, c, we, ck, cv, valid[:, :P], s.ar[P:], Hq, Hkv, d)
+    assert np.array_equal(got, want)
+    # and the cache's padded slots do not matter
+    ck2, cv2 = ck.copy(), cv.copy()
+    ck2[1, P - 3:] = 1e3
+    cv2[1, P - 3:] = -1e3
+    assert np.array_equal(Y.expert_layer_decode(h_e, c, we, ck2, cv2, valid[:, :P], s.ar[P:], Hq, Hkv, d), got)
