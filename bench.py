@@ -13,8 +13,8 @@ Besides the step, the two kernels the metric names are measured live with HIP
 events on the stream they run on:
     prefill at the π0.5 training shape (B=32, L=962, three blocks) -> MFMA fraction
     cached decode at the serving shape (B=64, 816 slots)           -> HBM GB/s
-plus the rotary embedding, single-token decode, attention backward and joint
-layer legs,
+plus the rotary embedding, single-token decode, attention backward, joint
+layer and cached expert-layer legs,
 and the fp64 oracle is timed on the host's cores over a bounded sample.
 Prints ONE JSON line.
 """
@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward",
-                                      "layer"],
+                                      "layer", "expert"],
                    default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
@@ -233,6 +233,42 @@ def layer_leg(cx: Ctx, iters: int):
             "gemm_gflop": gemm / 1e9, "attention_gflop": attn / 1e9, "achieved_tflops": tflops,
             "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
             "kernel": "norm_kernel + gemm_nt_kernel (QKV, out, FFN up/down) + prefill_kernel"}
+
+
+def expert_decode_leg(cx: Ctx, iters: int):
+    """The expert stream's π0.5 layer in the cached form (pi_expert_layer_decode)
+    at the serving shape: B=64 robots, 50 action tokens of width 1024 (FFN 4096,
+    adaptive norm) against one cache layer of 816 slots (valid U[600, 816])."""
+    torch, Bd, I, np = cx.torch, cx.Bd, cx.I, cx.np
+    w = I.serving_decode()
+    B, P, S, W = w.B, w.structure.n_prefix, 50, 1024
+    pm = w.input_mask()[:, :P]
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(w.seed_base + 61)
+    ck = torch.randn((1, B, P, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cv = torch.randn((1, B, P, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cache = Bd.KVCache(ck, cv, cx.u8(pm), P)
+    wt = I.layer_weights(w.seed_base + 62, W, True)
+    t = {k: (cx.bf(v) if v.dtype == np.uint16 else cx.f32(v)) for k, v in wt.items()}
+    se = Bd.LayerStream(t["w_qkv"], t["w_o"], t["w_up"], t["w_down"], None, None, t["mod1"], t["mod2"])
+    h = cx.f32(I.f32_normal(w.seed_base + 63, (B, S, W)))
+    c = cx.f32(I.f32_normal(w.seed_base + 64, (B, W)))
+    sar = np.zeros(S, np.uint8)
+    sar[0] = 1
+    sar = cx.u8(sar)
+    ws = Bd.expert_decode_workspace(se, cache, S)
+    ms = cx.time_ms(lambda: Bd.pi_expert_layer_decode(se, cache, 0, h, c, sar, ws), iters)
+    lens = pm.sum(axis=1)
+    pairs = int(S * 8 * lens.sum() + B * 8 * S * S)      # every action token sees the valid slots and the chunk
+    gemm = 2.0 * B * S * W * (2560 + 1024 + 2 * 4 * W) + 2.0 * 2 * B * W * 2 * W
+    flops = gemm + 4.0 * 256 * pairs
+    weights = 2 * (2560 * W + W * 2048 + 2 * 4 * W * W + 2 * 2 * W * W)
+    byts = weights + int(lens.sum()) * 256 * 2 * 2 + B * S * W * 4 * 2
+    return {"workload": "pi05_expert_layer_decode", "B": B, "slots": P, "tokens": S, "width": W,
+            "us_per_layer": ms * 1e3, "gflop_per_layer": flops / 1e9,
+            "achieved_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
+            "algorithmic_bytes": byts, "achieved_gbs": byts / (ms * 1e-3) / 1e9,
+            "kernel": "norm_kernel + gemm_nt_kernel + decode_kernel (+ combine)"}
 
 
 def decode_kernel_leg(cx: Ctx, iters: int):
@@ -504,6 +540,10 @@ def main():
         log("joint layer leg (pi05 B=32, 912 + 50 tokens)")
         kernels["layer"] = layer_leg(cx, max(3, args.kernel_iters // 10))
         log(str(kernels["layer"]))
+    if args.only in (None, "expert"):
+        log("expert layer, cached form (B=64, 816 slots, 50 tokens)")
+        kernels["expert"] = expert_decode_leg(cx, max(5, args.kernel_iters // 5))
+        log(str(kernels["expert"]))
     if args.only in (None, "backward"):
         log("attention backward leg (pi05 B=32 L=962)")
         kernels["backward"] = backward_leg(cx, max(5, args.kernel_iters // 5))
@@ -564,6 +604,11 @@ def main():
                         "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": kernels["layer"]["mfma_frac"],
                         "us_per_layer": kernels["layer"]["us_per_layer"],
                         "gflop_per_layer": kernels["layer"]["gemm_gflop"] + kernels["layer"]["attention_gflop"]},
+        "expert_layer_decode": {"kernel": kernels["expert"]["kernel"] + " (B=64, 816 slots, 50 tokens, width 1024)",
+                                "bound": "mfma", "achieved": kernels["expert"]["achieved_tflops"],
+                                "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                                "frac": kernels["expert"]["mfma_frac"], "us_per_layer": kernels["expert"]["us_per_layer"],
+                                "achieved_gbs": kernels["expert"]["achieved_gbs"]},
         "breakdown_us": result["breakdown_us"],
         "cpu_baseline": cpu,
     }

@@ -207,6 +207,23 @@ pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const pi_layer_s
                                  pi_stream stream);
 
 /*
+ * The expert stream's half of the same layer in the cached form ([P1] §1.6: at
+ * inference the prefix is computed once and each Euler step runs only the
+ * suffix against the cache): the S expert tokens h_e fp32 [B, S, W] (updated in
+ * place) take norm 1 and their fused QKV as in pi_joint_layer_forward, attend
+ * to the valid slots of cache layer `layer` plus their own K/V under suffix_ar
+ * (pi_suffix_decode_step), then take the output projection, norm 2 and FFN.
+ * The cache holds the prefix stream's K/V of that layer.  Same stream
+ * weights and cond as above; S and the cache as pi_suffix_decode_step supports.
+ * workspace (device, 256-byte aligned, required):
+ * pi_expert_layer_decode_workspace_bytes(expert, B, S, cache->len).
+ */
+size_t pi_expert_layer_decode_workspace_bytes(const pi_layer_stream* expert, int B, int S, int len);
+pi_status pi_expert_layer_decode(const pi_layer_stream* expert, const pi_kv_cache* cache, int layer,
+                                 float* h_e, const float* cond, const uint8_t* suffix_ar, int B, int S,
+                                 float scale, void* workspace, size_t workspace_bytes, pi_stream stream);
+
+/*
  * Per-layer prefix KV cache ([P1] §1.6; [P4] §4.1).  Device memory owned by the caller.
  *   k, v         bf16 [layers, B, capacity, Hkv, d]
  *   prefix_mask  uint8 [B, capacity]: nonzero = slot holds a valid prefix token

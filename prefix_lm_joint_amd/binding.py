@@ -65,6 +65,9 @@ _SIGS = {
                                                          _c_i, _c_i, _c_i]),
     "pi_joint_layer_forward": (_c_i, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiLayerStream), _c_p, _c_p, _c_p,
                                       _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask), _c_p, ctypes.c_size_t, _c_p]),
+    "pi_expert_layer_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiLayerStream), _c_i, _c_i, _c_i]),
+    "pi_expert_layer_decode": (_c_i, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p,
+                                      _c_i, _c_i, _c_f, _c_p, ctypes.c_size_t, _c_p]),
     "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
                                      _c_f, _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
@@ -334,6 +337,30 @@ def pi_joint_layer_forward(prefix: LayerStream, expert: LayerStream, h_p: torch.
         _ptr(h_e, torch.float32, "h_e"), _ptr(cond, torch.float32, "cond") if cond is not None else None, B, Np, Ne,
         scale, ctypes.byref(mask.struct), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream)))
+
+
+def pi_expert_layer_decode_workspace_bytes(expert: LayerStream, B: int, S: int, length: int) -> int:
+    return int(lib().pi_expert_layer_decode_workspace_bytes(ctypes.byref(expert.struct), B, S, length))
+
+
+def expert_decode_workspace(expert: LayerStream, cache: "KVCache", S: int) -> torch.Tensor:
+    n = pi_expert_layer_decode_workspace_bytes(expert, cache.struct.B, S, cache.struct.len)
+    if n == 0:
+        raise ValueError("pi_expert_layer_decode does not support this stream")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+
+
+def pi_expert_layer_decode(expert: LayerStream, cache: "KVCache", layer: int, h_e: torch.Tensor,
+                           cond: Optional[torch.Tensor], suffix_ar: torch.Tensor, workspace: torch.Tensor,
+                           scale: Optional[float] = None, stream=None) -> None:
+    """The expert stream's layer against cache layer `layer`; updates h_e [B, S, W] (fp32) in place."""
+    B, S = h_e.shape[:2]
+    if scale is None:
+        scale = 256 ** -0.5
+    _check("pi_expert_layer_decode", lib().pi_expert_layer_decode(
+        ctypes.byref(expert.struct), ctypes.byref(cache.struct), layer, _ptr(h_e, torch.float32, "h_e"),
+        _ptr(cond, torch.float32, "cond") if cond is not None else None, _ptr(suffix_ar, torch.uint8, "suffix_ar"),
+        B, S, scale, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def pi_decode_workspace_bytes(B: int, S: int, Hq: int, length: int) -> int:

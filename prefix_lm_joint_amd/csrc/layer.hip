@@ -267,7 +267,8 @@ struct LayerWs {
   size_t attn_bytes, total;
 };
 
-LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, char* base) {
+// attn_bytes: the attention's own workspace (the joint prefill's or the cached decode's)
+LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, size_t attn_bytes, char* base) {
   const int64_t N = (int64_t)Np + Ne;
   const int64_t rows_max = (int64_t)B * (Np > Ne ? Np : Ne);
   const int64_t wmax = Wp > We ? Wp : We;
@@ -287,7 +288,7 @@ LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, char* ba
   w.u = reinterpret_cast<__bf16*>(take(fmax * 2));
   w.sc = reinterpret_cast<__bf16*>(take((size_t)B * wmax * 2));
   w.mod = reinterpret_cast<float*>(take((size_t)2 * B * 2 * wmax * 4));
-  w.attn_bytes = pi_prefill_workspace_bytes(B, (int)N, LHq, LHkv, LD);
+  w.attn_bytes = attn_bytes;
   w.attn = take(w.attn_bytes);
   w.total = off;
   return w;
@@ -388,7 +389,8 @@ pi_status stream_mod(const pi_layer_stream* sw, const float* cond, int B, const 
 extern "C" size_t pi_joint_layer_workspace_bytes(const pi_layer_stream* prefix, const pi_layer_stream* expert, int B,
                                                  int Np, int Ne) {
   if (!stream_ok(prefix) || !stream_ok(expert) || B < 1 || Np < 0 || Ne < 0 || Np + Ne < 1) return 0;
-  return layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, nullptr).total;
+  return layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn,
+                  pi_prefill_workspace_bytes(B, Np + Ne, LHq, LHkv, LD), nullptr).total;
 }
 
 extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const pi_layer_stream* expert, float* h_p,
@@ -416,13 +418,14 @@ extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const
   const int64_t ub = (int64_t)B * (Np > Ne ? Np : Ne) * (prefix->ffn > expert->ffn ? prefix->ffn : expert->ffn) * 2;
   PI_REQUIRE(big < 0x7FFF0000ll && ub < 0x7FFF0000ll, PI_ERR_UNSUPPORTED,
              "pi_joint_layer_forward: an activation exceeds 2 GiB");
-  const LayerWs need = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, nullptr);
+  const size_t attn_bytes = pi_prefill_workspace_bytes(B, N, LHq, LHkv, LD);
+  const LayerWs need = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, attn_bytes, nullptr);
   PI_REQUIRE(workspace && workspace_bytes >= need.total, PI_ERR_WORKSPACE,
              "pi_joint_layer_forward: needs %zu workspace bytes, got %zu", need.total, workspace_bytes);
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_joint_layer_forward: workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const LayerWs w = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn,
+  const LayerWs w = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, attn_bytes,
                              static_cast<char*>(workspace));
   pi_status st = PI_OK;
   // modulations of the adaptive stream(s): mod1 at w.mod, mod2 after it
@@ -439,4 +442,45 @@ extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const
   if (Np > 0 && (st = stream_out(prefix, h_p, B, Np, N, 0, mod2, w, s)) != PI_OK) return st;
   if (Ne > 0 && (st = stream_out(expert, h_e, B, Ne, N, Np, mod2, w, s)) != PI_OK) return st;
   return PI_OK;
+}
+
+extern "C" size_t pi_expert_layer_decode_workspace_bytes(const pi_layer_stream* expert, int B, int S, int len) {
+  if (!stream_ok(expert) || B < 1 || S < 1 || len < 0) return 0;
+  return layer_ws(B, 0, S, expert->width, expert->width, expert->ffn, expert->ffn,
+                  pi_decode_workspace_bytes(B, S, LHq, len), nullptr).total;
+}
+
+extern "C" pi_status pi_expert_layer_decode(const pi_layer_stream* expert, const pi_kv_cache* cache, int layer,
+                                            float* h_e, const float* cond, const uint8_t* suffix_ar, int B, int S,
+                                            float scale, void* workspace, size_t workspace_bytes, pi_stream stream) {
+  PI_REQUIRE(stream_ok(expert), PI_ERR_INVALID_ARG,
+             "pi_expert_layer_decode: the stream needs w_qkv, w_o, w_up, w_down, a width and ffn that are multiples "
+             "of 256 (width <= 4096), and either norm1 + norm2 or mod1 + mod2");
+  PI_REQUIRE(cache && h_e && suffix_ar, PI_ERR_INVALID_ARG, "pi_expert_layer_decode: null pointer");
+  PI_REQUIRE(B >= 1 && S >= 1 && cache->B == B && cache->Hkv == LHkv && cache->d == LD && layer >= 0 &&
+                 layer < cache->layers,
+             PI_ERR_INVALID_ARG, "pi_expert_layer_decode: cache / shape mismatch (B=%d S=%d layer %d)", B, S, layer);
+  PI_REQUIRE(pi::aligned16(h_e), PI_ERR_INVALID_ARG, "pi_expert_layer_decode: h_e must be 16-byte aligned");
+  PI_REQUIRE(!expert->mod1 || cond, PI_ERR_INVALID_ARG, "pi_expert_layer_decode: an adaptive norm needs cond");
+  PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_expert_layer_decode: scale must be > 0");
+  PI_REQUIRE((int64_t)B * S * expert->ffn * 2 < 0x7FFF0000ll, PI_ERR_UNSUPPORTED,
+             "pi_expert_layer_decode: an activation exceeds 2 GiB");
+  const size_t attn_bytes = pi_decode_workspace_bytes(B, S, LHq, cache->len);
+  const LayerWs need = layer_ws(B, 0, S, expert->width, expert->width, expert->ffn, expert->ffn, attn_bytes, nullptr);
+  PI_REQUIRE(workspace && workspace_bytes >= need.total, PI_ERR_WORKSPACE,
+             "pi_expert_layer_decode: needs %zu workspace bytes, got %zu", need.total, workspace_bytes);
+  PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "pi_expert_layer_decode: workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const LayerWs w = layer_ws(B, 0, S, expert->width, expert->width, expert->ffn, expert->ffn, attn_bytes,
+                             static_cast<char*>(workspace));
+  pi_status st = PI_OK;
+  if (expert->mod1 && (st = stream_mod(expert, cond, B, w, s)) != PI_OK) return st;
+  const float* mod1 = w.mod;
+  const float* mod2 = w.mod + (size_t)B * 2 * expert->width;
+  if ((st = stream_qkv(expert, h_e, B, S, S, 0, mod1, w, s)) != PI_OK) return st;
+  st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, LHq, scale, 0.f, w.o, w.attn, w.attn_bytes,
+                             stream);
+  if (st != PI_OK) return st;
+  return stream_out(expert, h_e, B, S, S, 0, mod2, w, s);
 }

@@ -136,6 +136,16 @@ def test_layer_rejects_bad_arguments_before_launch():
     assert call(p=ada_p) == -2                                  # two adaptive streams
     assert lib.pi_joint_layer_workspace_bytes(ctypes.byref(odd), ctypes.byref(se), 2, 50, 10) == 0
     assert b"pi_joint_layer_forward" in lib.pi_last_error()
+    # the cached form of the expert's layer
+    cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 2, 816, 1, 256, 816)
+    need_d = lib.pi_expert_layer_decode_workspace_bytes(ctypes.byref(se), 2, 50, 816)
+    assert need_d > 2 * 50 * 4096 * 2 and lib.pi_expert_layer_decode_workspace_bytes(ctypes.byref(odd), 2, 50, 816) == 0
+    dec = lambda e=se, **kw: lib.pi_expert_layer_decode(
+        ctypes.byref(e), ctypes.byref(cache), kw.get("layer", 0), FAKE, kw.get("cond", FAKE), FAKE, kw.get("B", 2),
+        50, 0.0625, kw.get("ws", P(0x100000)), kw.get("ws_bytes", need_d), None)
+    assert dec(layer=18) == -1 and dec(B=3) == -1 and dec(cond=None) == -1
+    assert dec(ws_bytes=need_d - 1) == -3 and dec(e=odd) == -1
+    assert b"pi_expert_layer_decode" in lib.pi_last_error()
 
 
 @needs_lib

@@ -95,3 +95,44 @@ def test_layer_training_shape_sampled():
     w = I.pi05_train()
     note("layer training shape B=32 sampled")
     _run(4, w.B, w.structure, 2048, 1024, check=[31])
+
+
+def _expert_decode(seed, B, P, S, W, check=None, lens=None):
+    """The expert layer in the cached form against random cached prefix K/V."""
+    Bd = _bd()
+    dev = torch.device("cuda:0")
+    r = np.random.default_rng(seed + 900)
+    pm = I.tail_padding_mask(r.integers(P // 2, P + 1, B) if lens is None else lens, P)
+    ck = I.bf16_normal(seed * 10 + 901, (1, B, P, 1, 256))
+    cv = I.bf16_normal(seed * 10 + 902, (1, B, P, 1, 256))
+    h_e = I.f32_normal(seed * 10 + 903, (B, S, W))
+    c = I.f32_normal(seed * 10 + 904, (B, W))
+    sar = np.zeros(S, np.uint8)
+    sar[0] = 1                              # the action chunk: one bidirectional block
+    we = I.layer_weights(seed * 100 + 50, W, True)
+    cache = Bd.KVCache(bf16_dev(ck), bf16_dev(cv), u8_dev(pm), P)
+    se = _dev_stream(we)
+    ws = Bd.expert_decode_workspace(se, cache, S)
+    hd = f32_dev(h_e)
+    Bd.pi_expert_layer_decode(se, cache, 0, hd, f32_dev(c), u8_dev(sar), ws)
+    torch.cuda.synchronize()
+    got = hd.cpu().numpy().astype(np.float64)
+    for b in (range(B) if check is None else check):
+        want = Y.expert_layer_decode(h_e[b:b + 1], c[b:b + 1], _host_stream(we), f64(ck[0, b:b + 1]),
+                                     f64(cv[0, b:b + 1]), pm[b:b + 1], sar)
+        assert_close(got[b:b + 1], want, f"expert decode b={b} (W={W}, P={P}, S={S})", LAYER_MAX_ABS, LAYER_MEAN_ABS)
+
+
+@pytest.mark.parametrize("seed,B,P,S,W", [(0, 2, 100, 50, 1024), (1, 3, 37, 17, 256)])
+def test_expert_layer_decode_matches_oracle(seed, B, P, S, W):
+    note(f"expert decode seed={seed} B={B} P={P} S={S} W={W}")
+    _expert_decode(seed, B, P, S, W)
+
+
+def test_expert_layer_decode_serving_shape_sampled():
+    """B = 64 robots, 816 cached slots with valid lengths U[600, 816], 50 action
+    tokens, width 1024: two samples against the oracle."""
+    note("expert decode B=64 P=816 sampled")
+    w = I.serving_decode()
+    lens = w.input_mask()[:, :816].sum(axis=1)
+    _expert_decode(2, 64, 816, 50, 1024, check=[0, 63], lens=lens)
