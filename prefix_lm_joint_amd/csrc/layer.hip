@@ -16,12 +16,11 @@
 //   * gemm_nt_kernel: C = A W^T for row-major bf16 A [M, K] and W [N, K] with fp32
 //     accumulation, on the matrix cores.  A workgroup owns a 256 (N) x 256 (M)
 //     tile (256 x 128 for few rows) with 8 waves of 64 x 128 (64 x 64); K
-//     advances 32 at a time through three LDS stages filled by direct-to-LDS
-//     buffer loads.  Each load instruction
-//     fetches one 16 x 32 operand fragment (16 rows x 64 bytes) and lands it in
-//     the exact image the fragment read expects (lane L's 16 bytes at 16 L), so
-//     every LDS read is 1 KB contiguous per wave, free of bank conflicts, and
-//     every fragment read feeds four (W) or eight (A) products.  Products are computed
+//     advances 64 at a time through two (three) LDS stages filled by
+//     direct-to-LDS buffer loads.  Each load instruction fetches 8 operand rows
+//     x 128 bytes (whole cache lines) into a row-swizzled LDS image whose
+//     fragment reads are free of bank conflicts, and every fragment read feeds
+//     four (W) or eight (A) products.  Products are computed
 //     transposed (A operand = W rows, B operand = A rows) so a lane ends with
 //     four consecutive output columns of one row for the epilogue: bf16 store,
 //     gelu, residual add into fp32, fp32 store, or the QKV scatter into the
@@ -39,21 +38,26 @@ namespace {
 
 using namespace pi_engine;
 
-constexpr int GN = 256, GK = 32;                // workgroup tile N and k step (the M tile is a parameter)
+constexpr int GN = 256, GK = 64;                // workgroup tile N and k step (the M tile is a parameter)
 constexpr int GW = 8;                           // waves: 4 along N x 2 along M
-constexpr int GSTAGES = 3;
+constexpr int kRowBytes = GK * 2;               // one operand row's k step: a full 128-byte line
+constexpr int kFragBytes = 16 * kRowBytes;      // 16 rows of the LDS image
 constexpr int kGroupM = 4;                      // m tiles per group of the tile order
-constexpr int kFragBytes = 1024;                // one 16 x 32 bf16 operand fragment
-constexpr int kWFrags = GN / 16;
 template <int GM>
 struct GTile {
-  static constexpr int AFrags = GM / 16;                          // A fragments per stage
+  static constexpr int StageBytes = (GN + GM) * kRowBytes;        // 64 KB (GM 256) or 48 KB (GM 128)
+  static constexpr int Stages = GM == 256 ? 2 : 3;                // 128 or 144 KB of LDS
+  static constexpr int WLoads = GN / 8 / GW;                      // 1 KB (8-row) loads per wave and step: W
+  static constexpr int ALoads = GM / 8 / GW;                      //                                        A
+  static constexpr int Loads = WLoads + ALoads;
   static constexpr int MI = GM / 32;                              // A fragments per wave (its GM/2 rows)
-  static constexpr int ALoads = AFrags / GW;                      // A fragment loads per wave and stage
-  static constexpr int Loads = 2 + ALoads;                        // loads per wave and stage
-  static constexpr int StageBytes = (kWFrags + AFrags) * kFragBytes;
-  static_assert(AFrags % GW == 0, "whole A fragments per wave");
+  static_assert(Loads < 16, "vmcnt field");
 };
+
+// LDS image of an operand tile: row r (128 bytes, 8 chunks of 16) holds logical
+// chunk x at physical chunk x ^ swz(r); with swz(r) = (r >> 1) & 7 the fragment
+// read (16 rows x one chunk per 16-lane group) measures no bank conflicts.
+__host__ __device__ constexpr int swz(int r) { return (r >> 1) & 7; }
 
 enum { E_BF16 = 0, E_GELU = 1, E_RESID = 2, E_F32 = 3, E_QKV = 4 };
 
@@ -102,13 +106,11 @@ __device__ __forceinline__ void gemm_store(const GemmParams& p, int64_t m, int n
   }
 }
 
-// vmcnt <= n for n = j * L (j = 0 .. 2; L loads per wave and step, at most 5);
-// expcnt and lgkmcnt left at their maxima
+// vmcnt <= n for n in {0, L} (L loads per wave and step); expcnt and lgkmcnt
+// left at their maxima
 template <int L>
 __device__ __forceinline__ void wait_vmem_le(int n) {
-  static_assert(2 * L < 16, "vmcnt field");
-  if (n >= 2 * L) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * L));
-  else if (n >= L) __builtin_amdgcn_s_waitcnt(0x0F70 | L);
+  if (n >= L) __builtin_amdgcn_s_waitcnt(0x0F70 | L);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
@@ -127,7 +129,8 @@ __device__ __forceinline__ void step_barrier() {
 template <int EPI, int GM>
 __global__ void __launch_bounds__(GW * 64) gemm_nt_kernel(GemmParams p) {
   using G = GTile<GM>;
-  __shared__ __attribute__((aligned(16))) char smem[GSTAGES * G::StageBytes];
+  constexpr int NS = G::Stages;
+  __shared__ __attribute__((aligned(16))) char smem[NS * G::StageBytes];
   // XCD-aware tile order: the workgroups of one XCD take a contiguous run of
   // tiles, and within it groups of kGroupM m tiles x all n tiles, m fastest, so
   // the ~32 workgroups an XCD runs at once cover 4 m tiles x 8 n tiles and share
@@ -144,49 +147,65 @@ __global__ void __launch_bounds__(GW * 64) gemm_nt_kernel(GemmParams p) {
   const int c = lane & 15, g = lane >> 4;
   const int wn = wave & 3, wm = wave >> 2;
   const int nk = p.K / GK;
-  // this wave's loads: W fragments 2 wave, 2 wave + 1 and A fragments wave * ALoads ..
+  // Loads: each instruction fetches 8 rows x 128 bytes (lane L: row L / 8,
+  // physical chunk L % 8, so the source chunk is (L % 8) ^ swz(row)); this wave
+  // takes W rows 8 (WLoads wave + j) .. and A rows 8 (ALoads wave + j) ..
   const i32x4 rw = make_rsrc(p.w + (int64_t)nt * GN * p.K);
   const i32x4 ra = make_rsrc(p.a);
   const uint32_t kb = (uint32_t)p.K * 2u;
-  uint32_t ow[2], oa[G::ALoads];
+  uint32_t ow[G::WLoads], oa[G::ALoads];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) ow[j] = (uint32_t)((2 * wave + j) * 16 + c) * kb + 16u * (uint32_t)g;
+  for (int j = 0; j < G::WLoads; ++j) {
+    const int r = 8 * (G::WLoads * wave + j) + (lane >> 3);
+    ow[j] = (uint32_t)r * kb + 16u * (uint32_t)((lane & 7) ^ swz(r));
+  }
 #pragma unroll
   for (int j = 0; j < G::ALoads; ++j) {
-    const int64_t am = (int64_t)mt * GM + (wave * G::ALoads + j) * 16 + c;
-    oa[j] = am < p.M ? (uint32_t)(p.amap(am) * p.K * 2 + 16 * g) : kOOB;
+    const int r = 8 * (G::ALoads * wave + j) + (lane >> 3);
+    const int64_t am = (int64_t)mt * GM + r;
+    oa[j] = am < p.M ? (uint32_t)(p.amap(am) * p.K * 2 + 16 * ((lane & 7) ^ swz(r))) : kOOB;
   }
   auto issue = [&](int i) {
-    char* st = smem + (i % GSTAGES) * G::StageBytes;
+    char* st = smem + (i % NS) * G::StageBytes;
     const int so = __builtin_amdgcn_readfirstlane(i * GK * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      pi_buffer_load_lds(rw, lds_u32(st + (2 * wave + j) * kFragBytes), 16, (int)ow[j], so, 0, 0);
+    for (int j = 0; j < G::WLoads; ++j)
+      pi_buffer_load_lds(rw, lds_u32(st + 8 * (G::WLoads * wave + j) * kRowBytes), 16, (int)ow[j], so, 0, 0);
 #pragma unroll
     for (int j = 0; j < G::ALoads; ++j)
-      pi_buffer_load_lds(ra, lds_u32(st + (kWFrags + wave * G::ALoads + j) * kFragBytes), 16, (int)oa[j], so, 0, 0);
+      pi_buffer_load_lds(ra, lds_u32(st + (GN + 8 * (G::ALoads * wave + j)) * kRowBytes), 16, (int)oa[j], so, 0,
+                         0);
   };
+  // fragment reads: lane (c, g) reads row 16 f + c, logical chunk 4 kk + g; the
+  // swizzle term of row 16 f + c is swz(c) for every f
+  uint32_t lo[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) lo[kk] = (uint32_t)(c * kRowBytes + 16 * ((4 * kk + g) ^ swz(c)));
   f32x4 acc[4][G::MI];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < G::MI; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < GSTAGES - 1 && j < nk; ++j) issue(j);
+  for (int j = 0; j < NS - 1 && j < nk; ++j) issue(j);
   for (int i = 0; i < nk; ++i) {
-    wait_vmem_le<G::Loads>(G::Loads * min(nk - 1 - i, GSTAGES - 2));   // this wave's loads of step i have landed
+    wait_vmem_le<G::Loads>(G::Loads * min(nk - 1 - i, NS - 2));   // this wave's loads of step i have landed
     step_barrier();                          // everyone's; and every wave is done with step i - 1
-    if (i + GSTAGES - 1 < nk) issue(i + GSTAGES - 1);  // into the stage of step i - 1
-    const char* st = smem + (i % GSTAGES) * G::StageBytes;
-    bf16x8 wf[4], af[G::MI];
+    if (i + NS - 1 < nk) issue(i + NS - 1);  // into the stage of step i - 1
+    const char* st = smem + (i % NS) * G::StageBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wf[j] = *reinterpret_cast<const bf16x8*>(st + (4 * wn + j) * kFragBytes + lane * 16);
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 wf[4], af[G::MI];
 #pragma unroll
-    for (int j = 0; j < G::MI; ++j)
-      af[j] = *reinterpret_cast<const bf16x8*>(st + (kWFrags + G::MI * wm + j) * kFragBytes + lane * 16);
+      for (int j = 0; j < 4; ++j)
+        wf[j] = *reinterpret_cast<const bf16x8*>(st + (4 * wn + j) * kFragBytes + lo[kk]);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int j = 0; j < G::MI; ++j)
+        af[j] = *reinterpret_cast<const bf16x8*>(st + GN * kRowBytes + (G::MI * wm + j) * kFragBytes + lo[kk]);
 #pragma unroll
-      for (int b = 0; b < G::MI; ++b) acc[a][b] = mfma16x16x32(wf[a], af[b], acc[a][b]);
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < G::MI; ++b) acc[a][b] = mfma16x16x32(wf[a], af[b], acc[a][b]);
+    }
   }
   // acc[a][b][i] = C[m = mt*GM + (GM/2) wm + 16 b + c][n = nt*256 + 64 wn + 16 a + 4 g + i]
 #pragma unroll
