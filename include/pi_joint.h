@@ -183,7 +183,8 @@ pi_status pi_joint_attn_backward(const void* q, const void* k, const void* v, co
  * Weights (device, bf16 row-major, out x in): w_qkv [2560, W], w_o [W, 2048],
  * w_up [ffn, W], w_down [W, ffn]; norm1 / norm2 fp32 [W] for a plain norm, or
  * mod1 / mod2 bf16 [2W, W] for an adaptive one (exactly one of the two pairs;
- * at most one adaptive stream).  W and ffn multiples of 256, W <= 4096.  Every
+ * at most one adaptive stream).  W and ffn multiples of 256, W <= 4096,
+ * ffn <= 65536; every activation below 2 GiB (else PI_ERR_UNSUPPORTED).  Every
  * product runs on the matrix cores with fp32 accumulation.
  * workspace (device, 256-byte aligned, required): pi_joint_layer_workspace_bytes
  * (0 = unsupported streams).  Calls sharing a workspace must not overlap.

@@ -315,7 +315,8 @@ LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, size_t a
 
 bool stream_ok(const pi_layer_stream* s) {
   if (s == nullptr || !s->w_qkv || !s->w_o || !s->w_up || !s->w_down) return false;
-  if (s->width < 256 || s->width > 4096 || s->width % 256 || s->ffn < 256 || s->ffn % 256) return false;
+  if (s->width < 256 || s->width > 4096 || s->width % 256 || s->ffn < 256 || s->ffn > 65536 || s->ffn % 256)
+    return false;
   const bool plain = s->norm1 && s->norm2, ada = s->mod1 && s->mod2;
   return plain != ada;
 }
@@ -433,9 +434,11 @@ extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const
              "pi_joint_layer_forward: mask built for B=%d N=%d, call has B=%d N=%d", mask->B, mask->N, B, N);
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_layer_forward: scale must be > 0");
   // 32-bit buffer offsets: every operand a GEMM reads stays below 2 GiB
+  const int64_t rows = (int64_t)B * (Np > Ne ? Np : Ne);
   const int64_t big = (int64_t)B * N * LHq * LD * 2;
-  const int64_t ub = (int64_t)B * (Np > Ne ? Np : Ne) * (prefix->ffn > expert->ffn ? prefix->ffn : expert->ffn) * 2;
-  PI_REQUIRE(big < 0x7FFF0000ll && ub < 0x7FFF0000ll, PI_ERR_UNSUPPORTED,
+  const int64_t ub = rows * (prefix->ffn > expert->ffn ? prefix->ffn : expert->ffn) * 2;
+  const int64_t ab = rows * (prefix->width > expert->width ? prefix->width : expert->width) * 2;
+  PI_REQUIRE(big < 0x7FFF0000ll && ub < 0x7FFF0000ll && ab < 0x7FFF0000ll, PI_ERR_UNSUPPORTED,
              "pi_joint_layer_forward: an activation exceeds 2 GiB");
   const size_t attn_bytes = pi_prefill_workspace_bytes(B, N, LHq, LHkv, LD);
   const LayerWs need = layer_ws(B, Np, Ne, prefix->width, expert->width, prefix->ffn, expert->ffn, attn_bytes, nullptr);
@@ -482,8 +485,8 @@ extern "C" pi_status pi_expert_layer_decode(const pi_layer_stream* expert, const
   PI_REQUIRE(pi::aligned16(h_e), PI_ERR_INVALID_ARG, "pi_expert_layer_decode: h_e must be 16-byte aligned");
   PI_REQUIRE(!expert->mod1 || cond, PI_ERR_INVALID_ARG, "pi_expert_layer_decode: an adaptive norm needs cond");
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_expert_layer_decode: scale must be > 0");
-  PI_REQUIRE((int64_t)B * S * expert->ffn * 2 < 0x7FFF0000ll, PI_ERR_UNSUPPORTED,
-             "pi_expert_layer_decode: an activation exceeds 2 GiB");
+  PI_REQUIRE((int64_t)B * S * expert->ffn * 2 < 0x7FFF0000ll && (int64_t)B * S * LHq * LD * 2 < 0x7FFF0000ll,
+             PI_ERR_UNSUPPORTED, "pi_expert_layer_decode: an activation exceeds 2 GiB");
   const size_t attn_bytes = pi_decode_workspace_bytes(B, S, LHq, cache->len);
   const LayerWs need = layer_ws(B, 0, S, expert->width, expert->width, expert->ffn, expert->ffn, attn_bytes, nullptr);
   PI_REQUIRE(workspace && workspace_bytes >= need.total, PI_ERR_WORKSPACE,
