@@ -451,7 +451,8 @@ extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const
                              static_cast<char*>(workspace));
   pi_status st = PI_OK;
   // modulations of the adaptive stream(s): mod1 at w.mod, mod2 after it
-  const pi_layer_stream* ada = expert->mod1 ? expert : (prefix->mod1 ? prefix : nullptr);
+  // (only a stream with tokens needs its modulation; cond may be null otherwise)
+  const pi_layer_stream* ada = (Ne > 0 && expert->mod1) ? expert : ((Np > 0 && prefix->mod1) ? prefix : nullptr);
   if (ada && (st = stream_mod(ada, cond, B, w, s)) != PI_OK) return st;
   const int wa = ada ? ada->width : 0;
   const float* mod1 = w.mod;

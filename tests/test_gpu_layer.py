@@ -83,6 +83,41 @@ def test_layer_small_widths_match_oracle(seed, B, P, F, E, Wp, We):
     _run(seed, B, s, Wp, We)
 
 
+@pytest.mark.parametrize("which", ["prefix_only", "expert_only"])
+def test_layer_one_empty_stream(which):
+    """A stream with no tokens (Np = 0 or Ne = 0): the other stream's layer alone,
+    against the oracle's joint layer with an empty stream."""
+    Bd = _bd()
+    B, W = 2, 512
+    n = 70
+    s = I.bidirectional_structure(n)
+    valid = np.ones((B, n), np.uint8)
+    valid[1, 60:] = 0
+    note(f"layer with one empty stream: {which}")
+    wp = I.layer_weights(810, W, False)
+    we = I.layer_weights(820, 256, True)
+    h = I.f32_normal(811, (B, n, W if which == "prefix_only" else 256))
+    c = I.f32_normal(812, (B, 256))
+    m = Bd.pi_mask_build(u8_dev(valid), u8_dev(s.ar), u8_dev(s.seg), 0)
+    sp, se = _dev_stream(wp), _dev_stream(we)
+    empty_p = torch.empty((B, 0, W), dtype=torch.float32, device="cuda:0")
+    empty_e = torch.empty((B, 0, 256), dtype=torch.float32, device="cuda:0")
+    hd = f32_dev(h)
+    if which == "prefix_only":
+        ws = Bd.layer_workspace(sp, se, B, n, 0, torch.device("cuda:0"))
+        Bd.pi_joint_layer_forward(sp, se, hd, empty_e, None, m, ws)
+    else:
+        ws = Bd.layer_workspace(sp, se, B, 0, n, torch.device("cuda:0"))
+        Bd.pi_joint_layer_forward(sp, se, empty_p, hd, f32_dev(c), m, ws)
+    torch.cuda.synchronize()
+    mm = M.attn_mask(valid, s.ar)
+    if which == "prefix_only":
+        want = Y.joint_layer(h, np.zeros((B, 0, 256)), c, _host_stream(wp), _host_stream(we), mm)[0]
+    else:
+        want = Y.joint_layer(np.zeros((B, 0, W)), h, c, _host_stream(wp), _host_stream(we), mm)[1]
+    assert_close(hd.cpu().numpy().astype(np.float64), want, f"layer {which}", LAYER_MAX_ABS, LAYER_MEAN_ABS)
+
+
 def test_layer_real_widths_match_oracle():
     s = I.pi05_structure(200, 16, 50)
     note("layer real widths 2048 / 1024, B=2")
@@ -123,7 +158,7 @@ def _expert_decode(seed, B, P, S, W, check=None, lens=None):
         assert_close(got[b:b + 1], want, f"expert decode b={b} (W={W}, P={P}, S={S})", LAYER_MAX_ABS, LAYER_MEAN_ABS)
 
 
-@pytest.mark.parametrize("seed,B,P,S,W", [(0, 2, 100, 50, 1024), (1, 3, 37, 17, 256)])
+@pytest.mark.parametrize("seed,B,P,S,W", [(0, 2, 100, 50, 1024), (1, 3, 37, 17, 256), (3, 1, 816, 50, 1024)])
 def test_expert_layer_decode_matches_oracle(seed, B, P, S, W):
     note(f"expert decode seed={seed} B={B} P={P} S={S} W={W}")
     _expert_decode(seed, B, P, S, W)
