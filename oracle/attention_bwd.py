@@ -21,8 +21,15 @@ Keys outside J receive nothing from that row.
 
 Also: the natural-log log-sum-exp of each row's visible scaled scores (the
 statistic a forward pass keeps for its backward), -inf for a row with none.
+
+With the rotary embedding (oracle.rope: q and k rotated at their positions
+before the scores, each pair (i, i + d/2) by an orthogonal 2x2 rotation R(p)),
+the chain rule gives the gradients of the unrotated inputs as the transposed
+rotation of the rotated inputs' gradients, and R(p)^T = R(-p).
 """
 import numpy as np
+
+from . import rope as _rope
 
 
 def lse_rows(q, k, m, scale=None) -> np.ndarray:
@@ -82,3 +89,11 @@ def masked_attention_grads(q, k, v, m, u, scale=None):
                 dq[b, i, h] = scale * (ds @ kk)
                 dk[b, idx, g, :] += scale * ds[:, None] * q[b, i, h][None, :]
     return dq, dk, dv
+
+
+def masked_attention_grads_rope(q, k, v, m, u, pos, base=10000.0, scale=None):
+    """(dq, dk, dv) of the attention with q and k rotated at positions pos [B, N]
+    (oracle.rope.joint_attention_rope), for upstream gradient u."""
+    pos = np.asarray(pos)
+    dq, dk, dv = masked_attention_grads(_rope.rope(q, pos, base), _rope.rope(k, pos, base), v, m, u, scale)
+    return _rope.rope(dq, -pos, base), _rope.rope(dk, -pos, base), dv

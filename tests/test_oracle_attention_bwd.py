@@ -100,3 +100,24 @@ def test_lse_rows_against_scipy():
                     assert abs(lse[b, i, h] - scipy.special.logsumexp(s[m[b, i]])) < 1e-12
                 else:
                     assert lse[b, i, h] == -np.inf
+
+
+def test_rope_gradients_match_finite_differences():
+    """Gradients through the rotary embedding: the transposed rotation of the
+    rotated inputs' gradients equals central differences of the rotated forward."""
+    from oracle import rope as R
+    q, k, v, u, m = _case(5, 1, 6, 2, 1, 4)
+    pos = np.array([[0, 3, 4, 9, 11, 17]])
+    dq, dk, dv = G.masked_attention_grads_rope(q, k, v, m, u, pos, base=100.0)
+    loss = lambda q_, k_, v_: float(np.sum(u * R.joint_attention_rope(q_, k_, v_, m, pos, 100.0)))
+    h = 1e-6
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            a_p = [xp if nm == name else a for nm, a in zip("qkv", (q, k, v))]
+            a_m = [xm if nm == name else a for nm, a in zip("qkv", (q, k, v))]
+            fd[idx] = (loss(*a_p) - loss(*a_m)) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-8, err_msg=name)
