@@ -146,22 +146,25 @@ pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int
  * dk = dv = 0.
  *   q, o, dout, dq  bf16 [B, L, Hq, d]    k, v, dk, dv  bf16 [B, L, Hkv, d]
  *   lse  fp32 [B, L, Hq]: the forward's log-sum-exp (pi_joint_attn_prefill's lse
- *        output for the same q, k, mask and scale, rope_base 0); o: its output.
+ *        output for the same q, k, mask, scale and rope_base); o: its output.
  *   mask built for the same B and N = L; scale as in the forward.
- * Supported: (Hq, Hkv, d) = (8, 1, 256), no rotary embedding (for a rotated
- * forward pass the rotated q and k, then rotate dq and dk back with the negated
- * positions).  bf16 matrix-core products with fp32 accumulation; P and dS are
+ * Supported: (Hq, Hkv, d) = (8, 1, 256).  rope_base: 0, or the forward's rotary
+ * base (> 1): q and k are then the unrotated inputs the forward rotated at the
+ * mask's positions, and dq, dk are the gradients of those (the rotated
+ * gradients turned back by the negated positions, R(p)^T = R(-p); one more bf16
+ * rounding).  bf16 matrix-core products with fp32 accumulation; P and dS are
  * rounded to bf16 as operands, the gradients to bf16 on output.  Outputs must
  * not overlap the inputs.  Three kernels on `stream` (row statistics, dk/dv
  * key-major, dq query-major); no atomics, so results are deterministic.
  * workspace (device, 256-byte aligned, required):
- * pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d) bytes (0 = unsupported).
+ * pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d, rope_base) bytes (0 = unsupported).
  */
-size_t pi_attn_backward_workspace_bytes(int B, int L, int Hq, int Hkv, int d);
+size_t pi_attn_backward_workspace_bytes(int B, int L, int Hq, int Hkv, int d, float rope_base);
 pi_status pi_joint_attn_backward(const void* q, const void* k, const void* v, const void* o,
                                  const void* dout, const float* lse, int B, int L, int Hq, int Hkv,
-                                 int d, float scale, const pi_mask* mask, void* dq, void* dk, void* dv,
-                                 void* workspace, size_t workspace_bytes, pi_stream stream);
+                                 int d, float scale, float rope_base, const pi_mask* mask, void* dq,
+                                 void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                 pi_stream stream);
 
 /*
  * One π0.5 joint transformer layer around the joint attention ([P3] first

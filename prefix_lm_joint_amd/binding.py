@@ -58,8 +58,8 @@ _SIGS = {
     "pi_joint_attn_prefill": (_c_i, [_c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, _c_f,
                                      ctypes.POINTER(PiMask), _c_p, _c_p, ctypes.POINTER(PiKvCache), _c_i, _c_p,
                                      ctypes.c_size_t, _c_p]),
-    "pi_attn_backward_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i]),
-    "pi_joint_attn_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f,
+    "pi_attn_backward_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i, _c_i, _c_f]),
+    "pi_joint_attn_backward": (_c_i, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_i, _c_f, _c_f,
                                       ctypes.POINTER(PiMask), _c_p, _c_p, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "pi_joint_layer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiLayerStream),
                                                          _c_i, _c_i, _c_i]),
@@ -265,13 +265,14 @@ def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
     return o
 
 
-def pi_attn_backward_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int) -> int:
-    return int(lib().pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d))
+def pi_attn_backward_workspace_bytes(B: int, L: int, Hq: int, Hkv: int, d: int, rope_base: float = 0.0) -> int:
+    return int(lib().pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d, rope_base))
 
 
-def backward_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device) -> torch.Tensor:
-    """Device workspace of pi_joint_attn_backward (the rows' statistics)."""
-    n = pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d)
+def backward_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device, rope_base: float = 0.0) -> torch.Tensor:
+    """Device workspace of pi_joint_attn_backward (the rows' statistics; with the
+    rotary embedding also the rotated Q/K)."""
+    n = pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d, rope_base)
     if n == 0:
         raise ValueError(f"pi_joint_attn_backward does not support (Hq={Hq}, Hkv={Hkv}, d={d})")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -280,9 +281,9 @@ def backward_workspace(B: int, L: int, Hq: int, Hkv: int, d: int, device) -> tor
 def pi_joint_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
                            lse: torch.Tensor, mask: Mask, workspace: torch.Tensor, scale: Optional[float] = None,
                            dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                           dv: Optional[torch.Tensor] = None, stream=None):
+                           dv: Optional[torch.Tensor] = None, stream=None, rope_base: float = 0.0):
     """Gradients (dq, dk, dv) of the prefill for upstream gradient ``dout``; ``o`` and ``lse``
-    are the prefill's output and log-sum-exp."""
+    are the prefill's output and log-sum-exp (taken with the same ``rope_base``)."""
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
     if scale is None:
@@ -293,7 +294,7 @@ def pi_joint_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o:
     _check("pi_joint_attn_backward", lib().pi_joint_attn_backward(
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(v, torch.bfloat16, "v"),
         _ptr(o, torch.bfloat16, "o"), _ptr(dout, torch.bfloat16, "dout"), _ptr(lse, torch.float32, "lse"),
-        B, L, Hq, Hkv, d, scale, ctypes.byref(mask.struct), _ptr(dq, torch.bfloat16, "dq"),
+        B, L, Hq, Hkv, d, scale, rope_base, ctypes.byref(mask.struct), _ptr(dq, torch.bfloat16, "dq"),
         _ptr(dk, torch.bfloat16, "dk"), _ptr(dv, torch.bfloat16, "dv"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream)))
     return dq, dk, dv

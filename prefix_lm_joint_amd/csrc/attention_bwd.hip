@@ -9,7 +9,9 @@
 //   dS_j = P_j (dP_j - Dr)
 //   dQ   = scale sum_j dS_j k_j,   dK_j += scale dS_j q,   dV_j += P_j dO.
 // Masked pairs get P = 0 by selection; a row with no visible key contributes
-// nothing.
+// nothing.  With the rotary embedding the kernels run on the rotated Q and K
+// and the gradients of the unrotated inputs are the rotated ones turned back by
+// the negated positions (the rotation is orthogonal).
 //
 // Kernels:
 //   * bwd_prep_kernel: Dr of every row from the bf16 O and dO (fp32 sum), and
@@ -612,17 +614,30 @@ dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __
 
 size_t stats_bytes(int B, int L) { return pi::align_up((size_t)B * L * BG * sizeof(float), 256); }
 
+// With the rotary embedding: rotated Q [B, L, 8, 256] and K [B, L, 1, 256] (bf16)
+// and the negated positions [B, L] the gradients are rotated back with.
+size_t rope_bytes(int B, int L) {
+  return pi::align_up((size_t)B * L * BG * BD * 2, 256) + pi::align_up((size_t)B * L * BD * 2, 256) +
+         pi::align_up((size_t)B * L * sizeof(int32_t), 256);
+}
+
+__global__ void negate_kernel(const int32_t* __restrict__ pos, int32_t* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = -pos[i];
+}
+
 }  // namespace
 
-extern "C" size_t pi_attn_backward_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
+extern "C" size_t pi_attn_backward_workspace_bytes(int B, int L, int Hq, int Hkv, int d, float rope_base) {
   if (B < 1 || L < 1 || Hq != BG || Hkv != 1 || d != BD) return 0;
-  return 2 * stats_bytes(B, L);
+  return 2 * stats_bytes(B, L) + (rope_base > 0.f ? rope_bytes(B, L) : 0);
 }
 
 extern "C" pi_status pi_joint_attn_backward(const void* q, const void* k, const void* v, const void* o,
                                             const void* dout, const float* lse, int B, int L, int Hq, int Hkv,
-                                            int d, float scale, const pi_mask* mask, void* dq, void* dk, void* dv,
-                                            void* workspace, size_t workspace_bytes, pi_stream stream) {
+                                            int d, float scale, float rope_base, const pi_mask* mask, void* dq,
+                                            void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                                            pi_stream stream) {
   PI_REQUIRE(q && k && v && o && dout && lse && mask && dq && dk && dv, PI_ERR_INVALID_ARG,
              "pi_joint_attn_backward: null pointer");
   PI_REQUIRE(pi::aligned16(q) && pi::aligned16(k) && pi::aligned16(v) && pi::aligned16(o) && pi::aligned16(dout) &&
@@ -637,7 +652,10 @@ extern "C" pi_status pi_joint_attn_backward(const void* q, const void* k, const 
              "pi_joint_attn_backward: unsupported (Hq=%d, Hkv=%d, d=%d); supported: (8,1,256)", Hq, Hkv, d);
   PI_REQUIRE(L <= kMaxTiles * TK, PI_ERR_UNSUPPORTED, "pi_joint_attn_backward: L=%d exceeds %d tokens", L,
              kMaxTiles * TK);
-  const size_t need = pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d);
+  PI_REQUIRE(rope_base == 0.f || (rope_base > 1.f && isfinite(rope_base)), PI_ERR_INVALID_ARG,
+             "pi_joint_attn_backward: rope_base must be 0 (off) or > 1");
+  PI_REQUIRE(rope_base == 0.f || mask->pos, PI_ERR_INVALID_ARG, "pi_joint_attn_backward: mask has no positions");
+  const size_t need = pi_attn_backward_workspace_bytes(B, L, Hq, Hkv, d, rope_base);
   PI_REQUIRE(workspace != nullptr && workspace_bytes >= need, PI_ERR_WORKSPACE,
              "pi_joint_attn_backward: needs %zu workspace bytes, got %zu", need, workspace_bytes);
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
@@ -646,11 +664,24 @@ extern "C" pi_status pi_joint_attn_backward(const void* q, const void* k, const 
   float* lse2 = static_cast<float*>(workspace);
   float* dr = reinterpret_cast<float*>(static_cast<char*>(workspace) + stats_bytes(B, L));
   const int64_t rows = (int64_t)B * L * BG;
+  pi_status st;
+  // the rotary embedding: the kernels below see the rotated Q and K; the
+  // gradients of the unrotated inputs are the rotated ones turned back by -p
+  const bool rope = rope_base > 0.f;
+  char* rw = static_cast<char*>(workspace) + 2 * stats_bytes(B, L);
+  void* q_rot = rw;
+  void* k_rot = rw + pi::align_up((size_t)B * L * BG * BD * 2, 256);
+  int32_t* neg_pos = reinterpret_cast<int32_t*>(static_cast<char*>(k_rot) + pi::align_up((size_t)B * L * BD * 2, 256));
+  if (rope) {
+    if ((st = pi::rope_rows(q, q_rot, (int64_t)B * L, BG, BD, mask->pos, rope_base, s)) != PI_OK) return st;
+    if ((st = pi::rope_rows(k, k_rot, (int64_t)B * L, 1, BD, mask->pos, rope_base, s)) != PI_OK) return st;
+    q = q_rot;
+    k = k_rot;
+  }
   const float c2 = scale * kLog2e;
   bwd_prep_kernel<<<(unsigned)((rows * 32 + 255) / 256), 256, 0, s>>>(
       static_cast<const __bf16*>(o), static_cast<const __bf16*>(dout), lse, lse2, dr, rows);
-  pi_status st = pi::check_launch("bwd_prep_kernel");
-  if (st != PI_OK) return st;
+  if ((st = pi::check_launch("bwd_prep_kernel")) != PI_OK) return st;
   const Placement pk = make_placement(B, (L + kKeyBlk - 1) / kKeyBlk);
   dkdv_kernel<<<(unsigned)placement_grid(pk), kNWk * 64, 0, s>>>(
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
@@ -663,5 +694,10 @@ extern "C" pi_status pi_joint_attn_backward(const void* q, const void* k, const 
       static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
       static_cast<const __bf16*>(dout), lse2, dr, static_cast<__bf16*>(dq), L, scale, c2, mask->tok, mask->tiles,
       mask->n_qt, mask->n_kt, mask->forbid_bits, pq);
-  return pi::check_launch("dq_kernel");
+  if ((st = pi::check_launch("dq_kernel")) != PI_OK || !rope) return st;
+  const int64_t n = (int64_t)B * L;
+  negate_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(mask->pos, neg_pos, n);
+  if ((st = pi::check_launch("negate_kernel")) != PI_OK) return st;
+  if ((st = pi::rope_rows(dq, dq, n, BG, BD, neg_pos, rope_base, s)) != PI_OK) return st;
+  return pi::rope_rows(dk, dk, n, 1, BD, neg_pos, rope_base, s);
 }

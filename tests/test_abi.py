@@ -93,12 +93,16 @@ def test_prefill_rejects_bad_arguments_before_launch():
 def test_backward_rejects_bad_arguments_before_launch():
     lib = Bd.lib()
     m = Bd.PiMask(B=2, N=64, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
-    need = lib.pi_attn_backward_workspace_bytes(2, 64, 8, 1, 256)
+    need = lib.pi_attn_backward_workspace_bytes(2, 64, 8, 1, 256, 0.0)
     assert need == 2 * (2 * 64 * 8 * 4)     # lse2 and Dr, fp32 per row of 2*64*8 rows
-    assert lib.pi_attn_backward_workspace_bytes(2, 64, 24, 24, 64) == 0     # unsupported heads
+    # with the rotary embedding also the rotated Q and K and the negated positions
+    assert lib.pi_attn_backward_workspace_bytes(2, 64, 8, 1, 256, 10000.0) == need + 2 * 64 * 8 * 256 * 2 + \
+        2 * 64 * 256 * 2 + 512
+    assert lib.pi_attn_backward_workspace_bytes(2, 64, 24, 24, 64, 0.0) == 0     # unsupported heads
     call = lambda **kw: lib.pi_joint_attn_backward(
         kw.get("q", FAKE), FAKE, FAKE, FAKE, FAKE, kw.get("lse", FAKE), kw.get("B", 2), kw.get("L", 64),
-        kw.get("Hq", 8), kw.get("Hkv", 1), kw.get("d", 256), kw.get("scale", 0.0625), ctypes.byref(m),
+        kw.get("Hq", 8), kw.get("Hkv", 1), kw.get("d", 256), kw.get("scale", 0.0625), kw.get("rope", 0.0),
+        ctypes.byref(m),
         kw.get("dq", FAKE), FAKE, FAKE, kw.get("ws", P(0x100000)), kw.get("ws_bytes", need), None)
     assert call(d=64, Hq=1) == -2            # unsupported heads
     assert call(L=65) == -1                  # mask built for another length
@@ -109,6 +113,8 @@ def test_backward_rejects_bad_arguments_before_launch():
     assert call(ws=None) == -3
     assert call(ws_bytes=need - 1) == -3
     assert call(ws=P(0x100010)) == -1        # misaligned workspace
+    assert call(rope=0.5) == -1              # rope_base must be 0 or > 1
+    assert call(rope=10000.0) == -3          # the rotary embedding needs the larger workspace
     assert b"pi_joint_attn_backward" in lib.pi_last_error()
 
 
