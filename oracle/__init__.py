@@ -32,6 +32,12 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
       concatenated KV pool, one masked softmax, split, output projection and
       FFN per stream ("π0.5 vs MM-DiT joint attention", first section; "VLA
       代码精读" §1.4, §2.7; the norm, FFN and rounding details are readings).
+  expert_flow.expert_velocity / expert_flow.expert_flow_sample
+      π0.5's action expert at its true shape driving the Euler sampler: action
+      in-projection, time embedding and time MLP conditioning the adaptive
+      norms, the expert layers against the cache layer by layer, a final
+      adaptive norm and the action out-projection ("VLA 代码精读" §1.2, §1.4,
+      §1.6; the embedding, MLP activation and final norm are readings).
   flow.velocity_net
       the random-weight stand-in velocity network.  The pages give no weights
       or exact layer for it: **parity unpinned** as a whole (only its pieces
@@ -39,4 +45,4 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
 
 Readings of points the pages leave open are listed in each docstring.
 """
-from . import bf16, mask, attention, attention_bwd, flow, layer, rope  # noqa: F401
+from . import bf16, mask, attention, attention_bwd, flow, layer, rope, expert_flow  # noqa: F401

@@ -263,3 +263,26 @@ def layer_weights(seed: int, width: int, adaptive: bool, Hq: int = 8, Hkv: int =
         w["norm1"] = (np.float32(1.0) + f32_normal(seed + 5, (W,), 0.1)).astype(np.float32)
         w["norm2"] = (np.float32(1.0) + f32_normal(seed + 6, (W,), 0.1)).astype(np.float32)
     return w
+
+
+def expert_net_weights(seed: int, width: int = 1024, action_dim: int = 32, layers: int = 18, Hq: int = 8,
+                       Hkv: int = 1, d: int = 256, ffn_mult: int = 4, bias_std: float = 0.1) -> dict:
+    """Random weights of π0.5's action expert at its true shape: action in-projection
+    w_in [W, A] with bias b_in [W], time MLP w_t1 / w_t2 [W, W] with biases b_t1 /
+    b_t2 [W], `layers` adaptive-norm expert layers (layer_weights), the final
+    norm's modulation mod_f [2W, W] and the action out-projection w_out [A, W]
+    with bias b_out [A].  Matrices are bf16 bits N(0, 1/fan_in) (mod_f
+    N(0, 0.25/W)); biases fp32 N(0, bias_std^2)."""
+    W, A = width, action_dim
+    return {
+        "w_in": bf16_normal(seed + 1, (W, A), A ** -0.5),
+        "b_in": f32_normal(seed + 2, (W,), bias_std),
+        "w_t1": bf16_normal(seed + 3, (W, W), W ** -0.5),
+        "b_t1": f32_normal(seed + 4, (W,), bias_std),
+        "w_t2": bf16_normal(seed + 5, (W, W), W ** -0.5),
+        "b_t2": f32_normal(seed + 6, (W,), bias_std),
+        "layers": [layer_weights(seed + 100 * (l + 1), W, True, Hq, Hkv, d, ffn_mult) for l in range(layers)],
+        "mod_f": bf16_normal(seed + 7, (2 * W, W), 0.5 * W ** -0.5),
+        "w_out": bf16_normal(seed + 8, (A, W), W ** -0.5),
+        "b_out": f32_normal(seed + 9, (A,), bias_std),
+    }

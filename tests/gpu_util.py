@@ -24,6 +24,12 @@ NET_MEAN_ABS = 2.5e-3
 # (up to 1.5e-3 mean-abs, 8.6e-3 max-abs); the bound is about twice that.
 LAYER_MAX_ABS = 2e-2
 LAYER_MEAN_ABS = 3e-3
+# π0.5's expert velocity at the true width through two expert layers (in- and
+# out-projections, time MLP, final adaptive norm): the same floor, measured by
+# tests/test_oracle_expert_flow.py::test_expert_velocity_tolerance_is_twice_the_fp32_floor
+# (up to 2.3e-3 mean-abs, 1.2e-2 max-abs for velocities of mean magnitude ~0.8).
+EXPERT_VEL_MAX_ABS = 3e-2
+EXPERT_VEL_MEAN_ABS = 5e-3
 
 
 def dev():
