@@ -364,6 +364,62 @@ pi_status pi_flow_sample(const pi_velocity_net* net, const pi_kv_cache* cache,
                          float* x, int B, int H, int A, int num_steps, void* workspace,
                          size_t workspace_bytes, pi_stream stream);
 
+/*
+ * π0.5's action expert at its true shape as the velocity net of the Euler
+ * sampler ([P1] §1.4: the noisy actions are projected to the expert's width,
+ * the flow time passes through the expert's own two-layer MLP whose output
+ * conditions the adaptive RMS norms, and the expert's outputs are projected back
+ * to the action dim; §1.6: the prefix is cached once and each step runs only the
+ * expert tokens against it; §1.2: the sampler).  Per evaluation at time t, with
+ * r() rounding to bf16 and W the width:
+ *   emb[j] = sin(2 pi t / p_j), emb[W/2 + j] = cos(2 pi t / p_j),  p_j = 4e-3 * 1000^(j / (W/2 - 1))
+ *   c = r(silu(r(emb) w_t1^T + b_t1)) w_t2^T + b_t2           (the same for every sample)
+ *   h = r(x) w_in^T + b_in                                     (the H action tokens)
+ *   h = layer l in the cached form against cache layer l, l < layers (pi_expert_layer_decode, cond = c)
+ *   v = r(n(h) * (1 + scale) + shift) w_out^T + b_out,  [shift | scale] = r(silu(c)) mod_f^T
+ * The embedding, the MLP's activation and the final norm are readings of the
+ * pages.  Attention scale 1/16 (head_dim 256).
+ * Weights (device): w_in bf16 [W, A], w_t1 / w_t2 bf16 [W, W], mod_f bf16 [2W, W],
+ * w_out bf16 [A, W]; biases fp32 b_in / b_t1 / b_t2 [W], b_out [A]; `layer` is a
+ * host array of `layers` expert streams of width W with adaptive norms (mod1,
+ * mod2).  W a multiple of 256 (<= 4096), 1 <= A <= 256, layers >= 1, the cache
+ * with B samples and at least `layers` layers, H <= 128.
+ */
+typedef struct pi_expert_net {
+  int32_t width, action_dim, layers;
+  const void* w_in;
+  const float* b_in;
+  const void* w_t1;
+  const float* b_t1;
+  const void* w_t2;
+  const float* b_t2;
+  const pi_layer_stream* layer;
+  const void* mod_f;
+  const void* w_out;
+  const float* b_out;
+} pi_expert_net;
+
+/* Workspace bytes of pi_expert_velocity_eval (num_steps = 1) and pi_expert_flow_sample
+ * for B samples of H actions over a cache of `len` slots (0 = unsupported). */
+size_t pi_expert_flow_workspace_bytes(const pi_expert_net* net, int B, int H, int len, int num_steps);
+
+/* One evaluation at time t (the embedding is taken at (double)t): x fp32 [B,H,A],
+ * vel fp32 [B,H,A]; suffix_ar uint8 [H] (device), the expert tokens' block
+ * starts (π0.5: the first action opens the block). */
+pi_status pi_expert_velocity_eval(const pi_expert_net* net, const pi_kv_cache* cache,
+                                  const uint8_t* suffix_ar, const float* x, float t, float* vel,
+                                  int B, int H, int A, void* workspace, size_t workspace_bytes,
+                                  pi_stream stream);
+
+/* The Euler sampler with this net: x holds the noise on entry and the actions on
+ * exit; dt = -1/num_steps, step k at t_k = 1 + k*dt (computed in double); the
+ * conditioning rows of all steps are computed once at the start; the output
+ * projection and x <- x + dt*v are fused.  1 <= num_steps <= 1000. */
+pi_status pi_expert_flow_sample(const pi_expert_net* net, const pi_kv_cache* cache,
+                                const uint8_t* suffix_ar, float* x, int B, int H, int A,
+                                int num_steps, void* workspace, size_t workspace_bytes,
+                                pi_stream stream);
+
 /* Text of a status code, and the last failure's description on this thread. */
 const char* pi_status_string(pi_status status);
 const char* pi_last_error(void);

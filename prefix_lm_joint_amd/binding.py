@@ -49,6 +49,12 @@ class PiLayerStream(ctypes.Structure):
                 ("w_down", _c_p), ("norm1", _c_p), ("norm2", _c_p), ("mod1", _c_p), ("mod2", _c_p)]
 
 
+class PiExpertNet(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32), ("action_dim", ctypes.c_int32), ("layers", ctypes.c_int32),
+                ("w_in", _c_p), ("b_in", _c_p), ("w_t1", _c_p), ("b_t1", _c_p), ("w_t2", _c_p), ("b_t2", _c_p),
+                ("layer", ctypes.POINTER(PiLayerStream)), ("mod_f", _c_p), ("w_out", _c_p), ("b_out", _c_p)]
+
+
 _SIGS = {
     "pi_mask_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i]),
     "pi_mask_build": (_c_i, [_c_p, _c_p, _c_p, ctypes.c_uint32, _c_i, _c_i, _c_p, ctypes.c_size_t,
@@ -79,6 +85,11 @@ _SIGS = {
                                 _c_p, _c_i, _c_i, _c_i, _c_p, ctypes.c_size_t, _c_p]),
     "pi_flow_sample": (_c_i, [ctypes.POINTER(PiVelocityNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_p, _c_p,
                               _c_i, _c_i, _c_i, _c_i, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_expert_flow_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiExpertNet), _c_i, _c_i, _c_i, _c_i]),
+    "pi_expert_velocity_eval": (_c_i, [ctypes.POINTER(PiExpertNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_f, _c_p,
+                                       _c_i, _c_i, _c_i, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_expert_flow_sample": (_c_i, [ctypes.POINTER(PiExpertNet), ctypes.POINTER(PiKvCache), _c_p, _c_p, _c_i, _c_i,
+                                     _c_i, _c_i, _c_p, ctypes.c_size_t, _c_p]),
     "pi_status_string": (ctypes.c_char_p, [_c_i]),
     "pi_last_error": (ctypes.c_char_p, []),
 }
@@ -491,4 +502,79 @@ def pi_flow_sample(net: Optional[VelocityNet], cache: Optional[KVCache], suffix_
         _ptr(v_const, torch.float32, "v_const"), _ptr(x, torch.float32, "x"), B, H, A, num_steps,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
         _stream(stream)))
+    return x
+
+
+# ---------------------------------------------------------------------------
+# π0.5 action expert at its true shape and the sampler driven by it
+# ---------------------------------------------------------------------------
+
+class ExpertNet:
+    """Device weights of π0.5's action expert (see pi_joint.h; keeps the tensors alive)."""
+
+    FIELDS = ("w_in", "b_in", "w_t1", "b_t1", "w_t2", "b_t2", "mod_f", "w_out", "b_out")
+
+    def __init__(self, tensors: dict, layers: list):
+        self.t = tensors
+        self.layers = layers
+        W, A = tensors["w_in"].shape
+        self._arr = (PiLayerStream * len(layers))(*[l.struct for l in layers])
+        p = {f: _ptr(tensors[f], torch.bfloat16 if f.startswith(("w_", "mod")) else torch.float32, f)
+             for f in self.FIELDS}
+        self.struct = PiExpertNet(W, A, len(layers), p["w_in"], p["b_in"], p["w_t1"], p["b_t1"], p["w_t2"],
+                                  p["b_t2"], ctypes.cast(self._arr, ctypes.POINTER(PiLayerStream)), p["mod_f"],
+                                  p["w_out"], p["b_out"])
+        self.width, self.action_dim = W, A
+
+    @classmethod
+    def from_numpy(cls, weights: dict, device):
+        """``weights``: inputs.expert_net_weights (bf16 bits as uint16, vectors float32)."""
+        import numpy as np
+
+        def up(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(device)
+            return torch.from_numpy(a.astype(np.float32)).to(device)
+
+        t = {f: up(weights[f]) for f in cls.FIELDS}
+        layers = [LayerStream(**{k: up(v) for k, v in lw.items()}) for lw in weights["layers"]]
+        return cls(t, layers)
+
+
+def pi_expert_flow_workspace_bytes(net: ExpertNet, B: int, H: int, length: int, num_steps: int) -> int:
+    return int(lib().pi_expert_flow_workspace_bytes(ctypes.byref(net.struct), B, H, length, num_steps))
+
+
+def expert_flow_workspace(net: ExpertNet, cache: KVCache, H: int, num_steps: int) -> torch.Tensor:
+    n = pi_expert_flow_workspace_bytes(net, cache.struct.B, H, cache.struct.len, num_steps)
+    if n == 0:
+        raise ValueError("pi_expert_flow_sample does not support this net / shape")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+
+
+def pi_expert_velocity_eval(net: ExpertNet, cache: KVCache, suffix_ar: torch.Tensor, x: torch.Tensor, t: float,
+                            vel: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    B, H, A = x.shape
+    if vel is None:
+        vel = torch.empty_like(x)
+    if workspace is None:
+        workspace = expert_flow_workspace(net, cache, H, 1)
+    _check("pi_expert_velocity_eval", lib().pi_expert_velocity_eval(
+        ctypes.byref(net.struct), ctypes.byref(cache.struct), _ptr(suffix_ar, torch.uint8, "suffix_ar"),
+        _ptr(x, torch.float32, "x"), t, _ptr(vel, torch.float32, "vel"), B, H, A,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return vel
+
+
+def pi_expert_flow_sample(net: ExpertNet, cache: KVCache, suffix_ar: torch.Tensor, x: torch.Tensor,
+                          num_steps: int = 10, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Euler sampler with the expert net: x [B, H, A] fp32 holds the noise and ends as the actions."""
+    B, H, A = x.shape
+    if workspace is None:
+        workspace = expert_flow_workspace(net, cache, H, num_steps)
+    _check("pi_expert_flow_sample", lib().pi_expert_flow_sample(
+        ctypes.byref(net.struct), ctypes.byref(cache.struct), _ptr(suffix_ar, torch.uint8, "suffix_ar"),
+        _ptr(x, torch.float32, "x"), B, H, A, num_steps, _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream)))
     return x

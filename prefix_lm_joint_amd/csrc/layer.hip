@@ -404,6 +404,21 @@ pi_status stream_mod(const pi_layer_stream* sw, const float* cond, int B, const 
   return PI_OK;
 }
 
+// The expert stream's layer in the cached form: norm 1, QKV, the suffix decode
+// against cache layer `layer`, output projection, norm 2 and FFN (h updated in place).
+pi_status expert_layer(const pi_layer_stream* sw, const pi_kv_cache* cache, int layer, float* h, const float* cond,
+                       const uint8_t* suffix_ar, int B, int S, float scale, const LayerWs& w, hipStream_t s) {
+  pi_status st = PI_OK;
+  if (sw->mod1 && (st = stream_mod(sw, cond, B, w, s)) != PI_OK) return st;
+  const float* mod1 = w.mod;
+  const float* mod2 = w.mod + (size_t)B * 2 * sw->width;
+  if ((st = stream_qkv(sw, h, B, S, S, 0, mod1, w, s)) != PI_OK) return st;
+  st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, LHq, scale, 0.f, w.o, w.attn, w.attn_bytes,
+                             s);
+  if (st != PI_OK) return st;
+  return stream_out(sw, h, B, S, S, 0, mod2, w, s);
+}
+
 }  // namespace
 
 extern "C" size_t pi_joint_layer_workspace_bytes(const pi_layer_stream* prefix, const pi_layer_stream* expert, int B,
@@ -494,16 +509,292 @@ extern "C" pi_status pi_expert_layer_decode(const pi_layer_stream* expert, const
              "pi_expert_layer_decode: needs %zu workspace bytes, got %zu", need.total, workspace_bytes);
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_expert_layer_decode: workspace must be 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const LayerWs w = layer_ws(B, 0, S, expert->width, expert->width, expert->ffn, expert->ffn, attn_bytes,
                              static_cast<char*>(workspace));
-  pi_status st = PI_OK;
-  if (expert->mod1 && (st = stream_mod(expert, cond, B, w, s)) != PI_OK) return st;
-  const float* mod1 = w.mod;
-  const float* mod2 = w.mod + (size_t)B * 2 * expert->width;
-  if ((st = stream_qkv(expert, h_e, B, S, S, 0, mod1, w, s)) != PI_OK) return st;
-  st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, LHq, scale, 0.f, w.o, w.attn, w.attn_bytes,
-                             stream);
+  return expert_layer(expert, cache, layer, h_e, cond, suffix_ar, B, S, scale, w, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// π0.5's action expert at its true shape driving the Euler sampler ("VLA 代码精读"
+// §1.2, §1.4, §1.6):
+//   c_k = r(silu(r(emb(t_k)) W_t1^T + b_t1)) W_t2^T + b_t2     (one row per step, every sample)
+//   h = r(x) W_in^T + b_in;  h = expert_layer_l(h, c_k) for l < layers (cache layer l)
+//   v = r(final adaptive norm of h) W_out^T + b_out;  x += dt v
+// emb(t)[j] = sin(2 pi t / p_j), emb(t)[W/2 + j] = cos(2 pi t / p_j), with
+// p_j = 4e-3 * 1000^(j / (W/2 - 1)).  The embedding, the MLP's activation and the
+// final norm are readings of the pages.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Row k of the time embedding at t = t0 + k*dt (double precision, then bf16).
+__global__ void time_embed_kernel(double t0, double dt, int n, int W, __bf16* __restrict__ emb) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = W / 2;
+  if (i >= n * half) return;
+  const int k = i / half, j = i % half;
+  const double t = t0 + k * dt;
+  const double period = 4e-3 * pow(1000.0, (double)j / (double)(half - 1));
+  const double ang = 6.283185307179586 * t / period;
+  emb[(int64_t)k * W + j] = f2bf((float)sin(ang));
+  emb[(int64_t)k * W + half + j] = f2bf((float)cos(ang));
+}
+
+// in fp32 [n, W] + bias: act = 1: bf16 silu(.) into out_b [n, W]; act = 0: fp32
+// into out_f, row k repeated `rep` times (rows k*rep .. k*rep + rep - 1).
+__global__ void bias_act_kernel(const float* __restrict__ in, const float* __restrict__ bias, int n, int W, int act,
+                                __bf16* __restrict__ out_b, float* __restrict__ out_f, int rep) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)n * W) return;
+  const int k = (int)(i / W), j = (int)(i % W);
+  const float y = in[i] + bias[j];
+  if (act) {
+    out_b[i] = f2bf(y / (1.0f + expf(-y)));
+  } else {
+    for (int r = 0; r < rep; ++r) out_f[((int64_t)k * rep + r) * W + j] = y;
+  }
+}
+
+// h[m][n] = sum_a r(x[m][a]) w_in[n][a] + b_in[n]  (A <= 256; one row per block.y)
+__global__ void __launch_bounds__(256)
+action_embed_kernel(const float* __restrict__ x, const __bf16* __restrict__ w_in, const float* __restrict__ b_in,
+                    float* __restrict__ h, int A, int W) {
+  __shared__ float xs[256];
+  const int64_t m = blockIdx.y;
+  if (threadIdx.x < A) xs[threadIdx.x] = bf2f(f2bf(x[m * A + threadIdx.x]));
+  __syncthreads();
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= W) return;
+  const __bf16* wr = w_in + (int64_t)n * A;
+  float acc = 0.f;
+  for (int a = 0; a < A; ++a) acc += xs[a] * bf2f(wr[a]);
+  h[m * W + n] = acc + b_in[n];
+}
+
+// dst [rows_pad, K] = src [rows, K] with zero rows after (one thread per 8 elements)
+__global__ void pad_rows_kernel(const __bf16* __restrict__ src, __bf16* __restrict__ dst, int rows, int rows_pad,
+                                int K) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int k8 = K / 8;
+  if (i >= (int64_t)rows_pad * k8) return;
+  const int r = (int)(i / k8), k = (int)(i % k8) * 8;
+  *reinterpret_cast<bf16x8*>(dst + (int64_t)r * K + k) =
+      r < rows ? *reinterpret_cast<const bf16x8*>(src + (int64_t)r * K + k) : bf16x8{};
+}
+
+// v = vel[m][a] + b_out[a] (vel fp32 [M, 256]); euler: x[m][a] += dt v, else out[m][a] = v
+__global__ void velocity_out_kernel(const float* __restrict__ vel, const float* __restrict__ b_out,
+                                    float* __restrict__ x, float* __restrict__ out, int64_t M, int A, float dt,
+                                    int euler) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= M * A) return;
+  const int64_t m = i / A;
+  const int a = (int)(i % A);
+  const float v = vel[m * 256 + a] + b_out[a];
+  if (euler) x[i] += dt * v;
+  else out[i] = v;
+}
+
+constexpr int kMaxSteps = 1000;
+
+struct ExpertFlowWs {
+  LayerWs layer;
+  __bf16 *emb, *u, *wout;
+  float *t1, *cond, *h, *vel;
+  size_t total;
+};
+
+ExpertFlowWs expert_flow_ws(int W, int F, int B, int H, int n_steps, size_t attn_bytes, char* base) {
+  ExpertFlowWs w{};
+  w.layer = layer_ws(B, 0, H, W, W, F, F, attn_bytes, base);
+  size_t off = w.layer.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = pi::align_up(off + bytes, 256);
+    return base ? base + at : nullptr;
+  };
+  const int64_t M = (int64_t)B * H;
+  w.emb = reinterpret_cast<__bf16*>(take((size_t)n_steps * W * 2));
+  w.u = reinterpret_cast<__bf16*>(take((size_t)n_steps * W * 2));
+  w.wout = reinterpret_cast<__bf16*>(take((size_t)256 * W * 2));
+  w.t1 = reinterpret_cast<float*>(take((size_t)n_steps * W * 4));
+  w.cond = reinterpret_cast<float*>(take((size_t)n_steps * B * W * 4));
+  w.h = reinterpret_cast<float*>(take((size_t)M * W * 4));
+  w.vel = reinterpret_cast<float*>(take((size_t)M * 256 * 4));
+  w.total = off;
+  return w;
+}
+
+int expert_ffn_max(const pi_expert_net* n) {
+  int f = 256;
+  for (int l = 0; l < n->layers; ++l) f = n->layer[l].ffn > f ? n->layer[l].ffn : f;
+  return f;
+}
+
+bool expert_net_ok(const pi_expert_net* n) {
+  if (n == nullptr || n->layer == nullptr || n->layers < 1) return false;
+  if (n->width < 256 || n->width > 4096 || n->width % 256 || n->action_dim < 1 || n->action_dim > 256) return false;
+  if (!n->w_in || !n->b_in || !n->w_t1 || !n->b_t1 || !n->w_t2 || !n->b_t2 || !n->mod_f || !n->w_out || !n->b_out)
+    return false;
+  // matrices read 16 bytes per lane (the GEMMs' buffer loads, the out-projection's padding copy)
+  if (!pi::aligned16(n->w_t1) || !pi::aligned16(n->w_t2) || !pi::aligned16(n->mod_f) || !pi::aligned16(n->w_out))
+    return false;
+  for (int l = 0; l < n->layers; ++l) {
+    const pi_layer_stream& sl = n->layer[l];
+    if (!stream_ok(&sl) || !sl.mod1 || sl.width != n->width) return false;
+    if (!pi::aligned16(sl.w_qkv) || !pi::aligned16(sl.w_o) || !pi::aligned16(sl.w_up) || !pi::aligned16(sl.w_down) ||
+        !pi::aligned16(sl.mod1) || !pi::aligned16(sl.mod2))
+      return false;
+  }
+  return true;
+}
+
+// Conditioning rows c_k for t_k = t0 + k*dt, k < n, each repeated for the B samples.
+pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, int B, const ExpertFlowWs& w,
+                      hipStream_t s) {
+  const int W = n->width;
+  const int half = W / 2;
+  time_embed_kernel<<<(unsigned)((steps * half + 255) / 256), 256, 0, s>>>(t0, dt, steps, W, w.emb);
+  pi_status st = pi::check_launch("time_embed_kernel");
   if (st != PI_OK) return st;
-  return stream_out(expert, h_e, B, S, S, 0, mod2, w, s);
+  for (int j = 0; j < 2; ++j) {
+    GemmParams p{};
+    p.a = j == 0 ? w.emb : w.u;
+    p.w = static_cast<const __bf16*>(j == 0 ? n->w_t1 : n->w_t2);
+    p.M = steps;
+    p.N = W;
+    p.K = W;
+    p.amap = RowMap{steps, 0, 0};
+    p.out = w.t1;
+    if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
+    const int64_t cnt = (int64_t)steps * W;
+    bias_act_kernel<<<(unsigned)((cnt + 255) / 256), 256, 0, s>>>(w.t1, j == 0 ? n->b_t1 : n->b_t2, steps, W,
+                                                                 j == 0 ? 1 : 0, w.u, w.cond, B);
+    if ((st = pi::check_launch("bias_act_kernel")) != PI_OK) return st;
+  }
+  return PI_OK;
+}
+
+// One velocity evaluation with conditioning rows `cond` [B, W]: into `vel` (euler
+// = false) or fused x += dt v.
+pi_status expert_velocity(const pi_expert_net* n, const pi_kv_cache* cache, const uint8_t* suffix_ar, float* x,
+                          const float* cond, float* vel, float dt, bool euler, int B, int H, const ExpertFlowWs& w,
+                          hipStream_t s) {
+  const int W = n->width, A = n->action_dim;
+  const int64_t M = (int64_t)B * H;
+  action_embed_kernel<<<dim3((unsigned)((W + 255) / 256), (unsigned)M), 256, 0, s>>>(
+      x, static_cast<const __bf16*>(n->w_in), n->b_in, w.h, A, W);
+  pi_status st = pi::check_launch("action_embed_kernel");
+  if (st != PI_OK) return st;
+  const float scale = 1.0f / 16.0f;   // 1 / sqrt(head_dim 256)
+  for (int l = 0; l < n->layers; ++l)
+    if ((st = expert_layer(&n->layer[l], cache, l, w.h, cond, suffix_ar, B, H, scale, w.layer, s)) != PI_OK)
+      return st;
+  // final adaptive norm: [shift | scale] = r(silu(c)) mod_f^T into the layer's first modulation slot
+  const int64_t nb = (int64_t)B * W;
+  silu_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(cond, w.layer.sc, nb);
+  if ((st = pi::check_launch("silu_kernel")) != PI_OK) return st;
+  GemmParams pm{};
+  pm.a = w.layer.sc;
+  pm.w = static_cast<const __bf16*>(n->mod_f);
+  pm.M = B;
+  pm.N = 2 * W;
+  pm.K = W;
+  pm.amap = RowMap{B, 0, 0};
+  pm.out = w.layer.mod;
+  if ((st = launch_gemm<E_F32>(pm, s)) != PI_OK) return st;
+  norm_kernel<<<(unsigned)((M + 3) / 4), 256, 0, s>>>(w.h, w.layer.a, M, W, nullptr, w.layer.mod, H);
+  if ((st = pi::check_launch("norm_kernel")) != PI_OK) return st;
+  GemmParams po{};
+  po.a = w.layer.a;
+  po.w = w.wout;
+  po.M = (int)M;
+  po.N = 256;
+  po.K = W;
+  po.amap = RowMap{(int)M, 0, 0};
+  po.out = w.vel;
+  if ((st = launch_gemm<E_F32>(po, s)) != PI_OK) return st;
+  velocity_out_kernel<<<(unsigned)((M * A + 255) / 256), 256, 0, s>>>(w.vel, n->b_out, x, vel, M, A, dt,
+                                                                       euler ? 1 : 0);
+  return pi::check_launch("velocity_out_kernel");
+}
+
+// Shared checks of the two entry points; fills *w on success.
+pi_status expert_setup(const pi_expert_net* n, const pi_kv_cache* cache, const uint8_t* suffix_ar, const float* x,
+                       int B, int H, int A, int steps, void* workspace, size_t workspace_bytes, ExpertFlowWs* w,
+                       const char* who) {
+  PI_REQUIRE(expert_net_ok(n), PI_ERR_INVALID_ARG,
+             "%s: the net needs every weight (matrices 16-byte aligned), 1 <= layers, a width that is a multiple "
+             "of 256 (<= 4096), action_dim in [1, 256], and layers of that width with adaptive norms (mod1 + mod2)",
+             who);
+  PI_REQUIRE(cache && suffix_ar && x, PI_ERR_INVALID_ARG, "%s: null pointer", who);
+  PI_REQUIRE(A == n->action_dim, PI_ERR_INVALID_ARG, "%s: A=%d but the net's action_dim is %d", who, A,
+             n->action_dim);
+  PI_REQUIRE(B >= 1 && H >= 1 && H <= 128, PI_ERR_INVALID_ARG, "%s: B=%d H=%d (1 <= H <= 128)", who, B, H);
+  PI_REQUIRE(steps >= 1 && steps <= kMaxSteps, PI_ERR_INVALID_ARG, "%s: num_steps=%d (1..%d)", who, steps,
+             kMaxSteps);
+  PI_REQUIRE(cache->B == B && cache->Hkv == LHkv && cache->d == LD && cache->layers >= n->layers, PI_ERR_INVALID_ARG,
+             "%s: the cache must have B=%d, one KV head of d=256 and at least %d layers", who, B, n->layers);
+  const int F = expert_ffn_max(n);
+  PI_REQUIRE((int64_t)B * H * F * 2 < 0x7FFF0000ll && (int64_t)B * H * LHq * LD * 2 < 0x7FFF0000ll &&
+                 (int64_t)B * H * n->width * 4 < 0x7FFF0000ll,
+             PI_ERR_UNSUPPORTED, "%s: an activation exceeds 2 GiB", who);
+  const size_t attn_bytes = pi_decode_workspace_bytes(B, H, LHq, cache->len);
+  const ExpertFlowWs need = expert_flow_ws(n->width, F, B, H, steps, attn_bytes, nullptr);
+  PI_REQUIRE(workspace && workspace_bytes >= need.total, PI_ERR_WORKSPACE, "%s: needs %zu workspace bytes, got %zu",
+             who, need.total, workspace_bytes);
+  PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
+             "%s: workspace must be 256-byte aligned", who);
+  *w = expert_flow_ws(n->width, F, B, H, steps, attn_bytes, static_cast<char*>(workspace));
+  return PI_OK;
+}
+
+pi_status expert_pad_out(const pi_expert_net* n, const ExpertFlowWs& w, hipStream_t s) {
+  const int64_t cnt = (int64_t)256 * (n->width / 8);
+  pad_rows_kernel<<<(unsigned)((cnt + 255) / 256), 256, 0, s>>>(static_cast<const __bf16*>(n->w_out), w.wout,
+                                                                 n->action_dim, 256, n->width);
+  return pi::check_launch("pad_rows_kernel");
+}
+
+}  // namespace
+
+extern "C" size_t pi_expert_flow_workspace_bytes(const pi_expert_net* net, int B, int H, int len, int num_steps) {
+  if (!expert_net_ok(net) || B < 1 || H < 1 || H > 128 || len < 0 || num_steps < 1 || num_steps > kMaxSteps)
+    return 0;
+  return expert_flow_ws(net->width, expert_ffn_max(net), B, H, num_steps, pi_decode_workspace_bytes(B, H, LHq, len),
+                        nullptr)
+      .total;
+}
+
+extern "C" pi_status pi_expert_velocity_eval(const pi_expert_net* net, const pi_kv_cache* cache,
+                                             const uint8_t* suffix_ar, const float* x, float t, float* vel, int B,
+                                             int H, int A, void* workspace, size_t workspace_bytes, pi_stream stream) {
+  ExpertFlowWs w;
+  pi_status st = expert_setup(net, cache, suffix_ar, x, B, H, A, 1, workspace, workspace_bytes, &w,
+                              "pi_expert_velocity_eval");
+  if (st != PI_OK) return st;
+  PI_REQUIRE(vel != nullptr, PI_ERR_INVALID_ARG, "pi_expert_velocity_eval: null vel");
+  PI_REQUIRE(isfinite(t), PI_ERR_INVALID_ARG, "pi_expert_velocity_eval: t must be finite");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = expert_pad_out(net, w, s)) != PI_OK) return st;
+  if ((st = expert_cond(net, (double)t, 0.0, 1, B, w, s)) != PI_OK) return st;
+  return expert_velocity(net, cache, suffix_ar, const_cast<float*>(x), w.cond, vel, 0.f, false, B, H, w, s);
+}
+
+extern "C" pi_status pi_expert_flow_sample(const pi_expert_net* net, const pi_kv_cache* cache,
+                                           const uint8_t* suffix_ar, float* x, int B, int H, int A, int num_steps,
+                                           void* workspace, size_t workspace_bytes, pi_stream stream) {
+  ExpertFlowWs w;
+  pi_status st = expert_setup(net, cache, suffix_ar, x, B, H, A, num_steps, workspace, workspace_bytes, &w,
+                              "pi_expert_flow_sample");
+  if (st != PI_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const double dt = -1.0 / num_steps;
+  if ((st = expert_pad_out(net, w, s)) != PI_OK) return st;
+  if ((st = expert_cond(net, 1.0, dt, num_steps, B, w, s)) != PI_OK) return st;
+  for (int k = 0; k < num_steps; ++k) {
+    st = expert_velocity(net, cache, suffix_ar, x, w.cond + (size_t)k * B * net->width, nullptr, (float)dt, true, B, H,
+                         w, s);
+    if (st != PI_OK) return st;
+  }
+  return PI_OK;
 }

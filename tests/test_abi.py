@@ -226,3 +226,43 @@ def test_mask_build_rejects_bad_arguments_before_launch():
     assert lib.pi_mask_build(FAKE, FAKE, None, 0, 0, 100, P(0x100000), need, ctypes.byref(out), None) == -1
     assert lib.pi_mask_build(FAKE, FAKE, None, 1 << 16, 2, 100, P(0x100000), need, ctypes.byref(out), None) == -1
     assert lib.pi_mask_build(FAKE, FAKE, None, 0, 2, 100, P(0x100010), need, ctypes.byref(out), None) == -1
+
+
+@needs_lib
+def test_expert_sampler_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 2, 816, 1, 256, 816)
+    ada = Bd.PiLayerStream(1024, 4096, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
+    plain = Bd.PiLayerStream(1024, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    narrow = Bd.PiLayerStream(512, 2048, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE)
+
+    def net(layers, width=1024, A=32, n=None):
+        arr = (Bd.PiLayerStream * len(layers))(*layers)
+        return Bd.PiExpertNet(width, A, len(layers) if n is None else n, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              ctypes.cast(arr, ctypes.POINTER(Bd.PiLayerStream)), FAKE, FAKE, FAKE), arr
+
+    good, keep = net([ada] * 18)
+    need = lib.pi_expert_flow_workspace_bytes(ctypes.byref(good), 2, 50, 816, 10)
+    need1 = lib.pi_expert_flow_workspace_bytes(ctypes.byref(good), 2, 50, 816, 1)
+    assert need > need1 > 2 * 50 * 4096 * 2           # at least the FFN activations
+    for bad in (net([plain] * 18), net([ada] * 17 + [narrow]), net([ada] * 18, width=1000), net([ada] * 18, A=0),
+                net([ada] * 18, A=257)):
+        assert lib.pi_expert_flow_workspace_bytes(ctypes.byref(bad[0]), 2, 50, 816, 10) == 0
+    assert lib.pi_expert_flow_workspace_bytes(ctypes.byref(good), 2, 129, 816, 10) == 0     # H > 128
+    assert lib.pi_expert_flow_workspace_bytes(ctypes.byref(good), 2, 50, 816, 1001) == 0    # too many steps
+    samp = lambda n=good, **kw: lib.pi_expert_flow_sample(
+        ctypes.byref(n), ctypes.byref(kw.get("cache", cache)), FAKE, FAKE, kw.get("B", 2), 50, kw.get("A", 32),
+        kw.get("steps", 10), kw.get("ws", P(0x100000)), kw.get("ws_bytes", need), None)
+    assert samp(B=3) == -1                              # cache built for another batch
+    assert samp(A=16) == -1                             # action dim differs from the net's
+    assert samp(steps=0) == -1
+    assert samp(ws=None) == -3 and samp(ws_bytes=need - 1) == -3
+    assert samp(ws=P(0x100010)) == -1                   # misaligned workspace
+    deep, keep2 = net([ada] * 19)
+    assert samp(n=deep, ws_bytes=1 << 40) == -1         # more layers than the cache
+    assert b"pi_expert_flow_sample" in lib.pi_last_error()
+    ev = lambda **kw: lib.pi_expert_velocity_eval(
+        ctypes.byref(good), ctypes.byref(cache), FAKE, FAKE, kw.get("t", 0.5), kw.get("vel", FAKE), 2, 50, 32,
+        P(0x100000), kw.get("ws_bytes", need1), None)
+    assert ev(vel=None) == -1 and ev(t=float("nan")) == -1 and ev(ws_bytes=need1 - 1) == -3
+    assert b"pi_expert_velocity_eval" in lib.pi_last_error()
