@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward",
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward", "sampler",
                                       "layer", "expert"],
                    default=None,
                    help="run just one leg (for profiling)")
@@ -260,7 +260,7 @@ def expert_decode_leg(cx: Ctx, iters: int):
     ms = cx.time_ms(lambda: Bd.pi_expert_layer_decode(se, cache, 0, h, c, sar, ws), iters)
     lens = pm.sum(axis=1)
     pairs = int(S * 8 * lens.sum() + B * 8 * S * S)      # every action token sees the valid slots and the chunk
-    gemm = 2.0 * B * S * W * (2560 + 1024 + 2 * 4 * W) + 2.0 * 2 * B * W * 2 * W
+    gemm = 2.0 * B * S * W * (2560 + 2048 + 2 * 4 * W) + 2.0 * 2 * B * W * 2 * W
     flops = gemm + 4.0 * 256 * pairs
     weights = 2 * (2560 * W + W * 2048 + 2 * 4 * W * W + 2 * 2 * W * W)
     byts = weights + int(lens.sum()) * 256 * 2 * 2 + B * S * W * 4 * 2
@@ -269,6 +269,56 @@ def expert_decode_leg(cx: Ctx, iters: int):
             "achieved_tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16_FLOPS,
             "algorithmic_bytes": byts, "achieved_gbs": byts / (ms * 1e-3) / 1e9,
             "kernel": "norm_kernel + gemm_nt_kernel + decode_kernel (+ combine)"}
+
+
+def expert_sampler_leg(cx: Ctx, iters: int, B: int):
+    """π0.5's control step after the prefix: the Euler sampler with the action expert at
+    its true shape (pi_expert_flow_sample: 18 expert layers of width 1024, FFN 4096,
+    adaptive norms from the time MLP, 10 steps) for B robots over an 816-slot cache
+    (valid U[600, 816] for B > 1, all valid for B = 1), 50 action tokens of dim 32.
+    Weights and cache are drawn on the device from a seeded generator (bench-only
+    inputs; parity is covered by the tests)."""
+    torch, Bd, I, np = cx.torch, cx.Bd, cx.I, cx.np
+    w = I.serving_decode()
+    P, H, A, W, F, L, N = w.structure.n_prefix, 50, 32, 1024, 4096, w.layers, w.steps
+    pm = w.input_mask()[:B, :P] if B > 1 else np.ones((1, P), np.uint8)
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(w.seed_base + 71 + B)
+
+    def bf(shape, std):
+        return (torch.randn(shape, generator=gen, device=cx.dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    def f32(shape, std):
+        return torch.randn(shape, generator=gen, device=cx.dev, dtype=torch.float32) * std
+
+    ck = bf((L, B, P, 1, 256), 1.0)
+    cv = bf((L, B, P, 1, 256), 1.0)
+    cache = Bd.KVCache(ck, cv, cx.u8(pm), P)
+    layers = [Bd.LayerStream(bf((2560, W), W ** -0.5), bf((W, 2048), 2048 ** -0.5), bf((F, W), W ** -0.5),
+                             bf((W, F), F ** -0.5), None, None, bf((2 * W, W), 0.5 * W ** -0.5),
+                             bf((2 * W, W), 0.5 * W ** -0.5)) for _ in range(L)]
+    t = {"w_in": bf((W, A), A ** -0.5), "b_in": f32((W,), 0.1), "w_t1": bf((W, W), W ** -0.5),
+         "b_t1": f32((W,), 0.1), "w_t2": bf((W, W), W ** -0.5), "b_t2": f32((W,), 0.1),
+         "mod_f": bf((2 * W, W), 0.5 * W ** -0.5), "w_out": bf((A, W), W ** -0.5), "b_out": f32((A,), 0.1)}
+    net = Bd.ExpertNet(t, layers)
+    sar = np.zeros(H, np.uint8)
+    sar[0] = 1
+    sar = cx.u8(sar)
+    noise = f32((B, H, A), 1.0)
+    x = torch.empty_like(noise)
+    ws = Bd.expert_flow_workspace(net, cache, H, N)
+    ms = cx.time_ms(lambda: (x.copy_(noise), Bd.pi_expert_flow_sample(net, cache, sar, x, N, ws)), iters)
+    lens = pm.sum(axis=1)
+    M = B * H
+    pairs = int(H * 8 * lens.sum() + B * 8 * H * H)
+    per_layer = 2.0 * M * W * (2560 + 2048 + 2 * F) + 2.0 * 2 * B * W * 2 * W + 4.0 * 256 * pairs
+    per_step = L * per_layer + 2.0 * M * A * W * 2 + 2.0 * B * W * 2 * W
+    flops = N * per_step + 2.0 * 2 * N * W * W
+    return {"workload": "pi05_expert_sampler", "B": B, "slots": P, "actions": H, "action_dim": A, "width": W,
+            "ffn": F, "layers": L, "euler_steps": N, "ms_per_control_step": ms,
+            "control_steps_per_s": 1e3 / ms, "robot_steps_per_s": B * 1e3 / ms,
+            "tflop_per_control_step": flops / 1e12, "achieved_tflops": flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16_FLOPS}
 
 
 def decode_kernel_leg(cx: Ctx, iters: int):
@@ -544,6 +594,11 @@ def main():
         log("expert layer, cached form (B=64, 816 slots, 50 tokens)")
         kernels["expert"] = expert_decode_leg(cx, max(5, args.kernel_iters // 5))
         log(str(kernels["expert"]))
+    if args.only in (None, "sampler"):
+        for B in (1, 64):
+            log(f"pi05 expert sampler leg (B={B}, 18 layers, 10 Euler steps)")
+            kernels[f"sampler_b{B}"] = expert_sampler_leg(cx, 3, B)
+            log(str(kernels[f"sampler_b{B}"]))
     if args.only in (None, "backward"):
         log("attention backward leg (pi05 B=32 L=962)")
         kernels["backward"] = backward_leg(cx, max(5, args.kernel_iters // 5))
@@ -609,6 +664,12 @@ def main():
                                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                                 "frac": kernels["expert"]["mfma_frac"], "us_per_layer": kernels["expert"]["us_per_layer"],
                                 "achieved_gbs": kernels["expert"]["achieved_gbs"]},
+        "pi05_expert_sampler": {
+            "what": "control step after the cached prefix: 10 Euler steps of the true-shape action expert "
+                    "(18 layers, width 1024, FFN 4096, adaptive norms), 50 actions of dim 32, 816-slot cache",
+            **{f"B{b}": {k: kernels[f"sampler_b{b}"][k] for k in ("ms_per_control_step", "robot_steps_per_s",
+                                                                 "achieved_tflops", "mfma_frac")}
+               for b in (1, 64)}},
         "breakdown_us": result["breakdown_us"],
         "cpu_baseline": cpu,
     }

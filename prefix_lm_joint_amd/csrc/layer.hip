@@ -263,9 +263,76 @@ __global__ void silu_kernel(const float* __restrict__ c, __bf16* __restrict__ y,
   y[i] = f2bf(x / (1.0f + expf(-x)));
 }
 
-// 256 x 256 tiles once the rows alone give a few hundred workgroups, else 256 x 128.
+// C = A W^T for few rows (M <= kSmallM): a workgroup owns 16 output columns of up
+// to 64 rows and its 16 waves split the contraction, each over a contiguous range
+// of 32-wide k steps, four steps of fragment loads in flight (16 bytes per lane
+// straight from the row-major operands); the partial tiles are summed through
+// LDS and the sum goes through the same epilogues as the tiled kernel.  With few
+// rows the tiled kernel would have a handful of workgroups each walking all of K.
+constexpr int kSmallM = 256, kSmallWaves = 16, kSmallKB = 4;
+
+template <int EPI>
+__global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams p) {
+  __shared__ float part[kSmallWaves][64 * 16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int64_t m0 = (int64_t)blockIdx.y * 64;
+  const int ks = p.K / 32;
+  const int per = (ks + kSmallWaves - 1) / kSmallWaves;
+  const int k_lo = wave * per, k_hi = min(ks, k_lo + per);
+  // this lane's operand rows: W row n0 + c; A rows m0 + 16 j + c (through the row map), or none
+  const __bf16* wrow = p.w + (int64_t)(n0 + c) * p.K + 8 * g;
+  const __bf16* arow[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m0 + 16 * j + c;
+    arow[j] = m < p.M ? p.a + p.amap(m) * p.K + 8 * g : nullptr;
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = k_lo; k0 < k_hi; k0 += kSmallKB) {
+    bf16x8 wf[kSmallKB], af[kSmallKB][4];
+#pragma unroll
+    for (int u = 0; u < kSmallKB; ++u) {
+      const bool live = k0 + u < k_hi;     // uniform over the wave
+      wf[u] = live ? *reinterpret_cast<const bf16x8*>(wrow + 32 * (k0 + u)) : bf16x8{};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        af[u][j] = (live && arow[j]) ? *reinterpret_cast<const bf16x8*>(arow[j] + 32 * (k0 + u)) : bf16x8{};
+    }
+    __builtin_amdgcn_sched_barrier(0);     // the batch's loads all go out before the first wait
+#pragma unroll
+    for (int u = 0; u < kSmallKB; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(wf[u], af[u][j], acc[j]);
+  }
+  // acc[j][i] = C[m0 + 16 j + c][n0 + 4 g + i]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<f32x4*>(&part[wave][(16 * j + c) * 16 + 4 * g]) = acc[j];
+  __syncthreads();
+  if (threadIdx.x < 256) {
+    const int ml = threadIdx.x >> 2, nl = 4 * (threadIdx.x & 3);
+    const int64_t m = m0 + ml;
+    if (m < p.M) {
+      f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * 16 + nl]);
+#pragma unroll
+      for (int w = 1; w < kSmallWaves; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * 16 + nl]);
+      gemm_store<EPI>(p, m, n0 + nl, r);
+    }
+  }
+}
+
+// 256 x 256 tiles once the rows alone give a few hundred workgroups, else 256 x 128;
+// the split-contraction kernel for few rows.
 template <int EPI>
 pi_status launch_gemm(GemmParams p, hipStream_t s) {
+  if (p.M <= kSmallM) {
+    gemm_small_kernel<EPI><<<dim3((unsigned)(p.N / 16), (unsigned)((p.M + 63) / 64)), kSmallWaves * 64, 0, s>>>(p);
+    return pi::check_launch("gemm_small_kernel");
+  }
   const bool wide = p.M >= 8192;
   const int gm = wide ? 256 : 128;
   p.n_mt = (p.M + gm - 1) / gm;
@@ -322,11 +389,12 @@ bool stream_ok(const pi_layer_stream* s) {
 }
 
 // One stream's half of the layer before the attention: norm 1 and the QKV scatter.
+// mod_T: rows per modulation row (T: one per sample; B * T: one shared by all)
 pi_status stream_qkv(const pi_layer_stream* sw, const float* h, int B, int T, int Ntot, int tok_off,
-                     const float* mod, const LayerWs& w, hipStream_t s) {
+                     const float* mod, const LayerWs& w, hipStream_t s, int mod_T = 0) {
   const int64_t rows = (int64_t)B * T;
   norm_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(h, w.a, rows, sw->width, sw->norm1, sw->norm1 ? nullptr : mod,
-                                                          T);
+                                                          mod_T ? mod_T : T);
   pi_status st = pi::check_launch("norm_kernel");
   if (st != PI_OK) return st;
   GemmParams p{};
@@ -349,7 +417,7 @@ pi_status stream_qkv(const pi_layer_stream* sw, const float* h, int B, int T, in
 
 // One stream's half after the attention: output projection, norm 2, FFN.
 pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot, int tok_off, const float* mod,
-                     const LayerWs& w, hipStream_t s) {
+                     const LayerWs& w, hipStream_t s, int mod_T = 0) {
   const int64_t rows = (int64_t)B * T;
   GemmParams p{};
   p.a = w.o;
@@ -362,7 +430,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   pi_status st = launch_gemm<E_RESID>(p, s);
   if (st != PI_OK) return st;
   norm_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(h, w.a, rows, sw->width, sw->norm2,
-                                                          sw->norm2 ? nullptr : mod, T);
+                                                          sw->norm2 ? nullptr : mod, mod_T ? mod_T : T);
   if ((st = pi::check_launch("norm_kernel")) != PI_OK) return st;
   GemmParams up{};
   up.a = w.a;
@@ -406,17 +474,22 @@ pi_status stream_mod(const pi_layer_stream* sw, const float* cond, int B, const 
 
 // The expert stream's layer in the cached form: norm 1, QKV, the suffix decode
 // against cache layer `layer`, output projection, norm 2 and FFN (h updated in place).
+// shared_mods: the two modulations ([2W] fp32 each, at shared_mods[0] and [1]) shared
+// by every sample, when the caller has them already; else null (computed here from
+// cond [B, W], one per sample).
 pi_status expert_layer(const pi_layer_stream* sw, const pi_kv_cache* cache, int layer, float* h, const float* cond,
-                       const uint8_t* suffix_ar, int B, int S, float scale, const LayerWs& w, hipStream_t s) {
+                       const uint8_t* suffix_ar, int B, int S, float scale, const LayerWs& w, hipStream_t s,
+                       const float* const* shared_mods = nullptr) {
   pi_status st = PI_OK;
-  if (sw->mod1 && (st = stream_mod(sw, cond, B, w, s)) != PI_OK) return st;
-  const float* mod1 = w.mod;
-  const float* mod2 = w.mod + (size_t)B * 2 * sw->width;
-  if ((st = stream_qkv(sw, h, B, S, S, 0, mod1, w, s)) != PI_OK) return st;
+  if (sw->mod1 && !shared_mods && (st = stream_mod(sw, cond, B, w, s)) != PI_OK) return st;
+  const float* mod1 = shared_mods ? shared_mods[0] : w.mod;
+  const float* mod2 = shared_mods ? shared_mods[1] : w.mod + (size_t)B * 2 * sw->width;
+  const int mod_T = shared_mods ? B * S : S;
+  if ((st = stream_qkv(sw, h, B, S, S, 0, mod1, w, s, mod_T)) != PI_OK) return st;
   st = pi_suffix_decode_step(cache, layer, w.q, w.k, w.v, suffix_ar, B, S, LHq, scale, 0.f, w.o, w.attn, w.attn_bytes,
                              s);
   if (st != PI_OK) return st;
-  return stream_out(sw, h, B, S, S, 0, mod2, w, s);
+  return stream_out(sw, h, B, S, S, 0, mod2, w, s, mod_T);
 }
 
 }  // namespace
@@ -596,14 +669,18 @@ __global__ void velocity_out_kernel(const float* __restrict__ vel, const float* 
 
 constexpr int kMaxSteps = 1000;
 
+// The conditioning c is the same for every sample of a step, and so is every
+// norm's modulation: mods holds all of a call's, computed once: for matrix i
+// (layer l's norm j at i = 2 l + j, the final norm at i = 2 layers) and step k,
+// [shift | scale] at mods + (i * steps + k) * 2W.
 struct ExpertFlowWs {
   LayerWs layer;
-  __bf16 *emb, *u, *wout;
-  float *t1, *cond, *h, *vel;
+  __bf16 *emb, *u, *wout, *sc;
+  float *t1, *cond, *h, *vel, *mods;
   size_t total;
 };
 
-ExpertFlowWs expert_flow_ws(int W, int F, int B, int H, int n_steps, size_t attn_bytes, char* base) {
+ExpertFlowWs expert_flow_ws(int W, int F, int L, int B, int H, int n_steps, size_t attn_bytes, char* base) {
   ExpertFlowWs w{};
   w.layer = layer_ws(B, 0, H, W, W, F, F, attn_bytes, base);
   size_t off = w.layer.total;
@@ -617,9 +694,11 @@ ExpertFlowWs expert_flow_ws(int W, int F, int B, int H, int n_steps, size_t attn
   w.u = reinterpret_cast<__bf16*>(take((size_t)n_steps * W * 2));
   w.wout = reinterpret_cast<__bf16*>(take((size_t)256 * W * 2));
   w.t1 = reinterpret_cast<float*>(take((size_t)n_steps * W * 4));
-  w.cond = reinterpret_cast<float*>(take((size_t)n_steps * B * W * 4));
+  w.cond = reinterpret_cast<float*>(take((size_t)n_steps * W * 4));
   w.h = reinterpret_cast<float*>(take((size_t)M * W * 4));
   w.vel = reinterpret_cast<float*>(take((size_t)M * 256 * 4));
+  w.sc = reinterpret_cast<__bf16*>(take((size_t)n_steps * W * 2));
+  w.mods = reinterpret_cast<float*>(take((size_t)(2 * L + 1) * n_steps * 2 * W * 4));
   w.total = off;
   return w;
 }
@@ -648,8 +727,9 @@ bool expert_net_ok(const pi_expert_net* n) {
   return true;
 }
 
-// Conditioning rows c_k for t_k = t0 + k*dt, k < n, each repeated for the B samples.
-pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, int B, const ExpertFlowWs& w,
+// Conditioning rows c_k for t_k = t0 + k*dt, k < steps, and from them every norm's
+// modulation of every step.
+pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, const ExpertFlowWs& w,
                       hipStream_t s) {
   const int W = n->width;
   const int half = W / 2;
@@ -668,8 +748,24 @@ pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, i
     if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
     const int64_t cnt = (int64_t)steps * W;
     bias_act_kernel<<<(unsigned)((cnt + 255) / 256), 256, 0, s>>>(w.t1, j == 0 ? n->b_t1 : n->b_t2, steps, W,
-                                                                 j == 0 ? 1 : 0, w.u, w.cond, B);
+                                                                 j == 0 ? 1 : 0, w.u, w.cond, 1);
     if ((st = pi::check_launch("bias_act_kernel")) != PI_OK) return st;
+  }
+  // every norm's [shift | scale] = r(silu(c)) mod^T for all steps at once
+  const int64_t rows = steps;
+  silu_kernel<<<(unsigned)((rows * W + 255) / 256), 256, 0, s>>>(w.cond, w.sc, rows * W);
+  if ((st = pi::check_launch("silu_kernel")) != PI_OK) return st;
+  for (int i = 0; i <= 2 * n->layers; ++i) {
+    GemmParams p{};
+    p.a = w.sc;
+    p.w = static_cast<const __bf16*>(i == 2 * n->layers ? n->mod_f
+                                     : (i % 2 == 0 ? n->layer[i / 2].mod1 : n->layer[i / 2].mod2));
+    p.M = (int)rows;
+    p.N = 2 * W;
+    p.K = W;
+    p.amap = RowMap{(int)rows, 0, 0};
+    p.out = w.mods + (size_t)i * rows * 2 * W;
+    if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
   }
   return PI_OK;
 }
@@ -677,7 +773,7 @@ pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, i
 // One velocity evaluation with conditioning rows `cond` [B, W]: into `vel` (euler
 // = false) or fused x += dt v.
 pi_status expert_velocity(const pi_expert_net* n, const pi_kv_cache* cache, const uint8_t* suffix_ar, float* x,
-                          const float* cond, float* vel, float dt, bool euler, int B, int H, const ExpertFlowWs& w,
+                          int k, int steps, float* vel, float dt, bool euler, int B, int H, const ExpertFlowWs& w,
                           hipStream_t s) {
   const int W = n->width, A = n->action_dim;
   const int64_t M = (int64_t)B * H;
@@ -686,23 +782,13 @@ pi_status expert_velocity(const pi_expert_net* n, const pi_kv_cache* cache, cons
   pi_status st = pi::check_launch("action_embed_kernel");
   if (st != PI_OK) return st;
   const float scale = 1.0f / 16.0f;   // 1 / sqrt(head_dim 256)
-  for (int l = 0; l < n->layers; ++l)
-    if ((st = expert_layer(&n->layer[l], cache, l, w.h, cond, suffix_ar, B, H, scale, w.layer, s)) != PI_OK)
+  auto mod_at = [&](int i) { return w.mods + ((size_t)i * steps + k) * 2 * W; };
+  for (int l = 0; l < n->layers; ++l) {
+    const float* mods[2] = {mod_at(2 * l), mod_at(2 * l + 1)};
+    if ((st = expert_layer(&n->layer[l], cache, l, w.h, nullptr, suffix_ar, B, H, scale, w.layer, s, mods)) != PI_OK)
       return st;
-  // final adaptive norm: [shift | scale] = r(silu(c)) mod_f^T into the layer's first modulation slot
-  const int64_t nb = (int64_t)B * W;
-  silu_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>(cond, w.layer.sc, nb);
-  if ((st = pi::check_launch("silu_kernel")) != PI_OK) return st;
-  GemmParams pm{};
-  pm.a = w.layer.sc;
-  pm.w = static_cast<const __bf16*>(n->mod_f);
-  pm.M = B;
-  pm.N = 2 * W;
-  pm.K = W;
-  pm.amap = RowMap{B, 0, 0};
-  pm.out = w.layer.mod;
-  if ((st = launch_gemm<E_F32>(pm, s)) != PI_OK) return st;
-  norm_kernel<<<(unsigned)((M + 3) / 4), 256, 0, s>>>(w.h, w.layer.a, M, W, nullptr, w.layer.mod, H);
+  }
+  norm_kernel<<<(unsigned)((M + 3) / 4), 256, 0, s>>>(w.h, w.layer.a, M, W, nullptr, mod_at(2 * n->layers), (int)M);
   if ((st = pi::check_launch("norm_kernel")) != PI_OK) return st;
   GemmParams po{};
   po.a = w.layer.a;
@@ -739,12 +825,12 @@ pi_status expert_setup(const pi_expert_net* n, const pi_kv_cache* cache, const u
                  (int64_t)B * H * n->width * 4 < 0x7FFF0000ll,
              PI_ERR_UNSUPPORTED, "%s: an activation exceeds 2 GiB", who);
   const size_t attn_bytes = pi_decode_workspace_bytes(B, H, LHq, cache->len);
-  const ExpertFlowWs need = expert_flow_ws(n->width, F, B, H, steps, attn_bytes, nullptr);
+  const ExpertFlowWs need = expert_flow_ws(n->width, F, n->layers, B, H, steps, attn_bytes, nullptr);
   PI_REQUIRE(workspace && workspace_bytes >= need.total, PI_ERR_WORKSPACE, "%s: needs %zu workspace bytes, got %zu",
              who, need.total, workspace_bytes);
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "%s: workspace must be 256-byte aligned", who);
-  *w = expert_flow_ws(n->width, F, B, H, steps, attn_bytes, static_cast<char*>(workspace));
+  *w = expert_flow_ws(n->width, F, n->layers, B, H, steps, attn_bytes, static_cast<char*>(workspace));
   return PI_OK;
 }
 
@@ -760,8 +846,8 @@ pi_status expert_pad_out(const pi_expert_net* n, const ExpertFlowWs& w, hipStrea
 extern "C" size_t pi_expert_flow_workspace_bytes(const pi_expert_net* net, int B, int H, int len, int num_steps) {
   if (!expert_net_ok(net) || B < 1 || H < 1 || H > 128 || len < 0 || num_steps < 1 || num_steps > kMaxSteps)
     return 0;
-  return expert_flow_ws(net->width, expert_ffn_max(net), B, H, num_steps, pi_decode_workspace_bytes(B, H, LHq, len),
-                        nullptr)
+  return expert_flow_ws(net->width, expert_ffn_max(net), net->layers, B, H, num_steps,
+                        pi_decode_workspace_bytes(B, H, LHq, len), nullptr)
       .total;
 }
 
@@ -776,8 +862,8 @@ extern "C" pi_status pi_expert_velocity_eval(const pi_expert_net* net, const pi_
   PI_REQUIRE(isfinite(t), PI_ERR_INVALID_ARG, "pi_expert_velocity_eval: t must be finite");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = expert_pad_out(net, w, s)) != PI_OK) return st;
-  if ((st = expert_cond(net, (double)t, 0.0, 1, B, w, s)) != PI_OK) return st;
-  return expert_velocity(net, cache, suffix_ar, const_cast<float*>(x), w.cond, vel, 0.f, false, B, H, w, s);
+  if ((st = expert_cond(net, (double)t, 0.0, 1, w, s)) != PI_OK) return st;
+  return expert_velocity(net, cache, suffix_ar, const_cast<float*>(x), 0, 1, vel, 0.f, false, B, H, w, s);
 }
 
 extern "C" pi_status pi_expert_flow_sample(const pi_expert_net* net, const pi_kv_cache* cache,
@@ -790,10 +876,9 @@ extern "C" pi_status pi_expert_flow_sample(const pi_expert_net* net, const pi_kv
   hipStream_t s = static_cast<hipStream_t>(stream);
   const double dt = -1.0 / num_steps;
   if ((st = expert_pad_out(net, w, s)) != PI_OK) return st;
-  if ((st = expert_cond(net, 1.0, dt, num_steps, B, w, s)) != PI_OK) return st;
+  if ((st = expert_cond(net, 1.0, dt, num_steps, w, s)) != PI_OK) return st;
   for (int k = 0; k < num_steps; ++k) {
-    st = expert_velocity(net, cache, suffix_ar, x, w.cond + (size_t)k * B * net->width, nullptr, (float)dt, true, B, H,
-                         w, s);
+    st = expert_velocity(net, cache, suffix_ar, x, k, num_steps, nullptr, (float)dt, true, B, H, w, s);
     if (st != PI_OK) return st;
   }
   return PI_OK;
