@@ -78,6 +78,8 @@ struct GemmParams {
   __bf16 *q, *k, *v;
   int nq, nkv, T, Ntot, tok_off;
   int n_mt, n_nt;      // tile counts
+  float* split_ws;     // few-row split-contraction partials (kSplitWsBytes), or null: no split
+  int splits;
 };
 
 __device__ __forceinline__ float gelu_exact(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
@@ -269,7 +271,12 @@ __global__ void silu_kernel(const float* __restrict__ c, __bf16* __restrict__ y,
 // straight from the row-major operands); the partial tiles are summed through
 // LDS and the sum goes through the same epilogues as the tiled kernel.  With few
 // rows the tiled kernel would have a handful of workgroups each walking all of K.
+// With few column tiles the contraction is also split across workgroups
+// (blockIdx.z): each stores its 64 x 16 partial and gemm_split_reduce_kernel sums
+// them in split order (deterministic) through the epilogue.
 constexpr int kSmallM = 256, kSmallWaves = 16, kSmallKB = 4;
+constexpr int kMaxSplitTiles = 512;                              // splits x tiles
+constexpr size_t kSplitWsBytes = (size_t)kMaxSplitTiles * 64 * 16 * 4;
 
 template <int EPI>
 __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams p) {
@@ -278,9 +285,11 @@ __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams
   const int c = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int64_t m0 = (int64_t)blockIdx.y * 64;
-  const int ks = p.K / 32;
+  const int ks_all = p.K / 32;
+  const int kz = (ks_all + p.splits - 1) / p.splits;            // this split's k steps
+  const int kz_lo = blockIdx.z * kz, ks = min(ks_all, kz_lo + kz) - kz_lo;
   const int per = (ks + kSmallWaves - 1) / kSmallWaves;
-  const int k_lo = wave * per, k_hi = min(ks, k_lo + per);
+  const int k_lo = kz_lo + wave * per, k_hi = kz_lo + min(ks, wave * per + per);
   // this lane's operand rows: W row n0 + c; A rows m0 + 16 j + c (through the row map), or none
   const __bf16* wrow = p.w + (int64_t)(n0 + c) * p.K + 8 * g;
   const __bf16* arow[4];
@@ -316,13 +325,31 @@ __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams
   if (threadIdx.x < 256) {
     const int ml = threadIdx.x >> 2, nl = 4 * (threadIdx.x & 3);
     const int64_t m = m0 + ml;
-    if (m < p.M) {
-      f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * 16 + nl]);
+    f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * 16 + nl]);
 #pragma unroll
-      for (int w = 1; w < kSmallWaves; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * 16 + nl]);
+    for (int w = 1; w < kSmallWaves; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * 16 + nl]);
+    if (p.splits > 1) {
+      const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+      const int64_t at = (blockIdx.z * (int64_t)gridDim.x * gridDim.y + tile) * 1024 + ml * 16 + nl;
+      *reinterpret_cast<f32x4*>(p.split_ws + at) = r;
+    } else if (m < p.M) {
       gemm_store<EPI>(p, m, n0 + nl, r);
     }
   }
+}
+
+// Sum of the split partials (in split order) through the epilogue; grid as the
+// split kernel's x, y; 256 threads, each four columns of one row.
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_split_reduce_kernel(GemmParams p) {
+  const int ml = threadIdx.x >> 2, nl = 4 * (threadIdx.x & 3);
+  const int64_t m = (int64_t)blockIdx.y * 64 + ml;
+  if (m >= p.M) return;
+  const int64_t tiles = (int64_t)gridDim.x * gridDim.y;
+  const int64_t at = ((int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 1024 + ml * 16 + nl;
+  f32x4 r = *reinterpret_cast<const f32x4*>(p.split_ws + at);
+  for (int z = 1; z < p.splits; ++z) r += *reinterpret_cast<const f32x4*>(p.split_ws + z * tiles * 1024 + at);
+  gemm_store<EPI>(p, m, blockIdx.x * 16 + nl, r);
 }
 
 // 256 x 256 tiles once the rows alone give a few hundred workgroups, else 256 x 128;
@@ -330,8 +357,21 @@ __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams
 template <int EPI>
 pi_status launch_gemm(GemmParams p, hipStream_t s) {
   if (p.M <= kSmallM) {
-    gemm_small_kernel<EPI><<<dim3((unsigned)(p.N / 16), (unsigned)((p.M + 63) / 64)), kSmallWaves * 64, 0, s>>>(p);
-    return pi::check_launch("gemm_small_kernel");
+    // split the contraction across workgroups when the column tiles alone leave
+    // most of the chip idle and every split keeps at least 16 k steps of 32
+    const int tiles = (p.N / 16) * ((p.M + 63) / 64);
+    int splits = 1;
+    if (p.split_ws != nullptr)
+      while (splits < 8 && tiles * splits * 2 <= 256 && p.K / 32 >= 16 * splits * 2 &&
+             tiles * splits * 2 <= kMaxSplitTiles)
+        splits *= 2;
+    p.splits = splits;
+    const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.M + 63) / 64), (unsigned)splits);
+    gemm_small_kernel<EPI><<<grid, kSmallWaves * 64, 0, s>>>(p);
+    pi_status st = pi::check_launch("gemm_small_kernel");
+    if (st != PI_OK || splits == 1) return st;
+    gemm_split_reduce_kernel<EPI><<<dim3(grid.x, grid.y), 256, 0, s>>>(p);
+    return pi::check_launch("gemm_split_reduce_kernel");
   }
   const bool wide = p.M >= 8192;
   const int gm = wide ? 256 : 128;
@@ -348,7 +388,7 @@ constexpr int LHq = 8, LHkv = 1, LD = 256, LQKV = (LHq + 2 * LHkv) * LD;
 
 struct LayerWs {
   __bf16 *a, *q, *k, *v, *o, *u, *sc;
-  float* mod;
+  float *mod, *gsplit;
   void* attn;
   size_t attn_bytes, total;
 };
@@ -374,6 +414,7 @@ LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, size_t a
   w.u = reinterpret_cast<__bf16*>(take(fmax * 2));
   w.sc = reinterpret_cast<__bf16*>(take((size_t)B * wmax * 2));
   w.mod = reinterpret_cast<float*>(take((size_t)2 * B * 2 * wmax * 4));
+  w.gsplit = reinterpret_cast<float*>(take(kSplitWsBytes));
   w.attn_bytes = attn_bytes;
   w.attn = take(w.attn_bytes);
   w.total = off;
@@ -412,6 +453,7 @@ pi_status stream_qkv(const pi_layer_stream* sw, const float* h, int B, int T, in
   p.T = T;
   p.Ntot = Ntot;
   p.tok_off = tok_off;
+  p.split_ws = w.gsplit;
   return launch_gemm<E_QKV>(p, s);
 }
 
@@ -427,6 +469,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   p.K = LHq * LD;
   p.amap = RowMap{T, Ntot, tok_off};
   p.out = h;
+  p.split_ws = w.gsplit;
   pi_status st = launch_gemm<E_RESID>(p, s);
   if (st != PI_OK) return st;
   norm_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(h, w.a, rows, sw->width, sw->norm2,
@@ -440,6 +483,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   up.K = sw->width;
   up.amap = RowMap{(int)rows, 0, 0};
   up.out = w.u;
+  up.split_ws = w.gsplit;
   if ((st = launch_gemm<E_GELU>(up, s)) != PI_OK) return st;
   GemmParams dn{};
   dn.a = w.u;
@@ -449,6 +493,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   dn.K = sw->ffn;
   dn.amap = RowMap{(int)rows, 0, 0};
   dn.out = h;
+  dn.split_ws = w.gsplit;
   return launch_gemm<E_RESID>(dn, s);
 }
 
@@ -467,6 +512,7 @@ pi_status stream_mod(const pi_layer_stream* sw, const float* cond, int B, const 
     p.K = sw->width;
     p.amap = RowMap{B, 0, 0};
     p.out = w.mod + (size_t)j * B * 2 * sw->width;
+    p.split_ws = w.gsplit;
     if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
   }
   return PI_OK;
@@ -745,6 +791,7 @@ pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, c
     p.K = W;
     p.amap = RowMap{steps, 0, 0};
     p.out = w.t1;
+    p.split_ws = w.layer.gsplit;
     if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
     const int64_t cnt = (int64_t)steps * W;
     bias_act_kernel<<<(unsigned)((cnt + 255) / 256), 256, 0, s>>>(w.t1, j == 0 ? n->b_t1 : n->b_t2, steps, W,
@@ -765,6 +812,7 @@ pi_status expert_cond(const pi_expert_net* n, double t0, double dt, int steps, c
     p.K = W;
     p.amap = RowMap{(int)rows, 0, 0};
     p.out = w.mods + (size_t)i * rows * 2 * W;
+    p.split_ws = w.layer.gsplit;
     if ((st = launch_gemm<E_F32>(p, s)) != PI_OK) return st;
   }
   return PI_OK;
@@ -798,6 +846,7 @@ pi_status expert_velocity(const pi_expert_net* n, const pi_kv_cache* cache, cons
   po.K = W;
   po.amap = RowMap{(int)M, 0, 0};
   po.out = w.vel;
+  po.split_ws = w.layer.gsplit;
   if ((st = launch_gemm<E_F32>(po, s)) != PI_OK) return st;
   velocity_out_kernel<<<(unsigned)((M * A + 255) / 256), 256, 0, s>>>(w.vel, n->b_out, x, vel, M, A, dt,
                                                                        euler ? 1 : 0);
