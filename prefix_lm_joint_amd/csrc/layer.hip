@@ -45,7 +45,7 @@ constexpr int kFragBytes = 16 * kRowBytes;      // 16 rows of the LDS image
 constexpr int kGroupM = 4;                      // m tiles per group of the tile order
 template <int GM>
 struct GTile {
-  static constexpr int StageBytes = (GN + GM) * kRowBytes;        // 64 KB (GM 256) or 48 KB (GM 128)
+  static constexpr int StageBytes = (GN + GM) * kRowBytes;        // 64, 48 or 40 KB (GM 256, 128, 64)
   static constexpr int Stages = GM == 256 ? 2 : 3;                // 128 or 144 KB of LDS
   static constexpr int WLoads = GN / 8 / GW;                      // 1 KB (8-row) loads per wave and step: W
   static constexpr int ALoads = GM / 8 / GW;                      //                                        A
@@ -373,14 +373,16 @@ pi_status launch_gemm(GemmParams p, hipStream_t s) {
     gemm_split_reduce_kernel<EPI><<<dim3(grid.x, grid.y), 256, 0, s>>>(p);
     return pi::check_launch("gemm_split_reduce_kernel");
   }
-  const bool wide = p.M >= 8192;
-  const int gm = wide ? 256 : 128;
+  // the M tile: 256 once the rows alone give a few hundred workgroups, else 128, or
+  // 64 when 128-row tiles would leave most of the 256 compute units idle
+  const int gm = p.M >= 8192 ? 256 : ((p.M + 127) / 128 * (p.N / GN) >= 256 ? 128 : 64);
   p.n_mt = (p.M + gm - 1) / gm;
   p.n_nt = p.N / GN;
   const int total = p.n_mt * p.n_nt;
   const int grid = (total + 7) / 8 * 8;
-  if (wide) gemm_nt_kernel<EPI, 256><<<grid, GW * 64, 0, s>>>(p);
-  else gemm_nt_kernel<EPI, 128><<<grid, GW * 64, 0, s>>>(p);
+  if (gm == 256) gemm_nt_kernel<EPI, 256><<<grid, GW * 64, 0, s>>>(p);
+  else if (gm == 128) gemm_nt_kernel<EPI, 128><<<grid, GW * 64, 0, s>>>(p);
+  else gemm_nt_kernel<EPI, 64><<<grid, GW * 64, 0, s>>>(p);
   return pi::check_launch("gemm_nt_kernel");
 }
 
