@@ -83,3 +83,20 @@ def test_full_shape_sampler_is_deterministic_and_sample_independent():
     torch.cuda.synchronize()
     G.note(f"B=1 vs row 2 of B=4: max diff {np.abs(G.host64(x2)[0] - outs[0][2]).max():.3e}")
     np.testing.assert_allclose(G.host64(x2)[0], outs[0][2], rtol=0, atol=G.EXPERT_VEL_MAX_ABS)
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_small_odd_shapes_match_oracle(seed):
+    """Width 256, 7 actions of dim 7, B = 3 over a 37-slot cache with ragged valid
+    lengths: a velocity evaluation and two sampler steps (the same fp32 floor as the
+    real width, measured for these shapes at mean 2.2e-3 / max 1.1e-2)."""
+    G.note(f"expert small odd shapes seed={seed} B=3 P=37 H=7 A=7 W=256 layers=2")
+    net, ck, cv, pm, ar, x = real_case(seed, 3, 37, 7, 2, W=256, A=7)
+    dnet, cache, sar = _upload(net, ck, cv, pm, ar)
+    vel = Bd.pi_expert_velocity_eval(dnet, cache, sar, G.f32_dev(x), 0.625)
+    xd = G.f32_dev(x)
+    Bd.pi_expert_flow_sample(dnet, cache, sar, xd, num_steps=2)
+    torch.cuda.synchronize()
+    n64, ck64, cv64 = _f64(net), _f64(ck), _f64(cv)
+    _close(G.host64(vel), X.expert_velocity(x, 0.625, n64, ck64, cv64, pm, ar), "small velocity")
+    _close(G.host64(xd), X.expert_flow_sample(x, n64, ck64, cv64, pm, ar, num_steps=2), "small sampler")
