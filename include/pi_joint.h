@@ -211,6 +211,22 @@ pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const pi_layer_s
                                  pi_stream stream);
 
 /*
+ * The prefix stream's half of the same layer alone, writing the layer's K/V into
+ * the cache ([P1] §1.6: at inference the prefix is run once and its K/V cached;
+ * under the π0.5 mask no prefix token sees an expert token, so the prefix rows of
+ * pi_joint_layer_forward do not depend on the expert and this is that layer with
+ * Ne = 0).  h_p fp32 [B, Np, width] updated in place; mask built for B and N = Np
+ * (the prefix's own block mask); the cache (cache->B == B, cache->len == Np) gets
+ * the prefix tokens' K/V in slots [0, Np) of layer `layer`; the caller sets the
+ * cache's prefix_mask to the prefix's input mask.  cond as pi_joint_layer_forward
+ * (NULL for a plain-norm stream).  workspace: pi_prefix_layer_workspace_bytes.
+ */
+size_t pi_prefix_layer_workspace_bytes(const pi_layer_stream* prefix, int B, int Np);
+pi_status pi_prefix_layer_forward(const pi_layer_stream* prefix, float* h_p, const float* cond, int B,
+                                  int Np, float scale, const pi_mask* mask, const pi_kv_cache* cache,
+                                  int layer, void* workspace, size_t workspace_bytes, pi_stream stream);
+
+/*
  * The expert stream's half of the same layer in the cached form ([P1] §1.6: at
  * inference the prefix is computed once and each Euler step runs only the
  * suffix against the cache): the S expert tokens h_e fp32 [B, S, W] (updated in

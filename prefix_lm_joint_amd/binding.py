@@ -71,6 +71,10 @@ _SIGS = {
                                                          _c_i, _c_i, _c_i]),
     "pi_joint_layer_forward": (_c_i, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiLayerStream), _c_p, _c_p, _c_p,
                                       _c_i, _c_i, _c_i, _c_f, ctypes.POINTER(PiMask), _c_p, ctypes.c_size_t, _c_p]),
+    "pi_prefix_layer_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiLayerStream), _c_i, _c_i]),
+    "pi_prefix_layer_forward": (_c_i, [ctypes.POINTER(PiLayerStream), _c_p, _c_p, _c_i, _c_i, _c_f,
+                                       ctypes.POINTER(PiMask), ctypes.POINTER(PiKvCache), _c_i, _c_p, ctypes.c_size_t,
+                                       _c_p]),
     "pi_expert_layer_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(PiLayerStream), _c_i, _c_i, _c_i]),
     "pi_expert_layer_decode": (_c_i, [ctypes.POINTER(PiLayerStream), ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p,
                                       _c_i, _c_i, _c_f, _c_p, ctypes.c_size_t, _c_p]),
@@ -348,6 +352,28 @@ def pi_joint_layer_forward(prefix: LayerStream, expert: LayerStream, h_p: torch.
         ctypes.byref(prefix.struct), ctypes.byref(expert.struct), _ptr(h_p, torch.float32, "h_p"),
         _ptr(h_e, torch.float32, "h_e"), _ptr(cond, torch.float32, "cond") if cond is not None else None, B, Np, Ne,
         scale, ctypes.byref(mask.struct), _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream)))
+
+
+def prefix_layer_workspace(prefix: LayerStream, B: int, Np: int, device) -> torch.Tensor:
+    n = int(lib().pi_prefix_layer_workspace_bytes(ctypes.byref(prefix.struct), B, Np))
+    if n == 0:
+        raise ValueError("pi_prefix_layer_forward does not support this stream")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pi_prefix_layer_forward(prefix: LayerStream, h_p: torch.Tensor, mask: Mask, cache: "KVCache", layer: int,
+                            workspace: torch.Tensor, cond: Optional[torch.Tensor] = None,
+                            scale: Optional[float] = None, stream=None) -> None:
+    """The prefix stream's layer alone; updates h_p [B, Np, W] (fp32) in place and writes
+    the layer's K/V into cache layer `layer` (slots [0, Np))."""
+    B, Np = h_p.shape[:2]
+    if scale is None:
+        scale = 256 ** -0.5
+    _check("pi_prefix_layer_forward", lib().pi_prefix_layer_forward(
+        ctypes.byref(prefix.struct), _ptr(h_p, torch.float32, "h_p"),
+        _ptr(cond, torch.float32, "cond") if cond is not None else None, B, Np, scale, ctypes.byref(mask.struct),
+        ctypes.byref(cache.struct), layer, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream)))
 
 

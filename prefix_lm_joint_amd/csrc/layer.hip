@@ -549,10 +549,41 @@ extern "C" size_t pi_joint_layer_workspace_bytes(const pi_layer_stream* prefix, 
                   pi_prefill_workspace_bytes(B, Np + Ne, LHq, LHkv, LD), nullptr).total;
 }
 
+namespace {
+pi_status joint_layer(const pi_layer_stream* prefix, const pi_layer_stream* expert, float* h_p, float* h_e,
+                      const float* cond, int B, int Np, int Ne, float scale, const pi_mask* mask,
+                      const pi_kv_cache* cache, int layer, void* workspace, size_t workspace_bytes,
+                      pi_stream stream);
+}  // namespace
+
 extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const pi_layer_stream* expert, float* h_p,
                                             float* h_e, const float* cond, int B, int Np, int Ne, float scale,
                                             const pi_mask* mask, void* workspace, size_t workspace_bytes,
                                             pi_stream stream) {
+  return joint_layer(prefix, expert, h_p, h_e, cond, B, Np, Ne, scale, mask, nullptr, 0, workspace, workspace_bytes,
+                     stream);
+}
+
+extern "C" size_t pi_prefix_layer_workspace_bytes(const pi_layer_stream* prefix, int B, int Np) {
+  return pi_joint_layer_workspace_bytes(prefix, prefix, B, Np, 0);
+}
+
+extern "C" pi_status pi_prefix_layer_forward(const pi_layer_stream* prefix, float* h_p, const float* cond, int B,
+                                             int Np, float scale, const pi_mask* mask, const pi_kv_cache* cache,
+                                             int layer, void* workspace, size_t workspace_bytes, pi_stream stream) {
+  PI_REQUIRE(cache != nullptr, PI_ERR_INVALID_ARG, "pi_prefix_layer_forward: null cache");
+  PI_REQUIRE(cache->len == Np, PI_ERR_INVALID_ARG,
+             "pi_prefix_layer_forward: the cache must hold exactly the Np = %d prefix tokens (len %d)", Np,
+             cache->len);
+  return joint_layer(prefix, prefix, h_p, nullptr, cond, B, Np, 0, scale, mask, cache, layer, workspace,
+                     workspace_bytes, stream);
+}
+
+namespace {
+pi_status joint_layer(const pi_layer_stream* prefix, const pi_layer_stream* expert, float* h_p, float* h_e,
+                      const float* cond, int B, int Np, int Ne, float scale, const pi_mask* mask,
+                      const pi_kv_cache* cache, int layer, void* workspace, size_t workspace_bytes,
+                      pi_stream stream) {
   PI_REQUIRE(stream_ok(prefix) && stream_ok(expert), PI_ERR_INVALID_ARG,
              "pi_joint_layer_forward: a stream needs w_qkv, w_o, w_up, w_down, a width and ffn that are multiples "
              "of 256 (width <= 4096), and either norm1 + norm2 or mod1 + mod2");
@@ -595,13 +626,14 @@ extern "C" pi_status pi_joint_layer_forward(const pi_layer_stream* prefix, const
   const float* mod2 = w.mod + (size_t)B * 2 * wa;
   if (Np > 0 && (st = stream_qkv(prefix, h_p, B, Np, N, 0, mod1, w, s)) != PI_OK) return st;
   if (Ne > 0 && (st = stream_qkv(expert, h_e, B, Ne, N, Np, mod1, w, s)) != PI_OK) return st;
-  st = pi_joint_attn_prefill(w.q, w.k, w.v, B, N, LHq, LHkv, LD, scale, 0.f, mask, w.o, nullptr, nullptr, 0, w.attn,
-                             w.attn_bytes, stream);
+  st = pi_joint_attn_prefill(w.q, w.k, w.v, B, N, LHq, LHkv, LD, scale, 0.f, mask, w.o, nullptr, cache, layer,
+                             w.attn, w.attn_bytes, stream);
   if (st != PI_OK) return st;
   if (Np > 0 && (st = stream_out(prefix, h_p, B, Np, N, 0, mod2, w, s)) != PI_OK) return st;
   if (Ne > 0 && (st = stream_out(expert, h_e, B, Ne, N, Np, mod2, w, s)) != PI_OK) return st;
   return PI_OK;
 }
+}  // namespace
 
 extern "C" size_t pi_expert_layer_decode_workspace_bytes(const pi_layer_stream* expert, int B, int S, int len) {
   if (!stream_ok(expert) || B < 1 || S < 1 || len < 0) return 0;
