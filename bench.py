@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward", "sampler",
+    p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward", "sampler", "pi05",
                                       "layer", "expert"],
                    default=None,
                    help="run just one leg (for profiling)")
@@ -321,6 +321,70 @@ def expert_sampler_leg(cx: Ctx, iters: int, B: int):
             "mfma_frac": flops / (ms * 1e-3) / PEAK_BF16_FLOPS}
 
 
+def pi05_control_step_leg(cx: Ctx, iters: int):
+    """π0.5's whole control step at the true layer shapes, B = 1: the prefix (3 x 256
+    image + 48 text + 32 discrete-state tokens = 848, bidirectional) through 18
+    prefix-stream layers (width 2048, FFN 8192, plain RMS norm; pi_prefix_layer_forward
+    writing each layer's K/V into the cache), then the expert sampler
+    (pi_expert_flow_sample, 18 expert layers, 10 Euler steps, 50 actions of dim 32).
+    Weights and inputs are drawn on the device from a seeded generator."""
+    torch, Bd, I, np = cx.torch, cx.Bd, cx.I, cx.np
+    P, H, A, Wp, We, L, N = 848, 50, 32, 2048, 1024, 18, 10
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(9001)
+
+    def bf(shape, std):
+        return (torch.randn(shape, generator=gen, device=cx.dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    def f32(shape, std):
+        return torch.randn(shape, generator=gen, device=cx.dev, dtype=torch.float32) * std
+
+    def stream(W, adaptive):
+        F = 4 * W
+        norms = (None, None, bf((2 * W, W), 0.5 * W ** -0.5), bf((2 * W, W), 0.5 * W ** -0.5)) if adaptive else \
+            (1.0 + f32((W,), 0.1), 1.0 + f32((W,), 0.1), None, None)
+        return Bd.LayerStream(bf((2560, W), W ** -0.5), bf((W, 2048), 2048 ** -0.5), bf((F, W), W ** -0.5),
+                              bf((W, F), F ** -0.5), *norms)
+
+    prefix = [stream(Wp, False) for _ in range(L)]
+    t = {"w_in": bf((We, A), A ** -0.5), "b_in": f32((We,), 0.1), "w_t1": bf((We, We), We ** -0.5),
+         "b_t1": f32((We,), 0.1), "w_t2": bf((We, We), We ** -0.5), "b_t2": f32((We,), 0.1),
+         "mod_f": bf((2 * We, We), 0.5 * We ** -0.5), "w_out": bf((A, We), We ** -0.5), "b_out": f32((A,), 0.1)}
+    net = Bd.ExpertNet(t, [stream(We, True) for _ in range(L)])
+    ck = torch.zeros((L, 1, P, 1, 256), dtype=torch.bfloat16, device=cx.dev)
+    cv = torch.zeros_like(ck)
+    valid = cx.u8(np.ones((1, P), np.uint8))
+    cache = Bd.KVCache(ck, cv, valid, P)
+    mask_ws = torch.empty(Bd.pi_mask_workspace_bytes(1, P), dtype=torch.uint8, device=cx.dev)
+    zeros = cx.u8(np.zeros(P, np.uint8))
+    emb = f32((1, P, Wp), 1.0)
+    h = torch.empty_like(emb)
+    pws = Bd.prefix_layer_workspace(prefix[0], 1, P, cx.dev)
+    sar = np.zeros(H, np.uint8)
+    sar[0] = 1
+    sar = cx.u8(sar)
+    noise = f32((1, H, A), 1.0)
+    x = torch.empty_like(noise)
+    fws = Bd.expert_flow_workspace(net, cache, H, N)
+
+    def prefix_pass():
+        m = Bd.pi_mask_build(valid, zeros, zeros, 0, workspace=mask_ws)
+        h.copy_(emb)
+        for l in range(L):
+            Bd.pi_prefix_layer_forward(prefix[l], h, m, cache, l, pws)
+
+    def step():
+        prefix_pass()
+        x.copy_(noise)
+        Bd.pi_expert_flow_sample(net, cache, sar, x, N, fws)
+
+    ms = cx.time_ms(step, iters)
+    ms_prefix = cx.time_ms(prefix_pass, iters)
+    return {"workload": "pi05_control_step_true_shape", "B": 1, "prefix_tokens": P, "actions": H, "layers": L,
+            "euler_steps": N, "prefix_width": Wp, "expert_width": We, "ms_per_control_step": ms,
+            "control_steps_per_s": 1e3 / ms, "ms_prefix_pass": ms_prefix}
+
+
 def decode_kernel_leg(cx: Ctx, iters: int):
     np, torch, Bd, I = cx.np, cx.torch, cx.Bd, cx.I
     w = I.serving_decode()
@@ -594,6 +658,10 @@ def main():
         log("expert layer, cached form (B=64, 816 slots, 50 tokens)")
         kernels["expert"] = expert_decode_leg(cx, max(5, args.kernel_iters // 5))
         log(str(kernels["expert"]))
+    if args.only in (None, "pi05"):
+        log("pi05 control step at the true shapes (B=1: 18 prefix layers, then the expert sampler)")
+        kernels["pi05"] = pi05_control_step_leg(cx, 3)
+        log(str(kernels["pi05"]))
     if args.only in (None, "sampler"):
         for B in (1, 64):
             log(f"pi05 expert sampler leg (B={B}, 18 layers, 10 Euler steps)")
@@ -670,6 +738,10 @@ def main():
             **{f"B{b}": {k: kernels[f"sampler_b{b}"][k] for k in ("ms_per_control_step", "robot_steps_per_s",
                                                                  "achieved_tflops", "mfma_frac")}
                for b in (1, 64)}},
+        "pi05_control_step": {
+            "what": "B = 1: 848 prefix tokens through 18 prefix-stream layers (width 2048, FFN 8192) writing the "
+                    "cache, then the expert sampler (18 layers, 10 Euler steps)",
+            **{k: kernels["pi05"][k] for k in ("ms_per_control_step", "control_steps_per_s", "ms_prefix_pass")}},
         "breakdown_us": result["breakdown_us"],
         "cpu_baseline": cpu,
     }
