@@ -80,6 +80,8 @@ struct GemmParams {
   int n_mt, n_nt;      // tile counts
   float* split_ws;     // few-row split-contraction partials (kSplitWsBytes), or null: no split
   int splits;
+  float* tsplit_ws;    // tiled split-contraction partials (kTiledSplitBytes), or null: no split
+  int tsplit;
 };
 
 __device__ __forceinline__ float gelu_exact(float x) { return 0.5f * x * (1.0f + erff(x * 0.7071067811865476f)); }
@@ -148,12 +150,16 @@ __global__ void __launch_bounds__(GW * 64) gemm_nt_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int wn = wave & 3, wm = wave >> 2;
-  const int nk = p.K / GK;
+  // split contraction (blockIdx.y of p.tsplit): this workgroup's k steps
+  const int nk_all = p.K / GK;
+  const int per = (nk_all + p.tsplit - 1) / p.tsplit;
+  const int kz0 = (int)blockIdx.y * per;
+  const int nk = min(nk_all, kz0 + per) - kz0;
   // Loads: each instruction fetches 8 rows x 128 bytes (lane L: row L / 8,
   // physical chunk L % 8, so the source chunk is (L % 8) ^ swz(row)); this wave
   // takes W rows 8 (WLoads wave + j) .. and A rows 8 (ALoads wave + j) ..
-  const i32x4 rw = make_rsrc(p.w + (int64_t)nt * GN * p.K);
-  const i32x4 ra = make_rsrc(p.a);
+  const i32x4 rw = make_rsrc(p.w + (int64_t)nt * GN * p.K + (int64_t)kz0 * GK);
+  const i32x4 ra = make_rsrc(p.a + (int64_t)kz0 * GK);
   const uint32_t kb = (uint32_t)p.K * 2u;
   uint32_t ow[G::WLoads], oa[G::ALoads];
 #pragma unroll
@@ -215,8 +221,29 @@ __global__ void __launch_bounds__(GW * 64) gemm_nt_kernel(GemmParams p) {
     const int64_t m = (int64_t)mt * GM + (GM / 2) * wm + 16 * b + c;
     if (m >= p.M) continue;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) gemm_store<EPI>(p, m, nt * GN + 64 * wn + 16 * a + 4 * g, acc[a][b]);
+    for (int a = 0; a < 4; ++a) {
+      const int n = nt * GN + 64 * wn + 16 * a + 4 * g;
+      if (p.tsplit > 1)
+        *reinterpret_cast<f32x4*>(p.tsplit_ws + ((int64_t)blockIdx.y * p.M + m) * p.N + n) = acc[a][b];
+      else
+        gemm_store<EPI>(p, m, n, acc[a][b]);
+    }
   }
+}
+
+// Sum of the tiled split partials (in split order) through the epilogue; one
+// thread per four columns of a row.
+template <int EPI>
+__global__ void __launch_bounds__(256) gemm_tsplit_reduce_kernel(GemmParams p) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t quads = (int64_t)p.M * (p.N / 4);
+  if (q >= quads) return;
+  const int64_t m = q / (p.N / 4);
+  const int n = (int)(q % (p.N / 4)) * 4;
+  const int64_t plane = (int64_t)p.M * p.N;
+  f32x4 r = *reinterpret_cast<const f32x4*>(p.tsplit_ws + m * p.N + n);
+  for (int z = 1; z < p.tsplit; ++z) r += *reinterpret_cast<const f32x4*>(p.tsplit_ws + z * plane + m * p.N + n);
+  gemm_store<EPI>(p, m, n, r);
 }
 
 // RMS norm of one fp32 row of width W (a multiple of 256, at most 4096) per wave:
@@ -277,6 +304,7 @@ __global__ void silu_kernel(const float* __restrict__ c, __bf16* __restrict__ y,
 constexpr int kSmallM = 256, kSmallWaves = 16, kSmallKB = 4;
 constexpr int kMaxSplitTiles = 512;                              // splits x tiles
 constexpr size_t kSplitWsBytes = (size_t)kMaxSplitTiles * 64 * 16 * 4;
+constexpr size_t kTiledSplitBytes = (size_t)32 << 20;              // tiled split partials (M x N x splits fp32)
 
 template <int EPI>
 __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams p) {
@@ -380,17 +408,31 @@ pi_status launch_gemm(GemmParams p, hipStream_t s) {
   p.n_nt = p.N / GN;
   const int total = p.n_mt * p.n_nt;
   const int grid = (total + 7) / 8 * 8;
-  if (gm == 256) gemm_nt_kernel<EPI, 256><<<grid, GW * 64, 0, s>>>(p);
-  else if (gm == 128) gemm_nt_kernel<EPI, 128><<<grid, GW * 64, 0, s>>>(p);
-  else gemm_nt_kernel<EPI, 64><<<grid, GW * 64, 0, s>>>(p);
-  return pi::check_launch("gemm_nt_kernel");
+  // split the contraction when the tiles leave more than half the compute units
+  // idle and each split keeps at least 32 k steps of 64 (measured: an 848-row FFN
+  // down product of 112 tiles gains 4-way; a 3200-row one of 200 tiles loses 2-way)
+  int ts = 1;
+  if (p.tsplit_ws != nullptr && total < 128)
+    while (ts < 4 && total * ts * 2 <= 512 && p.K / GK >= 32 * ts * 2 &&
+           (size_t)p.M * p.N * ts * 2 * 4 <= kTiledSplitBytes)
+      ts *= 2;
+  p.tsplit = ts;
+  const dim3 g3((unsigned)grid, (unsigned)ts);
+  if (gm == 256) gemm_nt_kernel<EPI, 256><<<g3, GW * 64, 0, s>>>(p);
+  else if (gm == 128) gemm_nt_kernel<EPI, 128><<<g3, GW * 64, 0, s>>>(p);
+  else gemm_nt_kernel<EPI, 64><<<g3, GW * 64, 0, s>>>(p);
+  pi_status st = pi::check_launch("gemm_nt_kernel");
+  if (st != PI_OK || ts == 1) return st;
+  const int64_t quads = (int64_t)p.M * (p.N / 4);
+  gemm_tsplit_reduce_kernel<EPI><<<(unsigned)((quads + 255) / 256), 256, 0, s>>>(p);
+  return pi::check_launch("gemm_tsplit_reduce_kernel");
 }
 
 constexpr int LHq = 8, LHkv = 1, LD = 256, LQKV = (LHq + 2 * LHkv) * LD;
 
 struct LayerWs {
   __bf16 *a, *q, *k, *v, *o, *u, *sc;
-  float *mod, *gsplit;
+  float *mod, *gsplit, *tsplit;
   void* attn;
   size_t attn_bytes, total;
 };
@@ -417,6 +459,7 @@ LayerWs layer_ws(int B, int Np, int Ne, int Wp, int We, int Fp, int Fe, size_t a
   w.sc = reinterpret_cast<__bf16*>(take((size_t)B * wmax * 2));
   w.mod = reinterpret_cast<float*>(take((size_t)2 * B * 2 * wmax * 4));
   w.gsplit = reinterpret_cast<float*>(take(kSplitWsBytes));
+  w.tsplit = rows_max > kSmallM ? reinterpret_cast<float*>(take(kTiledSplitBytes)) : nullptr;
   w.attn_bytes = attn_bytes;
   w.attn = take(w.attn_bytes);
   w.total = off;
@@ -456,6 +499,7 @@ pi_status stream_qkv(const pi_layer_stream* sw, const float* h, int B, int T, in
   p.Ntot = Ntot;
   p.tok_off = tok_off;
   p.split_ws = w.gsplit;
+  p.tsplit_ws = w.tsplit;
   return launch_gemm<E_QKV>(p, s);
 }
 
@@ -472,6 +516,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   p.amap = RowMap{T, Ntot, tok_off};
   p.out = h;
   p.split_ws = w.gsplit;
+  p.tsplit_ws = w.tsplit;
   pi_status st = launch_gemm<E_RESID>(p, s);
   if (st != PI_OK) return st;
   norm_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(h, w.a, rows, sw->width, sw->norm2,
@@ -486,6 +531,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   up.amap = RowMap{(int)rows, 0, 0};
   up.out = w.u;
   up.split_ws = w.gsplit;
+  up.tsplit_ws = w.tsplit;
   if ((st = launch_gemm<E_GELU>(up, s)) != PI_OK) return st;
   GemmParams dn{};
   dn.a = w.u;
@@ -496,6 +542,7 @@ pi_status stream_out(const pi_layer_stream* sw, float* h, int B, int T, int Ntot
   dn.amap = RowMap{(int)rows, 0, 0};
   dn.out = h;
   dn.split_ws = w.gsplit;
+  dn.tsplit_ws = w.tsplit;
   return launch_gemm<E_RESID>(dn, s);
 }
 
