@@ -622,6 +622,11 @@ extern "C" pi_status pi_prefix_layer_forward(const pi_layer_stream* prefix, floa
   PI_REQUIRE(cache->len == Np, PI_ERR_INVALID_ARG,
              "pi_prefix_layer_forward: the cache must hold exactly the Np = %d prefix tokens (len %d)", Np,
              cache->len);
+  // the whole cache contract here, so that nothing is launched for a call the attention would reject
+  PI_REQUIRE(cache->k && cache->v && cache->B == B && cache->Hkv == LHkv && cache->d == LD && layer >= 0 &&
+                 layer < cache->layers && Np >= 1 && Np <= cache->capacity,
+             PI_ERR_INVALID_ARG, "pi_prefix_layer_forward: cache does not match (B=%d, layer %d of %d, %d slots)", B,
+             layer, cache->layers, cache->capacity);
   return joint_layer(prefix, prefix, h_p, nullptr, cond, B, Np, 0, scale, mask, cache, layer, workspace,
                      workspace_bytes, stream);
 }
@@ -644,6 +649,8 @@ pi_status joint_layer(const pi_layer_stream* prefix, const pi_layer_stream* expe
   PI_REQUIRE(!(prefix->mod1 && expert->mod1), PI_ERR_UNSUPPORTED,
              "pi_joint_layer_forward: at most one stream may use the adaptive norm");
   const int N = Np + Ne;
+  PI_REQUIRE(N <= kMaxTiles * TK, PI_ERR_UNSUPPORTED, "pi_joint_layer_forward: %d tokens exceed %d", N,
+             kMaxTiles * TK);
   PI_REQUIRE(mask->B == B && mask->N == N, PI_ERR_INVALID_ARG,
              "pi_joint_layer_forward: mask built for B=%d N=%d, call has B=%d N=%d", mask->B, mask->N, B, N);
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_joint_layer_forward: scale must be > 0");
@@ -698,6 +705,12 @@ extern "C" pi_status pi_expert_layer_decode(const pi_layer_stream* expert, const
   PI_REQUIRE(B >= 1 && S >= 1 && cache->B == B && cache->Hkv == LHkv && cache->d == LD && layer >= 0 &&
                  layer < cache->layers,
              PI_ERR_INVALID_ARG, "pi_expert_layer_decode: cache / shape mismatch (B=%d S=%d layer %d)", B, S, layer);
+  PI_REQUIRE(S <= 128 && cache->k && cache->v && cache->prefix_mask && cache->len >= 0 &&
+                 cache->len <= cache->capacity,
+             PI_ERR_INVALID_ARG, "pi_expert_layer_decode: S=%d (<= 128) or the cache (len %d of %d slots) is invalid",
+             S, cache->len, cache->capacity);
+  PI_REQUIRE((cache->len + TK - 1) / TK + (S + TK - 1) / TK <= kMaxTiles, PI_ERR_UNSUPPORTED,
+             "pi_expert_layer_decode: cache length %d too long", cache->len);
   PI_REQUIRE(pi::aligned16(h_e), PI_ERR_INVALID_ARG, "pi_expert_layer_decode: h_e must be 16-byte aligned");
   PI_REQUIRE(!expert->mod1 || cond, PI_ERR_INVALID_ARG, "pi_expert_layer_decode: an adaptive norm needs cond");
   PI_REQUIRE(scale > 0.f && isfinite(scale), PI_ERR_INVALID_ARG, "pi_expert_layer_decode: scale must be > 0");
@@ -948,8 +961,12 @@ pi_status expert_setup(const pi_expert_net* n, const pi_kv_cache* cache, const u
   PI_REQUIRE(B >= 1 && H >= 1 && H <= 128, PI_ERR_INVALID_ARG, "%s: B=%d H=%d (1 <= H <= 128)", who, B, H);
   PI_REQUIRE(steps >= 1 && steps <= kMaxSteps, PI_ERR_INVALID_ARG, "%s: num_steps=%d (1..%d)", who, steps,
              kMaxSteps);
-  PI_REQUIRE(cache->B == B && cache->Hkv == LHkv && cache->d == LD && cache->layers >= n->layers, PI_ERR_INVALID_ARG,
-             "%s: the cache must have B=%d, one KV head of d=256 and at least %d layers", who, B, n->layers);
+  PI_REQUIRE(cache->B == B && cache->Hkv == LHkv && cache->d == LD && cache->layers >= n->layers && cache->k &&
+                 cache->v && cache->prefix_mask && cache->len >= 0 && cache->len <= cache->capacity,
+             PI_ERR_INVALID_ARG, "%s: the cache must have B=%d, one KV head of d=256, at least %d layers and a valid "
+             "length", who, B, n->layers);
+  PI_REQUIRE((cache->len + TK - 1) / TK + (H + TK - 1) / TK <= kMaxTiles, PI_ERR_UNSUPPORTED,
+             "%s: cache length %d too long", who, cache->len);
   const int F = expert_ffn_max(n);
   PI_REQUIRE((int64_t)B * H * F * 2 < 0x7FFF0000ll && (int64_t)B * H * LHq * LD * 2 < 0x7FFF0000ll &&
                  (int64_t)B * H * n->width * 4 < 0x7FFF0000ll,

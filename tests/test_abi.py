@@ -150,6 +150,9 @@ def test_layer_rejects_bad_arguments_before_launch():
         ctypes.byref(e), ctypes.byref(cache), kw.get("layer", 0), FAKE, kw.get("cond", FAKE), FAKE, kw.get("B", 2),
         50, 0.0625, kw.get("ws", P(0x100000)), kw.get("ws_bytes", need_d), None)
     assert dec(layer=18) == -1 and dec(B=3) == -1 and dec(cond=None) == -1
+    long_s = lambda: lib.pi_expert_layer_decode(ctypes.byref(se), ctypes.byref(cache), 0, FAKE, FAKE, FAKE, 2, 129,
+                                                0.0625, P(0x100000), 1 << 40, None)
+    assert long_s() == -1                                       # S > 128, rejected before any launch
     assert dec(ws_bytes=need_d - 1) == -3 and dec(e=odd) == -1
     assert b"pi_expert_layer_decode" in lib.pi_last_error()
 
@@ -266,3 +269,21 @@ def test_expert_sampler_rejects_bad_arguments_before_launch():
         P(0x100000), kw.get("ws_bytes", need1), None)
     assert ev(vel=None) == -1 and ev(t=float("nan")) == -1 and ev(ws_bytes=need1 - 1) == -3
     assert b"pi_expert_velocity_eval" in lib.pi_last_error()
+
+
+@needs_lib
+def test_prefix_layer_rejects_bad_arguments_before_launch():
+    lib = Bd.lib()
+    sp = Bd.PiLayerStream(2048, 8192, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    m = Bd.PiMask(B=2, N=60, n_qt=4, n_kt=2, forbid_bits=0, bid=FAKE, pos=FAKE, tok=FAKE, tiles=FAKE)
+    need = lib.pi_prefix_layer_workspace_bytes(ctypes.byref(sp), 2, 60)
+    assert need == lib.pi_joint_layer_workspace_bytes(ctypes.byref(sp), ctypes.byref(sp), 2, 60, 0) > 0
+    cache = Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 2, 816, 1, 256, 60)
+    call = lambda c=cache, **kw: lib.pi_prefix_layer_forward(
+        ctypes.byref(sp), FAKE, None, 2, kw.get("Np", 60), 0.0625, ctypes.byref(m),
+        ctypes.byref(c) if c is not None else None, kw.get("layer", 0), P(0x100000), kw.get("ws_bytes", need), None)
+    assert call(c=None) == -1                                   # the prefix pass writes the cache
+    assert call(c=Bd.PiKvCache(FAKE, FAKE, FAKE, 18, 2, 816, 1, 256, 59)) == -1   # cache length != Np
+    assert call(layer=18) == -1                                 # past the cache's layers
+    assert call(ws_bytes=need - 1) == -3
+    assert b"pi_" in lib.pi_last_error()
