@@ -443,7 +443,7 @@ __device__ __forceinline__ void store_partials(const WaveState<D, NR>& st, float
     const int64_t at = split * n_chunks + chunk;
     f32x4* dst = reinterpret_cast<f32x4*>(opart) + at * (D / 16) * 64 + lane;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) dst[dt * 64] = st.o[r][dt];
+    for (int dt = 0; dt < D / 16; ++dt) __builtin_nontemporal_store(st.o[r][dt], &dst[dt * 64]);   // read once, by the merge
     if (g == 0) {
       mlpart[at * 32 + 2 * c] = st.m[r];
       mlpart[at * 32 + 2 * c + 1] = st.l[r][0];
@@ -819,7 +819,7 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
       const int64_t at = sp * n_chunks + chunk;
       m[sp] = mlpart[at * 32 + 2 * c];
       l[sp] = mlpart[at * 32 + 2 * c + 1];
-      op[sp] = reinterpret_cast<const f32x4*>(opart)[(at * (D / 16) + dt) * 64 + lane];
+      op[sp] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(opart) + (at * (D / 16) + dt) * 64 + lane);
     }
     M = fmaxf(M, m[sp]);
   }
