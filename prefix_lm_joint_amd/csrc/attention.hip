@@ -925,6 +925,12 @@ constexpr int kNWar = 1;
 constexpr int kNR64 = 1, kNW64 = 7;
 using CfgG8 = Cfg<256, 8, kNR256, kNW256>;
 using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
+// A decode of a few samples (at most 16 query blocks of seven waves) takes
+// workgroups of three compute waves: twice the workgroups over the same splits,
+// each with a shorter chain (measured: 3 % off the B = 1 control step; at B = 64
+// it would halve the work per workgroup launch and run 2x slower).
+constexpr int kNWdecS = 3;
+using CfgDecS = Cfg<256, 8, kNR256, kNWdecS>;
 using CfgAr = Cfg<256, 8, kNR256, kNWar>;
 
 template <int D, int G, int NR, int NW>
@@ -947,15 +953,18 @@ pi_status launch_prefill(const void* q, const void* k, const void* v, void* o, i
 
 // Key splits for a decode of B samples: enough workgroups to cover the chip
 // (about 256) while giving each split at least two key tiles.
+// (min_tiles: the fewest key tiles a split gets; three for the small-batch shape.)
 template <typename C>
-int decode_splits_for(int B, int S, int len) {
+int decode_splits_for(int B, int S, int len, int min_tiles = 2) {
   const int n_qblk = (S + C::TOK - 1) / C::TOK;
   const int tiles = (len + TK - 1) / TK + (S + TK - 1) / TK;
   const int by_chip = 256 / std::max(1, B * n_qblk);
-  return std::max(1, std::min({kMaxSplit, by_chip, tiles / 2}));
+  return std::max(1, std::min({kMaxSplit, by_chip, tiles / min_tiles}));
 }
+bool small_decode(int B, int S) { return S > 1 && B * ((S + CfgDec::TOK - 1) / CfgDec::TOK) <= 16; }
 int decode_splits(int B, int S, int len) {
-  return S == 1 ? decode_splits_for<CfgAr>(B, S, len) : decode_splits_for<CfgDec>(B, S, len);
+  if (S == 1) return decode_splits_for<CfgAr>(B, S, len);
+  return small_decode(B, S) ? decode_splits_for<CfgDecS>(B, S, len, 3) : decode_splits_for<CfgDec>(B, S, len);
 }
 
 // Key splits for a GQA 8:1 prefill of B samples of L tokens (same rule as the
@@ -982,7 +991,8 @@ size_t rope_ks_bytes(int B, int S) { return pi::align_up((size_t)B * S * 256 * 2
 
 // Decode workspace: [rotated suffix K (rotary embedding only)] [key-split partials].
 size_t decode_split_bytes(int B, int S, int splits) {
-  return S == 1 ? split_ws_bytes<CfgAr>(B, S, splits) : split_ws_bytes<CfgDec>(B, S, splits);
+  if (S == 1) return split_ws_bytes<CfgAr>(B, S, splits);
+  return small_decode(B, S) ? split_ws_bytes<CfgDecS>(B, S, splits) : split_ws_bytes<CfgDec>(B, S, splits);
 }
 size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
   (void)Hq;
@@ -992,7 +1002,10 @@ size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
 }  // namespace
 
 size_t pi::decode_workspace_max(int B, int S, int Hq) {
-  const int n_qblk = (S + CfgDec::TOK - 1) / CfgDec::TOK;
+  // the most splits any cache length can take, for the shape decode_splits picks
+  const bool sm = small_decode(B, S);
+  const int tok = sm ? CfgDecS::TOK : CfgDec::TOK;
+  const int n_qblk = (S + tok - 1) / tok;
   const int splits = std::max(1, std::min(kMaxSplit, 256 / std::max(1, B * n_qblk)));
   return decode_ws_bytes(B, S, Hq, splits);
 }
@@ -1103,7 +1116,7 @@ pi_status launch_decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf1
                         float rope_base, void* o_s, bool tiled, char* split_ws, size_t split_avail, hipStream_t s) {
   using C = Cfg<256, 8, kNR256, NWD>;
   const int n_qblk = (S + C::TOK - 1) / C::TOK;
-  int splits = decode_splits_for<C>(B, S, cache->len);
+  int splits = decode_splits_for<C>(B, S, cache->len, NWD == kNWdecS ? 3 : 2);
   if (split_ws == nullptr || split_avail < split_ws_bytes<C>(B, S, splits)) splits = 1;   // one pass per sample
   const size_t chunks = (size_t)splits * B * n_qblk * NWD * kNR256;
   float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
@@ -1170,6 +1183,9 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   if (S == 1)
     return launch_decode<kNWar>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
                                 split_ws, split_avail, s);
+  if (small_decode(B, S))
+    return launch_decode<kNWdecS>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
+                                  split_ws, split_avail, s);
   return launch_decode<kNWdec>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
                                split_ws, split_avail, s);
 }
