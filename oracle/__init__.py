@@ -38,10 +38,12 @@ What it computes, in plain numpy float64 with an explicit [B, N, N] mask:
       norms, the expert layers against the cache layer by layer, a final
       adaptive norm and the action out-projection ("VLA 代码精读" §1.2, §1.4,
       §1.6; the embedding, MLP activation and final norm are readings).
-  flow.velocity_net
-      the random-weight stand-in velocity network.  The pages give no weights
-      or exact layer for it: **parity unpinned** as a whole (only its pieces
-      and its W_o = 0 reduction are pinned).
+  flow.velocity_net / flow.embed_suffix / flow.rms
+      the random-weight stand-in velocity network.  The pages give only its
+      shapes; its definition is a reading, pinned against a float64 composition
+      of library calls (F.linear, scaled_dot_product_attention, vector_norm),
+      a hand-written closed form with the attention path zeroed, and the
+      state token's place at row 0.
 
 Readings of points the pages leave open are listed in each docstring.
 """

@@ -39,9 +39,13 @@ def euler_sample(noise, velocity, num_steps: int = 10) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Stand-in velocity net.  PARITY UNPINNED as a whole: the pages give neither
-# the weights nor the exact layer of the action expert; this is a random-
-# weight stand-in with the expert's head geometry.  Its definition:
+# Stand-in velocity net.  The pages give neither the weights nor the exact
+# layer of the action expert; this is a random-weight stand-in with the
+# expert's head geometry, so its definition is a reading.  It is pinned to
+# that reading, not to the pages' numbers: a float64 composition of library
+# calls (F.linear, scaled_dot_product_attention with a hand-built mask,
+# vector_norm), a closed form with the attention path zeroed, and the state
+# token at row 0.  Its definition:
 #
 #   tokens      h[:,0]   = r(state) W_state^T + b_state            (state token)
 #               h[:,1+i] = r(x_i) W_in^T + b_in + t * w_time        (action tokens)
