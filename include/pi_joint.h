@@ -105,8 +105,19 @@ pi_status pi_mask_materialize(const pi_mask* mask, uint8_t* dense, pi_stream str
  * Joint-attention prefill over one shared KV pool ([P3] first section; [P1] §1.5):
  *   O[b,i,h,:] = sum_j softmax_j(scale * q[b,i,h,:].k[b,j,g,:]) v[b,j,g,:]
  * over the keys j visible from i under `mask`, g = floor(h*Hkv/Hq); one softmax
- * per (b, i, h).  Masked keys are excluded by selection (their K/V values can
- * never reach an output, NaN included).  A query with no visible key gets O = 0.
+ * per (b, i, h).  Masked keys are excluded by selection: a masked score never
+ * enters the maximum or the sum and its weight is exactly 0.  What that
+ * guarantees for the values a masked key holds:
+ *   - K of a masked key, and K and V of a padded (invalid) key, never reach an
+ *     output, whatever they hold (NaN and inf included): padded keys are
+ *     staged as zeros;
+ *   - a finite V of a valid key that is masked for some rows cannot change
+ *     those rows' outputs (bit-exact);
+ *   - NOT guaranteed: an inf or NaN in the V of a valid key that some rows of
+ *     the same 16-query x 32-key tile may read and others may not (say a FAST
+ *     token's V, which π0.5's expert rows may not read) enters the masked
+ *     rows' product with weight 0 and gives 0 * inf = NaN there.
+ * A query with no visible key gets O = 0.
  *   q  bf16 [B, L, Hq, d]    k, v  bf16 [B, L, Hkv, d]    o  bf16 [B, L, Hq, d]
  *   mask built for the same B and N = L.  scale > 0 (usually 1/sqrt(d)).
  * Supported heads: (Hq, Hkv, d) = (8, 1, 256) and (Hq, Hkv, d) with Hq == Hkv and
@@ -143,7 +154,10 @@ pi_status pi_joint_attn_prefill(const void* q, const void* k, const void* v, int
  *   dq[b,i,h] = scale sum_j dS_j k_j;   dk[b,j] += scale dS_j q[b,i,h];   dv[b,j] += P_j dO[b,i,h]
  * (sums over every row that sees key j).  Masked pairs contribute exactly
  * nothing; a row with no visible key gets dq = 0, and a key no row sees gets
- * dk = dv = 0.
+ * dk = dv = 0.  Q/dO of padded tokens and K/V of padded keys may hold anything
+ * (staged as zeros).  As in the forward, an inf or NaN in the K or V of a valid
+ * key that only some rows of a tile may read reaches the other rows' dq as NaN
+ * (its weight is 0, its dP is not finite).
  *   q, o, dout, dq  bf16 [B, L, Hq, d]    k, v, dk, dv  bf16 [B, L, Hkv, d]
  *   lse  fp32 [B, L, Hq]: the forward's log-sum-exp (pi_joint_attn_prefill's lse
  *        output for the same q, k, mask, scale and rope_base); o: its output.
@@ -277,6 +291,9 @@ struct pi_kv_cache {
  * optional: with it a small batch splits each sample's keys over several
  * workgroups and merges the partial softmaxes, without it the call runs unsplit
  * (same result up to rounding).
+ * Masked keys as in pi_joint_attn_prefill: padded cache slots may hold anything
+ * (staged as zeros); an inf or NaN in the V of a suffix key that only some
+ * suffix rows may read can reach the others as NaN.
  */
 size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len);
 pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s,

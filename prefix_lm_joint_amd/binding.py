@@ -1,10 +1,14 @@
 """Thin ctypes binding of libpi_joint.so (include/pi_joint.h).
 
 Argument marshalling only: every step runs in the HIP library.  Tensors are torch
-tensors on a ROCm device; their dtype and contiguity are checked here because
-the C ABI cannot see them, and shapes are passed through for the library to
-validate.  There is no fallback: if the library is missing or a call fails, an
-exception is raised.
+tensors on a ROCm device.  The C ABI sees only pointers and sizes, so every
+wrapper checks the full shape and dtype of each tensor it passes against the
+sizes it passes (ValueError before anything reaches the library, so a wrong or
+undersized tensor can never turn into an out-of-bounds device access), plus
+device placement and contiguity; the library then validates the sizes
+themselves.  Workspaces a wrapper allocates for a caller-given stream are
+recorded on that stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
 """
 from __future__ import annotations
 
@@ -134,6 +138,27 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _expect(t: Optional[torch.Tensor], shape, dtype, name: str, optional: bool = False) -> None:
+    """ValueError unless t has exactly `shape` (entries None match any size) and `dtype`."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    got = tuple(t.shape)
+    if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+        raise ValueError(f"{name} has shape {got}, expected {tuple('*' if w is None else w for w in shape)}")
+
+
+def _own(workspace: Optional[torch.Tensor], stream) -> None:
+    """Keep a wrapper-allocated workspace alive until the work queued on `stream` is done."""
+    if workspace is not None and stream is not None:
+        workspace.record_stream(stream)
+
+
 def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
     if t is None:
         return None
@@ -191,10 +216,18 @@ def pi_mask_workspace_bytes(B: int, N: int) -> int:
 
 def pi_mask_build(input_mask: torch.Tensor, ar: torch.Tensor, seg: Optional[torch.Tensor] = None,
                   forbid_bits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> Mask:
+    if input_mask.dim() != 2:
+        raise ValueError(f"input_mask must be [B, N], got {tuple(input_mask.shape)}")
     B, N = input_mask.shape
+    _expect(input_mask, (B, N), torch.uint8, "input_mask")
+    _expect(ar, (N,), torch.uint8, "ar")
+    _expect(seg, (N,), torch.uint8, "seg", optional=True)
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
     nbytes = pi_mask_workspace_bytes(B, N)
-    if workspace is None:
+    own = workspace is None
+    if own:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=input_mask.device)
+        _own(workspace, stream)
     out = PiMask()
     _check("pi_mask_build", lib().pi_mask_build(
         _ptr(input_mask, torch.uint8, "input_mask"), _ptr(ar, torch.uint8, "ar"), _ptr(seg, torch.uint8, "seg"),
@@ -206,6 +239,7 @@ def pi_mask_build(input_mask: torch.Tensor, ar: torch.Tensor, seg: Optional[torc
 def pi_mask_materialize(mask: Mask, dense: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     if dense is None:
         dense = torch.empty((mask.B, mask.N, mask.N), dtype=torch.uint8, device=mask.workspace.device)
+    _expect(dense, (mask.B, mask.N, mask.N), torch.uint8, "dense")
     _check("pi_mask_materialize", lib().pi_mask_materialize(ctypes.byref(mask.struct),
                                                             _ptr(dense, torch.uint8, "dense"), _stream(stream)))
     return dense
@@ -219,8 +253,14 @@ class KVCache:
     """Caller-owned per-layer prefix KV cache: k, v bf16 [layers, B, capacity, Hkv, d]."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, prefix_mask: torch.Tensor, length: Optional[int] = None):
+        if k.dim() != 5:
+            raise ValueError(f"cache k must be [layers, B, capacity, Hkv, d], got {tuple(k.shape)}")
         layers, B, cap, Hkv, d = k.shape
-        assert v.shape == k.shape and prefix_mask.shape == (B, cap)
+        _expect(k, (layers, B, cap, Hkv, d), torch.bfloat16, "cache.k")
+        _expect(v, (layers, B, cap, Hkv, d), torch.bfloat16, "cache.v")
+        _expect(prefix_mask, (B, cap), torch.uint8, "prefix_mask")
+        if length is not None and not 0 <= length <= cap:
+            raise ValueError(f"cache length {length} outside [0, {cap}]")
         self.k, self.v, self.prefix_mask = k, v, prefix_mask
         self.struct = PiKvCache(_ptr(k, torch.bfloat16, "cache.k"), _ptr(v, torch.bfloat16, "cache.v"),
                                 _ptr(prefix_mask, torch.uint8, "prefix_mask"), layers, B, cap, Hkv, d,
@@ -264,8 +304,20 @@ def pi_joint_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mas
                           workspace: Optional[torch.Tensor] = None, stream=None,
                           rope_base: float = 0.0, lse: Optional[torch.Tensor] = None) -> torch.Tensor:
     """``lse`` (fp32 [B, L, Hq]), when given, receives each row's log-sum-exp for a backward pass."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"q, k must be [B, L, H, d], got {tuple(q.shape)}, {tuple(k.shape)}")
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
+    _expect(q, (B, L, Hq, d), torch.bfloat16, "q")
+    _expect(k, (B, L, Hkv, d), torch.bfloat16, "k")
+    _expect(v, (B, L, Hkv, d), torch.bfloat16, "v")
+    _expect(o, (B, L, Hq, d), torch.bfloat16, "o", optional=True)
+    _expect(lse, (B, L, Hq), torch.float32, "lse", optional=True)
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
+    if (mask.B, mask.N) != (B, L):
+        raise ValueError(f"mask built for B={mask.B} N={mask.N}, q has B={B} L={L}")
+    if cache is not None and (cache.struct.B, cache.struct.Hkv, cache.struct.d) != (B, Hkv, d):
+        raise ValueError("cache batch / heads / head_dim do not match q, k")
     if scale is None:
         scale = d ** -0.5
     if o is None:
@@ -299,8 +351,18 @@ def pi_joint_attn_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o:
                            dv: Optional[torch.Tensor] = None, stream=None, rope_base: float = 0.0):
     """Gradients (dq, dk, dv) of the prefill for upstream gradient ``dout``; ``o`` and ``lse``
     are the prefill's output and log-sum-exp (taken with the same ``rope_base``)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"q, k must be [B, L, H, d], got {tuple(q.shape)}, {tuple(k.shape)}")
     B, L, Hq, d = q.shape
     Hkv = k.shape[2]
+    for t, n in ((q, "q"), (o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(t, (B, L, Hq, d), torch.bfloat16, n, optional=n == "dq")
+    for t, n in ((k, "k"), (v, "v"), (dk, "dk"), (dv, "dv")):
+        _expect(t, (B, L, Hkv, d), torch.bfloat16, n, optional=n in ("dk", "dv"))
+    _expect(lse, (B, L, Hq), torch.float32, "lse")
+    _expect(workspace, (None,), torch.uint8, "workspace")
+    if (mask.B, mask.N) != (B, L):
+        raise ValueError(f"mask built for B={mask.B} N={mask.N}, q has B={B} L={L}")
     if scale is None:
         scale = d ** -0.5
     dq = torch.empty_like(q) if dq is None else dq
@@ -319,6 +381,19 @@ class LayerStream:
     """Device weights of one stream of a joint layer (keeps the tensors alive)."""
 
     def __init__(self, w_qkv, w_o, w_up, w_down, norm1=None, norm2=None, mod1=None, mod2=None):
+        if w_qkv.dim() != 2 or w_up.dim() != 2:
+            raise ValueError("w_qkv and w_up must be matrices")
+        W, F = int(w_qkv.shape[1]), int(w_up.shape[0])
+        _expect(w_qkv, (None, W), torch.bfloat16, "w_qkv")
+        _expect(w_o, (W, None), torch.bfloat16, "w_o")
+        _expect(w_up, (F, W), torch.bfloat16, "w_up")
+        _expect(w_down, (W, F), torch.bfloat16, "w_down")
+        if w_qkv.shape[0] != w_o.shape[1] + 2 * 256:
+            raise ValueError(f"w_qkv has {w_qkv.shape[0]} rows, expected Hq*d + 2*Hkv*d = {w_o.shape[1] + 512}")
+        for t, n in ((norm1, "norm1"), (norm2, "norm2")):
+            _expect(t, (W,), torch.float32, n, optional=True)
+        for t, n in ((mod1, "mod1"), (mod2, "mod2")):
+            _expect(t, (2 * W, W), torch.bfloat16, n, optional=True)
         self.tensors = dict(w_qkv=w_qkv, w_o=w_o, w_up=w_up, w_down=w_down, norm1=norm1, norm2=norm2, mod1=mod1,
                             mod2=mod2)
         bf = lambda t, n: _ptr(t, torch.bfloat16, n) if t is not None else None
@@ -346,6 +421,15 @@ def pi_joint_layer_forward(prefix: LayerStream, expert: LayerStream, h_p: torch.
     """One joint layer; updates h_p [B, Np, Wp] and h_e [B, Ne, We] (fp32) in place."""
     B, Np = h_p.shape[:2]
     Ne = h_e.shape[1]
+    _expect(h_p, (B, Np, prefix.struct.width), torch.float32, "h_p")
+    _expect(h_e, (B, Ne, expert.struct.width), torch.float32, "h_e")
+    # cond conditions the adaptive stream; a stream with no tokens needs none
+    adaptive = [st for st, n in ((prefix, Np), (expert, Ne)) if st.tensors["mod1"] is not None and n > 0]
+    if adaptive:
+        _expect(cond, (B, adaptive[0].struct.width), torch.float32, "cond")
+    _expect(workspace, (None,), torch.uint8, "workspace")
+    if (mask.B, mask.N) != (B, Np + Ne):
+        raise ValueError(f"mask built for B={mask.B} N={mask.N}, layer has B={B} N={Np + Ne}")
     if scale is None:
         scale = 256 ** -0.5
     _check("pi_joint_layer_forward", lib().pi_joint_layer_forward(
@@ -368,6 +452,12 @@ def pi_prefix_layer_forward(prefix: LayerStream, h_p: torch.Tensor, mask: Mask, 
     """The prefix stream's layer alone; updates h_p [B, Np, W] (fp32) in place and writes
     the layer's K/V into cache layer `layer` (slots [0, Np))."""
     B, Np = h_p.shape[:2]
+    _expect(h_p, (B, Np, prefix.struct.width), torch.float32, "h_p")
+    if prefix.tensors["mod1"] is not None:
+        _expect(cond, (B, prefix.struct.width), torch.float32, "cond")
+    _expect(workspace, (None,), torch.uint8, "workspace")
+    if (mask.B, mask.N) != (B, Np):
+        raise ValueError(f"mask built for B={mask.B} N={mask.N}, prefix has B={B} N={Np}")
     if scale is None:
         scale = 256 ** -0.5
     _check("pi_prefix_layer_forward", lib().pi_prefix_layer_forward(
@@ -393,6 +483,13 @@ def pi_expert_layer_decode(expert: LayerStream, cache: "KVCache", layer: int, h_
                            scale: Optional[float] = None, stream=None) -> None:
     """The expert stream's layer against cache layer `layer`; updates h_e [B, S, W] (fp32) in place."""
     B, S = h_e.shape[:2]
+    _expect(h_e, (B, S, expert.struct.width), torch.float32, "h_e")
+    if expert.tensors["mod1"] is not None:
+        _expect(cond, (B, expert.struct.width), torch.float32, "cond")
+    _expect(suffix_ar, (S,), torch.uint8, "suffix_ar")
+    _expect(workspace, (None,), torch.uint8, "workspace")
+    if cache.struct.B != B:
+        raise ValueError(f"cache holds B={cache.struct.B} samples, h_e has {B}")
     if scale is None:
         scale = 256 ** -0.5
     _check("pi_expert_layer_decode", lib().pi_expert_layer_decode(
@@ -417,7 +514,18 @@ def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: to
                           rope_base: float = 0.0) -> torch.Tensor:
     """``workspace`` from decode_workspace() enables the key split of small batches (None runs unsplit)
     and is required with ``rope_base`` > 0."""
+    if q_s.dim() != 4:
+        raise ValueError(f"q_s must be [B, S, Hq, d], got {tuple(q_s.shape)}")
     B, S, Hq, d = q_s.shape
+    c = cache.struct
+    if (c.B, c.d) != (B, d):
+        raise ValueError(f"cache holds B={c.B}, d={c.d}; q_s has B={B}, d={d}")
+    _expect(q_s, (B, S, Hq, d), torch.bfloat16, "q_s")
+    _expect(k_s, (B, S, c.Hkv, d), torch.bfloat16, "k_s")
+    _expect(v_s, (B, S, c.Hkv, d), torch.bfloat16, "v_s")
+    _expect(suffix_ar, (S,), torch.uint8, "suffix_ar")
+    _expect(o_s, (B, S, Hq, d), torch.bfloat16, "o_s", optional=True)
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
     if scale is None:
         scale = d ** -0.5
     if o_s is None:
@@ -433,8 +541,12 @@ def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: to
 def pi_rope_apply(x: torch.Tensor, pos: torch.Tensor, base: float = 10000.0, y: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """Rotary embedding of x [B, L, H, d] bf16 at positions pos [B, L] int32 (y may be x)."""
+    if x.dim() != 4:
+        raise ValueError(f"x must be [B, L, H, d], got {tuple(x.shape)}")
     B, L, H, d = x.shape
-    assert pos.shape == (B, L)
+    _expect(x, (B, L, H, d), torch.bfloat16, "x")
+    _expect(pos, (B, L), torch.int32, "pos")
+    _expect(y, (B, L, H, d), torch.bfloat16, "y", optional=True)
     if y is None:
         y = torch.empty_like(x)
     _check("pi_rope_apply", lib().pi_rope_apply(_ptr(x, torch.bfloat16, "x"), _ptr(y, torch.bfloat16, "y"), B, L, H,
@@ -446,14 +558,20 @@ def pi_kv_cache_append(cache: KVCache, layer: int, k_new: torch.Tensor, v_new: t
                        rope_base: float = 0.0, stream=None) -> None:
     """Write k_new/v_new [B, n, Hkv, d] at slots [len, len + n) of one layer and mark them valid.
     The caller advances the length (KVCache.advance) once every layer has its tokens."""
+    c = cache.struct
+    if k_new.dim() != 4:
+        raise ValueError(f"k_new must be [B, n, Hkv, d], got {tuple(k_new.shape)}")
     n = k_new.shape[1]
+    _expect(k_new, (c.B, n, c.Hkv, c.d), torch.bfloat16, "k_new")
+    _expect(v_new, (c.B, n, c.Hkv, c.d), torch.bfloat16, "v_new")
     _check("pi_kv_cache_append", lib().pi_kv_cache_append(
         ctypes.byref(cache.struct), layer, _ptr(k_new, torch.bfloat16, "k_new"), _ptr(v_new, torch.bfloat16, "v_new"),
         n, rope_base, _stream(stream)))
 
 
 def pi_euler_update(x: torch.Tensor, v: torch.Tensor, dt: float, stream=None) -> torch.Tensor:
-    assert x.numel() == v.numel()
+    _expect(x, tuple(x.shape), torch.float32, "x")
+    _expect(v, tuple(x.shape), torch.float32, "v")
     _check("pi_euler_update", lib().pi_euler_update(_ptr(x, torch.float32, "x"), _ptr(v, torch.float32, "v"), dt,
                                                     x.numel(), _stream(stream)))
     return x
@@ -470,7 +588,14 @@ class VelocityNet:
 
     def __init__(self, tensors: dict, Hq=8, Hkv=1, d=256):
         self.t = tensors
+        if tensors["w_in"].dim() != 2:
+            raise ValueError("w_in must be [W, A]")
         W, A = tensors["w_in"].shape
+        shapes = dict(w_state=(W, A), b_state=(W,), w_in=(W, A), b_in=(W,), w_time=(W,), w_q=(Hq * d, W),
+                      w_k=(Hkv * d, W), w_v=(Hkv * d, W), w_o=(W, Hq * d), w_out=(A, W), b_out=(A,))
+        for f in self.FIELDS:
+            want = torch.bfloat16 if f.startswith("w_") and f != "w_time" else torch.float32
+            _expect(tensors[f], shapes[f], want, f)
         ptrs = []
         for f in self.FIELDS:
             want = torch.bfloat16 if f.startswith("w_") and f != "w_time" else torch.float32
@@ -503,11 +628,21 @@ def flow_workspace(net: VelocityNet, B: int, H: int, device) -> torch.Tensor:
 def pi_velocity_eval(net: VelocityNet, cache: KVCache, suffix_ar: torch.Tensor, state: torch.Tensor, x: torch.Tensor,
                      t: float, vel: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, H, A], got {tuple(x.shape)}")
     B, H, A = x.shape
+    _expect(x, (B, H, net.action_dim), torch.float32, "x")
+    _expect(state, (B, A), torch.float32, "state")
+    _expect(suffix_ar, (H + 1,), torch.uint8, "suffix_ar")
+    _expect(vel, (B, H, A), torch.float32, "vel", optional=True)
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
+    if cache.struct.B != B:
+        raise ValueError(f"cache holds B={cache.struct.B} samples, x has {B}")
     if vel is None:
         vel = torch.empty_like(x)
     if workspace is None:
         workspace = flow_workspace(net, B, H, x.device)
+        _own(workspace, stream)
     _check("pi_velocity_eval", lib().pi_velocity_eval(
         ctypes.byref(net.struct), ctypes.byref(cache.struct), _ptr(suffix_ar, torch.uint8, "suffix_ar"),
         _ptr(state, torch.float32, "state"), _ptr(x, torch.float32, "x"), t, _ptr(vel, torch.float32, "vel"), B, H,
@@ -518,9 +653,22 @@ def pi_velocity_eval(net: VelocityNet, cache: KVCache, suffix_ar: torch.Tensor, 
 def pi_flow_sample(net: Optional[VelocityNet], cache: Optional[KVCache], suffix_ar: Optional[torch.Tensor],
                    state: Optional[torch.Tensor], v_const: Optional[torch.Tensor], x: torch.Tensor,
                    num_steps: int = 10, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, H, A], got {tuple(x.shape)}")
     B, H, A = x.shape
+    _expect(x, (B, H, A), torch.float32, "x")
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
+    if net is not None:
+        if cache is None or cache.struct.B != B:
+            raise ValueError("net mode needs a cache holding the batch's B samples")
+        _expect(x, (B, H, net.action_dim), torch.float32, "x")
+        _expect(state, (B, A), torch.float32, "state")
+        _expect(suffix_ar, (H + 1,), torch.uint8, "suffix_ar")
+    else:
+        _expect(v_const, (B, H, A), torch.float32, "v_const")
     if net is not None and workspace is None:
         workspace = flow_workspace(net, B, H, x.device)
+        _own(workspace, stream)
     _check("pi_flow_sample", lib().pi_flow_sample(
         ctypes.byref(net.struct) if net is not None else None,
         ctypes.byref(cache.struct) if cache is not None else None,
@@ -543,7 +691,16 @@ class ExpertNet:
     def __init__(self, tensors: dict, layers: list):
         self.t = tensors
         self.layers = layers
+        if tensors["w_in"].dim() != 2:
+            raise ValueError("w_in must be [W, A]")
         W, A = tensors["w_in"].shape
+        shapes = dict(w_in=(W, A), b_in=(W,), w_t1=(W, W), b_t1=(W,), w_t2=(W, W), b_t2=(W,), mod_f=(2 * W, W),
+                      w_out=(A, W), b_out=(A,))
+        for f in self.FIELDS:
+            _expect(tensors[f], shapes[f], torch.bfloat16 if f.startswith(("w_", "mod")) else torch.float32, f)
+        for i, l in enumerate(layers):
+            if l.struct.width != W or l.tensors["mod1"] is None:
+                raise ValueError(f"expert layer {i} must be an adaptive stream of width {W}")
         self._arr = (PiLayerStream * len(layers))(*[l.struct for l in layers])
         p = {f: _ptr(tensors[f], torch.bfloat16 if f.startswith(("w_", "mod")) else torch.float32, f)
              for f in self.FIELDS}
@@ -581,11 +738,20 @@ def expert_flow_workspace(net: ExpertNet, cache: KVCache, H: int, num_steps: int
 def pi_expert_velocity_eval(net: ExpertNet, cache: KVCache, suffix_ar: torch.Tensor, x: torch.Tensor, t: float,
                             vel: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                             stream=None) -> torch.Tensor:
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, H, A], got {tuple(x.shape)}")
     B, H, A = x.shape
+    _expect(x, (B, H, net.action_dim), torch.float32, "x")
+    _expect(suffix_ar, (H,), torch.uint8, "suffix_ar")
+    _expect(vel, (B, H, A), torch.float32, "vel", optional=True)
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
+    if cache.struct.B != B:
+        raise ValueError(f"cache holds B={cache.struct.B} samples, x has {B}")
     if vel is None:
         vel = torch.empty_like(x)
     if workspace is None:
         workspace = expert_flow_workspace(net, cache, H, 1)
+        _own(workspace, stream)
     _check("pi_expert_velocity_eval", lib().pi_expert_velocity_eval(
         ctypes.byref(net.struct), ctypes.byref(cache.struct), _ptr(suffix_ar, torch.uint8, "suffix_ar"),
         _ptr(x, torch.float32, "x"), t, _ptr(vel, torch.float32, "vel"), B, H, A,
@@ -596,9 +762,17 @@ def pi_expert_velocity_eval(net: ExpertNet, cache: KVCache, suffix_ar: torch.Ten
 def pi_expert_flow_sample(net: ExpertNet, cache: KVCache, suffix_ar: torch.Tensor, x: torch.Tensor,
                           num_steps: int = 10, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Euler sampler with the expert net: x [B, H, A] fp32 holds the noise and ends as the actions."""
+    if x.dim() != 3:
+        raise ValueError(f"x must be [B, H, A], got {tuple(x.shape)}")
     B, H, A = x.shape
+    _expect(x, (B, H, net.action_dim), torch.float32, "x")
+    _expect(suffix_ar, (H,), torch.uint8, "suffix_ar")
+    _expect(workspace, (None,), torch.uint8, "workspace", optional=True)
+    if cache.struct.B != B:
+        raise ValueError(f"cache holds B={cache.struct.B} samples, x has {B}")
     if workspace is None:
         workspace = expert_flow_workspace(net, cache, H, num_steps)
+        _own(workspace, stream)
     _check("pi_expert_flow_sample", lib().pi_expert_flow_sample(
         ctypes.byref(net.struct), ctypes.byref(cache.struct), _ptr(suffix_ar, torch.uint8, "suffix_ar"),
         _ptr(x, torch.float32, "x"), B, H, A, num_steps, _ptr(workspace, torch.uint8, "workspace"),

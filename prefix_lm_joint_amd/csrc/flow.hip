@@ -220,6 +220,20 @@ __global__ void repack_kernel(const __bf16* __restrict__ src, __bf16* __restrict
   *reinterpret_cast<bf16x8*>(dst + tiled_offset(row0 + r, k, K)) = v;
 }
 
+// Zero the pad rows [S*Hq, pad16(S*Hq)) of each sample's queries in the decode's
+// tile layout (width d).  No product writes them, yet the decode reads them as
+// whole 16-row blocks: left as they were, leftover values would reach the
+// scores of rows that are never stored (and could make the softmax redo a
+// workgroup for nothing).  One thread per element.
+__global__ void zero_q_pad_kernel(__bf16* __restrict__ q, int rows, int rows_pad, int d, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int per = (rows_pad - rows) * d;
+  const int64_t b = i / per;
+  const int j = (int)(i % per);
+  q[tiled_offset(b * rows_pad + rows + j / d, j % d, d)] = f2bf(0.f);
+}
+
 __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v, float dt, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t i4 = 4 * i;
@@ -335,6 +349,15 @@ pi_status repack_weights(const pi_velocity_net* n, const FlowWs& w, hipStream_t 
   return st;
 }
 
+// Once per call: zero the pad rows of the tiled queries (see zero_q_pad_kernel).
+pi_status clear_q_pad(const pi_velocity_net* n, const FlowWs& w, int B, int S, hipStream_t s) {
+  const int rows = S * n->Hq, rows_pad = pad16(rows);
+  if (rows_pad == rows) return PI_OK;
+  const int64_t total = (int64_t)B * (rows_pad - rows) * n->d;
+  zero_q_pad_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(w.q, rows, rows_pad, n->d, total);
+  return pi::check_launch("zero_q_pad_kernel");
+}
+
 // v = net(x, t) into `vel` (EPI_VEL) or fused x += dt*v (EPI_EULER, vel ignored).
 template <int EPI>
 pi_status run_net(const pi_velocity_net* n, const pi_kv_cache* cache, const uint8_t* suffix_ar,
@@ -429,6 +452,7 @@ extern "C" pi_status pi_velocity_eval(const pi_velocity_net* net, const pi_kv_ca
              "pi_velocity_eval: workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = repack_weights(net, w, s);
+  if (st == PI_OK) st = clear_q_pad(net, w, B, H + 1, s);
   if (st != PI_OK) return st;
   return run_net<EPI_VEL>(net, cache, suffix_ar, state, const_cast<float*>(x), t, 0.f, vel, B, H, A, w, s);
 }
@@ -458,6 +482,7 @@ extern "C" pi_status pi_flow_sample(const pi_velocity_net* net, const pi_kv_cach
   PI_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255u) == 0, PI_ERR_INVALID_ARG,
              "pi_flow_sample: workspace must be 256-byte aligned");
   st = repack_weights(net, w, s);
+  if (st == PI_OK) st = clear_q_pad(net, w, B, H + 1, s);
   if (st != PI_OK) return st;
   for (int k = 0; k < num_steps; ++k) {
     const float t = (float)(1.0 + k * dt);
