@@ -41,6 +41,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--kernel-iters", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward", "sampler", "pi05",
                                       "layer", "expert"],
                    default=None,
@@ -552,55 +553,113 @@ def counted_traffic(kernel, summary):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle on the host cores, bounded sample
+# CPU baseline: the fp64 oracle on the host cores, bounded sample.  It runs in a
+# child process of its own (`--cpu-baseline-child`) that never touches the GPU,
+# so its process pool can fork freely.
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(sample_prefill_layers=2, sample_evals=1):
+_CPU = {}   # the sample's inputs, set before the pool forks (workers inherit them)
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    _CPU["limit"] = threadpool_limits(1)      # one BLAS thread per worker process
+
+
+def _cpu_prefill_rows(task):
+    from oracle import attention as OA
+    layer, rows = task
+    q, k, v = _CPU["qkv"][layer]
+    out = OA.joint_attention(q, k, v, _CPU["valid"], _CPU["ar"], rows=rows)
+    return [out[b, i] for b, i in rows]
+
+
+def cpu_baseline_child(sample_prefill_layers=3, sample_evals=2):
+    """The oracle's π0 control step (prefill of the 816-token prefix x 18 layers,
+    then 10 velocity evaluations through the 18 cache layers), timed on a bounded
+    sample and scaled: once on one core (every BLAS pool limited to one thread),
+    once on all usable cores (prefill rows over a process pool of one-thread
+    workers; the velocity net, sequential over layers, with that many BLAS
+    threads).  Prints one JSON object."""
+    import multiprocessing as mp
     import numpy as np
+    from threadpoolctl import threadpool_limits
     from oracle import attention as OA
     from oracle import flow as OF
     from prefix_lm_joint_amd import inputs as I
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    host_cores = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else host_cores
+    workers = max(1, min(usable, 16))
     w = I.pi0_step()
     s = w.structure
     P, H, A, L = s.n_prefix, w.horizon, w.action_dim, w.layers
     f64 = I.bf16_bits_to_f64
     valid = np.ones((1, P), np.uint8)
-    t0 = time.perf_counter()
-    for l in range(sample_prefill_layers):
-        q = f64(I.bf16_normal(9000 + l, (1, P, 8, 256)))
-        k = f64(I.bf16_normal(9100 + l, (1, P, 1, 256)))
-        v = f64(I.bf16_normal(9200 + l, (1, P, 1, 256)))
-        OA.joint_attention(q, k, v, valid, s.ar[:P])
-    t_pre = (time.perf_counter() - t0) / sample_prefill_layers
+    _CPU.update(valid=valid, ar=s.ar[:P], qkv=[
+        (f64(I.bf16_normal(9000 + l, (1, P, 8, 256))), f64(I.bf16_normal(9100 + l, (1, P, 1, 256))),
+         f64(I.bf16_normal(9200 + l, (1, P, 1, 256)))) for l in range(sample_prefill_layers)])
     nw = I.net_weights(9300, width=w.width, action_dim=A)
     wf = {f: (f64(getattr(nw, f)) if getattr(nw, f).dtype == np.uint16 else getattr(nw, f).astype(np.float64))
           for f in nw.__dataclass_fields__}
     ck = f64(I.bf16_normal(9400, (L, 1, P, 1, 256)))
     cv = f64(I.bf16_normal(9401, (L, 1, P, 1, 256)))
     state = I.f32_normal(9402, (1, A)).astype(np.float64)
-    x = I.f32_normal(9403, (1, H, A)).astype(np.float64)
-    t0 = time.perf_counter()
-    for _ in range(sample_evals):
-        vel = OF.velocity_net(x, 0.5, state, wf, ck, cv, valid, s.ar[P:], 8, 1, 256)
-        x = OF.euler_update(x, vel, -0.1)
-    t_eval = (time.perf_counter() - t0) / sample_evals
-    t_step = L * t_pre + w.steps * t_eval
-    return {
-        "value": 1.0 / t_step, "unit": "control steps/s", "cores": int(cores), "kind": "oracle",
-        "sample": (f"pi0 control step scaled from {sample_prefill_layers} timed prefill layers "
-                   f"({t_pre:.2f} s/layer, x{L}) and {sample_evals} timed velocity evaluations "
-                   f"({t_eval:.2f} s each, 18 layers, x{w.steps}); fp64 numpy"),
-        "seconds_per_control_step": t_step,
-    }
+    x0 = I.f32_normal(9403, (1, H, A)).astype(np.float64)
+
+    def evals():
+        x = x0
+        t0 = time.perf_counter()
+        for k in range(sample_evals):
+            x = OF.euler_update(x, OF.velocity_net(x, 1.0 - 0.1 * k, state, wf, ck, cv, valid, s.ar[P:], 8, 1, 256),
+                                -0.1)
+        return (time.perf_counter() - t0) / sample_evals
+
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for l in range(sample_prefill_layers):
+            q, k, v = _CPU["qkv"][l]
+            OA.joint_attention(q, k, v, valid, s.ar[:P])
+        pre_1 = (time.perf_counter() - t0) / sample_prefill_layers
+        eval_1 = evals()
+    rows = [(0, i) for i in range(P)]
+    chunks = [rows[j::workers] for j in range(workers)]
+    with mp.get_context("fork").Pool(workers, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_prefill_rows, [(0, c) for c in chunks])          # start the workers
+        t0 = time.perf_counter()
+        for l in range(sample_prefill_layers):
+            pool.map(_cpu_prefill_rows, [(l, c) for c in chunks])
+        pre_n = (time.perf_counter() - t0) / sample_prefill_layers
+    with threadpool_limits(workers):
+        eval_n = evals()
+    step_1 = L * pre_1 + w.steps * eval_1
+    step_n = L * pre_n + w.steps * eval_n
+    print(json.dumps({
+        "value": 1.0 / step_n, "unit": "control steps/s", "cores": workers, "kind": "oracle",
+        "extrapolated": True, "host_cores": host_cores, "usable_cores": usable, "threads_used": workers,
+        "single_core_s": step_1, "seconds_per_control_step": step_n,
+        "sample": (f"pi0 control step (B=1, 816-token prefix x 18 layers, then 10 velocity evaluations x 18 layers), "
+                   f"extrapolated from {sample_prefill_layers} timed prefill layers and {sample_evals} timed velocity "
+                   f"evaluations; all cores: {pre_n:.3f} s/prefill layer over {workers} one-thread processes, "
+                   f"{eval_n:.3f} s/evaluation with {workers} BLAS threads; one core: {pre_1:.3f} and {eval_1:.3f} s; "
+                   f"fp64 numpy oracle"),
+    }))
+
+
+def cpu_baseline():
+    """Run cpu_baseline_child in a child process (the oracle never shares a process with the GPU work)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child"], capture_output=True,
+                       text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"cpu baseline failed ({r.returncode}): {r.stderr[-2000:]}")
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def main():
     args = parse()
+    if args.cpu_baseline_child:
+        cpu_baseline_child()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this path is "
