@@ -26,7 +26,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["mask.hip", "attention.hip", "attention_bwd.hip", "layer.hip", "flow.hip", "rope.hip", "status.cpp"]
+SOURCES = ["mask.hip", "attention.hip", "attention32.hip", "attention_bwd.hip", "layer.hip", "flow.hip", "rope.hip", "status.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -32,6 +32,7 @@
 //   * Key tiles classified EMPTY by the mask builder are skipped; FULL tiles skip
 //     the per-pair rule.  Workgroups of one (sample, KV head) are placed on one
 //     XCD so their K/V reads share that XCD's L2.
+#include "attention32.h"
 #include "common.h"
 #include "engine.h"
 
@@ -964,7 +965,7 @@ int decode_splits_for(int B, int S, int len, int min_tiles = 2) {
 bool small_decode(int B, int S) { return S > 1 && B * ((S + CfgDec::TOK - 1) / CfgDec::TOK) <= 16; }
 int decode_splits(int B, int S, int len) {
   if (S == 1) return decode_splits_for<CfgAr>(B, S, len);
-  return small_decode(B, S) ? decode_splits_for<CfgDecS>(B, S, len, 3) : decode_splits_for<CfgDec>(B, S, len);
+  return small_decode(B, S) ? decode_splits_for<CfgDecS>(B, S, len, 3) : pi32::decode_splits(B, S, len);
 }
 
 // Key splits for a GQA 8:1 prefill of B samples of L tokens (same rule as the
@@ -992,7 +993,7 @@ size_t rope_ks_bytes(int B, int S) { return pi::align_up((size_t)B * S * 256 * 2
 // Decode workspace: [rotated suffix K (rotary embedding only)] [key-split partials].
 size_t decode_split_bytes(int B, int S, int splits) {
   if (S == 1) return split_ws_bytes<CfgAr>(B, S, splits);
-  return small_decode(B, S) ? split_ws_bytes<CfgDecS>(B, S, splits) : split_ws_bytes<CfgDec>(B, S, splits);
+  return small_decode(B, S) ? split_ws_bytes<CfgDecS>(B, S, splits) : pi32::decode_split_bytes(B, S, splits);
 }
 size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
   (void)Hq;
@@ -1003,11 +1004,7 @@ size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
 
 size_t pi::decode_workspace_max(int B, int S, int Hq) {
   // the most splits any cache length can take, for the shape decode_splits picks
-  const bool sm = small_decode(B, S);
-  const int tok = sm ? CfgDecS::TOK : CfgDec::TOK;
-  const int n_qblk = (S + tok - 1) / tok;
-  const int splits = std::max(1, std::min(kMaxSplit, 256 / std::max(1, B * n_qblk)));
-  return decode_ws_bytes(B, S, Hq, splits);
+  return decode_ws_bytes(B, S, Hq, decode_splits(B, S, kMaxTiles * TK));
 }
 
 // Bytes of the rotated K a prefill with the rotary embedding keeps in its workspace.
@@ -1015,7 +1012,8 @@ static size_t rope_k_bytes(int B, int L, int Hkv, int d) { return pi::align_up((
 
 extern "C" size_t pi_prefill_workspace_bytes(int B, int L, int Hq, int Hkv, int d) {
   if (B < 1 || L < 1) return 0;
-  if (Hq == 8 && Hkv == 1 && d == 256) return rope_k_bytes(B, L, Hkv, d) + split_ws_bytes<CfgG8>(B, L, prefill_splits(B, L));
+  if (Hq == 8 && Hkv == 1 && d == 256)
+    return rope_k_bytes(B, L, Hkv, d) + pi32::prefill_split_bytes(B, Hkv, L, pi32::prefill_splits(B, Hkv, L));
   if (Hq == Hkv && d == 64) return rope_k_bytes(B, L, Hkv, d);
   return 0;
 }
@@ -1069,20 +1067,7 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
   char* split_ws = workspace ? static_cast<char*>(workspace) + rot_bytes : nullptr;
   const size_t split_avail = workspace ? workspace_bytes - rot_bytes : 0;
   if (gqa8) {
-    int splits = prefill_splits(B, L);
-    if (split_ws == nullptr || split_avail < split_ws_bytes<CfgG8>(B, L, splits)) splits = 1;
-    const int n_qblk = (L + CfgG8::TOK - 1) / CfgG8::TOK;
-    const size_t chunks = (size_t)splits * B * n_qblk * kNW256 * kNR256;
-    float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
-    float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
-                               : nullptr;
-    st = launch_prefill<256, 8, kNR256, kNW256>(q, kk, v, o, B, L, Hq, Hkv, scale, mask, splits, opart, mlpart,
-                                                rope_base, splits > 1 ? nullptr : lse, s);
-    if (st == PI_OK && splits > 1) {
-      decode_combine_kernel<kNR256, kNW256><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
-          opart, mlpart, static_cast<__bf16*>(o), 0, B, L, n_qblk, splits, lse);
-      st = pi::check_launch("decode_combine_kernel");
-    }
+    st = pi32::prefill(q, kk, v, o, B, L, Hq, Hkv, scale, mask, rope_base, lse, split_ws, split_avail, s);
   } else {
     st = launch_prefill<64, 1, kNR64, kNW64>(q, kk, v, o, B, L, Hq, Hkv, scale, mask, 1, nullptr, nullptr,
                                              rope_base, lse, s);
@@ -1186,8 +1171,8 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   if (small_decode(B, S))
     return launch_decode<kNWdecS>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
                                   split_ws, split_avail, s);
-  return launch_decode<kNWdec>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
-                               split_ws, split_avail, s);
+  return pi32::decode(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled, split_ws,
+                      split_avail, s);
 }
 
 extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s, const void* k_s,

@@ -1,0 +1,908 @@
+// Grouped-query attention at head_dim 256 with 8 query heads per KV head on
+// 32x32x16 matrix-core steps, gfx950: the prefill over the pooled K/V and the
+// cached suffix decode.
+//
+// What is computed ("π0.5 vs MM-DiT joint attention", first section; "VLA 代码精读"
+// §1.5, §1.6): per (sample, query token, head) one softmax over every visible key
+// of the concatenated pool, query head h reading KV head floor(h*Hkv/Hq); masked
+// keys are excluded by selection (score -inf before the maximum, weight 0).
+//
+// Organisation:
+//   * A wave owns 32 query rows = 4 tokens x 8 heads, so every K/V element it
+//     reads from LDS serves 8 heads and each matrix-core operand fragment feeds a
+//     32 x 32 product: half the LDS bytes per flop of 16-row tiles.  A workgroup
+//     is four waves (128 rows = 16 tokens), one per SIMD, each holding its Q
+//     fragments (64 registers) and its fp32 O^T (128 registers) for the whole
+//     key loop.
+//   * Products are transposed: S^T = K Q^T (A = K from LDS, B = Q^T from
+//     registers), then O^T += V^T P^T with P^T taken straight from the S^T
+//     accumulators.  In the 32x32 accumulator a lane holds 16 keys of ONE query
+//     row (lane l: row l % 32, keys 8(i/4) + 4(l/32) + i%4), so a row's
+//     statistics live in two lanes (l and l ^ 32).  The P^T operand of the
+//     product over keys 16a..16a+15 is the lane's own elements 8a..8a+7 when the
+//     contraction index k = 8(l/32) + t stands for key 16a + 4(l/32) + (t&3) +
+//     8(t>>2); the V^T operand is read in that key order by two transposing LDS
+//     reads (ds_read_b64_tr_b16) of 4 keys each.
+//   * K/V tiles of 32 keys go from global memory straight into LDS (buffer loads
+//     with the LDS destination) over four stages; every wave issues a quarter of
+//     a tile's loads, spread through its products.  LDS rows are unpadded;
+//     16-byte chunks are XOR-swizzled by row (K: chunk ^ (r & 15), for 16 lanes
+//     reading 16 rows at one chunk; V: chunk ^ 4(r & 3), for 32 lanes reading 4
+//     rows x 64 bytes transposed), applied to the global source chunk each lane
+//     fetches, so both operand reads are bank-conflict free.
+//   * Softmax in base 2 against a per-row reference maximum fixed at the row's
+//     first tile with a visible key; weights may exceed 1 and the final 1/l
+//     removes the reference.  If a row's maximum ends more than kGrowth above
+//     it, the workgroup redoes its tiles with the true maximum.  Row sums add the
+//     bf16 weights that multiply V (v_dot2 with ones).
+//   * Step i runs tile i-1's PV and tile i+1's scores on the matrix cores, with
+//     tile i's weights computed between them, while tile i+2 streams in.
+#include "attention32.h"
+
+#include <math.h>
+
+#include <algorithm>
+#include <type_traits>
+
+namespace {
+
+using namespace pi_engine;
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+constexpr int D = 256;
+constexpr int G = 8;              // query heads per KV head
+constexpr int ROWS_W = 32;        // query rows per wave
+constexpr int NW = 4;             // waves per workgroup
+constexpr int ROWS = NW * ROWS_W; // 128
+constexpr int TOK = ROWS / G;     // 16 query tokens per workgroup
+constexpr int THREADS = NW * 64;
+constexpr int kLoadsPerWave = (TK * D * 2 / 1024) / NW;   // 1 KB loads of each tensor per wave and tile: 4
+constexpr float kGrowth = 64.0f;
+constexpr int kMaxSplit32 = 16;
+
+struct Stage {
+  alignas(16) __bf16 k[TK * D];
+  alignas(16) __bf16 v[TK * D];
+  alignas(16) uint32_t w[64];     // per-key mask words (lanes >= 32 land as zeros)
+};
+
+__device__ __forceinline__ int fk(int r) { return r & 15; }
+__device__ __forceinline__ int fv(int r) { return 4 * (r & 3); }
+
+// Per-lane byte offsets computed once.
+//   kr[j]: K fragment j (j < 8; j + 8 is kr[j] + 256): key row l % 32, logical chunk 2j + l/32.
+//   vr[c]: V^T fragment of d chunk c (c < 4; c + 4 is vr[c] + 256), key half 0, first read;
+//          key half a and read e add (16a + 8e) rows.
+//   ld_k/ld_v[n], ld_row[n]: this wave's n-th 1 KB load of a tile (rows 2N, 2N+1 with
+//          N = wave * 4 + n), the source chunk pre-swizzled.
+struct Lanes {
+  uint32_t kr[8];
+  uint32_t vr[4];
+  uint32_t ld_k[kLoadsPerWave], ld_v[kLoadsPerWave];
+  int ld_row[kLoadsPerWave];
+};
+
+__device__ __forceinline__ Lanes make_lanes(int tsb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 31, h = lane >> 5;
+  Lanes lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lo.kr[j] = (uint32_t)(r * D * 2 + 16 * ((2 * j + h) ^ fk(r)));
+  const int g16 = (lane >> 4) & 1, jj = lane & 15;
+  const int vrow = 4 * h + (jj >> 2);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int lchunk = 4 * c + 2 * g16 + ((jj & 3) >> 1);
+    lo.vr[c] = (uint32_t)(vrow * D * 2 + 16 * (lchunk ^ fv(vrow)) + 8 * (jj & 1));
+  }
+#pragma unroll
+  for (int n = 0; n < kLoadsPerWave; ++n) {
+    const int row = 2 * (wave * kLoadsPerWave + n) + (lane >> 5);
+    const int p = lane & 31;
+    lo.ld_row[n] = row;
+    lo.ld_k[n] = (uint32_t)row * (uint32_t)tsb + 16u * (uint32_t)(p ^ fk(row));
+    lo.ld_v[n] = (uint32_t)row * (uint32_t)tsb + 16u * (uint32_t)(p ^ fv(row));
+  }
+  return lo;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* at_bytes(const void* base, uint32_t off) {
+  return reinterpret_cast<const T*>(static_cast<const char*>(base) + off);
+}
+
+__device__ __forceinline__ bf16x8 read_k(const Stage& s, const Lanes& lo, int j) {
+  return *at_bytes<bf16x8>(s.k, lo.kr[j & 7] + (j >> 3) * 256u);
+}
+
+// V^T fragment for product slot j: d chunk j / 2, key half j % 2.
+__device__ __forceinline__ bf16x8 read_v(const Stage& s, const Lanes& lo, int j) {
+  const int c = j >> 1, a = j & 1;
+  const __bf16* p = at_bytes<__bf16>(s.v, lo.vr[c & 3]) + (c >> 2) * 128 + 16 * a * D;
+  const bf16x4 x0 = lds_read_tr4(p);
+  const bf16x4 x1 = lds_read_tr4(p + 8 * D);
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per-wave state: Q^T fragments, O^T, and the row statistics of this lane's row
+// (m: reference maximum in base 2, the same in lanes l and l ^ 32; mobs: this
+// lane's running maximum of its raw scores; l: this lane's sum of its weights).
+struct State {
+  bf16x8 qf[16];
+  f32x16 o[8];
+  float m, mobs, l;
+  uint32_t wq;
+  bool all_set;
+};
+
+__device__ __forceinline__ void init_state(State& st) {
+  st.m = -INFINITY;
+  st.mobs = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[c][i] = 0.f;
+  st.all_set = false;
+}
+
+__device__ __forceinline__ float xhalf_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
+
+// Softmax, branchy part (tile i, before its weights): the per-pair rule of a
+// PARTIAL tile, and until every row of the wave has a reference maximum, the
+// maxima of rows that lack one.
+//   words(q): the key words of this lane's keys 8q + 4(lane/32) .. + 3 of the tile.
+template <typename Words>
+__device__ __forceinline__ void softmax_pre(State& st, f32x16& s, int cls, uint32_t forbid, float scale_log2,
+                                            Words words) {
+  if (cls == PI_TILE_PARTIAL) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w = words(q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!pair_visible(st.wq, w[e], forbid)) s[4 * q + e] = -INFINITY;
+    }
+  }
+  if (!st.all_set) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    const float mt = xhalf_max(mx) * scale_log2;
+    st.m = (st.m == -INFINITY) ? mt : st.m;
+    st.all_set = __ballot(st.m == -INFINITY) == 0ull;
+  }
+}
+
+// A key tile as the loop sees it: d = tile index | class << 16 (| 1 << 24 for a
+// decode suffix tile), m = its key-validity bitmap (w unused).
+struct TileDesc {
+  uint32_t d, m, w;
+};
+
+__device__ __forceinline__ int tile_cls(const TileDesc& t) { return (int)((t.d >> 16) & 0xFFu); }
+
+// This wave's loads of one K/V tile, prepared once per step so that issuing one in
+// a product slot is a single instruction: the two buffer resources (K and V at the
+// tile's first key) and the per-lane offsets of the wave's 2 * kLoadsPerWave loads,
+// out-of-range (zeros) for keys outside the tile's validity mask.
+struct LoadPlan {
+  i32x4 rk, rv;
+  uint32_t off[2 * kLoadsPerWave];
+  uint32_t wo;        // prefill: this lane's offset of the key-word load (out of range: none)
+};
+
+__device__ __forceinline__ LoadPlan plan_kv(const Lanes& lo, const __bf16* k0, const __bf16* v0, int key0, int tsb,
+                                           uint32_t keymask, bool live) {
+  LoadPlan pl;
+  const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(key0) * tsb;
+  pl.rk = make_rsrc(reinterpret_cast<const char*>(k0) + at);
+  pl.rv = make_rsrc(reinterpret_cast<const char*>(v0) + at);
+  // keys to fetch (uniform): every key of a full tile, none past the end
+  const uint32_t fetch = live ? __builtin_amdgcn_readfirstlane(keymask) : 0u;
+  if (fetch == 0xFFFFFFFFu) {
+#pragma unroll
+    for (int n = 0; n < kLoadsPerWave; ++n) {
+      pl.off[n] = lo.ld_k[n];
+      pl.off[kLoadsPerWave + n] = lo.ld_v[n];
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < kLoadsPerWave; ++n) {
+      const bool ok = (fetch >> lo.ld_row[n]) & 1u;
+      pl.off[n] = ok ? lo.ld_k[n] : kOOB;
+      pl.off[kLoadsPerWave + n] = ok ? lo.ld_v[n] : kOOB;
+    }
+  }
+  return pl;
+}
+
+__device__ __forceinline__ void issue_planned(Stage* __restrict__ sg, const LoadPlan& pl, int n) {
+  const bool isv = n >= kLoadsPerWave;
+  const int nn = isv ? n - kLoadsPerWave : n;
+  const int wave = threadIdx.x >> 6;
+  __bf16* dst = (isv ? sg->v : sg->k) + (size_t)(wave * kLoadsPerWave + nn) * 512;
+  pi_buffer_load_lds(isv ? pl.rv : pl.rk, lds_u32(dst), 16, (int)pl.off[n], 0, 0, 0);
+}
+
+// One pipeline step (its parts do not depend on one another):
+//   the branchy softmax part of tile i (mask words in cs);
+//   PV:  O^T += V^T P^T for tile i-1 (weights pp, V in vs);
+//   QK:  S^T = K Q^T for tile i+1 (K in ks) into sn;
+//   weights of tile i (sc -> pn), the row sums and the lane maxima;
+//   this wave's loads of tile i+2 into ld (plan pl), one per slot in the first half.
+// Slot j holds product j of both.  A wave issues in order, so anything in a slot
+// that waits on a result produced in the same slot stalls the products behind it;
+// every chain is therefore spread over slots: the LDS reads run AH slots ahead of
+// their products, and weight j is scaled in slot j-1, exponentiated in slot j,
+// rounded to bf16 (as a pair) two slots later and summed into the row sum two
+// slots after that.  Empty asm statements pin each result to its slot (left
+// alone, the compiler sinks all of them below the last product).  The four
+// stages are distinct, and saying so (restrict) lets the compiler see that the
+// LDS reads do not depend on the loads in flight.
+//   words(cs, t, q): key words of the lane's keys of tile i (descriptor t; see softmax_pre);
+//   issue_words(ld, pl): the key-word load of tile i+2, if the kernel has one;
+//   mid(): work for the next step (its load plan), run halfway, under the products.
+template <bool PV, typename Words, typename IssueWords, typename Mid>
+__device__ __forceinline__ void step_block(const Stage* __restrict__ vs, const Stage* __restrict__ cs,
+                                           const Stage* __restrict__ ks, Stage* __restrict__ ld, const Lanes& lo,
+                                           State& st, const bf16x8 (&pp)[2], f32x16& sc, bf16x8 (&pn)[2],
+                                           f32x16& sn, const TileDesc& tcur, uint32_t forbid, float scale_log2,
+                                           const LoadPlan& pl, Words words, IssueWords issue_words, Mid mid) {
+  constexpr int AH = 3;
+  softmax_pre(st, sc, tile_cls(tcur), forbid, scale_log2, [&](int q) { return words(cs, tcur, q); });
+  issue_words(ld, pl);
+  const float m_use = (st.m == -INFINITY) ? 0.f : st.m;
+  bf16x8 vb[AH], kb[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    if constexpr (PV) vb[j] = read_v(*vs, lo, j);
+    kb[j] = read_k(*ks, lo, j);
+  }
+  float x[16], e[16];
+  bf16x2 pk[8];
+  bf16x2 ones;
+  ones[0] = f2bf(1.0f);
+  ones[1] = f2bf(1.0f);
+  float mloc = st.mobs;
+  x[0] = fmaf(sc[0], scale_log2, -m_use);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if constexpr (PV) st.o[j >> 1] = mfma32(vb[j % AH], pp[j & 1], st.o[j >> 1]);
+    sn = mfma32(kb[j % AH], st.qf[j], j == 0 ? f32x16{} : sn);
+    if (j + AH < 16) {
+      if constexpr (PV) vb[j % AH] = read_v(*vs, lo, j + AH);
+      kb[j % AH] = read_k(*ks, lo, j + AH);
+    }
+    e[j] = __builtin_amdgcn_exp2f(x[j]);
+    asm volatile("" : "+v"(e[j]));
+    if (j + 1 < 16) {
+      x[j + 1] = fmaf(sc[j + 1], scale_log2, -m_use);
+      asm volatile("" : "+v"(x[j + 1]));
+    }
+    if (j & 1) {
+      mloc = fmaxf(mloc, fmaxf(sc[j - 1], sc[j]));
+      asm volatile("" : "+v"(mloc));
+    }
+    if (j >= 3 && (j & 1)) {            // pair (j-3, j-2), exponentiated one and two slots ago
+      const int pr = (j - 3) >> 1;
+      pk[pr][0] = f2bf(e[j - 3]);
+      pk[pr][1] = f2bf(e[j - 2]);
+      asm volatile("" : "+v"(pk[pr]));
+    }
+    if (j >= 5 && (j & 1)) {            // the pair rounded two slots ago
+      const int pr = (j - 5) >> 1;
+      st.l = __builtin_amdgcn_fdot2_f32_bf16(pk[pr], ones, st.l, false);
+      asm volatile("" : "+v"(st.l));
+    }
+    if (j < kLoadsPerWave * 2) issue_planned(ld, pl, j);   // early, so they land before the next barrier
+    if (j == 8) mid();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the next tile's scores stay in vector registers: the products write them there
+  // and the next step's weights read them without a copy out of the accumulators
+  asm volatile("" : "+v"(sn));
+  // the last pairs
+  pk[7][0] = f2bf(e[14]);
+  pk[7][1] = f2bf(e[15]);
+  st.l = __builtin_amdgcn_fdot2_f32_bf16(pk[6], ones, st.l, false);
+  st.l = __builtin_amdgcn_fdot2_f32_bf16(pk[7], ones, st.l, false);
+#pragma unroll
+  for (int pr = 0; pr < 8; ++pr) {
+    pn[pr >> 2][2 * (pr & 3)] = pk[pr][0];
+    pn[pr >> 2][2 * (pr & 3) + 1] = pk[pr][1];
+  }
+  st.mobs = mloc;
+}
+
+__device__ __forceinline__ void pv_last(const Stage& vs, const Lanes& lo, State& st, const bf16x8 (&pp)[2]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.o[j >> 1] = mfma32(read_v(vs, lo, j), pp[j & 1], st.o[j >> 1]);
+}
+
+
+// Tile loop over tiles [i_lo, i_hi); tile j lives in stage (j - i_lo) % 4, and the
+// loop is unrolled by four so every step names its stages statically.  The four
+// stages are four separate LDS objects: the compiler then sees that a step's
+// reads never touch the stage its loads are filling (with one array indexed at
+// run time it makes every transposing read after a load wait for that load).
+// Step i: barrier (this wave's loads of tile i+1 have landed; every wave is past
+// step i-1, so the stage of tile i-2 is free), then the block above with tile
+// i+2's loads spread through it.  Past the end, loads keep going to the free
+// stage with every key out of range (zeros, no memory traffic) and the scores of
+// the missing tile are computed and dropped, which keeps the block free of
+// branches.
+//   desc(j): tile j's descriptor (LDS reads only)
+//   plan(t, live): this wave's load plan of tile t (registers only)
+//   words(stage, q), issue_words(stage, plan): see step_block
+//   prep(): row work that needs the Q registers, once the first loads are out
+template <typename Desc, typename Plan, typename Words, typename IssueWords, typename Prep>
+__device__ __forceinline__ void run_tiles(Stage& s0, Stage& s1, Stage& s2, Stage& s3, const Lanes& lo, State& st,
+                                          int i_lo, int i_hi, Desc desc, Plan plan, Words words,
+                                          IssueWords issue_words, Prep prep, uint32_t forbid, float scale_log2) {
+  if (i_lo >= i_hi) return;
+  auto clamp = [&](int i) { return i < i_hi ? i : i_lo; };
+  {
+    const LoadPlan p0 = plan(desc(i_lo), true);
+    issue_words(&s0, p0);
+#pragma unroll
+    for (int n = 0; n < 2 * kLoadsPerWave; ++n) issue_planned(&s0, p0, n);
+    const bool two = i_lo + 1 < i_hi;
+    const LoadPlan p1 = plan(desc(clamp(i_lo + 1)), two);
+    issue_words(&s1, p1);
+#pragma unroll
+    for (int n = 0; n < 2 * kLoadsPerWave; ++n) issue_planned(&s1, p1, n);
+  }
+  prep();
+  // descriptors of tiles i, i+1 and i+3 and the load plan of tile i+2, for step i = i_lo
+  TileDesc t_cur = desc(i_lo);
+  TileDesc t_n1 = desc(clamp(i_lo + 1));
+  TileDesc t_n3 = desc(clamp(i_lo + 3));
+  LoadPlan pl = plan(desc(clamp(i_lo + 2)), i_lo + 2 < i_hi);
+  __syncthreads();      // the first two tiles have landed
+  f32x16 sc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sc = mfma32(read_k(s0, lo, j), st.qf[j], sc);
+  bf16x8 pp[2];
+  // Step i: tile i+2's loads go out on the plan made during step i-1; halfway
+  // through, the plan of tile i+3 is made from its descriptor, read in step i-1;
+  // tile i+4's descriptor is read at the start.
+  auto step = [&](auto pv, int i, Stage& prev, Stage& cur, Stage& nxt, Stage& ld) {
+    __syncthreads();      // tile i+1 has landed; every wave is done with tile i-2
+    const TileDesc t_n4 = desc(clamp(i + 4));
+    const TileDesc t3 = t_n3;
+    LoadPlan pl_next;
+    bf16x8 pn[2];
+    f32x16 sn;
+    step_block<decltype(pv)::value>(&prev, &cur, &nxt, &ld, lo, st, pp, sc, pn, sn, t_cur, forbid,
+                                    scale_log2, pl, words, issue_words,
+                                    [&]() { pl_next = plan(t3, i + 3 < i_hi); });
+    t_cur = t_n1;
+    t_n1 = desc(clamp(i + 2));
+    t_n3 = t_n4;
+    pl = pl_next;
+    pp[0] = pn[0];
+    pp[1] = pn[1];
+    sc = sn;
+  };
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
+  step(NoPV{}, i_lo, s3, s0, s1, s2);
+  for (int i = i_lo + 1; i < i_hi; i += 4) {
+    step(WithPV{}, i, s0, s1, s2, s3);
+    if (i + 1 < i_hi) step(WithPV{}, i + 1, s1, s2, s3, s0);
+    if (i + 2 < i_hi) step(WithPV{}, i + 2, s2, s3, s0, s1);
+    if (i + 3 < i_hi) step(WithPV{}, i + 3, s3, s0, s1, s2);
+  }
+  const int last = (i_hi - 1 - i_lo) & 3;
+  pv_last(last == 0 ? s0 : last == 1 ? s1 : last == 2 ? s2 : s3, lo, st, pp);
+}
+
+// True if this lane's row maximum (its raw scores, both halves, scaled to base 2
+// here, once) grew past the reference by more than kGrowth.
+__device__ __forceinline__ bool needs_rerun(State& st, float scale_log2) {
+  st.mobs = xhalf_max(st.mobs) * scale_log2;
+  return st.mobs > st.m + kGrowth;
+}
+
+// Reset for the second pass: the reference becomes the row's true maximum.
+__device__ __forceinline__ void reset_for_rerun(State& st) {
+  st.m = st.mobs;
+  st.l = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.o[c][i] = 0.f;
+  st.all_set = true;
+}
+
+// Q^T fragments of this lane's row (row-major [.., d] at `qrow`): fragment j holds
+// d = 16 j + 8 (lane / 32) .. + 7.
+__device__ __forceinline__ void load_q_row(State& st, const __bf16* qrow) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.qf[j] = *reinterpret_cast<const bf16x8*>(qrow + 16 * j + 8 * h);
+}
+
+// The same from the operand tile layout (tiled_offset) of a matrix of width d:
+// row `row` of that matrix.
+__device__ __forceinline__ void load_q_tiled(State& st, const __bf16* q, int64_t row) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.qf[j] = *reinterpret_cast<const bf16x8*>(q + tiled_offset(row, 16 * j + 8 * h, D));
+}
+
+// Rotary embedding of the lane's Q row in registers: pairs (i, i + 128) sit in
+// fragments j and j + 8 at the same element; pair i = 16 j + 8 (lane / 32) + e.
+__device__ __forceinline__ void rotate_q(State& st, int pos, const double* inv_freq) {
+  const int h = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c, sn;
+      rope_cos_sin(pos, inv_freq[16 * j + 8 * h + e], c, sn);
+      const float a = bf2f(st.qf[j][e]), b = bf2f(st.qf[j + 8][e]);
+      st.qf[j][e] = f2bf(a * c - b * sn);
+      st.qf[j + 8][e] = f2bf(b * c + a * sn);
+    }
+}
+
+// Row sum of this lane's row (both halves) and the normalised output store:
+// dst(q, c) -> where d = 32 c + 8 q + 4 (lane / 32) .. + 3 go (nullptr: no row).
+template <typename Dst>
+__device__ __forceinline__ void store_rows(const State& st, float l_row, Dst dst) {
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __bf16* p = dst(q, c);
+      if (p == nullptr) continue;
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = f2bf(st.o[c][4 * q + e] * inv);
+      *reinterpret_cast<bf16x4*>(p) = v;
+    }
+}
+
+// Key-split epilogue: the unnormalised partial O^T of the wave's 32 rows in
+// accumulator lane order (each store 1 KB contiguous), and (m, l) per row.
+// chunk = (group * n_qblk + qblk) * NW + wave; split s at s * n_chunks + chunk.
+__device__ __forceinline__ void store_partials(const State& st, float l_row, float* __restrict__ opart,
+                                               float* __restrict__ mlpart, int64_t n_chunks, int64_t chunk, int split) {
+  const int lane = threadIdx.x & 63;
+  const int64_t at = split * n_chunks + chunk;
+  f32x4* dst = reinterpret_cast<f32x4*>(opart) + at * 32 * 64 + lane;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 v = {st.o[c][4 * q], st.o[c][4 * q + 1], st.o[c][4 * q + 2], st.o[c][4 * q + 3]};
+      __builtin_nontemporal_store(v, &dst[(4 * c + q) * 64]);
+    }
+  if (lane < 32) {
+    mlpart[at * 64 + 2 * lane] = st.m;
+    mlpart[at * 64 + 2 * lane + 1] = l_row;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one group per (sample, KV head, key split), n_qblk blocks of 16 query
+// tokens each, XCD-placed.  The workgroup reads its 16-token row of the mask's
+// tile table and compacts its non-EMPTY key tiles into an LDS list.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+prefill32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+                 __bf16* __restrict__ o, int B, int L, int Hq, int Hkv, float scale_log2,
+                 const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
+                 uint32_t forbid, Placement place, int n_split, float* __restrict__ opart,
+                 float* __restrict__ mlpart, const int32_t* __restrict__ rope_pos, double rope_log2_base,
+                 float* __restrict__ lse) {
+  __shared__ Stage stage0, stage1, stage2, stage3;
+  __shared__ uint32_t kmask[kMaxTiles];
+  __shared__ uint32_t tlist[kMaxTiles];
+  __shared__ u32x2 tdesc[kMaxTiles];      // (tile | class << 16, key-validity bitmap) of list entry i
+  __shared__ double rope_if[D / 2];
+  __shared__ int tcount;
+  int grp, qblk;
+  if (!xcd_place(place, grp, qblk)) return;
+  if (rope_pos != nullptr)
+    for (int i = threadIdx.x; i < D / 2; i += THREADS) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
+  const int group = grp / n_split, split = grp % n_split;
+  const int b = group / Hkv, kvh = group % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = qblk * TOK;
+  const uint32_t* tk = tok + (size_t)b * L;
+  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, TOK, NW, kmask, tlist, &tcount);
+
+  // this lane's row: token t, head h (rows past the last token read token 0 and are never stored)
+  const int row = wave * ROWS_W + (lane & 31);
+  const int t = tok0 + row / G;
+  const int hq = kvh * G + row % G;
+  const bool row_ok = t < L;
+  State st;
+  init_state(st);
+  st.wq = row_ok ? tk[t] : 0u;
+  load_q_row(st, q + (((int64_t)b * L + (row_ok ? t : 0)) * Hq + hq) * D);
+  __syncthreads();
+  const int count = tcount;
+  // one 8-byte descriptor per list entry, so the loop fetches a tile's with a single read
+  for (int i = threadIdx.x; i < count; i += THREADS) {
+    const uint32_t d = tlist[i];
+    tdesc[i] = u32x2{d, kmask[d & 0xFFFFu]};
+  }
+  __syncthreads();
+
+  const __bf16* k0 = k + ((size_t)b * L * Hkv + kvh) * D;
+  const __bf16* v0 = v + ((size_t)b * L * Hkv + kvh) * D;
+  const i32x4 rw = make_rsrc(tk);
+  const int tsb = Hkv * D * 2;
+  const Lanes lo = make_lanes(tsb);
+  auto desc = [&](int i) {
+    const u32x2 dm = tdesc[i];
+    return TileDesc{dm[0], dm[1], 0u};
+  };
+  auto plan = [&](const TileDesc& td, bool live) {
+    const int key0 = (int)(td.d & 0xFFFFu) * TK;
+    LoadPlan pl = plan_kv(lo, k0, v0, key0, tsb, td.m, live);
+    pl.wo = (live && lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
+    return pl;
+  };
+  // the tile's key words: one small load by wave 0, with its K/V loads
+  auto issue_words = [&](Stage* sg, const LoadPlan& pl) {
+    if (wave == 0) pi_buffer_load_lds(rw, lds_u32(&sg->w[0]), 4, (int)pl.wo, 0, 0, 0);
+  };
+  auto words = [&](const Stage* cs, const TileDesc&, int q) {
+    return *reinterpret_cast<const u32x4*>(&cs->w[8 * q + 4 * (lane >> 5)]);
+  };
+  const int i_lo = (int)((int64_t)count * split / n_split);
+  const int i_hi = (int)((int64_t)count * (split + 1) / n_split);
+  bool rotated = rope_pos == nullptr;
+  auto prep = [&]() {
+    if (rotated) return;
+    rotate_q(st, rope_pos[(int64_t)b * L + min(t, L - 1)], rope_if);
+    rotated = true;
+  };
+  auto run = [&]() { run_tiles(stage0, stage1, stage2, stage3, lo, st, i_lo, i_hi, desc, plan, words, issue_words, prep, forbid,
+              scale_log2);
+  };
+  run();
+  if (__syncthreads_or(needs_rerun(st, scale_log2))) {
+    reset_for_rerun(st);
+    run();
+  }
+  const float l_row = st.l + __shfl_xor(st.l, 32);
+  if (n_split == 1) {
+    if (lse != nullptr && lane < 32 && row_ok)
+      lse[((int64_t)b * L + t) * Hq + hq] =
+          l_row > 0.f ? (st.m + log2f(l_row)) * 0.6931471805599453f : -INFINITY;
+    __bf16* orow = row_ok ? o + (((int64_t)b * L + t) * Hq + hq) * D : nullptr;
+    const int h = lane >> 5;
+    store_rows(st, l_row, [&](int qq, int c) -> __bf16* {
+      return orow ? orow + 32 * c + 8 * qq + 4 * h : nullptr;
+    });
+    return;
+  }
+  const int64_t n_chunks = (int64_t)B * Hkv * place.n_sub * NW;
+  store_partials(st, l_row, opart, mlpart, n_chunks, ((int64_t)group * place.n_sub + qblk) * NW + wave, split);
+}
+
+// ---------------------------------------------------------------------------
+// Cached suffix decode (Hq = 8, Hkv = 1): one group per (sample, key split),
+// n_qblk blocks of 16 suffix tokens each, XCD-placed.  Keys: the valid prefix
+// slots of the cache layer, then the suffix's own K/V; query / key words reuse
+// the prefill rule with bid 0 for every prefix slot and 1 + cumsum(suffix_ar)
+// for suffix tokens.  Fully padded cache tiles are never fetched.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
+                const uint8_t* __restrict__ prefix_mask, int cap, int P,
+                const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
+                const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
+                __bf16* __restrict__ os, int tiled, Placement place, int n_split, float* __restrict__ opart,
+                float* __restrict__ mlpart, int rope, double rope_log2_base) {
+  __shared__ Stage stage0, stage1, stage2, stage3;
+  __shared__ uint32_t sbid[128];
+  __shared__ uint32_t pmask[kMaxTiles];
+  __shared__ u32x2 tdesc[kMaxTiles];      // (tile | class << 16 | suffix << 24, key-validity bitmap)
+  __shared__ double rope_if[D / 2];
+  __shared__ int tcount;
+  int grp, qblk;
+  if (!xcd_place(place, grp, qblk)) return;
+  if (rope)
+    for (int i = threadIdx.x; i < D / 2; i += THREADS) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
+  const int b = grp / n_split, split = grp % n_split;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = qblk * TOK;
+  const int n_pt = (P + TK - 1) / TK;
+  const int n_st = (S + TK - 1) / TK;
+
+  // suffix block ids: inclusive cumsum of suffix_ar (S <= 128), by wave 0
+  if (wave == 0) {
+    int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
+    int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int u0 = __shfl_up(a0, off), u1 = __shfl_up(a1, off);
+      if (lane >= off) {
+        a0 += u0;
+        a1 += u1;
+      }
+    }
+    const int tot0 = __shfl(a0, 63);
+    sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
+    sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
+  }
+  // validity bitmap of the prefix slots, one 32-bit word per tile
+  const uint8_t* pm = prefix_mask + (size_t)b * cap;
+  for (int base = wave * 64; base < n_pt * TK; base += THREADS) {
+    const int slot = base + lane;
+    const bool valid = slot < P && pm[slot] != 0;
+    const unsigned long long bal = __ballot(valid);
+    if (lane == 0) pmask[base / TK] = (uint32_t)bal;
+    if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
+  }
+  __syncthreads();
+  // compact tile list: non-empty prefix tiles, then the suffix tiles
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < n_pt + n_st; base += 64) {
+      const int i = base + lane;
+      uint32_t m = 0u, d = 0u;
+      if (i < n_pt) {
+        m = pmask[i];
+        d = (uint32_t)i | ((uint32_t)(m == 0xFFFFFFFFu ? PI_TILE_FULL : PI_TILE_PARTIAL) << 16);
+      } else if (i < n_pt + n_st) {
+        const int nv = min(TK, S - (i - n_pt) * TK);
+        m = nv == TK ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+        d = (uint32_t)(i - n_pt) | ((uint32_t)PI_TILE_PARTIAL << 16) | (1u << 24);
+      }
+      const unsigned long long bal = __ballot(m != 0u);
+      if (m != 0u) {
+        const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+        tdesc[pos] = u32x2{d, m};
+      }
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) tcount = cnt;
+  }
+  const int row = wave * ROWS_W + (lane & 31);
+  const int t = tok0 + row / G;
+  const int hq = row % G;
+  const bool row_ok = t < S;
+  State st;
+  init_state(st);
+  if (tiled) {
+    // this sample's queries: rows t*8 + head of a tile-layout matrix of width 256,
+    // padded to whole 16-row blocks; blocks past the padding read block 0
+    const int padded = (S * G + 15) / 16 * 16;
+    int r = tok0 * G + row;
+    if (r >= padded) r &= 15;
+    load_q_tiled(st, qs, (int64_t)b * padded + r);
+  } else {
+    load_q_row(st, qs + (((int64_t)b * S + (row_ok ? t : 0)) * G + hq) * D);
+  }
+  __syncthreads();
+  st.wq = row_ok ? sbid[t] : 0u;
+  const int i_lo = (int)((int64_t)tcount * split / n_split);
+  const int i_hi = (int)((int64_t)tcount * (split + 1) / n_split);
+
+  const __bf16* k0 = ck + (size_t)b * cap * D;
+  const __bf16* v0 = cv + (size_t)b * cap * D;
+  const __bf16* ks0 = ks + (size_t)b * S * D;
+  const __bf16* vs0 = vs + (size_t)b * S * D;
+  const Lanes lo = make_lanes(D * 2);
+  auto desc = [&](int i) {
+    const u32x2 dm = tdesc[i];
+    return TileDesc{dm[0], dm[1], 0u};
+  };
+  auto plan = [&](const TileDesc& td, bool live) {
+    const int key0 = (int)(td.d & 0xFFFFu) * TK;
+    const bool suffix = (td.d >> 24) & 1u;
+    LoadPlan pl = plan_kv(lo, suffix ? ks0 : k0, suffix ? vs0 : v0, key0, D * 2, td.m, live);
+    pl.wo = kOOB;
+    return pl;
+  };
+  auto issue_words = [](Stage*, const LoadPlan&) {};
+  // key words of the current tile (masked tiles only): a cache slot's is its validity
+  // bit (block id 0), a suffix key's its block id, 0 for keys outside the tile
+  auto words = [&](const Stage*, const TileDesc& t, int q) {
+    const uint32_t d = t.d, m = t.m;
+    const int key0 = (int)(d & 0xFFFFu) * TK;
+    const bool suffix = (d >> 24) & 1u;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 8 * q + 4 * (lane >> 5) + e;
+      const uint32_t bit = (m >> key) & 1u;
+      w[e] = suffix ? (bit ? sbid[min(key0 + key, 127)] : 0u) : bit;
+    }
+    return w;
+  };
+  bool rotated = !rope;
+  auto prep = [&]() {
+    if (rotated) return;
+    int n_valid = 0;
+    for (int w = lane; w < n_pt; w += 64) n_valid += __popc(pmask[w]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) n_valid += __shfl_xor(n_valid, off);
+    rotate_q(st, n_valid + t, rope_if);
+    rotated = true;
+  };
+  auto run = [&]() { run_tiles(stage0, stage1, stage2, stage3, lo, st, i_lo, i_hi, desc, plan, words, issue_words, prep, 0u,
+              scale_log2);
+  };
+  run();
+  if (__syncthreads_or(needs_rerun(st, scale_log2))) {
+    reset_for_rerun(st);
+    run();
+  }
+  const float l_row = st.l + __shfl_xor(st.l, 32);
+  if (n_split == 1) {
+    const int h = lane >> 5;
+    if (tiled) {
+      store_rows(st, l_row, [&](int qq, int c) -> __bf16* {
+        if (!row_ok) return nullptr;
+        return os + tiled_offset((int64_t)b * S + t, hq * D + 32 * c + 8 * qq + 4 * h, G * D);
+      });
+    } else {
+      __bf16* orow = row_ok ? os + (((int64_t)b * S + t) * G + hq) * D : nullptr;
+      store_rows(st, l_row, [&](int qq, int c) -> __bf16* {
+        return orow ? orow + 32 * c + 8 * qq + 4 * h : nullptr;
+      });
+    }
+    return;
+  }
+  const int64_t n_chunks = (int64_t)B * place.n_sub * NW;
+  store_partials(st, l_row, opart, mlpart, n_chunks, ((int64_t)b * place.n_sub + qblk) * NW + wave, split);
+}
+
+// Merge the key splits of one 32-row chunk: O = sum_s 2^(m_s - M) O_s / sum_s
+// 2^(m_s - M) l_s, M = max_s m_s.  One wave per (chunk, 32-wide d chunk), four
+// waves per workgroup; every lane merges its row's 16 values of the d chunk.
+__global__ void __launch_bounds__(256)
+combine32_kernel(const float* __restrict__ opart, const float* __restrict__ mlpart, __bf16* __restrict__ out,
+                 int o_tiled, int64_t n_chunks, int n_qblk, int L, int Hq, int n_split, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t chunk = blockIdx.x >> 1;
+  const int c = (blockIdx.x & 1) * 4 + (threadIdx.x >> 6);
+  if (chunk >= n_chunks) return;
+  const int wave_in = (int)(chunk % NW);
+  const int64_t gq = chunk / NW;               // group * n_qblk + qblk
+  const int qblk = (int)(gq % n_qblk);
+  const int64_t group = gq / n_qblk;           // sample * Hkv + kv head
+  const int Hkv = Hq / G;
+  const int64_t b = group / Hkv;
+  const int kvh = (int)(group % Hkv);
+  const int row = wave_in * ROWS_W + (lane & 31);
+  const int t = qblk * TOK + row / G;
+  const int hq = kvh * G + row % G;
+  const int h = lane >> 5;
+  float M = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, mlpart[(sp * n_chunks + chunk) * 64 + 2 * (lane & 31)]);
+  f32x4 acc[4] = {};
+  float Ls = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < n_split; ++sp) {
+      const int64_t at = sp * n_chunks + chunk;
+      const float m = mlpart[at * 64 + 2 * (lane & 31)];
+      const float l = mlpart[at * 64 + 2 * (lane & 31) + 1];
+      const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+      Ls += w * l;
+      const f32x4* src = reinterpret_cast<const f32x4*>(opart) + at * 32 * 64 + lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += w * __builtin_nontemporal_load(&src[(4 * c + q) * 64]);
+    }
+  }
+  if (t >= L) return;
+  const float inv = Ls > 0.f ? 1.f / Ls : 0.f;
+  if (lse != nullptr && c == 0 && h == 0)
+    lse[(b * L + t) * Hq + hq] = Ls > 0.f ? (M + log2f(Ls)) * 0.6931471805599453f : -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = f2bf(acc[q][e] * inv);
+    const int d = 32 * c + 8 * q + 4 * h;
+    __bf16* dst = o_tiled ? out + tiled_offset(b * L + t, hq * D + d, Hq * D) : out + ((b * L + t) * Hq + hq) * D + d;
+    *reinterpret_cast<bf16x4*>(dst) = v;
+  }
+}
+
+// Key splits: enough workgroups to cover the chip (about 256), each split with
+// at least min_tiles key tiles, at most 16 splits.
+int splits_for(int groups, int n_qblk, int tiles, int min_tiles) {
+  const int by_chip = 256 / std::max(1, groups * n_qblk);
+  return std::max(1, std::min({kMaxSplit32, by_chip, tiles / min_tiles}));
+}
+
+size_t split_bytes(int groups, int n_qblk, int splits) {
+  if (splits <= 1) return 0;
+  const size_t chunks = (size_t)splits * groups * n_qblk * NW;
+  return pi::align_up(chunks * 32 * 256 * sizeof(float), 256) + chunks * 64 * sizeof(float);
+}
+
+}  // namespace
+
+namespace pi32 {
+
+int prefill_splits(int B, int Hkv, int L) {
+  const int n_qblk = (L + TOK - 1) / TOK;
+  return splits_for(B * Hkv, n_qblk, (L + TK - 1) / TK, 2);
+}
+
+size_t prefill_split_bytes(int B, int Hkv, int L, int splits) {
+  return split_bytes(B * Hkv, (L + TOK - 1) / TOK, splits);
+}
+
+pi_status prefill(const void* q, const void* k, const void* v, void* o, int B, int L, int Hq, int Hkv, float scale,
+                  const pi_mask* m, float rope_base, float* lse, void* split_ws, size_t split_avail,
+                  hipStream_t s) {
+  const int n_qblk = (L + TOK - 1) / TOK;
+  int splits = prefill_splits(B, Hkv, L);
+  if (split_ws == nullptr || split_avail < prefill_split_bytes(B, Hkv, L, splits)) splits = 1;
+  const Placement place = make_placement(B * Hkv * splits, n_qblk);
+  const int64_t grid = placement_grid(place);
+  PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "prefill: grid too large");
+  const size_t chunks = (size_t)splits * B * Hkv * n_qblk * NW;
+  float* opart = splits > 1 ? static_cast<float*>(split_ws) : nullptr;
+  float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(split_ws) +
+                                                        pi::align_up(chunks * 32 * 256 * sizeof(float), 256))
+                             : nullptr;
+  prefill32_kernel<<<(unsigned)grid, THREADS, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<__bf16*>(o), B, L, Hq, Hkv, scale * 1.4426950408889634f, m->tok, m->tiles, m->n_qt, m->n_kt,
+      m->forbid_bits, place, splits, opart, mlpart, rope_base > 0.f ? m->pos : nullptr,
+      rope_base > 0.f ? log2((double)rope_base) : 0.0, splits > 1 ? nullptr : lse);
+  pi_status st = pi::check_launch("prefill32_kernel");
+  if (st != PI_OK || splits == 1) return st;
+  const int64_t n_chunks = (int64_t)B * Hkv * n_qblk * NW;
+  combine32_kernel<<<(unsigned)(n_chunks * 2), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o), 0, n_chunks,
+                                                              n_qblk, L, Hq, splits, lse);
+  return pi::check_launch("combine32_kernel");
+}
+
+int decode_splits(int B, int S, int len) {
+  const int n_qblk = (S + TOK - 1) / TOK;
+  return splits_for(B, n_qblk, (len + TK - 1) / TK + (S + TK - 1) / TK, 2);
+}
+
+size_t decode_split_bytes(int B, int S, int splits) { return split_bytes(B, (S + TOK - 1) / TOK, splits); }
+
+pi_status decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf16* cvl, const void* q_s, const void* k_s,
+                 const void* v_s, const uint8_t* suffix_ar, int B, int S, float scale, float rope_base, void* o_s,
+                 bool tiled, void* split_ws, size_t split_avail, hipStream_t s) {
+  const int n_qblk = (S + TOK - 1) / TOK;
+  int splits = decode_splits(B, S, cache->len);
+  if (split_ws == nullptr || split_avail < decode_split_bytes(B, S, splits)) splits = 1;
+  const size_t chunks = (size_t)splits * B * n_qblk * NW;
+  float* opart = splits > 1 ? static_cast<float*>(split_ws) : nullptr;
+  float* mlpart = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(split_ws) +
+                                                        pi::align_up(chunks * 32 * 256 * sizeof(float), 256))
+                             : nullptr;
+  const Placement place = make_placement(B * splits, n_qblk);
+  const bool rope = rope_base > 0.f;
+  decode32_kernel<<<(unsigned)placement_grid(place), THREADS, 0, s>>>(
+      ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
+      static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart,
+      rope ? 1 : 0, rope ? log2((double)rope_base) : 0.0);
+  pi_status st = pi::check_launch("decode32_kernel");
+  if (st != PI_OK || splits == 1) return st;
+  const int64_t n_chunks = (int64_t)B * n_qblk * NW;
+  combine32_kernel<<<(unsigned)(n_chunks * 2), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o_s),
+                                                              tiled ? 1 : 0, n_chunks, n_qblk, S, G, splits, nullptr);
+  return pi::check_launch("combine32_kernel");
+}
+
+}  // namespace pi32
