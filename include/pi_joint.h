@@ -302,6 +302,29 @@ pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void*
                                 void* workspace, size_t workspace_bytes, pi_stream stream);
 
 /*
+ * Allocation-free variant of pi_suffix_decode_step, for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * layouts and result as pi_suffix_decode_step minus the workspace.  Its scratch
+ * (the rotated suffix keys under the rotary embedding, the key-split partials
+ * of a small batch) is one file-scope device array of PI_NOALLOC_SCRATCH_BYTES
+ * per GPU, held from the library's load until the process ends; the call
+ * allocates and frees nothing.  The key split runs when its partials fit the
+ * scratch, exactly as pi_suffix_decode_step with a workspace of that size
+ * (bit-identical to it then); otherwise the call runs unsplit.  Returns
+ * PI_ERR_UNSUPPORTED, launching nothing, when the rotated suffix keys alone
+ * (B * S * 512 bytes, rope_base > 0) exceed the scratch.  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents (nothing in it
+ * needs to start at zero): calls that overlap on one GPU (different streams,
+ * threads) race and must be serialised by the caller.
+ */
+#define PI_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+pi_status pi_suffix_decode_step_noalloc(const pi_kv_cache* cache, int layer, const void* q_s,
+                                        const void* k_s, const void* v_s, const uint8_t* suffix_ar,
+                                        int B, int S, int Hq, float scale, float rope_base, void* o_s,
+                                        pi_stream stream);
+
+/*
  * Single-token autoregressive decode ([P4] §4.1: after the prefill, every step
  * runs one new token against the cache, which then keeps its K/V).  A step is
  * pi_suffix_decode_step with S = 1 and suffix_ar = {1} (the token sees every

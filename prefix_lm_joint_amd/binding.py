@@ -85,6 +85,8 @@ _SIGS = {
     "pi_decode_workspace_bytes": (ctypes.c_size_t, [_c_i, _c_i, _c_i, _c_i]),
     "pi_suffix_decode_step": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i, _c_i,
                                      _c_f, _c_f, _c_p, _c_p, ctypes.c_size_t, _c_p]),
+    "pi_suffix_decode_step_noalloc": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_p, _c_p, _c_i, _c_i,
+                                             _c_i, _c_f, _c_f, _c_p, _c_p]),
     "pi_rope_apply": (_c_i, [_c_p, _c_p, _c_i, _c_i, _c_i, _c_i, _c_p, _c_f, _c_p]),
     "pi_kv_cache_append": (_c_i, [ctypes.POINTER(PiKvCache), _c_i, _c_p, _c_p, _c_i, _c_f, _c_p]),
     "pi_euler_update": (_c_i, [_c_p, _c_p, _c_f, ctypes.c_int64, _c_p]),
@@ -535,6 +537,32 @@ def pi_suffix_decode_step(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: to
         _ptr(v_s, torch.bfloat16, "v_s"), _ptr(suffix_ar, torch.uint8, "suffix_ar"), B, S, Hq, scale, rope_base,
         _ptr(o_s, torch.bfloat16, "o_s"), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return o_s
+
+
+def pi_suffix_decode_step_noalloc(cache: KVCache, layer: int, q_s: torch.Tensor, k_s: torch.Tensor,
+                                  v_s: torch.Tensor, suffix_ar: torch.Tensor, o_s: torch.Tensor,
+                                  scale: Optional[float] = None, stream=None, rope_base: float = 0.0) -> torch.Tensor:
+    """pi_suffix_decode_step without a workspace: the library's own per-GPU scratch
+    stands in for it, and neither this wrapper nor the library allocates (o_s is
+    required).  Calls overlapping on one GPU race on that scratch."""
+    if q_s.dim() != 4:
+        raise ValueError(f"q_s must be [B, S, Hq, d], got {tuple(q_s.shape)}")
+    B, S, Hq, d = q_s.shape
+    c = cache.struct
+    if (c.B, c.d) != (B, d):
+        raise ValueError(f"cache holds B={c.B}, d={c.d}; q_s has B={B}, d={d}")
+    _expect(q_s, (B, S, Hq, d), torch.bfloat16, "q_s")
+    _expect(k_s, (B, S, c.Hkv, d), torch.bfloat16, "k_s")
+    _expect(v_s, (B, S, c.Hkv, d), torch.bfloat16, "v_s")
+    _expect(suffix_ar, (S,), torch.uint8, "suffix_ar")
+    _expect(o_s, (B, S, Hq, d), torch.bfloat16, "o_s")
+    if scale is None:
+        scale = d ** -0.5
+    _check("pi_suffix_decode_step_noalloc", lib().pi_suffix_decode_step_noalloc(
+        ctypes.byref(cache.struct), layer, _ptr(q_s, torch.bfloat16, "q_s"), _ptr(k_s, torch.bfloat16, "k_s"),
+        _ptr(v_s, torch.bfloat16, "v_s"), _ptr(suffix_ar, torch.uint8, "suffix_ar"), B, S, Hq, scale, rope_base,
+        _ptr(o_s, torch.bfloat16, "o_s"), _stream(stream)))
     return o_s
 
 

@@ -39,6 +39,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 namespace {
@@ -1181,6 +1182,70 @@ extern "C" pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, 
                                            size_t workspace_bytes, pi_stream stream) {
   return pi::decode_layer(cache, layer, q_s, k_s, v_s, suffix_ar, B, S, Hq, scale, rope_base, o_s, false,
                           workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free cached decode for callers that cannot allocate (code under
+// graph capture, tight serving loops): the decode's scratch (the rotated suffix
+// keys and the key-split partials) lives in one file-scope device array per
+// GPU instead of a caller workspace.  Host code never passes the array's name
+// to a kernel (on the host it only stands for the symbol); its device address
+// is looked up once per device with that device current and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PI_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device (null: not looked up yet)
+
+// The scratch address on the device that owns `stream` (the current device for
+// the null stream), looked up on the first call there.
+pi_status scratch_address(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess) {
+    dev = cur;
+    if (stream != nullptr) e = hipStreamGetDevice(stream, &dev);
+  }
+  PI_REQUIRE(e == hipSuccess, PI_ERR_HIP, "pi_suffix_decode_step_noalloc: no device for the stream: %s",
+             hipGetErrorString(e));
+  PI_REQUIRE(dev >= 0 && dev < kMaxDevices, PI_ERR_UNSUPPORTED, "pi_suffix_decode_step_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    PI_REQUIRE(e == hipSuccess && p != nullptr, PI_ERR_HIP,
+               "pi_suffix_decode_step_noalloc: scratch address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PI_OK;
+}
+}  // namespace
+
+extern "C" pi_status pi_suffix_decode_step_noalloc(const pi_kv_cache* cache, int layer, const void* q_s,
+                                                   const void* k_s, const void* v_s, const uint8_t* suffix_ar,
+                                                   int B, int S, int Hq, float scale, float rope_base, void* o_s,
+                                                   pi_stream stream) {
+  PI_REQUIRE(B >= 1 && S >= 1 && S <= 128, PI_ERR_INVALID_ARG, "pi_suffix_decode_step_noalloc: B=%d S=%d (S <= 128)",
+             B, S);
+  const size_t rot = rope_base > 0.f ? rope_ks_bytes(B, S) : 0;
+  PI_REQUIRE(rot <= PI_NOALLOC_SCRATCH_BYTES, PI_ERR_UNSUPPORTED,
+             "pi_suffix_decode_step_noalloc: the rotated suffix keys of B=%d x S=%d need %zu bytes, more than the "
+             "%zu-byte scratch", B, S, rot, (size_t)PI_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const pi_status st = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (st != PI_OK) return st;
+  // the scratch stands in for a workspace of its size: the key split runs when its
+  // partials fit (as it would with that workspace), otherwise the call runs unsplit
+  return pi::decode_layer(cache, layer, q_s, k_s, v_s, suffix_ar, B, S, Hq, scale, rope_base, o_s, false, ws,
+                          PI_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
 }
 
 extern "C" pi_status pi_kv_cache_append(const pi_kv_cache* cache, int layer, const void* k_new, const void* v_new,
