@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     p.add_argument("--only", choices=["step", "prefill", "decode", "mmdit", "copy", "rope", "ar", "backward", "sampler", "pi05",
-                                      "layer", "expert"],
+                                      "layer", "expert", "serving"],
                    default=None,
                    help="run just one leg (for profiling)")
     return p.parse_args()
@@ -511,6 +511,60 @@ def ar_decode_leg(cx: Ctx, iters: int):
             "kernel": "decode_kernel (one wave, S=1) + decode_combine_kernel"}
 
 
+def serving_control_step_leg(cx: Ctx, iters: int):
+    """The batched serving control step on the stand-in path: B = 64 robots, each
+    with its own 816-slot cache of 18 layers (valid lengths U[600, 816]), the whole
+    10-step Euler loop of pi_flow_sample with the stand-in velocity net (width
+    1024, 18 cache layers, 51 suffix tokens, 50 actions of dim 32) per control step.
+    Cache and noise are drawn on the device from a seeded generator, the weights by
+    the seeded host generator (bench-only inputs; parity is covered by the tests)."""
+    torch, Bd, I = cx.torch, cx.Bd, cx.I
+    w = I.serving_decode()
+    s = w.structure
+    P, S, B, L, N, A = s.n_prefix, s.n - s.n_prefix, w.B, w.layers, w.steps, w.action_dim
+    H = S - 1
+    pm = w.input_mask()[:, :P]
+    lens = pm.sum(axis=1)
+    gen = torch.Generator(device=cx.dev)
+    gen.manual_seed(w.seed_base + 91)
+    ck = torch.randn((L, B, P, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cv = torch.randn((L, B, P, 1, 256), generator=gen, device=cx.dev, dtype=torch.float32).to(torch.bfloat16)
+    cache = Bd.KVCache(ck, cv, cx.u8(pm), P)
+    net = Bd.VelocityNet.from_numpy(I.net_weights(w.seed_base + 92, width=1024, action_dim=A), cx.dev)
+    ws = Bd.flow_workspace(net, B, H, cx.dev)
+    sar = cx.u8(s.ar[P:])
+    state = torch.randn((B, A), generator=gen, device=cx.dev, dtype=torch.float32)
+    noise = torch.randn((B, H, A), generator=gen, device=cx.dev, dtype=torch.float32)
+    x = torch.empty_like(noise)
+    ms = cx.time_ms(lambda: (x.copy_(noise), Bd.pi_flow_sample(net, cache, sar, state, None, x, num_steps=N,
+                                                                  workspace=ws)), iters)
+    # attention bytes per Euler step (each layer's valid K/V, the queries, outputs and suffix K/V)
+    att_bytes = L * (int(lens.sum()) * 256 * 2 * 2 + B * S * 8 * 256 * 2 * 2 + B * S * 256 * 2 * 2)
+    W, M = 1024, B * S
+    gemm_flops = L * 2.0 * M * W * (2048 + 512 + 2048) + 2.0 * M * W * A
+    pairs = int(lens.sum()) * S + B * (1 + (S - 1) * S)
+    att_flops = L * 4.0 * 256 * 8 * pairs
+    return {"workload": "batched_serving_control_step", "B": B, "slots": P, "valid_len_mean": float(lens.mean()),
+            "suffix_tokens": S, "layers": L, "euler_steps": N, "ms_per_control_step": ms,
+            "control_steps_per_s": 1e3 / ms, "robot_steps_per_s": B * 1e3 / ms,
+            "attention_bytes_per_control_step": N * att_bytes,
+            "attention_gbs_over_the_step": N * att_bytes / (ms * 1e-3) / 1e9,
+            "tflop_per_control_step": N * (gemm_flops + att_flops) / 1e12,
+            "achieved_tflops": N * (gemm_flops + att_flops) / (ms * 1e-3) / 1e12}
+
+
+def mmdit_leg(cx: Ctx, iters: int):
+    """The MM-DiT contrast: B = 2, 4096 image + 154 text tokens, full bidirectional,
+    24 heads of d = 64, the whole joint attention recomputed at each of 28 sampling
+    steps (no cache): 28 prefill calls per sample."""
+    w = cx.I.mmdit()
+    one = prefill_kernel_leg(cx, iters, "mmdit_full_bidirectional")
+    calls = w.steps
+    return {**one, "calls_per_sample": calls, "ms_per_sample": calls * one["us_per_launch"] / 1e3,
+            "gflop_per_sample": calls * one["gflop_per_launch"],
+            "pairs_per_sample_per_head": calls * one["allowed_pairs"]}
+
+
 def copy_kernel_leg(cx: Ctx, iters: int):
     """A plain device-to-device copy of known size.  Its HBM byte counters give
     the scale factor that turns the counters of the path's kernels into bytes."""
@@ -525,8 +579,8 @@ def copy_kernel_leg(cx: Ctx, iters: int):
 
 # HBM bytes per launch from the committed counter summaries; a summary only counts
 # while the kernel sources it was taken from are unchanged.
-_ENGINE = ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/common.h",
-           "prefix_lm_joint_amd/csrc/engine.h"]
+_ENGINE = ["prefix_lm_joint_amd/csrc/attention.hip", "prefix_lm_joint_amd/csrc/attention32.hip",
+           "prefix_lm_joint_amd/csrc/common.h", "prefix_lm_joint_amd/csrc/engine.h"]
 KERNEL_SOURCES = {"decode_kernel": _ENGINE, "prefill_kernel": _ENGINE}
 
 
@@ -698,9 +752,14 @@ def main():
     if args.only == "copy":
         kernels["copy"] = copy_kernel_leg(cx, 5)
         log(str(kernels["copy"]))
-    if args.only == "mmdit":
-        kernels["mmdit"] = prefill_kernel_leg(cx, args.kernel_iters, "mmdit_full_bidirectional")
+    if args.only in (None, "mmdit"):
+        log("MM-DiT contrast leg (B=2, 4250 tokens, 24 heads d=64, 28 calls)")
+        kernels["mmdit"] = mmdit_leg(cx, max(5, args.kernel_iters // 5))
         log(str(kernels["mmdit"]))
+    if args.only in (None, "serving"):
+        log("batched serving control step (B=64, 18 layers x 10 Euler steps, stand-in net)")
+        kernels["serving"] = serving_control_step_leg(cx, 3)
+        log(str(kernels["serving"]))
     if args.only in (None, "ar"):
         log("autoregressive single-token decode leg (B=64 816 slots)")
         kernels["ar"] = ar_decode_leg(cx, args.kernel_iters)
@@ -791,6 +850,17 @@ def main():
                                 "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                                 "frac": kernels["expert"]["mfma_frac"], "us_per_layer": kernels["expert"]["us_per_layer"],
                                 "achieved_gbs": kernels["expert"]["achieved_gbs"]},
+        "serving_control_step": {
+            "what": "B = 64 robots, 816-slot caches (valid U[600, 816]), pi_flow_sample with the stand-in net: "
+                    "18 cache layers x 10 Euler steps, 51 suffix tokens, 50 actions of dim 32",
+            **{k: kernels["serving"][k] for k in ("ms_per_control_step", "control_steps_per_s", "robot_steps_per_s",
+                                                  "attention_gbs_over_the_step", "achieved_tflops")}},
+        "mmdit": {"kernel": "prefill_kernel (MM-DiT: B=2, 4096 + 154 tokens, full bidirectional, Hq=Hkv=24, d=64)",
+                  "bound": "mfma", "achieved": kernels["mmdit"]["achieved_tflops"], "peak": PEAK_BF16_FLOPS / 1e12,
+                  "unit": "TFLOP/s", "frac": kernels["mmdit"]["mfma_frac"],
+                  "us_per_launch": kernels["mmdit"]["us_per_launch"], "calls_per_sample": 28,
+                  "ms_per_sample": kernels["mmdit"]["ms_per_sample"],
+                  "gflop_per_launch": kernels["mmdit"]["gflop_per_launch"]},
         "pi05_expert_sampler": {
             "what": "control step after the cached prefix: 10 Euler steps of the true-shape action expert "
                     "(18 layers, width 1024, FFN 4096, adaptive norms), 50 actions of dim 32, 816-slot cache",
