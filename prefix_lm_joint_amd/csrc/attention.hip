@@ -847,6 +847,220 @@ decode_combine_kernel(const float* __restrict__ opart, const float* __restrict__
   *reinterpret_cast<bf16x4*>(dst) = v;
 }
 
+// ---------------------------------------------------------------------------
+// Cached suffix decode of a few samples (the single-robot sampler), built for
+// latency.  Each workgroup of NW waves owns query block qblk of one sample and
+// at most kStages key tiles (a contiguous share of the sample's tile sequence:
+// the prefix tiles 0 .. ceil(len/32)-1, then the suffix tiles), all resident in
+// LDS at once.  So everything a workgroup reads goes out in the first few
+// instructions, before any wait: its K/V tiles (direct to LDS, each wave a
+// quarter of every tile), its Q rows, the validity bytes of its prefix slots and
+// the suffix's block flags; one memory latency later the whole share is there.
+// The loads take the static key range (prefix slots < len, suffix tokens < S;
+// beyond it they land as zeros).  Padded prefix slots inside that range are
+// found from the validity bytes once they arrive: their V rows are zeroed in LDS
+// and their scores masked, so no padded K/V reaches an output, NaN included.
+// With every score of the share in registers, the softmax takes each row's exact
+// maximum over the share: no reference maximum, no second pass.  The partials
+// (key split) use the layout decode_combine_kernel<NR, NW> merges.
+// ---------------------------------------------------------------------------
+template <int D, int G, int NR, int NW>
+__global__ void __launch_bounds__(NW * 64)
+decode_small_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
+                    const uint8_t* __restrict__ prefix_mask, int cap, int P,
+                    const __bf16* __restrict__ qs, const __bf16* __restrict__ ks, const __bf16* __restrict__ vs,
+                    const uint8_t* __restrict__ suffix_ar, int B, int S, float scale_log2,
+                    __bf16* __restrict__ os, int tiled, Placement place, int n_split, float* __restrict__ opart,
+                    float* __restrict__ mlpart, int rope, double rope_log2_base) {
+  using T = Tile<D>;
+  constexpr int ROWS_W = NR * 16;
+  constexpr int TOK = NW * ROWS_W / G;
+  constexpr int JW = T::INSTS / NW;         // load instructions per tensor tile and wave
+  static_assert(T::INSTS % NW == 0, "a tile's loads split evenly over the waves");
+  __shared__ Stage<D> stage[kStages];
+  __shared__ uint32_t sbid[128];
+  __shared__ double rope_if[D / 2];
+  int grp, qblk;
+  if (!xcd_place(place, grp, qblk)) return;
+  const int b = grp / n_split, split = grp % n_split;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int tok0 = qblk * TOK;
+  const int n_pt = (P + TK - 1) / TK;
+  const int nt = n_pt + (S + TK - 1) / TK;
+  const int i_lo = (int)((int64_t)nt * split / n_split);
+  const int n = (int)((int64_t)nt * (split + 1) / n_split) - i_lo;   // <= kStages (the launcher's rule)
+
+  // 1. this wave's quarter of every K/V tile of the share, static key range
+  const __bf16* k0 = ck + (size_t)b * cap * D;
+  const __bf16* v0 = cv + (size_t)b * cap * D;
+  const __bf16* ks0 = ks + (size_t)b * S * D;
+  const __bf16* vs0 = vs + (size_t)b * S * D;
+  uint32_t smask[kStages];
+#pragma unroll
+  for (int t = 0; t < kStages; ++t) {
+    smask[t] = 0u;
+    if (t >= n) continue;
+    const int i = i_lo + t;
+    const bool suf = i >= n_pt;
+    const int key0 = (suf ? i - n_pt : i) * TK;
+    const int left = (suf ? S : P) - key0;
+    smask[t] = left >= TK ? 0xFFFFFFFFu : ((1u << left) - 1u);
+    const int64_t at = (int64_t)key0 * D * 2;
+    const i32x4 rk = make_rsrc(reinterpret_cast<const char*>(suf ? ks0 : k0) + at);
+    const i32x4 rv = make_rsrc(reinterpret_cast<const char*>(suf ? vs0 : v0) + at);
+    const int p = lane % T::CHR;
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      const int j = wave * JW + jj;
+      const int r = j * T::RPI + lane / T::CHR;
+      uint32_t ok = (uint32_t)r * (D * 2) + 16u * (uint32_t)(p ^ T::fk(r));
+      uint32_t ov = (uint32_t)r * (D * 2) + 16u * (uint32_t)(p ^ T::fv(r));
+      if (!((smask[t] >> r) & 1u)) ok = ov = kOOB;
+      pi_buffer_load_lds(rk, lds_u32(&stage[t].k[j * T::RPI * D]), 16, (int)ok, 0, 0, 0);
+      pi_buffer_load_lds(rv, lds_u32(&stage[t].v[j * T::RPI * D]), 16, (int)ov, 0, 0, 0);
+    }
+  }
+  // 2. the Q rows
+  WaveState<D, NR> st;
+  init_state(st);
+  __bf16* row_base[NR];
+  const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
+  load_rows<D, G, NR, ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, G, 0, tok0, nullptr, q_tiled);
+  // 3. validity of the share's prefix slots (lanes < 32: one slot of each tile)
+  const uint8_t* pm = prefix_mask + (size_t)b * cap;
+  uint32_t pv[kStages];
+#pragma unroll
+  for (int t = 0; t < kStages; ++t) {
+    const int i = i_lo + t;
+    const int key = i * TK + lane;
+    pv[t] = (t < n && i < n_pt && lane < TK && key < P) ? pm[key] : 0u;
+  }
+  int n_valid = 0;   // valid prefix slots (the suffix's rotary positions start there)
+  if (rope) {
+    for (int j = lane; j < P; j += 64) n_valid += pm[j] != 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) n_valid += __shfl_xor(n_valid, off);
+    for (int i = threadIdx.x; i < D / 2; i += NW * 64) rope_if[i] = rope_inv_freq(i, D, rope_log2_base);
+  }
+  // 4. suffix block ids: inclusive cumsum of suffix_ar (S <= 128), wave 0
+  if (wave == 0) {
+    int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
+    int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      int u0 = __shfl_up(a0, off), u1 = __shfl_up(a1, off);
+      if (lane >= off) { a0 += u0; a1 += u1; }
+    }
+    const int tot0 = __shfl(a0, 63);
+    sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
+    sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
+  }
+  wait_vmem();
+  __syncthreads();      // every wave's tiles have landed; sbid is written
+
+  // 5. per tile: the dynamic validity, the key words (written by wave 0), the
+  // padded slots inside the loaded range (V rows zeroed: 0 * NaN would be NaN)
+  int cls[kStages];
+#pragma unroll
+  for (int t = 0; t < kStages; ++t) {
+    cls[t] = PI_TILE_FULL;
+    if (t >= n) continue;
+    const int i = i_lo + t;
+    const bool suf = i >= n_pt;
+    uint32_t dyn, w = 0u;
+    if (!suf) {
+      dyn = (uint32_t)__ballot(pv[t] != 0u);
+      w = (dyn >> (lane & 31)) & 1u;
+    } else {
+      dyn = smask[t];
+      const int u = (i - n_pt) * TK + (lane & 31);
+      w = ((dyn >> (lane & 31)) & 1u) ? sbid[u] : 0u;
+    }
+    cls[t] = (!suf && dyn == 0xFFFFFFFFu) ? PI_TILE_FULL : PI_TILE_PARTIAL;
+    if (wave == 0 && lane < TK) stage[t].w[lane] = w;
+    for (uint32_t zz = smask[t] & ~dyn; zz != 0u; zz &= zz - 1u) {
+      const int r = __builtin_ctz(zz);
+      if (r % NW == wave) reinterpret_cast<u32x2*>(&stage[t].v[r * D])[lane] = u32x2{0u, 0u};
+    }
+  }
+  __syncthreads();      // key words and zeroed rows are visible
+
+  // 6. scores of the share, each row's exact maximum, weights, PV
+  set_row_words<D, G, NR, ROWS_W>(st, S, tok0, sbid);
+  if (rope) {
+    int pos[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) pos[r] = n_valid + tok0 + (wave * ROWS_W + r * 16 + (lane & 15)) / G;
+    rotate_q<D, NR>(st, pos, rope_if);
+  }
+  const LaneOffsets<D> lo = lane_offsets<D>();
+  const float NEG_INF = -INFINITY;
+  f32x4 sc[kStages][NR][2];
+  float mx[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) mx[r] = NEG_INF;
+#pragma unroll
+  for (int t = 0; t < kStages; ++t) {
+    if (t >= n) continue;
+    qk_tile<D, NR>(stage[t], lo, st, sc[t]);
+    if (cls[t] == PI_TILE_PARTIAL) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wk = stage[t].w[kt * 16 + 4 * g + i];
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+            if (!pair_visible(st.wq[r], wk, 0u)) sc[t][r][kt][i] = NEG_INF;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx[r] = fmaxf(mx[r], sc[t][r][kt][i]);
+  }
+  float m_use[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    st.m[r] = group4_max(mx[r] * scale_log2);
+    // a row with no visible key in the share keeps m = -inf; 0 makes its weights exp2(-inf) = 0
+    m_use[r] = st.m[r] == NEG_INF ? 0.f : st.m[r];
+  }
+#pragma unroll
+  for (int t = 0; t < kStages; ++t) {
+    if (t >= n) continue;
+    bf16x8 pf[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf[r][4 * kt + i] = f2bf(fast_exp2(fmaf(sc[t][r][kt][i], scale_log2, -m_use[r])));
+    pv_last<D, NR>(stage[t], lo, st, pf);
+  }
+
+  // 7. output rows, or the partials of the key split
+  if (n_split == 1) {
+    if (tiled) {
+      const int c = lane & 15;
+      auto dst = [&](int r, int dt) -> __bf16* {
+        const int row = wave * ROWS_W + r * 16 + c;
+        const int t = tok0 + row / G;
+        if (t >= S) return nullptr;
+        return os + tiled_offset((int64_t)b * S + t, (row % G) * D + dt * 16 + 4 * g, G * D);
+      };
+      store_rows<D, NR>(st, dst);
+    } else {
+      store_rows<D, NR>(st, RowMajorDst<D>{row_base});
+    }
+    return;
+  }
+  store_partials<D, NR, NW>(st, opart, mlpart, (int64_t)B * place.n_sub * NW * NR, b, place.n_sub, qblk, split);
+}
+
 // K/V rows of tokens [0, P) into cache layer slices; one thread per 16 bytes.
 __global__ void cache_write_kernel(const u32x4* __restrict__ k, const u32x4* __restrict__ v,
                                    u32x4* __restrict__ ck, u32x4* __restrict__ cv, int L, int cap, int P,
@@ -933,6 +1147,10 @@ using CfgDec = Cfg<256, 8, kNR256, kNWdec>;
 // it would halve the work per workgroup launch and run 2x slower).
 constexpr int kNWdecS = 3;
 using CfgDecS = Cfg<256, 8, kNR256, kNWdecS>;
+// The latency-lean decode of a few samples (decode_small_kernel): four waves of
+// one 16-row tile (8 query tokens per workgroup), at most kStages key tiles each.
+constexpr int kNWsmall = 4;
+using CfgSmall = Cfg<256, 8, kNR256, kNWsmall>;
 using CfgAr = Cfg<256, 8, kNR256, kNWar>;
 
 template <int D, int G, int NR, int NW>
@@ -964,10 +1182,10 @@ int decode_splits_for(int B, int S, int len, int min_tiles = 2) {
   return std::max(1, std::min({kMaxSplit, by_chip, tiles / min_tiles}));
 }
 bool small_decode(int B, int S) { return S > 1 && B * ((S + CfgDec::TOK - 1) / CfgDec::TOK) <= 16; }
-int decode_splits(int B, int S, int len) {
-  if (S == 1) return decode_splits_for<CfgAr>(B, S, len);
-  return small_decode(B, S) ? decode_splits_for<CfgDecS>(B, S, len, 3) : pi32::decode_splits(B, S, len);
-}
+// decode_small_kernel: key tiles of a sample (prefix slots, then suffix tokens)
+// and its key split, one to two tiles per split up to kMaxSplit splits.
+int small_tiles(int S, int len) { return (len + TK - 1) / TK + (S + TK - 1) / TK; }
+int small_splits(int S, int len) { return std::max(1, std::min(kMaxSplit, small_tiles(S, len))); }
 
 // Key splits for a GQA 8:1 prefill of B samples of L tokens (same rule as the
 // decode's, over the prefill's query blocks).
@@ -991,21 +1209,25 @@ size_t split_ws_bytes(int B, int S, int splits) {
 // Bytes of the rotated suffix K a decode with the rotary embedding keeps in its workspace.
 size_t rope_ks_bytes(int B, int S) { return pi::align_up((size_t)B * S * 256 * 2, 256); }
 
-// Decode workspace: [rotated suffix K (rotary embedding only)] [key-split partials].
-size_t decode_split_bytes(int B, int S, int splits) {
-  if (S == 1) return split_ws_bytes<CfgAr>(B, S, splits);
-  return small_decode(B, S) ? split_ws_bytes<CfgDecS>(B, S, splits) : pi32::decode_split_bytes(B, S, splits);
+// Decode workspace: [rotated suffix K (rotary embedding only)] [key-split partials
+// of whichever kernel a cache of len slots takes].
+size_t decode_split_bytes(int B, int S, int len) {
+  if (S == 1) return split_ws_bytes<CfgAr>(B, S, decode_splits_for<CfgAr>(B, S, len));
+  if (small_decode(B, S))
+    return std::max(split_ws_bytes<CfgSmall>(B, S, small_splits(S, len)),
+                    split_ws_bytes<CfgDecS>(B, S, decode_splits_for<CfgDecS>(B, S, len, 3)));
+  return pi32::decode_split_bytes(B, S, pi32::decode_splits(B, S, len));
 }
-size_t decode_ws_bytes(int B, int S, int Hq, int splits) {
+size_t decode_ws_bytes(int B, int S, int Hq, int len) {
   (void)Hq;
-  return rope_ks_bytes(B, S) + decode_split_bytes(B, S, splits);
+  return rope_ks_bytes(B, S) + decode_split_bytes(B, S, len);
 }
 
 }  // namespace
 
 size_t pi::decode_workspace_max(int B, int S, int Hq) {
-  // the most splits any cache length can take, for the shape decode_splits picks
-  return decode_ws_bytes(B, S, Hq, decode_splits(B, S, kMaxTiles * TK));
+  // the longest cache takes the most splits
+  return decode_ws_bytes(B, S, Hq, kMaxTiles * TK);
 }
 
 // Bytes of the rotated K a prefill with the rotary embedding keeps in its workspace.
@@ -1089,7 +1311,7 @@ extern "C" pi_status pi_joint_attn_prefill(const void* q, const void* k, const v
 
 extern "C" size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len) {
   if (B < 1 || S < 1 || Hq < 1 || len < 0) return 0;
-  return decode_ws_bytes(B, S, Hq, decode_splits(B, S, len));
+  return decode_ws_bytes(B, S, Hq, len);
 }
 
 namespace {
@@ -1120,6 +1342,41 @@ pi_status launch_decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf1
   decode_combine_kernel<kNR256, NWD><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
       opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits, nullptr);
   return pi::check_launch("decode_combine_kernel");
+}
+
+// The few-sample decode (decode_small_kernel) when the cache's tiles fit its
+// shares (at most kStages tiles per split) and the partials fit the workspace;
+// false: not launched, the caller takes the streaming kernel.
+bool try_decode_small(pi_status& st, const pi_kv_cache* cache, const __bf16* ckl, const __bf16* cvl,
+                      const void* q_s, const void* k_s, const void* v_s, const uint8_t* suffix_ar, int B, int S,
+                      float scale, float rope_base, void* o_s, bool tiled, char* split_ws, size_t split_avail,
+                      hipStream_t s) {
+  using C = CfgSmall;
+  const int nt = small_tiles(S, cache->len);
+  int splits = small_splits(S, cache->len);
+  if (nt > kStages * splits) return false;
+  if (splits > 1 && (split_ws == nullptr || split_avail < split_ws_bytes<C>(B, S, splits))) {
+    if (nt > kStages) return false;
+    splits = 1;   // without room for the partials, a short cache still fits one share
+  }
+  const int n_qblk = (S + C::TOK - 1) / C::TOK;
+  const size_t chunks = (size_t)splits * B * n_qblk * kNWsmall * kNR256;
+  float* opart = splits > 1 ? reinterpret_cast<float*>(split_ws) : nullptr;
+  float* mlpart = splits > 1 ? reinterpret_cast<float*>(split_ws + pi::align_up(chunks * 16 * 256 * sizeof(float), 256))
+                             : nullptr;
+  const Placement place = make_placement(B * splits, n_qblk);
+  const bool rope = rope_base > 0.f;
+  decode_small_kernel<256, 8, kNR256, kNWsmall><<<(unsigned)placement_grid(place), kNWsmall * 64, 0, s>>>(
+      ckl, cvl, cache->prefix_mask, cache->capacity, cache->len, static_cast<const __bf16*>(q_s),
+      static_cast<const __bf16*>(k_s), static_cast<const __bf16*>(v_s), suffix_ar, B, S,
+      scale * 1.4426950408889634f, static_cast<__bf16*>(o_s), tiled ? 1 : 0, place, splits, opart, mlpart,
+      rope ? 1 : 0, rope ? log2((double)rope_base) : 0.0);
+  st = pi::check_launch("decode_small_kernel");
+  if (st != PI_OK || splits == 1) return true;
+  decode_combine_kernel<kNR256, kNWsmall><<<(unsigned)(chunks / splits * 4), 256, 0, s>>>(
+      opart, mlpart, static_cast<__bf16*>(o_s), tiled ? 1 : 0, B, S, n_qblk, splits, nullptr);
+  st = pi::check_launch("decode_combine_kernel");
+  return true;
 }
 
 }  // namespace
@@ -1169,9 +1426,14 @@ pi_status pi::decode_layer(const pi_kv_cache* cache, int layer, const void* q_s,
   if (S == 1)
     return launch_decode<kNWar>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
                                 split_ws, split_avail, s);
-  if (small_decode(B, S))
+  if (small_decode(B, S)) {
+    pi_status st = PI_OK;
+    if (try_decode_small(st, cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled, split_ws,
+                         split_avail, s))
+      return st;
     return launch_decode<kNWdecS>(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled,
                                   split_ws, split_avail, s);
+  }
   return pi32::decode(cache, ckl, cvl, q_s, kk, v_s, suffix_ar, B, S, scale, rope_base, o_s, tiled, split_ws,
                       split_avail, s);
 }

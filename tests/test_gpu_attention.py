@@ -246,6 +246,50 @@ def test_decode_parity_small(seed, B, P, S, split):
         assert_close(host64(o), want, f"decode seed={seed} layer={layer} split={split}")
 
 
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("seed,B,P,cap,S", [(10, 1, 816, 840, 51), (11, 2, 300, 300, 20), (12, 1, 70, 96, 51),
+                                            (13, 1, 1, 32, 51), (14, 1, 0, 64, 51)])
+def test_decode_few_samples_holes_nan_and_spike(seed, B, P, cap, S, split):
+    """The few-sample decode (a handful of key tiles per workgroup, all loaded at
+    once): padded slots scattered inside the cache length holding NaN K/V, a cache
+    capacity beyond its length, a late score maximum of 90 above the rest, an
+    empty cache, against the oracle."""
+    Bd = _bd()
+    note(f"few-sample decode seed={seed} B={B} len={P} cap={cap} S={S} split={split}")
+    r = np.random.default_rng(seed)
+    ck = I.bf16_normal(seed * 7 + 1, (1, B, cap, 1, 256))
+    cv = I.bf16_normal(seed * 7 + 2, (1, B, cap, 1, 256))
+    pm = (r.random((B, cap)) < 0.8).astype(np.uint8)
+    pm[:, P:] = 0
+    if P > 0:
+        pm[:, 0] = 1
+    pad = pm == 0
+    ck_dev, cv_dev = ck.copy(), cv.copy()
+    ck_dev[0][pad] = 0x7FC0      # NaN in every padded slot of what the kernel reads
+    cv_dev[0][pad] = 0x7FC0
+    sar = np.array([1, 1] + [0] * (S - 2), np.uint8)
+    qs = I.bf16_normal(seed * 7 + 3, (B, S, 8, 256))
+    ks = I.bf16_normal(seed * 7 + 4, (B, S, 1, 256))
+    vs = I.bf16_normal(seed * 7 + 5, (B, S, 1, 256))
+    if P > 40:
+        # one late valid slot scores 90 against query row (token 3, head 2) of sample 0
+        j = int(np.flatnonzero(pm[0, :P])[-1])
+        qv = np.zeros(256)
+        qv[:4] = 1.0
+        qs[0, 3, 2] = I.f32_to_bf16_bits(qv)
+        kv = np.zeros(256)
+        kv[:4] = 90.0 * 16.0 / 4.0   # score 90 after the 1/16 scale
+        ck[0, 0, j, 0] = ck_dev[0, 0, j, 0] = I.f32_to_bf16_bits(kv)
+    cache = _cache_from(ck_dev, cv_dev, pm, length=P)
+    ws = Bd.decode_workspace(cache, S) if split else None
+    o = Bd.pi_suffix_decode_step(cache, 0, bf16_dev(qs), bf16_dev(ks), bf16_dev(vs), u8_dev(sar), workspace=ws)
+    torch.cuda.synchronize()
+    got = host64(o)
+    assert np.isfinite(got).all()
+    want = A.cached_decode(f64(qs), f64(ks), f64(vs), f64(ck[0, :, :P]), f64(cv[0, :, :P]), pm[:, :P], sar)
+    assert_close(got, want, f"few-sample decode seed={seed} split={split}")
+
+
 def test_decode_matches_full_recompute():
     """The cached path equals the suffix rows of the joint prefill (same inputs)."""
     Bd = _bd()
