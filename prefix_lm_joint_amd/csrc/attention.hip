@@ -552,14 +552,14 @@ prefill_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const
   const int tok0 = qblk * C::TOK;
   const uint32_t* tk = tok + (size_t)b * L;
 
-  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, C::TOK, C::NWT, kmask, tlist,
-                    &tcount);
-  // the Q loads go out after the setup's own global reads (which wait on their
-  // results) and stay in flight through the barrier and the first K/V loads
+  // the Q loads go out first, with the setup's own reads, so one memory latency
+  // covers them all (the barrier below waits for every load in flight)
   WaveState<D, NR> st;
   init_state(st);
   __bf16* row_base[NR];
   if (!loader) load_rows<D, G, NR, C::ROWS_W>(st, row_base, q, o, (int64_t)b * L, L, Hq, kvh * G, tok0, tk);
+  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, C::TOK, C::NWT, kmask, tlist,
+                    &tcount);
   __syncthreads();
   const int count = tcount;
 
@@ -659,10 +659,36 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const int n_pt = (P + TK - 1) / TK;
   const int n_st = (S + TK - 1) / TK;
 
-  // suffix block ids: inclusive cumsum of suffix_ar (S <= 128), computed by wave 0
+  // the Q loads and all of the setup's reads (the suffix's block flags, the prefix
+  // slots' validity bytes, up to eight rounds before the first ballot) go out
+  // before any wait: one memory latency for the whole setup
+  WaveState<D, NR> st;
+  init_state(st);
+  __bf16* row_base[NR];
+  const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
+  if (!loader) load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, nullptr, q_tiled);
+  int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
+  int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
+  // validity bitmap of the prefix slots, one 32-bit word per tile
+  const uint8_t* pm = prefix_mask + (size_t)b * cap;
+  for (int base0 = wave * 64; base0 < n_pt * TK; base0 += 8 * C::NWT * 64) {
+    bool valid[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int slot = base0 + u * C::NWT * 64 + lane;
+      valid[u] = slot < P && pm[slot] != 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int base = base0 + u * C::NWT * 64;
+      if (base >= n_pt * TK) break;
+      const unsigned long long bal = __ballot(valid[u]);
+      if (lane == 0) pmask[base / TK] = (uint32_t)bal;
+      if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  // suffix block ids: inclusive cumsum of the flags (S <= 128), computed by wave 0
   if (wave == 0) {
-    int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
-    int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       int u0 = __shfl_up(a0, off), u1 = __shfl_up(a1, off);
@@ -671,15 +697,6 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     const int tot0 = __shfl(a0, 63);
     sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
     sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
-  }
-  // validity bitmap of the prefix slots, one 32-bit word per tile
-  const uint8_t* pm = prefix_mask + (size_t)b * cap;
-  for (int base = wave * 64; base < n_pt * TK; base += C::NWT * 64) {
-    const int slot = base + lane;
-    const bool valid = slot < P && pm[slot] != 0;
-    const unsigned long long bal = __ballot(valid);
-    if (lane == 0) pmask[base / TK] = (uint32_t)bal;
-    if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
   }
   __syncthreads();
   // compact tile list: non-empty prefix tiles, then the suffix tiles
@@ -707,13 +724,6 @@ decode_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     }
     if (lane == 0) tcount = cnt;
   }
-  // the Q loads go out after the setup's own global reads (which wait on their
-  // results) and stay in flight through the barrier and the first K/V loads
-  WaveState<D, NR> st;
-  init_state(st);
-  __bf16* row_base[NR];
-  const __bf16* q_tiled = tiled ? qs + (int64_t)b * ((S * G + 15) / 16 * 16) * D : nullptr;
-  if (!loader) load_rows<D, G, NR, C::ROWS_W>(st, row_base, qs, os, (int64_t)b * S, S, Hq, 0, tok0, nullptr, q_tiled);
   __syncthreads();
   // this workgroup's share of the tile list (all of it when the keys are not split)
   const int i_lo = (int)((int64_t)tcount * split / n_split);

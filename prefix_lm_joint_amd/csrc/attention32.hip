@@ -523,9 +523,12 @@ prefill32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, con
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int tok0 = qblk * TOK;
   const uint32_t* tk = tok + (size_t)b * L;
+
   query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, TOK, NW, kmask, tlist, &tcount);
 
-  // this lane's row: token t, head h (rows past the last token read token 0 and are never stored)
+  // this lane's row: token t, head h (rows past the last token read token 0 and are
+  // never stored); the Q loads go out after the setup's reads (measured: issuing
+  // them first, so the setup's waits cover them too, costs 2-3 %)
   const int row = wave * ROWS_W + (lane & 31);
   const int t = tok0 + row / G;
   const int hq = kvh * G + row % G;
@@ -627,10 +630,47 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const int n_pt = (P + TK - 1) / TK;
   const int n_st = (S + TK - 1) / TK;
 
-  // suffix block ids: inclusive cumsum of suffix_ar (S <= 128), by wave 0
+  // this lane's row; its Q loads go out first and stay in flight through the setup
+  const int row = wave * ROWS_W + (lane & 31);
+  const int t = tok0 + row / G;
+  const int hq = row % G;
+  const bool row_ok = t < S;
+  State st;
+  init_state(st);
+  if (tiled) {
+    // this sample's queries: rows t*8 + head of a tile-layout matrix of width 256,
+    // padded to whole 16-row blocks; blocks past the padding read block 0
+    const int padded = (S * G + 15) / 16 * 16;
+    int r = tok0 * G + row;
+    if (r >= padded) r &= 15;
+    load_q_tiled(st, qs, (int64_t)b * padded + r);
+  } else {
+    load_q_row(st, qs + (((int64_t)b * S + (row_ok ? t : 0)) * G + hq) * D);
+  }
+  // the suffix's block flags (S <= 128), then the validity bitmap of the prefix
+  // slots, one 32-bit word per tile, the bytes of up to eight rounds loaded
+  // before the first ballot: one memory latency for all of the setup's reads
+  int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
+  int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
+  const uint8_t* pm = prefix_mask + (size_t)b * cap;
+  for (int base0 = wave * 64; base0 < n_pt * TK; base0 += 8 * THREADS) {
+    bool valid[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int slot = base0 + u * THREADS + lane;
+      valid[u] = slot < P && pm[slot] != 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int base = base0 + u * THREADS;
+      if (base >= n_pt * TK) break;
+      const unsigned long long bal = __ballot(valid[u]);
+      if (lane == 0) pmask[base / TK] = (uint32_t)bal;
+      if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
+    }
+  }
+  // suffix block ids: inclusive cumsum of the flags, by wave 0
   if (wave == 0) {
-    int a0 = lane < S ? (suffix_ar[lane] != 0) : 0;
-    int a1 = lane + 64 < S ? (suffix_ar[lane + 64] != 0) : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int u0 = __shfl_up(a0, off), u1 = __shfl_up(a1, off);
@@ -642,15 +682,6 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     const int tot0 = __shfl(a0, 63);
     sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
     sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
-  }
-  // validity bitmap of the prefix slots, one 32-bit word per tile
-  const uint8_t* pm = prefix_mask + (size_t)b * cap;
-  for (int base = wave * 64; base < n_pt * TK; base += THREADS) {
-    const int slot = base + lane;
-    const bool valid = slot < P && pm[slot] != 0;
-    const unsigned long long bal = __ballot(valid);
-    if (lane == 0) pmask[base / TK] = (uint32_t)bal;
-    if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
   }
   __syncthreads();
   // compact tile list: non-empty prefix tiles, then the suffix tiles
@@ -675,22 +706,6 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
       cnt += __popcll(bal);
     }
     if (lane == 0) tcount = cnt;
-  }
-  const int row = wave * ROWS_W + (lane & 31);
-  const int t = tok0 + row / G;
-  const int hq = row % G;
-  const bool row_ok = t < S;
-  State st;
-  init_state(st);
-  if (tiled) {
-    // this sample's queries: rows t*8 + head of a tile-layout matrix of width 256,
-    // padded to whole 16-row blocks; blocks past the padding read block 0
-    const int padded = (S * G + 15) / 16 * 16;
-    int r = tok0 * G + row;
-    if (r >= padded) r &= 15;
-    load_q_tiled(st, qs, (int64_t)b * padded + r);
-  } else {
-    load_q_row(st, qs + (((int64_t)b * S + (row_ok ? t : 0)) * G + hq) * D);
   }
   __syncthreads();
   st.wq = row_ok ? sbid[t] : 0u;

@@ -167,15 +167,28 @@ __device__ __forceinline__ bool xcd_place(const Placement& p, int& group, int& s
 
 // bits[w] (w < n_words) = validity of tokens 32 w .. 32 w + 31 of one sample
 // (bit j set: token 32 w + j < L and its word's valid bit is set); one ballot per
-// 32 tokens, shared by the nwaves waves of the workgroup.
+// 32 tokens, shared by the nwaves waves of the workgroup.  The token words of
+// up to kBatch rounds are loaded before the first ballot needs one, so a whole
+// row costs one memory latency, not one per round.
 __device__ __forceinline__ void token_bitmap(const uint32_t* tk, int L, int n_words, int nwaves, uint32_t* bits) {
+  constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int base = wave * 64; base < n_words * TK; base += nwaves * 64) {
-    const int t = base + lane;
-    const bool valid = t < L && (tk[t] & 1u);
-    const unsigned long long bal = __ballot(valid);
-    if (lane == 0) bits[base / TK] = (uint32_t)bal;
-    if (lane == 32 && base / TK + 1 < n_words) bits[base / TK + 1] = (uint32_t)(bal >> 32);
+  const int stride = nwaves * 64, end = n_words * TK;
+  for (int base0 = wave * 64; base0 < end; base0 += kBatch * stride) {
+    uint32_t w[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int t = base0 + u * stride + lane;
+      w[u] = t < L ? tk[t] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int base = base0 + u * stride;
+      if (base >= end) break;
+      const unsigned long long bal = __ballot(w[u] & 1u);
+      if (lane == 0) bits[base / TK] = (uint32_t)bal;
+      if (lane == 32 && base / TK + 1 < n_words) bits[base / TK + 1] = (uint32_t)(bal >> 32);
+    }
   }
 }
 
@@ -185,24 +198,38 @@ __device__ __forceinline__ void token_bitmap(const uint32_t* tk, int L, int n_wo
 // the key tiles holding a visible pair for query tokens [tok0, tok0 + ntok), each
 // as tile | class << 16, the class merged over the 16-token query tiles those
 // tokens span (kept where they agree, else PARTIAL).  trow: this sample's
-// [n_qt, n_kt] tile classes.  The caller synchronises before reading them.
+// [n_qt, n_kt] tile classes.  Wave 0 loads the classes of the first two query
+// tiles before the token words, so both arrive within one memory latency.  The
+// caller synchronises before reading them.
 __device__ __forceinline__ void query_block_tiles(const uint32_t* tk, int L, const uint8_t* trow, int n_qt, int n_kt,
                                                   int tok0, int ntok, int nwaves, uint32_t* kmask, uint32_t* tlist,
                                                   int* tcount) {
+  constexpr int kC = kMaxTiles / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  token_bitmap(tk, L, n_kt, nwaves, kmask);
-  if (wave != 0) return;
   const int qt_lo = tok0 / PI_MASK_TILE_Q;
   const int qt_hi = min(n_qt, (tok0 + ntok + PI_MASK_TILE_Q - 1) / PI_MASK_TILE_Q);
+  int c0[kC], c1[kC];
+  if (wave == 0) {
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      const int kt = u * 64 + lane;
+      c0[u] = (kt < n_kt && qt_lo < qt_hi) ? trow[(size_t)qt_lo * n_kt + kt] : 0;
+      c1[u] = (kt < n_kt && qt_lo + 1 < qt_hi) ? trow[(size_t)(qt_lo + 1) * n_kt + kt] : c0[u];
+    }
+  }
+  token_bitmap(tk, L, n_kt, nwaves, kmask);
+  if (wave != 0) return;
   int cnt = 0;
-  for (int base = 0; base < n_kt; base += 64) {
-    const int kt = base + lane;
+#pragma unroll
+  for (int u = 0; u < kC; ++u) {
+    if (u * 64 >= n_kt) break;
+    const int kt = u * 64 + lane;
     int cls = 0;
     if (kt < n_kt) {
-      cls = -1;
-      for (int qt = qt_lo; qt < qt_hi; ++qt) {
+      cls = c0[u] == c1[u] ? c0[u] : PI_TILE_PARTIAL;
+      for (int qt = qt_lo + 2; qt < qt_hi; ++qt) {   // a block spanning three or more query tiles
         const int cl = trow[(size_t)qt * n_kt + kt];
-        cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
+        cls = cls == cl ? cls : PI_TILE_PARTIAL;
       }
     }
     const unsigned long long bal = __ballot(cls > 0);
