@@ -189,21 +189,23 @@ struct TileDesc {
 __device__ __forceinline__ int tile_cls(const TileDesc& t) { return (int)((t.d >> 16) & 0xFFu); }
 
 // This wave's loads of one K/V tile, prepared once per step so that issuing one in
-// a product slot is a single instruction: the two buffer resources (K and V at the
-// tile's first key) and the per-lane offsets of the wave's 2 * kLoadsPerWave loads,
-// out-of-range (zeros) for keys outside the tile's validity mask.
+// a product slot is a single instruction: the two buffer resources (K and V of the
+// sample, built once per kernel), the tile's byte offset from them (scalar, the
+// loads' soffset) and the per-lane offsets of the wave's 2 * kLoadsPerWave loads,
+// out of range (zeros) for keys outside the tile's validity mask.
 struct LoadPlan {
   i32x4 rk, rv;
+  uint32_t soff;
   uint32_t off[2 * kLoadsPerWave];
   uint32_t wo;        // prefill: this lane's offset of the key-word load (out of range: none)
 };
 
-__device__ __forceinline__ LoadPlan plan_kv(const Lanes& lo, const __bf16* k0, const __bf16* v0, int key0, int tsb,
+__device__ __forceinline__ LoadPlan plan_kv(const Lanes& lo, const i32x4& rk, const i32x4& rv, int key0, int tsb,
                                            uint32_t keymask, bool live) {
   LoadPlan pl;
-  const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(key0) * tsb;
-  pl.rk = make_rsrc(reinterpret_cast<const char*>(k0) + at);
-  pl.rv = make_rsrc(reinterpret_cast<const char*>(v0) + at);
+  pl.rk = rk;
+  pl.rv = rv;
+  pl.soff = (uint32_t)__builtin_amdgcn_readfirstlane(key0) * (uint32_t)tsb;
   // keys to fetch (uniform): every key of a full tile, none past the end
   const uint32_t fetch = live ? __builtin_amdgcn_readfirstlane(keymask) : 0u;
   if (fetch == 0xFFFFFFFFu) {
@@ -228,7 +230,7 @@ __device__ __forceinline__ void issue_planned(Stage* __restrict__ sg, const Load
   const int nn = isv ? n - kLoadsPerWave : n;
   const int wave = threadIdx.x >> 6;
   __bf16* dst = (isv ? sg->v : sg->k) + (size_t)(wave * kLoadsPerWave + nn) * 512;
-  pi_buffer_load_lds(isv ? pl.rv : pl.rk, lds_u32(dst), 16, (int)pl.off[n], 0, 0, 0);
+  pi_buffer_load_lds(isv ? pl.rv : pl.rk, lds_u32(dst), 16, (int)pl.off[n], (int)pl.soff, 0, 0);
 }
 
 // One pipeline step (its parts do not depend on one another):
@@ -549,6 +551,7 @@ prefill32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, con
   const __bf16* k0 = k + ((size_t)b * L * Hkv + kvh) * D;
   const __bf16* v0 = v + ((size_t)b * L * Hkv + kvh) * D;
   const i32x4 rw = make_rsrc(tk);
+  const i32x4 rk0 = make_rsrc(k0), rv0 = make_rsrc(v0);
   const int tsb = Hkv * D * 2;
   const Lanes lo = make_lanes(tsb);
   auto desc = [&](int i) {
@@ -557,7 +560,7 @@ prefill32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, con
   };
   auto plan = [&](const TileDesc& td, bool live) {
     const int key0 = (int)(td.d & 0xFFFFu) * TK;
-    LoadPlan pl = plan_kv(lo, k0, v0, key0, tsb, td.m, live);
+    LoadPlan pl = plan_kv(lo, rk0, rv0, key0, tsb, td.m, live);
     pl.wo = (live && lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
     return pl;
   };
@@ -716,15 +719,17 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   const __bf16* v0 = cv + (size_t)b * cap * D;
   const __bf16* ks0 = ks + (size_t)b * S * D;
   const __bf16* vs0 = vs + (size_t)b * S * D;
+  const i32x4 rk0 = make_rsrc(k0), rv0 = make_rsrc(v0), rks = make_rsrc(ks0), rvs = make_rsrc(vs0);
   const Lanes lo = make_lanes(D * 2);
   auto desc = [&](int i) {
     const u32x2 dm = tdesc[i];
     return TileDesc{dm[0], dm[1], 0u};
   };
   auto plan = [&](const TileDesc& td, bool live) {
-    const int key0 = (int)(td.d & 0xFFFFu) * TK;
-    const bool suffix = (td.d >> 24) & 1u;
-    LoadPlan pl = plan_kv(lo, suffix ? ks0 : k0, suffix ? vs0 : v0, key0, D * 2, td.m, live);
+    const uint32_t d = __builtin_amdgcn_readfirstlane(td.d);   // uniform: the resources are picked in scalars
+    const int key0 = (int)(d & 0xFFFFu) * TK;
+    const bool suffix = (d >> 24) & 1u;
+    LoadPlan pl = plan_kv(lo, suffix ? rks : rk0, suffix ? rvs : rv0, key0, D * 2, td.m, live);
     pl.wo = kOOB;
     return pl;
   };
@@ -803,20 +808,43 @@ combine32_kernel(const float* __restrict__ opart, const float* __restrict__ mlpa
   const int t = qblk * TOK + row / G;
   const int hq = kvh * G + row % G;
   const int h = lane >> 5;
-  float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, mlpart[(sp * n_chunks + chunk) * 64 + 2 * (lane & 31)]);
-  f32x4 acc[4] = {};
-  float Ls = 0.f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < n_split; ++sp) {
-      const int64_t at = sp * n_chunks + chunk;
-      const float m = mlpart[at * 64 + 2 * (lane & 31)];
-      const float l = mlpart[at * 64 + 2 * (lane & 31) + 1];
-      const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
-      Ls += w * l;
-      const f32x4* src = reinterpret_cast<const f32x4*>(opart) + at * 32 * 64 + lane;
+  // every split's (m, l) and the first eight splits' O values are loaded before
+  // the first use, so the merge waits on one memory latency (two past 8 splits)
+  constexpr int kBatch = 8;
+  static_assert(kMaxSplit32 == 2 * kBatch, "two batches of splits");
+  float ms[kMaxSplit32], ls[kMaxSplit32];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += w * __builtin_nontemporal_load(&src[(4 * c + q) * 64]);
+  for (int sp = 0; sp < kMaxSplit32; ++sp) {
+    const int64_t at = sp * n_chunks + chunk;
+    ms[sp] = sp < n_split ? mlpart[at * 64 + 2 * (lane & 31)] : -INFINITY;
+    ls[sp] = sp < n_split ? mlpart[at * 64 + 2 * (lane & 31) + 1] : 0.f;
+  }
+  f32x4 acc[4] = {};
+  float Ls = 0.f, M = -INFINITY;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half * kBatch >= n_split) break;
+    f32x4 op[kBatch][4];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = half * kBatch + u;
+      const f32x4* src = reinterpret_cast<const f32x4*>(opart) + (sp * n_chunks + chunk) * 32 * 64 + lane;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        op[u][q] = sp < n_split ? __builtin_nontemporal_load(&src[(4 * c + q) * 64]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (half == 0) {
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplit32; ++sp) M = fmaxf(M, ms[sp]);
+    }
+    if (M == -INFINITY) break;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = half * kBatch + u;
+      const float w = (ms[sp] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms[sp] - M);
+      Ls += w * ls[sp];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += w * op[u][q];
     }
   }
   if (t >= L) return;

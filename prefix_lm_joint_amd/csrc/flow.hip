@@ -59,34 +59,37 @@ constexpr float kRmsEps = 1e-6f;
 // one short batch of loads.  Products are computed transposed (A operand =
 // weights, B operand = activations) so a lane holds four consecutive output
 // columns of one row.
-template <int EPI, bool NORM, int NT, int NWV>
+template <int EPI, bool NORM, int NT, int NWV, int MF>
 __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
   constexpr int TN = 16 * NT;
+  constexpr int TM = 16 * MF;                    // rows per workgroup: MF 16-row fragments
   constexpr int PS = TN + 4;                     // LDS row stride (floats) of a partial tile
   constexpr int KB = 4;                          // k-steps of loads in flight
-  __shared__ float part[NWV][64 * PS];
-  __shared__ float ssp[NWV][64];
+  __shared__ float part[NWV][TM * PS];
+  __shared__ float ssp[NWV][TM];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * TN;
-  const int m0 = blockIdx.y * 64;
+  const int m0 = blockIdx.y * TM;
   const int kb = p.K / 32;
 
   // fragment (row block, k-step) of a tile-layout matrix
   const bf16x8* wt = reinterpret_cast<const bf16x8*>(p.w) + (int64_t)(n0 / 16) * kb * 64 + lane;
   const bf16x8* at = reinterpret_cast<const bf16x8*>(p.a) + (int64_t)(m0 / 16) * kb * 64 + lane;
 
-  f32x4 acc[NT][4];
+  f32x4 acc[NT][MF];
 #pragma unroll
   for (int i = 0; i < NT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < MF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss[MF];
+#pragma unroll
+  for (int j = 0; j < MF; ++j) ss[j] = 0.f;
 
   const int per = (kb + NWV - 1) / NWV;
   const int ks_lo = wave * per, ks_hi = min(kb, ks_lo + per);
   for (int ks0 = ks_lo; ks0 < ks_hi; ks0 += KB) {
-    bf16x8 wf[KB][NT], af[KB][4];
+    bf16x8 wf[KB][NT], af[KB][MF];
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const bool live = ks0 + u < ks_hi;          // uniform over the wave
@@ -94,14 +97,14 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
       for (int j = 0; j < NT; ++j)
         wf[u][j] = (live && n0 + 16 * j < p.N) ? wt[((int64_t)j * kb + ks0 + u) * 64] : bf16x8{};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) af[u][j] = live ? at[((int64_t)j * kb + ks0 + u) * 64] : bf16x8{};
+      for (int j = 0; j < MF; ++j) af[u][j] = live ? at[((int64_t)j * kb + ks0 + u) * 64] : bf16x8{};
     }
     __builtin_amdgcn_sched_barrier(0);   // every load of the batch is issued before the first wait
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       if constexpr (NORM) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < MF; ++j)
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float x = bf2f(af[u][j][i]);
@@ -111,7 +114,7 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int jn = 0; jn < NT; ++jn)
 #pragma unroll
-        for (int jm = 0; jm < 4; ++jm) acc[jn][jm] = mfma16x16x32(wf[u][jn], af[u][jm], acc[jn][jm]);
+        for (int jm = 0; jm < MF; ++jm) acc[jn][jm] = mfma16x16x32(wf[u][jn], af[u][jm], acc[jn][jm]);
     }
   }
 
@@ -119,11 +122,11 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
 #pragma unroll
   for (int jn = 0; jn < NT; ++jn)
 #pragma unroll
-    for (int jm = 0; jm < 4; ++jm)
+    for (int jm = 0; jm < MF; ++jm)
       *reinterpret_cast<f32x4*>(&part[wave][(16 * jm + c) * PS + 16 * jn + 4 * g]) = acc[jn][jm];
   if constexpr (NORM) {
 #pragma unroll
-    for (int jm = 0; jm < 4; ++jm) {
+    for (int jm = 0; jm < MF; ++jm) {
       const float t = group4_sum(ss[jm]);
       if (g == 0) ssp[wave][16 * jm + c] = t;
     }
@@ -131,7 +134,7 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
   __syncthreads();
 
   // finish: each task is four consecutive columns of one row
-  for (int task = threadIdx.x; task < 16 * TN; task += NWV * 64) {
+  for (int task = threadIdx.x; task < TM * TN / 4; task += NWV * 64) {
     const int ml = task / (TN / 4);
     const int nl = 4 * (task % (TN / 4));
     const int m = m0 + ml, nb = n0 + nl;
@@ -251,15 +254,20 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
 // Tile choice: 16-column tiles with sixteen waves splitting the contraction for
 // the few rows of a small batch (each wave then waits on a single short batch of
 // loads), 64 x 64 tiles with four waves once the rows alone give enough
-// workgroups.
+// workgroups.  A small batch with few column tiles (the output projection back to
+// the width) also splits the rows into 16-row tiles, so more workgroups share the
+// reads of the activations.
 template <int EPI, bool NORM>
 pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
-  if (a.M <= 256) {
+  if (a.M <= 256 && (a.N + 15) / 16 * ((a.M + 63) / 64) < 128) {
+    dim3 grid((a.N + 15) / 16, (a.M + 15) / 16);
+    gemm_kernel<EPI, NORM, 1, 16, 1><<<grid, 1024, 0, s>>>(a);
+  } else if (a.M <= 256) {
     dim3 grid((a.N + 15) / 16, (a.M + 63) / 64);
-    gemm_kernel<EPI, NORM, 1, 16><<<grid, 1024, 0, s>>>(a);
+    gemm_kernel<EPI, NORM, 1, 16, 4><<<grid, 1024, 0, s>>>(a);
   } else {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
-    gemm_kernel<EPI, NORM, 4, 4><<<grid, 256, 0, s>>>(a);
+    gemm_kernel<EPI, NORM, 4, 4, 4><<<grid, 256, 0, s>>>(a);
   }
   return pi::check_launch(name);
 }
