@@ -619,6 +619,7 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
                 float* __restrict__ mlpart, int rope, double rope_log2_base) {
   __shared__ Stage stage0, stage1, stage2, stage3;
   __shared__ uint32_t sbid[128];
+  __shared__ alignas(16) uint32_t swords[128 + TK];   // key word of suffix key u (0 past the suffix)
   __shared__ uint32_t pmask[kMaxTiles];
   __shared__ u32x2 tdesc[kMaxTiles];      // (tile | class << 16 | suffix << 24, key-validity bitmap)
   __shared__ double rope_if[D / 2];
@@ -685,6 +686,9 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     const int tot0 = __shfl(a0, 63);
     sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
     sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
+    swords[lane] = lane < S ? 1u | ((uint32_t)(1 + a0) << 3) : 0u;
+    swords[lane + 64] = lane + 64 < S ? 1u | ((uint32_t)(1 + tot0 + a1) << 3) : 0u;
+    if (lane < TK) swords[128 + lane] = 0u;
   }
   __syncthreads();
   // compact tile list: non-empty prefix tiles, then the suffix tiles
@@ -735,17 +739,17 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   };
   auto issue_words = [](Stage*, const LoadPlan&) {};
   // key words of the current tile (masked tiles only): a cache slot's is its validity
-  // bit (block id 0), a suffix key's its block id, 0 for keys outside the tile
+  // bit (block id 0); a suffix key's comes from the table (its block id, 0 past the
+  // suffix), four consecutive keys in one read
   auto words = [&](const Stage*, const TileDesc& t, int q) {
     const uint32_t d = t.d, m = t.m;
-    const int key0 = (int)(d & 0xFFFFu) * TK;
-    const bool suffix = (d >> 24) & 1u;
+    const int k4 = 8 * q + 4 * (lane >> 5);
     u32x4 w;
+    if ((d >> 24) & 1u) {
+      w = *reinterpret_cast<const u32x4*>(&swords[(int)(d & 0xFFFFu) * TK + k4]);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int key = 8 * q + 4 * (lane >> 5) + e;
-      const uint32_t bit = (m >> key) & 1u;
-      w[e] = suffix ? (bit ? sbid[min(key0 + key, 127)] : 0u) : bit;
+      for (int e = 0; e < 4; ++e) w[e] = (m >> (k4 + e)) & 1u;
     }
     return w;
   };
