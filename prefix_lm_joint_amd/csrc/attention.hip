@@ -1193,9 +1193,16 @@ int decode_splits_for(int B, int S, int len, int min_tiles = 2) {
 }
 bool small_decode(int B, int S) { return S > 1 && B * ((S + CfgDec::TOK - 1) / CfgDec::TOK) <= 16; }
 // decode_small_kernel: key tiles of a sample (prefix slots, then suffix tokens)
-// and its key split, one to two tiles per split up to kMaxSplit splits.
+// and its key split: twelve splits (measured at B = 1 against 8, 10 and 16: the
+// partials the merge reads against each workgroup's chain), at least one tile
+// each, at most kStages each, at most kMaxSplit (the merge's limit; a longer cache
+// takes the streaming kernel).
+constexpr int kSmallSplits = 12;
 int small_tiles(int S, int len) { return (len + TK - 1) / TK + (S + TK - 1) / TK; }
-int small_splits(int S, int len) { return std::max(1, std::min(kMaxSplit, small_tiles(S, len))); }
+int small_splits(int S, int len) {
+  const int nt = small_tiles(S, len);
+  return std::min(kMaxSplit, std::max((nt + kStages - 1) / kStages, std::min(kSmallSplits, nt)));
+}
 
 // Key splits for a GQA 8:1 prefill of B samples of L tokens (same rule as the
 // decode's, over the prefill's query blocks).

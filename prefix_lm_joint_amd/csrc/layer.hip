@@ -306,13 +306,16 @@ constexpr int kMaxSplitTiles = 512;                              // splits x til
 constexpr size_t kSplitWsBytes = (size_t)kMaxSplitTiles * 64 * 16 * 4;
 constexpr size_t kTiledSplitBytes = (size_t)32 << 20;              // tiled split partials (M x N x splits fp32)
 
-template <int EPI>
+// MF: 16-row fragments per workgroup (4: 64-row tiles, with the optional split of
+// the contraction; 1: 16-row tiles, no split, eight k steps of loads in flight).
+template <int EPI, int MF>
 __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams p) {
-  __shared__ float part[kSmallWaves][64 * 16];
+  constexpr int KB = MF == 1 ? 2 * kSmallKB : kSmallKB;
+  __shared__ float part[kSmallWaves][16 * MF * 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
-  const int64_t m0 = (int64_t)blockIdx.y * 64;
+  const int64_t m0 = (int64_t)blockIdx.y * 16 * MF;
   const int ks_all = p.K / 32;
   const int kz = (ks_all + p.splits - 1) / p.splits;            // this split's k steps
   const int kz_lo = blockIdx.z * kz, ks = min(ks_all, kz_lo + kz) - kz_lo;
@@ -320,43 +323,43 @@ __global__ void __launch_bounds__(kSmallWaves * 64) gemm_small_kernel(GemmParams
   const int k_lo = kz_lo + wave * per, k_hi = kz_lo + min(ks, wave * per + per);
   // this lane's operand rows: W row n0 + c; A rows m0 + 16 j + c (through the row map), or none
   const __bf16* wrow = p.w + (int64_t)(n0 + c) * p.K + 8 * g;
-  const __bf16* arow[4];
+  const __bf16* arow[MF];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < MF; ++j) {
     const int64_t m = m0 + 16 * j + c;
     arow[j] = m < p.M ? p.a + p.amap(m) * p.K + 8 * g : nullptr;
   }
-  f32x4 acc[4];
+  f32x4 acc[MF];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = k_lo; k0 < k_hi; k0 += kSmallKB) {
-    bf16x8 wf[kSmallKB], af[kSmallKB][4];
+  for (int j = 0; j < MF; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = k_lo; k0 < k_hi; k0 += KB) {
+    bf16x8 wf[KB], af[KB][MF];
 #pragma unroll
-    for (int u = 0; u < kSmallKB; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const bool live = k0 + u < k_hi;     // uniform over the wave
       wf[u] = live ? *reinterpret_cast<const bf16x8*>(wrow + 32 * (k0 + u)) : bf16x8{};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < MF; ++j)
         af[u][j] = (live && arow[j]) ? *reinterpret_cast<const bf16x8*>(arow[j] + 32 * (k0 + u)) : bf16x8{};
     }
     __builtin_amdgcn_sched_barrier(0);     // the batch's loads all go out before the first wait
 #pragma unroll
-    for (int u = 0; u < kSmallKB; ++u)
+    for (int u = 0; u < KB; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(wf[u], af[u][j], acc[j]);
+      for (int j = 0; j < MF; ++j) acc[j] = mfma16x16x32(wf[u], af[u][j], acc[j]);
   }
   // acc[j][i] = C[m0 + 16 j + c][n0 + 4 g + i]
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < MF; ++j)
     *reinterpret_cast<f32x4*>(&part[wave][(16 * j + c) * 16 + 4 * g]) = acc[j];
   __syncthreads();
-  if (threadIdx.x < 256) {
+  if (threadIdx.x < 64 * MF) {
     const int ml = threadIdx.x >> 2, nl = 4 * (threadIdx.x & 3);
     const int64_t m = m0 + ml;
     f32x4 r = *reinterpret_cast<const f32x4*>(&part[0][ml * 16 + nl]);
 #pragma unroll
     for (int w = 1; w < kSmallWaves; ++w) r += *reinterpret_cast<const f32x4*>(&part[w][ml * 16 + nl]);
-    if (p.splits > 1) {
+    if (MF == 4 && p.splits > 1) {
       const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       const int64_t at = (blockIdx.z * (int64_t)gridDim.x * gridDim.y + tile) * 1024 + ml * 16 + nl;
       *reinterpret_cast<f32x4*>(p.split_ws + at) = r;
@@ -381,9 +384,17 @@ __global__ void __launch_bounds__(256) gemm_split_reduce_kernel(GemmParams p) {
 }
 
 // 256 x 256 tiles once the rows alone give a few hundred workgroups, else 256 x 128;
-// the split-contraction kernel for few rows.
+// the split-contraction kernel for few rows.  With few rows and few column tiles
+// (the output projection and the FFN down product back to the width) 16-row
+// tiles fill the chip instead of a split contraction, so no reduce kernel follows.
 template <int EPI>
 pi_status launch_gemm(GemmParams p, hipStream_t s) {
+  if (p.M <= kSmallM && (p.N / 16) * ((p.M + 63) / 64) < 128) {
+    p.splits = 1;
+    const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.M + 15) / 16), 1);
+    gemm_small_kernel<EPI, 1><<<grid, kSmallWaves * 64, 0, s>>>(p);
+    return pi::check_launch("gemm_small_kernel");
+  }
   if (p.M <= kSmallM) {
     // split the contraction across workgroups when the column tiles alone leave
     // most of the chip idle and every split keeps at least 16 k steps of 32
@@ -395,7 +406,7 @@ pi_status launch_gemm(GemmParams p, hipStream_t s) {
         splits *= 2;
     p.splits = splits;
     const dim3 grid((unsigned)(p.N / 16), (unsigned)((p.M + 63) / 64), (unsigned)splits);
-    gemm_small_kernel<EPI><<<grid, kSmallWaves * 64, 0, s>>>(p);
+    gemm_small_kernel<EPI, 4><<<grid, kSmallWaves * 64, 0, s>>>(p);
     pi_status st = pi::check_launch("gemm_small_kernel");
     if (st != PI_OK || splits == 1) return st;
     gemm_split_reduce_kernel<EPI><<<dim3(grid.x, grid.y), 256, 0, s>>>(p);
