@@ -134,23 +134,6 @@ struct DqWave {
   uint32_t wq;
 };
 
-// dS^T of one tile from its S^T and dP^T: lane (c, g) holds keys 16 kt + 4 g + i
-// of row c; the result is packed as the B operand of dQ^T += K^T dS^T.
-__device__ __forceinline__ bf16x8 dq_dscores(const Stage<BD>& cst, const DqWave& w, const f32x4 (&s)[2],
-                                             const f32x4 (&dp)[2], int cls, uint32_t forbid, float c2) {
-  const int g = (threadIdx.x & 63) >> 4;
-  bf16x8 ds;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p = hw_exp2(fmaf(s[kt][i], c2, -w.lse2));
-      if (cls == PI_TILE_PARTIAL && !pair_visible(w.wq, cst.w[kt * 16 + 4 * g + i], forbid)) p = 0.f;
-      ds[4 * kt + i] = f2bf(p * (dp[kt][i] - w.dr));
-    }
-  return ds;
-}
-
 // S^T = K Q^T and dP^T = V dO^T of one tile (the pipeline's first).
 __device__ __forceinline__ void dq_products(const Stage<BD>& st, const BwdOffsets& lo, const DqWave& w,
                                             f32x4 (&s)[2], f32x4 (&dp)[2]) {
@@ -165,8 +148,11 @@ __device__ __forceinline__ void dq_products(const Stage<BD>& st, const BwdOffset
 
 // One dq step's block: dQ^T += K^T dS^T for tile i-1 (K of `pst`, transposing
 // read; its dS^T in dsp), S^T = K Q^T and dP^T = V dO^T for tile i+1 (row-wise
-// reads of `nst`) into s_n / dp_n, in 16 slots with the reads 2 slots ahead;
-// then dS^T of tile i (its mask words in `cst`).
+// reads of `nst`) into s_n / dp_n, in 16 slots with the reads 2 slots ahead; and
+// dS^T of tile i (its mask words in `cst`), one weight per two slots (exponential
+// in the even slot, dS and the bf16 rounding in the odd one), so the vector work
+// runs under the products instead of after them.  Each lane holds keys
+// 16 kt + 4 g + i of row c; dS^T is packed as the B operand of the next dQ product.
 template <bool PV>
 __device__ __forceinline__ void dq_block(const Stage<BD>& pst, const Stage<BD>& cst, const Stage<BD>& nst,
                                          const BwdOffsets& lo, DqWave& w, const bf16x8& dsp, const f32x4 (&s)[2],
@@ -178,6 +164,16 @@ __device__ __forceinline__ void dq_block(const Stage<BD>& pst, const Stage<BD>& 
   auto rk = [&](int j) { return read_row(nst.k, lo.row(j >> 1) + (j & 1) * kHalf); };
   auto rv = [&](int j) { return read_row(nst.v, lo.row(j >> 1) + (j & 1) * kHalf); };
   auto rt = [&](int j) { return read_tr(pst.k, lo.tr(j)); };
+  // visibility of this lane's 8 (key, row) pairs of tile i (all of a FULL tile)
+  const int g = (threadIdx.x & 63) >> 4;
+  uint32_t vis = 0xFFu;
+  if (cls == PI_TILE_PARTIAL) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!pair_visible(w.wq, cst.w[kt * 16 + 4 * g + i], forbid)) vis &= ~(1u << (4 * kt + i));
+  }
   bf16x8 kb[AH], vb[AH], tb[AH];
 #pragma unroll
   for (int j = 0; j < AH; ++j) {
@@ -185,6 +181,7 @@ __device__ __forceinline__ void dq_block(const Stage<BD>& pst, const Stage<BD>& 
     kb[j] = rk(j);
     vb[j] = rv(j);
   }
+  float pe[8];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -196,9 +193,16 @@ __device__ __forceinline__ void dq_block(const Stage<BD>& pst, const Stage<BD>& 
       kb[j % AH] = rk(j + AH);
       vb[j % AH] = rv(j + AH);
     }
+    const int e = j >> 1, kt = e >> 2, i = e & 3;
+    if ((j & 1) == 0) {
+      const float p = hw_exp2(fmaf(s[kt][i], c2, -w.lse2));
+      pe[e] = ((vis >> e) & 1u) ? p : 0.f;
+      asm volatile("" : "+v"(pe[e]));
+    } else {
+      ds_new[e] = f2bf(pe[e] * (dp[kt][i] - w.dr));
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
-  ds_new = dq_dscores(cst, w, s, dp, cls, forbid, c2);
 }
 
 __device__ __forceinline__ void dq_last(const Stage<BD>& pst, const BwdOffsets& lo, DqWave& w, const bf16x8& dsp) {
@@ -353,28 +357,6 @@ struct DkvWave {
   uint32_t wk;
 };
 
-// P^T and dS^T of one tile: lane (c, g) holds rows 16 h + 4 g + i for key c,
-// packed as the B operands of dV^T += dO^T P^T and dK^T += Q^T dS^T.
-__device__ __forceinline__ void dkv_weights(const DkvStage& cst, const DkvWave& w, const f32x4 (&s)[2],
-                                            const f32x4 (&dp)[2], bf16x8& pf, bf16x8& dsf, int cls,
-                                            uint32_t forbid, float c2) {
-  const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x4 l2 = *reinterpret_cast<const f32x4*>(&cst.lse2[16 * h + 4 * g]);
-    const f32x4 d2 = *reinterpret_cast<const f32x4*>(&cst.dr[16 * h + 4 * g]);
-    u32x4 wq = {0u, 0u, 0u, 0u};
-    if (cls == PI_TILE_PARTIAL) wq = *reinterpret_cast<const u32x4*>(&cst.t.w[16 * h + 4 * g]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float p = hw_exp2(fmaf(s[h][i], c2, -l2[i]));
-      if (cls == PI_TILE_PARTIAL && !pair_visible(wq[i], w.wk, forbid)) p = 0.f;
-      pf[4 * h + i] = f2bf(p);
-      dsf[4 * h + i] = f2bf(p * (dp[h][i] - d2[i]));
-    }
-  }
-}
-
 // S^T = Q K^T and dP^T = dO V^T of one tile (the pipeline's first).
 __device__ __forceinline__ void dkv_products(const DkvStage& st, const BwdOffsets& lo, const DkvWave& w,
                                              f32x4 (&s)[2], f32x4 (&dp)[2]) {
@@ -389,7 +371,11 @@ __device__ __forceinline__ void dkv_products(const DkvStage& st, const BwdOffset
 
 // One dK/dV step's block: dV^T += dO^T P^T and dK^T += Q^T dS^T for tile i-1
 // (transposing reads of `pst`), S^T = Q K^T and dP^T = dO V^T for tile i+1
-// (row-wise reads of `nst`), then P^T and dS^T of tile i (statistics in `cst`).
+// (row-wise reads of `nst`), and P^T and dS^T of tile i (statistics in `cst`),
+// one weight per two slots (exponential in the even slot, dS and the bf16
+// roundings in the odd one) under the products.  Lane (c, g) holds rows
+// 16 h + 4 g + i for key c, packed as the B operands of dV^T += dO^T P^T and
+// dK^T += Q^T dS^T.
 template <bool PV>
 __device__ __forceinline__ void dkv_block(const DkvStage& pst, const DkvStage& cst, const DkvStage& nst,
                                           const BwdOffsets& lo, DkvWave& w, const bf16x8& pfp, const bf16x8& dsp,
@@ -403,6 +389,21 @@ __device__ __forceinline__ void dkv_block(const DkvStage& pst, const DkvStage& c
   auto ro = [&](int j) { return read_row(nst.t.v, lo.row(j >> 1) + (j & 1) * kHalf); };
   auto tq = [&](int j) { return read_tr(pst.t.k, lo.tr(j)); };
   auto to = [&](int j) { return read_tr(pst.t.v, lo.tr(j)); };
+  // tile i's row statistics and the visibility of this lane's 8 (row, key) pairs
+  const int g = (threadIdx.x & 63) >> 4;
+  f32x4 l2[2], d2[2];
+  uint32_t vis = 0xFFu;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    l2[h] = *reinterpret_cast<const f32x4*>(&cst.lse2[16 * h + 4 * g]);
+    d2[h] = *reinterpret_cast<const f32x4*>(&cst.dr[16 * h + 4 * g]);
+    if (cls == PI_TILE_PARTIAL) {
+      const u32x4 wq = *reinterpret_cast<const u32x4*>(&cst.t.w[16 * h + 4 * g]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!pair_visible(wq[i], w.wk, forbid)) vis &= ~(1u << (4 * h + i));
+    }
+  }
   bf16x8 qb[AH], ob[AH], tqb[AH], tob[AH];
 #pragma unroll
   for (int j = 0; j < AH; ++j) {
@@ -413,6 +414,7 @@ __device__ __forceinline__ void dkv_block(const DkvStage& pst, const DkvStage& c
     qb[j] = rq(j);
     ob[j] = ro(j);
   }
+  float pe[8];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -430,9 +432,17 @@ __device__ __forceinline__ void dkv_block(const DkvStage& pst, const DkvStage& c
       qb[j % AH] = rq(j + AH);
       ob[j % AH] = ro(j + AH);
     }
+    const int e = j >> 1, h = e >> 2, i = e & 3;
+    if ((j & 1) == 0) {
+      const float p = hw_exp2(fmaf(s[h][i], c2, -l2[h][i]));
+      pe[e] = ((vis >> e) & 1u) ? p : 0.f;
+      asm volatile("" : "+v"(pe[e]));
+    } else {
+      pf_new[e] = f2bf(pe[e]);
+      ds_new[e] = f2bf(pe[e] * (dp[h][i] - d2[h][i]));
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
-  dkv_weights(cst, w, s, dp, pf_new, ds_new, cls, forbid, c2);
 }
 
 __device__ __forceinline__ void dkv_last(const DkvStage& pst, const BwdOffsets& lo, DkvWave& w, const bf16x8& pfp,
