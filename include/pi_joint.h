@@ -291,9 +291,10 @@ struct pi_kv_cache {
  * optional: with it a small batch splits each sample's keys over several
  * workgroups and merges the partial softmaxes, without it the call runs unsplit
  * (same result up to rounding).
- * Masked keys as in pi_joint_attn_prefill: padded cache slots may hold anything
- * (staged as zeros); an inf or NaN in the V of a suffix key that only some
- * suffix rows may read can reach the others as NaN.
+ * Masked keys as in pi_joint_attn_prefill: padded cache slots may hold anything,
+ * NaN included (they are staged as zeros, or, in the few-sample kernel, loaded,
+ * their V rows zeroed and their scores masked); an inf or NaN in the V of a
+ * suffix key that only some suffix rows may read can reach the others as NaN.
  */
 size_t pi_decode_workspace_bytes(int B, int S, int Hq, int len);
 pi_status pi_suffix_decode_step(const pi_kv_cache* cache, int layer, const void* q_s,
