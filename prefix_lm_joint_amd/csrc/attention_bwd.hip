@@ -455,25 +455,30 @@ __device__ __forceinline__ void dkv_last(const DkvStage& pst, const BwdOffsets& 
 }
 
 // The dK/dV tile loop: four stages, one barrier per tile; every wave issues its
-// share of tile i+2's loads right after step i's barrier.
+// share of tile i+2's loads right after step i's barrier.  The four stages are
+// four LDS objects and every step names the one its loads fill, so the compiler
+// sees that the step's reads of the other three do not depend on the loads in
+// flight (with one array, or a stage picked at run time, it made the first
+// read after the loads wait for them, every step).
 template <typename Desc, typename Issue>
-__device__ __forceinline__ void dkv_tiles(DkvStage (&stage)[kStagesB], const BwdOffsets& lo, DkvWave& w, int n,
-                                          Desc desc, Issue issue, uint32_t forbid, float c2) {
+__device__ __forceinline__ void dkv_tiles(DkvStage& s0, DkvStage& s1, DkvStage& s2, DkvStage& s3,
+                                          const BwdOffsets& lo, DkvWave& w, int n, Desc desc, Issue issue,
+                                          uint32_t forbid, float c2) {
   if (n <= 0) return;
-  issue(0, stage[0]);
-  if (n > 1) issue(1, stage[1]);
+  issue(0, s0);
+  if (n > 1) issue(1, s1);
   int cls_cur = entry_cls(desc(0)), cls_nxt = n > 1 ? entry_cls(desc(1)) : 0;
   wait_vmem();          // the K/V rows and this wave's share of tiles 0 and 1
   __syncthreads();
   f32x4 s[2], dp[2];
-  dkv_products(stage[0], lo, w, s, dp);
+  dkv_products(s0, lo, w, s, dp);
   bf16x8 pfp, dsp;
 #pragma unroll
   for (int e = 0; e < 8; ++e) pfp[e] = dsp[e] = f2bf(0.f);
-  auto step = [&](auto pv, int i, DkvStage& prev, DkvStage& cur, DkvStage& nxt) {
+  auto step = [&](auto pv, int i, DkvStage& prev, DkvStage& cur, DkvStage& nxt, DkvStage& ld) {
     wait_vmem();          // this wave's loads of tile i+1
     __syncthreads();      // everyone's; and every wave is done with tile i-2
-    if (i + 2 < n) issue(i + 2, stage[(i + 2) & 3]);
+    if (i + 2 < n) issue(i + 2, ld);
     bf16x8 pf_new, ds_new;
     f32x4 s_n[2], dp_n[2];
     dkv_block<decltype(pv)::value>(prev, cur, nxt, lo, w, pfp, dsp, s, dp, pf_new, ds_new, s_n, dp_n, cls_cur,
@@ -490,14 +495,15 @@ __device__ __forceinline__ void dkv_tiles(DkvStage (&stage)[kStagesB], const Bwd
   };
   using NoPV = std::integral_constant<bool, false>;
   using WithPV = std::integral_constant<bool, true>;
-  step(NoPV{}, 0, stage[3], stage[0], stage[1]);
+  step(NoPV{}, 0, s3, s0, s1, s2);
   for (int i = 1; i < n; i += 4) {
-    step(WithPV{}, i, stage[0], stage[1], stage[2]);
-    if (i + 1 < n) step(WithPV{}, i + 1, stage[1], stage[2], stage[3]);
-    if (i + 2 < n) step(WithPV{}, i + 2, stage[2], stage[3], stage[0]);
-    if (i + 3 < n) step(WithPV{}, i + 3, stage[3], stage[0], stage[1]);
+    step(WithPV{}, i, s0, s1, s2, s3);
+    if (i + 1 < n) step(WithPV{}, i + 1, s1, s2, s3, s0);
+    if (i + 2 < n) step(WithPV{}, i + 2, s2, s3, s0, s1);
+    if (i + 3 < n) step(WithPV{}, i + 3, s3, s0, s1, s2);
   }
-  dkv_last(stage[(n - 1) & 3], lo, w, pfp, dsp);
+  const int last = (n - 1) & 3;
+  dkv_last(last == 0 ? s0 : last == 1 ? s1 : last == 2 ? s2 : s3, lo, w, pfp, dsp);
 }
 
 // One workgroup per (sample, block of 64 keys), XCD-placed per sample.  Up
@@ -511,7 +517,7 @@ dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __
             __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, float scale, float c2,
             const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
             uint32_t forbid, Placement place) {
-  __shared__ DkvStage stage[kStagesB];
+  __shared__ DkvStage st0, st1, st2, st3;
   __shared__ uint32_t qlist[kMaxQTiles];
   __shared__ uint32_t qvalid[kMaxTiles];
   __shared__ int qcount;
@@ -606,7 +612,7 @@ dkdv_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __
     }
   };
   const BwdOffsets lo = bwd_offsets();
-  dkv_tiles(stage, lo, w, n, desc, issue, forbid, c2);
+  dkv_tiles(st0, st1, st2, st3, lo, w, n, desc, issue, forbid, c2);
   if (!ok) return;
   const int64_t r = ((int64_t)b * L + key) * BD + 4 * g;
 #pragma unroll
