@@ -228,7 +228,7 @@ __device__ __forceinline__ LoadPlan plan_kv(const Lanes& lo, const i32x4& rk, co
 __device__ __forceinline__ void issue_planned(Stage* __restrict__ sg, const LoadPlan& pl, int n) {
   const bool isv = n >= kLoadsPerWave;
   const int nn = isv ? n - kLoadsPerWave : n;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   __bf16* dst = (isv ? sg->v : sg->k) + (size_t)(wave * kLoadsPerWave + nn) * 512;
   pi_buffer_load_lds(isv ? pl.rv : pl.rk, lds_u32(dst), 16, (int)pl.off[n], (int)pl.soff, 0, 0);
 }
