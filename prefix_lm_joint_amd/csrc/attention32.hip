@@ -200,7 +200,8 @@ struct LoadPlan {
   uint32_t wo;        // prefill: this lane's offset of the key-word load (out of range: none)
 };
 
-__device__ __forceinline__ LoadPlan plan_kv(const Lanes& lo, const i32x4& rk, const i32x4& rv, int key0, int tsb,
+template <typename LN>
+__device__ __forceinline__ LoadPlan plan_kv(const LN& lo, const i32x4& rk, const i32x4& rv, int key0, int tsb,
                                            uint32_t keymask, bool live) {
   LoadPlan pl;
   pl.rk = rk;
@@ -879,6 +880,324 @@ size_t split_bytes(int groups, int n_qblk, int splits) {
   return pi::align_up(chunks * 32 * 256 * sizeof(float), 256) + chunks * 64 * sizeof(float);
 }
 
+// ---------------------------------------------------------------------------
+// dQ of the attention backward on the same engine (Hq = 8, Hkv = 1): the
+// forward's step with the softmax replaced by the weights of the backward.  Per
+// query row (this lane's row of the wave's 32): P = exp2(c2 S - lse2) from the
+// row's log-sum-exp (no running maximum), dS = P (dP - Dr), dQ = scale sum_j
+// dS_j k_j.  Per 32-key tile: S^T = K Q^T and dP^T = V dO^T (row-wise reads of
+// K and V, Q^T and dO^T from registers), then dQ^T += K^T dS^T with dS^T taken
+// straight from the accumulators as the forward's P^T, and K^T from two
+// transposing reads of the K tile.  K is read both ways, so its tile takes a
+// swizzle that serves both (dqsw); V is only read row-wise (fk).
+// ---------------------------------------------------------------------------
+
+// Logical 16-byte chunk x of K row r sits at x ^ dqsw(r): over r & 15 every value
+// once, rows r and r + 8 differ in chunk bit 3 (row-wise read), and each aligned
+// group of 4 rows differs in chunk bits 2-3 (the transposing read's 4 rows x 64
+// bytes then cover all 64 banks).
+__device__ __forceinline__ int dqsw(int r) { return (((r & 3) ^ ((r >> 2) & 2)) << 2) | ((r >> 2) & 3); }
+
+// Per-lane byte offsets (lane l, h = l / 32):
+//   kr[j] / vr[j]: row-wise A fragment j (< 8; j + 8 is + 256 bytes) of K / V: row
+//                  l % 32, logical chunk 2j + h.
+//   tr[c][e]: transposing read e of the K^T fragment of d chunk c (< 4; c + 4 is
+//             + 256 bytes): keys 8e + 4h .. + 3, column 32c + l % 32 (key half a
+//             adds 16 keys: dqsw sees only r & 15).
+//   ld_k / ld_v / ld_row: this wave's loads, as in Lanes.
+struct DqLanes {
+  uint32_t kr[8], vr[8];
+  uint32_t tr[4][2];
+  uint32_t ld_k[kLoadsPerWave], ld_v[kLoadsPerWave];
+  int ld_row[kLoadsPerWave];
+};
+
+__device__ __forceinline__ DqLanes make_dq_lanes(int tsb) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  DqLanes lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    lo.kr[j] = (uint32_t)(r * D * 2 + 16 * ((2 * j + h) ^ dqsw(r)));
+    lo.vr[j] = (uint32_t)(r * D * 2 + 16 * ((2 * j + h) ^ fk(r)));
+  }
+  const int g16 = (lane >> 4) & 1, jj = lane & 15;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int kr = 8 * e + 4 * h + (jj >> 2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int x = 4 * c + 2 * g16 + ((jj & 3) >> 1);
+      lo.tr[c][e] = (uint32_t)(kr * D * 2 + 16 * (x ^ dqsw(kr)) + 8 * (jj & 1));
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < kLoadsPerWave; ++n) {
+    const int row = 2 * (wave * kLoadsPerWave + n) + (lane >> 5);
+    const int p = lane & 31;
+    lo.ld_row[n] = row;
+    lo.ld_k[n] = (uint32_t)row * (uint32_t)tsb + 16u * (uint32_t)(p ^ dqsw(row));
+    lo.ld_v[n] = (uint32_t)row * (uint32_t)tsb + 16u * (uint32_t)(p ^ fk(row));
+  }
+  return lo;
+}
+
+__device__ __forceinline__ bf16x8 dq_read_k(const Stage& s, const DqLanes& lo, int j) {
+  return *at_bytes<bf16x8>(s.k, lo.kr[j & 7] + (j >> 3) * 256u);
+}
+__device__ __forceinline__ bf16x8 dq_read_v(const Stage& s, const DqLanes& lo, int j) {
+  return *at_bytes<bf16x8>(s.v, lo.vr[j & 7] + (j >> 3) * 256u);
+}
+// K^T fragment for product slot j: d chunk j / 2, key half j % 2.
+__device__ __forceinline__ bf16x8 dq_read_kt(const Stage& s, const DqLanes& lo, int j) {
+  const int c = j >> 1, a = j & 1;
+  const char* base = reinterpret_cast<const char*>(s.k) + (c >> 2) * 256 + a * (16 * D * 2);
+  const bf16x4 x0 = lds_read_tr4(reinterpret_cast<const __bf16*>(base + lo.tr[c & 3][0]));
+  const bf16x4 x1 = lds_read_tr4(reinterpret_cast<const __bf16*>(base + lo.tr[c & 3][1]));
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Per wave: Q^T and dO^T fragments of this lane's row (as State::qf), dQ^T in
+// the accumulator layout (chunk c, element i: d = 32c + 8(i/4) + 4h + i%4), the
+// row's lse2 (base 2; +inf: no visible key) and Dr, and its query word.
+struct DqState {
+  bf16x8 qf[16], of[16];
+  f32x16 acc[8];
+  float l2, dr;
+  uint32_t wq;
+};
+
+// One dQ step: S^T and dP^T of tile i+1 (K, V in `ks`), dQ^T += K^T dS^T of tile
+// i-1 (K of `vs`, dS^T in pp), and tile i's weights from sc / dc (mask words in
+// `cs`), with this wave's loads of tile i+2 into `ld` and the next plan (mid)
+// halfway.  Weight j: scaled in slot j-1, exponentiated in slot j, multiplied
+// by (dP - Dr) in slot j+1, rounded to bf16 as a pair two slots after that.
+template <bool PV, typename Words, typename IssueWords, typename Mid>
+__device__ __forceinline__ void dq_block(const Stage* __restrict__ vs, const Stage* __restrict__ cs,
+                                         const Stage* __restrict__ ks, Stage* __restrict__ ld, const DqLanes& lo,
+                                         DqState& st, const bf16x8 (&pp)[2], f32x16& sc, const f32x16& dc,
+                                         bf16x8 (&pn)[2], f32x16& sn, f32x16& dn, const TileDesc& tcur,
+                                         uint32_t forbid, float c2, const LoadPlan& pl, Words words,
+                                         IssueWords issue_words, Mid mid) {
+  constexpr int AH = 2;
+  if (tile_cls(tcur) == PI_TILE_PARTIAL) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 w = words(cs, tcur, q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!pair_visible(st.wq, w[e], forbid)) sc[4 * q + e] = -INFINITY;
+    }
+  }
+  issue_words(ld, pl);
+  bf16x8 tb[AH], kb[AH], vb[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    if constexpr (PV) tb[j] = dq_read_kt(*vs, lo, j);
+    kb[j] = dq_read_k(*ks, lo, j);
+    vb[j] = dq_read_v(*ks, lo, j);
+  }
+  float x[16], e[16];
+  bf16x2 pk[8];
+  x[0] = fmaf(sc[0], c2, -st.l2);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if constexpr (PV) st.acc[j >> 1] = mfma32(tb[j % AH], pp[j & 1], st.acc[j >> 1]);
+    sn = mfma32(kb[j % AH], st.qf[j], j == 0 ? f32x16{} : sn);
+    dn = mfma32(vb[j % AH], st.of[j], j == 0 ? f32x16{} : dn);
+    if (j + AH < 16) {
+      if constexpr (PV) tb[j % AH] = dq_read_kt(*vs, lo, j + AH);
+      kb[j % AH] = dq_read_k(*ks, lo, j + AH);
+      vb[j % AH] = dq_read_v(*ks, lo, j + AH);
+    }
+    e[j] = __builtin_amdgcn_exp2f(x[j]);
+    asm volatile("" : "+v"(e[j]));
+    if (j + 1 < 16) {
+      x[j + 1] = fmaf(sc[j + 1], c2, -st.l2);
+      asm volatile("" : "+v"(x[j + 1]));
+    }
+    if (j >= 1) {
+      e[j - 1] *= dc[j - 1] - st.dr;
+      asm volatile("" : "+v"(e[j - 1]));
+    }
+    if (j >= 3 && (j & 1)) {            // pair (j-3, j-2)
+      const int pr = (j - 3) >> 1;
+      pk[pr][0] = f2bf(e[j - 3]);
+      pk[pr][1] = f2bf(e[j - 2]);
+      asm volatile("" : "+v"(pk[pr]));
+    }
+    if (j < kLoadsPerWave * 2) issue_planned(ld, pl, j);
+    if (j == 8) mid();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("" : "+v"(sn));
+  asm volatile("" : "+v"(dn));
+  e[15] *= dc[15] - st.dr;
+  pk[6][0] = f2bf(e[12]);
+  pk[6][1] = f2bf(e[13]);
+  pk[7][0] = f2bf(e[14]);
+  pk[7][1] = f2bf(e[15]);
+#pragma unroll
+  for (int pr = 0; pr < 8; ++pr) {
+    pn[pr >> 2][2 * (pr & 3)] = pk[pr][0];
+    pn[pr >> 2][2 * (pr & 3) + 1] = pk[pr][1];
+  }
+}
+
+// The dQ tile loop, organised as run_tiles: tile j in stage (j - i_lo) % 4, tile
+// i+2 loading during step i, descriptors and plans one step ahead.
+template <typename Desc, typename Plan, typename Words, typename IssueWords>
+__device__ __forceinline__ void dq_tiles(Stage& s0, Stage& s1, Stage& s2, Stage& s3, const DqLanes& lo, DqState& st,
+                                         int i_lo, int i_hi, Desc desc, Plan plan, Words words,
+                                         IssueWords issue_words, uint32_t forbid, float c2) {
+  if (i_lo >= i_hi) return;
+  auto clamp = [&](int i) { return i < i_hi ? i : i_lo; };
+  {
+    const LoadPlan p0 = plan(desc(i_lo), true);
+    issue_words(&s0, p0);
+#pragma unroll
+    for (int n = 0; n < 2 * kLoadsPerWave; ++n) issue_planned(&s0, p0, n);
+    const bool two = i_lo + 1 < i_hi;
+    const LoadPlan p1 = plan(desc(clamp(i_lo + 1)), two);
+    issue_words(&s1, p1);
+#pragma unroll
+    for (int n = 0; n < 2 * kLoadsPerWave; ++n) issue_planned(&s1, p1, n);
+  }
+  TileDesc t_cur = desc(i_lo);
+  TileDesc t_n1 = desc(clamp(i_lo + 1));
+  TileDesc t_n3 = desc(clamp(i_lo + 3));
+  LoadPlan pl = plan(desc(clamp(i_lo + 2)), i_lo + 2 < i_hi);
+  __syncthreads();      // the first two tiles have landed
+  f32x16 sc = {}, dc = {};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sc = mfma32(dq_read_k(s0, lo, j), st.qf[j], sc);
+    dc = mfma32(dq_read_v(s0, lo, j), st.of[j], dc);
+  }
+  bf16x8 pp[2];
+  auto step = [&](auto pv, int i, Stage& prev, Stage& cur, Stage& nxt, Stage& ld) {
+    __syncthreads();      // tile i+1 has landed; every wave is done with tile i-2
+    const TileDesc t_n4 = desc(clamp(i + 4));
+    const TileDesc t3 = t_n3;
+    LoadPlan pl_next;
+    bf16x8 pn[2];
+    f32x16 sn, dn;
+    dq_block<decltype(pv)::value>(&prev, &cur, &nxt, &ld, lo, st, pp, sc, dc, pn, sn, dn, t_cur, forbid, c2, pl,
+                                  words, issue_words, [&]() { pl_next = plan(t3, i + 3 < i_hi); });
+    t_cur = t_n1;
+    t_n1 = desc(clamp(i + 2));
+    t_n3 = t_n4;
+    pl = pl_next;
+    pp[0] = pn[0];
+    pp[1] = pn[1];
+    sc = sn;
+    dc = dn;
+  };
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
+  step(NoPV{}, i_lo, s3, s0, s1, s2);
+  for (int i = i_lo + 1; i < i_hi; i += 4) {
+    step(WithPV{}, i, s0, s1, s2, s3);
+    if (i + 1 < i_hi) step(WithPV{}, i + 1, s1, s2, s3, s0);
+    if (i + 2 < i_hi) step(WithPV{}, i + 2, s2, s3, s0, s1);
+    if (i + 3 < i_hi) step(WithPV{}, i + 3, s3, s0, s1, s2);
+  }
+  const int last = (i_hi - 1 - i_lo) & 3;
+  const Stage& sl = last == 0 ? s0 : last == 1 ? s1 : last == 2 ? s2 : s3;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) st.acc[j >> 1] = mfma32(dq_read_kt(sl, lo, j), pp[j & 1], st.acc[j >> 1]);
+}
+
+// One workgroup per (sample, block of 16 query tokens), XCD-placed per sample
+// (q, dO, dq [B, L, 8, 256]; k, v [B, L, 1, 256]; lse2, dr [B, L, 8]).  Rows of
+// padded tokens take zero Q and dO, rows past the last token read token 0 and
+// are never stored.
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+dq32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+            const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dr,
+            __bf16* __restrict__ dq, int L, float scale, float c2, const uint32_t* __restrict__ tok,
+            const uint8_t* __restrict__ tiles, int n_qt, int n_kt, uint32_t forbid, Placement place) {
+  __shared__ Stage stage0, stage1, stage2, stage3;
+  __shared__ uint32_t kmask[kMaxTiles];
+  __shared__ uint32_t tlist[kMaxTiles];
+  __shared__ u32x2 tdesc[kMaxTiles];
+  __shared__ int tcount;
+  int b, qblk;
+  if (!xcd_place(place, b, qblk)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = qblk * TOK;
+  const uint32_t* tk = tok + (size_t)b * L;
+
+  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, TOK, NW, kmask, tlist, &tcount);
+
+  const int row = wave * ROWS_W + (lane & 31);
+  const int t = tok0 + row / G;
+  const int hq = row % G;
+  const bool row_ok = t < L;
+  DqState st;
+  {
+    const int64_t r = ((int64_t)b * L + (row_ok ? t : 0)) * G + hq;
+    st.wq = row_ok ? tk[t] : 0u;
+    const bool live = (st.wq & 1u) != 0u;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(q + r * D + 16 * j + 8 * h);
+      const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + r * D + 16 * j + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        st.qf[j][e] = live ? a[e] : f2bf(0.f);
+        st.of[j][e] = live ? d[e] : f2bf(0.f);
+      }
+    }
+    st.l2 = lse2[r];
+    st.dr = dr[r];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.acc[c] = f32x16{};
+  }
+  __syncthreads();
+  const int count = tcount;
+  for (int i = threadIdx.x; i < count; i += THREADS) {
+    const uint32_t d = tlist[i];
+    tdesc[i] = u32x2{d, kmask[d & 0xFFFFu]};
+  }
+  __syncthreads();
+
+  const i32x4 rw = make_rsrc(tk);
+  const i32x4 rk0 = make_rsrc(k + (size_t)b * L * D), rv0 = make_rsrc(v + (size_t)b * L * D);
+  const int tsb = D * 2;
+  const DqLanes lo = make_dq_lanes(tsb);
+  auto desc = [&](int i) {
+    const u32x2 dm = tdesc[i];
+    return TileDesc{dm[0], dm[1], 0u};
+  };
+  auto plan = [&](const TileDesc& td, bool live) {
+    const int key0 = (int)(td.d & 0xFFFFu) * TK;
+    LoadPlan pl = plan_kv(lo, rk0, rv0, key0, tsb, td.m, live);
+    pl.wo = (live && lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
+    return pl;
+  };
+  auto issue_words = [&](Stage* sg, const LoadPlan& pl) {
+    if (wave == 0) pi_buffer_load_lds(rw, lds_u32(&sg->w[0]), 4, (int)pl.wo, 0, 0, 0);
+  };
+  auto words = [&](const Stage* cs, const TileDesc&, int qq) {
+    return *reinterpret_cast<const u32x4*>(&cs->w[8 * qq + 4 * (lane >> 5)]);
+  };
+  dq_tiles(stage0, stage1, stage2, stage3, lo, st, 0, count, desc, plan, words, issue_words, forbid, c2);
+  if (!row_ok) return;
+  __bf16* dst = dq + (((int64_t)b * L + t) * G + hq) * D + 4 * (lane >> 5);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      bf16x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = f2bf(st.acc[c][4 * qq + e] * scale);
+      *reinterpret_cast<bf16x4*>(dst + 32 * c + 8 * qq) = x;
+    }
+}
+
 }  // namespace
 
 namespace pi32 {
@@ -950,6 +1269,18 @@ pi_status decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf16* cvl,
   combine32_kernel<<<(unsigned)(n_chunks * 2), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o_s),
                                                               tiled ? 1 : 0, n_chunks, n_qblk, S, G, splits, nullptr);
   return pi::check_launch("combine32_kernel");
+}
+
+pi_status dq(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* dr, void* dq,
+             int B, int L, float scale, const pi_mask* m, hipStream_t s) {
+  const Placement place = make_placement(B, (L + TOK - 1) / TOK);
+  const int64_t grid = placement_grid(place);
+  PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "dq: grid too large");
+  dq32_kernel<<<(unsigned)grid, THREADS, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(dout), lse2, dr, static_cast<__bf16*>(dq), L, scale, scale * 1.4426950408889634f,
+      m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits, place);
+  return pi::check_launch("dq32_kernel");
 }
 
 }  // namespace pi32

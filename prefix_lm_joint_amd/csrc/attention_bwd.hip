@@ -17,12 +17,12 @@
 //   * bwd_prep_kernel: Dr of every row from the bf16 O and dO (fp32 sum), and
 //     the row's lse in base 2 (+inf for a row with no visible key, whose
 //     weights then come out exactly 0).
-//   * dq_kernel: query-major, organised like the forward: 7 waves x 16 rows
-//     (14 tokens x 8 heads) per workgroup with Q and dO rows in registers; a load
-//     wave streams K/V tiles of 32 keys over four LDS stages.  Per tile:
-//     S^T = K Q^T and dP^T = V dO^T (row-wise reads of K and V), dS^T
-//     elementwise, dQ^T += K^T dS^T (the transposing read of K, dS^T straight
-//     from the accumulators as in the forward's PV).
+//   * dq32_kernel (attention32.hip, pi32::dq): query-major, on the forward's
+//     32 x 32 x 16 engine: 4 waves x 32 rows (16 tokens x 8 heads) per
+//     workgroup with Q and dO rows in registers.  Per 32-key tile: S^T = K Q^T
+//     and dP^T = V dO^T (row-wise reads of K and V), dS^T elementwise from the
+//     row's lse2 and Dr, dQ^T += K^T dS^T (transposing reads of K, dS^T straight
+//     from the accumulators as the forward's P^T).
 //   * dkdv_kernel: key-major, the same engine with queries and keys swapped: 4
 //     waves x 16 keys per workgroup with K and V rows in registers, tiles of 32
 //     query rows (4 tokens x 8 heads) of Q, dO and the row statistics streamed
@@ -31,13 +31,14 @@
 //     (transposing reads).  The fp32 dK and dV of 16 keys x 256 take 128
 //     registers per lane, so each wave runs alone on its SIMD with the whole
 //     register file and issues its share of the tile loads itself.
-//   * Every tile is swizzled with f_U, so one copy in LDS serves both the
-//     row-wise and the transposing read without bank conflicts.
+//   * dkdv_kernel's tiles are swizzled with f_U, so one copy in LDS serves both
+//     the row-wise and the transposing read without bank conflicts.
 // Each pipeline step runs one block on the matrix cores: the transposed
 // products of tile i-1 and the row-wise products of tile i+1, then the
 // elementwise work of tile i; tile i+2 streams in meanwhile.
 #include "common.h"
 #include "engine.h"
+#include "attention32.h"
 
 #include <math.h>
 
@@ -49,7 +50,6 @@ using namespace pi_engine;
 
 constexpr int BD = 256;                       // head dim
 constexpr int BG = 8;                         // query heads (the KV head is shared)
-constexpr int kStagesB = 4;
 constexpr uint32_t kHalf = 16u * BD * 2u;     // bytes of 16 tile rows
 constexpr float kLog2e = 1.4426950408889634f;
 using T256 = Tile<BD>;
@@ -122,222 +122,10 @@ bwd_prep_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout, c
 }
 
 // ---------------------------------------------------------------------------
-// dQ (query-major).
-// ---------------------------------------------------------------------------
-constexpr int kNWq = 7;                        // compute waves; one more loads
-constexpr int kTokQ = kNWq * 16 / BG;          // query tokens per workgroup (14)
-
-struct DqWave {
-  bf16x8 qf[BD / 32], df[BD / 32];   // B operands: Q and dO of row c, d = 32 ds + 8 g ..
-  f32x4 acc[BD / 16];                 // dQ^T[16 j + 4 g + i][row c]
-  float lse2, dr;
-  uint32_t wq;
-};
-
-// S^T = K Q^T and dP^T = V dO^T of one tile (the pipeline's first).
-__device__ __forceinline__ void dq_products(const Stage<BD>& st, const BwdOffsets& lo, const DqWave& w,
-                                            f32x4 (&s)[2], f32x4 (&dp)[2]) {
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) s[kt] = dp[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < BD / 16; ++j) {
-    s[j & 1] = mfma16x16x32(read_row(st.k, lo.row(j >> 1) + (j & 1) * kHalf), w.qf[j >> 1], s[j & 1]);
-    dp[j & 1] = mfma16x16x32(read_row(st.v, lo.row(j >> 1) + (j & 1) * kHalf), w.df[j >> 1], dp[j & 1]);
-  }
-}
-
-// One dq step's block: dQ^T += K^T dS^T for tile i-1 (K of `pst`, transposing
-// read; its dS^T in dsp), S^T = K Q^T and dP^T = V dO^T for tile i+1 (row-wise
-// reads of `nst`) into s_n / dp_n, in 16 slots with the reads 2 slots ahead; and
-// dS^T of tile i (its mask words in `cst`), one weight per two slots (exponential
-// in the even slot, dS and the bf16 rounding in the odd one), so the vector work
-// runs under the products instead of after them.  Each lane holds keys
-// 16 kt + 4 g + i of row c; dS^T is packed as the B operand of the next dQ product.
-template <bool PV>
-__device__ __forceinline__ void dq_block(const Stage<BD>& pst, const Stage<BD>& cst, const Stage<BD>& nst,
-                                         const BwdOffsets& lo, DqWave& w, const bf16x8& dsp, const f32x4 (&s)[2],
-                                         const f32x4 (&dp)[2], bf16x8& ds_new, f32x4 (&s_n)[2], f32x4 (&dp_n)[2],
-                                         int cls, uint32_t forbid, float c2) {
-  constexpr int NS = BD / 16, AH = 2;
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) s_n[kt] = dp_n[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto rk = [&](int j) { return read_row(nst.k, lo.row(j >> 1) + (j & 1) * kHalf); };
-  auto rv = [&](int j) { return read_row(nst.v, lo.row(j >> 1) + (j & 1) * kHalf); };
-  auto rt = [&](int j) { return read_tr(pst.k, lo.tr(j)); };
-  // visibility of this lane's 8 (key, row) pairs of tile i (all of a FULL tile)
-  const int g = (threadIdx.x & 63) >> 4;
-  uint32_t vis = 0xFFu;
-  if (cls == PI_TILE_PARTIAL) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!pair_visible(w.wq, cst.w[kt * 16 + 4 * g + i], forbid)) vis &= ~(1u << (4 * kt + i));
-  }
-  bf16x8 kb[AH], vb[AH], tb[AH];
-#pragma unroll
-  for (int j = 0; j < AH; ++j) {
-    if constexpr (PV) tb[j] = rt(j);
-    kb[j] = rk(j);
-    vb[j] = rv(j);
-  }
-  float pe[8];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    if constexpr (PV) w.acc[j] = mfma16x16x32(tb[j % AH], dsp, w.acc[j]);
-    s_n[j & 1] = mfma16x16x32(kb[j % AH], w.qf[j >> 1], s_n[j & 1]);
-    dp_n[j & 1] = mfma16x16x32(vb[j % AH], w.df[j >> 1], dp_n[j & 1]);
-    if (j + AH < NS) {
-      if constexpr (PV) tb[j % AH] = rt(j + AH);
-      kb[j % AH] = rk(j + AH);
-      vb[j % AH] = rv(j + AH);
-    }
-    const int e = j >> 1, kt = e >> 2, i = e & 3;
-    if ((j & 1) == 0) {
-      const float p = hw_exp2(fmaf(s[kt][i], c2, -w.lse2));
-      pe[e] = ((vis >> e) & 1u) ? p : 0.f;
-      asm volatile("" : "+v"(pe[e]));
-    } else {
-      ds_new[e] = f2bf(pe[e] * (dp[kt][i] - w.dr));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-__device__ __forceinline__ void dq_last(const Stage<BD>& pst, const BwdOffsets& lo, DqWave& w, const bf16x8& dsp) {
-#pragma unroll
-  for (int j = 0; j < BD / 16; ++j) w.acc[j] = mfma16x16x32(read_tr(pst.k, lo.tr(j)), dsp, w.acc[j]);
-}
-
-__device__ __forceinline__ int entry_cls(uint32_t e) { return (int)((e >> 16) & 0xFFu); }
-
-// The dq tile loop: the forward's pipeline (a load wave, four stages, one
-// barrier per tile) with the dq block.  desc(i): tile i's list entry.
-template <typename Desc, typename Issue>
-__device__ __forceinline__ void dq_tiles(Stage<BD> (&stage)[kStagesB], const BwdOffsets& lo, DqWave& w, int n,
-                                         bool loader, Desc desc, Issue issue, uint32_t forbid, float c2) {
-  if (n <= 0) return;
-  if (loader) {
-    issue(desc(0), stage[0]);
-    if (n > 1) issue(desc(1), stage[1]);
-    wait_vmem();
-    __syncthreads();
-    for (int i = 0; i < n; ++i) {
-      const bool more = i + 2 < n;
-      const uint32_t t = desc(more ? i + 2 : i);
-      wait_vmem();          // tile i+1 has landed
-      __syncthreads();      // ... and every wave is done with tile i-2
-      if (more) issue(t, stage[(i + 2) & 3]);
-    }
-    return;
-  }
-  int cls_cur = entry_cls(desc(0)), cls_nxt = n > 1 ? entry_cls(desc(1)) : 0;
-  wait_vmem();          // the Q/dO rows
-  __syncthreads();
-  f32x4 s[2], dp[2];
-  dq_products(stage[0], lo, w, s, dp);
-  bf16x8 dsp;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dsp[e] = f2bf(0.f);
-  auto step = [&](auto pv, int i, Stage<BD>& prev, Stage<BD>& cur, Stage<BD>& nxt) {
-    __syncthreads();
-    bf16x8 ds_new;
-    f32x4 s_n[2], dp_n[2];
-    dq_block<decltype(pv)::value>(prev, cur, nxt, lo, w, dsp, s, dp, ds_new, s_n, dp_n, cls_cur, forbid, c2);
-    cls_cur = cls_nxt;
-    if (i + 2 < n) cls_nxt = entry_cls(desc(i + 2));
-    dsp = ds_new;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = s_n[kt];
-      dp[kt] = dp_n[kt];
-    }
-  };
-  using NoPV = std::integral_constant<bool, false>;
-  using WithPV = std::integral_constant<bool, true>;
-  step(NoPV{}, 0, stage[3], stage[0], stage[1]);
-  for (int i = 1; i < n; i += 4) {
-    step(WithPV{}, i, stage[0], stage[1], stage[2]);
-    if (i + 1 < n) step(WithPV{}, i + 1, stage[1], stage[2], stage[3]);
-    if (i + 2 < n) step(WithPV{}, i + 2, stage[2], stage[3], stage[0]);
-    if (i + 3 < n) step(WithPV{}, i + 3, stage[3], stage[0], stage[1]);
-  }
-  dq_last(stage[(n - 1) & 3], lo, w, dsp);
-}
-
-// One workgroup per (sample, block of 14 query tokens), XCD-placed per sample.
-__global__ void __launch_bounds__((kNWq + 1) * 64)
-dq_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-          const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dr,
-          __bf16* __restrict__ dq, int L, float scale, float c2, const uint32_t* __restrict__ tok,
-          const uint8_t* __restrict__ tiles, int n_qt, int n_kt, uint32_t forbid, Placement place) {
-  __shared__ Stage<BD> stage[kStagesB];
-  __shared__ uint32_t kmask[kMaxTiles];
-  __shared__ uint32_t tlist[kMaxTiles];
-  __shared__ int tcount;
-  int b, qblk;
-  if (!xcd_place(place, b, qblk)) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, g = lane >> 4;
-  const bool loader = wave == kNWq;
-  const int tok0 = qblk * kTokQ;
-  const uint32_t* tk = tok + (size_t)b * L;
-  query_block_tiles(tk, L, tiles + (size_t)b * n_qt * n_kt, n_qt, n_kt, tok0, kTokQ, kNWq + 1, kmask, tlist,
-                    &tcount);
-  DqWave w;
-  const int row = wave * 16 + c;
-  const int t = tok0 + row / BG, h = row % BG;
-  const bool ok = !loader && t < L;
-  if (!loader) {
-    // rows past the last token read token 0 and are never stored; a padded
-    // row's Q and dO are replaced by zeros so nothing it holds reaches a product
-    const int64_t r = ((int64_t)b * L + (t < L ? t : 0)) * BG + h;
-    w.wq = t < L ? tk[t] : 0u;
-    const bool live = (w.wq & 1u) != 0u;
-#pragma unroll
-    for (int ds = 0; ds < BD / 32; ++ds) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(q + r * BD + ds * 32 + 8 * g);
-      const bf16x8 d = *reinterpret_cast<const bf16x8*>(dout + r * BD + ds * 32 + 8 * g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        w.qf[ds][e] = live ? a[e] : f2bf(0.f);
-        w.df[ds][e] = live ? d[e] : f2bf(0.f);
-      }
-    }
-    w.lse2 = lse2[r];
-    w.dr = dr[r];
-#pragma unroll
-    for (int j = 0; j < BD / 16; ++j) w.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();
-  const int count = tcount;
-  const __bf16* k0 = k + (size_t)b * L * BD;
-  const __bf16* v0 = v + (size_t)b * L * BD;
-  const i32x4 rw = make_rsrc(tk);
-  const BwdOffsets lo = bwd_offsets();
-  auto desc = [&](int i) { return tlist[i]; };
-  auto issue = [&](uint32_t e, Stage<BD>& sg) {
-    const int kt = (int)(e & 0xFFFFu), key0 = kt * TK;
-    issue_kv<BD>(sg, kv_lanes<BD>(BD * 2, true), k0, v0, key0, BD * 2, kmask[kt]);
-    const uint32_t off = (lane < TK && key0 + lane < L) ? (uint32_t)(key0 + lane) * 4u : kOOB;
-    pi_buffer_load_lds(rw, lds_u32(&sg.w[0]), 4, (int)off, 0, 0, 0);
-  };
-  dq_tiles(stage, lo, w, count, loader, desc, issue, forbid, c2);
-  if (!ok) return;
-  __bf16* dst = dq + (((int64_t)b * L + t) * BG + h) * BD + 4 * g;
-#pragma unroll
-  for (int j = 0; j < BD / 16; ++j) {
-    bf16x4 x;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = f2bf(w.acc[j][i] * scale);
-    *reinterpret_cast<bf16x4*>(dst + 16 * j) = x;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dK, dV (key-major).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int entry_cls(uint32_t e) { return (int)((e >> 16) & 0xFFu); }
+
 constexpr int kNWk = 4;                                    // waves, 16 keys each
 constexpr int kKeyBlk = kNWk * 16;                         // keys per workgroup
 constexpr int kMaxQTiles = kMaxTiles * TK / PI_MASK_TILE_Q;
@@ -705,12 +493,7 @@ extern "C" pi_status pi_joint_attn_backward(const void* q, const void* k, const 
       mask->tok, mask->tiles, mask->n_qt, mask->n_kt, mask->forbid_bits, pk);
   st = pi::check_launch("dkdv_kernel");
   if (st != PI_OK) return st;
-  const Placement pq = make_placement(B, (L + kTokQ - 1) / kTokQ);
-  dq_kernel<<<(unsigned)placement_grid(pq), (kNWq + 1) * 64, 0, s>>>(
-      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
-      static_cast<const __bf16*>(dout), lse2, dr, static_cast<__bf16*>(dq), L, scale, c2, mask->tok, mask->tiles,
-      mask->n_qt, mask->n_kt, mask->forbid_bits, pq);
-  if ((st = pi::check_launch("dq_kernel")) != PI_OK || !rope) return st;
+  if ((st = pi32::dq(q, k, v, dout, lse2, dr, dq, B, L, scale, mask, s)) != PI_OK || !rope) return st;
   const int64_t n = (int64_t)B * L;
   negate_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(mask->pos, neg_pos, n);
   if ((st = pi::check_launch("negate_kernel")) != PI_OK) return st;
