@@ -55,7 +55,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
 //   V transposing read: 16 lanes read 4 rows x 32 bytes (two chunks).
 //     d = 256: f_V(r) = 2r & 31; d = 64: f_V(r) = r & 6; 32 lanes (8 rows) then
 //     cover all 64 banks once.
-//   Both reads of one tile (d = 256, the backward kernels): f_U(r) = 2(r & 7) ^
+//   Both reads of one tile (d = 256, the backward dK/dV kernel): f_U(r) = 2(r & 7) ^
 //     ((r >> 3) & 1) ^ (r & 8).  Over 16 consecutive rows it takes each value
 //     0..15 once; rows 8h .. 8h+7 share the low bit and have distinct 2(r & 7),
 //     so the transposing read's 8 rows x chunks (2x, 2x+1) hit 16 distinct chunk
@@ -94,9 +94,9 @@ struct KvLanes {
   int row[N];
 };
 
-// unified = false: K with f_K, V with f_V (the forward); true: both with f_U.
+// K with f_K, V with f_V.
 template <int D>
-__device__ __forceinline__ KvLanes<D> kv_lanes(int tsb, bool unified = false) {
+__device__ __forceinline__ KvLanes<D> kv_lanes(int tsb) {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int p = lane % T::CHR;
@@ -105,8 +105,8 @@ __device__ __forceinline__ KvLanes<D> kv_lanes(int tsb, bool unified = false) {
   for (int j = 0; j < KvLanes<D>::N; ++j) {
     const int r = j * T::RPI + lane / T::CHR;
     kl.row[j] = r;
-    kl.k[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ (unified ? T::fu(r) : T::fk(r)));
-    kl.v[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ (unified ? T::fu(r) : T::fv(r)));
+    kl.k[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fk(r));
+    kl.v[j] = (uint32_t)r * (uint32_t)tsb + 16u * (uint32_t)(p ^ T::fv(r));
   }
   return kl;
 }
