@@ -460,22 +460,36 @@ __device__ __forceinline__ void rotate_q(State& st, int pos, const double* inv_f
     }
 }
 
-// Row sum of this lane's row (both halves) and the normalised output store:
-// dst(q, c) -> where d = 32 c + 8 q + 4 (lane / 32) .. + 3 go (nullptr: no row).
+// The normalised output store (l_row: the row's sum over both lane halves),
+// staged through LDS: the wave writes its rows into `buf` (32 rows x 512 bytes;
+// 16-byte chunk x of row r at chunk x ^ r), then reads them back a row per
+// half-wave, so that every global store writes two whole rows in 16-byte pieces
+// (each cache line from one instruction instead of from eight).
+//   dst(r, x) -> where d = 8x .. 8x + 7 of the wave's row r go (nullptr: no row).
+// The caller makes sure no wave still reads `buf` and no load still fills it.
 template <typename Dst>
-__device__ __forceinline__ void store_rows(const State& st, float l_row, Dst dst) {
+__device__ __forceinline__ void store_rows_staged(const State& st, float l_row, __bf16* buf, Dst dst) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, h = lane >> 5;
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  char* base = reinterpret_cast<char*>(buf);
 #pragma unroll
   for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      __bf16* p = dst(q, c);
-      if (p == nullptr) continue;
       bf16x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = f2bf(st.o[c][4 * q + e] * inv);
-      *reinterpret_cast<bf16x4*>(p) = v;
+      *reinterpret_cast<bf16x4*>(base + r * 512 + 16 * ((4 * c + q) ^ r) + 8 * h) = v;
     }
+  const int x = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int rr = 2 * i + h;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(base + rr * 512 + 16 * (x ^ rr));
+    __bf16* p = dst(rr, x);
+    if (p != nullptr) *reinterpret_cast<bf16x8*>(p) = v;
+  }
 }
 
 // Key-split epilogue: the unnormalised partial O^T of the wave's 32 rows in
@@ -593,10 +607,14 @@ prefill32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, con
     if (lse != nullptr && lane < 32 && row_ok)
       lse[((int64_t)b * L + t) * Hq + hq] =
           l_row > 0.f ? (st.m + log2f(l_row)) * 0.6931471805599453f : -INFINITY;
-    __bf16* orow = row_ok ? o + (((int64_t)b * L + t) * Hq + hq) * D : nullptr;
-    const int h = lane >> 5;
-    store_rows(st, l_row, [&](int qq, int c) -> __bf16* {
-      return orow ? orow + 32 * c + 8 * qq + 4 * h : nullptr;
+    // the stages are free once every wave is past its last read and its (dead) loads have landed
+    wait_vmem();
+    __syncthreads();
+    __bf16* buf = wave == 0 ? stage0.k : wave == 1 ? stage0.v : wave == 2 ? stage1.k : stage1.v;
+    // the wave's rows are 4 consecutive tokens x this KV head's 8 query heads
+    store_rows_staged(st, l_row, buf, [&](int r, int x) -> __bf16* {
+      const int tr = tok0 + (wave * ROWS_W + r) / G;
+      return tr < L ? o + (((int64_t)b * L + tr) * Hq + kvh * G + r % G) * D + 8 * x : nullptr;
     });
     return;
   }
@@ -774,16 +792,19 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   }
   const float l_row = st.l + __shfl_xor(st.l, 32);
   if (n_split == 1) {
-    const int h = lane >> 5;
+    wait_vmem();
+    __syncthreads();
+    __bf16* buf = wave == 0 ? stage0.k : wave == 1 ? stage0.v : wave == 2 ? stage1.k : stage1.v;
+    // the wave's rows: 4 consecutive suffix tokens x 8 heads
     if (tiled) {
-      store_rows(st, l_row, [&](int qq, int c) -> __bf16* {
-        if (!row_ok) return nullptr;
-        return os + tiled_offset((int64_t)b * S + t, hq * D + 32 * c + 8 * qq + 4 * h, G * D);
+      store_rows_staged(st, l_row, buf, [&](int r, int x) -> __bf16* {
+        const int tr = tok0 + (wave * ROWS_W + r) / G;
+        return tr < S ? os + tiled_offset((int64_t)b * S + tr, (r % G) * D + 8 * x, G * D) : nullptr;
       });
     } else {
-      __bf16* orow = row_ok ? os + (((int64_t)b * S + t) * G + hq) * D : nullptr;
-      store_rows(st, l_row, [&](int qq, int c) -> __bf16* {
-        return orow ? orow + 32 * c + 8 * qq + 4 * h : nullptr;
+      store_rows_staged(st, l_row, buf, [&](int r, int x) -> __bf16* {
+        const int tr = tok0 + (wave * ROWS_W + r) / G;
+        return tr < S ? os + (((int64_t)b * S + tr) * G + r % G) * D + 8 * x : nullptr;
       });
     }
     return;
