@@ -73,11 +73,18 @@ class Ctx:
     def f32(self, a):
         return self.torch.from_numpy(self.np.ascontiguousarray(a, dtype=self.np.float32)).to(self.dev)
 
-    def time_ms(self, fn, iters, warmup=2):
-        """Average ms per call of fn over `iters` calls, HIP events on the launch stream."""
+    def time_ms(self, fn, iters, warmup=2, warm_s=0.1):
+        """Average ms per call of fn over `iters` calls, HIP events on the launch stream,
+        after at least `warmup` calls and `warm_s` seconds of back-to-back calls: the
+        GPU's clocks ramp up under sustained load, and a leg that starts after its
+        host-side setup would otherwise time its first milliseconds at idle clocks."""
         torch = self.torch
-        for _ in range(warmup):
+        t0, n = time.perf_counter(), 0
+        while n < warmup or time.perf_counter() - t0 < warm_s:
             fn()
+            n += 1
+            if n % 4 == 0:
+                torch.cuda.synchronize()      # the host stays within a few calls of the GPU
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(self.stream)
