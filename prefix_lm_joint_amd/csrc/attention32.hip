@@ -460,18 +460,19 @@ __device__ __forceinline__ void rotate_q(State& st, int pos, const double* inv_f
     }
 }
 
-// The normalised output store (l_row: the row's sum over both lane halves),
-// staged through LDS: the wave writes its rows into `buf` (32 rows x 512 bytes;
-// 16-byte chunk x of row r at chunk x ^ r), then reads them back a row per
-// half-wave, so that every global store writes two whole rows in 16-byte pieces
-// (each cache line from one instruction instead of from eight).
+// Output store of the wave's 32 rows held transposed in accumulators (element
+// 4q + e of acc[c] in lane l: row l % 32, d = 32 c + 8 q + 4 (l / 32) + e), each
+// value times `mul`, rounded to bf16, staged through LDS: the wave writes its rows
+// into `buf` (32 rows x 512 bytes; 16-byte chunk x of row r at chunk x ^ r), then
+// reads them back a row per half-wave, so that every global store writes two
+// whole rows in 16-byte pieces (each cache line from one instruction instead of
+// from eight).
 //   dst(r, x) -> where d = 8x .. 8x + 7 of the wave's row r go (nullptr: no row).
 // The caller makes sure no wave still reads `buf` and no load still fills it.
 template <typename Dst>
-__device__ __forceinline__ void store_rows_staged(const State& st, float l_row, __bf16* buf, Dst dst) {
+__device__ __forceinline__ void store_rows_staged(const f32x16 (&acc)[8], float mul, __bf16* buf, Dst dst) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, h = lane >> 5;
-  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
   char* base = reinterpret_cast<char*>(buf);
 #pragma unroll
   for (int c = 0; c < 8; ++c)
@@ -479,7 +480,7 @@ __device__ __forceinline__ void store_rows_staged(const State& st, float l_row, 
     for (int q = 0; q < 4; ++q) {
       bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = f2bf(st.o[c][4 * q + e] * inv);
+      for (int e = 0; e < 4; ++e) v[e] = f2bf(acc[c][4 * q + e] * mul);
       *reinterpret_cast<bf16x4*>(base + r * 512 + 16 * ((4 * c + q) ^ r) + 8 * h) = v;
     }
   const int x = lane & 31;
@@ -612,7 +613,7 @@ prefill32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, con
     __syncthreads();
     __bf16* buf = wave == 0 ? stage0.k : wave == 1 ? stage0.v : wave == 2 ? stage1.k : stage1.v;
     // the wave's rows are 4 consecutive tokens x this KV head's 8 query heads
-    store_rows_staged(st, l_row, buf, [&](int r, int x) -> __bf16* {
+    store_rows_staged(st.o, l_row > 0.f ? 1.f / l_row : 0.f, buf, [&](int r, int x) -> __bf16* {
       const int tr = tok0 + (wave * ROWS_W + r) / G;
       return tr < L ? o + (((int64_t)b * L + tr) * Hq + kvh * G + r % G) * D + 8 * x : nullptr;
     });
@@ -795,14 +796,15 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     wait_vmem();
     __syncthreads();
     __bf16* buf = wave == 0 ? stage0.k : wave == 1 ? stage0.v : wave == 2 ? stage1.k : stage1.v;
+    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
     // the wave's rows: 4 consecutive suffix tokens x 8 heads
     if (tiled) {
-      store_rows_staged(st, l_row, buf, [&](int r, int x) -> __bf16* {
+      store_rows_staged(st.o, inv, buf, [&](int r, int x) -> __bf16* {
         const int tr = tok0 + (wave * ROWS_W + r) / G;
         return tr < S ? os + tiled_offset((int64_t)b * S + tr, (r % G) * D + 8 * x, G * D) : nullptr;
       });
     } else {
-      store_rows_staged(st, l_row, buf, [&](int r, int x) -> __bf16* {
+      store_rows_staged(st.o, inv, buf, [&](int r, int x) -> __bf16* {
         const int tr = tok0 + (wave * ROWS_W + r) / G;
         return tr < S ? os + (((int64_t)b * S + tr) * G + r % G) * D + 8 * x : nullptr;
       });
@@ -1206,17 +1208,14 @@ dq32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __
     return *reinterpret_cast<const u32x4*>(&cs->w[8 * qq + 4 * (lane >> 5)]);
   };
   dq_tiles(stage0, stage1, stage2, stage3, lo, st, 0, count, desc, plan, words, issue_words, forbid, c2);
-  if (!row_ok) return;
-  __bf16* dst = dq + (((int64_t)b * L + t) * G + hq) * D + 4 * (lane >> 5);
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq) {
-      bf16x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = f2bf(st.acc[c][4 * qq + e] * scale);
-      *reinterpret_cast<bf16x4*>(dst + 32 * c + 8 * qq) = x;
-    }
+  // the stages are free once every wave is past its last read and its (dead) loads have landed
+  wait_vmem();
+  __syncthreads();
+  __bf16* buf = wave == 0 ? stage0.k : wave == 1 ? stage0.v : wave == 2 ? stage1.k : stage1.v;
+  store_rows_staged(st.acc, scale, buf, [&](int r, int x) -> __bf16* {
+    const int tr = tok0 + (wave * ROWS_W + r) / G;
+    return tr < L ? dq + (((int64_t)b * L + tr) * G + r % G) * D + 8 * x : nullptr;
+  });
 }
 
 }  // namespace
