@@ -178,6 +178,36 @@ def test_prefix_rows_invariant_to_suffix_kv_bit_exact(split):
     assert torch.equal(o1[:, :P + t + 1].view(torch.int16), o4[:, :P + t + 1].view(torch.int16))
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_padded_keys_in_first_tiles(split):
+    """Padded keys inside the first two key tiles (a hole in tile 0, all of tile 0
+    padded, a hole in tile 1, tile 1 partly padded), holding NaN in K and V: the
+    tile loop's first loads are issued before its steady state, and a padded key
+    must land as zeros there too.  Compared with the oracle on every row, and
+    padded rows are zero."""
+    s = I.pi05_structure(150, 20, 13)
+    B, N, P = 4, s.n, 150
+    note(f"prefill padded first tiles split={split}")
+    valid = np.ones((B, N), np.uint8)
+    valid[0, 3:9] = 0          # hole in tile 0
+    valid[1, 0:32] = 0         # tile 0 fully padded (EMPTY for every query block)
+    valid[2, 40:41] = 0        # hole in tile 1
+    valid[3, 50:P] = 0         # tile 1 partly padded, the rest of the prefix too
+    q = I.bf16_normal(91, (B, N, 8, 256))
+    k = I.bf16_normal(92, (B, N, 1, 256))
+    v = I.bf16_normal(93, (B, N, 1, 256))
+    k[valid == 0] = 0x7FC0
+    v[valid == 0] = 0x7FC0
+    o = host64(_prefill(q, k, v, valid, s, split=split))
+    kz, vz = k.copy(), v.copy()
+    kz[valid == 0] = 0
+    vz[valid == 0] = 0
+    want = A.joint_attention(f64(q), f64(kz), f64(vz), valid, s.ar, s.seg, s.forbid)
+    assert np.isfinite(o).all()
+    assert_close(o, want, f"prefill padded first tiles split={split}")
+    assert (o[valid == 0] == 0).all()
+
+
 def test_decode_ignores_garbage_in_padded_slots():
     """Padded cache slots may hold anything (uninitialised memory, NaN)."""
     Bd = _bd()
