@@ -198,7 +198,7 @@ def backward_leg(cx: Ctx, iters: int):
     return {
         "workload": w.name, "B": w.B, "L": w.N, "allowed_pairs": pairs, "gflop_per_launch": flops / 1e9,
         "us_per_launch": ms * 1e3, "achieved_tflops": tflops, "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
-        "forward_with_lse_us": ms_fwd * 1e3, "kernel": "bwd_prep_kernel + dkdv_kernel + dq32_kernel",
+        "forward_with_lse_us": ms_fwd * 1e3, "kernel": "bwd_prep_kernel + dkdv32_kernel + dq32_kernel",
     }
 
 

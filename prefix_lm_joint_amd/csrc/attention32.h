@@ -27,6 +27,11 @@ pi_status decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf16* cvl,
                  const void* v_s, const uint8_t* suffix_ar, int B, int S, float scale, float rope_base, void* o_s,
                  bool tiled, void* split_ws, size_t split_avail, hipStream_t s);
 
+// dK, dV of the attention backward (shapes as dq below; dk, dv [B, L, 1, 256]):
+// dk = scale * sum over visible rows of dS q, dv = sum of P dO.
+pi_status dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* dr,
+               void* dk, void* dv, int B, int L, float scale, const pi_mask* m, hipStream_t s);
+
 // dQ of the attention backward (Hq = 8, Hkv = 1, d = 256; q, dout, dq [B, L, 8, 256],
 // k, v [B, L, 1, 256], lse2 / dr [B, L, 8]: the rows' log-sum-exp in base 2 and
 // dO . O): dq = scale * sum over visible keys of P (dP - Dr) k.

@@ -1218,6 +1218,375 @@ dq32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __
   });
 }
 
+// ---------------------------------------------------------------------------
+// dK, dV on the 32 x 32 x 16 engine (key-major).  A workgroup owns 64 keys of one
+// sample as two pairs of waves, 32 keys per pair; the query rows stream through
+// four stages, 32 rows (4 tokens x 8 heads) per step.  In a pair, wave A holds
+// its keys' K^T fragments and dV^T, wave B their V^T fragments and dK^T:
+//   A: S = Q K^T (row-wise Q reads), P = exp2(S c2 - lse2) on the visible pairs,
+//      dV^T += dO^T P (transposing dO reads); P goes to B through LDS, in fp32;
+//   B: dP = dO V^T (row-wise dO reads), dS = P (dP - Dr), dK^T += Q^T dS
+//      (transposing Q reads).
+// Lane l of either wave holds key l % 32 and query rows 8(i/4) + 4(l/32) + i%4 of
+// its S / dP accumulator, which is the B-operand layout of the dV / dK products
+// once their A operands (the transposing reads) order the rows the same way.
+// Step m: A runs dV += dO^T(m-1) P(m-1) and S(m+1) slot by slot while it turns
+// S(m) into P(m) (written to the exchange slot of tile m); B reads P(m-1)
+// (written by A in step m-1), forms dS(m-1) while its dP(m) products start, and
+// runs dK += Q^T(m-1) dS(m-1) four slots behind them.  A step touches tiles
+// m-1, m and m+1 while tile m+2 loads: four stages.  Steps run for m = 0 .. n,
+// the first without the dV / dK products, the last with its S / dP dropped.
+// ---------------------------------------------------------------------------
+constexpr int kKeys32 = 64;                       // keys per workgroup
+constexpr int kMaxQTiles32 = kMaxTiles * TK / PI_MASK_TILE_Q;
+
+// A stage: Q rows (t.k) and dO rows (t.v) of 32 query rows, their query words
+// (t.w), lse2 and Dr (lanes >= 32 of their loads land as zeros).
+struct BwStage {
+  Stage t;
+  alignas(16) float lse2[64];
+  alignas(16) float dr[64];
+};
+
+// Per-lane byte offsets: row-wise fragment j (< 8; j + 8 is + 256 bytes) of a
+// tile: row l % 32, logical chunk 2j + h; transposing reads as DqLanes::tr; the
+// wave's loads: rows 8 wave + 2 jj + h of the tile, chunk l % 32, pre-swizzled.
+struct BwLanes {
+  uint32_t kr[8];
+  uint32_t tr[4][2];
+  uint32_t ld[4];
+};
+
+__device__ __forceinline__ BwLanes make_bw_lanes() {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 31, h = lane >> 5;
+  BwLanes lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lo.kr[j] = (uint32_t)(r * D * 2 + 16 * ((2 * j + h) ^ dqsw(r)));
+  const int g16 = (lane >> 4) & 1, jj = lane & 15;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int kr = 8 * e + 4 * h + (jj >> 2);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int x = 4 * c + 2 * g16 + ((jj & 3) >> 1);
+      lo.tr[c][e] = (uint32_t)(kr * D * 2 + 16 * (x ^ dqsw(kr)) + 8 * (jj & 1));
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int row = 8 * wave + 2 * n + h;
+    lo.ld[n] = (uint32_t)row * (uint32_t)(D * 2) + 16u * (uint32_t)(r ^ dqsw(row));
+  }
+  return lo;
+}
+
+__device__ __forceinline__ bf16x8 bw_read_row(const __bf16* tile, const BwLanes& lo, int j) {
+  return *at_bytes<bf16x8>(tile, lo.kr[j & 7] + (j >> 3) * 256u);
+}
+// Transposed fragment for product slot j: d chunk j / 2, query-row half j % 2.
+__device__ __forceinline__ bf16x8 bw_read_tr(const __bf16* tile, const BwLanes& lo, int j) {
+  const int c = j >> 1, a = j & 1;
+  const char* base = reinterpret_cast<const char*>(tile) + (c >> 2) * 256 + a * (16 * D * 2);
+  const bf16x4 x0 = lds_read_tr4(reinterpret_cast<const __bf16*>(base + lo.tr[c & 3][0]));
+  const bf16x4 x1 = lds_read_tr4(reinterpret_cast<const __bf16*>(base + lo.tr[c & 3][1]));
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Register state of one wave: B-operand fragments of its 32 keys (K for A, V for
+// B; fragment j holds d = 16 j + 8 h .. + 7 of key l % 32), the dV^T or dK^T
+// accumulators (chunk c, element i: d = 32 c + 8(i/4) + 4h + i%4), the key's word,
+// the carried product of the next tile (S or dP) and the bf16 weights of tile i
+// (A: P(i)).
+struct BwWave {
+  bf16x8 f[16];
+  f32x16 acc[8];
+  f32x16 nx;
+  bf16x8 pp[2];
+  uint32_t wk;
+};
+
+// The visibility of this lane's 16 (row, key) pairs of a PARTIAL tile.
+__device__ __forceinline__ uint32_t bw_visible(const BwStage& st, uint32_t wk, uint32_t forbid, bool partial) {
+  if (!partial) return 0xFFFFu;
+  const int h = (threadIdx.x >> 5) & 1;
+  uint32_t vis = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 wq = *reinterpret_cast<const u32x4*>(&st.t.w[8 * q + 4 * h]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (pair_visible(wq[e], wk, forbid)) vis |= 1u << (4 * q + e);
+  }
+  return vis;
+}
+
+// One step m of wave A (tiles m-1, m, m+1 in `pst`, `cst`, `nst`): dV^T +=
+// dO^T(m-1) P(m-1) (PV; P(m-1) in w.pp), S(m+1) = Q(m+1) K^T into w.nx, and the
+// weights P(m) from S(m) (w.nx on entry) with tile m's statistics, spread over
+// the product slots as in the forward step (scaled in slot j-1, exponentiated in
+// slot j, rounded as a pair two slots later); P(m) goes to w.pp and, in fp32, to
+// the exchange slot `xo`.
+template <bool PV>
+__device__ __forceinline__ void bw_step_a(const BwStage& pst, const BwStage& cst, const BwStage& nst,
+                                          const BwLanes& lo, BwWave& w, bool partial_cur, uint32_t forbid, float c2,
+                                          f32x4* __restrict__ xo) {
+  constexpr int AH = 3;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  f32x4 l2[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) l2[q] = *reinterpret_cast<const f32x4*>(&cst.lse2[8 * q + 4 * h]);
+  const uint32_t vis = bw_visible(cst, w.wk, forbid, partial_cur);
+  bf16x8 qb[AH], tb[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    qb[j] = bw_read_row(nst.t.k, lo, j);
+    if constexpr (PV) tb[j] = bw_read_tr(pst.t.v, lo, j);
+  }
+  const f32x16 sc = w.nx;
+  float x[16], e[16];
+  bf16x2 pk[8];
+  f32x16 sn = {};
+  x[0] = fmaf(sc[0], c2, -l2[0][0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if constexpr (PV) w.acc[j >> 1] = mfma32(tb[j % AH], w.pp[j & 1], w.acc[j >> 1]);
+    sn = mfma32(qb[j % AH], w.f[j], sn);
+    if (j + AH < 16) {
+      if constexpr (PV) tb[j % AH] = bw_read_tr(pst.t.v, lo, j + AH);
+      qb[j % AH] = bw_read_row(nst.t.k, lo, j + AH);
+    }
+    e[j] = ((vis >> j) & 1u) ? __builtin_amdgcn_exp2f(x[j]) : 0.f;
+    asm volatile("" : "+v"(e[j]));
+    if (j + 1 < 16) {
+      x[j + 1] = fmaf(sc[j + 1], c2, -l2[(j + 1) >> 2][(j + 1) & 3]);
+      asm volatile("" : "+v"(x[j + 1]));
+    }
+    if (j >= 3 && (j & 1)) {            // pair (j-3, j-2)
+      const int pr = (j - 3) >> 1;
+      pk[pr][0] = f2bf(e[j - 3]);
+      pk[pr][1] = f2bf(e[j - 2]);
+      asm volatile("" : "+v"(pk[pr]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  pk[6][0] = f2bf(e[12]);
+  pk[6][1] = f2bf(e[13]);
+  pk[7][0] = f2bf(e[14]);
+  pk[7][1] = f2bf(e[15]);
+#pragma unroll
+  for (int pr = 0; pr < 8; ++pr) {
+    w.pp[pr >> 2][2 * (pr & 3)] = pk[pr][0];
+    w.pp[pr >> 2][2 * (pr & 3) + 1] = pk[pr][1];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xo[q * 64 + lane] = f32x4{e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]};
+  w.nx = sn;
+}
+
+// One step m of wave B (tiles m-1, m in `pst`, `cst`): with PV, dS(m-1) =
+// P(m-1) (dP(m-1) - Dr) from the exchange slot `xi`, w.nx (dP(m-1)) and tile
+// m-1's Dr, and dK^T += Q^T(m-1) dS(m-1) four slots behind; dP(m) = dO(m) V^T
+// into w.nx.
+template <bool PV>
+__device__ __forceinline__ void bw_step_b(const BwStage& pst, const BwStage& cst, const BwLanes& lo, BwWave& w,
+                                          const f32x4* __restrict__ xi) {
+  constexpr int AH = 3;
+  const int lane = threadIdx.x & 63, h = lane >> 5;
+  f32x4 pv[4], d4[4];
+  if constexpr (PV) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pv[q] = xi[q * 64 + lane];
+      d4[q] = *reinterpret_cast<const f32x4*>(&pst.dr[8 * q + 4 * h]);
+    }
+  }
+  bf16x8 ob[AH], tb[AH];
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    ob[j] = bw_read_row(cst.t.v, lo, j);
+    if constexpr (PV) tb[j] = bw_read_tr(pst.t.k, lo, j);
+  }
+  const f32x16 dc = w.nx;
+  bf16x8 dsp[2];
+  f32x16 dn = {};
+  __builtin_amdgcn_sched_barrier(0);
+  // slot j: product j of dP(m), dS weights 4j .. 4j+3 (j < 4), and product j - 4
+  // of dK^T once the weights are packed
+#pragma unroll
+  for (int j = 0; j < 20; ++j) {
+    if (j < 16) {
+      dn = mfma32(ob[j % AH], w.f[j], dn);
+      if (j + AH < 16) ob[j % AH] = bw_read_row(cst.t.v, lo, j + AH);
+    }
+    if constexpr (PV) {
+      if (j < 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsp[j >> 1][4 * (j & 1) + e] = f2bf(pv[j][e] * (dc[4 * j + e] - d4[j][e]));
+      }
+      if (j >= 4) {
+        const int jk = j - 4;
+        w.acc[jk >> 1] = mfma32(tb[jk % AH], dsp[jk & 1], w.acc[jk >> 1]);
+        if (jk + AH < 16) tb[jk % AH] = bw_read_tr(pst.t.k, lo, jk + AH);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  w.nx = dn;
+}
+
+// One workgroup per (sample, block of 64 keys), XCD-placed per sample; the
+// query tiles (16 tokens) with a visible pair for any key of the block are
+// listed up front (class merged over the block's two key tiles), each is four
+// steps of 4 tokens.  Rows of padded tokens and rows past the last token load
+// as zeros: their dO and dS rows are zero, so they add exactly nothing.  Keys
+// past the end read key 0 and are never stored; a padded key's K and V are
+// zeros and its pairs are masked (its tiles are PARTIAL).
+__global__ void __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+dkdv32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+              const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dr,
+              __bf16* __restrict__ dk, __bf16* __restrict__ dv, int L, float scale, float c2,
+              const uint32_t* __restrict__ tok, const uint8_t* __restrict__ tiles, int n_qt, int n_kt,
+              uint32_t forbid, Placement place) {
+  __shared__ BwStage st0, st1, st2, st3;
+  __shared__ f32x4 xch[2][2][4 * 64];     // [slot][pair]: P of a tile, lane-ordered
+  __shared__ uint32_t qlist[kMaxQTiles32];
+  __shared__ uint32_t qvalid[kMaxTiles];
+  __shared__ int qcount;
+  int b, kblk;
+  if (!xcd_place(place, b, kblk)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int role = __builtin_amdgcn_readfirstlane(wave & 1), pair = __builtin_amdgcn_readfirstlane(wave >> 1);
+  const int key0 = kblk * kKeys32;
+  const uint32_t* tk = tok + (size_t)b * L;
+  token_bitmap(tk, L, n_kt, NW, qvalid);
+  if (wave == 0) {
+    const uint8_t* trow = tiles + (size_t)b * n_qt * n_kt;
+    const int kt_lo = key0 / TK, kt_hi = min(n_kt, (key0 + kKeys32 + TK - 1) / TK);
+    int cnt = 0;
+    for (int base = 0; base < n_qt; base += 64) {
+      const int qt = base + lane;
+      int cls = 0;
+      if (qt < n_qt) {
+        cls = -1;
+        for (int kt = kt_lo; kt < kt_hi; ++kt) {
+          const int cl = trow[(size_t)qt * n_kt + kt];
+          cls = (cls < 0) ? cl : (cls == cl ? cls : PI_TILE_PARTIAL);
+        }
+      }
+      const unsigned long long bal = __ballot(cls > 0);
+      if (cls > 0) qlist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (uint32_t)qt | ((uint32_t)cls << 16);
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) qcount = cnt;
+  }
+  BwWave w;
+  const int key = key0 + 32 * pair + (lane & 31);
+  const bool ok = key < L;
+  {
+    const int64_t r = (int64_t)b * L + (ok ? key : 0);
+    w.wk = ok ? tk[key] : 0u;
+    const bool live = (w.wk & 1u) != 0u;
+    const __bf16* src = (role == 0 ? k : v) + r * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(src + 16 * j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w.f[j][e] = live ? a[e] : f2bf(0.f);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) w.acc[c] = f32x16{};
+  }
+  __syncthreads();
+  const int n = 4 * qcount;
+  const BwLanes lo = make_bw_lanes();
+  const float* lse2_b = lse2 + (size_t)b * L * G;
+  const float* dr_b = dr + (size_t)b * L * G;
+  const __bf16* q_b = q + (size_t)b * L * G * D;
+  const __bf16* o_b = dout + (size_t)b * L * G * D;
+  auto partial = [&](int i) { return (int)((qlist[i >> 2] >> 16) & 0xFFu) == PI_TILE_PARTIAL; };
+  // this wave's loads of step i: the 8 rows of token t0 + wave of Q and dO, and the
+  // statistics of the 32 rows (wave 0 the query words, 1 lse2, 2 Dr)
+  auto issue = [&](int i, BwStage& sg) {
+    const int t0 = (int)(qlist[i >> 2] & 0xFFFFu) * PI_MASK_TILE_Q + (i & 3) * 4;
+    const int tw = t0 + wave;
+    const bool in = (qvalid[tw >> 5] >> (tw & 31)) & 1u;
+    const int64_t at = (int64_t)__builtin_amdgcn_readfirstlane(t0) * G * D * 2;
+    const i32x4 rq = make_rsrc(reinterpret_cast<const char*>(q_b) + at);
+    const i32x4 ro = make_rsrc(reinterpret_cast<const char*>(o_b) + at);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t off = in ? lo.ld[jj] : kOOB;
+      pi_buffer_load_lds(rq, lds_u32(&sg.t.k[(8 * wave + 2 * jj) * D]), 16, (int)off, 0, 0, 0);
+      pi_buffer_load_lds(ro, lds_u32(&sg.t.v[(8 * wave + 2 * jj) * D]), 16, (int)off, 0, 0, 0);
+    }
+    const bool row_in = lane < 32 && t0 + (lane >> 3) < L;
+    if (wave == 0) {
+      const uint32_t off = row_in ? (uint32_t)(t0 + (lane >> 3)) * 4u : kOOB;
+      pi_buffer_load_lds(make_rsrc(tk), lds_u32(&sg.t.w[0]), 4, (int)off, 0, 0, 0);
+    } else if (wave == 1) {
+      const uint32_t off = row_in ? (uint32_t)(t0 * G + lane) * 4u : kOOB;
+      pi_buffer_load_lds(make_rsrc(lse2_b), lds_u32(&sg.lse2[0]), 4, (int)off, 0, 0, 0);
+    } else if (wave == 2) {
+      const uint32_t off = row_in ? (uint32_t)(t0 * G + lane) * 4u : kOOB;
+      pi_buffer_load_lds(make_rsrc(dr_b), lds_u32(&sg.dr[0]), 4, (int)off, 0, 0, 0);
+    }
+  };
+  // The two roles run separate copies of the loop (the same barriers in the
+  // same order), so each keeps only its own values in registers.
+  auto run = [&](auto role_tag) {
+    constexpr int R = decltype(role_tag)::value;
+    if (n <= 0) return;
+    issue(0, st0);
+    if (n > 1) issue(1, st1);
+    wait_vmem();
+    __syncthreads();      // tiles 0 and 1 have landed
+    // prologue: A forms S(0)
+    if constexpr (R == 0) {
+      f32x16 x0 = {};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x0 = mfma32(bw_read_row(st0.t.k, lo, j), w.f[j], x0);
+      w.nx = x0;
+    }
+    // Step m: barrier (tile m+1 has landed; every wave is done with step m-1, so
+    // the stage of tile m-2 and the exchange slot A writes in this step are free),
+    // then this wave's loads of tile m+2 and its half of the pair's work.
+    auto step = [&](auto pv, int m, BwStage& prv, BwStage& cur, BwStage& nxt, BwStage& ld) {
+      constexpr bool PV = decltype(pv)::value;
+      wait_vmem();
+      __syncthreads();
+      if (m + 2 < n) issue(m + 2, ld);
+      if constexpr (R == 0)
+        bw_step_a<PV>(prv, cur, nxt, lo, w, m < n && partial(m), forbid, c2, &xch[m & 1][pair][0]);
+      else
+        bw_step_b<PV>(prv, cur, lo, w, &xch[(m + 1) & 1][pair][0]);
+    };
+    using NoPV = std::integral_constant<bool, false>;
+    using WithPV = std::integral_constant<bool, true>;
+    step(NoPV{}, 0, st3, st0, st1, st2);
+    for (int m = 1; m <= n; m += 4) {
+      step(WithPV{}, m, st0, st1, st2, st3);
+      if (m + 1 <= n) step(WithPV{}, m + 1, st1, st2, st3, st0);
+      if (m + 2 <= n) step(WithPV{}, m + 2, st2, st3, st0, st1);
+      if (m + 3 <= n) step(WithPV{}, m + 3, st3, st0, st1, st2);
+    }
+  };
+  if (role == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
+  // outputs through a free stage: dV (A waves) and dK (B waves), 32 key rows each
+  wait_vmem();
+  __syncthreads();
+  __bf16* buf = wave == 0 ? st0.t.k : wave == 1 ? st0.t.v : wave == 2 ? st1.t.k : st1.t.v;
+  __bf16* out = role == 0 ? dv : dk;
+  store_rows_staged(w.acc, role == 0 ? 1.f : scale, buf, [&](int r, int x) -> __bf16* {
+    const int kr = key0 + 32 * pair + r;
+    return kr < L ? out + ((int64_t)b * L + kr) * D + 8 * x : nullptr;
+  });
+}
+
 }  // namespace
 
 namespace pi32 {
@@ -1289,6 +1658,18 @@ pi_status decode(const pi_kv_cache* cache, const __bf16* ckl, const __bf16* cvl,
   combine32_kernel<<<(unsigned)(n_chunks * 2), 256, 0, s>>>(opart, mlpart, static_cast<__bf16*>(o_s),
                                                               tiled ? 1 : 0, n_chunks, n_qblk, S, G, splits, nullptr);
   return pi::check_launch("combine32_kernel");
+}
+
+pi_status dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* dr,
+               void* dk, void* dv, int B, int L, float scale, const pi_mask* m, hipStream_t s) {
+  const Placement place = make_placement(B, (L + kKeys32 - 1) / kKeys32);
+  const int64_t grid = placement_grid(place);
+  PI_REQUIRE(grid < (1ll << 31), PI_ERR_UNSUPPORTED, "dkdv: grid too large");
+  dkdv32_kernel<<<(unsigned)grid, THREADS, 0, s>>>(
+      static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+      static_cast<const __bf16*>(dout), lse2, dr, static_cast<__bf16*>(dk), static_cast<__bf16*>(dv), L, scale,
+      scale * 1.4426950408889634f, m->tok, m->tiles, m->n_qt, m->n_kt, m->forbid_bits, place);
+  return pi::check_launch("dkdv32_kernel");
 }
 
 pi_status dq(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* dr, void* dq,

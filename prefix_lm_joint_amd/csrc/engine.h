@@ -55,14 +55,8 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
 //   V transposing read: 16 lanes read 4 rows x 32 bytes (two chunks).
 //     d = 256: f_V(r) = 2r & 31; d = 64: f_V(r) = r & 6; 32 lanes (8 rows) then
 //     cover all 64 banks once.
-//   Both reads of one tile (d = 256, the backward dK/dV kernel): f_U(r) = 2(r & 7) ^
-//     ((r >> 3) & 1) ^ (r & 8).  Over 16 consecutive rows it takes each value
-//     0..15 once; rows 8h .. 8h+7 share the low bit and have distinct 2(r & 7),
-//     so the transposing read's 8 rows x chunks (2x, 2x+1) hit 16 distinct chunk
-//     positions.  Rows r and r + 8 must also differ in chunk bit 3: with only
-//     the low bit between them, the row-wise 16-byte read measures 2-way bank
-//     conflicts on gfx950 (the LDS conflict counter), with bit 3 as well it
-//     measures none, like the transposing read.
+// (The 32 x 32 x 16 engine's tiles, read both row-wise and transposed in the
+// backward, use their own swizzle: attention32.hip.)
 // ---------------------------------------------------------------------------
 template <int D>
 struct Tile {
@@ -71,7 +65,6 @@ struct Tile {
   static constexpr int INSTS = TK / RPI;            // load instructions per tensor tile
   __device__ static __forceinline__ int fk(int r) { return D == 256 ? (r & 15) : ((r >> 1) & 7); }
   __device__ static __forceinline__ int fv(int r) { return D == 256 ? ((2 * r) & 31) : (r & 6); }
-  __device__ static __forceinline__ int fu(int r) { return (2 * (r & 7)) ^ ((r >> 3) & 1) ^ (r & 8); }
 };
 
 template <int D>
