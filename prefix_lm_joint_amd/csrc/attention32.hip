@@ -1233,7 +1233,7 @@ dq32_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __
 // Step m: A runs dV += dO^T(m-1) P(m-1) and S(m+1) slot by slot while it turns
 // S(m) into P(m) (written to the exchange slot of tile m); B reads P(m-1)
 // (written by A in step m-1), forms dS(m-1) while its dP(m) products start, and
-// runs dK += Q^T(m-1) dS(m-1) four slots behind them.  A step touches tiles
+// runs dK += Q^T(m-1) dS(m-1) eight slots behind them.  A step touches tiles
 // m-1, m and m+1 while tile m+2 loads: four stages.  Steps run for m = 0 .. n,
 // the first without the dV / dK products, the last with its S / dP dropped.
 // ---------------------------------------------------------------------------
@@ -1387,7 +1387,7 @@ __device__ __forceinline__ void bw_step_a(const BwStage& pst, const BwStage& cst
 
 // One step m of wave B (tiles m-1, m in `pst`, `cst`): with PV, dS(m-1) =
 // P(m-1) (dP(m-1) - Dr) from the exchange slot `xi`, w.nx (dP(m-1)) and tile
-// m-1's Dr, and dK^T += Q^T(m-1) dS(m-1) four slots behind; dP(m) = dO(m) V^T
+// m-1's Dr, and dK^T += Q^T(m-1) dS(m-1) eight slots behind; dP(m) = dO(m) V^T
 // into w.nx.
 template <bool PV>
 __device__ __forceinline__ void bw_step_b(const BwStage& pst, const BwStage& cst, const BwLanes& lo, BwWave& w,
@@ -1412,21 +1412,23 @@ __device__ __forceinline__ void bw_step_b(const BwStage& pst, const BwStage& cst
   bf16x8 dsp[2];
   f32x16 dn = {};
   __builtin_amdgcn_sched_barrier(0);
-  // slot j: product j of dP(m), dS weights 4j .. 4j+3 (j < 4), and product j - 4
-  // of dK^T once the weights are packed
+  // slot j: product j of dP(m); in slots 4..7 (once the exchanged weights have
+  // arrived) dS weights 4(j-4) .. +3; product j - 8 of dK^T once they are packed
+  constexpr int DS0 = 4, DK0 = 8;
 #pragma unroll
-  for (int j = 0; j < 20; ++j) {
+  for (int j = 0; j < 16 + DK0; ++j) {
     if (j < 16) {
       dn = mfma32(ob[j % AH], w.f[j], dn);
       if (j + AH < 16) ob[j % AH] = bw_read_row(cst.t.v, lo, j + AH);
     }
     if constexpr (PV) {
-      if (j < 4) {
+      if (j >= DS0 && j < DS0 + 4) {
+        const int q = j - DS0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dsp[j >> 1][4 * (j & 1) + e] = f2bf(pv[j][e] * (dc[4 * j + e] - d4[j][e]));
+        for (int e = 0; e < 4; ++e) dsp[q >> 1][4 * (q & 1) + e] = f2bf(pv[q][e] * (dc[4 * q + e] - d4[q][e]));
       }
-      if (j >= 4) {
-        const int jk = j - 4;
+      if (j >= DK0) {
+        const int jk = j - DK0;
         w.acc[jk >> 1] = mfma32(tb[jk % AH], dsp[jk & 1], w.acc[jk >> 1]);
         if (jk + AH < 16) tb[jk % AH] = bw_read_tr(pst.t.k, lo, jk + AH);
       }
