@@ -154,20 +154,41 @@ __device__ __forceinline__ void init_state(State& st) {
 
 __device__ __forceinline__ float xhalf_max(float v) { return fmaxf(v, __shfl_xor(v, 32)); }
 
+// Visibility of a tile's keys for this lane's row, when a kernel can form it
+// without the per-pair rule: bit k set if key k of the tile is visible.
+struct VisWord {
+  uint32_t w;
+};
+
 // Softmax, branchy part (tile i, before its weights): the per-pair rule of a
 // PARTIAL tile, and until every row of the wave has a reference maximum, the
 // maxima of rows that lack one.
-//   words(q): the key words of this lane's keys 8q + 4(lane/32) .. + 3 of the tile.
+//   words(q): the key words of this lane's keys 8q + 4(lane/32) .. + 3 of the tile,
+//             or a VisWord of the whole tile (then called once).
+// A masked score becomes -inf; with a VisWord each element costs a bit-field
+// extract (0 or all ones) and a bit-field insert of -inf.
 template <typename Words>
 __device__ __forceinline__ void softmax_pre(State& st, f32x16& s, int cls, uint32_t forbid, float scale_log2,
                                             Words words) {
   if (cls == PI_TILE_PARTIAL) {
+    if constexpr (std::is_same<decltype(words(0)), VisWord>::value) {
+      const uint32_t mh = words(0).w >> (4 * ((threadIdx.x >> 5) & 1));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 w = words(q);
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!pair_visible(st.wq, w[e], forbid)) s[4 * q + e] = -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          const int bit = 8 * q + e;
+          const uint32_t keep = (uint32_t)((int32_t)(mh << (31 - bit)) >> 31);
+          s[4 * q + e] = __uint_as_float((__float_as_uint(s[4 * q + e]) & keep) | (0xFF800000u & ~keep));
+        }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w = words(q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!pair_visible(st.wq, w[e], forbid)) s[4 * q + e] = -INFINITY;
+      }
     }
   }
   if (!st.all_set) {
@@ -639,7 +660,7 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
                 float* __restrict__ mlpart, int rope, double rope_log2_base) {
   __shared__ Stage stage0, stage1, stage2, stage3;
   __shared__ uint32_t sbid[128];
-  __shared__ alignas(16) uint32_t swords[128 + TK];   // key word of suffix key u (0 past the suffix)
+  __shared__ int send[128];        // end of suffix token u's block: the first later block start, or S
   __shared__ uint32_t pmask[kMaxTiles];
   __shared__ u32x2 tdesc[kMaxTiles];      // (tile | class << 16 | suffix << 24, key-validity bitmap)
   __shared__ double rope_if[D / 2];
@@ -693,8 +714,24 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
       if (lane == 32 && base / TK + 1 < n_pt) pmask[base / TK + 1] = (uint32_t)(bal >> 32);
     }
   }
-  // suffix block ids: inclusive cumsum of the flags, by wave 0
+  // suffix block ids: inclusive cumsum of the flags, by wave 0; and the end of
+  // each token's block (the first flagged position after it, or S), from a
+  // suffix minimum of the flagged positions
   if (wave == 0) {
+    constexpr int kNone = 1 << 20;
+    int p0 = a0 ? lane : kNone, p1 = a1 ? lane + 64 : kNone;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v0 = __shfl_down(p0, off), v1 = __shfl_down(p1, off);
+      if (lane + off < 64) {
+        p0 = min(p0, v0);
+        p1 = min(p1, v1);
+      }
+    }
+    const int min_hi = __shfl(p1, 0);          // first flag in [64, 128)
+    const int n0 = __shfl_down(p0, 1), n1 = __shfl_down(p1, 1);
+    send[lane] = min(S, lane == 63 ? min_hi : min(n0, min_hi));
+    send[lane + 64] = min(S, lane == 63 ? kNone : n1);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int u0 = __shfl_up(a0, off), u1 = __shfl_up(a1, off);
@@ -706,9 +743,6 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     const int tot0 = __shfl(a0, 63);
     sbid[lane] = 1u | ((uint32_t)(1 + a0) << 3);
     sbid[lane + 64] = 1u | ((uint32_t)(1 + tot0 + a1) << 3);
-    swords[lane] = lane < S ? 1u | ((uint32_t)(1 + a0) << 3) : 0u;
-    swords[lane + 64] = lane + 64 < S ? 1u | ((uint32_t)(1 + tot0 + a1) << 3) : 0u;
-    if (lane < TK) swords[128 + lane] = 0u;
   }
   __syncthreads();
   // compact tile list: non-empty prefix tiles, then the suffix tiles
@@ -736,6 +770,8 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
   }
   __syncthreads();
   st.wq = row_ok ? sbid[t] : 0u;
+  // the suffix keys this row sees: [0, lim) (block ids never decrease along the suffix)
+  const int lim = row_ok ? send[t] : 0;
   const int i_lo = (int)((int64_t)tcount * split / n_split);
   const int i_hi = (int)((int64_t)tcount * (split + 1) / n_split);
 
@@ -758,20 +794,16 @@ decode32_kernel(const __bf16* __restrict__ ck, const __bf16* __restrict__ cv,
     return pl;
   };
   auto issue_words = [](Stage*, const LoadPlan&) {};
-  // key words of the current tile (masked tiles only): a cache slot's is its validity
-  // bit (block id 0); a suffix key's comes from the table (its block id, 0 past the
-  // suffix), four consecutive keys in one read
-  auto words = [&](const Stage*, const TileDesc& t, int q) {
-    const uint32_t d = t.d, m = t.m;
-    const int k4 = 8 * q + 4 * (lane >> 5);
-    u32x4 w;
+  // visibility of the current tile's keys (masked tiles only): a cache slot is seen
+  // by every row of the suffix if it is valid; suffix key u by the rows whose block
+  // ends past u
+  auto words = [&](const Stage*, const TileDesc& tl, int) {
+    const uint32_t d = tl.d;
     if ((d >> 24) & 1u) {
-      w = *reinterpret_cast<const u32x4*>(&swords[(int)(d & 0xFFFFu) * TK + k4]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = (m >> (k4 + e)) & 1u;
+      const int lj = lim - TK * (int)(d & 0xFFFFu);
+      return VisWord{lj >= TK ? 0xFFFFFFFFu : lj <= 0 ? 0u : (1u << lj) - 1u};
     }
-    return w;
+    return VisWord{row_ok ? tl.m : 0u};
   };
   bool rotated = !rope;
   auto prep = [&]() {

@@ -320,6 +320,40 @@ def test_decode_few_samples_holes_nan_and_spike(seed, B, P, cap, S, split):
     assert_close(got, want, f"few-sample decode seed={seed} split={split}")
 
 
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("seed,B,P,S,flags", [(20, 6, 70, 128, "random"), (21, 5, 40, 100, "all"),
+                                              (22, 7, 33, 37, "random"), (23, 6, 64, 65, "last")])
+def test_decode_multi_block_suffix(seed, B, P, S, flags, split):
+    """The batched decode with suffixes of several blocks (random block starts,
+    every token its own block as in an autoregressive suffix, a lone block start
+    at the last token), up to the 128-token limit: each row sees the cache's valid
+    slots and the suffix up to the end of its own block.  Every row against the
+    oracle."""
+    Bd = _bd()
+    note(f"decode multi-block suffix seed={seed} B={B} P={P} S={S} flags={flags} split={split}")
+    r = np.random.default_rng(seed)
+    ck = I.bf16_normal(seed * 7 + 1, (1, B, P, 1, 256))
+    cv = I.bf16_normal(seed * 7 + 2, (1, B, P, 1, 256))
+    pm = I.tail_padding_mask(r.integers(P // 2, P + 1, B), P)
+    if flags == "random":
+        sar = (r.random(S) < 0.2).astype(np.uint8)
+    elif flags == "all":
+        sar = np.ones(S, np.uint8)
+    else:
+        sar = np.zeros(S, np.uint8)
+        sar[S - 1] = 1
+    sar[0] = 1
+    qs = I.bf16_normal(seed * 7 + 3, (B, S, 8, 256))
+    ks = I.bf16_normal(seed * 7 + 4, (B, S, 1, 256))
+    vs = I.bf16_normal(seed * 7 + 5, (B, S, 1, 256))
+    cache = _cache_from(ck, cv, pm)
+    ws = Bd.decode_workspace(cache, S) if split else None
+    o = Bd.pi_suffix_decode_step(cache, 0, bf16_dev(qs), bf16_dev(ks), bf16_dev(vs), u8_dev(sar), workspace=ws)
+    torch.cuda.synchronize()
+    want = A.cached_decode(f64(qs), f64(ks), f64(vs), f64(ck[0]), f64(cv[0]), pm, sar)
+    assert_close(host64(o), want, f"decode multi-block seed={seed} split={split}")
+
+
 def test_decode_matches_full_recompute():
     """The cached path equals the suffix rows of the joint prefill (same inputs)."""
     Bd = _bd()
