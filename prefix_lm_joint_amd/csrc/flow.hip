@@ -48,6 +48,46 @@ struct GemmArgs {
 
 constexpr float kRmsEps = 1e-6f;
 
+// Epilogue of four consecutive output columns nb .. nb+3 of row m (r: the
+// product, already divided by the row's rms when the product normalises).
+template <int EPI>
+__device__ __forceinline__ void finish_store(const GemmArgs& p, int m, int nb, f32x4 r) {
+  if constexpr (EPI == EPI_QKV) {
+    // q in the decode's tile layout (rows t*8 + head per sample, padded to 16),
+    // k and v row-major
+    __bf16* dst;
+    if (nb < p.n1) {
+      const int64_t qrow = (int64_t)(m / p.S) * ((p.S * 8 + 15) / 16 * 16) + (m % p.S) * 8 + nb / 256;
+      dst = p.o0 + tiled_offset(qrow, nb % 256, 256);
+    } else if (nb < p.n1 + p.n2) dst = p.o1 + (int64_t)m * p.n2 + (nb - p.n1);
+    else dst = p.o2 + (int64_t)m * (p.N - p.n1 - p.n2) + (nb - p.n1 - p.n2);
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = f2bf(r[i]);
+    *reinterpret_cast<bf16x4*>(dst) = v;
+  } else if constexpr (EPI == EPI_RESID) {
+    // h += o W_o^T, and r(h) for the next projection (N is a multiple of 64)
+    f32x4* dst = reinterpret_cast<f32x4*>(p.out + (int64_t)m * p.N + nb);
+    f32x4 hv = *dst;
+    hv += r;
+    *dst = hv;
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = f2bf(hv[i]);
+    *reinterpret_cast<bf16x4*>(p.a_out + tiled_offset(m, nb, p.N)) = v;
+  } else {
+    const int j = m % p.S;
+    if (j == 0) return;                            // state token: no velocity
+    float* dst = p.out + ((int64_t)(m / p.S) * (p.S - 1) + j - 1) * p.N + nb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (nb + i >= p.N) break;
+      if constexpr (EPI == EPI_VEL) dst[i] = r[i] + p.bias[nb + i];
+      else dst[i] += p.dt * (r[i] + p.bias[nb + i]);
+    }
+  }
+}
+
 // out[m][n] = sum_k A[m][k] W[n][k]  (divided by rms(A[m]) when NORM).
 //
 // Workgroup tile TN = 16*NT columns x 64 rows.  The NWV waves split the
@@ -148,40 +188,93 @@ __global__ void __launch_bounds__(NWV * 64) gemm_kernel(GemmArgs p) {
       for (int w = 0; w < NWV; ++w) t += ssp[w][ml];
       r *= rsqrtf(t / (float)p.K + kRmsEps);
     }
-    if constexpr (EPI == EPI_QKV) {
-      // q in the decode's tile layout (rows t*8 + head per sample, padded to 16),
-      // k and v row-major
-      __bf16* dst;
-      if (nb < p.n1) {
-        const int64_t qrow = (int64_t)(m / p.S) * ((p.S * 8 + 15) / 16 * 16) + (m % p.S) * 8 + nb / 256;
-        dst = p.o0 + tiled_offset(qrow, nb % 256, 256);
-      } else if (nb < p.n1 + p.n2) dst = p.o1 + (int64_t)m * p.n2 + (nb - p.n1);
-      else dst = p.o2 + (int64_t)m * (p.N - p.n1 - p.n2) + (nb - p.n1 - p.n2);
-      bf16x4 v;
+    finish_store<EPI>(p, m, nb, r);
+  }
+}
+
+// Products of many rows (a batch of samples: M > 256, N a multiple of 256, K of
+// 128): workgroup tile 64 rows x 256 columns, four waves each owning 64 columns
+// of all 64 rows (4 x 4 products of 16 x 16 per k-step of 32).  A wave streams
+// its own fragments, the tile's four A fragments (the same for the four waves,
+// shared through the L1) and its four W fragments, kWideAhead k-steps ahead of
+// its products, so no LDS stage and no barrier sits in the loop.  Tiles go to
+// the XCDs in contiguous runs of a grouped order (eight row tiles, columns
+// fastest), so each XCD's L2 holds about eight row tiles of A and eight column
+// blocks of W.  With NORM, wave w also sums the squares of row block w.
+constexpr int kWideAhead = 4;
+
+template <int EPI, bool NORM>
+__global__ void __launch_bounds__(256) gemm_wide_kernel(GemmArgs p) {
+  constexpr int P = kWideAhead;
+  __shared__ float ssq[64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int n_mt = (p.M + 63) / 64, n_nt = p.N / 256, T = n_mt * n_nt;
+  const int per = (T + 7) / 8;
+  const int t = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
+  if (t >= T) return;
+  const int gsz = 8 * n_nt;
+  const int grp = t / gsz, rem = t % gsz;
+  const int rows_in_grp = min(8, n_mt - grp * 8);
+  const int mt = grp * 8 + rem % rows_in_grp, nt = rem / rows_in_grp;
+  const int m0 = mt * 64, n0 = nt * 256 + 64 * wave;
+  const int kb = p.K / 32;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  const bf16x8* at = reinterpret_cast<const bf16x8*>(p.a) + (int64_t)(m0 / 16) * kb * 64 + lane;
+  const bf16x8* wt = reinterpret_cast<const bf16x8*>(p.w) + (int64_t)(n0 / 16) * kb * 64 + lane;
+
+  f32x4 acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = f2bf(r[i]);
-      *reinterpret_cast<bf16x4*>(dst) = v;
-    } else if constexpr (EPI == EPI_RESID) {
-      // h += o W_o^T, and r(h) for the next projection (N is a multiple of 64)
-      f32x4* dst = reinterpret_cast<f32x4*>(p.out + (int64_t)m * p.N + nb);
-      f32x4 hv = *dst;
-      hv += r;
-      *dst = hv;
-      bf16x4 v;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = f2bf(hv[i]);
-      *reinterpret_cast<bf16x4*>(p.a_out + tiled_offset(m, nb, p.N)) = v;
-    } else {
-      const int j = m % p.S;
-      if (j == 0) continue;                          // state token: no velocity
-      float* dst = p.out + ((int64_t)(m / p.S) * (p.S - 1) + j - 1) * p.N + nb;
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  bf16x8 af[P][4], wf[P][4];
+  auto load = [&](int slot, int ks) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (nb + i >= p.N) break;
-        if constexpr (EPI == EPI_VEL) dst[i] = r[i] + p.bias[nb + i];
-        else dst[i] += p.dt * (r[i] + p.bias[nb + i]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      af[slot][j] = at[((int64_t)j * kb + ks) * 64];
+      wf[slot][j] = wt[((int64_t)j * kb + ks) * 64];
     }
+  };
+#pragma unroll
+  for (int u = 0; u < P; ++u) load(u, u);
+  for (int ks0 = 0; ks0 < kb; ks0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      if constexpr (NORM) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j == wv) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float x = bf2f(af[u][j][i]);
+              ss += x * x;
+            }
+          }
+      }
+#pragma unroll
+      for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+        for (int jm = 0; jm < 4; ++jm) acc[jn][jm] = mfma16x16x32(wf[u][jn], af[u][jm], acc[jn][jm]);
+      if (ks0 + u + P < kb) load(u, ks0 + u + P);
+    }
+  }
+  float inv[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (NORM) {
+    const float tsum = group4_sum(ss);
+    if (g == 0) ssq[16 * wave + c] = tsum;
+    __syncthreads();
+#pragma unroll
+    for (int jm = 0; jm < 4; ++jm) inv[jm] = rsqrtf(ssq[16 * jm + c] / (float)p.K + kRmsEps);
+  }
+#pragma unroll
+  for (int jm = 0; jm < 4; ++jm) {
+    const int m = m0 + 16 * jm + c;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn) finish_store<EPI>(p, m, n0 + 16 * jn + 4 * g, acc[jn][jm] * inv[jm]);
   }
 }
 
@@ -257,8 +350,10 @@ __global__ void euler_kernel(float* __restrict__ x, const float* __restrict__ v,
 // (the output projection back to the width: 256 workgroups, each with a quarter of
 // the activations), 32 x 32 when they are many (the QKV projection: 160
 // workgroups reading 64 KB of weights and 64 KB of activations each; measured
-// against 16 x 64 and 64 x 16: 4 % and 8 % faster at B = 1).  64 x 64 tiles with
-// four waves once the rows alone give enough workgroups.
+// against 16 x 64 and 64 x 16: 4 % and 8 % faster at B = 1).  A batch of samples
+// (more rows) takes the wide tiles of gemm_wide_kernel (at B = 64: the QKV
+// product 36.9 -> 27.4 us, the output projection 31.5 -> 28.4 us against 64 x 64
+// tiles of four waves splitting the contraction, which remain for other shapes).
 template <int EPI, bool NORM>
 pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
   if (a.M <= 256 && (a.N + 15) / 16 * ((a.M + 63) / 64) < 128) {
@@ -267,6 +362,9 @@ pi_status gemm(const GemmArgs& a, hipStream_t s, const char* name) {
   } else if (a.M <= 256) {
     dim3 grid((a.N + 31) / 32, (a.M + 31) / 32);
     gemm_kernel<EPI, NORM, 2, 16, 2><<<grid, 1024, 0, s>>>(a);
+  } else if (a.N % 256 == 0 && a.K % (32 * kWideAhead) == 0) {
+    const int tiles = (a.M + 63) / 64 * (a.N / 256);
+    gemm_wide_kernel<EPI, NORM><<<(unsigned)((tiles + 7) / 8 * 8), 256, 0, s>>>(a);
   } else {
     dim3 grid((a.N + 63) / 64, (a.M + 63) / 64);
     gemm_kernel<EPI, NORM, 4, 4, 4><<<grid, 256, 0, s>>>(a);

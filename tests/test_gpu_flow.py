@@ -61,8 +61,12 @@ def _net_case(seed, B, P, H, A, W, layers, lens=None):
     return net, cache, u8_dev(sar), state, x0, oracle_v
 
 
-@pytest.mark.parametrize("seed,B,P,H,A,W,layers", [(100, 2, 100, 50, 32, 256, 3), (200, 3, 45, 8, 4, 128, 2)])
+@pytest.mark.parametrize("seed,B,P,H,A,W,layers", [(100, 2, 100, 50, 32, 256, 3), (200, 3, 45, 8, 4, 128, 2),
+                                                   (600, 7, 64, 50, 32, 256, 2), (700, 6, 40, 50, 32, 512, 1)])
 def test_velocity_eval_small(seed, B, P, H, A, W, layers):
+    """Against the oracle on every row; the last two cases have more than 256 token
+    rows (357 and 306, a partial last 64-row tile), so their projections take the
+    wide-tile product of a batch of samples."""
     Bd = _bd()
     note(f"velocity eval seed={seed}")
     net, cache, sar, state, x0, oracle_v = _net_case(seed, B, P, H, A, W, layers)
