@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: device upload of the seeded inputs and the
-spec tolerance check (max-abs <= 1e-2, mean-abs <= 1e-3 against the fp64
+parity tolerance check (max-abs <= 1e-2, mean-abs <= 1e-3 against the fp64
 oracle on unit-variance bf16 inputs)."""
 import os
 import sys
