@@ -94,6 +94,21 @@ class Ctx:
         b.synchronize()
         return a.elapsed_time(b) / iters
 
+    def time_dist_us(self, fn, iters):
+        """p10 / p50 / p90 of the per-call time in µs: an event on the launch stream
+        between consecutive calls (run right after time_ms, at the same clocks)."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(self.stream)
+        for i in range(iters):
+            fn()
+            ev[i + 1].record(self.stream)
+        ev[-1].synchronize()
+        d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(iters))
+        pick = lambda q: d[min(iters - 1, int(q * iters))]
+        return {"p10": pick(0.1), "p50": pick(0.5), "p90": pick(0.9)}
+
 
 # ---------------------------------------------------------------------------
 # π0 control step (B = 1)
@@ -162,12 +177,13 @@ def prefill_kernel_leg(cx: Ctx, iters: int, workload: str):
     pairs = int(Bd.pi_mask_materialize(m).sum(dtype=torch.int64).item())
     o = torch.empty_like(q)
     ms = cx.time_ms(lambda: Bd.pi_joint_attn_prefill(q, k, v, m, o=o), iters)
+    dist = cx.time_dist_us(lambda: Bd.pi_joint_attn_prefill(q, k, v, m, o=o), iters)
     flops = 4.0 * w.d * w.Hq * pairs   # QK^T and PV, 2 flops per multiply-add, per head
     byts = (q.numel() + k.numel() + v.numel() + o.numel()) * 2
     tflops = flops / (ms * 1e-3) / 1e12
     return {
         "workload": w.name, "B": w.B, "L": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
-        "allowed_pairs": pairs, "gflop_per_launch": flops / 1e9, "us_per_launch": ms * 1e3,
+        "allowed_pairs": pairs, "gflop_per_launch": flops / 1e9, "us_per_launch": ms * 1e3, "us_per_call": dist,
         "achieved_tflops": tflops, "mfma_frac": tflops * 1e12 / PEAK_BF16_FLOPS,
         "algorithmic_bytes": byts, "kernel": "prefill_kernel",
     }
@@ -421,6 +437,7 @@ def decode_kernel_leg(cx: Ctx, iters: int):
         state["l"] += 1
 
     ms = cx.time_ms(call, iters)
+    dist = cx.time_dist_us(call, iters)
     kv_bytes = int(lens.sum()) * 256 * 2 * 2
     qo_bytes = B * S * 8 * 256 * 2 * 2
     skv_bytes = B * S * 256 * 2 * 2
@@ -431,7 +448,7 @@ def decode_kernel_leg(cx: Ctx, iters: int):
     gbs = byts / (ms * 1e-3) / 1e9
     return {
         "workload": w.name, "B": B, "slots": P, "valid_len_mean": float(lens.mean()), "S": S,
-        "algorithmic_bytes_per_launch": byts, "us_per_launch": ms * 1e3, "achieved_gbs": gbs,
+        "algorithmic_bytes_per_launch": byts, "us_per_launch": ms * 1e3, "us_per_call": dist, "achieved_gbs": gbs,
         "hbm_frac": gbs * 1e9 / PEAK_HBM_BYTES, "gflop_per_launch": flops / 1e9,
         "achieved_tflops": flops / (ms * 1e-3) / 1e12, "kernel": "decode_kernel",
     }
@@ -808,6 +825,7 @@ def main():
         "frac": dec["achieved_gbs"] * 1e9 / PEAK_HBM_BYTES,
         "traffic": counted_traffic("decode_kernel", "decode_kernel_serving_B64_816slots_traffic.md"),
         "algorithmic_bytes_per_launch": dec["algorithmic_bytes_per_launch"], "us_per_launch": dec["us_per_launch"],
+        "us_per_call": dec["us_per_call"],
     }
     cpu = None
     if not args.no_cpu_baseline:
@@ -826,7 +844,7 @@ def main():
         "prefill_mfma": {"kernel": "prefill_kernel (pi05 B=32 L=962)", "bound": "mfma",
                          "achieved": pre["achieved_tflops"], "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                          "frac": pre["mfma_frac"], "us_per_launch": pre["us_per_launch"],
-                         "gflop_per_launch": pre["gflop_per_launch"],
+                         "us_per_call": pre["us_per_call"], "gflop_per_launch": pre["gflop_per_launch"],
                          "traffic": counted_traffic("prefill_kernel", "prefill_kernel_pi05_B32_L962_traffic.md"),
                          "algorithmic_bytes_per_launch": pre["algorithmic_bytes"]},
         "decode_hbm": {"kernel": "decode_kernel (B=64 816 slots)", "achieved_gbs": dec["achieved_gbs"],
