@@ -78,7 +78,8 @@ def test_velocity_eval_small(seed, B, P, H, A, W, layers):
                      NET_MAX_ABS, NET_MEAN_ABS)
 
 
-@pytest.mark.parametrize("seed,B,P,H,A,W,layers", [(300, 2, 100, 50, 32, 256, 3), (400, 1, 32, 8, 4, 64, 1)])
+@pytest.mark.parametrize("seed,B,P,H,A,W,layers", [(300, 2, 100, 50, 32, 256, 3), (400, 1, 32, 8, 4, 64, 1),
+                                                   (800, 6, 40, 50, 32, 256, 1)])
 def test_flow_sample_end_to_end_small(seed, B, P, H, A, W, layers):
     Bd = _bd()
     note(f"flow sample seed={seed}")
